@@ -1,0 +1,157 @@
+"""fp64 CPU oracle for the selective scan -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``oracle_scan.c`` (plain C,
+double precision, sequential in time) through ctypes and shares no code with the
+HIP library.  Every function here is pinned by the CPU tests in
+``tests/test_oracle_pins.py`` (brute force, LTI closed form, exact decay,
+split/decode invariances, special cases, planted-mistake checks).
+
+Inputs are float64 numpy arrays (callers expand stored fp32/bf16 values exactly
+before the call); outputs are float64 and never rounded to a storage type.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle_scan.c")
+LIBRARY = os.path.join(_HERE, "liboracle_scan.so")
+
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+          "-pthread"]
+
+
+def build(source: str = SOURCE, output: str = LIBRARY, extra_flags=()) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    cmd = ["gcc", *CFLAGS, *extra_flags, source, "-o", output, "-lm"]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+class Oracle:
+    """A loaded oracle library (the committed one, or a test build of a variant)."""
+
+    def __init__(self, path: str = LIBRARY):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.oracle_scan.restype = ctypes.c_int
+        lib.oracle_scan.argtypes = [_dp] * 11 + [_i64] * 4 + [ctypes.c_int]
+        lib.oracle_step.restype = ctypes.c_int
+        lib.oracle_step.argtypes = [_dp] * 10 + [_i64] * 3
+        lib.oracle_softplus.restype = ctypes.c_double
+        lib.oracle_softplus.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        self._lib = lib
+
+    # -- scalar helpers -------------------------------------------------------
+    def softplus(self, x: float) -> float:
+        return self._lib.oracle_softplus(float(x))
+
+    def silu(self, z: float) -> float:
+        return self._lib.oracle_silu(float(z))
+
+    # -- full scan ------------------------------------------------------------
+    def scan(self, u, delta, A, B, C, D=None, z=None, bias=None, h0=None,
+             nthreads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """Return (y, h_last) in float64.
+
+        u, delta, z: (batch, L, d_inner); B, C: (batch, L, d_state);
+        A: (d_inner, d_state); D, bias: (d_inner,); h0: (batch, d_inner, d_state).
+        """
+        u = _c64(u)
+        batch, L, d_inner = u.shape
+        A = _c64(A)
+        d_state = A.shape[1]
+        delta, B, C = _c64(delta), _c64(B), _c64(C)
+        D, z, bias, h0 = _c64(D), _c64(z), _c64(bias), _c64(h0)
+        _check(delta, u.shape, "delta")
+        _check(B, (batch, L, d_state), "B")
+        _check(C, (batch, L, d_state), "C")
+        _check(A, (d_inner, d_state), "A")
+        _check(D, (d_inner,), "D")
+        _check(bias, (d_inner,), "bias")
+        _check(z, u.shape, "z")
+        _check(h0, (batch, d_inner, d_state), "h0")
+        y = np.empty(u.shape, dtype=np.float64)
+        h_last = np.empty((batch, d_inner, d_state), dtype=np.float64)
+        if nthreads is None:
+            nthreads = default_threads()
+        rc = self._lib.oracle_scan(_p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
+                                   _p(bias), _p(h0), _p(y), _p(h_last), batch, L, d_inner,
+                                   d_state, int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_scan rejected its arguments")
+        return y, h_last
+
+    # -- one decode step ------------------------------------------------------
+    def step(self, h, u, delta, A, B, C, D=None, z=None, bias=None
+             ) -> Tuple[np.ndarray, np.ndarray]:
+        """Return (y, h_new); h is not modified.  u, delta, z: (batch, d_inner);
+        B, C: (batch, d_state); h: (batch, d_inner, d_state)."""
+        h_new = np.array(h, dtype=np.float64, copy=True, order="C")
+        u = _c64(u)
+        batch, d_inner = u.shape
+        A = _c64(A)
+        d_state = A.shape[1]
+        delta, B, C, D, z, bias = (_c64(delta), _c64(B), _c64(C), _c64(D), _c64(z),
+                                   _c64(bias))
+        _check(h_new, (batch, d_inner, d_state), "h")
+        _check(delta, u.shape, "delta")
+        _check(B, (batch, d_state), "B")
+        _check(C, (batch, d_state), "C")
+        _check(z, u.shape, "z")
+        y = np.empty(u.shape, dtype=np.float64)
+        rc = self._lib.oracle_step(_p(h_new), _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
+                                   _p(z), _p(bias), _p(y), batch, d_inner, d_state)
+        if rc != 0:
+            raise ValueError("oracle_step rejected its arguments")
+        return y, h_new
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _c64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(_dp)
+
+
+def _check(a, shape, name):
+    if a is not None and tuple(a.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(a.shape)}")
+
+
+_default: Optional[Oracle] = None
+
+
+def load() -> Oracle:
+    """The committed oracle, compiled on first use if it has not been built."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default

@@ -1,0 +1,229 @@
+"""Seeded synthetic workloads for the selective scan.
+
+This module only draws numbers and stores them in the two storage formats the
+library accepts (fp32 and bf16).  It holds none of the scan's arithmetic, and it
+is the only code shared between the HIP path and the fp64 oracle: both sides are
+fed the very same bits.
+
+Recipe (every config):
+  * ``numpy.random.default_rng(seed)``; parameters are drawn first, in the order
+    A jitter, dt, D, then activations u, delta, z, B, C, h0.
+  * Activations are standard normal draws made directly in float32
+    (``standard_normal(dtype=float32)``) and, for bf16 configs, rounded to bf16
+    with round-to-nearest-even.  bf16 values are carried as raw ``uint16`` bits.
+  * Parameters are computed in float64 and rounded once to float32:
+      - A[d, n] = -exp(A_log[d, n]) with A_log = log(n + 1) (S4D-real, the
+        "A = -exp(A_log)" parameterisation of "Understanding Mamba"
+        (aiattnstudio.link), section 5.2), plus N(0, 0.1) jitter where the
+        config asks for it;
+      - dt bias = inverse softplus of dt, dt log-uniform in [1e-3, 1e-1] (the
+        0.001-0.1 initial step range of the hnwysp.cn Mamba slides, section
+        4.1): bias = log(expm1(dt));
+      - D = 1, or U(0.5, 1.5) where the config asks for it.
+
+Shapes follow the pages' workloads: d_state 16, expand 2 (d_model 768 -> d_inner
+1536; d_model 2560 -> d_inner 5120), packed length 4096, 128K-token sequences.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+# ----------------------------------------------------------------------------
+# storage formats
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32)
+    nan = np.isnan(x)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    rounded = bits + np.uint32(0x7FFF) + lsb
+    out = (rounded >> np.uint32(16)).astype(np.uint16)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bits (uint16) to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_f64(arr: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
+    """Exact float64 expansion of a stored array (fp32 values or bf16 bits)."""
+    if arr is None:
+        return None
+    if arr.dtype == np.uint16:
+        return bf16_bits_to_f32(arr).astype(np.float64)
+    return np.asarray(arr, dtype=np.float32).astype(np.float64)
+
+
+def _store(x_f32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == BF16:
+        return f32_to_bf16_bits(x_f32)
+    return np.ascontiguousarray(x_f32, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------
+# configurations
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class ScanConfig:
+    name: str
+    desc: str
+    batch: int
+    seqlen: int
+    d_inner: int
+    d_state: int
+    dtype: str
+    a_jitter: bool      # A_log = log(n+1) + N(0, 0.1)
+    d_uniform: bool     # D ~ U(0.5, 1.5) instead of 1
+    gate: bool          # z given
+    h0: bool            # nonzero initial state h0 ~ N(0, 1)
+    seed: int
+
+    @property
+    def chan_steps(self) -> int:
+        return self.batch * self.seqlen * self.d_inner
+
+    def min_bytes(self, with_h_last: bool = True) -> int:
+        """Each input read once and each output written once, in stored dtype."""
+        es = 4 if self.dtype == F32 else 2
+        bld = self.batch * self.seqlen * self.d_inner
+        bln = self.batch * self.seqlen * self.d_state
+        dn = self.d_inner * self.d_state
+        bdn = self.batch * dn
+        n = bld * es * (2 + (1 if self.gate else 0))      # u, delta, z
+        n += 2 * bln * es                                 # B, C
+        n += dn * 4 + 2 * self.d_inner * 4                # A, D, bias
+        n += bdn * 4 if self.h0 else 0                    # h0
+        n += bld * es                                     # y
+        n += bdn * 4 if with_h_last else 0                # h_last
+        return n
+
+
+CONFIGS = {
+    "c1": ScanConfig("c1", "tiny scan, fp32", 1, 64, 32, 16, F32,
+                     a_jitter=False, d_uniform=False, gate=False, h0=False, seed=7201),
+    "c2": ScanConfig("c2", "small-model prefill scan", 4, 2048, 1536, 16, BF16,
+                     a_jitter=False, d_uniform=False, gate=True, h0=False, seed=7202),
+    "c3": ScanConfig("c3", "large-model prefill scan", 8, 4096, 5120, 16, BF16,
+                     a_jitter=True, d_uniform=True, gate=True, h0=False, seed=7203),
+    "c4": ScanConfig("c4", "long-sequence scan", 1, 131072, 2048, 16, BF16,
+                     a_jitter=False, d_uniform=False, gate=False, h0=True, seed=7204),
+}
+
+# recurrent decode: persistent state (256, 5120, 16), 1024 chained one-token steps
+DECODE = dict(name="c5", batch=256, d_inner=5120, d_state=16, dtype=BF16, steps=1024, seed=7205)
+
+
+@dataclasses.dataclass
+class Params:
+    A: np.ndarray       # (D, N) float32
+    D: np.ndarray       # (D,) float32
+    bias: np.ndarray    # (D,) float32
+
+
+@dataclasses.dataclass
+class ScanInputs:
+    cfg: ScanConfig
+    params: Params
+    u: np.ndarray
+    delta: np.ndarray
+    z: Optional[np.ndarray]
+    B: np.ndarray
+    C: np.ndarray
+    h0: Optional[np.ndarray]
+
+    @property
+    def dtype(self) -> str:
+        return self.cfg.dtype
+
+
+def draw_params(rng: np.random.Generator, d_inner: int, d_state: int,
+                a_jitter: bool, d_uniform: bool) -> Params:
+    n = np.arange(d_state, dtype=np.float64)
+    a_log = np.broadcast_to(np.log(n + 1.0), (d_inner, d_state)).copy()
+    if a_jitter:
+        a_log += rng.normal(0.0, 0.1, size=(d_inner, d_state))
+    A = (-np.exp(a_log)).astype(np.float32)
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=d_inner))
+    bias = np.log(np.expm1(dt)).astype(np.float32)
+    if d_uniform:
+        Dv = rng.uniform(0.5, 1.5, size=d_inner).astype(np.float32)
+    else:
+        Dv = np.ones(d_inner, dtype=np.float32)
+    return Params(A=A, D=Dv, bias=bias)
+
+
+def _normal(rng, shape, dtype):
+    return _store(rng.standard_normal(shape, dtype=np.float32), dtype)
+
+
+def make_scan_inputs(cfg: ScanConfig, *, batch: Optional[int] = None,
+                     seqlen: Optional[int] = None, d_inner: Optional[int] = None,
+                     seed: Optional[int] = None) -> ScanInputs:
+    """Draw one workload.  Shape overrides give smaller cases with the same recipe."""
+    if batch is not None or seqlen is not None or d_inner is not None:
+        cfg = dataclasses.replace(cfg, batch=batch or cfg.batch,
+                                  seqlen=cfg.seqlen if seqlen is None else seqlen,
+                                  d_inner=d_inner or cfg.d_inner)
+    if seed is not None:
+        cfg = dataclasses.replace(cfg, seed=seed)
+    rng = np.random.default_rng(cfg.seed)
+    p = draw_params(rng, cfg.d_inner, cfg.d_state, cfg.a_jitter, cfg.d_uniform)
+    bld = (cfg.batch, cfg.seqlen, cfg.d_inner)
+    bln = (cfg.batch, cfg.seqlen, cfg.d_state)
+    u = _normal(rng, bld, cfg.dtype)
+    delta = _normal(rng, bld, cfg.dtype)
+    z = _normal(rng, bld, cfg.dtype) if cfg.gate else None
+    B = _normal(rng, bln, cfg.dtype)
+    C = _normal(rng, bln, cfg.dtype)
+    h0 = (rng.standard_normal((cfg.batch, cfg.d_inner, cfg.d_state), dtype=np.float32)
+          if cfg.h0 else None)
+    return ScanInputs(cfg=cfg, params=p, u=u, delta=delta, z=z, B=B, C=C, h0=h0)
+
+
+# ----------------------------------------------------------------------------
+# recurrent decode
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class DecodeStep:
+    u: np.ndarray       # (batch, d_inner)
+    delta: np.ndarray   # (batch, d_inner)
+    z: np.ndarray       # (batch, d_inner)
+    B: np.ndarray       # (batch, d_state)
+    C: np.ndarray       # (batch, d_state)
+
+
+def make_decode_state(batch: int = DECODE["batch"], d_inner: int = DECODE["d_inner"],
+                      d_state: int = DECODE["d_state"], seed: int = DECODE["seed"]):
+    """Parameters (drawn exactly as the large-model prefill config) and h ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    p = draw_params(rng, d_inner, d_state, a_jitter=True, d_uniform=True)
+    h = rng.standard_normal((batch, d_inner, d_state), dtype=np.float32)
+    return p, h
+
+
+def make_decode_step(step: int, batch: int = DECODE["batch"], d_inner: int = DECODE["d_inner"],
+                     d_state: int = DECODE["d_state"], dtype: str = DECODE["dtype"],
+                     seed: int = DECODE["seed"]) -> DecodeStep:
+    """Fresh one-token inputs for one step, from ``default_rng([seed, step])``."""
+    rng = np.random.default_rng([seed, step])
+    bd = (batch, d_inner)
+    bn = (batch, d_state)
+    return DecodeStep(u=_normal(rng, bd, dtype), delta=_normal(rng, bd, dtype),
+                      z=_normal(rng, bd, dtype), B=_normal(rng, bn, dtype),
+                      C=_normal(rng, bn, dtype))

@@ -1,0 +1,312 @@
+"""Pins for the fp64 oracle: checks against facts fixed outside the oracle.
+
+Each ``pin_*`` takes a loaded oracle (``oracle.Oracle``) and raises
+``AssertionError`` if the oracle disagrees with a closed form, a brute-force
+evaluation written a different way, an invariant, or the hand-worked example.
+The same pins are run against deliberately broken builds of the oracle
+(``test_oracle_mutants.py``) to show that a plausible mistake is caught.
+
+The independent formulas used here:
+  * softplus via ``numpy.logaddexp(0, x)``; the sigmoid via 0.5 (1 + tanh(z/2));
+  * the unrolled (dual, attention-like) form of the scan, y_k = sum_{j<=k}
+    C_k (prod_{l=j+1..k} Abar_l) Bbar_j u_j ("Understanding Mamba",
+    aiattnstudio.link, sections 6.1 and 12), with the products of Abar written
+    as exp(A (S_k - S_j)), S = cumulative sum of Delta;
+  * the LTI convolution kernel K = (C Bbar, C Abar Bbar, C Abar^2 Bbar, ...)
+    (hnwysp.cn Mamba slides, section 2.1), with Abar^k = exp(k Delta A).
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------
+# independent reference pieces
+# ----------------------------------------------------------------------------
+
+def ref_softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def ref_silu(z):
+    return z * 0.5 * (1.0 + np.tanh(0.5 * np.asarray(z, dtype=np.float64)))
+
+
+def brute_force(u, delta, A, B, C, D=None, z=None, bias=None, h0=None):
+    """O(L^2) evaluation of the unrolled form, independent of the recurrence."""
+    batch, L, Dn = u.shape
+    N = A.shape[1]
+    y = np.zeros_like(u)
+    h_last = np.zeros((batch, Dn, N))
+    bias_v = np.zeros(Dn) if bias is None else bias
+    for b in range(batch):
+        for d in range(Dn):
+            dt = ref_softplus(delta[b, :, d] + bias_v[d])          # (L,)
+            S = np.cumsum(dt)                                     # S_t
+            a = A[d]                                              # (N,)
+            # G[t, j, n] = exp(A_n (S_t - S_j)) for j <= t
+            diff = S[:, None] - S[None, :]
+            mask = np.tril(np.ones((L, L), dtype=bool))
+            G = np.exp(np.where(mask, diff, 0.0)[:, :, None] * a[None, None, :])
+            G = G * mask[:, :, None]
+            src = dt[:, None] * B[b] * u[b, :, d][:, None]        # Bbar_j u_j (L, N)
+            h_all = np.einsum("tjn,jn->tn", G, src)                # state after step t
+            if h0 is not None:
+                h_all = h_all + np.exp(S[:, None] * a[None, :]) * h0[b, d][None, :]
+            yt = np.sum(C[b] * h_all, axis=1)
+            if D is not None:
+                yt = yt + D[d] * u[b, :, d]
+            if z is not None:
+                yt = yt * ref_silu(z[b, :, d])
+            y[b, :, d] = yt
+            h_last[b, d] = h_all[-1] if L > 0 else (0 if h0 is None else h0[b, d])
+    return y, h_last
+
+
+def random_case(rng, batch=2, L=37, Dn=6, N=5, gate=True, with_h0=True, with_D=True,
+                with_bias=True):
+    """Random small inputs; d_inner != d_state so a transposed index shows."""
+    u = rng.standard_normal((batch, L, Dn))
+    delta = rng.standard_normal((batch, L, Dn))
+    B = rng.standard_normal((batch, L, N))
+    C = rng.standard_normal((batch, L, N))
+    A = -rng.uniform(0.3, 3.0, size=(Dn, N))
+    D = rng.uniform(0.5, 1.5, size=Dn) if with_D else None
+    dt = np.exp(rng.uniform(math.log(1e-2), math.log(0.5), size=Dn))
+    bias = np.log(np.expm1(dt)) if with_bias else None
+    z = rng.standard_normal((batch, L, Dn)) if gate else None
+    h0 = rng.standard_normal((batch, Dn, N)) if with_h0 else None
+    return dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, bias=bias, h0=h0)
+
+
+def rel_err(x, r):
+    x = np.asarray(x, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    scale = max(float(np.sqrt(np.mean(r * r))) if r.size else 0.0, 1e-300)
+    return float(np.max(np.abs(x - r) / np.maximum(np.abs(r), scale))) if r.size else 0.0
+
+
+# ----------------------------------------------------------------------------
+# pins
+# ----------------------------------------------------------------------------
+
+def pin_worked_example(orc):
+    """Hand-derived three-step example (tests/golden/worked_example.json)."""
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        g = json.load(f)
+    inp = {k: np.array(v, dtype=np.float64) for k, v in g["inputs"].items()}
+    y, h_last = orc.scan(**inp, nthreads=1)
+    exp_y = np.array(g["expected"]["y"])
+    exp_h = np.array(g["expected"]["h_last"])
+    assert np.allclose(y, exp_y, rtol=g["rtol"], atol=0), (y, exp_y)
+    assert np.allclose(h_last, exp_h, rtol=g["rtol"], atol=1e-15), (h_last, exp_h)
+
+
+def pin_brute_force(orc):
+    """Recurrence == unrolled O(L^2) sum, with and without gate / h0 / D / bias."""
+    rng = np.random.default_rng(11)
+    for kw in (dict(), dict(gate=False), dict(with_h0=False), dict(with_D=False),
+               dict(with_bias=False), dict(batch=1, L=1, Dn=3, N=4)):
+        case = random_case(rng, **kw)
+        y, h = orc.scan(**case, nthreads=2)
+        yr, hr = brute_force(**case)
+        assert rel_err(y, yr) < 1e-11, (kw, rel_err(y, yr))
+        assert rel_err(h, hr) < 1e-11, (kw, rel_err(h, hr))
+
+
+def pin_lti_convolution(orc):
+    """Constant Delta, B, C: y = causal conv(K, u) + D u (+ decayed h0), then gate."""
+    rng = np.random.default_rng(12)
+    batch, L, Dn, N = 2, 96, 4, 6
+    A = -rng.uniform(0.05, 2.0, size=(Dn, N))
+    dt_const = rng.uniform(0.01, 0.4, size=Dn)
+    bias = rng.uniform(-1.0, 1.0, size=Dn)
+    # delta chosen so softplus(delta + bias) equals dt_const exactly in real arithmetic
+    delta_row = np.log(np.expm1(dt_const)) - bias
+    delta = np.broadcast_to(delta_row, (batch, L, Dn)).copy()
+    Bc = rng.standard_normal((batch, N))
+    Cc = rng.standard_normal((batch, N))
+    B = np.broadcast_to(Bc[:, None, :], (batch, L, N)).copy()
+    C = np.broadcast_to(Cc[:, None, :], (batch, L, N)).copy()
+    u = rng.standard_normal((batch, L, Dn))
+    D = rng.uniform(0.5, 1.5, size=Dn)
+    z = rng.standard_normal((batch, L, Dn))
+    h0 = rng.standard_normal((batch, Dn, N))
+    y, h_last = orc.scan(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, bias=bias, h0=h0)
+    k = np.arange(L)
+    for b in range(batch):
+        for d in range(Dn):
+            dl = ref_softplus(delta_row[d] + bias[d])
+            abar_pow = np.exp(np.outer(k, dl * A[d]))                    # (L, N): Abar^k
+            K = abar_pow @ (Cc[b] * dl * Bc[b])                           # K_k
+            conv = np.convolve(u[b, :, d], K)[:L]
+            free = np.exp(np.outer(k + 1, dl * A[d])) @ (Cc[b] * h0[b, d])  # C Abar^{t+1} h0
+            ref = (conv + free + D[d] * u[b, :, d]) * ref_silu(z[b, :, d])
+            assert rel_err(y[b, :, d], ref) < 1e-11, (b, d, rel_err(y[b, :, d], ref))
+            h_ref = (np.exp(np.outer(np.arange(L)[::-1], dl * A[d])) * (dl * Bc[b])[None, :]
+                     * u[b, :, d][:, None]).sum(0) + np.exp(L * dl * A[d]) * h0[b, d]
+            assert rel_err(h_last[b, d], h_ref) < 1e-11
+
+
+def pin_lti_fft_long(orc):
+    """The LTI identity at L = 4096, evaluated with an FFT convolution."""
+    rng = np.random.default_rng(13)
+    L, Dn, N = 4096, 2, 16
+    A = -(np.arange(N) + 1.0)[None, :].repeat(Dn, 0)
+    dt_const = np.array([0.003, 0.05])
+    delta = np.broadcast_to(np.log(np.expm1(dt_const)), (1, L, Dn)).copy()
+    Bc = rng.standard_normal(N)
+    Cc = rng.standard_normal(N)
+    B = np.broadcast_to(Bc, (1, L, N)).copy()
+    C = np.broadcast_to(Cc, (1, L, N)).copy()
+    u = rng.standard_normal((1, L, Dn))
+    y, _ = orc.scan(u=u, delta=delta, A=A, B=B, C=C)
+    nfft = 2 * L
+    for d in range(Dn):
+        dl = ref_softplus(np.log(np.expm1(dt_const[d])))
+        K = np.exp(np.outer(np.arange(L), dl * A[d])) @ (Cc * dl * Bc)
+        conv = np.fft.irfft(np.fft.rfft(u[0, :, d], nfft) * np.fft.rfft(K, nfft), nfft)[:L]
+        scale = np.sqrt(np.mean(conv ** 2))
+        assert np.max(np.abs(y[0, :, d] - conv)) < 1e-9 * max(scale, 1.0)
+
+
+def pin_zero_input_decay(orc):
+    """u = 0: y_t = sum_n C_t[n] exp(A_n S_t) h0[n] * silu(z_t); h_last = exp(A S_L) h0.
+    With h0 = 0 as well, y is exactly zero."""
+    rng = np.random.default_rng(14)
+    case = random_case(rng, L=50)
+    case["u"] = np.zeros_like(case["u"])
+    y, h_last = orc.scan(**case)
+    batch, L, Dn = y.shape
+    for b in range(batch):
+        for d in range(Dn):
+            S = np.cumsum(ref_softplus(case["delta"][b, :, d] + case["bias"][d]))
+            decay = np.exp(np.outer(S, case["A"][d]))                     # (L, N)
+            ref = (case["C"][b] * decay * case["h0"][b, d]).sum(1) * ref_silu(case["z"][b, :, d])
+            assert rel_err(y[b, :, d], ref) < 1e-12
+            assert rel_err(h_last[b, d], decay[-1] * case["h0"][b, d]) < 1e-12
+            # 0 < Abar <= 1 for A < 0, Delta > 0: each state decays monotonically
+            mag = np.abs(decay * case["h0"][b, d])
+            assert np.all(np.diff(mag, axis=0) <= 0)
+    case["h0"] = None
+    y0, h0_last = orc.scan(**case)
+    assert np.all(y0 == 0.0) and np.all(h0_last == 0.0)
+
+
+def pin_special_cases(orc):
+    """B = 0 or C = 0 with h0 = 0: y = D u silu(z).  z = 0: y = 0.  Tiny Delta: h_last ~ h0."""
+    rng = np.random.default_rng(15)
+    case = random_case(rng, with_h0=False)
+    expect = case["D"][None, None, :] * case["u"] * ref_silu(case["z"])
+    for key in ("B", "C"):
+        c = dict(case)
+        c[key] = np.zeros_like(case[key])
+        y, _ = orc.scan(**c)
+        assert rel_err(y, expect) < 1e-13, key
+    c = dict(case)
+    c["z"] = np.zeros_like(case["z"])
+    y, _ = orc.scan(**c)
+    assert np.all(y == 0.0)
+    # Delta -> 0: softplus(-60) ~ 8.8e-27, the state stays at h0
+    c = random_case(rng)
+    c["delta"] = np.full_like(c["delta"], -60.0)
+    c["bias"] = np.zeros_like(c["bias"])
+    _, h_last = orc.scan(**c)
+    assert np.allclose(h_last, c["h0"], rtol=1e-20, atol=1e-20)
+
+
+def pin_split_invariance(orc):
+    """scan(0..L) == scan(0..k) then scan(k..L, h0 = h_k), at several k."""
+    rng = np.random.default_rng(16)
+    case = random_case(rng, L=41)
+    y, h = orc.scan(**case)
+    for k in (0, 1, 17, 40, 41):
+        a = {key: (v[:, :k] if key in ("u", "delta", "B", "C", "z") and v is not None else v)
+             for key, v in case.items()}
+        ya, ha = orc.scan(**a)
+        b = {key: (v[:, k:] if key in ("u", "delta", "B", "C", "z") and v is not None else v)
+             for key, v in case.items()}
+        b["h0"] = ha
+        yb, hb = orc.scan(**b)
+        assert np.array_equal(np.concatenate([ya, yb], axis=1), y), k
+        assert np.array_equal(hb, h), k
+
+
+def pin_decode_equals_scan(orc):
+    """L chained single-token steps reproduce the scan exactly."""
+    rng = np.random.default_rng(17)
+    case = random_case(rng, L=23)
+    y, h_last = orc.scan(**case)
+    h = case["h0"]
+    for t in range(case["u"].shape[1]):
+        yt, h = orc.step(h, case["u"][:, t], case["delta"][:, t], case["A"], case["B"][:, t],
+                         case["C"][:, t], D=case["D"], z=case["z"][:, t], bias=case["bias"])
+        assert np.array_equal(yt, y[:, t]), t
+    assert np.array_equal(h, h_last)
+
+
+def pin_linearity_causality(orc):
+    """Linear in (u, h0) for fixed delta, B, C, z; y_{<k} ignores inputs at t >= k."""
+    rng = np.random.default_rng(18)
+    c1 = random_case(rng)
+    c2 = dict(c1)
+    c2["u"] = rng.standard_normal(c1["u"].shape)
+    c2["h0"] = rng.standard_normal(c1["h0"].shape)
+    al, be = 0.7, -1.3
+    c3 = dict(c1)
+    c3["u"] = al * c1["u"] + be * c2["u"]
+    c3["h0"] = al * c1["h0"] + be * c2["h0"]
+    y1, h1 = orc.scan(**c1)
+    y2, h2 = orc.scan(**c2)
+    y3, h3 = orc.scan(**c3)
+    assert rel_err(y3, al * y1 + be * y2) < 1e-11
+    assert rel_err(h3, al * h1 + be * h2) < 1e-11
+    k = 20
+    c4 = {key: (v.copy() if isinstance(v, np.ndarray) else v) for key, v in c1.items()}
+    for key in ("u", "delta", "B", "C", "z"):
+        c4[key][:, k:] = rng.standard_normal(c4[key][:, k:].shape)
+    y4, _ = orc.scan(**c4)
+    assert np.array_equal(y4[:, :k], y1[:, :k])
+    assert not np.array_equal(y4[:, k:], y1[:, k:])
+
+
+def pin_scalar_closed_forms(orc):
+    """softplus and silu against closed forms."""
+    sp, si = orc.softplus, orc.silu
+    assert abs(sp(0.0) - math.log(2.0)) < 1e-16
+    assert abs(sp(math.log(math.e - 1.0)) - 1.0) < 1e-15
+    for t in (1e-3, 0.1, 5.0):
+        assert abs(sp(math.log(math.expm1(t))) - t) < 1e-14 * max(1.0, t)
+    assert abs(sp(-50.0) / math.exp(-50.0) - 1.0) < 1e-14
+    assert abs(sp(50.0) - 50.0) < 1e-15
+    assert abs(sp(-3.0) - math.log1p(math.exp(-3.0))) < 1e-16
+    assert abs(sp(7.5) - ref_softplus(7.5)) < 1e-14
+    assert si(0.0) == 0.0
+    assert abs(si(math.log(3.0)) - 0.75 * math.log(3.0)) < 1e-15
+    assert abs(si(-math.log(3.0)) + 0.25 * math.log(3.0)) < 1e-15
+    for zz in (-8.0, -0.5, 0.3, 9.0):
+        assert abs(si(zz) - ref_silu(zz)) < 1e-14
+
+
+def pin_empty_and_threads(orc):
+    """L = 0 returns h0 as the final state; the thread count does not change bits."""
+    rng = np.random.default_rng(19)
+    case = random_case(rng, L=0)
+    y, h = orc.scan(**case)
+    assert y.shape == case["u"].shape and np.array_equal(h, case["h0"])
+    case = random_case(rng, L=9, Dn=7)
+    y1, h1 = orc.scan(**case, nthreads=1)
+    y3, h3 = orc.scan(**case, nthreads=3)
+    assert np.array_equal(y1, y3) and np.array_equal(h1, h3)
+
+
+PINS = [pin_worked_example, pin_brute_force, pin_lti_convolution, pin_lti_fft_long,
+        pin_zero_input_decay, pin_special_cases, pin_split_invariance, pin_decode_equals_scan,
+        pin_linearity_causality, pin_scalar_closed_forms, pin_empty_and_threads]

@@ -1,0 +1,79 @@
+"""Plant plausible mistakes in copies of the oracle and check that a pin fails.
+
+Each mutant is a textual edit of ``oracle/oracle_scan.c`` compiled into a
+temporary directory (CPU only).  The committed oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+# (name, [(original text, replacement), ...])
+MUTANTS = [
+    ("drop_D_term", [("yt += (j->D ? j->D[d] : 0.0) * ut;", "yt += 0.0 * ut;")]),
+    ("exp_sign", [("const double abar = exp(dt * j->A[d * N + n]);",
+                   "const double abar = exp(-dt * j->A[d * N + n]);")]),
+    ("exp_drops_delta", [("const double abar = exp(dt * j->A[d * N + n]);",
+                          "const double abar = exp(j->A[d * N + n]);")]),
+    ("A_transposed", [("const double abar = exp(dt * j->A[d * N + n]);",
+                       "const double abar = exp(dt * j->A[n * Dn + d]);")]),
+    ("bbar_drops_delta", [("const double bbar = dt * j->B[bln + n];",
+                           "const double bbar = j->B[bln + n];")]),
+    ("B_C_swapped", [("const double bbar = dt * j->B[bln + n];",
+                      "const double bbar = dt * j->C[bln + n];"),
+                     ("yt += j->C[bln + n] * h[n];", "yt += j->B[bln + n] * h[n];")]),
+    ("C_previous_step", [("yt += j->C[bln + n] * h[n];",
+                          "yt += j->C[(bln >= N ? bln - N : bln) + n] * h[n];")]),
+    ("readout_before_update", [
+        ("            /* discretise and advance the state */\n",
+         "            double ypre = 0.0;\n"
+         "            for (int64_t n = 0; n < N; ++n) ypre += j->C[bln + n] * h[n];\n"),
+        ("            double yt = 0.0;\n            for (int64_t n = 0; n < N; ++n)\n"
+         "                yt += j->C[bln + n] * h[n];\n",
+         "            double yt = ypre;\n")]),
+    ("no_softplus", [("const double dt = oracle_softplus(j->delta[bld] + (j->bias ? j->bias[d] : 0.0));",
+                      "const double dt = j->delta[bld] + (j->bias ? j->bias[d] : 0.0);")]),
+    ("bias_outside_softplus", [
+        ("const double dt = oracle_softplus(j->delta[bld] + (j->bias ? j->bias[d] : 0.0));",
+         "const double dt = oracle_softplus(j->delta[bld]) + (j->bias ? j->bias[d] : 0.0);")]),
+    ("softplus_drops_x", [("return x + log1p(exp(-x));", "return log1p(exp(-x));")]),
+    ("silu_sign", [("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));")]),
+    ("gate_is_sigmoid", [("yt *= oracle_silu(j->z[bld]);",
+                          "yt *= 1.0 / (1.0 + exp(-j->z[bld]));")]),
+    ("h0_ignored", [("h[n] = j->h0 ? j->h0[(b * Dn + d) * N + n] : 0.0;", "h[n] = 0.0;")]),
+    ("h_last_wrong_index", [("j->h_last[(b * Dn + d) * N + n] = h[n];",
+                             "j->h_last[(b * Dn + d) * N + n] = h[0];")]),
+    ("u_from_wrong_channel", [("const double ut = j->u[bld];",
+                               "const double ut = j->u[bld - d];")]),
+    ("step_drops_delta_in_bbar", [("const double bbar = dt * B[b * d_state + n];",
+                                   "const double bbar = B[b * d_state + n];")]),
+    ("step_no_gate", [("            if (z)\n                yt *= oracle_silu(z[bd]);\n", "")]),
+]
+
+
+def _build_mutant(tmp_path, name, edits):
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    for old, new in edits:
+        assert src.count(old) >= 1, f"{name}: pattern not found: {old!r}"
+        src = src.replace(old, new)
+    cpath = os.path.join(tmp_path, f"{name}.c")
+    with open(cpath, "w") as f:
+        f.write(src)
+    return oracle.Oracle(oracle.build(cpath, os.path.join(tmp_path, f"lib{name}.so")))
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, edits):
+    orc = _build_mutant(str(tmp_path), name, edits)
+    failed = []
+    for pin in PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+        except (ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
