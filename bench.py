@@ -1,0 +1,271 @@
+"""Selective-scan benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one mamba_scan_fwd over the large-model prefill workload (batch 8,
+L 4096, d_inner 5120, d_state 16, bf16 u/delta/z/B/C, fp32 A/D/bias, silu gate,
+final state returned): every row of the fused path -- input streaming, softplus
+step size, discretisation, recurrence, readout, D term, gate, output store and
+final state -- runs inside the timed region on inputs already resident in HBM.
+
+Prints ONE JSON line: throughput as GB/s of minimum algorithmic traffic (each
+input read once, each output written once), with channel-steps/s and the
+fraction of the 8 TB/s HBM peak; the roofline of the dominant kernel; the fp64
+oracle timed on the host cores on a bounded sample; and the other workloads
+(small prefill, long sequence, decode step) measured briefly.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "selective-scan GB/s + Gchan-steps/s (B·L·D) and % of MI355X HBM peak"
+# Plain-ALU roofline of the scan kernel: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz fp32 VALU
+# lane-instructions (no packed math), 4 instructions + one v_exp_f32 per state update.
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--only-main", action="store_true", help="alias of --no-extra --no-cpu-baseline")
+    return ap.parse_args()
+
+
+def to_dev(a, dev):
+    import numpy as np
+    import torch
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.to(dev)
+
+
+class ScanCase:
+    """A scan workload resident on the GPU with preallocated outputs and workspace."""
+
+    def __init__(self, cfg, dev, with_h_last=True, **opts):
+        import torch
+        import selective_state_space_72_amd as ms
+        from selective_state_space_72_amd import synth
+        self.cfg = cfg
+        self.opts = opts
+        inp = synth.make_scan_inputs(cfg)
+        p = inp.params
+        self.t = {k: to_dev(v, dev) for k, v in dict(u=inp.u, delta=inp.delta, z=inp.z, B=inp.B,
+                                                      C=inp.C, A=p.A, D=p.D, bias=p.bias,
+                                                      h0=inp.h0).items()}
+        act = self.t["u"].dtype
+        self.y = torch.empty((cfg.batch, cfg.seqlen, cfg.d_inner), dtype=act, device=dev)
+        self.h_last = (torch.empty((cfg.batch, cfg.d_inner, cfg.d_state), dtype=torch.float32,
+                                   device=dev) if with_h_last else None)
+        nws = ms.mamba_scan_fwd_workspace_size(cfg.batch, cfg.seqlen, cfg.d_inner,
+                                               cfg.d_state, **opts)
+        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        self.n_spans_auto = nws > 0
+        self.min_bytes = cfg.min_bytes(with_h_last=with_h_last)
+        self.inp = inp
+
+    def step(self):
+        import selective_state_space_72_amd as ms
+        t = self.t
+        ms.mamba_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                          delta_bias=t["bias"], h0=t["h0"], out=self.y,
+                          h_last_out=self.h_last, workspace=self.ws, **self.opts)
+
+
+def time_steps(fn, steps, warmup, flush=None):
+    """Event-timed steps on the current stream.  Returns (ms/step over the back-to-back
+    loop, median ms of single steps each preceded by a MALL flush, wall ms/step)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - w0) * 1e3 / steps
+    loop_ms = e0.elapsed_time(e1) / steps
+    singles = []
+    if flush is not None:
+        for _ in range(min(steps, 10)):
+            flush()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            singles.append(a.elapsed_time(b))
+    med = sorted(singles)[len(singles) // 2] if singles else None
+    return loop_ms, med, wall
+
+
+def make_flush(dev):
+    """Writing 1 GiB evicts the 256 MB Infinity Cache (MALL) between timed runs."""
+    import torch
+    buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def flush():
+        buf.fill_(1.0)
+    return flush
+
+
+def cpu_baseline(cfg):
+    """The fp64 oracle on the host cores, on the first two batch rows of the workload."""
+    import numpy as np
+    import oracle
+    from selective_state_space_72_amd import synth
+    inp = synth.make_scan_inputs(cfg, batch=2)
+    f = lambda a: synth.to_f64(a, cfg.dtype)  # noqa: E731
+    p = inp.params
+    args = (f(inp.u), f(inp.delta), p.A.astype(np.float64), f(inp.B), f(inp.C))
+    kw = dict(D=p.D.astype(np.float64), z=f(inp.z), bias=p.bias.astype(np.float64))
+    orc = oracle.load()
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    orc.scan(*args, **kw, nthreads=threads)
+    sec = time.perf_counter() - t0
+    chan_steps = 2 * cfg.seqlen * cfg.d_inner
+    bytes_per_cs = cfg.min_bytes() / cfg.chan_steps
+    return {"value": round(chan_steps / sec * bytes_per_cs / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"batch rows 0-1 of the workload ({chan_steps} channel-steps, "
+                      f"{chan_steps * cfg.d_state} state updates), {sec:.2f} s wall",
+            "gchan_steps_per_s": round(chan_steps / sec / 1e9, 5)}
+
+
+def extra_workloads(dev, flush, steps):
+    import numpy as np
+    import torch
+    import selective_state_space_72_amd as ms
+    from selective_state_space_72_amd import synth
+    out = {}
+    for name in ("c2", "c4"):
+        cfg = synth.CONFIGS[name]
+        case = ScanCase(cfg, dev)
+        loop_ms, med, _ = time_steps(case.step, max(3, steps // 2), 2, flush)
+        ms_used = med if med is not None else loop_ms
+        out[name] = {"workload": f"{cfg.desc}: batch {cfg.batch}, L {cfg.seqlen}, d_inner "
+                                 f"{cfg.d_inner}, d_state {cfg.d_state}, {cfg.dtype}",
+                     "ms": round(ms_used, 4), "ms_back_to_back": round(loop_ms, 4),
+                     "GB_s": round(case.min_bytes / (ms_used * 1e-3) / 1e9, 1),
+                     "gchan_steps_per_s": round(cfg.chan_steps / (ms_used * 1e-3) / 1e9, 2),
+                     "hbm_frac": round(case.min_bytes / (ms_used * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del case
+        torch.cuda.empty_cache()
+    # decode: one-token state update on the (256, 5120, 16) fp32 state
+    dc = synth.DECODE
+    p, h = synth.make_decode_state()
+    st = synth.make_decode_step(0)
+    t = {k: to_dev(v, dev) for k, v in dict(u=st.u, delta=st.delta, z=st.z, B=st.B, C=st.C,
+                                              A=p.A, D=p.D, bias=p.bias, h=h).items()}
+    y = torch.empty((dc["batch"], dc["d_inner"]), dtype=torch.bfloat16, device=dev)
+
+    def dstep():
+        ms.mamba_state_update(t["h"], t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"],
+                              z=t["z"], delta_bias=t["bias"], out=y)
+    loop_ms, med, _ = time_steps(dstep, 50, 5, flush)
+    bd = dc["batch"] * dc["d_inner"]
+    dbytes = bd * dc["d_state"] * 8 + bd * 2 * 4 + dc["batch"] * dc["d_state"] * 2 * 2 + \
+        dc["d_inner"] * (dc["d_state"] + 2) * 4
+    out["c5"] = {"workload": "decode step: state (256, 5120, 16) fp32, bf16 token inputs",
+                 "ms": round(med, 5), "ms_chained_cache_warm": round(loop_ms, 5),
+                 "GB_s": round(dbytes / (med * 1e-3) / 1e9, 1),
+                 "GB_s_chained_cache_warm": round(dbytes / (loop_ms * 1e-3) / 1e9, 1),
+                 "gchan_steps_per_s": round(bd / (med * 1e-3) / 1e9, 2),
+                 "hbm_frac": round(dbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def main():
+    args = parse()
+    if args.only_main:
+        args.no_extra = args.no_cpu_baseline = True
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the scan shards over channels with no communication: see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from selective_state_space_72_amd import build as hip_build
+    if not hip_build.is_built():
+        hip_build.build()
+    import selective_state_space_72_amd as ms
+    from selective_state_space_72_amd import synth
+    ms.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = synth.CONFIGS["c3"]
+    log(f"bench: generating {cfg.name} inputs")
+    case = ScanCase(cfg, dev)
+    flush = make_flush(dev)
+    log("bench: timing")
+    loop_ms, med_ms, wall_ms = time_steps(case.step, args.steps, args.warmup, flush)
+    ms_per_step = loop_ms
+    gbs = case.min_bytes / (ms_per_step * 1e-3) / 1e9
+    gcs = cfg.chan_steps / (ms_per_step * 1e-3) / 1e9
+    elems = cfg.chan_steps * cfg.d_state
+
+    # One kernel launch per step on this workload (no sequence split), so the
+    # kernel's average duration is the event-timed step time.
+    kernel_ms = ms_per_step
+    kbytes = case.min_bytes
+    roof = {"bound": "hbm", "achieved": round(kbytes / (kernel_ms * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kbytes / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None, "kernel": "scan_chunk_kernel<bf16, N=16, waves=8, chunk=16>",
+            "alu": {"valu_lane_ops_per_update": 5,
+                    "achieved_Tops": round(elems * 5 / (kernel_ms * 1e-3) / 1e12, 2),
+                    "peak_Tops": round(VALU_LANE_OPS / 1e12, 2)}}
+    line = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": "large-model prefill scan: batch 8, L 4096, d_inner 5120, "
+                                   "d_state 16, bf16 u/delta/z/B/C and y, fp32 A/D/bias and "
+                                   "state, silu gate, final state returned",
+                       "batch": cfg.batch, "seq_len": cfg.seqlen, "d_inner": cfg.d_inner,
+                       "d_state": cfg.d_state, "io_dtype": "bf16", "parallelism": "none"},
+            "gchan_steps_per_s": round(gcs, 2),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "min_bytes_per_step": case.min_bytes,
+            "ms_single_step_mall_flushed": round(med_ms, 4) if med_ms else None,
+            "wall_ms_per_step": round(wall_ms, 4),
+            "roofline": roof}
+    del case
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        log("bench: other workloads")
+        line["other_workloads"] = extra_workloads(dev, flush, args.steps)
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

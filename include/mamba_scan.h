@@ -1,0 +1,189 @@
+/*
+ * mamba_scan.h -- C ABI of libmambascan.so, the Mamba selective scan on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operation (selective scan).  For every batch row b, channel d and state index
+ * n, sequentially over t = 0..L-1:
+ *
+ *   Delta_t   = softplus(delta[b,t,d] + delta_bias[d])
+ *   h_t[n]    = exp(Delta_t * A[d,n]) * h_{t-1}[n] + Delta_t * B[b,t,n] * u[b,t,d]
+ *   y[b,t,d]  = (sum_n C[b,t,n] * h_t[n] + D[d] * u[b,t,d]) * silu(z[b,t,d])
+ *
+ * with h_{-1} = h0[b,d,:] and h_last[b,d,:] = h_{L-1}.  This is the selective
+ * state-space recurrence with input-dependent B, C and step size of
+ * "Understanding Mamba" (aiattnstudio.link, sections 2.3, 4.4 and 5.2: the
+ * selective_scan / _selective_scan functions and MambaBlock.forward's
+ * y * silu(z) gate), in the readout form of "State Space Models and Mamba"
+ * (metaphor-xennon.pages.dev, selective_scan: einsum 'bdn,bn->bd') with the
+ * skip term y = C x + D u of "Understanding Mamba" section 12 and the bias
+ * inside the softplus (metaphor-xennon, MambaBlock.forward).  The input term
+ * is the Euler form Delta*B that all of the pages' code uses.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers (HIP device memory visible to the stream's
+ *     device).  The caller owns every buffer; the library never allocates,
+ *     frees or retains memory, and keeps no state between calls.
+ *   - dtype applies to u, delta, z, B, C and y (F32: float; BF16: bfloat16
+ *     stored as 16-bit words).  A, D, delta_bias and all states (h0, h_last,
+ *     h) are always float32.  Internal arithmetic is float32; y is rounded to
+ *     dtype with round-to-nearest-even.
+ *   - Layouts are dense, row-major, last index fastest:
+ *       u, delta, z, y : (batch, seqlen, d_inner)       [decode: (batch, d_inner)]
+ *       B, C           : (batch, seqlen, d_state)       [decode: (batch, d_state)]
+ *       A              : (d_inner, d_state)
+ *       D, delta_bias  : (d_inner)
+ *       h0, h_last, h  : (batch, d_inner, d_state)
+ *   - Optional pointers (documented as nullable) mean: D NULL -> 0,
+ *     delta_bias NULL -> 0, z NULL -> no gate, h0 NULL -> zero initial state,
+ *     h_last NULL -> final state not returned.
+ *   - Pointers must be aligned to their element size (4 bytes for float, 2 for
+ *     bf16); otherwise MAMBA_ERR_MISALIGNED.
+ *   - All argument checks happen on the host before anything is launched; a
+ *     failing call has no effect.  A successful call only means the work was
+ *     enqueued on `stream` (a hipStream_t; NULL selects the null stream).  The
+ *     call is asynchronous: device faults surface at the caller's next
+ *     synchronisation.  MAMBA_ERR_HIP reports a failed launch.
+ *   - Entry points are reentrant and thread-safe.  Results are bitwise
+ *     deterministic for given inputs and options (no atomics).
+ *   - NaN and Inf inputs propagate as IEEE arithmetic does; they are not
+ *     checked.  Denormal intermediates may be flushed to zero.
+ */
+#ifndef MAMBA_SCAN_H
+#define MAMBA_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MAMBA_API __attribute__((visibility("default")))
+#else
+#define MAMBA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MAMBA_DTYPE_F32 = 0,
+    MAMBA_DTYPE_BF16 = 1
+} mamba_dtype_t;
+
+typedef enum {
+    MAMBA_OK = 0,
+    MAMBA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                       */
+    MAMBA_ERR_BAD_SHAPE = 2,    /* negative size, or sizes whose products overflow  */
+    MAMBA_ERR_BAD_DTYPE = 3,    /* dtype is not a mamba_dtype_t value               */
+    MAMBA_ERR_UNSUPPORTED = 4,  /* d_state not compiled in, or an unsupported option */
+    MAMBA_ERR_MISALIGNED = 5,   /* a pointer is not aligned to its element size     */
+    MAMBA_ERR_ALIASING = 6,     /* an output overlaps an input or another output    */
+    MAMBA_ERR_WORKSPACE = 7,    /* workspace missing or smaller than required       */
+    MAMBA_ERR_HIP = 8           /* a HIP runtime call or kernel launch failed       */
+} mamba_status_t;
+
+/* d_state values compiled into the library. */
+#define MAMBA_MAX_D_STATE 64
+
+/* Tuning and testing options for mamba_scan_fwd_ex.  Zero fields mean "auto".
+ *   chunk_len : time steps staged per block iteration (8, 16 or 32).
+ *   waves     : wavefronts per block; each handles d_state/waves state indices
+ *               of 64 channels (4 or 8).
+ *   n_spans   : the sequence is split into n_spans spans scanned in parallel
+ *               and joined by a carry pass (1..64; 1 = no split).
+ * Every supported setting gives the same result up to float32 rounding. */
+typedef struct {
+    int32_t chunk_len;
+    int32_t waves;
+    int32_t n_spans;
+    int32_t reserved;
+} mamba_scan_opts_t;
+
+/* Returns 1 if d_state is supported by this build, else 0. */
+MAMBA_API int32_t mamba_d_state_supported(int64_t d_state);
+
+/*
+ * Number of bytes of device workspace mamba_scan_fwd needs for these sizes
+ * (auto options) -- 0 means no workspace is needed and NULL may be passed.
+ * Depends on the current device's compute-unit count.  Returns (size_t)-1
+ * for invalid sizes.
+ */
+MAMBA_API size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                     int64_t d_state);
+
+/* The same for explicit options (opts may be NULL for auto). */
+MAMBA_API size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                        int64_t d_state, const mamba_scan_opts_t *opts);
+
+/*
+ * Selective scan forward (the operation above) over a whole sequence.
+ *
+ *   u, delta   (batch, seqlen, d_inner) dtype        required
+ *   A          (d_inner, d_state) float32            required (normally A < 0)
+ *   B, C       (batch, seqlen, d_state) dtype        required
+ *   D          (d_inner) float32                     nullable
+ *   z          (batch, seqlen, d_inner) dtype        nullable (gate)
+ *   delta_bias (d_inner) float32                     nullable
+ *   h0         (batch, d_inner, d_state) float32     nullable
+ *   y          (batch, seqlen, d_inner) dtype        output, required if seqlen > 0
+ *   h_last     (batch, d_inner, d_state) float32     output, nullable
+ *   workspace  device memory of workspace_bytes      see mamba_scan_fwd_workspace_size
+ *
+ * Sizes: batch, seqlen, d_inner >= 0; d_state must be supported (see
+ * mamba_d_state_supported).  With seqlen == 0 only h_last is written (h0, or
+ * zeros); u, delta, B, C, z and y may then be NULL.  With batch == 0 or
+ * d_inner == 0 nothing is done.
+ * Aliasing: y must not overlap any other argument.  h_last may be exactly h0
+ * (in-place continuation of a state) but must not otherwise overlap anything.
+ * The workspace must not overlap any argument.
+ */
+MAMBA_API mamba_status_t mamba_scan_fwd(const void *u, const void *delta, const float *A, const void *B,
+                              const void *C, const float *D, const void *z,
+                              const float *delta_bias, const float *h0, void *y, float *h_last,
+                              int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                              mamba_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* mamba_scan_fwd with explicit tuning options (opts NULL = auto).  Used by the
+ * tests to check that the result does not depend on the internal split. */
+MAMBA_API mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *A,
+                                 const void *B, const void *C, const float *D, const void *z,
+                                 const float *delta_bias, const float *h0, void *y,
+                                 float *h_last, int64_t batch, int64_t seqlen, int64_t d_inner,
+                                 int64_t d_state, mamba_dtype_t dtype, void *workspace,
+                                 size_t workspace_bytes, const mamba_scan_opts_t *opts,
+                                 void *stream);
+
+/*
+ * One recurrent decode step (a single token) on a persistent state: the loop
+ * body of the operation above with seqlen = 1 and h read and written in place,
+ * as in the token-by-token decoder "output, h = ssm(token, h)" of "State Space
+ * Models and Mamba" (metaphor-xennon.pages.dev, MambaDecoder), whose memory is
+ * the constant-size state.
+ *
+ *   h          (batch, d_inner, d_state) float32     in/out, required
+ *   u, delta   (batch, d_inner) dtype                required
+ *   A          (d_inner, d_state) float32            required
+ *   B, C       (batch, d_state) dtype                required
+ *   D          (d_inner) float32                     nullable
+ *   z          (batch, d_inner) dtype                nullable (gate)
+ *   delta_bias (d_inner) float32                     nullable
+ *   y          (batch, d_inner) dtype                output, required
+ *
+ * Alignment: h and A must be 16-byte aligned (each lane moves 4 state values
+ * at once); the other pointers as for every entry point.
+ * Aliasing: y and h must not overlap each other or any input.
+ */
+MAMBA_API mamba_status_t mamba_state_update(float *h, const void *u, const void *delta, const float *A,
+                                  const void *B, const void *C, const float *D, const void *z,
+                                  const float *delta_bias, void *y, int64_t batch,
+                                  int64_t d_inner, int64_t d_state, mamba_dtype_t dtype,
+                                  void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+MAMBA_API const char *mamba_status_string(mamba_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SCAN_H */

@@ -1,0 +1,227 @@
+"""MI355X (gfx950) Mamba selective scan: Python binding of libmambascan.so.
+
+The binding only marshals arguments: torch tensors are checked for device, dtype,
+shape and contiguity, their device pointers and the current HIP stream are passed
+to the C entry points declared in ``include/mamba_scan.h``, and the workspace is
+allocated with torch.  Every step of the computation runs in the HIP kernels;
+there is no CPU or PyTorch fallback -- if the library is missing, the call fails.
+
+    y, h_last = mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                               h0=None, return_last_state=False)
+    y = mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmambascan.so")
+
+MAMBA_DTYPE_F32 = 0
+MAMBA_DTYPE_BF16 = 1
+
+STATUS = {
+    0: "MAMBA_OK", 1: "MAMBA_ERR_NULL_ARG", 2: "MAMBA_ERR_BAD_SHAPE", 3: "MAMBA_ERR_BAD_DTYPE",
+    4: "MAMBA_ERR_UNSUPPORTED", 5: "MAMBA_ERR_MISALIGNED", 6: "MAMBA_ERR_ALIASING",
+    7: "MAMBA_ERR_WORKSPACE", 8: "MAMBA_ERR_HIP",
+}
+
+# Every symbol include/mamba_scan.h declares.
+EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
+           "mamba_scan_fwd_workspace_size_ex", "mamba_scan_fwd", "mamba_scan_fwd_ex",
+           "mamba_state_update", "mamba_status_string")
+
+
+class MambaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class ScanOpts(ctypes.Structure):
+    _fields_ = [("chunk_len", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("n_spans", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_lib = None
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libmambascan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m selective_state_space_72_amd.build`"
+            " (there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    lib.mamba_d_state_supported.restype = ctypes.c_int32
+    lib.mamba_d_state_supported.argtypes = [_i64]
+    lib.mamba_scan_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.mamba_scan_fwd_workspace_size.argtypes = [_i64] * 4
+    lib.mamba_scan_fwd_workspace_size_ex.restype = ctypes.c_size_t
+    lib.mamba_scan_fwd_workspace_size_ex.argtypes = [_i64] * 4 + [ctypes.POINTER(ScanOpts)]
+    lib.mamba_scan_fwd.restype = ctypes.c_int
+    lib.mamba_scan_fwd.argtypes = [_vp] * 11 + [_i64] * 4 + [ctypes.c_int, _vp, ctypes.c_size_t,
+                                                              _vp]
+    lib.mamba_scan_fwd_ex.restype = ctypes.c_int
+    lib.mamba_scan_fwd_ex.argtypes = ([_vp] * 11 + [_i64] * 4 +
+                                      [ctypes.c_int, _vp, ctypes.c_size_t,
+                                       ctypes.POINTER(ScanOpts), _vp])
+    lib.mamba_state_update.restype = ctypes.c_int
+    lib.mamba_state_update.argtypes = [_vp] * 10 + [_i64] * 3 + [ctypes.c_int, _vp]
+    lib.mamba_status_string.restype = ctypes.c_char_p
+    lib.mamba_status_string.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    if _lib is not None:
+        return _lib.mamba_status_string(int(status)).decode()
+    return STATUS.get(int(status), f"status {status}")
+
+
+# ----------------------------------------------------------------------------
+# argument marshalling
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return MAMBA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return MAMBA_DTYPE_F32
+    raise TypeError(f"activations must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t, name, shape=None, dtype=None, device=None) -> Optional[int]:
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _opts(chunk_len=0, waves=0, n_spans=0):
+    return ScanOpts(int(chunk_len), int(waves), int(n_spans), 0)
+
+
+def mamba_scan_fwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state: int,
+                                  chunk_len: int = 0, waves: int = 0, n_spans: int = 0) -> int:
+    lib = load_library()
+    o = _opts(chunk_len, waves, n_spans)
+    n = lib.mamba_scan_fwd_workspace_size_ex(batch, seqlen, d_inner, d_state, ctypes.byref(o))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes or options for mamba_scan_fwd")
+    return int(n)
+
+
+def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
+                   return_last_state: bool = False, *, out=None, h_last_out=None,
+                   chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
+                   workspace=None) -> Tuple:
+    """Selective scan over (batch, seqlen, d_inner); see include/mamba_scan.h.
+
+    Returns (y, h_last) -- h_last is None unless return_last_state (or h_last_out).
+    """
+    torch = _torch()
+    lib = load_library()
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, seqlen, d_inner)")
+    batch, seqlen, d_inner = u.shape
+    if A.dim() != 2 or A.shape[0] != d_inner:
+        raise ValueError("A must be (d_inner, d_state)")
+    d_state = A.shape[1]
+    dev = u.device
+    act = u.dtype
+    code = _dtype_code(u)
+    f32 = torch.float32
+    p_u = _ptr(u, "u", (batch, seqlen, d_inner), act, dev)
+    p_delta = _ptr(delta, "delta", (batch, seqlen, d_inner), act, dev)
+    p_A = _ptr(A, "A", (d_inner, d_state), f32, dev)
+    p_B = _ptr(B, "B", (batch, seqlen, d_state), act, dev)
+    p_C = _ptr(C, "C", (batch, seqlen, d_state), act, dev)
+    p_D = _ptr(D, "D", (d_inner,), f32, dev)
+    p_z = _ptr(z, "z", (batch, seqlen, d_inner), act, dev)
+    p_bias = _ptr(delta_bias, "delta_bias", (d_inner,), f32, dev)
+    p_h0 = _ptr(h0, "h0", (batch, d_inner, d_state), f32, dev)
+    y = out if out is not None else torch.empty((batch, seqlen, d_inner), dtype=act, device=dev)
+    p_y = _ptr(y, "out", (batch, seqlen, d_inner), act, dev)
+    h_last = h_last_out
+    if h_last is None and return_last_state:
+        h_last = torch.empty((batch, d_inner, d_state), dtype=f32, device=dev)
+    p_hl = _ptr(h_last, "h_last_out", (batch, d_inner, d_state), f32, dev)
+
+    opts = _opts(chunk_len, waves, n_spans)
+    need = lib.mamba_scan_fwd_workspace_size_ex(batch, seqlen, d_inner, d_state,
+                                                ctypes.byref(opts))
+    if need == ctypes.c_size_t(-1).value:
+        raise MambaError(4, "mamba_scan_fwd_workspace_size")
+    ws = workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    p_ws = ws.data_ptr() if ws is not None and need > 0 else None
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = lib.mamba_scan_fwd_ex(p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_y, p_hl,
+                               batch, seqlen, d_inner, d_state, code, p_ws, ws_bytes,
+                               ctypes.byref(opts), _stream(dev))
+    if st != 0:
+        raise MambaError(st, "mamba_scan_fwd")
+    return y, h_last
+
+
+def mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None):
+    """One decode step; h (batch, d_inner, d_state) fp32 is updated in place.  Returns y."""
+    torch = _torch()
+    lib = load_library()
+    if u.dim() != 2:
+        raise ValueError("u must be (batch, d_inner)")
+    batch, d_inner = u.shape
+    d_state = A.shape[1]
+    dev = u.device
+    act = u.dtype
+    code = _dtype_code(u)
+    f32 = torch.float32
+    p_h = _ptr(h, "h", (batch, d_inner, d_state), f32, dev)
+    p_u = _ptr(u, "u", (batch, d_inner), act, dev)
+    p_delta = _ptr(delta, "delta", (batch, d_inner), act, dev)
+    p_A = _ptr(A, "A", (d_inner, d_state), f32, dev)
+    p_B = _ptr(B, "B", (batch, d_state), act, dev)
+    p_C = _ptr(C, "C", (batch, d_state), act, dev)
+    p_D = _ptr(D, "D", (d_inner,), f32, dev)
+    p_z = _ptr(z, "z", (batch, d_inner), act, dev)
+    p_bias = _ptr(delta_bias, "delta_bias", (d_inner,), f32, dev)
+    y = out if out is not None else torch.empty((batch, d_inner), dtype=act, device=dev)
+    p_y = _ptr(y, "out", (batch, d_inner), act, dev)
+    st = lib.mamba_state_update(p_h, p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_y,
+                                batch, d_inner, d_state, code, _stream(dev))
+    if st != 0:
+        raise MambaError(st, "mamba_state_update")
+    return y

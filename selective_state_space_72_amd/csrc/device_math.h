@@ -1,0 +1,55 @@
+// Device-side scalar helpers for the scan kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mambascan {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// --- storage formats --------------------------------------------------------
+
+__device__ __forceinline__ float load_val(const float *p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_val(const uint16_t *p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16); // bf16 -> f32 is exact
+}
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(uint16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+__device__ __forceinline__ void store_val(float *p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_val(uint16_t *p, int64_t i, float v) {
+    // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+    p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+
+// --- transcendental pieces ----------------------------------------------------
+// v_exp_f32 / v_log_f32 compute 2^x and log2(x) directly.
+
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(v) = log(1 + e^v) = max(v, 0) + log1p(e^-|v|).
+// log1p(e) for e in (0, 1] is evaluated as log(s) - ((s - 1) - e) with
+// s = fl(1 + e): (s - 1) - e is exactly the rounding error of 1 + e, and the
+// first-order correction log(1 + e) = log(s) - ((s - 1) - e) / s + O(err^2)
+// keeps the relative error near one ulp even when 1 + e rounds to 1 (where the
+// plain log(1 + e) would return 0 instead of about e).
+__device__ __forceinline__ float softplus_f(float v) {
+    const float e = hw_exp2(-__builtin_fabsf(v) * kLog2e);
+    const float s = 1.0f + e;
+    const float err = (s - 1.0f) - e;
+    const float l = __builtin_fmaf(hw_log2(s), kLn2, -err);
+    return __builtin_fmaxf(v, 0.0f) + l;
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z); e^-z = +inf gives -0 as the limit.
+__device__ __forceinline__ float silu_f(float z) {
+    return z * hw_rcp(1.0f + hw_exp2(-z * kLog2e));
+}
+
+} // namespace mambascan

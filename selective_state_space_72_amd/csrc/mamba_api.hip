@@ -1,0 +1,368 @@
+// C ABI of libmambascan: argument validation, launch planning and dispatch.
+// Declarations and the contract live in include/mamba_scan.h.
+#include "mamba_scan.h"
+#include "scan_common.h"
+
+#include <limits.h>
+#include <stdint.h>
+
+using namespace mambascan;
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi; // [lo, hi)
+};
+
+Range range_of(const void *p, int64_t bytes)
+{
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, p && bytes > 0 ? lo + static_cast<uintptr_t>(bytes) : lo};
+}
+
+bool overlaps(Range a, Range b)
+{
+    if (a.hi == a.lo || b.hi == b.lo)
+        return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
+
+bool d_state_ok(int64_t n) { return n == 4 || n == 8 || n == 16 || n == 32 || n == 64; }
+
+int cu_count()
+{
+    int dev = 0, cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cu <= 0) {
+        (void)hipGetLastError(); // do not leave a sticky error behind
+        return 256;
+    }
+    return cu;
+}
+
+struct Plan {
+    int waves, chunk, n_spans;
+    int64_t span_len;
+};
+
+// Launch plan.  Channel tiles of 64 lanes x `waves` waves are the unit of parallel work;
+// when a single span cannot give every SIMD a few waves, the sequence is split into spans
+// (at most 64, each at least 256 steps) joined by the carry pass.
+mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                         const mamba_scan_opts_t *opts, Plan *plan)
+{
+    Plan p{};
+    p.waves = opts && opts->waves ? opts->waves : default_waves(d_state);
+    p.chunk = opts && opts->chunk_len ? opts->chunk_len : default_chunk(d_state, p.waves);
+    if (!scan_variant_supported(d_state, p.waves, p.chunk))
+        return MAMBA_ERR_UNSUPPORTED;
+    int spans = 1;
+    if (opts && opts->n_spans) {
+        if (opts->n_spans < 1 || opts->n_spans > 64)
+            return MAMBA_ERR_UNSUPPORTED;
+        spans = opts->n_spans;
+    } else {
+        const int64_t tiles = batch * ((d_inner + 63) / 64);
+        const int64_t waves_per_span = tiles * p.waves;
+        const int64_t want = (int64_t)cu_count() * 4 /*SIMDs*/ * 4 /*waves each*/;
+        if (waves_per_span * 2 < want) {
+            int64_t s = 1;
+            while (s * waves_per_span < want && s < 64)
+                s <<= 1;
+            const int64_t by_len = seqlen / 256;
+            if (s > by_len)
+                s = by_len > 1 ? by_len : 1;
+            spans = (int)s;
+        }
+    }
+    if (seqlen <= 0)
+        spans = 1;
+    // span length: a multiple of the chunk so that only the last span has a partial chunk
+    int64_t len = (seqlen + spans - 1) / spans;
+    len = (len + p.chunk - 1) / p.chunk * p.chunk;
+    if (len < p.chunk)
+        len = p.chunk;
+    spans = (int)((seqlen + len - 1) / len);
+    if (spans < 1)
+        spans = 1;
+    p.n_spans = spans;
+    p.span_len = len;
+    *plan = p;
+    return MAMBA_OK;
+}
+
+size_t workspace_bytes_for(int64_t batch, int64_t d_inner, int64_t d_state, const Plan &p)
+{
+    if (p.n_spans <= 1)
+        return 0;
+    // decay [c][S], hloc [c][S], h_in [S][c]
+    return (size_t)3 * (size_t)p.n_spans * (size_t)(batch * d_inner * d_state) * sizeof(float);
+}
+
+mamba_status_t hip_status(hipError_t e) { return e == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP; }
+
+} // namespace
+
+extern "C" {
+
+const char *mamba_status_string(mamba_status_t s)
+{
+    switch (s) {
+    case MAMBA_OK: return "MAMBA_OK";
+    case MAMBA_ERR_NULL_ARG: return "MAMBA_ERR_NULL_ARG: a required pointer is NULL";
+    case MAMBA_ERR_BAD_SHAPE: return "MAMBA_ERR_BAD_SHAPE: negative or overflowing size";
+    case MAMBA_ERR_BAD_DTYPE: return "MAMBA_ERR_BAD_DTYPE: unknown dtype";
+    case MAMBA_ERR_UNSUPPORTED: return "MAMBA_ERR_UNSUPPORTED: d_state or option not supported";
+    case MAMBA_ERR_MISALIGNED: return "MAMBA_ERR_MISALIGNED: pointer not aligned";
+    case MAMBA_ERR_ALIASING: return "MAMBA_ERR_ALIASING: an output overlaps another argument";
+    case MAMBA_ERR_WORKSPACE: return "MAMBA_ERR_WORKSPACE: workspace missing or too small";
+    case MAMBA_ERR_HIP: return "MAMBA_ERR_HIP: HIP launch or runtime error";
+    }
+    return "MAMBA_ERR_UNKNOWN";
+}
+
+int32_t mamba_d_state_supported(int64_t d_state) { return d_state_ok(d_state) ? 1 : 0; }
+
+size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                        int64_t d_state, const mamba_scan_opts_t *opts)
+{
+    int64_t tmp;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 ||
+        !mul_ok(batch, d_inner, &tmp) || !mul_ok(tmp, d_state, &tmp) || !d_state_ok(d_state))
+        return (size_t)-1;
+    Plan p;
+    if (make_plan(batch, seqlen, d_inner, d_state, opts, &p) != MAMBA_OK)
+        return (size_t)-1;
+    return workspace_bytes_for(batch, d_inner, d_state, p);
+}
+
+size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                     int64_t d_state)
+{
+    return mamba_scan_fwd_workspace_size_ex(batch, seqlen, d_inner, d_state, nullptr);
+}
+
+mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *A,
+                                 const void *B, const void *C, const float *D, const void *z,
+                                 const float *delta_bias, const float *h0, void *y,
+                                 float *h_last, int64_t batch, int64_t seqlen, int64_t d_inner,
+                                 int64_t d_state, mamba_dtype_t dtype, void *workspace,
+                                 size_t workspace_bytes, const mamba_scan_opts_t *opts,
+                                 void *stream)
+{
+    // ---- sizes and dtype ----
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
+        return MAMBA_ERR_BAD_DTYPE;
+    if (!d_state_ok(d_state))
+        return MAMBA_ERR_UNSUPPORTED;
+    const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
+    int64_t bld, bln, bdn, dn, t;
+    if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, d_inner, &bld) || !mul_ok(bld, es, &t) ||
+        !mul_ok(batch, seqlen, &t) || !mul_ok(t, d_state, &bln) || !mul_ok(bln, es, &t) ||
+        !mul_ok(batch, d_inner, &t) || !mul_ok(t, d_state, &bdn) || !mul_ok(bdn, 4, &t) ||
+        !mul_ok(d_inner, d_state, &dn) || !mul_ok(dn, 4, &t) || d_inner > INT32_MAX ||
+        batch > INT32_MAX)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (batch == 0 || d_inner == 0)
+        return MAMBA_OK;
+
+    // ---- required pointers ----
+    const bool has_seq = seqlen > 0;
+    if (!A || (has_seq && (!u || !delta || !B || !C || !y)))
+        return MAMBA_ERR_NULL_ARG;
+
+    // ---- alignment ----
+    const void *elem_ptrs[] = {u, delta, B, C, z, y};
+    for (const void *p : elem_ptrs)
+        if (p && !aligned(p, (size_t)es))
+            return MAMBA_ERR_MISALIGNED;
+    const void *f32_ptrs[] = {A, D, delta_bias, h0, h_last};
+    for (const void *p : f32_ptrs)
+        if (p && !aligned(p, 4))
+            return MAMBA_ERR_MISALIGNED;
+
+    // ---- plan and workspace ----
+    Plan plan;
+    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, d_state, opts, &plan);
+    if (ps != MAMBA_OK)
+        return ps;
+    const size_t need = workspace_bytes_for(batch, d_inner, d_state, plan);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return MAMBA_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 4))
+        return MAMBA_ERR_MISALIGNED;
+
+    // ---- aliasing ----
+    const Range r_in[] = {range_of(u, bld * es),       range_of(delta, bld * es),
+                          range_of(z, bld * es),       range_of(B, bln * es),
+                          range_of(C, bln * es),       range_of(A, dn * 4),
+                          range_of(D, d_inner * 4),    range_of(delta_bias, d_inner * 4)};
+    const Range r_h0 = range_of(h0, bdn * 4);
+    const Range r_y = range_of(has_seq ? y : nullptr, bld * es);
+    const Range r_hl = range_of(h_last, bdn * 4);
+    const Range r_ws = range_of(need > 0 ? workspace : nullptr, (int64_t)need);
+    for (const Range &r : r_in) {
+        if (overlaps(r_y, r) || overlaps(r_hl, r) || overlaps(r_ws, r))
+            return MAMBA_ERR_ALIASING;
+    }
+    if (overlaps(r_y, r_h0) || overlaps(r_y, r_hl) || overlaps(r_y, r_ws) ||
+        overlaps(r_ws, r_h0) || overlaps(r_ws, r_hl))
+        return MAMBA_ERR_ALIASING;
+    if (overlaps(r_hl, r_h0) && (const void *)h_last != (const void *)h0)
+        return MAMBA_ERR_ALIASING;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+    // ---- empty sequence: the final state is the initial state ----
+    if (!has_seq) {
+        if (h_last)
+            return hip_status(launch_copy_state(h_last, h0, bdn, st));
+        return MAMBA_OK;
+    }
+
+    ScanLaunch L{};
+    L.u = u;
+    L.delta = delta;
+    L.z = z;
+    L.B = B;
+    L.C = C;
+    L.A = A;
+    L.D = D;
+    L.bias = delta_bias;
+    L.y = y;
+    L.h_last = h_last;
+    L.batch = batch;
+    L.L = seqlen;
+    L.d_inner = d_inner;
+    L.d_state = d_state;
+    L.span_len = plan.span_len;
+    L.n_spans = plan.n_spans;
+    L.waves = plan.waves;
+    L.chunk = plan.chunk;
+    L.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+
+    if (plan.n_spans == 1) {
+        L.h_init = h0;
+        L.h_init_span_stride = 0;
+        L.first_span = 0;
+        L.launch_spans = 1;
+        return hip_status(launch_scan_full(L, st));
+    }
+
+    // ---- split sequence: span summaries, carry pass, full rescan ----
+    const int64_t S = plan.n_spans;
+    float *ws = static_cast<float *>(workspace);
+    float *ws_decay = ws;
+    float *ws_hloc = ws + S * bdn;
+    float *ws_hin = ws + 2 * S * bdn;
+
+    ScanLaunch E = L;
+    E.h_init = nullptr;
+    E.h_init_span_stride = 0;
+    E.ws_decay = ws_decay;
+    E.ws_hloc = ws_hloc;
+    E.first_span = 0;
+    E.launch_spans = (int32_t)(S - 1);
+    hipError_t e = launch_scan_end(E, st);
+    if (e != hipSuccess)
+        return MAMBA_ERR_HIP;
+
+    CarryLaunch K{};
+    K.ws_decay = ws_decay;
+    K.ws_hloc = ws_hloc;
+    K.h0 = h0;
+    K.h_in = ws_hin;
+    K.columns = bdn;
+    K.n_spans = (int32_t)S;
+    e = launch_carry(K, st);
+    if (e != hipSuccess)
+        return MAMBA_ERR_HIP;
+
+    L.h_init = ws_hin;
+    L.h_init_span_stride = bdn;
+    L.first_span = 0;
+    L.launch_spans = (int32_t)S;
+    return hip_status(launch_scan_full(L, st));
+}
+
+mamba_status_t mamba_scan_fwd(const void *u, const void *delta, const float *A, const void *B,
+                              const void *C, const float *D, const void *z,
+                              const float *delta_bias, const float *h0, void *y, float *h_last,
+                              int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                              mamba_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                              void *stream)
+{
+    return mamba_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, y, h_last, batch, seqlen,
+                             d_inner, d_state, dtype, workspace, workspace_bytes, nullptr,
+                             stream);
+}
+
+mamba_status_t mamba_state_update(float *h, const void *u, const void *delta, const float *A,
+                                  const void *B, const void *C, const float *D, const void *z,
+                                  const float *delta_bias, void *y, int64_t batch,
+                                  int64_t d_inner, int64_t d_state, mamba_dtype_t dtype,
+                                  void *stream)
+{
+    if (batch < 0 || d_inner < 0 || d_state <= 0)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
+        return MAMBA_ERR_BAD_DTYPE;
+    if (!d_state_ok(d_state))
+        return MAMBA_ERR_UNSUPPORTED;
+    const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
+    int64_t bd, bn, bdn, dn, t;
+    if (!mul_ok(batch, d_inner, &bd) || !mul_ok(bd, es, &t) || !mul_ok(batch, d_state, &bn) ||
+        !mul_ok(bd, d_state, &bdn) || !mul_ok(bdn, 4, &t) || !mul_ok(d_inner, d_state, &dn) ||
+        !mul_ok(dn, 4, &t) || d_inner > INT32_MAX / 64)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (batch == 0 || d_inner == 0)
+        return MAMBA_OK;
+    if (!h || !u || !delta || !A || !B || !C || !y)
+        return MAMBA_ERR_NULL_ARG;
+
+    const void *elem_ptrs[] = {u, delta, B, C, z, y};
+    for (const void *p : elem_ptrs)
+        if (p && !aligned(p, (size_t)es))
+            return MAMBA_ERR_MISALIGNED;
+    if (!aligned(h, 16) || !aligned(A, 16) || (D && !aligned(D, 4)) ||
+        (delta_bias && !aligned(delta_bias, 4)))
+        return MAMBA_ERR_MISALIGNED;
+
+    const Range r_in[] = {range_of(u, bd * es),       range_of(delta, bd * es),
+                          range_of(z, bd * es),       range_of(B, bn * es),
+                          range_of(C, bn * es),       range_of(A, dn * 4),
+                          range_of(D, d_inner * 4),   range_of(delta_bias, d_inner * 4)};
+    const Range r_h = range_of(h, bdn * 4);
+    const Range r_y = range_of(y, bd * es);
+    if (overlaps(r_h, r_y))
+        return MAMBA_ERR_ALIASING;
+    for (const Range &r : r_in)
+        if (overlaps(r_h, r) || overlaps(r_y, r))
+            return MAMBA_ERR_ALIASING;
+
+    StepLaunch S{};
+    S.h = h;
+    S.u = u;
+    S.delta = delta;
+    S.z = z;
+    S.B = B;
+    S.C = C;
+    S.A = A;
+    S.D = D;
+    S.bias = delta_bias;
+    S.y = y;
+    S.batch = batch;
+    S.d_inner = d_inner;
+    S.d_state = d_state;
+    S.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+    return hip_status(launch_state_update(S, reinterpret_cast<hipStream_t>(stream)));
+}
+
+} // extern "C"

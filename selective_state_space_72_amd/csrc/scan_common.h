@@ -1,0 +1,62 @@
+// Internal declarations shared by the HIP translation units of libmambascan.
+// Not part of the public ABI (see include/mamba_scan.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mambascan {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+// One launch of the chunked scan kernel.  h_init points at the initial state of
+// span 0 (h0) or at the per-span carry-in states written by the carry pass.
+struct ScanLaunch {
+    const void *u, *delta, *z, *B, *C;
+    const float *A, *D, *bias;
+    const float *h_init;        // nullable: zero initial state
+    int64_t h_init_span_stride; // floats between consecutive spans' states (0: span 0 only)
+    void *y;                    // FULL mode output
+    float *h_last;              // FULL mode final state (nullable)
+    float *ws_decay, *ws_hloc;  // END mode outputs, layout [(b*D + d)*N + n][span]
+    int64_t batch, L, d_inner, d_state;
+    int64_t span_len;
+    int32_t n_spans;
+    int32_t first_span;         // spans [first_span, first_span + launch_spans) are launched
+    int32_t launch_spans;
+    int32_t waves, chunk;
+    DType dtype;
+};
+
+// The carry pass joining span end states: for every state column c = (b, d, n)
+// h_in[s][c] = state entering span s (s = 0 .. n_spans-1).
+struct CarryLaunch {
+    const float *ws_decay, *ws_hloc; // [c][span], spans 0 .. n_spans-2 used
+    const float *h0;                 // nullable
+    float *h_in;                     // [span][c]
+    int64_t columns;
+    int32_t n_spans;
+};
+
+struct StepLaunch {
+    float *h;
+    const void *u, *delta, *z, *B, *C;
+    const float *A, *D, *bias;
+    void *y;
+    int64_t batch, d_inner, d_state;
+    DType dtype;
+};
+
+// Returns true if the (d_state, waves, chunk) combination is compiled in.
+bool scan_variant_supported(int64_t d_state, int waves, int chunk);
+int default_waves(int64_t d_state);
+int default_chunk(int64_t d_state, int waves);
+
+hipError_t launch_scan_full(const ScanLaunch &p, hipStream_t stream);
+hipError_t launch_scan_end(const ScanLaunch &p, hipStream_t stream);
+hipError_t launch_carry(const CarryLaunch &p, hipStream_t stream);
+hipError_t launch_state_update(const StepLaunch &p, hipStream_t stream);
+// h_last = h0 (or zeros when h0 is NULL), for empty sequences.
+hipError_t launch_copy_state(float *dst, const float *src, int64_t count, hipStream_t stream);
+
+} // namespace mambascan

@@ -1,0 +1,111 @@
+// Single-token recurrent state update (decode) for gfx950.
+//
+// One step of h[n] = exp(Delta A[d,n]) h[n] + Delta B[n] u, y = (sum_n C[n] h[n] + D u)
+// * silu(z), Delta = softplus(delta + bias), on a persistent fp32 state of shape
+// (batch, d_inner, d_state) -- the constant-memory token loop "output, h = ssm(token, h)"
+// of "State Space Models and Mamba" (metaphor-xennon.pages.dev, MambaDecoder).
+//
+// The step is bound by the state's read-modify-write (8 bytes per state element), so the
+// layout is chosen for it: each lane owns 4 consecutive state indices of one channel and
+// moves them with one 16-byte load and one 16-byte store, consecutive lanes covering
+// consecutive addresses.  The N/4 lanes of a channel each compute the per-channel softplus
+// and gate (spare VALU in a memory-bound kernel) and combine their partial readouts with a
+// butterfly over N/4 lanes in a fixed order; the first lane of the channel stores y.
+#include "device_math.h"
+#include "scan_common.h"
+
+namespace mambascan {
+
+template <typename T, int N>
+__global__ void __launch_bounds__(256)
+state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__restrict__ delta,
+                    const T *__restrict__ z, const T *__restrict__ Bm, const T *__restrict__ Cm,
+                    const float *__restrict__ A, const float *__restrict__ Dv,
+                    const float *__restrict__ bias, T *__restrict__ y, int32_t Dn)
+{
+    constexpr int LPC = N / 4; // lanes per channel
+    static_assert(N % 4 == 0 && LPC <= 64, "bad d_state");
+    const int b = blockIdx.y;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; // (d, q) within row b
+    const bool valid = i < (int64_t)Dn * LPC;
+    const int d = valid ? (int)(i / LPC) : Dn - 1;
+    const int q = (int)(i % LPC);
+
+    const int64_t c = (int64_t)b * Dn + d; // channel index
+    float4 *hp = reinterpret_cast<float4 *>(h + c * N) + q;
+    const float4 hv = *hp;
+    const float4 av = reinterpret_cast<const float4 *>(A + (int64_t)d * N)[q];
+
+    const float uu = load_val(u, c);
+    const float dl = softplus_f(load_val(delta, c) + (bias ? bias[d] : 0.0f));
+    const float w = dl * uu;
+    const int64_t bn = (int64_t)b * N + 4 * q;
+
+    float hn[4];
+    const float hin[4] = {hv.x, hv.y, hv.z, hv.w};
+    const float ain[4] = {av.x, av.y, av.z, av.w};
+    float yp = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float a = hw_exp2(dl * ain[k] * kLog2e);
+        hn[k] = __builtin_fmaf(a, hin[k], w * load_val(Bm, bn + k));
+        yp = __builtin_fmaf(load_val(Cm, bn + k), hn[k], yp);
+    }
+#pragma unroll
+    for (int m = 1; m < LPC; m <<= 1)
+        yp += __shfl_xor(yp, m, 64);
+
+    if (!valid)
+        return;
+    *hp = make_float4(hn[0], hn[1], hn[2], hn[3]);
+    if (q == 0) {
+        float yv = yp + (Dv ? Dv[d] : 0.0f) * uu;
+        if (z)
+            yv *= silu_f(load_val(z, c));
+        store_val(y, c, yv);
+    }
+}
+
+template <typename T, int N>
+static hipError_t launch_step(const StepLaunch &p, hipStream_t stream)
+{
+    constexpr int LPC = N / 4;
+    const int64_t lanes = p.d_inner * LPC;
+    const uint32_t gx = (uint32_t)((lanes + 255) / 256);
+    // gridDim.y is limited; walk the batch in slices of at most 65535 rows
+    for (int64_t b0 = 0; b0 < p.batch; b0 += 65535) {
+        const int64_t nb = p.batch - b0 < 65535 ? p.batch - b0 : 65535;
+        const int64_t off_bd = b0 * p.d_inner, off_bn = b0 * N;
+        hipLaunchKernelGGL((state_update_kernel<T, N>), dim3(gx, (uint32_t)nb), dim3(256), 0,
+                           stream, p.h + off_bd * N, (const T *)p.u + off_bd,
+                           (const T *)p.delta + off_bd,
+                           p.z ? (const T *)p.z + off_bd : nullptr, (const T *)p.B + off_bn,
+                           (const T *)p.C + off_bn, p.A, p.D, p.bias, (T *)p.y + off_bd,
+                           (int32_t)p.d_inner);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_state_update(const StepLaunch &p, hipStream_t stream)
+{
+    if (p.batch <= 0 || p.d_inner <= 0)
+        return hipSuccess;
+#define STEP_CASE(N_)                                                   \
+    if (p.d_state == N_) {                                              \
+        if (p.dtype == DType::BF16)                                     \
+            return launch_step<uint16_t, N_>(p, stream);                \
+        return launch_step<float, N_>(p, stream);                       \
+    }
+    STEP_CASE(4)
+    STEP_CASE(8)
+    STEP_CASE(16)
+    STEP_CASE(32)
+    STEP_CASE(64)
+#undef STEP_CASE
+    return hipErrorInvalidValue;
+}
+
+} // namespace mambascan

@@ -6,11 +6,15 @@ is the only code shared between the HIP path and the fp64 oracle: both sides are
 fed the very same bits.
 
 Recipe (every config):
-  * ``numpy.random.default_rng(seed)``; parameters are drawn first, in the order
-    A jitter, dt, D, then activations u, delta, z, B, C, h0.
-  * Activations are standard normal draws made directly in float32
-    (``standard_normal(dtype=float32)``) and, for bf16 configs, rounded to bf16
-    with round-to-nearest-even.  bf16 values are carried as raw ``uint16`` bits.
+  * Parameters come from ``numpy.random.default_rng(seed)``, drawn in the order
+    A jitter, dt, D.
+  * Activations u, delta, z, B, C, h0 (tensor ids 0..5) are standard normal
+    draws made directly in float32.  Tensor k is filled in blocks of 2**18
+    values; block j is drawn by ``Generator(PCG64(SeedSequence(seed,
+    spawn_key=(k, j))))``, so the values do not depend on how many threads fill
+    the blocks.  For bf16 configs they are rounded to bf16 with
+    round-to-nearest-even and carried as raw ``uint16`` bits.
+  * Decode steps use spawn keys (1000 + step, k) for u, delta, z, B, C.
   * Parameters are computed in float64 and rounded once to float32:
       - A[d, n] = -exp(A_log[d, n]) with A_log = log(n + 1) (S4D-real, the
         "A = -exp(A_log)" parameterisation of "Understanding Mamba"
@@ -27,10 +31,16 @@ Shapes follow the pages' workloads: d_state 16, expand 2 (d_model 768 -> d_inner
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
+
+BLOCK = 1 << 18
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                      else (os.cpu_count() or 1)))
 
 F32 = "f32"
 BF16 = "bf16"
@@ -167,8 +177,35 @@ def draw_params(rng: np.random.Generator, d_inner: int, d_state: int,
     return Params(A=A, D=Dv, bias=bias)
 
 
-def _normal(rng, shape, dtype):
-    return _store(rng.standard_normal(shape, dtype=np.float32), dtype)
+def _normal(seed: int, key: tuple, shape, dtype: str) -> np.ndarray:
+    """Standard normal float32 draws for tensor `key`, stored as `dtype`."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16 if dtype == BF16 else np.float32)
+
+    def fill(j):
+        lo, hi = j * BLOCK, min(n, (j + 1) * BLOCK)
+        ss = np.random.SeedSequence(seed, spawn_key=tuple(key) + (j,))
+        g = np.random.Generator(np.random.PCG64(ss))
+        x = g.standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] = f32_to_bf16_bits(x) if dtype == BF16 else x
+
+    nblocks = (n + BLOCK - 1) // BLOCK
+    if nblocks <= 1:
+        for j in range(nblocks):
+            fill(j)
+    else:
+        list(_pool().map(fill, range(nblocks)))
+    return out.reshape(shape)
+
+
+_executor = None
+
+
+def _pool() -> concurrent.futures.ThreadPoolExecutor:
+    global _executor
+    if _executor is None:
+        _executor = concurrent.futures.ThreadPoolExecutor(_THREADS)
+    return _executor
 
 
 def make_scan_inputs(cfg: ScanConfig, *, batch: Optional[int] = None,
@@ -185,13 +222,13 @@ def make_scan_inputs(cfg: ScanConfig, *, batch: Optional[int] = None,
     p = draw_params(rng, cfg.d_inner, cfg.d_state, cfg.a_jitter, cfg.d_uniform)
     bld = (cfg.batch, cfg.seqlen, cfg.d_inner)
     bln = (cfg.batch, cfg.seqlen, cfg.d_state)
-    u = _normal(rng, bld, cfg.dtype)
-    delta = _normal(rng, bld, cfg.dtype)
-    z = _normal(rng, bld, cfg.dtype) if cfg.gate else None
-    B = _normal(rng, bln, cfg.dtype)
-    C = _normal(rng, bln, cfg.dtype)
-    h0 = (rng.standard_normal((cfg.batch, cfg.d_inner, cfg.d_state), dtype=np.float32)
-          if cfg.h0 else None)
+    sd = cfg.seed
+    u = _normal(sd, (0,), bld, cfg.dtype)
+    delta = _normal(sd, (1,), bld, cfg.dtype)
+    z = _normal(sd, (2,), bld, cfg.dtype) if cfg.gate else None
+    B = _normal(sd, (3,), bln, cfg.dtype)
+    C = _normal(sd, (4,), bln, cfg.dtype)
+    h0 = (_normal(sd, (5,), (cfg.batch, cfg.d_inner, cfg.d_state), F32) if cfg.h0 else None)
     return ScanInputs(cfg=cfg, params=p, u=u, delta=delta, z=z, B=B, C=C, h0=h0)
 
 
@@ -213,17 +250,17 @@ def make_decode_state(batch: int = DECODE["batch"], d_inner: int = DECODE["d_inn
     """Parameters (drawn exactly as the large-model prefill config) and h ~ N(0,1)."""
     rng = np.random.default_rng(seed)
     p = draw_params(rng, d_inner, d_state, a_jitter=True, d_uniform=True)
-    h = rng.standard_normal((batch, d_inner, d_state), dtype=np.float32)
+    h = _normal(seed, (5,), (batch, d_inner, d_state), F32)
     return p, h
 
 
 def make_decode_step(step: int, batch: int = DECODE["batch"], d_inner: int = DECODE["d_inner"],
                      d_state: int = DECODE["d_state"], dtype: str = DECODE["dtype"],
                      seed: int = DECODE["seed"]) -> DecodeStep:
-    """Fresh one-token inputs for one step, from ``default_rng([seed, step])``."""
-    rng = np.random.default_rng([seed, step])
+    """Fresh one-token inputs for one step (spawn keys (1000 + step, k))."""
     bd = (batch, d_inner)
     bn = (batch, d_state)
-    return DecodeStep(u=_normal(rng, bd, dtype), delta=_normal(rng, bd, dtype),
-                      z=_normal(rng, bd, dtype), B=_normal(rng, bn, dtype),
-                      C=_normal(rng, bn, dtype))
+    k = 1000 + step
+    return DecodeStep(u=_normal(seed, (k, 0), bd, dtype), delta=_normal(seed, (k, 1), bd, dtype),
+                      z=_normal(seed, (k, 2), bd, dtype), B=_normal(seed, (k, 3), bn, dtype),
+                      C=_normal(seed, (k, 4), bn, dtype))
