@@ -84,18 +84,26 @@ typedef enum {
 /* d_state values compiled into the library. */
 #define MAMBA_MAX_D_STATE 64
 
+/* Kernel families (mamba_scan_opts_t.kernel). */
+#define MAMBA_KERNEL_AUTO 0
+#define MAMBA_KERNEL_BLOCK 1 /* 64 channels per block; state indices split across its
+                                waves, which exchange through LDS with barriers      */
+#define MAMBA_KERNEL_ROWS 2  /* 16 channels per wave; state indices split across the
+                                wave's four 16-lane rows; no barriers                */
+
 /* Tuning and testing options for mamba_scan_fwd_ex.  Zero fields mean "auto".
- *   chunk_len : time steps staged per block iteration (8, 16 or 32).
- *   waves     : wavefronts per block; each handles d_state/waves state indices
- *               of 64 channels (4 or 8).
+ *   chunk_len : BLOCK kernel: time steps staged per iteration (8, 16 or 32).
+ *   waves     : BLOCK kernel: wavefronts per block (4 or 8); each handles
+ *               d_state/waves state indices of 64 channels.
  *   n_spans   : the sequence is split into n_spans spans scanned in parallel
  *               and joined by a carry pass (1..64; 1 = no split).
+ *   kernel    : MAMBA_KERNEL_* family.
  * Every supported setting gives the same result up to float32 rounding. */
 typedef struct {
     int32_t chunk_len;
     int32_t waves;
     int32_t n_spans;
-    int32_t reserved;
+    int32_t kernel;
 } mamba_scan_opts_t;
 
 /* Returns 1 if d_state is supported by this build, else 0. */

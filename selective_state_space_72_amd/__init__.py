@@ -40,9 +40,13 @@ class MambaError(RuntimeError):
         super().__init__(f"{where}: {status_string(status)}")
 
 
+MAMBA_KERNEL_AUTO, MAMBA_KERNEL_BLOCK, MAMBA_KERNEL_ROWS = 0, 1, 2
+KERNELS = {"auto": MAMBA_KERNEL_AUTO, "block": MAMBA_KERNEL_BLOCK, "rows": MAMBA_KERNEL_ROWS}
+
+
 class ScanOpts(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int32), ("waves", ctypes.c_int32),
-                ("n_spans", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("n_spans", ctypes.c_int32), ("kernel", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -129,14 +133,17 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _opts(chunk_len=0, waves=0, n_spans=0):
-    return ScanOpts(int(chunk_len), int(waves), int(n_spans), 0)
+def _opts(chunk_len=0, waves=0, n_spans=0, kernel="auto"):
+    if kernel not in KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
+    return ScanOpts(int(chunk_len), int(waves), int(n_spans), KERNELS[kernel])
 
 
 def mamba_scan_fwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state: int,
-                                  chunk_len: int = 0, waves: int = 0, n_spans: int = 0) -> int:
+                                  chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
+                                  kernel: str = "auto") -> int:
     lib = load_library()
-    o = _opts(chunk_len, waves, n_spans)
+    o = _opts(chunk_len, waves, n_spans, kernel)
     n = lib.mamba_scan_fwd_workspace_size_ex(batch, seqlen, d_inner, d_state, ctypes.byref(o))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes or options for mamba_scan_fwd")
@@ -146,7 +153,7 @@ def mamba_scan_fwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state
 def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
                    return_last_state: bool = False, *, out=None, h_last_out=None,
                    chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
-                   workspace=None) -> Tuple:
+                   kernel: str = "auto", workspace=None) -> Tuple:
     """Selective scan over (batch, seqlen, d_inner); see include/mamba_scan.h.
 
     Returns (y, h_last) -- h_last is None unless return_last_state (or h_last_out).
@@ -179,7 +186,7 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
         h_last = torch.empty((batch, d_inner, d_state), dtype=f32, device=dev)
     p_hl = _ptr(h_last, "h_last_out", (batch, d_inner, d_state), f32, dev)
 
-    opts = _opts(chunk_len, waves, n_spans)
+    opts = _opts(chunk_len, waves, n_spans, kernel)
     need = lib.mamba_scan_fwd_workspace_size_ex(batch, seqlen, d_inner, d_state,
                                                 ctypes.byref(opts))
     if need == ctypes.c_size_t(-1).value:

@@ -10,6 +10,9 @@ using namespace mambascan;
 
 namespace {
 
+// Kernel family used when the caller does not choose one.
+constexpr Family kAutoFamily = Family::Block;
+
 struct Range {
     uintptr_t lo, hi; // [lo, hi)
 };
@@ -46,6 +49,7 @@ int cu_count()
 }
 
 struct Plan {
+    Family family;
     int waves, chunk, n_spans;
     int64_t span_len;
 };
@@ -57,10 +61,22 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
                          const mamba_scan_opts_t *opts, Plan *plan)
 {
     Plan p{};
-    p.waves = opts && opts->waves ? opts->waves : default_waves(d_state);
-    p.chunk = opts && opts->chunk_len ? opts->chunk_len : default_chunk(d_state, p.waves);
-    if (!scan_variant_supported(d_state, p.waves, p.chunk))
+    const int fam = opts ? opts->kernel : MAMBA_KERNEL_AUTO;
+    if (fam == MAMBA_KERNEL_ROWS || (fam == MAMBA_KERNEL_AUTO && kAutoFamily == Family::Rows)) {
+        if ((opts && (opts->waves || opts->chunk_len)))
+            return MAMBA_ERR_UNSUPPORTED; // fixed shape: 4 waves x 16 channels, 4-step blocks
+        p.family = Family::Rows;
+        p.waves = 4;
+        p.chunk = 4;
+    } else if (fam == MAMBA_KERNEL_BLOCK || fam == MAMBA_KERNEL_AUTO) {
+        p.family = Family::Block;
+        p.waves = opts && opts->waves ? opts->waves : default_waves(d_state);
+        p.chunk = opts && opts->chunk_len ? opts->chunk_len : default_chunk(d_state, p.waves);
+        if (!scan_variant_supported(d_state, p.waves, p.chunk))
+            return MAMBA_ERR_UNSUPPORTED;
+    } else {
         return MAMBA_ERR_UNSUPPORTED;
+    }
     int spans = 1;
     if (opts && opts->n_spans) {
         if (opts->n_spans < 1 || opts->n_spans > 64)
@@ -248,12 +264,20 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
     L.chunk = plan.chunk;
     L.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
 
+    const bool rows = plan.family == Family::Rows;
+    auto full = [&](const ScanLaunch &x) {
+        return rows ? launch_rows_full(x, st) : launch_scan_full(x, st);
+    };
+    auto end = [&](const ScanLaunch &x) {
+        return rows ? launch_rows_end(x, st) : launch_scan_end(x, st);
+    };
+
     if (plan.n_spans == 1) {
         L.h_init = h0;
         L.h_init_span_stride = 0;
         L.first_span = 0;
         L.launch_spans = 1;
-        return hip_status(launch_scan_full(L, st));
+        return hip_status(full(L));
     }
 
     // ---- split sequence: span summaries, carry pass, full rescan ----
@@ -270,7 +294,7 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
     E.ws_hloc = ws_hloc;
     E.first_span = 0;
     E.launch_spans = (int32_t)(S - 1);
-    hipError_t e = launch_scan_end(E, st);
+    hipError_t e = end(E);
     if (e != hipSuccess)
         return MAMBA_ERR_HIP;
 
@@ -289,7 +313,7 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
     L.h_init_span_stride = bdn;
     L.first_span = 0;
     L.launch_spans = (int32_t)S;
-    return hip_status(launch_scan_full(L, st));
+    return hip_status(full(L));
 }
 
 mamba_status_t mamba_scan_fwd(const void *u, const void *delta, const float *A, const void *B,

@@ -28,6 +28,8 @@ struct ScanLaunch {
     DType dtype;
 };
 
+enum class Family : int { Auto = 0, Block = 1, Rows = 2 };
+
 // The carry pass joining span end states: for every state column c = (b, d, n)
 // h_in[s][c] = state entering span s (s = 0 .. n_spans-1).
 struct CarryLaunch {
@@ -52,8 +54,12 @@ bool scan_variant_supported(int64_t d_state, int waves, int chunk);
 int default_waves(int64_t d_state);
 int default_chunk(int64_t d_state, int waves);
 
+// LDS-exchange kernel: 64 channels per block, state indices split across its waves.
 hipError_t launch_scan_full(const ScanLaunch &p, hipStream_t stream);
 hipError_t launch_scan_end(const ScanLaunch &p, hipStream_t stream);
+// Barrier-free kernel: 16 channels per wave, state indices split across its DPP rows.
+hipError_t launch_rows_full(const ScanLaunch &p, hipStream_t stream);
+hipError_t launch_rows_end(const ScanLaunch &p, hipStream_t stream);
 hipError_t launch_carry(const CarryLaunch &p, hipStream_t stream);
 hipError_t launch_state_update(const StepLaunch &p, hipStream_t stream);
 // h_last = h0 (or zeros when h0 is NULL), for empty sequences.

@@ -27,12 +27,24 @@
 //     total decay exp(A * sum Delta); the carry kernel combines spans with the associative
 //     map (a, b) o (a', b') = (a a', a' b + b'); a FULL launch rescans each span from its
 //     true carry-in and emits y.
+#include <type_traits>
+
 #include "device_math.h"
 #include "scan_common.h"
 
 namespace mambascan {
 
-template <typename T, int N, int NW, int TC, bool FULL>
+// Compile-time loop: f(integral_constant<int, I>) for I in [I0, I1).
+template <int I0, int I1, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I0 < I1) {
+        f(std::integral_constant<int, I0>{});
+        static_for<I0 + 1, I1>(f);
+    }
+}
+
+template <typename T, int N, int NW, int TC, int PD, bool FULL>
 __global__ void __launch_bounds__(64 * NW)
 scan_chunk_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T *__restrict__ z,
                   const T *__restrict__ Bm, const T *__restrict__ Cm,
@@ -44,6 +56,7 @@ scan_chunk_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T 
 {
     constexpr int NQ = N / NW;   // state indices per lane
     constexpr int KPL = TC / NW; // prologue/epilogue channel-steps per lane per chunk
+    // PD: chunks of input in flight (prefetch depth)
     constexpr int NT = 64 * NW;  // threads per block
     constexpr int PBC = (TC * N + NT - 1) / NT; // B (and C) values staged per thread per chunk
     constexpr int BCW = FULL ? 2 * NQ : NQ;     // floats per (step, wave) in s_bc
@@ -83,20 +96,21 @@ scan_chunk_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T 
 
     const int64_t row_b = (int64_t)b * L; // row (b, t=0) of the (B, L, *) tensors
 
-    // Inputs of one chunk, requested one chunk ahead: u, delta, z for KPL (t, d) pairs per
-    // lane (coalesced rows of 64 channels) and PBC entries of the chunk's B and C rows,
-    // which are contiguous (TC * N values each) in memory.
-    T ru[KPL], rd[KPL], rz[KPL], rb[PBC], rc[PBC];
-    auto fetch = [&](int64_t t0) {
+    // Inputs of a chunk, requested PD chunks ahead into a ring of register buffers: u,
+    // delta, z for KPL (t, d) pairs per lane (coalesced rows of 64 channels) and PBC
+    // entries of the chunk's B and C rows, which are contiguous (TC * N values each).
+    T ru[PD][KPL], rd[PD][KPL], rz[PD][KPL], rb[PD][PBC], rc[PD][PBC];
+    auto fetch = [&](auto BUF, int64_t t0) {
+        constexpr int j = decltype(BUF)::value;
 #pragma unroll
         for (int k = 0; k < KPL; ++k) {
             const int64_t t = t0 + g + k * NW; // wave-uniform
             if (t < t_end) {
                 const int64_t i = (row_b + t) * Dn + dc;
-                ru[k] = u[i];
-                rd[k] = delta[i];
+                ru[j][k] = u[i];
+                rd[j][k] = delta[i];
                 if (gated)
-                    rz[k] = z[i];
+                    rz[j][k] = z[i];
             }
         }
 #pragma unroll
@@ -104,16 +118,16 @@ scan_chunk_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T 
             const int e = tid + k * NT; // element of the chunk's (TC, N) block
             if (e < TC * N && t0 + e / N < t_end) {
                 const int64_t i = (row_b + t0) * N + e;
-                rb[k] = Bm[i];
+                rb[j][k] = Bm[i];
                 if (FULL)
-                    rc[k] = Cm[i];
+                    rc[j][k] = Cm[i];
             }
         }
     };
 
     float sum_dt = 0.0f;
-    fetch(t_begin);
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += TC) {
+    auto chunk = [&](auto BUF, int64_t t0) {
+        constexpr int j = decltype(BUF)::value;
         const int nt = (int)min((int64_t)TC, t_end - t0);
 
         // ---- prologue: Delta and Delta*u once per (t, d); B and C widened to fp32 ----
@@ -125,13 +139,13 @@ scan_chunk_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T 
             du[k] = 0.0f;
             gz[k] = 1.0f;
             if (tl < nt) {
-                const float uu = widen(ru[k]);
-                dl = softplus_f(widen(rd[k]) + bias_d);
+                const float uu = widen(ru[j][k]);
+                dl = softplus_f(widen(rd[j][k]) + bias_d);
                 w = dl * uu;
                 if (FULL) {
                     du[k] = D_d * uu;
                     if (gated)
-                        gz[k] = silu_f(widen(rz[k]));
+                        gz[k] = silu_f(widen(rz[j][k]));
                 }
             }
             s_dw[tl][lane] = make_float2(dl, w);
@@ -142,13 +156,13 @@ scan_chunk_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T 
             if (e < TC * N) {
                 const int tl = e / N, n = e % N;
                 const bool ok = tl < nt;
-                s_bc[tl][n / NQ][n % NQ] = ok ? widen(rb[k]) : 0.0f;
+                s_bc[tl][n / NQ][n % NQ] = ok ? widen(rb[j][k]) : 0.0f;
                 if (FULL)
-                    s_bc[tl][n / NQ][NQ + n % NQ] = ok ? widen(rc[k]) : 0.0f;
+                    s_bc[tl][n / NQ][NQ + n % NQ] = ok ? widen(rc[j][k]) : 0.0f;
             }
         }
-        if (t0 + TC < t_end)
-            fetch(t0 + TC);
+        if (t0 + PD * TC < t_end)
+            fetch(BUF, t0 + PD * TC); // this buffer is free again: refill it PD chunks ahead
         __syncthreads();
 
         // ---- recurrence over the chunk ----
@@ -158,8 +172,8 @@ scan_chunk_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T 
             const float2 dw = s_dw[tl][lane];
             float bc[BCW];
 #pragma unroll
-            for (int j = 0; j < BCW; ++j)
-                bc[j] = s_bc[tl][g][j];
+            for (int i = 0; i < BCW; ++i)
+                bc[i] = s_bc[tl][g][i];
             float yp = 0.0f;
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
@@ -197,6 +211,19 @@ scan_chunk_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T 
                 }
             }
         }
+    };
+
+    static_for<0, PD>([&](auto BUF) {
+        const int64_t t0 = t_begin + decltype(BUF)::value * TC;
+        if (t0 < t_end)
+            fetch(BUF, t0);
+    });
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += PD * TC) {
+        static_for<0, PD>([&](auto BUF) {
+            const int64_t tc = t0 + decltype(BUF)::value * TC; // block-uniform
+            if (tc < t_end)
+                chunk(BUF, tc);
+        });
     }
 
     if (!dvalid)
@@ -222,45 +249,49 @@ scan_chunk_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T 
 // variant table
 // ---------------------------------------------------------------------------
 
+// (d_state, waves, chunk, prefetch depth)
 #define MAMBA_SCAN_VARIANTS(X) \
-    X(4, 4, 16)                \
-    X(8, 4, 16)                \
-    X(8, 8, 8)                 \
-    X(16, 4, 16)               \
-    X(16, 4, 32)               \
-    X(16, 8, 8)                \
-    X(16, 8, 16)               \
-    X(32, 4, 16)               \
-    X(32, 8, 8)                \
-    X(32, 8, 16)               \
-    X(64, 8, 8)                \
-    X(64, 8, 16)
+    X(4, 4, 16, 2)             \
+    X(8, 4, 16, 2)             \
+    X(8, 8, 8, 3)              \
+    X(16, 4, 16, 2)            \
+    X(16, 4, 32, 2)            \
+    X(16, 8, 8, 3)             \
+    X(16, 8, 16, 2)            \
+    X(32, 4, 16, 2)            \
+    X(32, 8, 8, 3)             \
+    X(32, 8, 16, 2)            \
+    X(64, 8, 8, 3)             \
+    X(64, 8, 16, 2)
 
 bool scan_variant_supported(int64_t d_state, int waves, int chunk)
 {
-#define X(N_, W_, C_)                                            \
+#define X(N_, W_, C_, P_)                                        \
     if (d_state == N_ && waves == W_ && chunk == C_) return true;
     MAMBA_SCAN_VARIANTS(X)
 #undef X
     return false;
 }
 
-int default_waves(int64_t d_state) { return d_state >= 8 ? 8 : 4; }
+// Defaults: 8 waves (d_state/8 state indices per lane) where d_state allows it, so a
+// block holds 512 lanes; 16-step chunks.  Every default is in the variant table.
+int default_waves(int64_t d_state) { return d_state >= 16 ? 8 : 4; }
 
 int default_chunk(int64_t d_state, int waves)
 {
     (void)d_state;
-    return waves == 8 ? 16 : 16;
+    (void)waves;
+    return 16;
 }
 
-template <typename T, int N, int NW, int TC, bool FULL>
+template <typename T, int N, int NW, int TC, int PD, bool FULL>
 static hipError_t launch_variant(const ScanLaunch &p, hipStream_t stream)
 {
     const int32_t tiles = (int32_t)((p.d_inner + 63) / 64);
     const int64_t blocks = (int64_t)tiles * p.batch * p.launch_spans;
     if (blocks <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL((scan_chunk_kernel<T, N, NW, TC, FULL>), dim3((uint32_t)blocks),
+    hipLaunchKernelGGL((scan_chunk_kernel<T, N, NW, TC, PD, FULL>), dim3((uint32_t)blocks),
                        dim3(64 * NW), 0, stream, (const T *)p.u, (const T *)p.delta,
                        (const T *)p.z, (const T *)p.B, (const T *)p.C, p.A, p.D, p.bias,
                        p.h_init, p.h_init_span_stride, (T *)p.y, p.h_last, p.ws_decay,
@@ -272,11 +303,11 @@ static hipError_t launch_variant(const ScanLaunch &p, hipStream_t stream)
 template <bool FULL>
 static hipError_t launch_any(const ScanLaunch &p, hipStream_t stream)
 {
-#define X(N_, W_, C_)                                                                    \
+#define X(N_, W_, C_, P_)                                                                \
     if (p.d_state == N_ && p.waves == W_ && p.chunk == C_) {                             \
         if (p.dtype == DType::BF16)                                                      \
-            return launch_variant<uint16_t, N_, W_, C_, FULL>(p, stream);                \
-        return launch_variant<float, N_, W_, C_, FULL>(p, stream);                       \
+            return launch_variant<uint16_t, N_, W_, C_, P_, FULL>(p, stream);            \
+        return launch_variant<float, N_, W_, C_, P_, FULL>(p, stream);                   \
     }
     MAMBA_SCAN_VARIANTS(X)
 #undef X

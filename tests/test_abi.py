@@ -141,6 +141,8 @@ def test_scan_rejects_bad_options(lib):
     assert scan(lib, opts=ms.ScanOpts(0, 0, 65, 0)) == UNSUP      # spans
     assert scan(lib, opts=ms.ScanOpts(0, 0, -2, 0)) == UNSUP
     assert scan(lib, N=4, opts=ms.ScanOpts(16, 8, 0, 0)) == UNSUP  # 8 waves need N >= 8
+    assert scan(lib, opts=ms.ScanOpts(0, 0, 0, 3)) == UNSUP       # kernel family
+    assert scan(lib, opts=ms.ScanOpts(16, 0, 0, 2)) == UNSUP      # rows: no chunk option
 
 
 def step(lib, *, h=BASE, u=BASE + 100 * MB, delta=BASE + 110 * MB, A=BASE + 120 * MB,
@@ -167,3 +169,11 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ms, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         ms.load_library(str(tmp_path / "libmambascan.so"))
+
+
+def test_default_plan_is_compiled_for_every_d_state(lib):
+    for n in (4, 8, 16, 32, 64):
+        for shape in ((1, 64, 32), (8, 4096, 5120), (1, 131072, 2048)):
+            b, L, d = shape
+            assert lib.mamba_scan_fwd_workspace_size(b, L, d, n) != ctypes.c_size_t(-1).value, \
+                (n, shape)

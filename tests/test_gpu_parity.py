@@ -36,7 +36,7 @@ def check(name, y, h, yr, hr, dtype):
 
 
 def full_check(name, inp, **kw):
-    opts = {k: kw.pop(k) for k in ("chunk_len", "waves", "n_spans") if k in kw}
+    opts = {k: kw.pop(k) for k in ("chunk_len", "waves", "n_spans", "kernel") if k in kw}
     log(f"case {name}: batch={inp.cfg.batch} L={inp.cfg.seqlen} D={inp.cfg.d_inner} "
         f"N={inp.cfg.d_state} {inp.dtype} opts={opts} {kw}")
     di = DevInputs(inp)
@@ -127,7 +127,8 @@ def test_c5_decode_1024_chained_steps():
 
 VARIANTS = [dict(waves=8, chunk_len=16), dict(waves=8, chunk_len=8), dict(waves=4, chunk_len=16),
             dict(waves=4, chunk_len=32), dict(n_spans=2), dict(n_spans=7), dict(n_spans=64),
-            dict(waves=4, chunk_len=16, n_spans=5)]
+            dict(waves=4, chunk_len=16, n_spans=5), dict(kernel="block"), dict(kernel="rows"),
+            dict(kernel="rows", n_spans=3), dict(kernel="rows", n_spans=64)]
 
 
 @pytest.mark.parametrize("opts", VARIANTS, ids=[str(v) for v in VARIANTS])
@@ -137,26 +138,28 @@ def test_variants_agree_with_oracle(opts):
     full_check(f"variant {opts}", inp, **opts)
 
 
-@pytest.mark.parametrize("n", [4, 8, 32, 64])
+@pytest.mark.parametrize("kernel", ["block", "rows"])
+@pytest.mark.parametrize("n", [4, 8, 16, 32, 64])
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
-def test_other_state_sizes(n, dtype):
+def test_other_state_sizes(n, dtype, kernel):
     import dataclasses
     cfg = dataclasses.replace(synth.CONFIGS["c3"], d_state=n, dtype=dtype, h0=True)
     inp = synth.make_scan_inputs(cfg, batch=2, seqlen=333, d_inner=72, seed=20 + n)
-    full_check(f"N={n} {dtype}", inp)
-    full_check(f"N={n} {dtype} split", inp, n_spans=3)
+    full_check(f"N={n} {dtype} {kernel}", inp, kernel=kernel)
+    full_check(f"N={n} {dtype} {kernel} split", inp, n_spans=3, kernel=kernel)
 
 
+@pytest.mark.parametrize("kernel", ["block", "rows"])
 @pytest.mark.parametrize("shape", [(1, 1, 1), (1, 1, 64), (2, 7, 65), (3, 17, 130),
-                                   (1, 4097, 64), (5, 129, 40)])
-def test_ragged_shapes_fp32(shape):
+                                   (1, 4097, 64), (5, 129, 40), (2, 6, 17)])
+def test_ragged_shapes_fp32(shape, kernel):
     import dataclasses
     b, L, d = shape
     cfg = dataclasses.replace(synth.CONFIGS["c1"], h0=True, gate=True)
     inp = synth.make_scan_inputs(cfg, batch=b, seqlen=L, d_inner=d, seed=b * 1000 + L + d)
-    full_check(f"fp32 {shape}", inp)
-    full_check(f"fp32 {shape} no D/bias/h0/z", inp, gate=False, use_D=False, use_bias=False,
-               use_h0=False)
+    full_check(f"fp32 {shape} {kernel}", inp, kernel=kernel)
+    full_check(f"fp32 {shape} {kernel} no D/bias/h0/z", inp, gate=False, use_D=False,
+               use_bias=False, use_h0=False, kernel=kernel)
 
 
 def test_empty_sequence_returns_h0():
@@ -172,18 +175,20 @@ def test_empty_sequence_returns_h0():
     assert torch.count_nonzero(h) == 0
 
 
+@pytest.mark.parametrize("kernel", ["block", "rows"])
 @pytest.mark.parametrize("n_spans", [1, 4])
-def test_in_place_state_continuation(n_spans):
+def test_in_place_state_continuation(n_spans, kernel):
     """h_last may be h0 itself: scanning two halves in place equals one scan."""
     inp = synth.make_scan_inputs(synth.CONFIGS["c4"], batch=1, seqlen=1024, d_inner=128, seed=9)
     di = DevInputs(inp)
-    y_full, h_full = di.run(gate=False, n_spans=n_spans)
+    y_full, h_full = di.run(gate=False, n_spans=n_spans, kernel=kernel)
     h = di.h0.clone()
     ys = []
     for lo, hi in ((0, 400), (400, 1024)):
         sl = lambda t: t[:, lo:hi].contiguous()  # noqa: E731
         y, _ = ms.mamba_scan_fwd(sl(di.u), sl(di.delta), di.A, sl(di.B), sl(di.C), D=di.D,
-                                 delta_bias=di.bias, h0=h, h_last_out=h, n_spans=n_spans)
+                                 delta_bias=di.bias, h0=h, h_last_out=h, n_spans=n_spans,
+                                 kernel=kernel)
         ys.append(y)
     torch.cuda.synchronize()
     y2 = torch.cat(ys, dim=1)
@@ -194,7 +199,7 @@ def test_in_place_state_continuation(n_spans):
 def test_deterministic():
     inp = synth.make_scan_inputs(synth.CONFIGS["c2"], batch=2, seqlen=700, d_inner=256, seed=4)
     di = DevInputs(inp)
-    for opts in (dict(), dict(n_spans=3)):
+    for opts in (dict(), dict(n_spans=3), dict(kernel="rows"), dict(kernel="rows", n_spans=3)):
         y1, h1 = di.run(**opts)
         y2, h2 = di.run(**opts)
         assert torch.equal(y1, y2) and torch.equal(h1, h2)
@@ -238,3 +243,43 @@ def test_decode_other_sizes_fp32():
                                     D=f(p.D), z=f(st.z), bias=f(p.bias))
         assert metric(from_dev(y), yr) <= TOL[synth.F32]
         assert metric(from_dev(h_dev), hr) <= TOL[synth.F32]
+
+
+def test_step_size_softplus_accuracy():
+    """L = 1, h0 = 0, u = B = 1, C = 1/N, no D or gate: y = Delta = softplus(delta + bias),
+    so the kernel's softplus is compared directly with the fp64 value over a wide range."""
+    n, d = 16, 4096
+    delta = np.linspace(-40.0, 40.0, d).astype(np.float32)
+    u = torch.ones(1, 1, d, device=DEV)
+    dl = torch.from_numpy(delta).view(1, 1, d).to(DEV)
+    A = -torch.ones(d, n, device=DEV)
+    B = torch.ones(1, 1, n, device=DEV)
+    C = torch.full((1, 1, n), 1.0 / n, device=DEV)
+    y, _ = ms.mamba_scan_fwd(u, dl, A, B, C)
+    torch.cuda.synchronize()
+    ref = np.logaddexp(0.0, delta.astype(np.float64))
+    rel = np.abs(from_dev(y).ravel() - ref) / ref
+    log(f"  softplus: max rel err {rel.max():.3e} at delta={delta[rel.argmax()]:.3f}")
+    assert rel.max() < 2e-6
+
+
+def test_long_fp32_decay_error_growth():
+    """u = 0, h0 = 1 over 4096 steps (fp32): y_t = sum_n C exp(A_n S_t); the error of the
+    running product of v_exp_f32 values grows with t and is reported per quarter."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS["c1"], h0=True, seqlen=4096, d_inner=64)
+    inp = synth.make_scan_inputs(cfg, seed=77)
+    inp.u = np.zeros_like(inp.u)
+    inp.h0 = np.ones_like(inp.h0)
+    inp.C = np.abs(inp.C)
+    di = DevInputs(inp)
+    y, h = di.run(gate=False)
+    yr, hr = oracle_scan(inp, gate=False)
+    yd = from_dev(y)
+    for q in range(4):
+        sl = slice(q * 1024, (q + 1) * 1024)
+        rel = np.max(np.abs(yd[:, sl] - yr[:, sl]) / np.abs(yr[:, sl]).clip(1e-30))
+        log(f"  decay t in [{q * 1024}, {(q + 1) * 1024}): max rel err {rel:.3e}")
+    e = metric(yd, yr)
+    log(f"  decay: y M={e:.3e}")
+    assert e <= TOL[synth.F32]
