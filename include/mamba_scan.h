@@ -90,11 +90,13 @@ typedef enum {
                                 waves, which exchange through LDS with barriers      */
 #define MAMBA_KERNEL_ROWS 2  /* 16 channels per wave; state indices split across the
                                 wave's four 16-lane rows; no barriers                */
+#define MAMBA_KERNEL_SCALAR 3 /* as BLOCK, with B/C repacked to fp32 by a staging pass
+                                 and read by each wave through scalar registers      */
 
 /* Tuning and testing options for mamba_scan_fwd_ex.  Zero fields mean "auto".
- *   chunk_len : BLOCK kernel: time steps staged per iteration (8, 16 or 32).
- *   waves     : BLOCK kernel: wavefronts per block (4 or 8); each handles
- *               d_state/waves state indices of 64 channels.
+ *   chunk_len : BLOCK/SCALAR kernels: time steps per iteration (4 to 32).
+ *   waves     : BLOCK/SCALAR kernels: wavefronts per block (4 or 8); each
+ *               handles d_state/waves state indices of 64 channels.
  *   n_spans   : the sequence is split into n_spans spans scanned in parallel
  *               and joined by a carry pass (1..64; 1 = no split).
  *   kernel    : MAMBA_KERNEL_* family.

@@ -40,8 +40,9 @@ class MambaError(RuntimeError):
         super().__init__(f"{where}: {status_string(status)}")
 
 
-MAMBA_KERNEL_AUTO, MAMBA_KERNEL_BLOCK, MAMBA_KERNEL_ROWS = 0, 1, 2
-KERNELS = {"auto": MAMBA_KERNEL_AUTO, "block": MAMBA_KERNEL_BLOCK, "rows": MAMBA_KERNEL_ROWS}
+MAMBA_KERNEL_AUTO, MAMBA_KERNEL_BLOCK, MAMBA_KERNEL_ROWS, MAMBA_KERNEL_SCALAR = 0, 1, 2, 3
+KERNELS = {"auto": MAMBA_KERNEL_AUTO, "block": MAMBA_KERNEL_BLOCK, "rows": MAMBA_KERNEL_ROWS,
+           "scalar": MAMBA_KERNEL_SCALAR}
 
 
 class ScanOpts(ctypes.Structure):

@@ -10,8 +10,17 @@ using namespace mambascan;
 
 namespace {
 
-// Kernel family used when the caller does not choose one.
-constexpr Family kAutoFamily = Family::Block;
+// Kernel family used when the caller does not choose one: the scalar-B/C kernel when
+// the channels alone give every SIMD several waves (no sequence split), else the
+// barrier-free row kernel with a sequence split (fastest measured there); d_state 64,
+// which the scalar kernel does not compile, uses the row kernel too.
+Family auto_family(int64_t batch, int64_t d_inner, int64_t d_state, int cus)
+{
+    const int64_t scalar_waves = batch * ((d_inner + 63) / 64) * 8;
+    if (d_state <= 32 && scalar_waves * 2 >= (int64_t)cus * 4 * 4)
+        return Family::Scalar;
+    return Family::Rows;
+}
 
 struct Range {
     uintptr_t lo, hi; // [lo, hi)
@@ -61,14 +70,26 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
                          const mamba_scan_opts_t *opts, Plan *plan)
 {
     Plan p{};
+    const int cus = cu_count();
     const int fam = opts ? opts->kernel : MAMBA_KERNEL_AUTO;
-    if (fam == MAMBA_KERNEL_ROWS || (fam == MAMBA_KERNEL_AUTO && kAutoFamily == Family::Rows)) {
+    const Family autof = auto_family(batch, d_inner, d_state, cus);
+    if (fam == MAMBA_KERNEL_ROWS || (fam == MAMBA_KERNEL_AUTO && autof == Family::Rows)) {
         if ((opts && (opts->waves || opts->chunk_len)))
             return MAMBA_ERR_UNSUPPORTED; // fixed shape: 4 waves x 16 channels, 4-step blocks
         p.family = Family::Rows;
         p.waves = 4;
         p.chunk = 4;
-    } else if (fam == MAMBA_KERNEL_BLOCK || fam == MAMBA_KERNEL_AUTO) {
+    } else if (fam == MAMBA_KERNEL_SCALAR ||
+               (fam == MAMBA_KERNEL_AUTO && autof == Family::Scalar)) {
+        p.family = Family::Scalar;
+        // defaults: (waves, chunk) = (4, 16), (4, 8), (8, 8), (8, 4) for d_state 4..32
+        const int dw = d_state >= 16 ? 8 : 4;
+        const int dc = d_state == 4 ? 16 : (d_state == 32 ? 4 : 8);
+        p.waves = opts && opts->waves ? opts->waves : dw;
+        p.chunk = opts && opts->chunk_len ? opts->chunk_len : dc;
+        if (!scalar_variant_supported(d_state, p.waves, p.chunk))
+            return MAMBA_ERR_UNSUPPORTED;
+    } else if (fam == MAMBA_KERNEL_BLOCK) {
         p.family = Family::Block;
         p.waves = opts && opts->waves ? opts->waves : default_waves(d_state);
         p.chunk = opts && opts->chunk_len ? opts->chunk_len : default_chunk(d_state, p.waves);
@@ -85,7 +106,7 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     } else {
         const int64_t tiles = batch * ((d_inner + 63) / 64);
         const int64_t waves_per_span = tiles * p.waves;
-        const int64_t want = (int64_t)cu_count() * 4 /*SIMDs*/ * 4 /*waves each*/;
+        const int64_t want = (int64_t)cus * 4 /*SIMDs*/ * 4 /*waves each*/;
         if (waves_per_span * 2 < want) {
             int64_t s = 1;
             while (s * waves_per_span < want && s < 64)
@@ -112,12 +133,23 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     return MAMBA_OK;
 }
 
-size_t workspace_bytes_for(int64_t batch, int64_t d_inner, int64_t d_state, const Plan &p)
+// Workspace layout: [staged B/C (scalar family), 256-byte aligned] [span summaries].
+size_t staged_bytes_for(int64_t batch, int64_t seqlen, int64_t d_state, const Plan &p)
 {
-    if (p.n_spans <= 1)
+    if (p.family != Family::Scalar || seqlen <= 0)
         return 0;
-    // decay [c][S], hloc [c][S], h_in [S][c]
-    return (size_t)3 * (size_t)p.n_spans * (size_t)(batch * d_inner * d_state) * sizeof(float);
+    const size_t rows = (size_t)seqlen + (size_t)p.chunk;
+    const size_t bytes = (size_t)batch * rows * 2 * (size_t)d_state * sizeof(float);
+    return (bytes + 255) / 256 * 256;
+}
+
+size_t workspace_bytes_for(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                           const Plan &p)
+{
+    size_t n = staged_bytes_for(batch, seqlen, d_state, p);
+    if (p.n_spans > 1) // decay [c][S], hloc [c][S], h_in [S][c]
+        n += (size_t)3 * (size_t)p.n_spans * (size_t)(batch * d_inner * d_state) * sizeof(float);
+    return n;
 }
 
 mamba_status_t hip_status(hipError_t e) { return e == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP; }
@@ -154,7 +186,7 @@ size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d
     Plan p;
     if (make_plan(batch, seqlen, d_inner, d_state, opts, &p) != MAMBA_OK)
         return (size_t)-1;
-    return workspace_bytes_for(batch, d_inner, d_state, p);
+    return workspace_bytes_for(batch, seqlen, d_inner, d_state, p);
 }
 
 size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
@@ -209,7 +241,7 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
     const mamba_status_t ps = make_plan(batch, seqlen, d_inner, d_state, opts, &plan);
     if (ps != MAMBA_OK)
         return ps;
-    const size_t need = workspace_bytes_for(batch, d_inner, d_state, plan);
+    const size_t need = workspace_bytes_for(batch, seqlen, d_inner, d_state, plan);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return MAMBA_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 4))
@@ -264,13 +296,29 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
     L.chunk = plan.chunk;
     L.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
 
-    const bool rows = plan.family == Family::Rows;
     auto full = [&](const ScanLaunch &x) {
-        return rows ? launch_rows_full(x, st) : launch_scan_full(x, st);
+        switch (plan.family) {
+        case Family::Rows: return launch_rows_full(x, st);
+        case Family::Scalar: return launch_scalar_full(x, st);
+        default: return launch_scan_full(x, st);
+        }
     };
     auto end = [&](const ScanLaunch &x) {
-        return rows ? launch_rows_end(x, st) : launch_scan_end(x, st);
+        switch (plan.family) {
+        case Family::Rows: return launch_rows_end(x, st);
+        case Family::Scalar: return launch_scalar_end(x, st);
+        default: return launch_scan_end(x, st);
+        }
     };
+
+    char *ws_bytes = static_cast<char *>(workspace);
+    const size_t staged = staged_bytes_for(batch, seqlen, d_state, plan);
+    if (plan.family == Family::Scalar) {
+        L.bc_staged = reinterpret_cast<float *>(ws_bytes);
+        L.staged_rows = seqlen + plan.chunk;
+        if (launch_stage_bc(L, st) != hipSuccess)
+            return MAMBA_ERR_HIP;
+    }
 
     if (plan.n_spans == 1) {
         L.h_init = h0;
@@ -282,7 +330,7 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
 
     // ---- split sequence: span summaries, carry pass, full rescan ----
     const int64_t S = plan.n_spans;
-    float *ws = static_cast<float *>(workspace);
+    float *ws = reinterpret_cast<float *>(ws_bytes + staged);
     float *ws_decay = ws;
     float *ws_hloc = ws + S * bdn;
     float *ws_hin = ws + 2 * S * bdn;

@@ -26,9 +26,11 @@ struct ScanLaunch {
     int32_t launch_spans;
     int32_t waves, chunk;
     DType dtype;
+    float *bc_staged;           // scalar family: B/C repacked as fp32 [b][wave][row][2 NQ]
+    int64_t staged_rows;        // rows per (b, wave) in bc_staged (L plus one chunk of padding)
 };
 
-enum class Family : int { Auto = 0, Block = 1, Rows = 2 };
+enum class Family : int { Auto = 0, Block = 1, Rows = 2, Scalar = 3 };
 
 // The carry pass joining span end states: for every state column c = (b, d, n)
 // h_in[s][c] = state entering span s (s = 0 .. n_spans-1).
@@ -60,6 +62,11 @@ hipError_t launch_scan_end(const ScanLaunch &p, hipStream_t stream);
 // Barrier-free kernel: 16 channels per wave, state indices split across its DPP rows.
 hipError_t launch_rows_full(const ScanLaunch &p, hipStream_t stream);
 hipError_t launch_rows_end(const ScanLaunch &p, hipStream_t stream);
+// Scalar kernel: as the LDS-exchange kernel, with B/C staged as fp32 and read into SGPRs.
+bool scalar_variant_supported(int64_t d_state, int waves, int chunk);
+hipError_t launch_stage_bc(const ScanLaunch &p, hipStream_t stream);
+hipError_t launch_scalar_full(const ScanLaunch &p, hipStream_t stream);
+hipError_t launch_scalar_end(const ScanLaunch &p, hipStream_t stream);
 hipError_t launch_carry(const CarryLaunch &p, hipStream_t stream);
 hipError_t launch_state_update(const StepLaunch &p, hipStream_t stream);
 // h_last = h0 (or zeros when h0 is NULL), for empty sequences.

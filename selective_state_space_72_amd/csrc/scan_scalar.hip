@@ -1,0 +1,372 @@
+// Chunked selective-scan kernel for gfx950 with B and C delivered through SGPRs.
+//
+// Operation as in scan_kernels.hip (the selective scan of "Understanding Mamba",
+// aiattnstudio.link, sections 4.4 and 5.2).  Work decomposition as the block kernel
+// there -- one block is 64 consecutive channels (the 64 lanes of every wave), wave g owns
+// the state indices [g*NQ, (g+1)*NQ) -- but B_t and C_t, which are uniform across a
+// wave, never pass through LDS or the vector register file's broadcast paths:
+//   * a staging kernel first rewrites B and C as fp32 in a layout where the values one
+//     wave needs for one chunk of TC steps are contiguous: bcp[b][g][t][B(NQ), C(NQ)];
+//   * the scan kernel fetches a chunk's values with a few wide scalar loads, issued
+//     while the chunk's prologue computes, so the inner update uses SGPR operands:
+//     v_mul (Delta*A'), v_exp_f32, v_mul (Delta*u * B), v_fmac (recurrence), v_fmac
+//     (readout) -- all plain single-cycle-issue VALU forms, no DPP, no LDS reads for B/C.
+//   * LDS carries only what must cross waves: Delta and Delta*u per (step, channel),
+//     read once per chunk into registers, and the partial readouts, summed in a fixed
+//     order in the epilogue (bitwise deterministic).
+#include <type_traits>
+
+#include "device_math.h"
+#include "scan_common.h"
+
+namespace mambascan {
+namespace {
+
+typedef const __attribute__((address_space(4))) float *cfloat_ptr;
+
+template <int I0, int I1, typename F>
+__device__ __forceinline__ void for_c(F &&f)
+{
+    if constexpr (I0 < I1) {
+        f(std::integral_constant<int, I0>{});
+        for_c<I0 + 1, I1>(f);
+    }
+}
+
+// bcp[((b * NW + g) * Lp + t) * 2 NQ + {q, NQ + q}] = {B, C}[b, t, g * NQ + q] (0 past L).
+template <typename T, int N, int NW>
+__global__ void __launch_bounds__(256)
+stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, float *__restrict__ bcp,
+                int64_t L, int64_t Lp, int64_t total)
+{
+    constexpr int NQ = N / NW;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; // over batch * Lp * N
+    if (i >= total)
+        return;
+    const int n = (int)(i % N);
+    const int64_t t = (i / N) % Lp;
+    const int64_t b = i / ((int64_t)N * Lp);
+    const int g = n / NQ, q = n % NQ;
+    float bv = 0.0f, cv = 0.0f;
+    if (t < L) {
+        bv = load_val(Bm, (b * L + t) * N + n);
+        cv = load_val(Cm, (b * L + t) * N + n);
+    }
+    float *dst = bcp + ((b * NW + g) * Lp + t) * (2 * NQ);
+    dst[q] = bv;
+    dst[NQ + q] = cv;
+}
+
+template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED>
+__global__ void __launch_bounds__(64 * NW)
+scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
+                   const T *__restrict__ z, const float *__restrict__ bcp,
+                   const float *__restrict__ A, const float *__restrict__ Dv,
+                   const float *__restrict__ bias, const float *h_init, int64_t h_init_stride,
+                   T *__restrict__ y, float *h_last, float *__restrict__ ws_decay,
+                   float *__restrict__ ws_hloc, int64_t L, int64_t Lp, int32_t Dn,
+                   int64_t span_len, int32_t n_spans, int32_t first_span, int32_t tiles,
+                   int32_t batch)
+{
+    constexpr int NQ = N / NW;                 // state indices per lane
+    constexpr int KPL = (TC + NW - 1) / NW;    // prologue/epilogue channel-steps per lane
+    constexpr int BCW = 2 * NQ;                // B then C, per step, in bcp
+    constexpr bool gated = FULL && GATED;
+    static_assert(NQ >= 1 && N % NW == 0, "bad variant");
+
+    // Double-buffered by chunk parity so that one barrier per chunk suffices: chunk c's
+    // prologue writes s_dw[c&1]; after the barrier every wave finishes chunk c-1 from
+    // s_yp[(c-1)&1] and scans chunk c into s_yp[c&1].
+    __shared__ float2 s_dw[2][TC][64];               // (Delta, Delta*u) per (step, channel)
+    __shared__ float s_yp[FULL ? 2 : 1][TC][NW][64]; // partial readouts per (step, wave, channel)
+
+    const int lane = threadIdx.x & 63;
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    int bid = blockIdx.x;
+    const int tile = bid % tiles;
+    bid /= tiles;
+    const int b = bid % batch;
+    const int span = first_span + bid / batch;
+
+    const int64_t t_begin = (int64_t)span * span_len;
+    const int64_t t_end = min(t_begin + span_len, L);
+    const int d = tile * 64 + lane;
+    const bool dvalid = d < Dn;
+    const int dc = dvalid ? d : Dn - 1; // tail lanes compute on a valid channel, store nothing
+    const int n0 = g * NQ;
+
+    const int64_t col0 = ((int64_t)b * Dn + dc) * N + n0;
+    float a2[NQ], h[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        a2[q] = A[(int64_t)dc * N + n0 + q] * kLog2e; // exp(Delta*A) = exp2(Delta*A*log2 e)
+        h[q] = h_init ? h_init[span * h_init_stride + col0 + q] : 0.0f;
+    }
+    const float bias_d = bias ? bias[dc] : 0.0f;
+    const float D_d = Dv ? Dv[dc] : 0.0f;
+
+    const int64_t row_b = (int64_t)b * L;
+    const T *u_row = u + row_b * Dn + dc; // this lane's channel at t = 0
+    const T *d_row = delta + row_b * Dn + dc;
+    const T *z_row = gated ? z + row_b * Dn + dc : nullptr;
+    const float *bc_wave = bcp + ((int64_t)b * NW + g) * Lp * BCW; // this wave's (t, B/C) rows
+
+    // raw inputs of PD chunks in flight: u, delta, z for this lane's KPL channel-steps
+    T ru[PD][KPL], rd[PD][KPL], rz[PD][KPL];
+    auto fetch = [&](auto BUF, int64_t t0) {
+        constexpr int j = decltype(BUF)::value;
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) {
+            const int tl = g + k * NW;
+            const int64_t t = t0 + tl; // wave-uniform
+            if (tl < TC && t < t_end) {
+                ru[j][k] = u_row[t * Dn];
+                rd[j][k] = d_row[t * Dn];
+                if (gated)
+                    rz[j][k] = z_row[t * Dn];
+            }
+        }
+    };
+
+    float sum_dt = 0.0f;
+    // pending epilogue (the previous chunk): this lane's D*u, gate, first step, valid steps
+    float e_du[KPL], e_gz[KPL];
+    int64_t e_t0 = -1;
+    int e_nt = 0;
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+        e_du[k] = 0.0f;
+        e_gz[k] = 1.0f;
+    }
+
+    // fixed-order sum of the partial readouts of the pending chunk, D*u, gate, store
+    auto epilogue = [&](auto PAR) {
+        constexpr int pp = FULL ? decltype(PAR)::value : 0; // s_yp has one slot when !FULL
+        if (FULL && e_t0 >= 0) {
+#pragma unroll
+            for (int k = 0; k < KPL; ++k) {
+                const int tl = g + k * NW;
+                if (tl < e_nt && dvalid) {
+                    float s = s_yp[pp][tl][0][lane];
+#pragma unroll
+                    for (int w = 1; w < NW; ++w)
+                        s += s_yp[pp][tl][w][lane];
+                    store_val(y, (row_b + e_t0 + tl) * Dn + d, (s + e_du[k]) * e_gz[k]);
+                }
+            }
+        }
+    };
+
+    auto chunk = [&](auto BUF, int64_t t0) {
+        constexpr int j = decltype(BUF)::value; // ring slot; its low bit is the LDS parity
+        constexpr int pp = j & 1;
+        const int nt = (int)min((int64_t)TC, t_end - t0);
+
+        // ---- prologue: Delta and Delta*u once per (t, d) ----
+        float du[KPL], gz[KPL];
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) {
+            const int tl = g + k * NW;
+            float dl = 0.0f, w = 0.0f;
+            du[k] = 0.0f;
+            gz[k] = 1.0f;
+            if (tl < nt) {
+                const float uu = widen(ru[j][k]);
+                dl = softplus_f(widen(rd[j][k]) + bias_d);
+                w = dl * uu;
+                if (FULL) {
+                    du[k] = D_d * uu;
+                    if (gated)
+                        gz[k] = silu_f(widen(rz[j][k]));
+                }
+            }
+            if (tl < TC)
+                s_dw[pp][tl][lane] = make_float2(dl, w);
+        }
+        // this wave's B/C for the chunk: wave-uniform, contiguous -> scalar loads
+        const cfloat_ptr bcq = (cfloat_ptr)(bc_wave + t0 * BCW);
+        float bc[TC][BCW];
+#pragma unroll
+        for (int tl = 0; tl < TC; ++tl)
+#pragma unroll
+            for (int i = 0; i < BCW; ++i)
+                bc[tl][i] = (FULL || i < NQ) ? bcq[tl * BCW + i] : 0.0f;
+        if (t0 + PD * TC < t_end)
+            fetch(BUF, t0 + PD * TC);
+        __syncthreads();
+
+        // the previous chunk's readouts are complete in s_yp[pp ^ 1]
+        epilogue(std::integral_constant<int, pp ^ 1>{});
+
+        float2 dw[TC];
+#pragma unroll
+        for (int tl = 0; tl < TC; ++tl)
+            dw[tl] = s_dw[pp][tl][lane];
+
+        // ---- recurrence over the chunk ----
+        auto step = [&](int tl) {
+            float yp = 0.0f;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const float a = hw_exp2(dw[tl].x * a2[q]);
+                h[q] = __builtin_fmaf(a, h[q], dw[tl].y * bc[tl][q]);
+                if (FULL)
+                    yp = __builtin_fmaf(bc[tl][NQ + q], h[q], yp);
+            }
+            if (FULL)
+                s_yp[FULL ? pp : 0][tl][g][lane] = yp;
+            else
+                sum_dt += dw[tl].x;
+        };
+        if (nt == TC) {
+#pragma unroll
+            for (int tl = 0; tl < TC; ++tl)
+                step(tl);
+        } else {
+#pragma unroll
+            for (int tl = 0; tl < TC; ++tl)
+                if (tl < nt)
+                    step(tl);
+        }
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) {
+            e_du[k] = du[k];
+            e_gz[k] = gz[k];
+        }
+        e_t0 = t0;
+        e_nt = nt;
+    };
+
+    for_c<0, PD>([&](auto BUF) {
+        const int64_t t0 = t_begin + decltype(BUF)::value * TC;
+        if (t0 < t_end)
+            fetch(BUF, t0);
+    });
+    static_assert(PD % 2 == 0, "ring slots double as LDS parity");
+    int last_parity = 0;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += PD * TC) {
+        for_c<0, PD>([&](auto BUF) {
+            const int64_t tc = t0 + decltype(BUF)::value * TC; // block-uniform
+            if (tc < t_end) {
+                chunk(BUF, tc);
+                last_parity = decltype(BUF)::value & 1;
+            }
+        });
+    }
+    if (FULL) {
+        __syncthreads();
+        if (last_parity == 0)
+            epilogue(std::integral_constant<int, 0>{});
+        else
+            epilogue(std::integral_constant<int, 1>{});
+    }
+
+    if (!dvalid)
+        return;
+    const int64_t col = ((int64_t)b * Dn + d) * N + n0;
+    if (FULL) {
+        if (h_last && span == n_spans - 1) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                h_last[col + q] = h[q];
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            ws_decay[(col + q) * n_spans + span] = hw_exp2(a2[q] * sum_dt);
+            ws_hloc[(col + q) * n_spans + span] = h[q];
+        }
+    }
+}
+
+// (d_state, waves, chunk, prefetch depth): variants whose chunk of B/C (chunk * 2 *
+// d_state / waves floats) fits the scalar register file without spilling.
+#define MAMBA_SCALAR_VARIANTS(X) \
+    X(4, 4, 16, 2)               \
+    X(8, 4, 8, 2)                \
+    X(16, 8, 4, 2)               \
+    X(16, 8, 8, 2)               \
+    X(32, 8, 4, 2)
+
+template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED>
+hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
+{
+    const int32_t tiles = (int32_t)((p.d_inner + 63) / 64);
+    const int64_t blocks = (int64_t)tiles * p.batch * p.launch_spans;
+    if (blocks <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((scan_scalar_kernel<T, N, NW, TC, PD, FULL, GATED>),
+                       dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, (const T *)p.u,
+                       (const T *)p.delta, (const T *)p.z, p.bc_staged, p.A, p.D, p.bias,
+                       p.h_init, p.h_init_span_stride, (T *)p.y, p.h_last, p.ws_decay,
+                       p.ws_hloc, p.L, p.staged_rows, (int32_t)p.d_inner, p.span_len,
+                       p.n_spans, p.first_span, tiles, (int32_t)p.batch);
+    return hipGetLastError();
+}
+
+template <typename T, int N, int NW>
+hipError_t launch_stage(const ScanLaunch &p, hipStream_t stream)
+{
+    const int64_t total = p.batch * p.staged_rows * N;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL((stage_bc_kernel<T, N, NW>), dim3((uint32_t)blocks), dim3(256), 0,
+                       stream, (const T *)p.B, (const T *)p.C, p.bc_staged, p.L, p.staged_rows,
+                       total);
+    return hipGetLastError();
+}
+
+template <bool FULL>
+hipError_t launch_scalar_any(const ScanLaunch &p, hipStream_t stream)
+{
+    const bool g = FULL && p.z != nullptr;
+#define X(N_, W_, C_, P_)                                                                     \
+    if (p.d_state == N_ && p.waves == W_ && p.chunk == C_) {                                  \
+        if (p.dtype == DType::BF16)                                                           \
+            return g ? launch_scalar_variant<uint16_t, N_, W_, C_, P_, FULL, true>(p, stream) \
+                     : launch_scalar_variant<uint16_t, N_, W_, C_, P_, FULL, false>(p, stream); \
+        return g ? launch_scalar_variant<float, N_, W_, C_, P_, FULL, true>(p, stream)        \
+                 : launch_scalar_variant<float, N_, W_, C_, P_, FULL, false>(p, stream);      \
+    }
+    MAMBA_SCALAR_VARIANTS(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+} // namespace
+
+bool scalar_variant_supported(int64_t d_state, int waves, int chunk)
+{
+#define X(N_, W_, C_, P_)                                        \
+    if (d_state == N_ && waves == W_ && chunk == C_) return true;
+    MAMBA_SCALAR_VARIANTS(X)
+#undef X
+    return false;
+}
+
+hipError_t launch_stage_bc(const ScanLaunch &p, hipStream_t stream)
+{
+#define X(N_, W_, C_, P_)                                               \
+    if (p.d_state == N_ && p.waves == W_) {                             \
+        if (p.dtype == DType::BF16)                                     \
+            return launch_stage<uint16_t, N_, W_>(p, stream);           \
+        return launch_stage<float, N_, W_>(p, stream);                  \
+    }
+    MAMBA_SCALAR_VARIANTS(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_scalar_full(const ScanLaunch &p, hipStream_t stream)
+{
+    return launch_scalar_any<true>(p, stream);
+}
+
+hipError_t launch_scalar_end(const ScanLaunch &p, hipStream_t stream)
+{
+    return launch_scalar_any<false>(p, stream);
+}
+
+} // namespace mambascan

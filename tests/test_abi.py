@@ -129,8 +129,12 @@ def test_scan_workspace_rules(lib):
     assert scan(lib, batch=1, L=131072, Dn=2048, u=BASE, delta=BASE + 600 * MB,
                 B=BASE + 1200 * MB, C=BASE + 1300 * MB, A=BASE + 1400 * MB,
                 y=BASE + 1500 * MB, ws=BASE + 1500 * MB, ws_bytes=n) == ALIAS
-    # many channels: no split, no workspace
-    assert lib.mamba_scan_fwd_workspace_size(8, 4096, 5120, 16) == 0
+    # many channels: no split; the scalar-B/C kernel stages B and C as fp32 with one
+    # chunk of padding rows: batch * (L + 8) * 2 * d_state * 4 bytes
+    assert lib.mamba_scan_fwd_workspace_size(8, 4096, 5120, 16) == 8 * (4096 + 8) * 2 * 16 * 4
+    # the LDS-exchange kernel without a split needs none
+    assert lib.mamba_scan_fwd_workspace_size_ex(8, 4096, 5120, 16,
+                                                ctypes.byref(ms.ScanOpts(0, 0, 1, 1))) == 0
     assert lib.mamba_scan_fwd_workspace_size(-1, 4, 4, 16) == ctypes.c_size_t(-1).value
     assert lib.mamba_scan_fwd_workspace_size(1, 4, 4, 12) == ctypes.c_size_t(-1).value
 
@@ -141,7 +145,11 @@ def test_scan_rejects_bad_options(lib):
     assert scan(lib, opts=ms.ScanOpts(0, 0, 65, 0)) == UNSUP      # spans
     assert scan(lib, opts=ms.ScanOpts(0, 0, -2, 0)) == UNSUP
     assert scan(lib, N=4, opts=ms.ScanOpts(16, 8, 0, 0)) == UNSUP  # 8 waves need N >= 8
-    assert scan(lib, opts=ms.ScanOpts(0, 0, 0, 3)) == UNSUP       # kernel family
+    assert scan(lib, opts=ms.ScanOpts(0, 0, 0, 4)) == UNSUP       # kernel family
+    assert scan(lib, opts=ms.ScanOpts(0, 0, 0, -1)) == UNSUP
+    assert scan(lib, N=64, opts=ms.ScanOpts(0, 0, 0, 3)) == UNSUP  # no scalar d_state 64
+    # the scalar-B/C kernel always stages B/C in the workspace
+    assert scan(lib, opts=ms.ScanOpts(0, 0, 0, 3)) == WS
     assert scan(lib, opts=ms.ScanOpts(16, 0, 0, 2)) == UNSUP      # rows: no chunk option
 
 

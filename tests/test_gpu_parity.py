@@ -128,7 +128,9 @@ def test_c5_decode_1024_chained_steps():
 VARIANTS = [dict(waves=8, chunk_len=16), dict(waves=8, chunk_len=8), dict(waves=4, chunk_len=16),
             dict(waves=4, chunk_len=32), dict(n_spans=2), dict(n_spans=7), dict(n_spans=64),
             dict(waves=4, chunk_len=16, n_spans=5), dict(kernel="block"), dict(kernel="rows"),
-            dict(kernel="rows", n_spans=3), dict(kernel="rows", n_spans=64)]
+            dict(kernel="rows", n_spans=3), dict(kernel="rows", n_spans=64),
+            dict(kernel="scalar"), dict(kernel="scalar", chunk_len=4),
+            dict(kernel="scalar", n_spans=5), dict(kernel="scalar", n_spans=64)]
 
 
 @pytest.mark.parametrize("opts", VARIANTS, ids=[str(v) for v in VARIANTS])
@@ -138,10 +140,12 @@ def test_variants_agree_with_oracle(opts):
     full_check(f"variant {opts}", inp, **opts)
 
 
-@pytest.mark.parametrize("kernel", ["block", "rows"])
+@pytest.mark.parametrize("kernel", ["block", "rows", "scalar"])
 @pytest.mark.parametrize("n", [4, 8, 16, 32, 64])
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
 def test_other_state_sizes(n, dtype, kernel):
+    if kernel == "scalar" and n == 64:
+        pytest.skip("the scalar kernel family has no d_state 64 variant")
     import dataclasses
     cfg = dataclasses.replace(synth.CONFIGS["c3"], d_state=n, dtype=dtype, h0=True)
     inp = synth.make_scan_inputs(cfg, batch=2, seqlen=333, d_inner=72, seed=20 + n)
@@ -149,7 +153,7 @@ def test_other_state_sizes(n, dtype, kernel):
     full_check(f"N={n} {dtype} {kernel} split", inp, n_spans=3, kernel=kernel)
 
 
-@pytest.mark.parametrize("kernel", ["block", "rows"])
+@pytest.mark.parametrize("kernel", ["block", "rows", "scalar"])
 @pytest.mark.parametrize("shape", [(1, 1, 1), (1, 1, 64), (2, 7, 65), (3, 17, 130),
                                    (1, 4097, 64), (5, 129, 40), (2, 6, 17)])
 def test_ragged_shapes_fp32(shape, kernel):
@@ -175,7 +179,7 @@ def test_empty_sequence_returns_h0():
     assert torch.count_nonzero(h) == 0
 
 
-@pytest.mark.parametrize("kernel", ["block", "rows"])
+@pytest.mark.parametrize("kernel", ["block", "rows", "scalar"])
 @pytest.mark.parametrize("n_spans", [1, 4])
 def test_in_place_state_continuation(n_spans, kernel):
     """h_last may be h0 itself: scanning two halves in place equals one scan."""
@@ -199,7 +203,8 @@ def test_in_place_state_continuation(n_spans, kernel):
 def test_deterministic():
     inp = synth.make_scan_inputs(synth.CONFIGS["c2"], batch=2, seqlen=700, d_inner=256, seed=4)
     di = DevInputs(inp)
-    for opts in (dict(), dict(n_spans=3), dict(kernel="rows"), dict(kernel="rows", n_spans=3)):
+    for opts in (dict(), dict(n_spans=3), dict(kernel="rows"), dict(kernel="rows", n_spans=3),
+                 dict(kernel="scalar"), dict(kernel="scalar", n_spans=3)):
         y1, h1 = di.run(**opts)
         y2, h2 = di.run(**opts)
         assert torch.equal(y1, y2) and torch.equal(h1, h2)
