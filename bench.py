@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--only-main", action="store_true", help="alias of --no-extra --no-cpu-baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 512 MiB device copy three times (the reference kernel for "
+                         "scaling FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -269,6 +272,13 @@ def main():
             "roofline": roof}
     del case
     torch.cuda.empty_cache()
+    if args.copy_calibration:
+        src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_extra:
         log("bench: other workloads")
         line["other_workloads"] = extra_workloads(dev, flush, args.steps)

@@ -99,8 +99,13 @@ typedef enum {
  *               handles d_state/waves state indices of 64 channels.
  *   n_spans   : the sequence is split into n_spans spans scanned in parallel
  *               and joined by a carry pass (1..64; 1 = no split).
- *   kernel    : MAMBA_KERNEL_* family.
- * Every supported setting gives the same result up to float32 rounding. */
+ *   kernel    : MAMBA_KERNEL_* family.  AUTO picks SCALAR when the grid fills the
+ *               device and d_state <= 32, else ROWS; with chunk_len or waves set,
+ *               AUTO picks SCALAR if it has that shape, else BLOCK.  SCALAR needs
+ *               span length x d_inner x 4 < 2^31 (it raises an automatic span count
+ *               to get there; a fixed n_spans that misses it is unsupported).
+ * Every supported setting gives the same result up to float32 rounding; an
+ * unsupported one makes the call return MAMBA_ERR_UNSUPPORTED. */
 typedef struct {
     int32_t chunk_len;
     int32_t waves;

@@ -22,6 +22,18 @@ Family auto_family(int64_t batch, int64_t d_inner, int64_t d_state, int cus)
     return Family::Rows;
 }
 
+// Scalar-family defaults: (waves, chunk) = (4, 8), (8, 8), (8, 8), (8, 4) for d_state 4..32.
+int scalar_default_waves(int64_t d_state) { return d_state >= 8 ? 8 : 4; }
+int scalar_default_chunk(int64_t d_state) { return d_state == 32 ? 4 : 8; }
+
+// The scalar kernel addresses one span of one batch row of an activation tensor with
+// 32-bit byte offsets: span length x d_inner x 4 bytes (fp32, the larger element) must
+// stay below 2^31.
+bool scalar_span_ok(int64_t span_len, int64_t d_inner)
+{
+    return d_inner <= INT32_MAX / 4 && span_len <= (int64_t)(INT32_MAX / 4) / d_inner;
+}
+
 struct Range {
     uintptr_t lo, hi; // [lo, hi)
 };
@@ -72,7 +84,15 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     Plan p{};
     const int cus = cu_count();
     const int fam = opts ? opts->kernel : MAMBA_KERNEL_AUTO;
-    const Family autof = auto_family(batch, d_inner, d_state, cus);
+    Family autof = auto_family(batch, d_inner, d_state, cus);
+    if (autof == Family::Scalar && !scalar_span_ok(seqlen, d_inner))
+        autof = Family::Rows;
+    if (fam == MAMBA_KERNEL_AUTO && opts && (opts->waves || opts->chunk_len)) {
+        // an explicit block shape: the scalar family if it has it, else the block family
+        const int w = opts->waves ? opts->waves : scalar_default_waves(d_state);
+        const int c = opts->chunk_len ? opts->chunk_len : scalar_default_chunk(d_state);
+        autof = scalar_variant_supported(d_state, w, c) ? Family::Scalar : Family::Block;
+    }
     if (fam == MAMBA_KERNEL_ROWS || (fam == MAMBA_KERNEL_AUTO && autof == Family::Rows)) {
         if ((opts && (opts->waves || opts->chunk_len)))
             return MAMBA_ERR_UNSUPPORTED; // fixed shape: 4 waves x 16 channels, 4-step blocks
@@ -82,14 +102,11 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     } else if (fam == MAMBA_KERNEL_SCALAR ||
                (fam == MAMBA_KERNEL_AUTO && autof == Family::Scalar)) {
         p.family = Family::Scalar;
-        // defaults: (waves, chunk) = (4, 16), (4, 8), (8, 8), (8, 4) for d_state 4..32
-        const int dw = d_state >= 16 ? 8 : 4;
-        const int dc = d_state == 4 ? 16 : (d_state == 32 ? 4 : 8);
-        p.waves = opts && opts->waves ? opts->waves : dw;
-        p.chunk = opts && opts->chunk_len ? opts->chunk_len : dc;
+        p.waves = opts && opts->waves ? opts->waves : scalar_default_waves(d_state);
+        p.chunk = opts && opts->chunk_len ? opts->chunk_len : scalar_default_chunk(d_state);
         if (!scalar_variant_supported(d_state, p.waves, p.chunk))
             return MAMBA_ERR_UNSUPPORTED;
-    } else if (fam == MAMBA_KERNEL_BLOCK) {
+    } else if (fam == MAMBA_KERNEL_BLOCK || (fam == MAMBA_KERNEL_AUTO && autof == Family::Block)) {
         p.family = Family::Block;
         p.waves = opts && opts->waves ? opts->waves : default_waves(d_state);
         p.chunk = opts && opts->chunk_len ? opts->chunk_len : default_chunk(d_state, p.waves);
@@ -98,8 +115,9 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     } else {
         return MAMBA_ERR_UNSUPPORTED;
     }
+    const bool fixed_spans = opts && opts->n_spans;
     int spans = 1;
-    if (opts && opts->n_spans) {
+    if (fixed_spans) {
         if (opts->n_spans < 1 || opts->n_spans > 64)
             return MAMBA_ERR_UNSUPPORTED;
         spans = opts->n_spans;
@@ -119,11 +137,19 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     }
     if (seqlen <= 0)
         spans = 1;
-    // span length: a multiple of the chunk so that only the last span has a partial chunk
-    int64_t len = (seqlen + spans - 1) / spans;
-    len = (len + p.chunk - 1) / p.chunk * p.chunk;
-    if (len < p.chunk)
-        len = p.chunk;
+    int64_t len = 0;
+    for (;;) {
+        // span length: a multiple of the chunk so that only the last span has a partial chunk
+        len = (seqlen + spans - 1) / spans;
+        len = (len + p.chunk - 1) / p.chunk * p.chunk;
+        if (len < p.chunk)
+            len = p.chunk;
+        if (p.family != Family::Scalar || scalar_span_ok(len, d_inner))
+            break;
+        if (fixed_spans || spans >= 64)
+            return MAMBA_ERR_UNSUPPORTED; // span too large for the scalar kernel's addressing
+        spans *= 2;
+    }
     spans = (int)((seqlen + len - 1) / len);
     if (spans < 1)
         spans = 1;

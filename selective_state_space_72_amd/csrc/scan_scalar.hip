@@ -57,6 +57,37 @@ stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, float *__res
     dst[NQ + q] = cv;
 }
 
+// Activations of one (batch row, span) are read and written through buffer resources
+// based at the span's first time step: the lane's channel is a 32-bit vector offset and
+// the step a 32-bit scalar offset, so an access needs no 64-bit vector address
+// arithmetic.  The planner keeps a span's bytes (span length x d_inner x element size)
+// below 2^31.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000; // gfx9 raw-buffer descriptor word 3
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint16_t buf_load(rsrc_t r, uint32_t vo, uint32_t so, uint16_t *)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, vo, so, 0);
+}
+__device__ __forceinline__ float buf_load(rsrc_t r, uint32_t vo, uint32_t so, float *)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, vo, so, 0));
+}
+__device__ __forceinline__ void buf_store(float v, rsrc_t r, uint32_t vo, uint32_t so, uint16_t *)
+{
+    // round to nearest even, as store_val
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)),
+                                          r, vo, so, 0);
+}
+__device__ __forceinline__ void buf_store(float v, rsrc_t r, uint32_t vo, uint32_t so, float *)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, vo, so, 0);
+}
+
 template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED>
 __global__ void __launch_bounds__(64 * NW)
 scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
@@ -73,6 +104,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     constexpr int BCW = 2 * NQ;                // B then C, per step, in bcp
     constexpr bool gated = FULL && GATED;
     static_assert(NQ >= 1 && N % NW == 0, "bad variant");
+    static_assert(PD % 2 == 0, "ring slots double as chunk parity");
 
     // Double-buffered by chunk parity so that one barrier per chunk suffices: chunk c's
     // prologue writes s_dw[c&1]; after the barrier every wave finishes chunk c-1 from
@@ -106,33 +138,58 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     const float bias_d = bias ? bias[dc] : 0.0f;
     const float D_d = Dv ? Dv[dc] : 0.0f;
 
-    const int64_t row_b = (int64_t)b * L;
-    const T *u_row = u + row_b * Dn + dc; // this lane's channel at t = 0
-    const T *d_row = delta + row_b * Dn + dc;
-    const T *z_row = gated ? z + row_b * Dn + dc : nullptr;
-    const float *bc_wave = bcp + ((int64_t)b * NW + g) * Lp * BCW; // this wave's (t, B/C) rows
+    // bytes per time step of one batch row; span bytes stay below 2^31 (planner)
+    const uint32_t step_bytes = (uint32_t)Dn * (uint32_t)sizeof(T);
+    const uint32_t vo_in = (uint32_t)dc * (uint32_t)sizeof(T);
+    const uint32_t vo_out = (uint32_t)d * (uint32_t)sizeof(T);
+    const int64_t span0 = ((int64_t)b * L + t_begin) * step_bytes; // byte offset of (b, t_begin)
+    // local time: 0 .. n_loc - 1 within this span (32-bit, as are all loop quantities)
+    const int n_loc = (int)(t_end - t_begin);
+    const uint32_t span_bytes = (uint32_t)n_loc * step_bytes;
+    const rsrc_t r_u = make_rsrc(reinterpret_cast<const char *>(u) + span0, span_bytes);
+    const rsrc_t r_d = make_rsrc(reinterpret_cast<const char *>(delta) + span0, span_bytes);
+    const rsrc_t r_z = gated ? make_rsrc(reinterpret_cast<const char *>(z) + span0, span_bytes)
+                             : r_u;
+    const rsrc_t r_y = FULL ? make_rsrc(reinterpret_cast<const char *>(y) + span0, span_bytes)
+                            : r_u;
+    // this wave's (t, B/C) rows from the span's first step
+    const float *bc_span = bcp + (((int64_t)b * NW + g) * Lp + t_begin) * BCW;
 
     // raw inputs of PD chunks in flight: u, delta, z for this lane's KPL channel-steps
     T ru[PD][KPL], rd[PD][KPL], rz[PD][KPL];
-    auto fetch = [&](auto BUF, int64_t t0) {
+    auto fetch = [&](auto BUF, int t0) {
         constexpr int j = decltype(BUF)::value;
 #pragma unroll
         for (int k = 0; k < KPL; ++k) {
             const int tl = g + k * NW;
-            const int64_t t = t0 + tl; // wave-uniform
-            if (tl < TC && t < t_end) {
-                ru[j][k] = u_row[t * Dn];
-                rd[j][k] = d_row[t * Dn];
+            const int t = t0 + tl;
+            if (tl < TC && t < n_loc) { // wave-uniform
+                const uint32_t so = (uint32_t)t * step_bytes;
+                ru[j][k] = buf_load(r_u, vo_in, so, (T *)nullptr);
+                rd[j][k] = buf_load(r_d, vo_in, so, (T *)nullptr);
                 if (gated)
-                    rz[j][k] = z_row[t * Dn];
+                    rz[j][k] = buf_load(r_z, vo_in, so, (T *)nullptr);
             }
         }
+    };
+
+    // B/C of one chunk in scalar registers.  Chunk c + 1's values are requested as soon
+    // as chunk c's recurrence has consumed chunk c's, so their latency overlaps the next
+    // prologue and the barrier (whose LDS wait drains them anyway).
+    float bcs[TC][BCW];
+    auto load_bc = [&](int t0) {
+        const cfloat_ptr q = (cfloat_ptr)(bc_span + (int64_t)t0 * BCW);
+#pragma unroll
+        for (int tl = 0; tl < TC; ++tl)
+#pragma unroll
+            for (int i = 0; i < BCW; ++i)
+                bcs[tl][i] = (FULL || i < NQ) ? q[tl * BCW + i] : 0.0f;
     };
 
     float sum_dt = 0.0f;
     // pending epilogue (the previous chunk): this lane's D*u, gate, first step, valid steps
     float e_du[KPL], e_gz[KPL];
-    int64_t e_t0 = -1;
+    int e_t0 = -1;
     int e_nt = 0;
 #pragma unroll
     for (int k = 0; k < KPL; ++k) {
@@ -140,28 +197,38 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
         e_gz[k] = 1.0f;
     }
 
-    // fixed-order sum of the partial readouts of the pending chunk, D*u, gate, store
-    auto epilogue = [&](auto PAR) {
+    // fixed-order sum of the pending chunk's partial readouts (LDS reads only)
+    auto epilogue_sum = [&](auto PAR, float (&s)[KPL]) {
         constexpr int pp = FULL ? decltype(PAR)::value : 0; // s_yp has one slot when !FULL
-        if (FULL && e_t0 >= 0) {
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) {
+            const int tl = g + k * NW;
+            s[k] = 0.0f;
+            if (FULL && tl < TC) {
+                s[k] = s_yp[pp][tl][0][lane];
+#pragma unroll
+                for (int w = 1; w < NW; ++w)
+                    s[k] += s_yp[pp][tl][w][lane];
+            }
+        }
+    };
+    // D*u, gate and store of the pending chunk
+    auto epilogue_store = [&](const float (&s)[KPL]) {
+        if (FULL && e_t0 >= 0 && dvalid) {
 #pragma unroll
             for (int k = 0; k < KPL; ++k) {
                 const int tl = g + k * NW;
-                if (tl < e_nt && dvalid) {
-                    float s = s_yp[pp][tl][0][lane];
-#pragma unroll
-                    for (int w = 1; w < NW; ++w)
-                        s += s_yp[pp][tl][w][lane];
-                    store_val(y, (row_b + e_t0 + tl) * Dn + d, (s + e_du[k]) * e_gz[k]);
-                }
+                if (tl < e_nt)
+                    buf_store((s[k] + e_du[k]) * e_gz[k], r_y, vo_out,
+                              (uint32_t)(e_t0 + tl) * step_bytes, (T *)nullptr);
             }
         }
     };
 
-    auto chunk = [&](auto BUF, int64_t t0) {
-        constexpr int j = decltype(BUF)::value; // ring slot; its low bit is the LDS parity
+    auto chunk = [&](auto BUF, int t0) {
+        constexpr int j = decltype(BUF)::value; // ring slot; its low bit is the chunk parity
         constexpr int pp = j & 1;
-        const int nt = (int)min((int64_t)TC, t_end - t0);
+        const int nt = min(TC, n_loc - t0);
 
         // ---- prologue: Delta and Delta*u once per (t, d) ----
         float du[KPL], gz[KPL];
@@ -184,25 +251,18 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
             if (tl < TC)
                 s_dw[pp][tl][lane] = make_float2(dl, w);
         }
-        // this wave's B/C for the chunk: wave-uniform, contiguous -> scalar loads
-        const cfloat_ptr bcq = (cfloat_ptr)(bc_wave + t0 * BCW);
-        float bc[TC][BCW];
-#pragma unroll
-        for (int tl = 0; tl < TC; ++tl)
-#pragma unroll
-            for (int i = 0; i < BCW; ++i)
-                bc[tl][i] = (FULL || i < NQ) ? bcq[tl * BCW + i] : 0.0f;
-        if (t0 + PD * TC < t_end)
+        if (t0 + PD * TC < n_loc)
             fetch(BUF, t0 + PD * TC);
         __syncthreads();
 
-        // the previous chunk's readouts are complete in s_yp[pp ^ 1]
-        epilogue(std::integral_constant<int, pp ^ 1>{});
-
+        // LDS reads: the previous chunk's partial readouts and this chunk's (Delta, Delta*u)
+        float es[KPL];
+        epilogue_sum(std::integral_constant<int, pp ^ 1>{}, es);
         float2 dw[TC];
 #pragma unroll
         for (int tl = 0; tl < TC; ++tl)
             dw[tl] = s_dw[pp][tl][lane];
+        epilogue_store(es);
 
         // ---- recurrence over the chunk ----
         auto step = [&](int tl) {
@@ -210,9 +270,9 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const float a = hw_exp2(dw[tl].x * a2[q]);
-                h[q] = __builtin_fmaf(a, h[q], dw[tl].y * bc[tl][q]);
+                h[q] = __builtin_fmaf(a, h[q], dw[tl].y * bcs[tl][q]);
                 if (FULL)
-                    yp = __builtin_fmaf(bc[tl][NQ + q], h[q], yp);
+                    yp = __builtin_fmaf(bcs[tl][NQ + q], h[q], yp);
             }
             if (FULL)
                 s_yp[FULL ? pp : 0][tl][g][lane] = yp;
@@ -229,6 +289,10 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                 if (tl < nt)
                     step(tl);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (t0 + TC < n_loc)
+            load_bc(t0 + TC);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < KPL; ++k) {
             e_du[k] = du[k];
@@ -239,16 +303,17 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     };
 
     for_c<0, PD>([&](auto BUF) {
-        const int64_t t0 = t_begin + decltype(BUF)::value * TC;
-        if (t0 < t_end)
+        const int t0 = decltype(BUF)::value * TC;
+        if (t0 < n_loc)
             fetch(BUF, t0);
     });
-    static_assert(PD % 2 == 0, "ring slots double as LDS parity");
+    if (n_loc > 0)
+        load_bc(0);
     int last_parity = 0;
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += PD * TC) {
+    for (int t0 = 0; t0 < n_loc; t0 += PD * TC) {
         for_c<0, PD>([&](auto BUF) {
-            const int64_t tc = t0 + decltype(BUF)::value * TC; // block-uniform
-            if (tc < t_end) {
+            const int tc = t0 + decltype(BUF)::value * TC; // block-uniform
+            if (tc < n_loc) {
                 chunk(BUF, tc);
                 last_parity = decltype(BUF)::value & 1;
             }
@@ -256,10 +321,12 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     }
     if (FULL) {
         __syncthreads();
+        float es[KPL];
         if (last_parity == 0)
-            epilogue(std::integral_constant<int, 0>{});
+            epilogue_sum(std::integral_constant<int, 0>{}, es);
         else
-            epilogue(std::integral_constant<int, 1>{});
+            epilogue_sum(std::integral_constant<int, 1>{}, es);
+        epilogue_store(es);
     }
 
     if (!dvalid)
@@ -283,8 +350,8 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
 // (d_state, waves, chunk, prefetch depth): variants whose chunk of B/C (chunk * 2 *
 // d_state / waves floats) fits the scalar register file without spilling.
 #define MAMBA_SCALAR_VARIANTS(X) \
-    X(4, 4, 16, 2)               \
-    X(8, 4, 8, 2)                \
+    X(4, 4, 8, 2)                \
+    X(8, 8, 8, 2)                \
     X(16, 8, 4, 2)               \
     X(16, 8, 8, 2)               \
     X(32, 8, 4, 2)

@@ -153,6 +153,34 @@ def test_scan_rejects_bad_options(lib):
     assert scan(lib, opts=ms.ScanOpts(16, 0, 0, 2)) == UNSUP      # rows: no chunk option
 
 
+def test_scalar_span_addressing_limit(lib):
+    ws = lambda *a, o: lib.mamba_scan_fwd_workspace_size_ex(*a, ctypes.byref(o))  # noqa: E731
+    bad = ctypes.c_size_t(-1).value
+    # one span of 2^20 steps x 1024 channels x 4 bytes = 4 GiB: beyond 32-bit offsets
+    assert ws(1, 1 << 20, 1024, 16, o=ms.ScanOpts(0, 0, 1, 3)) == bad
+    # an automatic span count (1 here: 64 batch rows fill the device) is raised until a
+    # span fits: 4 spans of 1 GiB
+    staged = 64 * (((1 << 20) + 8) * 2 * 16 * 4)
+    assert ws(64, 1 << 20, 1024, 16, o=ms.ScanOpts(0, 0, 0, 3)) == \
+        staged + 3 * 4 * 64 * 1024 * 16 * 4
+    # the automatic family avoids the scalar kernel there (no staged B/C in the workspace)
+    assert ws(64, 1 << 20, 1024, 16, o=ms.ScanOpts(0, 0, 0, 0)) == 0
+    # below the limit a single span is allowed
+    assert ws(1, (1 << 19) - 8, 1024, 16, o=ms.ScanOpts(0, 0, 1, 3)) == (1 << 19) * 2 * 16 * 4
+    assert ws(1, 1 << 19, 1024, 16, o=ms.ScanOpts(0, 0, 1, 3)) == bad
+
+
+def test_auto_family_with_block_shape(lib):
+    ws = lambda *a, o: lib.mamba_scan_fwd_workspace_size_ex(*a, ctypes.byref(o))  # noqa: E731
+    small = (3, 1000, 200, 16)
+    # a shape the scalar family has -> scalar, which always stages B/C (non-zero workspace)
+    assert ws(*small, o=ms.ScanOpts(8, 8, 1, 0)) == 3 * (1000 + 8) * 2 * 16 * 4
+    # shapes only the block family has -> block, no workspace without a split
+    assert ws(*small, o=ms.ScanOpts(16, 8, 1, 0)) == 0
+    assert ws(*small, o=ms.ScanOpts(32, 4, 1, 0)) == 0
+    assert ws(*small, o=ms.ScanOpts(0, 4, 1, 0)) == 0  # no scalar 4-wave d_state-16 shape
+
+
 def step(lib, *, h=BASE, u=BASE + 100 * MB, delta=BASE + 110 * MB, A=BASE + 120 * MB,
          B=BASE + 130 * MB, C=BASE + 131 * MB, D=None, z=None, bias=None, y=BASE + 140 * MB,
          batch=4, Dn=256, N=16, dtype=BF16):
