@@ -115,11 +115,13 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     const int lane = threadIdx.x & 63;
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
+    // Batch row fastest: consecutive blocks go to different XCDs, so with 8 batch rows on
+    // 8 XCDs each XCD's L2 holds the staged B/C of one row only.
     int bid = blockIdx.x;
-    const int tile = bid % tiles;
-    bid /= tiles;
     const int b = bid % batch;
-    const int span = first_span + bid / batch;
+    bid /= batch;
+    const int tile = bid % tiles;
+    const int span = first_span + bid / tiles;
 
     const int64_t t_begin = (int64_t)span * span_len;
     const int64_t t_end = min(t_begin + span_len, L);
