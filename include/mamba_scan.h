@@ -104,6 +104,13 @@ typedef enum {
  *               AUTO picks SCALAR if it has that shape, else BLOCK.  SCALAR needs
  *               span length x d_inner x 4 < 2^31 (it raises an automatic span count
  *               to get there; a fixed n_spans that misses it is unsupported).
+ *   relay     : SCALAR kernel, single span: the (batch row, 64-channel tile)
+ *               units left over after filling every compute unit equally are
+ *               split in time into parts run by different blocks, each part
+ *               handing its final state to the next (no recomputation).
+ *               0 = auto (two parts, when it evens out the load), 1 = off,
+ *               2..8 = that many equal parts (when no units are left over, every
+ *               unit is split; for testing).
  * Every supported setting gives the same result up to float32 rounding; an
  * unsupported one makes the call return MAMBA_ERR_UNSUPPORTED. */
 typedef struct {
@@ -111,6 +118,7 @@ typedef struct {
     int32_t waves;
     int32_t n_spans;
     int32_t kernel;
+    int32_t relay;
 } mamba_scan_opts_t;
 
 /* Returns 1 if d_state is supported by this build, else 0. */

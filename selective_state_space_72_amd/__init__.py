@@ -47,7 +47,8 @@ KERNELS = {"auto": MAMBA_KERNEL_AUTO, "block": MAMBA_KERNEL_BLOCK, "rows": MAMBA
 
 class ScanOpts(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int32), ("waves", ctypes.c_int32),
-                ("n_spans", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+                ("n_spans", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("relay", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -134,17 +135,17 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _opts(chunk_len=0, waves=0, n_spans=0, kernel="auto"):
+def _opts(chunk_len=0, waves=0, n_spans=0, kernel="auto", relay=0):
     if kernel not in KERNELS:
         raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
-    return ScanOpts(int(chunk_len), int(waves), int(n_spans), KERNELS[kernel])
+    return ScanOpts(int(chunk_len), int(waves), int(n_spans), KERNELS[kernel], int(relay))
 
 
 def mamba_scan_fwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state: int,
                                   chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
-                                  kernel: str = "auto") -> int:
+                                  kernel: str = "auto", relay: int = 0) -> int:
     lib = load_library()
-    o = _opts(chunk_len, waves, n_spans, kernel)
+    o = _opts(chunk_len, waves, n_spans, kernel, relay)
     n = lib.mamba_scan_fwd_workspace_size_ex(batch, seqlen, d_inner, d_state, ctypes.byref(o))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes or options for mamba_scan_fwd")
@@ -154,7 +155,7 @@ def mamba_scan_fwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state
 def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
                    return_last_state: bool = False, *, out=None, h_last_out=None,
                    chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
-                   kernel: str = "auto", workspace=None) -> Tuple:
+                   kernel: str = "auto", relay: int = 0, workspace=None) -> Tuple:
     """Selective scan over (batch, seqlen, d_inner); see include/mamba_scan.h.
 
     Returns (y, h_last) -- h_last is None unless return_last_state (or h_last_out).
@@ -187,7 +188,7 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
         h_last = torch.empty((batch, d_inner, d_state), dtype=f32, device=dev)
     p_hl = _ptr(h_last, "h_last_out", (batch, d_inner, d_state), f32, dev)
 
-    opts = _opts(chunk_len, waves, n_spans, kernel)
+    opts = _opts(chunk_len, waves, n_spans, kernel, relay)
     need = lib.mamba_scan_fwd_workspace_size_ex(batch, seqlen, d_inner, d_state,
                                                 ctypes.byref(opts))
     if need == ctypes.c_size_t(-1).value:

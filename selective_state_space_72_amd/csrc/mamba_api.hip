@@ -73,6 +73,9 @@ struct Plan {
     Family family;
     int waves, chunk, n_spans;
     int64_t span_len;
+    int relay_parts;      // 1: no relay
+    int64_t relay_tiles;  // relayed (batch row, tile) units
+    int64_t relay_len;    // steps per relay part (a multiple of chunk)
 };
 
 // Launch plan.  Channel tiles of 64 lanes x `waves` waves are the unit of parallel work;
@@ -155,6 +158,43 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
         spans = 1;
     p.n_spans = spans;
     p.span_len = len;
+
+    // Relay: with U units over `cus` compute units, U mod cus units would make a last,
+    // mostly idle round.  Splitting each of them in time into two halves, the first run in
+    // the first round and the second in the last round (workgroups are dispatched in index
+    // order, round-robin over compute units), gives those compute units half a unit each
+    // instead of a whole one (measured at 8 x 4096 x 5120: 747 us against 816 us; a 5/8
+    // first part gave 784 us).  More than two parts would chain inside the last round.
+    // Forced part counts (testing) use equal parts.
+    p.relay_parts = 1;
+    const int want_relay = opts ? opts->relay : 0;
+    if (want_relay < 0 || want_relay > 8)
+        return MAMBA_ERR_UNSUPPORTED;
+    if (want_relay >= 2 && (p.family != Family::Scalar || spans != 1))
+        return MAMBA_ERR_UNSUPPORTED;
+    if (p.family == Family::Scalar && spans == 1 && seqlen > 0 && want_relay != 1) {
+        const int64_t units = batch * ((d_inner + 63) / 64);
+        int64_t rem = units % cus;
+        int64_t k = 1, plen = 0;
+        if (want_relay >= 2) {
+            k = want_relay;
+            if (rem == 0)
+                rem = units;
+            plen = (seqlen + k - 1) / k;
+        } else if (units > cus && rem > 0 && rem * 2 <= cus && seqlen >= 512) {
+            k = 2;
+            plen = (seqlen + 1) / 2;
+        }
+        if (k >= 2) {
+            plen = (plen + p.chunk - 1) / p.chunk * p.chunk;
+            k = (seqlen + plen - 1) / plen; // every part non-empty
+            if (k >= 2) {
+                p.relay_parts = (int)k;
+                p.relay_tiles = rem;
+                p.relay_len = plen;
+            }
+        }
+    }
     *plan = p;
     return MAMBA_OK;
 }
@@ -169,10 +209,28 @@ size_t staged_bytes_for(int64_t batch, int64_t seqlen, int64_t d_state, const Pl
     return (bytes + 255) / 256 * 256;
 }
 
+// Relay area: [hand-off flags, 256-byte aligned][hand-off states].
+size_t relay_sync_bytes(const Plan &p)
+{
+    if (p.relay_parts < 2)
+        return 0;
+    const size_t words = (size_t)p.relay_tiles * (size_t)(p.relay_parts - 1);
+    return (words * sizeof(uint32_t) + 255) / 256 * 256;
+}
+
+size_t relay_state_bytes(int64_t d_state, const Plan &p)
+{
+    if (p.relay_parts < 2)
+        return 0;
+    return (size_t)p.relay_tiles * (size_t)(p.relay_parts - 1) * 64 * (size_t)d_state *
+           sizeof(float);
+}
+
 size_t workspace_bytes_for(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
                            const Plan &p)
 {
     size_t n = staged_bytes_for(batch, seqlen, d_state, p);
+    n += relay_sync_bytes(p) + relay_state_bytes(d_state, p);
     if (p.n_spans > 1) // decay [c][S], hloc [c][S], h_in [S][c]
         n += (size_t)3 * (size_t)p.n_spans * (size_t)(batch * d_inner * d_state) * sizeof(float);
     return n;
@@ -339,10 +397,18 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
 
     char *ws_bytes = static_cast<char *>(workspace);
     const size_t staged = staged_bytes_for(batch, seqlen, d_state, plan);
+    L.relay_parts = 1;
+    if (plan.relay_parts > 1) {
+        L.relay_sync = reinterpret_cast<uint32_t *>(ws_bytes + staged);
+        L.relay_state = reinterpret_cast<float *>(ws_bytes + staged + relay_sync_bytes(plan));
+        L.relay_tiles = (int32_t)plan.relay_tiles;
+        L.relay_parts = plan.relay_parts;
+        L.relay_len = plan.relay_len;
+    }
     if (plan.family == Family::Scalar) {
         L.bc_staged = reinterpret_cast<float *>(ws_bytes);
         L.staged_rows = seqlen + plan.chunk;
-        if (launch_stage_bc(L, st) != hipSuccess)
+        if (launch_stage_bc(L, st) != hipSuccess) // also clears the relay flags
             return MAMBA_ERR_HIP;
     }
 
@@ -356,7 +422,7 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
 
     // ---- split sequence: span summaries, carry pass, full rescan ----
     const int64_t S = plan.n_spans;
-    float *ws = reinterpret_cast<float *>(ws_bytes + staged);
+    float *ws = reinterpret_cast<float *>(ws_bytes + staged); // (no relay with spans)
     float *ws_decay = ws;
     float *ws_hloc = ws + S * bdn;
     float *ws_hin = ws + 2 * S * bdn;

@@ -28,6 +28,22 @@ struct ScanLaunch {
     DType dtype;
     float *bc_staged;           // scalar family: B/C repacked as fp32 [b][wave][row][2 NQ]
     int64_t staged_rows;        // rows per (b, wave) in bc_staged (L plus one chunk of padding)
+    // Relay (scalar family, single span): the last `relay_tiles` (batch row, channel tile)
+    // units are split in time into `relay_parts` parts of `relay_len` steps run by different
+    // blocks, each part handing its final state to the next through relay_state.
+    // relay_sync[slot] are the hand-off flags, zeroed by the staging pass of the same call.
+    uint32_t *relay_sync;
+    float *relay_state;         // [slot][n][lane], slot = tile * (parts - 1) + part
+    int32_t relay_tiles, relay_parts;
+    int64_t relay_len;
+};
+
+// Relay arguments as the scan kernel receives them.
+struct RelayArgs {
+    uint32_t *sync;
+    float *state;
+    int32_t tiles, parts, units; // units = batch * channel tiles
+    int32_t len;
 };
 
 enum class Family : int { Auto = 0, Block = 1, Rows = 2, Scalar = 3 };

@@ -177,7 +177,7 @@ scan_chunk_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T 
             float yp = 0.0f;
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
-                const float a = hw_exp2(dw.x * a2[q]);
+                const float a = decay_exp2(dw.x, a2[q]);
                 h[q] = __builtin_fmaf(a, h[q], dw.y * bc[q]);
                 if (FULL)
                     yp = __builtin_fmaf(bc[NQ + q], h[q], yp);

@@ -183,7 +183,7 @@ scan_rows_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T *
             unroll_for<0, NQ>([&](auto Q) {
                 constexpr int q = decltype(Q)::value;
                 constexpr int e = s * NQ + q;
-                const float a = hw_exp2(dls[s] * a2[q]);
+                const float a = decay_exp2(dls[s], a2[q]);
                 h[q] = __builtin_fmaf(a, h[q], row_bcast<e % 16>(bv[e / 16]) * ws[s]);
                 if (FULL) {
                     const float p = row_bcast<e % 16>(cv[e / 16]) * h[q];

@@ -34,13 +34,17 @@ __device__ __forceinline__ void for_c(F &&f)
 }
 
 // bcp[((b * NW + g) * Lp + t) * 2 NQ + {q, NQ + q}] = {B, C}[b, t, g * NQ + q] (0 past L).
+// Also zeroes the relay hand-off flags (n_sync words) for the scan launch that follows on
+// the same stream.
 template <typename T, int N, int NW>
 __global__ void __launch_bounds__(256)
 stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, float *__restrict__ bcp,
-                int64_t L, int64_t Lp, int64_t total)
+                int64_t L, int64_t Lp, int64_t total, uint32_t *__restrict__ sync, int32_t n_sync)
 {
     constexpr int NQ = N / NW;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; // over batch * Lp * N
+    if (i < n_sync)
+        sync[i] = 0u;
     if (i >= total)
         return;
     const int n = (int)(i % N);
@@ -88,6 +92,20 @@ __device__ __forceinline__ void buf_store(float v, rsrc_t r, uint32_t vo, uint32
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, vo, so, 0);
 }
 
+// Bounded wait for a relay flag.  Polls with relaxed device-scope loads (no cache
+// invalidation per poll, which would disturb every other wave on the XCD) and long
+// sleeps, then acquires once; gives up after 2^20 polls (a few seconds), so a missing
+// hand-off can never hang the device.
+__device__ __forceinline__ void relay_wait(uint32_t *flag)
+{
+    for (uint32_t i = 0; i < (1u << 20); ++i) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+            break;
+        __builtin_amdgcn_s_sleep(127);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
 template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED>
 __global__ void __launch_bounds__(64 * NW)
 scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
@@ -97,7 +115,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                    T *__restrict__ y, float *h_last, float *__restrict__ ws_decay,
                    float *__restrict__ ws_hloc, int64_t L, int64_t Lp, int32_t Dn,
                    int64_t span_len, int32_t n_spans, int32_t first_span, int32_t tiles,
-                   int32_t batch)
+                   int32_t batch, RelayArgs relay)
 {
     constexpr int NQ = N / NW;                 // state indices per lane
     constexpr int KPL = (TC + NW - 1) / NW;    // prologue/epilogue channel-steps per lane
@@ -115,16 +133,45 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     const int lane = threadIdx.x & 63;
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // Batch row fastest: consecutive blocks go to different XCDs, so with 8 batch rows on
-    // 8 XCDs each XCD's L2 holds the staged B/C of one row only.
-    int bid = blockIdx.x;
-    const int b = bid % batch;
-    bid /= batch;
-    const int tile = bid % tiles;
-    const int span = first_span + bid / tiles;
-
-    const int64_t t_begin = (int64_t)span * span_len;
-    const int64_t t_end = min(t_begin + span_len, L);
+    // Work unit of this block.  Without relay: blockIdx -> (batch row fastest, tile, span);
+    // consecutive blocks go to different XCDs, so with 8 batch rows on 8 XCDs each XCD's L2
+    // holds the staged B/C of one row only.  With relay the grid is ordered
+    // [part 0 of each relayed unit][whole units][part 1 ...]...[part k-1 ...]: workgroups
+    // are dispatched in index order, round-robin over the compute units, so the parts land
+    // on different compute units from the whole units' last round, and a part only waits
+    // for the previous part of its unit, which has a smaller index and therefore already
+    // holds a slot (its wait is bounded all the same).
+    int b, tile, span, part = -1, r_unit = 0;
+    int64_t t_begin, t_end;
+    const bool relayed = FULL && relay.parts > 1;
+    if (relayed) {
+        const int v = blockIdx.x;
+        const int nu = relay.units, nr = relay.tiles;
+        int unit;
+        if (v < nr) {
+            unit = nu - nr + v;
+            part = 0;
+        } else if (v < nu) {
+            unit = v - nr;
+        } else {
+            part = 1 + (v - nu) / nr;
+            unit = nu - nr + (v - nu) % nr;
+        }
+        r_unit = unit - (nu - nr);
+        b = unit % batch;
+        tile = unit / batch;
+        span = 0;
+        t_begin = part < 0 ? 0 : (int64_t)part * relay.len;
+        t_end = part < 0 ? L : min(t_begin + (int64_t)relay.len, L);
+    } else {
+        int bid = blockIdx.x;
+        b = bid % batch;
+        bid /= batch;
+        tile = bid % tiles;
+        span = first_span + bid / tiles;
+        t_begin = (int64_t)span * span_len;
+        t_end = min(t_begin + span_len, L);
+    }
     const int d = tile * 64 + lane;
     const bool dvalid = d < Dn;
     const int dc = dvalid ? d : Dn - 1; // tail lanes compute on a valid channel, store nothing
@@ -136,6 +183,17 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     for (int q = 0; q < NQ; ++q) {
         a2[q] = A[(int64_t)dc * N + n0 + q] * kLog2e; // exp(Delta*A) = exp2(Delta*A*log2 e)
         h[q] = h_init ? h_init[span * h_init_stride + col0 + q] : 0.0f;
+    }
+    if (relayed && part > 0) {
+        // the previous part's final state: wait for its flag, then read it
+        const int slot = r_unit * (relay.parts - 1) + part - 1;
+        if (threadIdx.x == 0)
+            relay_wait(relay.sync + slot);
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            h[q] = relay.state[((int64_t)slot * N + n0 + q) * 64 + lane];
     }
     const float bias_d = bias ? bias[dc] : 0.0f;
     const float D_d = Dv ? Dv[dc] : 0.0f;
@@ -271,7 +329,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
             float yp = 0.0f;
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
-                const float a = hw_exp2(dw[tl].x * a2[q]);
+                const float a = decay_exp2(dw[tl].x, a2[q]);
                 h[q] = __builtin_fmaf(a, h[q], dw[tl].y * bcs[tl][q]);
                 if (FULL)
                     yp = __builtin_fmaf(bcs[tl][NQ + q], h[q], yp);
@@ -331,6 +389,19 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
         epilogue_store(es);
     }
 
+    if (relayed && part >= 0 && part < relay.parts - 1) {
+        // hand the final state to the next part (every lane: the slot is dense)
+        const int slot = r_unit * (relay.parts - 1) + part;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            relay.state[((int64_t)slot * N + n0 + q) * 64 + lane] = h[q];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_store(relay.sync + slot, 1u, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     if (!dvalid)
         return;
     const int64_t col = ((int64_t)b * Dn + d) * N + n0;
@@ -362,7 +433,18 @@ template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED>
 hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
 {
     const int32_t tiles = (int32_t)((p.d_inner + 63) / 64);
-    const int64_t blocks = (int64_t)tiles * p.batch * p.launch_spans;
+    int64_t blocks = (int64_t)tiles * p.batch * p.launch_spans;
+    RelayArgs relay{};
+    relay.parts = 1;
+    if (FULL && p.relay_parts > 1) {
+        relay.sync = p.relay_sync;
+        relay.state = p.relay_state;
+        relay.tiles = p.relay_tiles;
+        relay.parts = p.relay_parts;
+        relay.units = (int32_t)(tiles * p.batch);
+        relay.len = (int32_t)p.relay_len;
+        blocks = (int64_t)relay.units + (int64_t)relay.tiles * (relay.parts - 1);
+    }
     if (blocks <= 0)
         return hipSuccess;
     hipLaunchKernelGGL((scan_scalar_kernel<T, N, NW, TC, PD, FULL, GATED>),
@@ -370,7 +452,7 @@ hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
                        (const T *)p.delta, (const T *)p.z, p.bc_staged, p.A, p.D, p.bias,
                        p.h_init, p.h_init_span_stride, (T *)p.y, p.h_last, p.ws_decay,
                        p.ws_hloc, p.L, p.staged_rows, (int32_t)p.d_inner, p.span_len,
-                       p.n_spans, p.first_span, tiles, (int32_t)p.batch);
+                       p.n_spans, p.first_span, tiles, (int32_t)p.batch, relay);
     return hipGetLastError();
 }
 
@@ -378,12 +460,13 @@ template <typename T, int N, int NW>
 hipError_t launch_stage(const ScanLaunch &p, hipStream_t stream)
 {
     const int64_t total = p.batch * p.staged_rows * N;
-    const int64_t blocks = (total + 255) / 256;
+    const int32_t n_sync = p.relay_parts > 1 ? p.relay_tiles * (p.relay_parts - 1) : 0;
+    const int64_t blocks = (max(total, (int64_t)n_sync) + 255) / 256;
     if (blocks <= 0)
         return hipSuccess;
     hipLaunchKernelGGL((stage_bc_kernel<T, N, NW>), dim3((uint32_t)blocks), dim3(256), 0,
                        stream, (const T *)p.B, (const T *)p.C, p.bc_staged, p.L, p.staged_rows,
-                       total);
+                       total, p.relay_sync, n_sync);
     return hipGetLastError();
 }
 

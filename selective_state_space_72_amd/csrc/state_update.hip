@@ -47,7 +47,7 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
     float yp = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const float a = hw_exp2(dl * ain[k] * kLog2e);
+        const float a = decay_exp2(dl, ain[k] * kLog2e);
         hn[k] = __builtin_fmaf(a, hin[k], w * load_val(Bm, bn + k));
         yp = __builtin_fmaf(load_val(Cm, bn + k), hn[k], yp);
     }

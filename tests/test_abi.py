@@ -130,8 +130,14 @@ def test_scan_workspace_rules(lib):
                 B=BASE + 1200 * MB, C=BASE + 1300 * MB, A=BASE + 1400 * MB,
                 y=BASE + 1500 * MB, ws=BASE + 1500 * MB, ws_bytes=n) == ALIAS
     # many channels: no split; the scalar-B/C kernel stages B and C as fp32 with one
-    # chunk of padding rows: batch * (L + 8) * 2 * d_state * 4 bytes
-    assert lib.mamba_scan_fwd_workspace_size(8, 4096, 5120, 16) == 8 * (4096 + 8) * 2 * 16 * 4
+    # chunk of padding rows: batch * (L + 8) * 2 * d_state * 4 bytes.  640 units over 256
+    # compute units leave 128 over: they are relayed in 2 parts (128 flags, padded to 256
+    # bytes, and 128 hand-off states of 64 x 16 floats)
+    staged = 8 * (4096 + 8) * 2 * 16 * 4
+    relay = 512 + 128 * 64 * 16 * 4
+    assert lib.mamba_scan_fwd_workspace_size(8, 4096, 5120, 16) == staged + relay
+    assert lib.mamba_scan_fwd_workspace_size_ex(8, 4096, 5120, 16,
+                                                ctypes.byref(ms.ScanOpts(0, 0, 0, 0, 1))) == staged
     # the LDS-exchange kernel without a split needs none
     assert lib.mamba_scan_fwd_workspace_size_ex(8, 4096, 5120, 16,
                                                 ctypes.byref(ms.ScanOpts(0, 0, 1, 1))) == 0
@@ -151,6 +157,28 @@ def test_scan_rejects_bad_options(lib):
     # the scalar-B/C kernel always stages B/C in the workspace
     assert scan(lib, opts=ms.ScanOpts(0, 0, 0, 3)) == WS
     assert scan(lib, opts=ms.ScanOpts(16, 0, 0, 2)) == UNSUP      # rows: no chunk option
+
+
+def test_relay_options(lib):
+    ws = lambda *a, o: lib.mamba_scan_fwd_workspace_size_ex(*a, ctypes.byref(o))  # noqa: E731
+    bad = ctypes.c_size_t(-1).value
+    small = (3, 1000, 200, 16)  # 3 x 4 = 12 units
+    staged = 3 * (1000 + 8) * 2 * 16 * 4
+    # forced relay needs the scalar family and a single span
+    assert ws(*small, o=ms.ScanOpts(0, 0, 0, 3, 3)) == bad       # auto spans split here
+    assert ws(*small, o=ms.ScanOpts(0, 0, 2, 3, 3)) == bad
+    assert ws(*small, o=ms.ScanOpts(0, 0, 1, 2, 3)) == bad       # row family
+    assert ws(*small, o=ms.ScanOpts(0, 0, 1, 3, 9)) == bad
+    assert ws(*small, o=ms.ScanOpts(0, 0, 1, 3, -1)) == bad
+    # 3 parts of 336 steps for all 12 units: 24 flags (256 B) + 24 states
+    assert ws(*small, o=ms.ScanOpts(0, 0, 1, 3, 3)) == staged + 256 + 24 * 64 * 16 * 4
+    assert ws(*small, o=ms.ScanOpts(0, 0, 1, 3, 1)) == staged
+    assert ws(*small, o=ms.ScanOpts(0, 0, 1, 3, 0)) == staged    # auto: one round, no relay
+    # parts are whole chunks and none is empty: 20 steps in chunks of 8 -> 3 parts (8, 8, 4)
+    assert ws(3, 20, 200, 16, o=ms.ScanOpts(0, 0, 1, 3, 8)) == \
+        3 * (20 + 8) * 2 * 16 * 4 + 256 + 24 * 64 * 16 * 4
+    # one chunk: no relay possible
+    assert ws(3, 8, 200, 16, o=ms.ScanOpts(0, 0, 1, 3, 2)) == 3 * (8 + 8) * 2 * 16 * 4
 
 
 def test_scalar_span_addressing_limit(lib):

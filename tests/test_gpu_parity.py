@@ -36,7 +36,8 @@ def check(name, y, h, yr, hr, dtype):
 
 
 def full_check(name, inp, **kw):
-    opts = {k: kw.pop(k) for k in ("chunk_len", "waves", "n_spans", "kernel") if k in kw}
+    opts = {k: kw.pop(k) for k in ("chunk_len", "waves", "n_spans", "kernel", "relay")
+            if k in kw}
     log(f"case {name}: batch={inp.cfg.batch} L={inp.cfg.seqlen} D={inp.cfg.d_inner} "
         f"N={inp.cfg.d_state} {inp.dtype} opts={opts} {kw}")
     di = DevInputs(inp)
@@ -198,6 +199,47 @@ def test_in_place_state_continuation(n_spans, kernel):
     y2 = torch.cat(ys, dim=1)
     assert metric(from_dev(y2), from_dev(y_full)) <= 1e-2
     assert metric(from_dev(h), from_dev(h_full)) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("parts", [2, 3, 8])
+def test_relay_parts_agree_with_oracle(parts, dtype):
+    """Units split in time across blocks, each part handing its state to the next."""
+    import dataclasses
+    # each dtype with its own config's recipe: the fp32 one (A = -(n+1), D = 1) for fp32,
+    # the large-prefill one for bf16; gate and h0 on in both
+    base = synth.CONFIGS["c1"] if dtype == synth.F32 else synth.CONFIGS["c3"]
+    cfg = dataclasses.replace(base, dtype=dtype, h0=True, gate=True)
+    inp = synth.make_scan_inputs(cfg, batch=3, seqlen=1001, d_inner=200, seed=30 + parts)
+    full_check(f"relay {parts} {dtype}", inp, kernel="scalar", n_spans=1, relay=parts)
+    # 17 steps in chunks of 8: parts of 8, 8 and 1 step
+    inp = synth.make_scan_inputs(cfg, batch=2, seqlen=17, d_inner=70, seed=40 + parts)
+    full_check(f"relay {parts} {dtype} short", inp, kernel="scalar", n_spans=1, relay=parts)
+
+
+def test_relay_is_bitwise_identical_to_one_block_per_unit():
+    inp = synth.make_scan_inputs(synth.CONFIGS["c3"], batch=2, seqlen=640, d_inner=192, seed=5)
+    inp.h0 = np.random.default_rng(6).standard_normal((2, 192, 16), dtype=np.float32)
+    di = DevInputs(inp)
+    y1, h1 = di.run(kernel="scalar", n_spans=1, relay=1)
+    for parts in (2, 5):
+        y2, h2 = di.run(kernel="scalar", n_spans=1, relay=parts)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(h1, h2), f"relay {parts} differs"
+
+
+def test_relay_in_place_continuation():
+    """h_last == h0 with relay: part 0 reads h0 before the last part overwrites it."""
+    inp = synth.make_scan_inputs(synth.CONFIGS["c3"], batch=2, seqlen=512, d_inner=128, seed=8)
+    inp.h0 = np.random.default_rng(9).standard_normal((2, 128, 16), dtype=np.float32)
+    di = DevInputs(inp)
+    y_ref, h_ref = di.run(kernel="scalar", n_spans=1, relay=1)
+    h = di.h0.clone()
+    y, _ = ms.mamba_scan_fwd(di.u, di.delta, di.A, di.B, di.C, D=di.D, z=di.z,
+                             delta_bias=di.bias, h0=h, h_last_out=h, kernel="scalar",
+                             n_spans=1, relay=4)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref) and torch.equal(h, h_ref)
 
 
 def test_deterministic():
