@@ -216,7 +216,9 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     const float *bc_span = bcp + (((int64_t)b * NW + g) * Lp + t_begin) * BCW;
 
     // raw inputs of PD chunks in flight: u, delta, z for this lane's KPL channel-steps
-    T ru[PD][KPL], rd[PD][KPL], rz[PD][KPL];
+    // (zeroed so that the prologue may process the unloaded steps of a last, partial chunk:
+    // their values are computed and never used)
+    T ru[PD][KPL] = {}, rd[PD][KPL] = {}, rz[PD][KPL] = {};
     auto fetch = [&](auto BUF, int t0) {
         constexpr int j = decltype(BUF)::value;
 #pragma unroll
@@ -291,25 +293,17 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
         const int nt = min(TC, n_loc - t0);
 
         // ---- prologue: Delta and Delta*u once per (t, d) ----
+        // (steps tl >= nt of a partial chunk are computed from stale registers and ignored)
         float du[KPL], gz[KPL];
 #pragma unroll
         for (int k = 0; k < KPL; ++k) {
             const int tl = g + k * NW;
-            float dl = 0.0f, w = 0.0f;
-            du[k] = 0.0f;
-            gz[k] = 1.0f;
-            if (tl < nt) {
-                const float uu = widen(ru[j][k]);
-                dl = softplus_f(widen(rd[j][k]) + bias_d);
-                w = dl * uu;
-                if (FULL) {
-                    du[k] = D_d * uu;
-                    if (gated)
-                        gz[k] = silu_f(widen(rz[j][k]));
-                }
-            }
+            const float uu = widen(ru[j][k]);
+            const float dl = softplus_f(widen(rd[j][k]) + bias_d);
+            du[k] = FULL ? D_d * uu : 0.0f;
+            gz[k] = gated ? silu_f(widen(rz[j][k])) : 1.0f;
             if (tl < TC)
-                s_dw[pp][tl][lane] = make_float2(dl, w);
+                s_dw[pp][tl][lane] = make_float2(dl, dl * uu);
         }
         if (t0 + PD * TC < n_loc)
             fetch(BUF, t0 + PD * TC);
