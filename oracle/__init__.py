@@ -1,11 +1,13 @@
-"""fp64 CPU oracle for the selective scan -- TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracles for the selective scan and the causal conv1d + SiLU --
+TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
-``bench.py`` may import this package.  It wraps ``oracle_scan.c`` (plain C,
-double precision, sequential in time) through ctypes and shares no code with the
-HIP library.  Every function here is pinned by the CPU tests in
-``tests/test_oracle_pins.py`` (brute force, LTI closed form, exact decay,
-split/decode invariances, special cases, planted-mistake checks).
+``bench.py`` may import this package.  It wraps ``oracle_scan.c`` and
+``oracle_conv.c`` (plain C, double precision, sequential in time) through ctypes
+and shares no code with the HIP library.  Every function here is pinned by the
+CPU tests in ``tests/test_oracle_pins.py`` and ``tests/test_oracle_conv_pins.py``
+(brute force, closed forms, exact decay, split/decode invariances, special cases,
+planted-mistake checks).
 
 Inputs are float64 numpy arrays (callers expand stored fp32/bf16 values exactly
 before the call); outputs are float64 and never rounded to a storage type.
@@ -23,6 +25,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "oracle_scan.c")
 LIBRARY = os.path.join(_HERE, "liboracle_scan.so")
+CONV_SOURCE = os.path.join(_HERE, "oracle_conv.c")
+CONV_LIBRARY = os.path.join(_HERE, "liboracle_conv.so")
 
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
           "-pthread"]
@@ -144,14 +148,79 @@ def _check(a, shape, name):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(a.shape)}")
 
 
+class ConvOracle:
+    """The causal depthwise conv1d + SiLU oracle (oracle_conv.c)."""
+
+    def __init__(self, path: str = CONV_LIBRARY):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.oracle_conv1d_silu.restype = ctypes.c_int
+        lib.oracle_conv1d_silu.argtypes = [_dp] * 7 + [_i64] * 4
+        lib.oracle_conv1d_step.restype = ctypes.c_int
+        lib.oracle_conv1d_step.argtypes = [_dp] * 6 + [_i64] * 3
+        self._lib = lib
+
+    def conv(self, x, w, bias=None, state_in=None):
+        """Return (pre, u, state_out) in float64.  x: (batch, L, D); w: (D, K);
+        bias: (D,); state_in: (batch, D, K - 1)."""
+        x, w = _c64(x), _c64(w)
+        batch, L, D = x.shape
+        K = w.shape[1]
+        bias, state_in = _c64(bias), _c64(state_in)
+        _check(w, (D, K), "w")
+        _check(bias, (D,), "bias")
+        _check(state_in, (batch, D, K - 1), "state_in")
+        pre = np.empty(x.shape, dtype=np.float64)
+        u = np.empty(x.shape, dtype=np.float64)
+        state_out = np.empty((batch, D, K - 1), dtype=np.float64)
+        rc = self._lib.oracle_conv1d_silu(_p(x), _p(w), _p(bias), _p(state_in), _p(pre),
+                                          _p(u), _p(state_out), batch, L, D, K)
+        if rc != 0:
+            raise ValueError("oracle_conv1d_silu rejected its arguments")
+        return pre, u, state_out
+
+    def step(self, state, x, w, bias=None):
+        """One decode step: return (pre, u, state_new); state is not modified.
+        state: (batch, D, K - 1); x: (batch, D)."""
+        x, w = _c64(x), _c64(w)
+        batch, D = x.shape
+        K = w.shape[1]
+        st = np.array(state, dtype=np.float64, copy=True, order="C")
+        _check(st, (batch, D, K - 1), "state")
+        bias = _c64(bias)
+        _check(bias, (D,), "bias")
+        pre = np.empty(x.shape, dtype=np.float64)
+        u = np.empty(x.shape, dtype=np.float64)
+        rc = self._lib.oracle_conv1d_step(_p(st), _p(x), _p(w), _p(bias), _p(pre), _p(u),
+                                          batch, D, K)
+        if rc != 0:
+            raise ValueError("oracle_conv1d_step rejected its arguments")
+        return pre, u, st
+
+
 _default: Optional[Oracle] = None
+_default_conv: Optional[ConvOracle] = None
+
+
+def _stale(lib, src):
+    return not os.path.exists(lib) or os.path.getmtime(lib) < os.path.getmtime(src)
 
 
 def load() -> Oracle:
     """The committed oracle, compiled on first use if it has not been built."""
     global _default
     if _default is None:
-        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+        if _stale(LIBRARY, SOURCE):
             build()
         _default = Oracle(LIBRARY)
     return _default
+
+
+def load_conv() -> ConvOracle:
+    """The committed conv1d + SiLU oracle, compiled on first use."""
+    global _default_conv
+    if _default_conv is None:
+        if _stale(CONV_LIBRARY, CONV_SOURCE):
+            build(CONV_SOURCE, CONV_LIBRARY)
+        _default_conv = ConvOracle(CONV_LIBRARY)
+    return _default_conv
