@@ -12,7 +12,8 @@ Prints ONE JSON line: throughput as GB/s of minimum algorithmic traffic (each
 input read once, each output written once), with channel-steps/s and the
 fraction of the 8 TB/s HBM peak; the roofline of the dominant kernel; the fp64
 oracle timed on the host cores on a bounded sample; and the other workloads
-(small prefill, long sequence, decode step) measured briefly.
+(small prefill, long sequence, decode step, and the causal conv1d + SiLU that
+produces the scan's input, prefill and decode token) measured briefly.
 """
 
 from __future__ import annotations
@@ -231,6 +232,39 @@ def extra_workloads(dev, flush, steps):
                      "hbm_frac": round(case.min_bytes / (ms_used * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del case
         torch.cuda.empty_cache()
+    # causal depthwise conv1d + SiLU producing the scan's u, on the large-prefill shape
+    ci = synth.make_conv_inputs(8, 4096, 5120, 4, synth.BF16)
+    cx, cw, cb = to_dev(ci.x, dev), to_dev(ci.w, dev), to_dev(ci.bias, dev)
+    cs_in, cs_out = to_dev(ci.state, dev), to_dev(ci.state, dev).clone()
+    cu = torch.empty_like(cx)
+
+    def cstep():
+        ms.mamba_conv1d_silu_fwd(cx, cw, cb, cs_in, out=cu, state_out=cs_out)
+    loop_ms, med, _ = time_steps(cstep, steps, 10, flush, warm_ms=100.0)
+    cbytes = (cx.numel() * 2 * 2 + cw.numel() * 4 + cb.numel() * 4 + cs_in.numel() * 2 * 2)
+    out["conv1d_silu"] = {
+        "workload": "causal depthwise conv1d (d_conv 4) + SiLU: x (8, 4096, 5120) bf16 -> u, "
+                    "with carried state in and out",
+        "ms": round(med, 4), "ms_back_to_back": round(loop_ms, 4),
+        "GB_s": round(cbytes / (med * 1e-3) / 1e9, 1),
+        "GB_s_back_to_back": round(cbytes / (loop_ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(cbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del cx, cu, ci
+    torch.cuda.empty_cache()
+    # its decode token on the decode shape (256, 5120)
+    dx = to_dev(synth.make_conv_step(0, 256, 5120), dev)
+    dstate = to_dev(synth.make_conv_inputs(256, 0, 5120, 4).state, dev)
+    du_out = torch.empty_like(dx)
+
+    def cdstep():
+        ms.mamba_conv1d_silu_update(dstate, dx, cw, cb, out=du_out)
+    loop_ms, med, _ = time_steps(cdstep, max(steps, 50), 10, flush, warm_ms=100.0)
+    dcb = dx.numel() * 2 * 2 + dstate.numel() * 2 * 2 + cw.numel() * 4 + cb.numel() * 4
+    out["conv1d_silu_decode"] = {
+        "workload": "conv1d + SiLU decode token: x (256, 5120) bf16, state (256, 5120, 3) bf16",
+        "ms": round(med, 5), "ms_chained_cache_warm": round(loop_ms, 5),
+        "GB_s": round(dcb / (med * 1e-3) / 1e9, 1),
+        "hbm_frac": round(dcb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     # decode: one-token state update on the (256, 5120, 16) fp32 state
     dc = synth.DECODE
     p, h = synth.make_decode_state()

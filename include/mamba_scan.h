@@ -202,6 +202,56 @@ MAMBA_API mamba_status_t mamba_state_update(float *h, const void *u, const void 
                                   int64_t d_inner, int64_t d_state, mamba_dtype_t dtype,
                                   void *stream);
 
+/* ------------------------------------------------------------------------
+ * Causal depthwise convolution + SiLU: the Mamba block's conv1d, which produces
+ * the scan's input u from the inner activations x.  "Understanding Mamba"
+ * (aiattnstudio.link), sections 3.2 and 5.2: a depthwise nn.Conv1d (one filter
+ * per channel) with kernel d_conv = K, padding K - 1 and a bias, of which the
+ * first seqlen outputs are kept, followed by F.silu; the same block in "State
+ * Space Models and Mamba" (metaphor-xennon.pages.dev), MambaBlock.forward.
+ * (The scan's Delta, B and C are projections of this output, so it runs before
+ * the scan as its own pass.)
+ *
+ *   u[b,t,d] = silu(conv_bias[d] + sum_{k<K} w[d,k] * xe[b, t-(K-1)+k, d])
+ *
+ * xe[b,s,d] = x[b,s,d] for s >= 0; for -(K-1) <= s < 0 it is the carried state
+ * state_in[b,d,(K-1)+s] -- the previous segment's last K-1 inputs, oldest
+ * first -- or 0 when state_in is NULL (the zero padding of nn.Conv1d).  On
+ * return state_out[b,d,j] = xe[b, seqlen-(K-1)+j, d], j < K-1, the state a
+ * following segment or decode step needs.
+ *
+ *   x, u                (batch, seqlen, d_inner) dtype   required (unless empty)
+ *   w                   (d_inner, d_conv) float32        required
+ *   conv_bias           (d_inner) float32                nullable (0)
+ *   state_in, state_out (batch, d_inner, d_conv-1) dtype nullable
+ *
+ * d_conv must be 2, 3 or 4 (else MAMBA_ERR_UNSUPPORTED).  state_in == state_out
+ * is allowed (in-place continuation); u must not overlap x, w or the states, and
+ * state_out must not overlap x (MAMBA_ERR_ALIASING).  Pointers must be aligned to
+ * their element size.  Other conventions as above.
+ */
+MAMBA_API mamba_status_t mamba_conv1d_silu_fwd(const void *x, const float *w,
+                                               const float *conv_bias, const void *state_in,
+                                               void *u, void *state_out, int64_t batch,
+                                               int64_t seqlen, int64_t d_inner, int64_t d_conv,
+                                               mamba_dtype_t dtype, void *stream);
+
+/* One decode token of the convolution:
+ *   u[b,d] = silu(conv_bias[d] + sum_{k<K-1} w[d,k] state[b,d,k] + w[d,K-1] x[b,d])
+ *   state[b,d,:] <- (state[b,d,1:], x[b,d])
+ *
+ *   state      (batch, d_inner, d_conv-1) dtype     in/out, required
+ *   x, u       (batch, d_inner) dtype               required
+ *   w          (d_inner, d_conv) float32            required
+ *   conv_bias  (d_inner) float32                    nullable
+ *
+ * d_conv 2..4.  u must not overlap state, x or w; state must not overlap x or w.
+ */
+MAMBA_API mamba_status_t mamba_conv1d_silu_update(void *state, const void *x, const float *w,
+                                                  const float *conv_bias, void *u,
+                                                  int64_t batch, int64_t d_inner, int64_t d_conv,
+                                                  mamba_dtype_t dtype, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 MAMBA_API const char *mamba_status_string(mamba_status_t status);
 

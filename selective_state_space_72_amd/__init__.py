@@ -9,6 +9,8 @@ there is no CPU or PyTorch fallback -- if the library is missing, the call fails
     y, h_last = mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                                h0=None, return_last_state=False)
     y = mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None)
+    u, state = mamba_conv1d_silu_fwd(x, w, conv_bias=None, state_in=None, return_state=False)
+    u = mamba_conv1d_silu_update(state, x, w, conv_bias=None)
 """
 
 from __future__ import annotations
@@ -31,7 +33,8 @@ STATUS = {
 # Every symbol include/mamba_scan.h declares.
 EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_scan_fwd_workspace_size_ex", "mamba_scan_fwd", "mamba_scan_fwd_ex",
-           "mamba_state_update", "mamba_status_string")
+           "mamba_state_update", "mamba_conv1d_silu_fwd", "mamba_conv1d_silu_update",
+           "mamba_status_string")
 
 
 class MambaError(RuntimeError):
@@ -81,6 +84,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                        ctypes.POINTER(ScanOpts), _vp])
     lib.mamba_state_update.restype = ctypes.c_int
     lib.mamba_state_update.argtypes = [_vp] * 10 + [_i64] * 3 + [ctypes.c_int, _vp]
+    lib.mamba_conv1d_silu_fwd.restype = ctypes.c_int
+    lib.mamba_conv1d_silu_fwd.argtypes = [_vp] * 6 + [_i64] * 4 + [ctypes.c_int, _vp]
+    lib.mamba_conv1d_silu_update.restype = ctypes.c_int
+    lib.mamba_conv1d_silu_update.argtypes = [_vp] * 5 + [_i64] * 3 + [ctypes.c_int, _vp]
     lib.mamba_status_string.restype = ctypes.c_char_p
     lib.mamba_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -234,3 +241,66 @@ def mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
     if st != 0:
         raise MambaError(st, "mamba_state_update")
     return y
+
+
+def mamba_conv1d_silu_fwd(x, w, conv_bias=None, state_in=None, *, out=None, state_out=None,
+                          return_state: bool = False):
+    """Causal depthwise conv1d + SiLU over (batch, seqlen, d_inner); see include/mamba_scan.h.
+
+    w: (d_inner, d_conv) fp32; conv_bias: (d_inner,) fp32; states (batch, d_inner,
+    d_conv - 1) in x's dtype.  Returns (u, state_out); state_out is None unless
+    return_state (or state_out is given).  state_out may be state_in itself.
+    """
+    torch = _torch()
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, seqlen, d_inner)")
+    batch, seqlen, d_inner = x.shape
+    if w.dim() != 2 or w.shape[0] != d_inner:
+        raise ValueError("w must be (d_inner, d_conv)")
+    d_conv = w.shape[1]
+    dev, act = x.device, x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    p_x = _ptr(x, "x", (batch, seqlen, d_inner), act, dev)
+    p_w = _ptr(w, "w", (d_inner, d_conv), f32, dev)
+    p_b = _ptr(conv_bias, "conv_bias", (d_inner,), f32, dev)
+    sshape = (batch, d_inner, d_conv - 1)
+    p_si = _ptr(state_in, "state_in", sshape, act, dev)
+    u = out if out is not None else torch.empty((batch, seqlen, d_inner), dtype=act, device=dev)
+    p_u = _ptr(u, "out", (batch, seqlen, d_inner), act, dev)
+    so = state_out
+    if so is None and return_state:
+        so = torch.empty(sshape, dtype=act, device=dev)
+    p_so = _ptr(so, "state_out", sshape, act, dev)
+    st = lib.mamba_conv1d_silu_fwd(p_x, p_w, p_b, p_si, p_u, p_so, batch, seqlen, d_inner,
+                                   d_conv, code, _stream(dev))
+    if st != 0:
+        raise MambaError(st, "mamba_conv1d_silu_fwd")
+    return u, so
+
+
+def mamba_conv1d_silu_update(state, x, w, conv_bias=None, *, out=None):
+    """One decode token of the conv1d + SiLU; state (batch, d_inner, d_conv - 1) is
+    updated in place.  Returns u (batch, d_inner)."""
+    torch = _torch()
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be (batch, d_inner)")
+    batch, d_inner = x.shape
+    if w.dim() != 2 or w.shape[0] != d_inner:
+        raise ValueError("w must be (d_inner, d_conv)")
+    d_conv = w.shape[1]
+    dev, act = x.device, x.dtype
+    code = _dtype_code(x)
+    p_s = _ptr(state, "state", (batch, d_inner, d_conv - 1), act, dev)
+    p_x = _ptr(x, "x", (batch, d_inner), act, dev)
+    p_w = _ptr(w, "w", (d_inner, d_conv), torch.float32, dev)
+    p_b = _ptr(conv_bias, "conv_bias", (d_inner,), torch.float32, dev)
+    u = out if out is not None else torch.empty((batch, d_inner), dtype=act, device=dev)
+    p_u = _ptr(u, "out", (batch, d_inner), act, dev)
+    st = lib.mamba_conv1d_silu_update(p_s, p_x, p_w, p_b, p_u, batch, d_inner, d_conv, code,
+                                      _stream(dev))
+    if st != 0:
+        raise MambaError(st, "mamba_conv1d_silu_update")
+    return u

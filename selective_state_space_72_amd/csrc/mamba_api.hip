@@ -529,4 +529,100 @@ mamba_status_t mamba_state_update(float *h, const void *u, const void *delta, co
     return hip_status(launch_state_update(S, reinterpret_cast<hipStream_t>(stream)));
 }
 
+mamba_status_t mamba_conv1d_silu_fwd(const void *x, const float *w, const float *conv_bias,
+                                     const void *state_in, void *u, void *state_out,
+                                     int64_t batch, int64_t seqlen, int64_t d_inner,
+                                     int64_t d_conv, mamba_dtype_t dtype, void *stream)
+{
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_conv < 1)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
+        return MAMBA_ERR_BAD_DTYPE;
+    if (d_conv < 2 || d_conv > 4)
+        return MAMBA_ERR_UNSUPPORTED;
+    const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
+    int64_t bld, bds, dk, t;
+    if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, d_inner, &bld) || !mul_ok(bld, es, &t) ||
+        !mul_ok(batch, d_inner, &t) || !mul_ok(t, d_conv - 1, &bds) || !mul_ok(bds, es, &t) ||
+        !mul_ok(d_inner, d_conv, &dk) || !mul_ok(dk, 4, &t) || d_inner > INT32_MAX ||
+        batch > 65535 || (seqlen + 127) / 128 > 65535)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (batch == 0 || d_inner == 0)
+        return MAMBA_OK;
+    if (!w || (seqlen > 0 && (!x || !u)))
+        return MAMBA_ERR_NULL_ARG;
+    if (!aligned(x, es) || !aligned(u, es) || !aligned(state_in, es) ||
+        !aligned(state_out, es) || !aligned(w, 4) || (conv_bias && !aligned(conv_bias, 4)))
+        return MAMBA_ERR_MISALIGNED;
+    const Range r_x = range_of(x, bld * es), r_u = range_of(u, bld * es);
+    const Range r_w = range_of(w, dk * 4), r_b = range_of(conv_bias, d_inner * 4);
+    const Range r_si = range_of(state_in, bds * es), r_so = range_of(state_out, bds * es);
+    if (overlaps(r_u, r_x) || overlaps(r_u, r_w) || overlaps(r_u, r_b) || overlaps(r_u, r_si) ||
+        overlaps(r_u, r_so) || overlaps(r_so, r_x) || overlaps(r_so, r_w) || overlaps(r_so, r_b))
+        return MAMBA_ERR_ALIASING;
+    if (overlaps(r_si, r_so) && state_in != state_out)
+        return MAMBA_ERR_ALIASING;
+
+    ConvLaunch P{};
+    P.x = x;
+    P.w = w;
+    P.bias = conv_bias;
+    P.state_in = state_in;
+    P.u = u;
+    P.state_out = state_out;
+    P.batch = batch;
+    P.L = seqlen;
+    P.d_inner = d_inner;
+    P.d_conv = d_conv;
+    P.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+    P.vec4 = d_inner % 4 == 0 && aligned(x, 4 * es) && aligned(u, 4 * es);
+    // (with seqlen == 0 the kernel only passes the state through)
+    if (seqlen == 0 && (!state_out || state_out == state_in))
+        return MAMBA_OK;
+    return hip_status(launch_conv1d_silu(P, reinterpret_cast<hipStream_t>(stream)));
+}
+
+mamba_status_t mamba_conv1d_silu_update(void *state, const void *x, const float *w,
+                                        const float *conv_bias, void *u, int64_t batch,
+                                        int64_t d_inner, int64_t d_conv, mamba_dtype_t dtype,
+                                        void *stream)
+{
+    if (batch < 0 || d_inner < 0 || d_conv < 1)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
+        return MAMBA_ERR_BAD_DTYPE;
+    if (d_conv < 2 || d_conv > 4)
+        return MAMBA_ERR_UNSUPPORTED;
+    const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
+    int64_t bd, bds, dk, t;
+    if (!mul_ok(batch, d_inner, &bd) || !mul_ok(bd, es, &t) || !mul_ok(bd, d_conv - 1, &bds) ||
+        !mul_ok(bds, es, &t) || !mul_ok(d_inner, d_conv, &dk) || !mul_ok(dk, 4, &t) ||
+        d_inner > INT32_MAX)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (bd == 0)
+        return MAMBA_OK;
+    if (!state || !x || !w || !u)
+        return MAMBA_ERR_NULL_ARG;
+    if (!aligned(state, es) || !aligned(x, es) || !aligned(u, es) || !aligned(w, 4) ||
+        (conv_bias && !aligned(conv_bias, 4)))
+        return MAMBA_ERR_MISALIGNED;
+    const Range r_s = range_of(state, bds * es), r_x = range_of(x, bd * es);
+    const Range r_u = range_of(u, bd * es), r_w = range_of(w, dk * 4);
+    const Range r_b = range_of(conv_bias, d_inner * 4);
+    if (overlaps(r_u, r_s) || overlaps(r_u, r_x) || overlaps(r_u, r_w) || overlaps(r_u, r_b) ||
+        overlaps(r_s, r_x) || overlaps(r_s, r_w) || overlaps(r_s, r_b))
+        return MAMBA_ERR_ALIASING;
+    ConvLaunch P{};
+    P.x = x;
+    P.w = w;
+    P.bias = conv_bias;
+    P.u = u;
+    P.state_out = state;
+    P.batch = batch;
+    P.d_inner = d_inner;
+    P.d_conv = d_conv;
+    P.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+    return hip_status(launch_conv1d_silu_update(P, reinterpret_cast<hipStream_t>(stream)));
+}
+
 } // extern "C"

@@ -58,6 +58,18 @@ struct CarryLaunch {
     int32_t n_spans;
 };
 
+// Causal depthwise conv1d + SiLU: prefill (x -> u, state_in -> state_out) or one
+// decode token (state_out is the in/out state).
+struct ConvLaunch {
+    const void *x;
+    const float *w, *bias;
+    const void *state_in;
+    void *u, *state_out;
+    int64_t batch, L, d_inner, d_conv;
+    DType dtype;
+    bool vec4; // 4 channels per lane (d_inner % 4 == 0, x and u 4-element aligned)
+};
+
 struct StepLaunch {
     float *h;
     const void *u, *delta, *z, *B, *C;
@@ -85,6 +97,8 @@ hipError_t launch_scalar_full(const ScanLaunch &p, hipStream_t stream);
 hipError_t launch_scalar_end(const ScanLaunch &p, hipStream_t stream);
 hipError_t launch_carry(const CarryLaunch &p, hipStream_t stream);
 hipError_t launch_state_update(const StepLaunch &p, hipStream_t stream);
+hipError_t launch_conv1d_silu(const ConvLaunch &p, hipStream_t stream);
+hipError_t launch_conv1d_silu_update(const ConvLaunch &p, hipStream_t stream);
 // h_last = h0 (or zeros when h0 is NULL), for empty sequences.
 hipError_t launch_copy_state(float *dst, const float *src, int64_t count, hipStream_t stream);
 

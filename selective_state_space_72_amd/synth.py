@@ -264,3 +264,36 @@ def make_decode_step(step: int, batch: int = DECODE["batch"], d_inner: int = DEC
     return DecodeStep(u=_normal(seed, (k, 0), bd, dtype), delta=_normal(seed, (k, 1), bd, dtype),
                       z=_normal(seed, (k, 2), bd, dtype), B=_normal(seed, (k, 3), bn, dtype),
                       C=_normal(seed, (k, 4), bn, dtype))
+
+
+# ----------------------------------------------------------------------------
+# causal depthwise conv1d + SiLU (the Mamba block's conv, upstream of the scan)
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class ConvInputs:
+    x: np.ndarray                  # (batch, L, d_inner), stored dtype
+    w: np.ndarray                  # (d_inner, d_conv) float32
+    bias: np.ndarray               # (d_inner,) float32
+    state: Optional[np.ndarray]    # (batch, d_inner, d_conv - 1), stored dtype
+    dtype: str
+
+
+def make_conv_inputs(batch: int, seqlen: int, d_inner: int, d_conv: int = 4,
+                     dtype: str = BF16, with_state: bool = True, seed: int = 7206) -> ConvInputs:
+    """x ~ N(0, 1) like the scan's activations; weights and bias drawn as nn.Conv1d
+    initialises them (uniform in +-1/sqrt(fan_in), fan_in = d_conv for a depthwise
+    filter), in float64 and rounded once; the carried state ~ N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    bound = 1.0 / np.sqrt(d_conv)
+    w = rng.uniform(-bound, bound, size=(d_inner, d_conv)).astype(np.float32)
+    bias = rng.uniform(-bound, bound, size=d_inner).astype(np.float32)
+    x = _normal(seed, (10,), (batch, seqlen, d_inner), dtype)
+    st = _normal(seed, (11,), (batch, d_inner, d_conv - 1), dtype) if with_state else None
+    return ConvInputs(x=x, w=w, bias=bias, state=st, dtype=dtype)
+
+
+def make_conv_step(step: int, batch: int, d_inner: int, dtype: str = BF16,
+                   seed: int = 7206) -> np.ndarray:
+    """One decode token's x (spawn keys (2000 + step, 10))."""
+    return _normal(seed, (2000 + step, 10), (batch, d_inner), dtype)

@@ -241,3 +241,40 @@ def test_default_plan_is_compiled_for_every_d_state(lib):
             b, L, d = shape
             assert lib.mamba_scan_fwd_workspace_size(b, L, d, n) != ctypes.c_size_t(-1).value, \
                 (n, shape)
+
+
+def conv(lib, *, x=BASE, w=BASE + 200 * MB, bias=None, si=None, u=BASE + 300 * MB, so=None,
+         batch=2, L=64, Dn=256, K=4, dtype=BF16):
+    return lib.mamba_conv1d_silu_fwd(x, w, bias, si, u, so, batch, L, Dn, K, dtype, None)
+
+
+def conv_step(lib, *, st=BASE, x=BASE + 100 * MB, w=BASE + 200 * MB, bias=None,
+              u=BASE + 300 * MB, batch=4, Dn=256, K=4, dtype=BF16):
+    return lib.mamba_conv1d_silu_update(st, x, w, bias, u, batch, Dn, K, dtype, None)
+
+
+def test_conv_validation(lib):
+    assert conv(lib, K=1) == UNSUP and conv(lib, K=5) == UNSUP
+    assert conv(lib, K=0) == SHAPE and conv(lib, L=-1) == SHAPE
+    assert conv(lib, batch=70000) == SHAPE
+    assert conv(lib, dtype=7) == DTYPE
+    assert conv(lib, w=None) == NULL and conv(lib, x=None) == NULL and conv(lib, u=None) == NULL
+    assert conv(lib, batch=0) == OK and conv(lib, Dn=0) == OK
+    assert conv(lib, L=0, x=None, u=None) == OK          # nothing to do without a state
+    assert conv(lib, x=BASE + 1) == ALIGN and conv(lib, w=BASE + 200 * MB + 2) == ALIGN
+    assert conv(lib, dtype=F32, u=BASE + 300 * MB + 2) == ALIGN
+    # u over x, over w, over a state; state_out over x; states partly overlapping
+    assert conv(lib, u=BASE + 100) == ALIAS
+    assert conv(lib, u=BASE + 200 * MB) == ALIAS
+    assert conv(lib, so=BASE + 300 * MB + 64) == ALIAS
+    assert conv(lib, so=BASE + 1024) == ALIAS
+    assert conv(lib, si=BASE + 400 * MB, so=BASE + 400 * MB + 2) == ALIAS
+
+
+def test_conv_update_validation(lib):
+    assert conv_step(lib, K=5) == UNSUP and conv_step(lib, K=0) == SHAPE
+    assert conv_step(lib, st=None) == NULL and conv_step(lib, u=None) == NULL
+    assert conv_step(lib, batch=0) == OK
+    assert conv_step(lib, x=BASE + 100 * MB + 1) == ALIGN
+    assert conv_step(lib, u=BASE) == ALIAS                 # u over the state
+    assert conv_step(lib, x=BASE + 64) == ALIAS            # state over x

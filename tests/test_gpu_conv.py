@@ -1,0 +1,164 @@
+"""HIP causal depthwise conv1d + SiLU (prefill and decode token) vs the fp64 oracle.
+
+Every call goes through the C-ABI library.  Tolerances as for the scan (metric in
+gpu_helpers.metric): 1e-5 for fp32, 2e-2 for bf16 (outputs rounded to bf16).
+States hold raw inputs and must match exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import DEV, TOL, from_dev, log, metric, to_dev
+import oracle
+import selective_state_space_72_amd as ms
+from selective_state_space_72_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from selective_state_space_72_amd import build as hip_build
+    if not hip_build.is_built():
+        hip_build.build()
+    ms.load_library()
+
+
+def f64(a, dtype):
+    return None if a is None else synth.to_f64(a, dtype)
+
+
+def run_and_check(name, ci, use_bias=True, use_state=True):
+    log(f"case {name}: x {ci.x.shape} K={ci.w.shape[1]} {ci.dtype} bias={use_bias} "
+        f"state={use_state and ci.state is not None}")
+    orc = oracle.load_conv()
+    st = ci.state if use_state else None
+    _, ur, sr = orc.conv(f64(ci.x, ci.dtype), ci.w.astype(np.float64),
+                         ci.bias.astype(np.float64) if use_bias else None, f64(st, ci.dtype))
+    u, so = ms.mamba_conv1d_silu_fwd(to_dev(ci.x), to_dev(ci.w),
+                                     to_dev(ci.bias) if use_bias else None, to_dev(st),
+                                     return_state=True)
+    torch.cuda.synchronize()
+    e = metric(from_dev(u), ur)
+    log(f"  {name}: u M={e:.3e}")
+    assert e <= TOL[ci.dtype], f"{name}: u error {e:.3e}"
+    assert np.array_equal(from_dev(so), sr), f"{name}: state differs"
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("shape", [(2, 37, 256), (3, 300, 1024), (1, 5, 70), (2, 129, 6),
+                                   (1, 2, 64), (2, 1, 12)])
+def test_conv_shapes(shape, K, dtype):
+    b, L, d = shape
+    ci = synth.make_conv_inputs(b, L, d, K, dtype, seed=100 + b * 7 + L + d + K)
+    run_and_check(f"{shape} K={K}", ci)
+    run_and_check(f"{shape} K={K} no bias/state", ci, use_bias=False, use_state=False)
+
+
+def test_conv_large_prefill_sampled():
+    """The large-prefill activation shape (8 x 4096 x 5120, bf16), sampled channels."""
+    ci = synth.make_conv_inputs(8, 4096, 5120, 4, synth.BF16, seed=7206)
+    u, so = ms.mamba_conv1d_silu_fwd(to_dev(ci.x), to_dev(ci.w), to_dev(ci.bias),
+                                     to_dev(ci.state), return_state=True)
+    rng = np.random.default_rng(7)
+    ds = np.unique(np.concatenate([[0, 3, 4, 5119], rng.choice(5120, 60, replace=False)]))
+    bs = np.array([0, 5, 7])
+    tb, td = torch.as_tensor(bs, device=DEV), torch.as_tensor(ds, device=DEV)
+    ug = from_dev(u.index_select(0, tb).index_select(2, td))
+    sg = from_dev(so.index_select(0, tb).index_select(1, td))
+    orc = oracle.load_conv()
+    xs = np.ascontiguousarray(ci.x[bs][:, :, ds])
+    ss = np.ascontiguousarray(ci.state[bs][:, ds])
+    _, ur, sr = orc.conv(f64(xs, ci.dtype), ci.w[ds].astype(np.float64),
+                         ci.bias[ds].astype(np.float64), f64(ss, ci.dtype))
+    e = metric(ug, ur)
+    log(f"  large prefill conv: u M={e:.3e}")
+    assert e <= TOL[synth.BF16]
+    assert np.array_equal(sg, sr)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_conv_in_place_continuation(dtype):
+    """Two segments with state_in == state_out equal one call (bitwise)."""
+    ci = synth.make_conv_inputs(2, 300, 512, 4, dtype, seed=3)
+    x, w, bias = to_dev(ci.x), to_dev(ci.w), to_dev(ci.bias)
+    u_full, s_full = ms.mamba_conv1d_silu_fwd(x, w, bias, to_dev(ci.state), return_state=True)
+    st = to_dev(ci.state)
+    us = []
+    for lo, hi in ((0, 2), (2, 131), (131, 300)):  # a first segment shorter than d_conv - 1
+        u, _ = ms.mamba_conv1d_silu_fwd(x[:, lo:hi].contiguous(), w, bias, st, state_out=st)
+        us.append(u)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(us, dim=1), u_full)
+    assert torch.equal(st, s_full)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_conv_empty_sequence_passes_state(dtype):
+    ci = synth.make_conv_inputs(2, 0, 64, 4, dtype, seed=4)
+    x = torch.empty((2, 0, 64), dtype=to_dev(ci.state).dtype, device=DEV)
+    _, so = ms.mamba_conv1d_silu_fwd(x, to_dev(ci.w), to_dev(ci.bias), to_dev(ci.state),
+                                     return_state=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(so), synth.to_f64(ci.state, dtype))
+    _, so0 = ms.mamba_conv1d_silu_fwd(x, to_dev(ci.w), to_dev(ci.bias), None, return_state=True)
+    torch.cuda.synchronize()
+    assert not from_dev(so0).any()
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_conv_decode_steps(dtype):
+    """Chained decode tokens equal the oracle's steps and, bitwise, the GPU prefill."""
+    b, d, K, steps = 4, 640, 4, 50
+    ci = synth.make_conv_inputs(b, 0, d, K, dtype, seed=5)
+    w, bias = to_dev(ci.w), to_dev(ci.bias)
+    st = to_dev(ci.state)
+    st_ref = synth.to_f64(ci.state, dtype)
+    orc = oracle.load_conv()
+    xs, us = [], []
+    worst = 0.0
+    for s in range(steps):
+        xt = synth.make_conv_step(s, b, d, dtype, seed=5)
+        xs.append(xt)
+        u = ms.mamba_conv1d_silu_update(st, to_dev(xt), w, bias)
+        us.append(u)
+        _, ur, st_ref = orc.step(st_ref, synth.to_f64(xt, dtype), ci.w.astype(np.float64),
+                                 ci.bias.astype(np.float64))
+        worst = max(worst, metric(from_dev(u), ur))
+    torch.cuda.synchronize()
+    log(f"  decode conv {dtype}: worst u M={worst:.3e}")
+    assert worst <= TOL[dtype]
+    assert np.array_equal(from_dev(st), st_ref)
+    xall = to_dev(np.ascontiguousarray(np.stack(xs, axis=1)))
+    u_pf, s_pf = ms.mamba_conv1d_silu_fwd(xall, w, bias, to_dev(ci.state), return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.stack(us, dim=1), u_pf)
+    assert torch.equal(s_pf, st)
+
+
+def test_conv_then_scan_matches_oracle_pipeline():
+    """GPU conv1d + SiLU feeding the GPU scan equals the oracle conv feeding the oracle scan."""
+    import dataclasses
+    from gpu_helpers import DevInputs, oracle_scan
+    cfg = dataclasses.replace(synth.CONFIGS["c3"], h0=True)
+    inp = synth.make_scan_inputs(cfg, batch=2, seqlen=500, d_inner=192, seed=12)
+    ci = synth.make_conv_inputs(2, 500, 192, 4, synth.BF16, seed=13)
+    u_gpu, _ = ms.mamba_conv1d_silu_fwd(to_dev(ci.x), to_dev(ci.w), to_dev(ci.bias),
+                                        to_dev(ci.state))
+    torch.cuda.synchronize()
+    # the oracle side rounds its u to bf16, the scan's input format, as the GPU stores it;
+    # where a rounding falls differently the two u differ by one bf16 ulp, which the bf16
+    # tolerance covers
+    _, u_ref, _ = oracle.load_conv().conv(f64(ci.x, synth.BF16), ci.w.astype(np.float64),
+                                          ci.bias.astype(np.float64), f64(ci.state, synth.BF16))
+    di = DevInputs(inp)
+    di.u = u_gpu
+    y, h = di.run()
+    inp_ref = dataclasses.replace(inp, u=synth.f32_to_bf16_bits(u_ref.astype(np.float32)))
+    yr, hr = oracle_scan(inp_ref)
+    ey, eh = metric(from_dev(y), yr), metric(from_dev(h), hr)
+    log(f"  conv -> scan: y M={ey:.3e}, h M={eh:.3e}")
+    assert ey <= TOL[synth.BF16] and eh <= TOL[synth.BF16]
