@@ -50,9 +50,9 @@ class Oracle:
         self.path = path
         lib = ctypes.CDLL(path)
         lib.oracle_scan.restype = ctypes.c_int
-        lib.oracle_scan.argtypes = [_dp] * 11 + [_i64] * 4 + [ctypes.c_int]
+        lib.oracle_scan.argtypes = [_dp] * 11 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_step.restype = ctypes.c_int
-        lib.oracle_step.argtypes = [_dp] * 10 + [_i64] * 3
+        lib.oracle_step.argtypes = [_dp] * 10 + [_i64] * 3 + [ctypes.c_int]
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
@@ -68,8 +68,8 @@ class Oracle:
 
     # -- full scan ------------------------------------------------------------
     def scan(self, u, delta, A, B, C, D=None, z=None, bias=None, h0=None,
-             nthreads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
-        """Return (y, h_last) in float64.
+             nthreads: Optional[int] = None, zoh: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+        """Return (y, h_last) in float64 (zoh: zero-order-hold Bbar instead of Euler's).
 
         u, delta, z: (batch, L, d_inner); B, C: (batch, L, d_state);
         A: (d_inner, d_state); D, bias: (d_inner,); h0: (batch, d_inner, d_state).
@@ -94,13 +94,13 @@ class Oracle:
             nthreads = default_threads()
         rc = self._lib.oracle_scan(_p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
                                    _p(bias), _p(h0), _p(y), _p(h_last), batch, L, d_inner,
-                                   d_state, int(nthreads))
+                                   d_state, int(nthreads), int(bool(zoh)))
         if rc != 0:
             raise ValueError("oracle_scan rejected its arguments")
         return y, h_last
 
     # -- one decode step ------------------------------------------------------
-    def step(self, h, u, delta, A, B, C, D=None, z=None, bias=None
+    def step(self, h, u, delta, A, B, C, D=None, z=None, bias=None, zoh: bool = False
              ) -> Tuple[np.ndarray, np.ndarray]:
         """Return (y, h_new); h is not modified.  u, delta, z: (batch, d_inner);
         B, C: (batch, d_state); h: (batch, d_inner, d_state)."""
@@ -118,7 +118,8 @@ class Oracle:
         _check(z, u.shape, "z")
         y = np.empty(u.shape, dtype=np.float64)
         rc = self._lib.oracle_step(_p(h_new), _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
-                                   _p(z), _p(bias), _p(y), batch, d_inner, d_state)
+                                   _p(z), _p(bias), _p(y), batch, d_inner, d_state,
+                                   int(bool(zoh)))
         if rc != 0:
             raise ValueError("oracle_step rejected its arguments")
         return y, h_new

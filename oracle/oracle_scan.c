@@ -29,8 +29,11 @@
  *   h_last[b,d,:] = h_{L-1}
  *
  * Readings taken where the pages disagree or are silent: softplus is applied
- * exactly once; Bbar is the Euler form Delta*B used by all of the pages' code
- * (not the zero-order-hold formula of their equations); y_t reads the state
+ * exactly once; Bbar is the Euler form Delta*B used by all of the pages' code,
+ * and on request (zoh != 0) the zero-order hold of their equations,
+ * Bbar = A^-1 (exp(Delta A) - I) B ("Understanding Mamba" section 12; "State
+ * Space Models and Mamba", ZOH), i.e. (exp(Delta A[d,n]) - 1) / A[d,n] * B[n] for
+ * the diagonal A, with the A -> 0 limit Delta*B; y_t reads the state
  * after the update with u_t; D*u uses the raw u and is added before the gate;
  * a missing D, bias or h0 means zero and a missing z means no gate.  All
  * arithmetic is double precision with libm exp/log1p and nothing is rounded to
@@ -62,7 +65,17 @@ typedef struct {
     double *y, *h_last;
     int64_t batch, L, Dn, N;
     int64_t chan_begin, chan_end; /* channel index c = b * Dn + d */
+    int zoh;
 } scan_job;
+
+/* Bbar[n] for step size dt, state coefficient a = A[d,n] and input coefficient b = B[n]:
+ * Euler dt * b, or the zero-order hold (exp(dt a) - 1) / a * b (limit dt * b at a = 0). */
+static double oracle_bbar(double dt, double a, double b, int zoh)
+{
+    if (!zoh || a == 0.0)
+        return dt * b;
+    return expm1(dt * a) / a * b;
+}
 
 static void scan_channels(const scan_job *j)
 {
@@ -84,7 +97,7 @@ static void scan_channels(const scan_job *j)
             /* discretise and advance the state */
             for (int64_t n = 0; n < N; ++n) {
                 const double abar = exp(dt * j->A[d * N + n]);
-                const double bbar = dt * j->B[bln + n];
+                const double bbar = oracle_bbar(dt, j->A[d * N + n], j->B[bln + n], j->zoh);
                 h[n] = abar * h[n] + bbar * ut;
             }
 
@@ -116,12 +129,13 @@ static void *scan_thread(void *arg)
  * Layouts (row-major, last index fastest): u, delta, z, y: (batch, L, d_inner);
  * B, C: (batch, L, d_state); A: (d_inner, d_state); D, bias: (d_inner);
  * h0, h_last: (batch, d_inner, d_state).  D, z, bias, h0 and h_last may be NULL.
+ * zoh selects the zero-order-hold Bbar instead of Euler's.
  * Returns 0, or -1 on a bad argument.
  */
 int oracle_scan(const double *u, const double *delta, const double *A, const double *B,
                 const double *C, const double *D, const double *z, const double *bias,
                 const double *h0, double *y, double *h_last, int64_t batch, int64_t L,
-                int64_t d_inner, int64_t d_state, int nthreads)
+                int64_t d_inner, int64_t d_state, int nthreads, int zoh)
 {
     if (batch < 0 || L < 0 || d_inner < 0 || d_state < 0)
         return -1;
@@ -148,6 +162,7 @@ int oracle_scan(const double *u, const double *delta, const double *A, const dou
         j->batch = batch; j->L = L; j->Dn = d_inner; j->N = d_state;
         j->chan_begin = chans * i / nthreads;
         j->chan_end = chans * (i + 1) / nthreads;
+        j->zoh = zoh;
     }
     for (int i = 1; i < nthreads; ++i)
         pthread_create(&tids[i], NULL, scan_thread, &jobs[i]);
@@ -168,7 +183,8 @@ int oracle_scan(const double *u, const double *delta, const double *A, const dou
  */
 int oracle_step(double *h, const double *u, const double *delta, const double *A,
                 const double *B, const double *C, const double *D, const double *z,
-                const double *bias, double *y, int64_t batch, int64_t d_inner, int64_t d_state)
+                const double *bias, double *y, int64_t batch, int64_t d_inner, int64_t d_state,
+                int zoh)
 {
     if (!h || !u || !delta || !A || !B || !C || !y || batch < 0 || d_inner < 0 || d_state < 0)
         return -1;
@@ -180,7 +196,7 @@ int oracle_step(double *h, const double *u, const double *delta, const double *A
             const double dt = oracle_softplus(delta[bd] + (bias ? bias[d] : 0.0));
             for (int64_t n = 0; n < d_state; ++n) {
                 const double abar = exp(dt * A[d * d_state + n]);
-                const double bbar = dt * B[b * d_state + n];
+                const double bbar = oracle_bbar(dt, A[d * d_state + n], B[b * d_state + n], zoh);
                 hb[n] = abar * hb[n] + bbar * ut;
             }
             double yt = 0.0;

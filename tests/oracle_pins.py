@@ -307,6 +307,98 @@ def pin_empty_and_threads(orc):
     assert np.array_equal(y1, y3) and np.array_equal(h1, h3)
 
 
+def _rk4_linear(a, f, h, T, m):
+    """Integrate h' = a h + f (constants) over [0, T] with m classical RK4 steps."""
+    dt = T / m
+    for _ in range(m):
+        k1 = a * h + f
+        k2 = a * (h + 0.5 * dt * k1) + f
+        k3 = a * (h + 0.5 * dt * k2) + f
+        k4 = a * (h + dt * k3) + f
+        h = h + dt / 6.0 * (k1 + 2 * k2 + 2 * k3 + k4)
+    return h
+
+
+def pin_zoh_samples_the_ode(orc):
+    """Zero-order hold is exact for inputs held constant over each step: the ZOH scan's
+    states equal a numerical integration (RK4, fine steps) of h' = A h + B_t u_t over
+    consecutive intervals of length Delta_t ("State Space Models and Mamba", ZOH;
+    "Understanding Mamba" section 12)."""
+    rng = np.random.default_rng(31)
+    case = random_case(rng, batch=1, L=12, Dn=3, N=4, gate=False, with_D=False)
+    y, h_last = orc.scan(**case, zoh=True)
+    u, delta, A, B, C, h0, bias = (case[k] for k in ("u", "delta", "A", "B", "C", "h0", "bias"))
+    for d in range(3):
+        h = h0[0, d].copy()
+        for t in range(12):
+            dt = ref_softplus(delta[0, t, d] + bias[d])
+            h = _rk4_linear(A[d], B[0, t] * u[0, t, d], h, dt, 400)
+            assert rel_err(y[0, t, d], np.dot(C[0, t], h)) < 1e-9, (d, t)
+        assert rel_err(h_last[0, d], h) < 1e-9, d
+    # and it is not the Euler rule
+    y_e, _ = orc.scan(**case)
+    assert rel_err(y_e, y) > 1e-3
+
+
+def pin_zoh_limits(orc):
+    """A = 0 gives Euler exactly; as Delta -> 0 the two rules agree to first order
+    (relative gap ~ |Delta A| / 2 per step)."""
+    rng = np.random.default_rng(32)
+    case = random_case(rng, L=9, Dn=4, N=3)
+    case["A"] = np.zeros_like(case["A"])
+    y_z, h_z = orc.scan(**case, zoh=True)
+    y_e, h_e = orc.scan(**case)
+    assert np.array_equal(y_z, y_e) and np.array_equal(h_z, h_e)
+    # tiny steps: one step from a zero state, Bbar_zoh / Bbar_euler = expm1(x)/x, x = Delta A
+    case = random_case(rng, batch=1, L=1, Dn=4, N=3, gate=False, with_h0=False, with_D=False)
+    case["delta"] = np.full((1, 1, 4), -12.0)   # Delta ~ 6e-6 (with the case's bias)
+    case["bias"] = np.zeros(4)
+    _, hz = orc.scan(**case, zoh=True)
+    _, he = orc.scan(**case)
+    dt = ref_softplus(-12.0)
+    ratio = hz[0] / he[0]
+    expect = 1.0 + dt * case["A"] / 2.0
+    assert np.allclose(ratio, expect, rtol=0, atol=1e-9)
+
+
+def pin_zoh_lti_convolution(orc):
+    """Constant Delta, B, C with ZOH: y = causal conv(K, u), K_k = C Abar^k Bbar with
+    Bbar = (Abar - 1) / A * B, Abar^k = exp(k Delta A)."""
+    rng = np.random.default_rng(33)
+    batch, L, Dn, N = 1, 64, 3, 5
+    A = -rng.uniform(0.05, 3.0, size=(Dn, N))
+    dt_const = rng.uniform(0.05, 0.8, size=Dn)
+    delta = np.broadcast_to(np.log(np.expm1(dt_const)), (batch, L, Dn)).copy()
+    Bc, Cc = rng.standard_normal(N), rng.standard_normal(N)
+    B = np.broadcast_to(Bc, (batch, L, N)).copy()
+    C = np.broadcast_to(Cc, (batch, L, N)).copy()
+    u = rng.standard_normal((batch, L, Dn))
+    y, _ = orc.scan(u=u, delta=delta, A=A, B=B, C=C, zoh=True)
+    k = np.arange(L)
+    for d in range(Dn):
+        dl = ref_softplus(delta[0, 0, d])
+        abar = np.exp(dl * A[d])
+        K = np.exp(np.outer(k, dl * A[d])) @ (Cc * (abar - 1.0) / A[d] * Bc)
+        ref = np.convolve(u[0, :, d], K)[:L]
+        assert rel_err(y[0, :, d], ref) < 1e-10, d
+
+
+def pin_zoh_decode_equals_scan(orc):
+    """Chained ZOH decode steps reproduce the ZOH scan exactly."""
+    rng = np.random.default_rng(34)
+    case = random_case(rng, L=15)
+    y, h_last = orc.scan(**case, zoh=True)
+    h = case["h0"].copy()
+    for t in range(15):
+        yt, h = orc.step(h, case["u"][:, t], case["delta"][:, t], case["A"], case["B"][:, t],
+                         case["C"][:, t], D=case["D"], z=case["z"][:, t], bias=case["bias"],
+                         zoh=True)
+        assert np.array_equal(yt, y[:, t]), t
+    assert np.array_equal(h, h_last)
+
+
 PINS = [pin_worked_example, pin_brute_force, pin_lti_convolution, pin_lti_fft_long,
         pin_zero_input_decay, pin_special_cases, pin_split_invariance, pin_decode_equals_scan,
-        pin_linearity_causality, pin_scalar_closed_forms, pin_empty_and_threads]
+        pin_linearity_causality, pin_scalar_closed_forms, pin_empty_and_threads,
+        pin_zoh_samples_the_ode, pin_zoh_limits, pin_zoh_lti_convolution,
+        pin_zoh_decode_equals_scan]

@@ -19,11 +19,14 @@ MUTANTS = [
                           "const double abar = exp(j->A[d * N + n]);")]),
     ("A_transposed", [("const double abar = exp(dt * j->A[d * N + n]);",
                        "const double abar = exp(dt * j->A[n * Dn + d]);")]),
-    ("bbar_drops_delta", [("const double bbar = dt * j->B[bln + n];",
-                           "const double bbar = j->B[bln + n];")]),
-    ("B_C_swapped", [("const double bbar = dt * j->B[bln + n];",
-                      "const double bbar = dt * j->C[bln + n];"),
+    ("bbar_drops_delta", [("        return dt * b;\n", "        return b;\n")]),
+    ("B_C_swapped", [("oracle_bbar(dt, j->A[d * N + n], j->B[bln + n], j->zoh)",
+                      "oracle_bbar(dt, j->A[d * N + n], j->C[bln + n], j->zoh)"),
                      ("yt += j->C[bln + n] * h[n];", "yt += j->B[bln + n] * h[n];")]),
+    ("zoh_drops_inverse_A", [("return expm1(dt * a) / a * b;", "return expm1(dt * a) * b;")]),
+    ("zoh_exp_not_expm1", [("return expm1(dt * a) / a * b;", "return exp(dt * a) / a * b;")]),
+    ("zoh_ignored", [("    if (!zoh || a == 0.0)", "    if (1)")]),
+    ("zoh_extra_delta", [("return expm1(dt * a) / a * b;", "return dt * expm1(dt * a) / a * b;")]),
     ("C_previous_step", [("yt += j->C[bln + n] * h[n];",
                           "yt += j->C[(bln >= N ? bln - N : bln) + n] * h[n];")]),
     ("readout_before_update", [
@@ -47,8 +50,8 @@ MUTANTS = [
                              "j->h_last[(b * Dn + d) * N + n] = h[0];")]),
     ("u_from_wrong_channel", [("const double ut = j->u[bld];",
                                "const double ut = j->u[bld - d];")]),
-    ("step_drops_delta_in_bbar", [("const double bbar = dt * B[b * d_state + n];",
-                                   "const double bbar = B[b * d_state + n];")]),
+    ("step_drops_delta_in_bbar", [("oracle_bbar(dt, A[d * d_state + n], B[b * d_state + n], zoh)",
+                                   "B[b * d_state + n]")]),
     ("step_no_gate", [("            if (z)\n                yt *= oracle_silu(z[bd]);\n", "")]),
 ]
 
