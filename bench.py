@@ -219,13 +219,14 @@ def extra_workloads(dev, flush, steps):
     import selective_state_space_72_amd as ms
     from selective_state_space_72_amd import synth
     out = {}
-    for name in ("c2", "c4"):
-        cfg = synth.CONFIGS[name]
-        case = ScanCase(cfg, dev)
+    for name, opts in (("c2", {}), ("c4", {}), ("c3_zoh", dict(discretization="zoh"))):
+        cfg = synth.CONFIGS[name.split("_")[0]]
+        case = ScanCase(cfg, dev, **opts)
         loop_ms, med, _ = time_steps(case.step, steps, 10, flush, warm_ms=100.0)
         ms_used = med if med is not None else loop_ms
         out[name] = {"workload": f"{cfg.desc}: batch {cfg.batch}, L {cfg.seqlen}, d_inner "
-                                 f"{cfg.d_inner}, d_state {cfg.d_state}, {cfg.dtype}",
+                                 f"{cfg.d_inner}, d_state {cfg.d_state}, {cfg.dtype}"
+                                 + (", zero-order-hold discretisation" if opts else ""),
                      "ms": round(ms_used, 4), "ms_back_to_back": round(loop_ms, 4),
                      "GB_s": round(case.min_bytes / (ms_used * 1e-3) / 1e9, 1),
                      "gchan_steps_per_s": round(cfg.chan_steps / (ms_used * 1e-3) / 1e9, 2),

@@ -111,15 +111,29 @@ typedef enum {
  *               0 = auto (two parts, when it evens out the load), 1 = off,
  *               2..8 = that many equal parts (when no units are left over, every
  *               unit is split; for testing).
- * Every supported setting gives the same result up to float32 rounding; an
- * unsupported one makes the call return MAMBA_ERR_UNSUPPORTED. */
+ *   discretization : MAMBA_DISC_EULER (0, default) or MAMBA_DISC_ZOH; the zero-
+ *               order hold needs the SCALAR family (AUTO selects it).
+ * Every supported setting of the other fields gives the same result up to
+ * float32 rounding; an unsupported one makes the call return
+ * MAMBA_ERR_UNSUPPORTED. */
 typedef struct {
     int32_t chunk_len;
     int32_t waves;
     int32_t n_spans;
     int32_t kernel;
     int32_t relay;
+    int32_t discretization;
 } mamba_scan_opts_t;
+
+/* Discretisation of the input matrix (mamba_scan_opts_t.discretization and
+ * mamba_state_update_ex):
+ *   EULER: Bbar = Delta * B, as all of the pages' selective_scan code does;
+ *   ZOH:   Bbar = A^-1 (exp(Delta A) - I) B = (exp(Delta A[d,n]) - 1) / A[d,n] * B[n],
+ *          the zero-order hold of "Understanding Mamba" section 12 and of "State
+ *          Space Models and Mamba" (ZOH); Delta * B where A[d,n] = 0 (the limit).
+ * Abar = exp(Delta A) in both. */
+#define MAMBA_DISC_EULER 0
+#define MAMBA_DISC_ZOH 1
 
 /* Returns 1 if d_state is supported by this build, else 0. */
 MAMBA_API int32_t mamba_d_state_supported(int64_t d_state);
@@ -251,6 +265,16 @@ MAMBA_API mamba_status_t mamba_conv1d_silu_update(void *state, const void *x, co
                                                   const float *conv_bias, void *u,
                                                   int64_t batch, int64_t d_inner, int64_t d_conv,
                                                   mamba_dtype_t dtype, void *stream);
+
+/* mamba_state_update with a choice of discretisation (MAMBA_DISC_*); anything
+ * else returns MAMBA_ERR_UNSUPPORTED. */
+MAMBA_API mamba_status_t mamba_state_update_ex(float *h, const void *u, const void *delta,
+                                               const float *A, const void *B, const void *C,
+                                               const float *D, const void *z,
+                                               const float *delta_bias, void *y, int64_t batch,
+                                               int64_t d_inner, int64_t d_state,
+                                               mamba_dtype_t dtype, int32_t discretization,
+                                               void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 MAMBA_API const char *mamba_status_string(mamba_status_t status);

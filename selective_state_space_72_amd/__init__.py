@@ -33,7 +33,8 @@ STATUS = {
 # Every symbol include/mamba_scan.h declares.
 EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_scan_fwd_workspace_size_ex", "mamba_scan_fwd", "mamba_scan_fwd_ex",
-           "mamba_state_update", "mamba_conv1d_silu_fwd", "mamba_conv1d_silu_update",
+           "mamba_state_update", "mamba_state_update_ex", "mamba_conv1d_silu_fwd",
+           "mamba_conv1d_silu_update",
            "mamba_status_string")
 
 
@@ -48,10 +49,14 @@ KERNELS = {"auto": MAMBA_KERNEL_AUTO, "block": MAMBA_KERNEL_BLOCK, "rows": MAMBA
            "scalar": MAMBA_KERNEL_SCALAR}
 
 
+MAMBA_DISC_EULER, MAMBA_DISC_ZOH = 0, 1
+DISCRETIZATIONS = {"euler": MAMBA_DISC_EULER, "zoh": MAMBA_DISC_ZOH}
+
+
 class ScanOpts(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("n_spans", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("relay", ctypes.c_int32)]
+                ("relay", ctypes.c_int32), ("discretization", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -84,6 +89,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                        ctypes.POINTER(ScanOpts), _vp])
     lib.mamba_state_update.restype = ctypes.c_int
     lib.mamba_state_update.argtypes = [_vp] * 10 + [_i64] * 3 + [ctypes.c_int, _vp]
+    lib.mamba_state_update_ex.restype = ctypes.c_int
+    lib.mamba_state_update_ex.argtypes = ([_vp] * 10 + [_i64] * 3 +
+                                          [ctypes.c_int, ctypes.c_int32, _vp])
     lib.mamba_conv1d_silu_fwd.restype = ctypes.c_int
     lib.mamba_conv1d_silu_fwd.argtypes = [_vp] * 6 + [_i64] * 4 + [ctypes.c_int, _vp]
     lib.mamba_conv1d_silu_update.restype = ctypes.c_int
@@ -142,17 +150,21 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _opts(chunk_len=0, waves=0, n_spans=0, kernel="auto", relay=0):
+def _opts(chunk_len=0, waves=0, n_spans=0, kernel="auto", relay=0, discretization="euler"):
     if kernel not in KERNELS:
         raise ValueError(f"kernel must be one of {sorted(KERNELS)}")
-    return ScanOpts(int(chunk_len), int(waves), int(n_spans), KERNELS[kernel], int(relay))
+    if discretization not in DISCRETIZATIONS:
+        raise ValueError(f"discretization must be one of {sorted(DISCRETIZATIONS)}")
+    return ScanOpts(int(chunk_len), int(waves), int(n_spans), KERNELS[kernel], int(relay),
+                    DISCRETIZATIONS[discretization])
 
 
 def mamba_scan_fwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state: int,
                                   chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
-                                  kernel: str = "auto", relay: int = 0) -> int:
+                                  kernel: str = "auto", relay: int = 0,
+                                  discretization: str = "euler") -> int:
     lib = load_library()
-    o = _opts(chunk_len, waves, n_spans, kernel, relay)
+    o = _opts(chunk_len, waves, n_spans, kernel, relay, discretization)
     n = lib.mamba_scan_fwd_workspace_size_ex(batch, seqlen, d_inner, d_state, ctypes.byref(o))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes or options for mamba_scan_fwd")
@@ -162,7 +174,8 @@ def mamba_scan_fwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state
 def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
                    return_last_state: bool = False, *, out=None, h_last_out=None,
                    chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
-                   kernel: str = "auto", relay: int = 0, workspace=None) -> Tuple:
+                   kernel: str = "auto", relay: int = 0, discretization: str = "euler",
+                   workspace=None) -> Tuple:
     """Selective scan over (batch, seqlen, d_inner); see include/mamba_scan.h.
 
     Returns (y, h_last) -- h_last is None unless return_last_state (or h_last_out).
@@ -195,7 +208,7 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
         h_last = torch.empty((batch, d_inner, d_state), dtype=f32, device=dev)
     p_hl = _ptr(h_last, "h_last_out", (batch, d_inner, d_state), f32, dev)
 
-    opts = _opts(chunk_len, waves, n_spans, kernel, relay)
+    opts = _opts(chunk_len, waves, n_spans, kernel, relay, discretization)
     need = lib.mamba_scan_fwd_workspace_size_ex(batch, seqlen, d_inner, d_state,
                                                 ctypes.byref(opts))
     if need == ctypes.c_size_t(-1).value:
@@ -213,7 +226,8 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
     return y, h_last
 
 
-def mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None):
+def mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None,
+                       discretization: str = "euler"):
     """One decode step; h (batch, d_inner, d_state) fp32 is updated in place.  Returns y."""
     torch = _torch()
     lib = load_library()
@@ -236,8 +250,11 @@ def mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
     p_bias = _ptr(delta_bias, "delta_bias", (d_inner,), f32, dev)
     y = out if out is not None else torch.empty((batch, d_inner), dtype=act, device=dev)
     p_y = _ptr(y, "out", (batch, d_inner), act, dev)
-    st = lib.mamba_state_update(p_h, p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_y,
-                                batch, d_inner, d_state, code, _stream(dev))
+    if discretization not in DISCRETIZATIONS:
+        raise ValueError(f"discretization must be one of {sorted(DISCRETIZATIONS)}")
+    st = lib.mamba_state_update_ex(p_h, p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_y,
+                                   batch, d_inner, d_state, code,
+                                   DISCRETIZATIONS[discretization], _stream(dev))
     if st != 0:
         raise MambaError(st, "mamba_state_update")
     return y

@@ -76,6 +76,7 @@ struct Plan {
     int relay_parts;      // 1: no relay
     int64_t relay_tiles;  // relayed (batch row, tile) units
     int64_t relay_len;    // steps per relay part (a multiple of chunk)
+    bool zoh;             // zero-order-hold discretisation (scalar family only)
 };
 
 // Launch plan.  Channel tiles of 64 lanes x `waves` waves are the unit of parallel work;
@@ -87,14 +88,24 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     Plan p{};
     const int cus = cu_count();
     const int fam = opts ? opts->kernel : MAMBA_KERNEL_AUTO;
+    const int disc = opts ? opts->discretization : MAMBA_DISC_EULER;
+    if (disc != MAMBA_DISC_EULER && disc != MAMBA_DISC_ZOH)
+        return MAMBA_ERR_UNSUPPORTED;
+    p.zoh = disc == MAMBA_DISC_ZOH;
     Family autof = auto_family(batch, d_inner, d_state, cus);
     if (autof == Family::Scalar && !scalar_span_ok(seqlen, d_inner))
         autof = Family::Rows;
+    if (p.zoh) {
+        // the zero-order hold is implemented in the scalar-B/C family only
+        if (fam == MAMBA_KERNEL_ROWS || fam == MAMBA_KERNEL_BLOCK)
+            return MAMBA_ERR_UNSUPPORTED;
+        autof = Family::Scalar;
+    }
     if (fam == MAMBA_KERNEL_AUTO && opts && (opts->waves || opts->chunk_len)) {
         // an explicit block shape: the scalar family if it has it, else the block family
         const int w = opts->waves ? opts->waves : scalar_default_waves(d_state);
         const int c = opts->chunk_len ? opts->chunk_len : scalar_default_chunk(d_state);
-        autof = scalar_variant_supported(d_state, w, c) ? Family::Scalar : Family::Block;
+        autof = scalar_variant_supported(d_state, w, c) || p.zoh ? Family::Scalar : Family::Block;
     }
     if (fam == MAMBA_KERNEL_ROWS || (fam == MAMBA_KERNEL_AUTO && autof == Family::Rows)) {
         if ((opts && (opts->waves || opts->chunk_len)))
@@ -379,6 +390,7 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
     L.waves = plan.waves;
     L.chunk = plan.chunk;
     L.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+    L.zoh = plan.zoh;
 
     auto full = [&](const ScanLaunch &x) {
         switch (plan.family) {
@@ -474,6 +486,18 @@ mamba_status_t mamba_state_update(float *h, const void *u, const void *delta, co
                                   int64_t d_inner, int64_t d_state, mamba_dtype_t dtype,
                                   void *stream)
 {
+    return mamba_state_update_ex(h, u, delta, A, B, C, D, z, delta_bias, y, batch, d_inner,
+                                 d_state, dtype, MAMBA_DISC_EULER, stream);
+}
+
+mamba_status_t mamba_state_update_ex(float *h, const void *u, const void *delta,
+                                     const float *A, const void *B, const void *C,
+                                     const float *D, const void *z, const float *delta_bias,
+                                     void *y, int64_t batch, int64_t d_inner, int64_t d_state,
+                                     mamba_dtype_t dtype, int32_t discretization, void *stream)
+{
+    if (discretization != MAMBA_DISC_EULER && discretization != MAMBA_DISC_ZOH)
+        return MAMBA_ERR_UNSUPPORTED;
     if (batch < 0 || d_inner < 0 || d_state <= 0)
         return MAMBA_ERR_BAD_SHAPE;
     if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
@@ -526,6 +550,7 @@ mamba_status_t mamba_state_update(float *h, const void *u, const void *delta, co
     S.d_inner = d_inner;
     S.d_state = d_state;
     S.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+    S.zoh = discretization == MAMBA_DISC_ZOH;
     return hip_status(launch_state_update(S, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -36,6 +36,7 @@ struct ScanLaunch {
     float *relay_state;         // [slot][n][lane], slot = tile * (parts - 1) + part
     int32_t relay_tiles, relay_parts;
     int64_t relay_len;
+    bool zoh; // zero-order-hold Bbar (scalar family); Euler otherwise
 };
 
 // Relay arguments as the scan kernel receives them.
@@ -77,6 +78,7 @@ struct StepLaunch {
     void *y;
     int64_t batch, d_inner, d_state;
     DType dtype;
+    bool zoh;
 };
 
 // Returns true if the (d_state, waves, chunk) combination is compiled in.

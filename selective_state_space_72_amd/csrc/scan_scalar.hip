@@ -106,7 +106,7 @@ __device__ __forceinline__ void relay_wait(uint32_t *flag)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED>
+template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED, bool ZOH>
 __global__ void __launch_bounds__(64 * NW)
 scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                    const T *__restrict__ z, const float *__restrict__ bcp,
@@ -127,7 +127,9 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     // Double-buffered by chunk parity so that one barrier per chunk suffices: chunk c's
     // prologue writes s_dw[c&1]; after the barrier every wave finishes chunk c-1 from
     // s_yp[(c-1)&1] and scans chunk c into s_yp[c&1].
-    __shared__ float2 s_dw[2][TC][64];               // (Delta, Delta*u) per (step, channel)
+    // (Delta, Delta*u) per (step, channel); with the zero-order hold also u
+    typedef typename std::conditional<ZOH, float4, float2>::type DW;
+    __shared__ DW s_dw[2][TC][64];
     __shared__ float s_yp[FULL ? 2 : 1][TC][NW][64]; // partial readouts per (step, wave, channel)
 
     const int lane = threadIdx.x & 63;
@@ -178,10 +180,13 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     const int n0 = g * NQ;
 
     const int64_t col0 = ((int64_t)b * Dn + dc) * N + n0;
-    float a2[NQ], h[NQ];
+    float a2[NQ], h[NQ], an[NQ], ia[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        a2[q] = A[(int64_t)dc * N + n0 + q] * kLog2e; // exp(Delta*A) = exp2(Delta*A*log2 e)
+        const float av = A[(int64_t)dc * N + n0 + q];
+        a2[q] = av * kLog2e; // exp(Delta*A) = exp2(Delta*A*log2 e)
+        an[q] = av;          // zero-order hold: A and 1/A
+        ia[q] = ZOH ? 1.0f / av : 0.0f;
         h[q] = h_init ? h_init[span * h_init_stride + col0 + q] : 0.0f;
     }
     if (relayed && part > 0) {
@@ -302,8 +307,12 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
             const float dl = softplus_f(widen(rd[j][k]) + bias_d);
             du[k] = FULL ? D_d * uu : 0.0f;
             gz[k] = gated ? silu_f(widen(rz[j][k])) : 1.0f;
-            if (tl < TC)
-                s_dw[pp][tl][lane] = make_float2(dl, dl * uu);
+            if (tl < TC) {
+                if constexpr (ZOH)
+                    s_dw[pp][tl][lane] = make_float4(dl, dl * uu, uu, 0.0f);
+                else
+                    s_dw[pp][tl][lane] = make_float2(dl, dl * uu);
+            }
         }
         if (t0 + PD * TC < n_loc)
             fetch(BUF, t0 + PD * TC);
@@ -312,7 +321,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
         // LDS reads: the previous chunk's partial readouts and this chunk's (Delta, Delta*u)
         float es[KPL];
         epilogue_sum(std::integral_constant<int, pp ^ 1>{}, es);
-        float2 dw[TC];
+        DW dw[TC];
 #pragma unroll
         for (int tl = 0; tl < TC; ++tl)
             dw[tl] = s_dw[pp][tl][lane];
@@ -324,7 +333,10 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const float a = decay_exp2(dw[tl].x, a2[q]);
-                h[q] = __builtin_fmaf(a, h[q], dw[tl].y * bcs[tl][q]);
+                float bu = dw[tl].y; // Bbar u / B: Euler Delta u
+                if constexpr (ZOH)
+                    bu = zoh_input(dw[tl].x * an[q], a, dw[tl].y, dw[tl].z * ia[q]);
+                h[q] = __builtin_fmaf(a, h[q], bu * bcs[tl][q]);
                 if (FULL)
                     yp = __builtin_fmaf(bcs[tl][NQ + q], h[q], yp);
             }
@@ -423,7 +435,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     X(16, 8, 8, 2)               \
     X(32, 8, 4, 2)
 
-template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED>
+template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED, bool ZOH>
 hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
 {
     const int32_t tiles = (int32_t)((p.d_inner + 63) / 64);
@@ -441,7 +453,7 @@ hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
     }
     if (blocks <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL((scan_scalar_kernel<T, N, NW, TC, PD, FULL, GATED>),
+    hipLaunchKernelGGL((scan_scalar_kernel<T, N, NW, TC, PD, FULL, GATED, ZOH>),
                        dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, (const T *)p.u,
                        (const T *)p.delta, (const T *)p.z, p.bc_staged, p.A, p.D, p.bias,
                        p.h_init, p.h_init_span_stride, (T *)p.y, p.h_last, p.ws_decay,
@@ -464,17 +476,25 @@ hipError_t launch_stage(const ScanLaunch &p, hipStream_t stream)
     return hipGetLastError();
 }
 
+template <typename T, int N, int NW, int TC, int PD, bool FULL>
+hipError_t launch_scalar_opts(const ScanLaunch &p, hipStream_t stream)
+{
+    const bool g = FULL && p.z != nullptr;
+    if (p.zoh)
+        return g ? launch_scalar_variant<T, N, NW, TC, PD, FULL, true, true>(p, stream)
+                 : launch_scalar_variant<T, N, NW, TC, PD, FULL, false, true>(p, stream);
+    return g ? launch_scalar_variant<T, N, NW, TC, PD, FULL, true, false>(p, stream)
+             : launch_scalar_variant<T, N, NW, TC, PD, FULL, false, false>(p, stream);
+}
+
 template <bool FULL>
 hipError_t launch_scalar_any(const ScanLaunch &p, hipStream_t stream)
 {
-    const bool g = FULL && p.z != nullptr;
-#define X(N_, W_, C_, P_)                                                                     \
-    if (p.d_state == N_ && p.waves == W_ && p.chunk == C_) {                                  \
-        if (p.dtype == DType::BF16)                                                           \
-            return g ? launch_scalar_variant<uint16_t, N_, W_, C_, P_, FULL, true>(p, stream) \
-                     : launch_scalar_variant<uint16_t, N_, W_, C_, P_, FULL, false>(p, stream); \
-        return g ? launch_scalar_variant<float, N_, W_, C_, P_, FULL, true>(p, stream)        \
-                 : launch_scalar_variant<float, N_, W_, C_, P_, FULL, false>(p, stream);      \
+#define X(N_, W_, C_, P_)                                                   \
+    if (p.d_state == N_ && p.waves == W_ && p.chunk == C_) {                \
+        if (p.dtype == DType::BF16)                                         \
+            return launch_scalar_opts<uint16_t, N_, W_, C_, P_, FULL>(p, stream); \
+        return launch_scalar_opts<float, N_, W_, C_, P_, FULL>(p, stream);  \
     }
     MAMBA_SCALAR_VARIANTS(X)
 #undef X

@@ -16,7 +16,7 @@
 
 namespace mambascan {
 
-template <typename T, int N>
+template <typename T, int N, bool ZOH>
 __global__ void __launch_bounds__(256)
 state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__restrict__ delta,
                     const T *__restrict__ z, const T *__restrict__ Bm, const T *__restrict__ Cm,
@@ -48,7 +48,10 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const float a = decay_exp2(dl, ain[k] * kLog2e);
-        hn[k] = __builtin_fmaf(a, hin[k], w * load_val(Bm, bn + k));
+        float bu = w; // Bbar u / B: Euler Delta u, or the zero-order hold
+        if constexpr (ZOH)
+            bu = zoh_input(dl * ain[k], a, w, uu / ain[k]);
+        hn[k] = __builtin_fmaf(a, hin[k], bu * load_val(Bm, bn + k));
         yp = __builtin_fmaf(load_val(Cm, bn + k), hn[k], yp);
     }
 #pragma unroll
@@ -66,7 +69,7 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
     }
 }
 
-template <typename T, int N>
+template <typename T, int N, bool ZOH>
 static hipError_t launch_step(const StepLaunch &p, hipStream_t stream)
 {
     constexpr int LPC = N / 4;
@@ -76,7 +79,7 @@ static hipError_t launch_step(const StepLaunch &p, hipStream_t stream)
     for (int64_t b0 = 0; b0 < p.batch; b0 += 65535) {
         const int64_t nb = p.batch - b0 < 65535 ? p.batch - b0 : 65535;
         const int64_t off_bd = b0 * p.d_inner, off_bn = b0 * N;
-        hipLaunchKernelGGL((state_update_kernel<T, N>), dim3(gx, (uint32_t)nb), dim3(256), 0,
+        hipLaunchKernelGGL((state_update_kernel<T, N, ZOH>), dim3(gx, (uint32_t)nb), dim3(256), 0,
                            stream, p.h + off_bd * N, (const T *)p.u + off_bd,
                            (const T *)p.delta + off_bd,
                            p.z ? (const T *)p.z + off_bd : nullptr, (const T *)p.B + off_bn,
@@ -96,8 +99,10 @@ hipError_t launch_state_update(const StepLaunch &p, hipStream_t stream)
 #define STEP_CASE(N_)                                                   \
     if (p.d_state == N_) {                                              \
         if (p.dtype == DType::BF16)                                     \
-            return launch_step<uint16_t, N_>(p, stream);                \
-        return launch_step<float, N_>(p, stream);                       \
+            return p.zoh ? launch_step<uint16_t, N_, true>(p, stream)   \
+                         : launch_step<uint16_t, N_, false>(p, stream); \
+        return p.zoh ? launch_step<float, N_, true>(p, stream)          \
+                     : launch_step<float, N_, false>(p, stream);        \
     }
     STEP_CASE(4)
     STEP_CASE(8)

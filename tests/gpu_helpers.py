@@ -82,7 +82,7 @@ class DevInputs:
 
 
 def oracle_scan(inp: synth.ScanInputs, bs=None, ds=None, *, gate=True, use_D=True,
-                use_bias=True, use_h0=True):
+                use_bias=True, use_h0=True, zoh=False):
     """Oracle on the sub-grid of batch rows bs x channels ds (all if None)."""
     dt = inp.dtype
     p = inp.params
@@ -98,4 +98,5 @@ def oracle_scan(inp: synth.ScanInputs, bs=None, ds=None, *, gate=True, use_D=Tru
     h0 = (inp.h0[bs][:, ds].astype(np.float64) if (use_h0 and inp.h0 is not None) else None)
     return oracle.load().scan(u, delta, p.A[ds].astype(np.float64), B, C,
                               D=p.D[ds].astype(np.float64) if use_D else None, z=z,
-                              bias=p.bias[ds].astype(np.float64) if use_bias else None, h0=h0)
+                              bias=p.bias[ds].astype(np.float64) if use_bias else None, h0=h0,
+                              zoh=zoh)

@@ -278,3 +278,20 @@ def test_conv_update_validation(lib):
     assert conv_step(lib, x=BASE + 100 * MB + 1) == ALIGN
     assert conv_step(lib, u=BASE) == ALIAS                 # u over the state
     assert conv_step(lib, x=BASE + 64) == ALIAS            # state over x
+
+
+def test_discretization_options(lib):
+    ws = lambda *a, o: lib.mamba_scan_fwd_workspace_size_ex(*a, ctypes.byref(o))  # noqa: E731
+    bad = ctypes.c_size_t(-1).value
+    small = (3, 1000, 200, 16)
+    assert ws(*small, o=ms.ScanOpts(0, 0, 0, 0, 0, 2)) == bad        # unknown rule
+    assert ws(*small, o=ms.ScanOpts(0, 0, 0, 2, 0, 1)) == bad        # ZOH: not the row family
+    assert ws(*small, o=ms.ScanOpts(0, 0, 0, 1, 0, 1)) == bad        # nor the block family
+    assert ws(3, 1000, 200, 64, o=ms.ScanOpts(0, 0, 0, 0, 0, 1)) == bad   # no scalar d_state 64
+    # AUTO with ZOH takes the scalar family: staged B/C, here with 3 spans of summaries
+    staged = 3 * (1000 + 8) * 2 * 16 * 4
+    assert ws(*small, o=ms.ScanOpts(0, 0, 0, 0, 0, 1)) == staged + 3 * 3 * 3 * 200 * 16 * 4
+    assert ws(*small, o=ms.ScanOpts(0, 0, 1, 0, 0, 1)) == staged
+    assert lib.mamba_state_update_ex(BASE, BASE + 100 * MB, BASE + 110 * MB, BASE + 120 * MB,
+                                     BASE + 130 * MB, BASE + 131 * MB, None, None, None,
+                                     BASE + 140 * MB, 4, 256, 16, BF16, 7, None) == UNSUP

@@ -36,12 +36,14 @@ def check(name, y, h, yr, hr, dtype):
 
 
 def full_check(name, inp, **kw):
-    opts = {k: kw.pop(k) for k in ("chunk_len", "waves", "n_spans", "kernel", "relay")
-            if k in kw}
+    opts = {k: kw.pop(k) for k in ("chunk_len", "waves", "n_spans", "kernel", "relay",
+                                   "discretization") if k in kw}
+    if opts.get("discretization") == "zoh":
+        kw["zoh"] = True
     log(f"case {name}: batch={inp.cfg.batch} L={inp.cfg.seqlen} D={inp.cfg.d_inner} "
         f"N={inp.cfg.d_state} {inp.dtype} opts={opts} {kw}")
     di = DevInputs(inp)
-    y, h = di.run(**kw, **opts)
+    y, h = di.run(**{k: v for k, v in kw.items() if k != "zoh"}, **opts)
     yr, hr = oracle_scan(inp, **kw)
     check(name, from_dev(y), from_dev(h), yr, hr, inp.dtype)
     return y, h
@@ -240,6 +242,57 @@ def test_relay_in_place_continuation():
                              n_spans=1, relay=4)
     torch.cuda.synchronize()
     assert torch.equal(y, y_ref) and torch.equal(h, h_ref)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("opts", [dict(), dict(n_spans=1), dict(n_spans=4), dict(n_spans=1, relay=3),
+                                  dict(chunk_len=4)], ids=str)
+def test_zoh_agrees_with_oracle(opts, dtype):
+    """Zero-order-hold discretisation (Bbar = (exp(Delta A) - 1) / A B)."""
+    import dataclasses
+    base = synth.CONFIGS["c1"] if dtype == synth.F32 else synth.CONFIGS["c3"]
+    cfg = dataclasses.replace(base, dtype=dtype, h0=True, gate=True)
+    inp = synth.make_scan_inputs(cfg, batch=2, seqlen=333, d_inner=200, seed=50)
+    full_check(f"zoh {opts} {dtype}", inp, discretization="zoh", **opts)
+
+
+def test_zoh_both_branches_and_zero_A():
+    """A spread so that Delta A falls on both sides of the series / decay-factor switch
+    (|Delta A| = 1/16), plus exactly zero entries (the Euler limit)."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS["c1"], h0=True, gate=True)
+    inp = synth.make_scan_inputs(cfg, batch=2, seqlen=200, d_inner=72, seed=51)
+    rng = np.random.default_rng(52)
+    A = -np.exp(rng.uniform(np.log(1e-3), np.log(30.0), size=inp.params.A.shape))
+    A[::7, ::5] = 0.0
+    inp.params.A = A.astype(np.float32)
+    full_check("zoh spread A", inp, discretization="zoh")
+    full_check("euler spread A", inp)
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_zoh_decode_steps(dtype):
+    """Chained zero-order-hold decode steps against the oracle's, and against the ZOH scan."""
+    import dataclasses
+    base = synth.CONFIGS["c1"] if dtype == synth.F32 else synth.CONFIGS["c3"]
+    cfg = dataclasses.replace(base, dtype=dtype, h0=True, gate=True)
+    inp = synth.make_scan_inputs(cfg, batch=3, seqlen=40, d_inner=96, seed=53)
+    di = DevInputs(inp)
+    y_scan, h_scan = di.run(discretization="zoh")
+    yr, hr = oracle_scan(inp, zoh=True)
+    h = di.h0.clone()
+    ys = []
+    for t in range(40):
+        y = ms.mamba_state_update(h, di.u[:, t].contiguous(), di.delta[:, t].contiguous(), di.A,
+                                  di.B[:, t].contiguous(), di.C[:, t].contiguous(), D=di.D,
+                                  z=di.z[:, t].contiguous(), delta_bias=di.bias,
+                                  discretization="zoh")
+        ys.append(y)
+    torch.cuda.synchronize()
+    y_dec = torch.stack(ys, dim=1)
+    check("zoh decode", from_dev(y_dec), from_dev(h), yr, hr, dtype)
+    assert metric(from_dev(y_dec), from_dev(y_scan)) <= TOL[dtype]
+    assert metric(from_dev(h), from_dev(h_scan)) <= TOL[dtype]
 
 
 def test_deterministic():
