@@ -53,6 +53,8 @@ class Oracle:
         lib.oracle_scan.argtypes = [_dp] * 11 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_step.restype = ctypes.c_int
         lib.oracle_step.argtypes = [_dp] * 10 + [_i64] * 3 + [ctypes.c_int]
+        lib.oracle_scan_bwd.restype = ctypes.c_int
+        lib.oracle_scan_bwd.argtypes = [_dp] * 20 + [_i64] * 4 + [ctypes.c_int]
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
@@ -98,6 +100,39 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_scan rejected its arguments")
         return y, h_last
+
+    # -- gradients ------------------------------------------------------------
+    def scan_bwd(self, u, delta, A, B, C, dy, D=None, z=None, bias=None, h0=None,
+                 dh_last=None, nthreads: Optional[int] = None) -> dict:
+        """Gradients of sum(dy * y) + sum(dh_last * h_last) (Euler scan) with respect to
+        every input: keys du, ddelta, dA, dB, dC, dD, dz, dbias, dh0 (float64; dD, dz,
+        dbias are returned even when D, z, bias are absent: the gradient at zero / no gate)."""
+        u = _c64(u)
+        batch, L, d_inner = u.shape
+        A = _c64(A)
+        d_state = A.shape[1]
+        delta, B, C, dy = _c64(delta), _c64(B), _c64(C), _c64(dy)
+        D, z, bias, h0, dh_last = _c64(D), _c64(z), _c64(bias), _c64(h0), _c64(dh_last)
+        for a, shp, name in ((delta, u.shape, "delta"), (dy, u.shape, "dy"),
+                             (B, (batch, L, d_state), "B"), (C, (batch, L, d_state), "C"),
+                             (D, (d_inner,), "D"), (bias, (d_inner,), "bias"),
+                             (z, u.shape, "z"), (h0, (batch, d_inner, d_state), "h0"),
+                             (dh_last, (batch, d_inner, d_state), "dh_last")):
+            _check(a, shp, name)
+        out = dict(du=np.zeros(u.shape), ddelta=np.zeros(u.shape), dA=np.zeros(A.shape),
+                   dB=np.zeros((batch, L, d_state)), dC=np.zeros((batch, L, d_state)),
+                   dD=np.zeros(d_inner), dz=np.zeros(u.shape), dbias=np.zeros(d_inner),
+                   dh0=np.zeros((batch, d_inner, d_state)))
+        if nthreads is None:
+            nthreads = default_threads()
+        rc = self._lib.oracle_scan_bwd(
+            _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z), _p(bias), _p(h0), _p(dy),
+            _p(dh_last), _p(out["du"]), _p(out["ddelta"]), _p(out["dA"]), _p(out["dB"]),
+            _p(out["dC"]), _p(out["dD"]), _p(out["dz"]), _p(out["dbias"]), _p(out["dh0"]),
+            batch, L, d_inner, d_state, int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd rejected its arguments")
+        return out
 
     # -- one decode step ------------------------------------------------------
     def step(self, h, u, delta, A, B, C, D=None, z=None, bias=None, zoh: bool = False

@@ -210,3 +210,186 @@ int oracle_step(double *h, const double *u, const double *delta, const double *A
     }
     return 0;
 }
+
+/*
+ * Gradients of the scan (Euler discretisation), for a loss whose derivatives with
+ * respect to the outputs are dy (batch, L, d_inner) and, optionally, dh_last
+ * (batch, d_inner, d_state).  Reverse-mode differentiation of the loop above, written
+ * out by hand: with mu_t[n] = dLoss/dh_t[n] (total), s_t = sum_n C_t h_t + D u_t,
+ * g_t = silu(z_t), ds_t = dy_t g_t,
+ *     mu_{L-1} = dh_last + ds_{L-1} C_{L-1};  mu_t = Abar_{t+1} mu_{t+1} + ds_t C_t
+ *     dDelta_t = sum_n mu_t[n] (A[n] Abar_t[n] h_{t-1}[n] + B_t[n] u_t)
+ *     du_t     = ds_t D + sum_n mu_t[n] Delta_t B_t[n]
+ *     dB_t[n]  = sum_d mu_t[n] Delta_t u_t        dC_t[n] = sum_d ds_t h_t[n]
+ *     dA[d,n]  = sum_{b,t} mu_t[n] Delta_t Abar_t[n] h_{t-1}[n]
+ *     dD[d]    = sum_{b,t} ds_t u_t               dz_t = dy_t s_t silu'(z_t)
+ *     ddelta_t = dDelta_t sigmoid(delta_t + bias)  (softplus' = sigmoid)
+ *     dbias[d] = sum_{b,t} ddelta_t               dh0 = Abar_0 mu_0
+ * The pages name the backward pass (recompute instead of storing the states, "Understanding
+ * Mamba" section 7.3; the hnwysp.cn slides, section 4.4) but do not write it out; this is
+ * the chain rule applied to the forward definition above, pinned by finite differences.
+ * Outputs other than du and ddelta may be NULL.  Threads split the batch rows; the sums
+ * over b are added in b order, so the result does not depend on the thread count.
+ */
+typedef struct {
+    const double *u, *delta, *A, *B, *C, *D, *z, *bias, *h0, *dy, *dh_last;
+    double *du, *ddelta, *dB, *dC, *dz, *dh0;
+    double *dA_part, *dD_part, *dbias_part; /* per batch row: [b][d][n], [b][d], [b][d] */
+    int64_t batch, L, Dn, N;
+    int64_t b_begin, b_end;
+} bwd_job;
+
+static void bwd_rows(const bwd_job *j)
+{
+    const int64_t L = j->L, Dn = j->Dn, N = j->N;
+    double *hs = (double *)malloc((size_t)((L + 1) * N > 0 ? (L + 1) * N : 1) * sizeof(double));
+    double *mu = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    for (int64_t b = j->b_begin; b < j->b_end; ++b) {
+        if (j->dB)
+            for (int64_t i = 0; i < L * N; ++i)
+                j->dB[b * L * N + i] = 0.0;
+        if (j->dC)
+            for (int64_t i = 0; i < L * N; ++i)
+                j->dC[b * L * N + i] = 0.0;
+        for (int64_t d = 0; d < Dn; ++d) {
+            /* forward: hs[(t + 1) * N + n] = h_t[n], hs[n] = h_{-1}[n] */
+            for (int64_t n = 0; n < N; ++n)
+                hs[n] = j->h0 ? j->h0[(b * Dn + d) * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t bld = (b * L + t) * Dn + d, bln = (b * L + t) * N;
+                const double dt = oracle_softplus(j->delta[bld] + (j->bias ? j->bias[d] : 0.0));
+                for (int64_t n = 0; n < N; ++n)
+                    hs[(t + 1) * N + n] = exp(dt * j->A[d * N + n]) * hs[t * N + n] +
+                                          dt * j->B[bln + n] * j->u[bld];
+            }
+            /* reverse */
+            for (int64_t n = 0; n < N; ++n)
+                mu[n] = j->dh_last ? j->dh_last[(b * Dn + d) * N + n] : 0.0;
+            double dD_acc = 0.0, dbias_acc = 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const int64_t bld = (b * L + t) * Dn + d, bln = (b * L + t) * N;
+                const double v = j->delta[bld] + (j->bias ? j->bias[d] : 0.0);
+                const double dt = oracle_softplus(v);
+                const double ut = j->u[bld];
+                double s = (j->D ? j->D[d] : 0.0) * ut;
+                for (int64_t n = 0; n < N; ++n)
+                    s += j->C[bln + n] * hs[(t + 1) * N + n];
+                double gate = 1.0, dgate = 0.0;
+                if (j->z) {
+                    const double zt = j->z[bld];
+                    const double sig = 1.0 / (1.0 + exp(-zt));
+                    gate = zt * sig;
+                    dgate = sig * (1.0 + zt * (1.0 - sig));
+                }
+                const double ds = j->dy[bld] * gate;
+                if (j->dz)
+                    j->dz[bld] = j->z ? j->dy[bld] * s * dgate : 0.0;
+                double ddt = 0.0, du = ds * (j->D ? j->D[d] : 0.0);
+                for (int64_t n = 0; n < N; ++n) {
+                    mu[n] += ds * j->C[bln + n];                 /* mu_t */
+                    const double a = j->A[d * N + n];
+                    const double abar = exp(dt * a);
+                    const double hprev = hs[t * N + n];
+                    ddt += mu[n] * (a * abar * hprev + j->B[bln + n] * ut);
+                    du += mu[n] * dt * j->B[bln + n];
+                    if (j->dB)
+                        j->dB[bln + n] += mu[n] * dt * ut;
+                    if (j->dC)
+                        j->dC[bln + n] += ds * hs[(t + 1) * N + n];
+                    if (j->dA_part)
+                        j->dA_part[(b * Dn + d) * N + n] += mu[n] * dt * abar * hprev;
+                    mu[n] *= abar;                               /* Abar_t mu_t, for t - 1 */
+                }
+                dD_acc += ds * ut;
+                const double dv = ddt / (1.0 + exp(-v));         /* softplus'(v) = sigmoid(v) */
+                j->du[bld] = du;
+                j->ddelta[bld] = dv;
+                dbias_acc += dv;
+            }
+            if (j->dh0)
+                for (int64_t n = 0; n < N; ++n)
+                    j->dh0[(b * Dn + d) * N + n] = mu[n];        /* = Abar_0 mu_0 */
+            if (j->dD_part)
+                j->dD_part[b * Dn + d] = dD_acc;
+            if (j->dbias_part)
+                j->dbias_part[b * Dn + d] = dbias_acc;
+        }
+    }
+    free(mu);
+    free(hs);
+}
+
+static void *bwd_thread(void *arg)
+{
+    bwd_rows((const bwd_job *)arg);
+    return NULL;
+}
+
+int oracle_scan_bwd(const double *u, const double *delta, const double *A, const double *B,
+                    const double *C, const double *D, const double *z, const double *bias,
+                    const double *h0, const double *dy, const double *dh_last, double *du,
+                    double *ddelta, double *dA, double *dB, double *dC, double *dD, double *dz,
+                    double *dbias, double *dh0, int64_t batch, int64_t L, int64_t d_inner,
+                    int64_t d_state, int nthreads)
+{
+    if (batch < 0 || L < 0 || d_inner < 0 || d_state < 0 || !A)
+        return -1;
+    if (L > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta))
+        return -1;
+    const int64_t Dn = d_inner, N = d_state;
+    double *dA_part = (double *)calloc((size_t)(batch * Dn * N > 0 ? batch * Dn * N : 1), sizeof(double));
+    double *dD_part = (double *)calloc((size_t)(batch * Dn > 0 ? batch * Dn : 1), sizeof(double));
+    double *dbias_part = (double *)calloc((size_t)(batch * Dn > 0 ? batch * Dn : 1), sizeof(double));
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > batch)
+        nthreads = (int)(batch > 0 ? batch : 1);
+    bwd_job *jobs = (bwd_job *)calloc((size_t)nthreads, sizeof(bwd_job));
+    pthread_t *tids = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    for (int i = 0; i < nthreads; ++i) {
+        bwd_job *j = &jobs[i];
+        j->u = u; j->delta = delta; j->A = A; j->B = B; j->C = C; j->D = D; j->z = z;
+        j->bias = bias; j->h0 = h0; j->dy = dy; j->dh_last = dh_last;
+        j->du = du; j->ddelta = ddelta; j->dB = dB; j->dC = dC; j->dz = dz; j->dh0 = dh0;
+        j->dA_part = dA_part; j->dD_part = dD_part; j->dbias_part = dbias_part;
+        j->batch = batch; j->L = L; j->Dn = Dn; j->N = N;
+        j->b_begin = batch * i / nthreads;
+        j->b_end = batch * (i + 1) / nthreads;
+    }
+    if (L > 0) {
+        for (int i = 1; i < nthreads; ++i)
+            pthread_create(&tids[i], NULL, bwd_thread, &jobs[i]);
+        bwd_rows(&jobs[0]);
+        for (int i = 1; i < nthreads; ++i)
+            pthread_join(tids[i], NULL);
+    } else if (dh0) { /* nothing happened: the initial state's gradient is dh_last */
+        for (int64_t i = 0; i < batch * Dn * N; ++i)
+            dh0[i] = dh_last ? dh_last[i] : 0.0;
+    }
+    /* sums over the batch, in b order */
+    if (dA)
+        for (int64_t i = 0; i < Dn * N; ++i) {
+            double s = 0.0;
+            for (int64_t b = 0; b < batch; ++b)
+                s += dA_part[b * Dn * N + i];
+            dA[i] = s;
+        }
+    if (dD || dbias)
+        for (int64_t d = 0; d < Dn; ++d) {
+            double sD = 0.0, sb = 0.0;
+            for (int64_t b = 0; b < batch; ++b) {
+                sD += dD_part[b * Dn + d];
+                sb += dbias_part[b * Dn + d];
+            }
+            if (dD)
+                dD[d] = sD;
+            if (dbias)
+                dbias[d] = sb;
+        }
+    free(tids);
+    free(jobs);
+    free(dbias_part);
+    free(dD_part);
+    free(dA_part);
+    return 0;
+}

@@ -402,3 +402,74 @@ PINS = [pin_worked_example, pin_brute_force, pin_lti_convolution, pin_lti_fft_lo
         pin_linearity_causality, pin_scalar_closed_forms, pin_empty_and_threads,
         pin_zoh_samples_the_ode, pin_zoh_limits, pin_zoh_lti_convolution,
         pin_zoh_decode_equals_scan]
+
+
+# ----------------------------------------------------------------------------
+# gradients: pinned by central finite differences of the forward oracle
+# ----------------------------------------------------------------------------
+
+def _loss(orc, case, dy, dh_last):
+    y, h = orc.scan(**case, nthreads=1)
+    return float(np.sum(dy * y) + (np.sum(dh_last * h) if dh_last is not None else 0.0))
+
+
+def _fd_check(orc, case, dy, dh_last, grads, names, eps=1e-6, tol=2e-7):
+    """Every entry of the listed inputs: (L(x + e) - L(x - e)) / 2e against the gradient."""
+    key = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD",
+           "z": "dz", "bias": "dbias", "h0": "dh0"}
+    for name in names:
+        base = case[name]
+        g = grads[key[name]]
+        worst = 0.0
+        scale = max(float(np.max(np.abs(g))), 1e-12)
+        for idx in np.ndindex(base.shape):
+            h = eps * max(1.0, abs(base[idx]))
+            old = base[idx]
+            base[idx] = old + h
+            lp = _loss(orc, case, dy, dh_last)
+            base[idx] = old - h
+            lm = _loss(orc, case, dy, dh_last)
+            base[idx] = old
+            fd = (lp - lm) / (2 * h)
+            worst = max(worst, abs(fd - g[idx]) / scale)
+        assert worst < tol, (name, worst)
+
+
+def pin_gradients_finite_differences(orc):
+    """Every gradient entry of a small gated problem with h0, D and bias, and of one with
+    none of them, against central differences of the forward oracle."""
+    rng = np.random.default_rng(41)
+    case = random_case(rng, batch=2, L=7, Dn=3, N=4)
+    dy = rng.standard_normal(case["u"].shape)
+    dh_last = rng.standard_normal(case["h0"].shape)
+    g = orc.scan_bwd(dy=dy, dh_last=dh_last, **case)
+    _fd_check(orc, case, dy, dh_last, g, ["u", "delta", "A", "B", "C", "D", "z", "bias", "h0"])
+    case = random_case(rng, batch=1, L=9, Dn=2, N=3, gate=False, with_h0=False, with_D=False,
+                       with_bias=False)
+    dy = rng.standard_normal(case["u"].shape)
+    g = orc.scan_bwd(dy=dy, **case)
+    _fd_check(orc, case, dy, None, g, ["u", "delta", "A", "B", "C"])
+
+
+def pin_gradient_closed_forms(orc):
+    """dD = sum_{b,t} dy g u; with dy = 0 only dh_last flows: dh0 = exp(A S_L) dh_last
+    (the adjoint of the exact decay), and du = dy D silu(z) when B = 0."""
+    rng = np.random.default_rng(42)
+    case = random_case(rng, L=11)
+    dy = rng.standard_normal(case["u"].shape)
+    g = orc.scan_bwd(dy=dy, **case)
+    ref_dD = np.sum(dy * ref_silu(case["z"]) * case["u"], axis=(0, 1))
+    assert np.allclose(g["dD"], ref_dD, rtol=1e-12, atol=1e-12)
+    dh_last = rng.standard_normal(case["h0"].shape)
+    g = orc.scan_bwd(dy=np.zeros_like(dy), dh_last=dh_last, **case)
+    for b in range(case["u"].shape[0]):
+        for d in range(case["u"].shape[2]):
+            S = np.sum(ref_softplus(case["delta"][b, :, d] + case["bias"][d]))
+            assert np.allclose(g["dh0"][b, d], np.exp(case["A"][d] * S) * dh_last[b, d],
+                               rtol=1e-12, atol=0)
+    case["B"] = np.zeros_like(case["B"])
+    g = orc.scan_bwd(dy=dy, **case)
+    assert np.allclose(g["du"], dy * ref_silu(case["z"]) * case["D"], rtol=1e-12, atol=1e-14)
+
+
+PINS += [pin_gradients_finite_differences, pin_gradient_closed_forms]

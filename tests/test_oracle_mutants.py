@@ -53,6 +53,22 @@ MUTANTS = [
     ("step_drops_delta_in_bbar", [("oracle_bbar(dt, A[d * d_state + n], B[b * d_state + n], zoh)",
                                    "B[b * d_state + n]")]),
     ("step_no_gate", [("            if (z)\n                yt *= oracle_silu(z[bd]);\n", "")]),
+    # gradients
+    ("bwd_mu_no_decay", [("mu[n] *= abar;                               /* Abar_t mu_t",
+                          "mu[n] *= 1.0;                                /* Abar_t mu_t")]),
+    ("bwd_dB_no_dt", [("j->dB[bln + n] += mu[n] * dt * ut;", "j->dB[bln + n] += mu[n] * ut;")]),
+    ("bwd_dC_old_state", [("j->dC[bln + n] += ds * hs[(t + 1) * N + n];",
+                           "j->dC[bln + n] += ds * hs[t * N + n];")]),
+    ("bwd_dA_no_abar", [("j->dA_part[(b * Dn + d) * N + n] += mu[n] * dt * abar * hprev;",
+                         "j->dA_part[(b * Dn + d) * N + n] += mu[n] * dt * hprev;")]),
+    ("bwd_softplus_grad_sign", [("const double dv = ddt / (1.0 + exp(-v));",
+                                 "const double dv = ddt / (1.0 + exp(v));")]),
+    ("bwd_dz_no_dgate", [("j->dz[bld] = j->z ? j->dy[bld] * s * dgate : 0.0;",
+                          "j->dz[bld] = j->z ? j->dy[bld] * s : 0.0;")]),
+    ("bwd_du_no_D", [("double ddt = 0.0, du = ds * (j->D ? j->D[d] : 0.0);",
+                      "double ddt = 0.0, du = 0.0;")]),
+    ("bwd_ddt_no_input_term", [("ddt += mu[n] * (a * abar * hprev + j->B[bln + n] * ut);",
+                                "ddt += mu[n] * (a * abar * hprev);")]),
 ]
 
 
