@@ -276,6 +276,61 @@ MAMBA_API mamba_status_t mamba_state_update_ex(float *h, const void *u, const vo
                                                mamba_dtype_t dtype, int32_t discretization,
                                                void *stream);
 
+/* ------------------------------------------------------------------------
+ * Backward pass of the selective scan (Euler discretisation): the gradients of a
+ * loss with respect to every input of mamba_scan_fwd, given its gradients dy with
+ * respect to y and, optionally, dh_last with respect to h_last.  "Understanding
+ * Mamba" (aiattnstudio.link) section 7.3 and the hnwysp.cn slides (section 4.4)
+ * train the scan with a backward pass that recomputes the states instead of storing
+ * them; the pages do not write the gradients out, so they are the chain rule
+ * applied to the recurrence at the top of this file.  With mu_t = dLoss/dh_t,
+ * s_t = sum_n C_t[n] h_t[n] + D u_t and ds_t = dy_t * silu(z_t) (ds_t = dy_t
+ * without a gate):
+ *
+ *   mu_{L-1} = dh_last + ds_{L-1} C_{L-1},   mu_t = Abar_{t+1} mu_{t+1} + ds_t C_t
+ *   du[b,t,d]     = ds_t D[d] + Delta_t sum_n mu_t[n] B_t[n]
+ *   ddelta[b,t,d] = sigmoid(delta + delta_bias) * sum_n mu_t[n] (A[d,n] Abar_t[n]
+ *                   h_{t-1}[n] + B_t[n] u_t)
+ *   dz[b,t,d]     = dy_t s_t silu'(z_t)
+ *   dB[b,t,n] = sum_d mu_t[n] Delta_t u_t          dC[b,t,n] = sum_d ds_t h_t[n]
+ *   dA[d,n]   = sum_{b,t} mu_t[n] Delta_t Abar_t[n] h_{t-1}[n]
+ *   dD[d]     = sum_{b,t} ds_t u_t                 d_delta_bias[d] = sum_{b,t} ddelta
+ *   dh0[b,d,n] = Abar_0[n] mu_0[n]
+ *
+ *   inputs u, delta, A, B, C, D, z, delta_bias, h0: as for mamba_scan_fwd
+ *   dy            (batch, seqlen, d_inner) dtype    required if seqlen > 0
+ *   dh_last       (batch, d_inner, d_state) float32 nullable (0)
+ *   du, ddelta    (batch, seqlen, d_inner) dtype    outputs, required if seqlen > 0
+ *   dz            (batch, seqlen, d_inner) dtype    output, required when z is given
+ *                                                   (ignored without z)
+ *   dB, dC        (batch, seqlen, d_state) dtype    outputs, nullable (not computed)
+ *   dA            (d_inner, d_state) float32        output, nullable
+ *   dD, d_delta_bias (d_inner) float32              outputs, nullable (dD is returned
+ *                                                   also when D is NULL)
+ *   dh0           (batch, d_inner, d_state) float32 output, nullable
+ *   workspace     see mamba_scan_bwd_workspace_size (required when seqlen > 0)
+ *
+ * Outputs are written, not accumulated.  Sums over channels, batch rows and time are
+ * formed in float32 in a fixed order (results are bitwise reproducible); outputs in
+ * dtype are rounded to nearest even.  d_state must be 4, 8, 16 or 32
+ * (MAMBA_ERR_UNSUPPORTED otherwise).  With seqlen == 0 only dh0 (= dh_last, or 0),
+ * dA, dD and d_delta_bias (0) are written.  Aliasing: no output may overlap an input
+ * or another output, and the workspace overlaps nothing (MAMBA_ERR_ALIASING).
+ * Other conventions as for every entry point.
+ */
+MAMBA_API size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                               int64_t d_state);
+
+MAMBA_API mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A,
+                                        const void *B, const void *C, const float *D,
+                                        const void *z, const float *delta_bias,
+                                        const float *h0, const void *dy, const float *dh_last,
+                                        void *du, void *ddelta, float *dA, void *dB, void *dC,
+                                        float *dD, void *dz, float *d_delta_bias, float *dh0,
+                                        int64_t batch, int64_t seqlen, int64_t d_inner,
+                                        int64_t d_state, mamba_dtype_t dtype, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 MAMBA_API const char *mamba_status_string(mamba_status_t status);
 

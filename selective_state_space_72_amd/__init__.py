@@ -11,6 +11,8 @@ there is no CPU or PyTorch fallback -- if the library is missing, the call fails
     y = mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None)
     u, state = mamba_conv1d_silu_fwd(x, w, conv_bias=None, state_in=None, return_state=False)
     u = mamba_conv1d_silu_update(state, x, w, conv_bias=None)
+    grads = mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
+                           h0=None, dh_last=None)
 """
 
 from __future__ import annotations
@@ -34,7 +36,7 @@ STATUS = {
 EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_scan_fwd_workspace_size_ex", "mamba_scan_fwd", "mamba_scan_fwd_ex",
            "mamba_state_update", "mamba_state_update_ex", "mamba_conv1d_silu_fwd",
-           "mamba_conv1d_silu_update",
+           "mamba_conv1d_silu_update", "mamba_scan_bwd_workspace_size", "mamba_scan_bwd",
            "mamba_status_string")
 
 
@@ -96,6 +98,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mamba_conv1d_silu_fwd.argtypes = [_vp] * 6 + [_i64] * 4 + [ctypes.c_int, _vp]
     lib.mamba_conv1d_silu_update.restype = ctypes.c_int
     lib.mamba_conv1d_silu_update.argtypes = [_vp] * 5 + [_i64] * 3 + [ctypes.c_int, _vp]
+    lib.mamba_scan_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.mamba_scan_bwd_workspace_size.argtypes = [_i64] * 4
+    lib.mamba_scan_bwd.restype = ctypes.c_int
+    lib.mamba_scan_bwd.argtypes = [_vp] * 20 + [_i64] * 4 + [ctypes.c_int, _vp, ctypes.c_size_t,
+                                                              _vp]
     lib.mamba_status_string.restype = ctypes.c_char_p
     lib.mamba_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -321,3 +328,83 @@ def mamba_conv1d_silu_update(state, x, w, conv_bias=None, *, out=None):
     if st != 0:
         raise MambaError(st, "mamba_conv1d_silu_update")
     return u
+
+
+def mamba_scan_bwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state: int) -> int:
+    lib = load_library()
+    n = lib.mamba_scan_bwd_workspace_size(batch, seqlen, d_inner, d_state)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes for mamba_scan_bwd")
+    return int(n)
+
+
+GRAD_NAMES = ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0")
+
+
+def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=None,
+                   dh_last=None, *, want=GRAD_NAMES, out=None, workspace=None) -> dict:
+    """Gradients of the selective scan (Euler); see include/mamba_scan.h.
+
+    Returns a dict with the names of ``want`` (a subset of GRAD_NAMES; du and ddelta are
+    always computed): du, ddelta, dz, dB, dC in the activations' dtype, dA, dD, dbias,
+    dh0 in float32.  dz is None without a gate.  ``out`` may map names to preallocated
+    tensors.
+    """
+    torch = _torch()
+    lib = load_library()
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, seqlen, d_inner)")
+    batch, seqlen, d_inner = u.shape
+    if A.dim() != 2 or A.shape[0] != d_inner:
+        raise ValueError("A must be (d_inner, d_state)")
+    d_state = A.shape[1]
+    dev, act = u.device, u.dtype
+    code = _dtype_code(u)
+    f32 = torch.float32
+    bld, bln, bdn = (batch, seqlen, d_inner), (batch, seqlen, d_state), (batch, d_inner, d_state)
+    p_u = _ptr(u, "u", bld, act, dev)
+    p_delta = _ptr(delta, "delta", bld, act, dev)
+    p_A = _ptr(A, "A", (d_inner, d_state), f32, dev)
+    p_B = _ptr(B, "B", bln, act, dev)
+    p_C = _ptr(C, "C", bln, act, dev)
+    p_D = _ptr(D, "D", (d_inner,), f32, dev)
+    p_z = _ptr(z, "z", bld, act, dev)
+    p_bias = _ptr(delta_bias, "delta_bias", (d_inner,), f32, dev)
+    p_h0 = _ptr(h0, "h0", bdn, f32, dev)
+    p_dy = _ptr(dy, "dy", bld, act, dev)
+    p_dhl = _ptr(dh_last, "dh_last", bdn, f32, dev)
+    unknown = set(want) - set(GRAD_NAMES)
+    if unknown:
+        raise ValueError(f"unknown gradient names {sorted(unknown)}")
+    shapes = {"du": (bld, act), "ddelta": (bld, act), "dz": (bld, act), "dB": (bln, act),
+              "dC": (bln, act), "dA": ((d_inner, d_state), f32), "dD": ((d_inner,), f32),
+              "dbias": ((d_inner,), f32), "dh0": (bdn, f32)}
+    out = dict(out or {})
+    res = {}
+    ptrs = {}
+    for name in GRAD_NAMES:
+        shape, dt = shapes[name]
+        # dz is always computed with a gate (the library requires it), returned if wanted
+        wanted = name in ("du", "ddelta") or name in want or (name == "dz" and z is not None)
+        if name == "dz" and z is None:
+            wanted = False
+        t = out.get(name) if wanted else None
+        if wanted and t is None:
+            t = torch.empty(shape, dtype=dt, device=dev)
+        res[name] = t
+        ptrs[name] = _ptr(t, name, shape, dt, dev)
+    need = lib.mamba_scan_bwd_workspace_size(batch, seqlen, d_inner, d_state)
+    if need == ctypes.c_size_t(-1).value:
+        raise MambaError(4, "mamba_scan_bwd_workspace_size")
+    ws = workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    p_ws = ws.data_ptr() if ws is not None and need > 0 else None
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = lib.mamba_scan_bwd(p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_dy, p_dhl,
+                            ptrs["du"], ptrs["ddelta"], ptrs["dA"], ptrs["dB"], ptrs["dC"],
+                            ptrs["dD"], ptrs["dz"], ptrs["dbias"], ptrs["dh0"],
+                            batch, seqlen, d_inner, d_state, code, p_ws, ws_bytes, _stream(dev))
+    if st != 0:
+        raise MambaError(st, "mamba_scan_bwd")
+    return {k: v for k, v in res.items() if k in ("du", "ddelta") or k in want}

@@ -247,6 +247,33 @@ size_t workspace_bytes_for(int64_t batch, int64_t seqlen, int64_t d_inner, int64
     return n;
 }
 
+// Backward workspace: [staged B/C][segment checkpoints][dB/dC tile partials][dA partials]
+// [dD, dbias partials], each region 256-byte aligned.  Offsets in bytes; total in [5].
+bool bwd_layout(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                size_t off[6], int *seg_len)
+{
+    int waves = 0, S = 0;
+    if (!bwd_variant(d_state, &waves, &S))
+        return false;
+    *seg_len = S;
+    auto al = [](size_t n) { return (n + 255) / 256 * 256; };
+    const size_t n_seg = (size_t)((seqlen + S - 1) / S);
+    const size_t units = (size_t)batch * (size_t)((d_inner + 63) / 64);
+    const size_t N = (size_t)d_state, f = sizeof(float);
+    size_t sz[5];
+    sz[0] = al((size_t)batch * n_seg * S * 2 * N * f);
+    sz[1] = al(units * n_seg * N * 64 * f);
+    sz[2] = al(units * (size_t)seqlen * 2 * N * f);
+    sz[3] = al((size_t)batch * (size_t)d_inner * N * f);
+    sz[4] = al((size_t)batch * (size_t)d_inner * 2 * f);
+    off[0] = 0;
+    for (int i = 0; i < 5; ++i)
+        off[i + 1] = off[i] + sz[i];
+    if (seqlen == 0)
+        off[5] = 0;
+    return true;
+}
+
 mamba_status_t hip_status(hipError_t e) { return e == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP; }
 
 } // namespace
@@ -648,6 +675,176 @@ mamba_status_t mamba_conv1d_silu_update(void *state, const void *x, const float 
     P.d_conv = d_conv;
     P.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
     return hip_status(launch_conv1d_silu_update(P, reinterpret_cast<hipStream_t>(stream)));
+}
+
+
+size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                     int64_t d_state)
+{
+    int64_t t;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 ||
+        !mul_ok(batch, seqlen, &t) || !mul_ok(t, d_inner, &t) || !mul_ok(t, d_state, &t) ||
+        !mul_ok(t, 8, &t))
+        return (size_t)-1;
+    size_t off[6];
+    int S = 0;
+    if (!bwd_layout(batch, seqlen, d_inner, d_state, off, &S))
+        return (size_t)-1;
+    return off[5];
+}
+
+mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, const void *B,
+                              const void *C, const float *D, const void *z,
+                              const float *delta_bias, const float *h0, const void *dy,
+                              const float *dh_last, void *du, void *ddelta, float *dA,
+                              void *dB, void *dC, float *dD, void *dz, float *d_delta_bias,
+                              float *dh0, int64_t batch, int64_t seqlen, int64_t d_inner,
+                              int64_t d_state, mamba_dtype_t dtype, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    // ---- sizes and dtype ----
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
+        return MAMBA_ERR_BAD_DTYPE;
+    int waves = 0, S = 0;
+    if (!bwd_variant(d_state, &waves, &S))
+        return MAMBA_ERR_UNSUPPORTED;
+    const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
+    int64_t bld, bln, bdn, dn, t;
+    if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, d_inner, &bld) || !mul_ok(bld, es, &t) ||
+        !mul_ok(batch, seqlen, &t) || !mul_ok(t, d_state, &bln) || !mul_ok(bln, es, &t) ||
+        !mul_ok(bld, d_state, &t) || !mul_ok(t, 8, &t) || !mul_ok(batch, d_inner, &t) ||
+        !mul_ok(t, d_state, &bdn) || !mul_ok(bdn, 4, &t) || !mul_ok(d_inner, d_state, &dn) ||
+        !mul_ok(dn, 4, &t) || d_inner > INT32_MAX || batch > INT32_MAX ||
+        (seqlen + S - 1) / S > INT32_MAX)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (batch == 0 || d_inner == 0)
+        return MAMBA_OK;
+
+    // ---- required pointers ----
+    const bool has_seq = seqlen > 0;
+    if (!A || (has_seq && (!u || !delta || !B || !C || !dy || !du || !ddelta)) ||
+        (has_seq && z && !dz))
+        return MAMBA_ERR_NULL_ARG;
+    if (!z)
+        dz = nullptr; // no gate: there is no dz to write
+
+    // ---- alignment ----
+    const void *elem_ptrs[] = {u, delta, B, C, z, dy, du, ddelta, dB, dC, dz};
+    for (const void *p : elem_ptrs)
+        if (p && !aligned(p, (size_t)es))
+            return MAMBA_ERR_MISALIGNED;
+    const void *f32_ptrs[] = {A, D, delta_bias, h0, dh_last, dA, dD, d_delta_bias, dh0};
+    for (const void *p : f32_ptrs)
+        if (p && !aligned(p, 4))
+            return MAMBA_ERR_MISALIGNED;
+
+    // ---- workspace ----
+    size_t off[6];
+    (void)bwd_layout(batch, seqlen, d_inner, d_state, off, &S);
+    const size_t need = off[5];
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return MAMBA_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 4))
+        return MAMBA_ERR_MISALIGNED;
+
+    // ---- aliasing: every output is disjoint from every input and every other output ----
+    const Range r_in[] = {range_of(u, bld * es),       range_of(delta, bld * es),
+                          range_of(z, bld * es),       range_of(dy, bld * es),
+                          range_of(B, bln * es),       range_of(C, bln * es),
+                          range_of(A, dn * 4),         range_of(D, d_inner * 4),
+                          range_of(delta_bias, d_inner * 4), range_of(h0, bdn * 4),
+                          range_of(dh_last, bdn * 4)};
+    const Range r_out[] = {range_of(has_seq ? du : nullptr, bld * es),
+                           range_of(has_seq ? ddelta : nullptr, bld * es),
+                           range_of(has_seq ? dz : nullptr, bld * es),
+                           range_of(has_seq ? dB : nullptr, bln * es),
+                           range_of(has_seq ? dC : nullptr, bln * es),
+                           range_of(dA, dn * 4),
+                           range_of(dD, d_inner * 4),
+                           range_of(d_delta_bias, d_inner * 4),
+                           range_of(dh0, bdn * 4),
+                           range_of(need > 0 ? workspace : nullptr, (int64_t)need)};
+    const int n_out = (int)(sizeof(r_out) / sizeof(r_out[0]));
+    for (int i = 0; i < n_out; ++i) {
+        for (const Range &r : r_in)
+            if (overlaps(r_out[i], r))
+                return MAMBA_ERR_ALIASING;
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlaps(r_out[i], r_out[j]))
+                return MAMBA_ERR_ALIASING;
+    }
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+    // ---- empty sequence: dh0 = dh_last, parameter gradients zero ----
+    if (!has_seq) {
+        hipError_t e = hipSuccess;
+        if (dh0)
+            e = launch_copy_state(dh0, dh_last, bdn, st);
+        if (e == hipSuccess && dA)
+            e = launch_copy_state(dA, nullptr, dn, st);
+        if (e == hipSuccess && dD)
+            e = launch_copy_state(dD, nullptr, d_inner, st);
+        if (e == hipSuccess && d_delta_bias)
+            e = launch_copy_state(d_delta_bias, nullptr, d_inner, st);
+        return hip_status(e);
+    }
+
+    char *ws = static_cast<char *>(workspace);
+    const int64_t n_seg = (seqlen + S - 1) / S;
+    const DType dt = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+
+    // B/C staged as fp32 rows for the scalar loads, n_seg * S rows (zero past seqlen)
+    ScanLaunch G{};
+    G.B = B;
+    G.C = C;
+    G.batch = batch;
+    G.L = seqlen;
+    G.d_inner = d_inner;
+    G.d_state = d_state;
+    G.waves = waves;
+    G.dtype = dt;
+    G.bc_staged = reinterpret_cast<float *>(ws + off[0]);
+    G.staged_rows = n_seg * S;
+    G.relay_parts = 1;
+    if (launch_stage_bc(G, st) != hipSuccess)
+        return MAMBA_ERR_HIP;
+
+    BwdLaunch P{};
+    P.u = u;
+    P.delta = delta;
+    P.z = z;
+    P.dy = dy;
+    P.B = B;
+    P.C = C;
+    P.A = A;
+    P.D = D;
+    P.bias = delta_bias;
+    P.h0 = h0;
+    P.dh_last = dh_last;
+    P.du = du;
+    P.ddelta = ddelta;
+    P.dz = dz;
+    P.dB = dB;
+    P.dC = dC;
+    P.dA = dA;
+    P.dD = dD;
+    P.dbias = d_delta_bias;
+    P.dh0 = dh0;
+    P.bc_staged = G.bc_staged;
+    P.staged_rows = G.staged_rows;
+    P.ckpt = reinterpret_cast<float *>(ws + off[1]);
+    P.dbc_part = reinterpret_cast<float *>(ws + off[2]);
+    P.dA_part = reinterpret_cast<float *>(ws + off[3]);
+    P.dDb_part = reinterpret_cast<float *>(ws + off[4]);
+    P.batch = batch;
+    P.L = seqlen;
+    P.d_inner = d_inner;
+    P.d_state = d_state;
+    P.dtype = dt;
+    return hip_status(launch_scan_bwd(P, st));
 }
 
 } // extern "C"

@@ -1,0 +1,605 @@
+// Backward pass of the selective scan (Euler discretisation) for gfx950.
+//
+// Gradients of the forward operation of scan_kernels.hip with respect to all of its
+// inputs, given dy (and optionally the gradient of the final state).  With
+// mu_t[n] = dLoss/dh_t[n], s_t = sum_n C_t[n] h_t[n] + D u_t, ds_t = dy_t silu(z_t):
+//   mu_t = Abar_{t+1} mu_{t+1} + ds_t C_t          (mu_{L-1} = dh_last + ds_{L-1} C_{L-1})
+//   dDelta_t = sum_n mu_t (A Abar_t h_{t-1} + B_t u_t),  du_t = ds_t D + Delta_t sum_n mu_t B_t
+//   dB_t[n] = sum_d mu_t Delta_t u_t,  dC_t[n] = sum_d ds_t h_t,  dA = sum mu_t Delta_t Abar_t h_{t-1}
+//   dD = sum ds_t u_t,  dz_t = dy_t s_t silu'(z_t),  ddelta_t = dDelta_t sigmoid(delta_t + bias)
+//   dh0 = Abar_0 mu_0.
+// This is the chain rule applied to the recurrence of "Understanding Mamba"
+// (aiattnstudio.link, sections 4.4 and 5.2), whose section 7.3 (and section 4.4 of the
+// hnwysp.cn slides) names the approach taken for the states: they are recomputed in the
+// backward pass rather than stored for every step.
+//
+// Work decomposition: the forward scalar kernel's -- one block per (batch row, 64-channel
+// tile), lane = channel, wave g owns state indices [g*NQ, (g+1)*NQ), B and C staged as
+// fp32 and read through SGPRs.  Each block
+//   1. runs the recurrence forward once and stores the state entering every segment of
+//      S steps (a checkpoint per lane and state index, in the workspace);
+//   2. walks the segments backwards: recomputes the segment's states and decay factors
+//      into registers from its checkpoint, then runs the adjoint recurrence mu backwards
+//      through it.
+// Per (step, channel) quantities (Delta, Delta*u, ds) are computed once and shared
+// through LDS; the per-wave partial sums over state indices (readout, sum mu B, sum
+// A mu Abar h) are summed across waves through LDS in a fixed order.  dB and dC need sums
+// over the block's 64 channels (the lanes): each wave reduces its values of 8 steps with a
+// transposed butterfly (every exchange halves the values a lane holds, so 2*NQ*8 sums
+// across 64 lanes cost about two exchanges per value) and writes one partial per
+// (tile, t, n); a second kernel sums the tiles, and dA, dD, dbias over the batch.
+// Nothing is accumulated with atomics: results are bitwise reproducible.
+#include <type_traits>
+
+#include "device_math.h"
+#include "scan_common.h"
+
+namespace mambascan {
+namespace {
+
+typedef const __attribute__((address_space(4))) float *cfloat_ptr;
+
+constexpr int kRH = 8;  // reverse steps per cross-wave exchange (and per lane reduction)
+constexpr int kTCF = 8; // steps per chunk of the checkpointing forward pass
+
+struct BwdArgs {
+    const void *u, *delta, *z, *dy;
+    const float *bcp; // staged B/C: [b][wave][t][B(NQ), C(NQ)], Lp rows
+    const float *A, *D, *bias, *h0, *dh_last;
+    void *du, *ddelta, *dz;
+    float *dh0;
+    float *ckpt;     // [block][segment][n][lane]
+    float *dbc_part; // [(block * L + t) * 2N + {n, N + n}]: this tile's dB, dC
+    float *dA_part;  // [b][d][n]
+    float *dDb_part; // [b][d][2]: dD, dbias of one batch row
+    int64_t L, Lp;
+    int32_t Dn, batch, n_seg;
+};
+
+// Value of lane (lane ^ pattern) for the butterfly's partner patterns.  Lane bits 3, 2, 1
+// and 0 use DPP row_mirror (l ^ 15 within a row), row_half_mirror (l ^ 7 within 8 lanes),
+// quad_perm [3,2,1,0] (l ^ 3) and quad_perm [1,0,3,2] (l ^ 1): each flips the named bit
+// and only lower ones, so applied from bit 3 down, partners always hold the same value
+// indices.  Bits 4 and 5 use lane shuffles.
+template <int BIT>
+__device__ __forceinline__ float partner(float v)
+{
+    const int x = __builtin_bit_cast(int, v);
+    if constexpr (BIT == 3)
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, true));
+    else if constexpr (BIT == 2)
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, true));
+    else if constexpr (BIT == 1)
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x1B, 0xF, 0xF, true));
+    else if constexpr (BIT == 0)
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true));
+    else if constexpr (BIT == 4)
+        return __shfl_xor(v, 16);
+    else
+        return __shfl_xor(v, 32);
+}
+
+// One butterfly exchange: lanes whose bit BIT is clear keep value index `lo`, the others
+// `hi`; each adds its partner's copy of the index it keeps.
+template <int BIT>
+__device__ __forceinline__ float halve(float lo, float hi, int lane)
+{
+    const bool up = (lane >> BIT) & 1;
+    const float keep = up ? hi : lo;
+    const float send = up ? lo : hi;
+    return keep + partner<BIT>(send);
+}
+
+template <typename T>
+__device__ __forceinline__ T zero_val()
+{
+    return T(0);
+}
+
+template <typename T, int N, int NW, int S, bool GATED>
+__global__ void __launch_bounds__(64 * NW)
+scan_bwd_kernel(BwdArgs p)
+{
+    constexpr int NQ = N / NW;     // state indices per lane
+    constexpr int BCW = 2 * NQ;    // staged B then C per step; also dB/dC values per step
+    constexpr int RH = kRH;
+    constexpr int NH = S / RH;     // reverse parts per segment
+    constexpr int KP = S / NW;     // a segment's (step, channel) items per lane
+    constexpr int KF = kTCF / NW;  // a forward chunk's items per lane
+    constexpr int KE = RH / NW;    // a reverse part's items per lane
+    static_assert(NQ >= 1 && N % NW == 0 && S % RH == 0 && RH % NW == 0 && kTCF % NW == 0 &&
+                  S % kTCF == 0, "bad variant");
+    static_assert(BCW == 2 || BCW == 4 || BCW == 8, "butterfly handles 2 to 8 values per step");
+
+    __shared__ float4 s_in[S][64];       // Delta, Delta*u, ds per (step, channel)
+    __shared__ float s_p[3][RH][NW][64]; // readout, sum mu B, sum A mu Abar h per wave
+
+    const int lane = threadIdx.x & 63;
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int bid = blockIdx.x;             // = tile * batch + b
+    const int b = bid % p.batch;
+    const int tile = bid / p.batch;
+    const int Dn = p.Dn;
+    const int d = tile * 64 + lane;
+    const bool dvalid = d < Dn;
+    const int dc = dvalid ? d : Dn - 1; // tail lanes compute on a valid channel with dy = 0
+    const int n0 = g * NQ;
+    const int64_t L = p.L;
+
+    float a2[NQ], an[NQ], h[NQ], hstart[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const float av = p.A[(int64_t)dc * N + n0 + q];
+        a2[q] = av * kLog2e;
+        an[q] = av;
+        h[q] = p.h0 ? p.h0[((int64_t)b * Dn + dc) * N + n0 + q] : 0.0f;
+        hstart[q] = h[q];
+    }
+    const float bias_d = p.bias ? p.bias[dc] : 0.0f;
+    const float D_d = p.D ? p.D[dc] : 0.0f;
+
+    const int64_t row0 = (int64_t)b * L * Dn; // element offset of (b, 0, 0)
+    const T *ub = (const T *)p.u + row0 + dc;
+    const T *db = (const T *)p.delta + row0 + dc;
+    const T *zb = GATED ? (const T *)p.z + row0 + dc : nullptr;
+    const T *gb = (const T *)p.dy + row0 + dc;
+    const float *bc_row = p.bcp + ((int64_t)b * NW + g) * p.Lp * BCW;
+    float *ck = p.ckpt + (int64_t)bid * p.n_seg * N * 64;
+
+    // ---- 1. forward pass: checkpoints at the start of segments 1 .. n_seg-1 ----
+    {
+        float2 *s_f = reinterpret_cast<float2 *>(&s_in[0][0]); // [2][kTCF][64]
+        const int64_t LF = (int64_t)(p.n_seg - 1) * S;          // whole segments only
+        T fu[KF], fd[KF];
+        auto ffetch = [&](int64_t t0) {
+#pragma unroll
+            for (int k = 0; k < KF; ++k) {
+                const int64_t t = t0 + g + k * NW;
+                fu[k] = ub[t * Dn];
+                fd[k] = db[t * Dn];
+            }
+        };
+        if (LF > 0)
+            ffetch(0);
+        int par = 0;
+        for (int64_t t0 = 0; t0 < LF; t0 += kTCF) {
+#pragma unroll
+            for (int k = 0; k < KF; ++k) {
+                const int tl = g + k * NW;
+                const float dl = softplus_f(widen(fd[k]) + bias_d);
+                s_f[(par * kTCF + tl) * 64 + lane] = make_float2(dl, dl * widen(fu[k]));
+            }
+            if (t0 + kTCF < LF)
+                ffetch(t0 + kTCF);
+            float bs[kTCF][NQ];
+            const cfloat_ptr q = (cfloat_ptr)(bc_row + t0 * BCW);
+#pragma unroll
+            for (int tl = 0; tl < kTCF; ++tl)
+#pragma unroll
+                for (int i = 0; i < NQ; ++i)
+                    bs[tl][i] = q[tl * BCW + i];
+            __syncthreads();
+#pragma unroll
+            for (int tl = 0; tl < kTCF; ++tl) {
+                const float2 w = s_f[(par * kTCF + tl) * 64 + lane];
+#pragma unroll
+                for (int i = 0; i < NQ; ++i)
+                    h[i] = __builtin_fmaf(decay_exp2(w.x, a2[i]), h[i], w.y * bs[tl][i]);
+            }
+            if ((t0 + kTCF) % S == 0) {
+                const int64_t seg = (t0 + kTCF) / S;
+#pragma unroll
+                for (int i = 0; i < NQ; ++i)
+                    ck[(seg * N + n0 + i) * 64 + lane] = h[i];
+            }
+            par ^= 1;
+        }
+        __syncthreads(); // s_f aliases s_in
+    }
+
+    // ---- 2. segments in reverse ----
+    float mu[NQ], dA[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        mu[q] = (p.dh_last && dvalid) ? p.dh_last[((int64_t)b * Dn + d) * N + n0 + q] : 0.0f;
+        dA[q] = 0.0f;
+    }
+    float dD_acc = 0.0f, db_acc = 0.0f;
+
+    T ru[KP], rd[KP], rz[KP], rg[KP];
+    auto rfetch = [&](int seg) {
+        const int64_t t0 = (int64_t)seg * S;
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            const int64_t t = t0 + g + k * NW;
+            ru[k] = rd[k] = rz[k] = rg[k] = zero_val<T>();
+            if (t < L) {
+                ru[k] = ub[t * Dn];
+                rd[k] = db[t * Dn];
+                if (GATED)
+                    rz[k] = zb[t * Dn];
+                if (dvalid)
+                    rg[k] = gb[t * Dn];
+            }
+        }
+    };
+    if (p.n_seg > 0)
+        rfetch(p.n_seg - 1);
+
+    float bcs[RH][BCW];
+    for (int seg = p.n_seg - 1; seg >= 0; --seg) {
+        const int64_t t0 = (int64_t)seg * S;
+        const int nt = (int)min((int64_t)S, L - t0);
+
+        // prologue: per (step, channel) values, kept by this lane for the epilogue
+        float e_u[KP], e_dl[KP], e_sig[KP], e_ds[KP], e_dyg[KP];
+#pragma unroll
+        for (int k = 0; k < KP; ++k) {
+            const int tl = g + k * NW;
+            const float uu = widen(ru[k]);
+            const float v = widen(rd[k]) + bias_d;
+            const float dl = softplus_f(v);
+            const float dyv = widen(rg[k]);
+            float gate = 1.0f, dgate = 0.0f;
+            if (GATED) {
+                const float zz = widen(rz[k]);
+                const float sz = hw_rcp(1.0f + hw_exp2(-zz * kLog2e));
+                gate = zz * sz;
+                dgate = sz * __builtin_fmaf(zz, 1.0f - sz, 1.0f);
+            }
+            const float ds = dyv * gate;
+            e_u[k] = uu;
+            e_dl[k] = dl;
+            e_sig[k] = hw_rcp(1.0f + hw_exp2(-v * kLog2e)); // softplus'(v)
+            e_ds[k] = ds;
+            e_dyg[k] = dyv * dgate;
+            s_in[tl][lane] = make_float4(dl, dl * uu, ds, 0.0f);
+        }
+        if (seg > 0)
+            rfetch(seg - 1);
+        float hin[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            hin[q] = seg == 0 ? hstart[q] : ck[((int64_t)seg * N + n0 + q) * 64 + lane];
+        __syncthreads();
+
+        auto load_bc = [&](int part) {
+            const cfloat_ptr q = (cfloat_ptr)(bc_row + (t0 + part * RH) * BCW);
+#pragma unroll
+            for (int tl = 0; tl < RH; ++tl)
+#pragma unroll
+                for (int i = 0; i < BCW; ++i)
+                    bcs[tl][i] = q[tl * BCW + i];
+        };
+
+        // recompute the segment's states and decay factors
+        float hs[S][NQ], ab[S][NQ];
+        {
+            float hc[NQ];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                hc[q] = hin[q];
+#pragma unroll
+            for (int part = 0; part < NH; ++part) {
+                load_bc(part);
+#pragma unroll
+                for (int tl = 0; tl < RH; ++tl) {
+                    const int T_ = part * RH + tl;
+                    if (T_ < nt) {
+                        const float4 w = s_in[T_][lane];
+#pragma unroll
+                        for (int q = 0; q < NQ; ++q) {
+                            const float a = decay_exp2(w.x, a2[q]);
+                            hc[q] = __builtin_fmaf(a, hc[q], w.y * bcs[tl][q]);
+                            ab[T_][q] = a;
+                            hs[T_][q] = hc[q];
+                        }
+                    }
+                }
+            }
+        }
+
+        // adjoint recurrence, last part first
+#pragma unroll
+        for (int part = NH - 1; part >= 0; --part) {
+            if (part != NH - 1)
+                load_bc(part);
+            float pend[BCW], r1[4][BCW], r2[2][BCW], r3[BCW];
+#pragma unroll
+            for (int tl = RH - 1; tl >= 0; --tl) {
+                const int T_ = part * RH + tl;
+                float xv[BCW];
+                float yp = 0.0f, p1 = 0.0f, p2 = 0.0f;
+#pragma unroll
+                for (int i = 0; i < BCW; ++i)
+                    xv[i] = 0.0f;
+                if (T_ < nt) {
+                    const float4 w = s_in[T_][lane]; // Delta, Delta*u, ds
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        const float cq = bcs[tl][NQ + q];
+                        yp = __builtin_fmaf(cq, hs[T_][q], yp);
+                        mu[q] = __builtin_fmaf(w.z, cq, mu[q]); // mu_t
+                        p1 = __builtin_fmaf(mu[q], bcs[tl][q], p1);
+                        xv[q] = mu[q] * w.y;                    // dB
+                        xv[NQ + q] = w.z * hs[T_][q];           // dC
+                        const float hp = T_ == 0 ? hin[q] : hs[T_ > 0 ? T_ - 1 : 0][q];
+                        const float m2 = mu[q] * ab[T_][q];     // Abar_t mu_t
+                        const float qv = m2 * hp;
+                        p2 = __builtin_fmaf(an[q], qv, p2);
+                        dA[q] = __builtin_fmaf(w.x, qv, dA[q]);
+                        mu[q] = m2;
+                    }
+                }
+                s_p[0][tl][g][lane] = yp;
+                s_p[1][tl][g][lane] = p1;
+                s_p[2][tl][g][lane] = p2;
+
+                // butterfly over the steps of this part: step bit 0, 1, 2 on lane bit 3, 2, 1
+                if (tl & 1) {
+#pragma unroll
+                    for (int i = 0; i < BCW; ++i)
+                        pend[i] = xv[i];
+                } else {
+                    const int m = tl >> 1;
+#pragma unroll
+                    for (int i = 0; i < BCW; ++i)
+                        r1[m][i] = halve<3>(xv[i], pend[i], lane);
+                    if ((m & 1) == 0) {
+#pragma unroll
+                        for (int i = 0; i < BCW; ++i)
+                            r2[m >> 1][i] = halve<2>(r1[m][i], r1[m + 1][i], lane);
+                        if (m == 0) {
+#pragma unroll
+                            for (int i = 0; i < BCW; ++i)
+                                r3[i] = halve<1>(r2[0][i], r2[1][i], lane);
+                        }
+                    }
+                }
+            }
+            // value bits (kind, state) on lane bits 0, 4, 5; the remaining lane bits sum
+            float v;
+            if constexpr (BCW == 2) {
+                v = halve<0>(r3[0], r3[1], lane);
+                v += partner<4>(v);
+                v += partner<5>(v);
+            } else if constexpr (BCW == 4) {
+                const float s0 = halve<0>(r3[0], r3[1], lane);
+                const float s1 = halve<0>(r3[2], r3[3], lane);
+                v = halve<4>(s0, s1, lane);
+                v += partner<5>(v);
+            } else {
+                float s1[4], s2[2];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s1[i] = halve<0>(r3[2 * i], r3[2 * i + 1], lane);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    s2[i] = halve<4>(s1[2 * i], s1[2 * i + 1], lane);
+                v = halve<5>(s2[0], s2[1], lane);
+            }
+            {
+                const int tlo = ((lane >> 3) & 1) | (((lane >> 2) & 1) << 1) | (((lane >> 1) & 1) << 2);
+                int j = lane & 1;
+                bool writer;
+                if constexpr (BCW == 2) {
+                    writer = (lane >> 4) == 0;
+                } else if constexpr (BCW == 4) {
+                    j |= ((lane >> 4) & 1) << 1;
+                    writer = (lane >> 5) == 0;
+                } else {
+                    j |= ((lane >> 4) & 1) << 1;
+                    j |= ((lane >> 5) & 1) << 2;
+                    writer = true;
+                }
+                const int64_t t = t0 + part * RH + tlo;
+                if (writer && t < L) {
+                    const int kind = j / NQ, q = j % NQ;
+                    p.dbc_part[((int64_t)bid * L + t) * (2 * N) + kind * N + n0 + q] = v;
+                }
+            }
+            __syncthreads();
+
+            // epilogue of this part: sums over waves, per (step, channel) gradients
+#pragma unroll
+            for (int k = part * KE; k < (part + 1) * KE; ++k) {
+                const int tl = g + k * NW;
+                const int lt = tl - part * RH;
+                float Y = s_p[0][lt][0][lane], P1 = s_p[1][lt][0][lane], P2 = s_p[2][lt][0][lane];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) {
+                    Y += s_p[0][lt][w][lane];
+                    P1 += s_p[1][lt][w][lane];
+                    P2 += s_p[2][lt][w][lane];
+                }
+                if (tl < nt) {
+                    const int64_t t = t0 + tl;
+                    const float ddt = __builtin_fmaf(e_u[k], P1, P2);
+                    const float dd = ddt * e_sig[k];
+                    const float duv = __builtin_fmaf(e_ds[k], D_d, e_dl[k] * P1);
+                    dD_acc = __builtin_fmaf(e_ds[k], e_u[k], dD_acc);
+                    db_acc += dd;
+                    if (dvalid) {
+                        const int64_t o = row0 + t * Dn + d;
+                        store_val((T *)p.du, o, duv);
+                        store_val((T *)p.ddelta, o, dd);
+                        if (GATED)
+                            store_val((T *)p.dz, o, e_dyg[k] * __builtin_fmaf(D_d, e_u[k], Y));
+                    }
+                }
+            }
+            if (part > 0)
+                __syncthreads(); // the next part rewrites s_p
+        }
+    }
+
+    // ---- 3. per-block results ----
+    if (dvalid) {
+        const int64_t col = ((int64_t)b * Dn + d) * N + n0;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            p.dA_part[col + q] = dA[q];
+            if (p.dh0)
+                p.dh0[col + q] = mu[q]; // Abar_0 mu_0
+        }
+    }
+    __syncthreads();
+    s_p[0][0][g][lane] = dD_acc;
+    s_p[1][0][g][lane] = db_acc;
+    __syncthreads();
+    if (g == 0 && dvalid) {
+        float sD = s_p[0][0][0][lane], sb = s_p[1][0][0][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            sD += s_p[0][0][w][lane];
+            sb += s_p[1][0][w][lane];
+        }
+        p.dDb_part[((int64_t)b * Dn + d) * 2 + 0] = sD;
+        p.dDb_part[((int64_t)b * Dn + d) * 2 + 1] = sb;
+    }
+}
+
+// dB, dC: sums of the tiles' partials (fixed tile order), rounded to the input dtype.
+template <typename T>
+__global__ void __launch_bounds__(256)
+bwd_reduce_bc_kernel(const float *__restrict__ part, T *dB, T *dC, int64_t batch, int64_t L,
+                     int32_t N, int32_t tiles)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; // (b * L + t) * 2N + j
+    const int64_t total = batch * L * 2 * N;
+    if (i >= total)
+        return;
+    const int j = (int)(i % (2 * N));
+    const int64_t bt = i / (2 * N);
+    const int64_t b = bt / L, t = bt % L;
+    float s = 0.0f;
+    for (int tile = 0; tile < tiles; ++tile)
+        s += part[(((int64_t)tile * batch + b) * L + t) * (2 * N) + j];
+    if (j < N) {
+        if (dB)
+            store_val(dB, bt * N + j, s);
+    } else if (dC) {
+        store_val(dC, bt * N + (j - N), s);
+    }
+}
+
+// dA = sum over batch rows of dA_part; dD, dbias likewise (fixed row order).
+__global__ void __launch_bounds__(256)
+bwd_reduce_params_kernel(const float *__restrict__ dA_part, const float *__restrict__ dDb_part,
+                         float *dA, float *dD, float *dbias, int64_t batch, int64_t Dn, int64_t N)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t dn = Dn * N;
+    if (i < dn) {
+        if (dA) {
+            float s = 0.0f;
+            for (int64_t b = 0; b < batch; ++b)
+                s += dA_part[b * dn + i];
+            dA[i] = s;
+        }
+    } else if (i < dn + Dn) {
+        const int64_t d = i - dn;
+        float sD = 0.0f, sb = 0.0f;
+        for (int64_t b = 0; b < batch; ++b) {
+            sD += dDb_part[(b * Dn + d) * 2 + 0];
+            sb += dDb_part[(b * Dn + d) * 2 + 1];
+        }
+        if (dD)
+            dD[d] = sD;
+        if (dbias)
+            dbias[d] = sb;
+    }
+}
+
+// (d_state, waves, segment length)
+#define MAMBA_BWD_VARIANTS(X) \
+    X(4, 4, 16)               \
+    X(8, 8, 16)               \
+    X(16, 8, 16)              \
+    X(32, 8, 8)
+
+template <typename T, int N, int NW, int S>
+hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
+{
+    BwdArgs a{};
+    a.u = q.u;
+    a.delta = q.delta;
+    a.z = q.z;
+    a.dy = q.dy;
+    a.bcp = q.bc_staged;
+    a.A = q.A;
+    a.D = q.D;
+    a.bias = q.bias;
+    a.h0 = q.h0;
+    a.dh_last = q.dh_last;
+    a.du = q.du;
+    a.ddelta = q.ddelta;
+    a.dz = q.dz;
+    a.dh0 = q.dh0;
+    a.ckpt = q.ckpt;
+    a.dbc_part = q.dbc_part;
+    a.dA_part = q.dA_part;
+    a.dDb_part = q.dDb_part;
+    a.L = q.L;
+    a.Lp = q.staged_rows;
+    a.Dn = (int32_t)q.d_inner;
+    a.batch = (int32_t)q.batch;
+    a.n_seg = (int32_t)((q.L + S - 1) / S);
+    const int64_t tiles = (q.d_inner + 63) / 64;
+    const int64_t blocks = tiles * q.batch;
+    if (blocks <= 0 || q.L <= 0)
+        return hipSuccess;
+    if (q.z)
+        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, true>), dim3((uint32_t)blocks),
+                           dim3(64 * NW), 0, stream, a);
+    else
+        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, false>), dim3((uint32_t)blocks),
+                           dim3(64 * NW), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t nbc = q.batch * q.L * 2 * N;
+    if (q.dB || q.dC)
+        hipLaunchKernelGGL((bwd_reduce_bc_kernel<T>), dim3((uint32_t)((nbc + 255) / 256)),
+                           dim3(256), 0, stream, q.dbc_part, (T *)q.dB, (T *)q.dC, q.batch,
+                           q.L, (int32_t)N, (int32_t)tiles);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t np = q.d_inner * N + q.d_inner;
+    if (q.dA || q.dD || q.dbias)
+        hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((uint32_t)((np + 255) / 256)),
+                           dim3(256), 0, stream, q.dA_part, q.dDb_part, q.dA, q.dD, q.dbias,
+                           q.batch, q.d_inner, (int64_t)N);
+    return hipGetLastError();
+}
+
+} // namespace
+
+bool bwd_variant(int64_t d_state, int *waves, int *seg_len)
+{
+#define X(N_, W_, S_)                 \
+    if (d_state == N_) {              \
+        *waves = W_;                  \
+        *seg_len = S_;                \
+        return true;                  \
+    }
+    MAMBA_BWD_VARIANTS(X)
+#undef X
+    return false;
+}
+
+hipError_t launch_scan_bwd(const BwdLaunch &q, hipStream_t stream)
+{
+#define X(N_, W_, S_)                                                  \
+    if (q.d_state == N_) {                                             \
+        if (q.dtype == DType::BF16)                                    \
+            return launch_bwd_t<uint16_t, N_, W_, S_>(q, stream);      \
+        return launch_bwd_t<float, N_, W_, S_>(q, stream);             \
+    }
+    MAMBA_BWD_VARIANTS(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+} // namespace mambascan

@@ -81,6 +81,22 @@ struct StepLaunch {
     bool zoh;
 };
 
+// Backward pass (Euler discretisation).  Optional outputs are NULL when not wanted.
+struct BwdLaunch {
+    const void *u, *delta, *z, *dy, *B, *C;
+    const float *A, *D, *bias, *h0, *dh_last;
+    void *du, *ddelta, *dz, *dB, *dC; // activation dtype
+    float *dA, *dD, *dbias, *dh0;
+    float *bc_staged;   // staged B/C (the scalar forward's layout), staged_rows rows
+    int64_t staged_rows;
+    float *ckpt;        // [block][segment][n][lane]
+    float *dbc_part;    // [block][t][2N]
+    float *dA_part;     // [b][d][n]
+    float *dDb_part;    // [b][d][2]
+    int64_t batch, L, d_inner, d_state;
+    DType dtype;
+};
+
 // Returns true if the (d_state, waves, chunk) combination is compiled in.
 bool scan_variant_supported(int64_t d_state, int waves, int chunk);
 int default_waves(int64_t d_state);
@@ -101,6 +117,9 @@ hipError_t launch_carry(const CarryLaunch &p, hipStream_t stream);
 hipError_t launch_state_update(const StepLaunch &p, hipStream_t stream);
 hipError_t launch_conv1d_silu(const ConvLaunch &p, hipStream_t stream);
 hipError_t launch_conv1d_silu_update(const ConvLaunch &p, hipStream_t stream);
+// Backward pass: (waves, segment length) of the compiled variant for d_state, and launch.
+bool bwd_variant(int64_t d_state, int *waves, int *seg_len);
+hipError_t launch_scan_bwd(const BwdLaunch &p, hipStream_t stream);
 // h_last = h0 (or zeros when h0 is NULL), for empty sequences.
 hipError_t launch_copy_state(float *dst, const float *src, int64_t count, hipStream_t stream);
 

@@ -297,3 +297,23 @@ def make_conv_step(step: int, batch: int, d_inner: int, dtype: str = BF16,
                    seed: int = 7206) -> np.ndarray:
     """One decode token's x (spawn keys (2000 + step, 10))."""
     return _normal(seed, (2000 + step, 10), (batch, d_inner), dtype)
+
+
+# ----------------------------------------------------------------------------
+# upstream gradients for the backward pass
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class UpstreamGrads:
+    dy: np.ndarray                  # (batch, L, d_inner), stored dtype
+    dh_last: Optional[np.ndarray]   # (batch, d_inner, d_state) float32
+
+
+def make_upstream_grads(cfg: ScanConfig, with_dh_last: bool = True) -> UpstreamGrads:
+    """dy ~ N(0, 1) in the config's dtype (tensor id 6) and dh_last ~ N(0, 1) float32
+    (id 7), drawn like the activations of the same config (pass the config of the
+    ScanInputs, which carries any shape overrides)."""
+    dy = _normal(cfg.seed, (6,), (cfg.batch, cfg.seqlen, cfg.d_inner), cfg.dtype)
+    dhl = (_normal(cfg.seed, (7,), (cfg.batch, cfg.d_inner, cfg.d_state), F32)
+           if with_dh_last else None)
+    return UpstreamGrads(dy=dy, dh_last=dhl)

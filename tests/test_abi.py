@@ -295,3 +295,55 @@ def test_discretization_options(lib):
     assert lib.mamba_state_update_ex(BASE, BASE + 100 * MB, BASE + 110 * MB, BASE + 120 * MB,
                                      BASE + 130 * MB, BASE + 131 * MB, None, None, None,
                                      BASE + 140 * MB, 4, 256, 16, BF16, 7, None) == UNSUP
+
+
+# ---- backward pass ----------------------------------------------------------------
+
+def bwd(lib, *, u=BASE, delta=BASE + 64 * MB, A=BASE + 128 * MB, B=BASE + 132 * MB,
+        C=BASE + 136 * MB, D=None, z=None, bias=None, h0=None, dy=BASE + 160 * MB,
+        dh_last=None, du=BASE + 256 * MB, ddelta=BASE + 320 * MB, dA=None, dB=None, dC=None,
+        dD=None, dz=None, dbias=None, dh0=None, batch=2, L=64, Dn=128, N=16, dtype=BF16,
+        ws=BASE + 1024 * MB, ws_bytes=None):
+    if ws_bytes is None:
+        n = lib.mamba_scan_bwd_workspace_size(batch, L, Dn, N)
+        ws_bytes = n if n != ctypes.c_size_t(-1).value else 0
+    return lib.mamba_scan_bwd(u, delta, A, B, C, D, z, bias, h0, dy, dh_last, du, ddelta, dA,
+                              dB, dC, dD, dz, dbias, dh0, batch, L, Dn, N, dtype, ws, ws_bytes,
+                              None)
+
+
+def test_bwd_workspace_size(lib):
+    n = lib.mamba_scan_bwd_workspace_size(8, 4096, 5120, 16)
+    # checkpoints (a state every 16 steps) plus the per-tile dB/dC partials dominate
+    ck = 8 * 80 * 256 * 16 * 64 * 4
+    part = 8 * 80 * 4096 * 32 * 4
+    assert ck + part < n < ck + part + 16 * MB
+    assert lib.mamba_scan_bwd_workspace_size(2, 0, 64, 16) == 0
+    bad = ctypes.c_size_t(-1).value
+    assert lib.mamba_scan_bwd_workspace_size(2, 64, 64, 64) == bad  # d_state 64: no backward
+    assert lib.mamba_scan_bwd_workspace_size(-1, 64, 64, 16) == bad
+    assert lib.mamba_scan_bwd_workspace_size(1 << 40, 1 << 40, 64, 16) == bad
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, u=None) == NULL
+    assert bwd(lib, dy=None) == NULL
+    assert bwd(lib, du=None) == NULL
+    assert bwd(lib, ddelta=None) == NULL
+    assert bwd(lib, A=None) == NULL
+    assert bwd(lib, z=BASE + 200 * MB) == NULL          # a gate needs dz
+    assert bwd(lib, N=64) == UNSUP
+    assert bwd(lib, N=12) == UNSUP
+    assert bwd(lib, dtype=5) == DTYPE
+    assert bwd(lib, batch=-1) == SHAPE
+    assert bwd(lib, batch=0, u=None, du=None) == OK
+    assert bwd(lib, u=BASE + 1) == ALIGN
+    assert bwd(lib, dA=BASE + 400 * MB + 2) == ALIGN
+    assert bwd(lib, ws=None) == WS
+    assert bwd(lib, ws_bytes=1024) == WS
+    # outputs may not overlap inputs, each other, or the workspace
+    assert bwd(lib, du=BASE + 64 * MB) == ALIAS
+    assert bwd(lib, ddelta=BASE + 256 * MB + 2) == ALIAS
+    assert bwd(lib, dB=BASE + 132 * MB) == ALIAS
+    assert bwd(lib, dh0=BASE + 1024 * MB + 4096) == ALIAS
+    assert bwd(lib, dA=BASE + 160 * MB) == ALIAS
