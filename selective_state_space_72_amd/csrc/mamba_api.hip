@@ -247,10 +247,10 @@ size_t workspace_bytes_for(int64_t batch, int64_t seqlen, int64_t d_inner, int64
     return n;
 }
 
-// Backward workspace: [staged B/C][segment checkpoints][dB/dC tile partials][dA partials]
-// [dD, dbias partials], each region 256-byte aligned.  Offsets in bytes; total in [5].
+// Backward workspace: [segment checkpoints][dB/dC tile partials][dA partials]
+// [dD, dbias partials], each region 256-byte aligned.  Offsets in bytes; total in off[4].
 bool bwd_layout(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                size_t off[6], int *seg_len)
+                size_t off[5], int *seg_len)
 {
     int waves = 0, S = 0;
     if (!bwd_variant(d_state, &waves, &S))
@@ -260,17 +260,16 @@ bool bwd_layout(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
     const size_t n_seg = (size_t)((seqlen + S - 1) / S);
     const size_t units = (size_t)batch * (size_t)((d_inner + 63) / 64);
     const size_t N = (size_t)d_state, f = sizeof(float);
-    size_t sz[5];
-    sz[0] = al((size_t)batch * n_seg * S * 2 * N * f);
-    sz[1] = al(units * n_seg * N * 64 * f);
-    sz[2] = al(units * (size_t)seqlen * 2 * N * f);
-    sz[3] = al((size_t)batch * (size_t)d_inner * N * f);
-    sz[4] = al((size_t)batch * (size_t)d_inner * 2 * f);
+    size_t sz[4];
+    sz[0] = al(units * n_seg * N * 64 * f);
+    sz[1] = al(units * (size_t)seqlen * 2 * N * f);
+    sz[2] = al((size_t)batch * (size_t)d_inner * N * f);
+    sz[3] = al((size_t)batch * (size_t)d_inner * 2 * f);
     off[0] = 0;
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < 4; ++i)
         off[i + 1] = off[i] + sz[i];
     if (seqlen == 0)
-        off[5] = 0;
+        off[4] = 0;
     return true;
 }
 
@@ -686,11 +685,11 @@ size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_in
         !mul_ok(batch, seqlen, &t) || !mul_ok(t, d_inner, &t) || !mul_ok(t, d_state, &t) ||
         !mul_ok(t, 8, &t))
         return (size_t)-1;
-    size_t off[6];
+    size_t off[5];
     int S = 0;
     if (!bwd_layout(batch, seqlen, d_inner, d_state, off, &S))
         return (size_t)-1;
-    return off[5];
+    return off[4];
 }
 
 mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, const void *B,
@@ -741,9 +740,9 @@ mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, 
             return MAMBA_ERR_MISALIGNED;
 
     // ---- workspace ----
-    size_t off[6];
+    size_t off[5];
     (void)bwd_layout(batch, seqlen, d_inner, d_state, off, &S);
-    const size_t need = off[5];
+    const size_t need = off[4];
     if (need > 0 && (!workspace || workspace_bytes < need))
         return MAMBA_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 4))
@@ -793,24 +792,7 @@ mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, 
     }
 
     char *ws = static_cast<char *>(workspace);
-    const int64_t n_seg = (seqlen + S - 1) / S;
     const DType dt = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
-
-    // B/C staged as fp32 rows for the scalar loads, n_seg * S rows (zero past seqlen)
-    ScanLaunch G{};
-    G.B = B;
-    G.C = C;
-    G.batch = batch;
-    G.L = seqlen;
-    G.d_inner = d_inner;
-    G.d_state = d_state;
-    G.waves = waves;
-    G.dtype = dt;
-    G.bc_staged = reinterpret_cast<float *>(ws + off[0]);
-    G.staged_rows = n_seg * S;
-    G.relay_parts = 1;
-    if (launch_stage_bc(G, st) != hipSuccess)
-        return MAMBA_ERR_HIP;
 
     BwdLaunch P{};
     P.u = u;
@@ -833,12 +815,10 @@ mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, 
     P.dD = dD;
     P.dbias = d_delta_bias;
     P.dh0 = dh0;
-    P.bc_staged = G.bc_staged;
-    P.staged_rows = G.staged_rows;
-    P.ckpt = reinterpret_cast<float *>(ws + off[1]);
-    P.dbc_part = reinterpret_cast<float *>(ws + off[2]);
-    P.dA_part = reinterpret_cast<float *>(ws + off[3]);
-    P.dDb_part = reinterpret_cast<float *>(ws + off[4]);
+    P.ckpt = reinterpret_cast<float *>(ws + off[0]);
+    P.dbc_part = reinterpret_cast<float *>(ws + off[1]);
+    P.dA_part = reinterpret_cast<float *>(ws + off[2]);
+    P.dDb_part = reinterpret_cast<float *>(ws + off[3]);
     P.batch = batch;
     P.L = seqlen;
     P.d_inner = d_inner;

@@ -14,15 +14,15 @@
 // backward pass rather than stored for every step.
 //
 // Work decomposition: the forward scalar kernel's -- one block per (batch row, 64-channel
-// tile), lane = channel, wave g owns state indices [g*NQ, (g+1)*NQ), B and C staged as
-// fp32 and read through SGPRs.  Each block
+// tile), lane = channel, wave g owns state indices [g*NQ, (g+1)*NQ).  Each block
 //   1. runs the recurrence forward once and stores the state entering every segment of
 //      S steps (a checkpoint per lane and state index, in the workspace);
 //   2. walks the segments backwards: recomputes the segment's states and decay factors
 //      into registers from its checkpoint, then runs the adjoint recurrence mu backwards
 //      through it.
 // Per (step, channel) quantities (Delta, Delta*u, ds) are computed once and shared
-// through LDS; the per-wave partial sums over state indices (readout, sum mu B, sum
+// through LDS, as are B and C (a wave loads its segment's values with one load per lane,
+// a segment ahead, and reads them back as broadcasts); the per-wave partial sums over state indices (readout, sum mu B, sum
 // A mu Abar h) are summed across waves through LDS in a fixed order.  dB and dC need sums
 // over the block's 64 channels (the lanes): each wave reduces its values of 8 steps with a
 // transposed butterfly (every exchange halves the values a lane holds, so 2*NQ*8 sums
@@ -37,14 +37,11 @@
 namespace mambascan {
 namespace {
 
-typedef const __attribute__((address_space(4))) float *cfloat_ptr;
-
 constexpr int kRH = 8;  // reverse steps per cross-wave exchange (and per lane reduction)
 constexpr int kTCF = 8; // steps per chunk of the checkpointing forward pass
 
 struct BwdArgs {
-    const void *u, *delta, *z, *dy;
-    const float *bcp; // staged B/C: [b][wave][t][B(NQ), C(NQ)], Lp rows
+    const void *u, *delta, *z, *dy, *B, *C;
     const float *A, *D, *bias, *h0, *dh_last;
     void *du, *ddelta, *dz;
     float *dh0;
@@ -52,7 +49,7 @@ struct BwdArgs {
     float *dbc_part; // [(block * L + t) * 2N + {n, N + n}]: this tile's dB, dC
     float *dA_part;  // [b][d][n]
     float *dDb_part; // [b][d][2]: dD, dbias of one batch row
-    int64_t L, Lp;
+    int64_t L;
     int32_t Dn, batch, n_seg;
 };
 
@@ -101,7 +98,7 @@ __global__ void __launch_bounds__(64 * NW)
 scan_bwd_kernel(BwdArgs p)
 {
     constexpr int NQ = N / NW;     // state indices per lane
-    constexpr int BCW = 2 * NQ;    // staged B then C per step; also dB/dC values per step
+    constexpr int BCW = 2 * NQ;    // B then C per step; also dB/dC values per step
     constexpr int RH = kRH;
     constexpr int NH = S / RH;     // reverse parts per segment
     constexpr int KP = S / NW;     // a segment's (step, channel) items per lane
@@ -110,9 +107,11 @@ scan_bwd_kernel(BwdArgs p)
     static_assert(NQ >= 1 && N % NW == 0 && S % RH == 0 && RH % NW == 0 && kTCF % NW == 0 &&
                   S % kTCF == 0, "bad variant");
     static_assert(BCW == 2 || BCW == 4 || BCW == 8, "butterfly handles 2 to 8 values per step");
+    static_assert(S * BCW <= 64 && kTCF * NQ <= 64, "one lane load per B/C value");
 
     __shared__ float4 s_in[S][64];       // Delta, Delta*u, ds per (step, channel)
     __shared__ float s_p[3][RH][NW][64]; // readout, sum mu B, sum A mu Abar h per wave
+    __shared__ float s_bc[NW][S * BCW];  // this segment's B, C per wave: [step][B(NQ), C(NQ)]
 
     const int lane = threadIdx.x & 63;
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -143,14 +142,31 @@ scan_bwd_kernel(BwdArgs p)
     const T *db = (const T *)p.delta + row0 + dc;
     const T *zb = GATED ? (const T *)p.z + row0 + dc : nullptr;
     const T *gb = (const T *)p.dy + row0 + dc;
-    const float *bc_row = p.bcp + ((int64_t)b * NW + g) * p.Lp * BCW;
     float *ck = p.ckpt + (int64_t)bid * p.n_seg * N * 64;
+
+    // One B/C value per lane: for a segment, lane l < S*BCW holds step l / BCW, value
+    // l % BCW (B for the first NQ, then C) of this wave's state indices; for a forward
+    // chunk, lane l < kTCF*NQ holds B of step l / NQ, state n0 + l % NQ.
+    const int r_step = lane / BCW, r_i = lane % BCW;
+    const T *r_src = (const T *)(r_i < NQ ? p.B : p.C) + (int64_t)b * L * N + n0 + r_i % NQ;
+    auto bc_fetch = [&](int64_t t0) -> float {
+        const int64_t t = t0 + r_step;
+        return (lane < S * BCW && t < L) ? load_val(r_src, t * N) : 0.0f;
+    };
+    const int f_step = lane / NQ, f_q = lane % NQ;
+    const T *f_src = (const T *)p.B + (int64_t)b * L * N + n0 + f_q;
+    auto b_fetch = [&](int64_t t0) -> float {
+        return lane < kTCF * NQ ? load_val(f_src, (t0 + f_step) * N) : 0.0f;
+    };
 
     // ---- 1. forward pass: checkpoints at the start of segments 1 .. n_seg-1 ----
     {
-        float2 *s_f = reinterpret_cast<float2 *>(&s_in[0][0]); // [2][kTCF][64]
-        const int64_t LF = (int64_t)(p.n_seg - 1) * S;          // whole segments only
+        // (Delta, Delta*u) and B of two chunks, alternating; aliases s_p
+        float2 *s_f = reinterpret_cast<float2 *>(&s_p[0][0][0][0]);   // [2][kTCF][64]
+        float *s_fb = reinterpret_cast<float *>(&s_p[2][0][0][0]);    // [2][NW][kTCF * NQ]
+        const int64_t LF = (int64_t)(p.n_seg - 1) * S;                 // whole segments only
         T fu[KF], fd[KF];
+        float fb = 0.0f;
         auto ffetch = [&](int64_t t0) {
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
@@ -158,6 +174,7 @@ scan_bwd_kernel(BwdArgs p)
                 fu[k] = ub[t * Dn];
                 fd[k] = db[t * Dn];
             }
+            fb = b_fetch(t0);
         };
         if (LF > 0)
             ffetch(0);
@@ -169,22 +186,18 @@ scan_bwd_kernel(BwdArgs p)
                 const float dl = softplus_f(widen(fd[k]) + bias_d);
                 s_f[(par * kTCF + tl) * 64 + lane] = make_float2(dl, dl * widen(fu[k]));
             }
+            if (lane < kTCF * NQ)
+                s_fb[(par * NW + g) * (kTCF * NQ) + lane] = fb;
             if (t0 + kTCF < LF)
                 ffetch(t0 + kTCF);
-            float bs[kTCF][NQ];
-            const cfloat_ptr q = (cfloat_ptr)(bc_row + t0 * BCW);
-#pragma unroll
-            for (int tl = 0; tl < kTCF; ++tl)
-#pragma unroll
-                for (int i = 0; i < NQ; ++i)
-                    bs[tl][i] = q[tl * BCW + i];
             __syncthreads();
+            const float *bs = s_fb + (par * NW + g) * (kTCF * NQ);
 #pragma unroll
             for (int tl = 0; tl < kTCF; ++tl) {
                 const float2 w = s_f[(par * kTCF + tl) * 64 + lane];
 #pragma unroll
                 for (int i = 0; i < NQ; ++i)
-                    h[i] = __builtin_fmaf(decay_exp2(w.x, a2[i]), h[i], w.y * bs[tl][i]);
+                    h[i] = __builtin_fmaf(decay_exp2(w.x, a2[i]), h[i], w.y * bs[tl * NQ + i]);
             }
             if ((t0 + kTCF) % S == 0) {
                 const int64_t seg = (t0 + kTCF) / S;
@@ -194,7 +207,7 @@ scan_bwd_kernel(BwdArgs p)
             }
             par ^= 1;
         }
-        __syncthreads(); // s_f aliases s_in
+        __syncthreads(); // s_f and s_fb alias s_p
     }
 
     // ---- 2. segments in reverse ----
@@ -206,7 +219,9 @@ scan_bwd_kernel(BwdArgs p)
     }
     float dD_acc = 0.0f, db_acc = 0.0f;
 
+    // inputs of the next segment to process, loaded one segment ahead
     T ru[KP], rd[KP], rz[KP], rg[KP];
+    float bcv = 0.0f, hnext[NQ];
     auto rfetch = [&](int seg) {
         const int64_t t0 = (int64_t)seg * S;
 #pragma unroll
@@ -222,14 +237,19 @@ scan_bwd_kernel(BwdArgs p)
                     rg[k] = gb[t * Dn];
             }
         }
+        bcv = bc_fetch(t0);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            hnext[q] = seg == 0 ? hstart[q] : ck[((int64_t)seg * N + n0 + q) * 64 + lane];
     };
     if (p.n_seg > 0)
         rfetch(p.n_seg - 1);
 
-    float bcs[RH][BCW];
-    for (int seg = p.n_seg - 1; seg >= 0; --seg) {
+    // One segment: t0 its first step; PARTIAL when it has fewer than S steps (the last).
+    auto segment = [&](auto PARTIAL_, int seg) {
+        constexpr bool PARTIAL = decltype(PARTIAL_)::value;
         const int64_t t0 = (int64_t)seg * S;
-        const int nt = (int)min((int64_t)S, L - t0);
+        const int nt = PARTIAL ? (int)(L - t0) : S;
 
         // prologue: per (step, channel) values, kept by this lane for the epilogue
         float e_u[KP], e_dl[KP], e_sig[KP], e_ds[KP], e_dyg[KP];
@@ -255,22 +275,15 @@ scan_bwd_kernel(BwdArgs p)
             e_dyg[k] = dyv * dgate;
             s_in[tl][lane] = make_float4(dl, dl * uu, ds, 0.0f);
         }
-        if (seg > 0)
-            rfetch(seg - 1);
+        if (lane < S * BCW)
+            s_bc[g][lane] = bcv;
         float hin[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
-            hin[q] = seg == 0 ? hstart[q] : ck[((int64_t)seg * N + n0 + q) * 64 + lane];
+            hin[q] = hnext[q];
+        if (seg > 0)
+            rfetch(seg - 1);
         __syncthreads();
-
-        auto load_bc = [&](int part) {
-            const cfloat_ptr q = (cfloat_ptr)(bc_row + (t0 + part * RH) * BCW);
-#pragma unroll
-            for (int tl = 0; tl < RH; ++tl)
-#pragma unroll
-                for (int i = 0; i < BCW; ++i)
-                    bcs[tl][i] = q[tl * BCW + i];
-        };
 
         // recompute the segment's states and decay factors
         float hs[S][NQ], ab[S][NQ];
@@ -280,30 +293,26 @@ scan_bwd_kernel(BwdArgs p)
             for (int q = 0; q < NQ; ++q)
                 hc[q] = hin[q];
 #pragma unroll
-            for (int part = 0; part < NH; ++part) {
-                load_bc(part);
+            for (int T_ = 0; T_ < S; ++T_) {
+                if (!PARTIAL || T_ < nt) {
+                    const float4 w = s_in[T_][lane];
 #pragma unroll
-                for (int tl = 0; tl < RH; ++tl) {
-                    const int T_ = part * RH + tl;
-                    if (T_ < nt) {
-                        const float4 w = s_in[T_][lane];
-#pragma unroll
-                        for (int q = 0; q < NQ; ++q) {
-                            const float a = decay_exp2(w.x, a2[q]);
-                            hc[q] = __builtin_fmaf(a, hc[q], w.y * bcs[tl][q]);
-                            ab[T_][q] = a;
-                            hs[T_][q] = hc[q];
-                        }
+                    for (int q = 0; q < NQ; ++q) {
+                        const float a = decay_exp2(w.x, a2[q]);
+                        hc[q] = __builtin_fmaf(a, hc[q], w.y * s_bc[g][T_ * BCW + q]);
+                        ab[T_][q] = a;
+                        hs[T_][q] = hc[q];
                     }
                 }
             }
         }
 
+        // (re-read Delta, B, C from LDS below rather than keeping the recompute's copies live)
+        asm volatile("" ::: "memory");
+
         // adjoint recurrence, last part first
 #pragma unroll
         for (int part = NH - 1; part >= 0; --part) {
-            if (part != NH - 1)
-                load_bc(part);
             float pend[BCW], r1[4][BCW], r2[2][BCW], r3[BCW];
 #pragma unroll
             for (int tl = RH - 1; tl >= 0; --tl) {
@@ -313,14 +322,15 @@ scan_bwd_kernel(BwdArgs p)
 #pragma unroll
                 for (int i = 0; i < BCW; ++i)
                     xv[i] = 0.0f;
-                if (T_ < nt) {
+                if (!PARTIAL || T_ < nt) {
                     const float4 w = s_in[T_][lane]; // Delta, Delta*u, ds
 #pragma unroll
                     for (int q = 0; q < NQ; ++q) {
-                        const float cq = bcs[tl][NQ + q];
+                        const float bq = s_bc[g][T_ * BCW + q];
+                        const float cq = s_bc[g][T_ * BCW + NQ + q];
                         yp = __builtin_fmaf(cq, hs[T_][q], yp);
                         mu[q] = __builtin_fmaf(w.z, cq, mu[q]); // mu_t
-                        p1 = __builtin_fmaf(mu[q], bcs[tl][q], p1);
+                        p1 = __builtin_fmaf(mu[q], bq, p1);
                         xv[q] = mu[q] * w.y;                    // dB
                         xv[NQ + q] = w.z * hs[T_][q];           // dC
                         const float hp = T_ == 0 ? hin[q] : hs[T_ > 0 ? T_ - 1 : 0][q];
@@ -393,7 +403,7 @@ scan_bwd_kernel(BwdArgs p)
                     writer = true;
                 }
                 const int64_t t = t0 + part * RH + tlo;
-                if (writer && t < L) {
+                if (writer && (!PARTIAL || t < L)) {
                     const int kind = j / NQ, q = j % NQ;
                     p.dbc_part[((int64_t)bid * L + t) * (2 * N) + kind * N + n0 + q] = v;
                 }
@@ -412,7 +422,7 @@ scan_bwd_kernel(BwdArgs p)
                     P1 += s_p[1][lt][w][lane];
                     P2 += s_p[2][lt][w][lane];
                 }
-                if (tl < nt) {
+                if (!PARTIAL || tl < nt) {
                     const int64_t t = t0 + tl;
                     const float ddt = __builtin_fmaf(e_u[k], P1, P2);
                     const float dd = ddt * e_sig[k];
@@ -431,7 +441,15 @@ scan_bwd_kernel(BwdArgs p)
             if (part > 0)
                 __syncthreads(); // the next part rewrites s_p
         }
+    };
+
+    int seg = p.n_seg - 1;
+    if (seg >= 0 && L - (int64_t)seg * S < S) {
+        segment(std::true_type{}, seg);
+        --seg;
     }
+    for (; seg >= 0; --seg)
+        segment(std::false_type{}, seg);
 
     // ---- 3. per-block results ----
     if (dvalid) {
@@ -513,9 +531,9 @@ bwd_reduce_params_kernel(const float *__restrict__ dA_part, const float *__restr
 
 // (d_state, waves, segment length)
 #define MAMBA_BWD_VARIANTS(X) \
-    X(4, 4, 16)               \
-    X(8, 8, 16)               \
-    X(16, 8, 16)              \
+    X(4, 4, 8)                \
+    X(8, 8, 8)                \
+    X(16, 8, 8)               \
     X(32, 8, 8)
 
 template <typename T, int N, int NW, int S>
@@ -526,7 +544,8 @@ hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
     a.delta = q.delta;
     a.z = q.z;
     a.dy = q.dy;
-    a.bcp = q.bc_staged;
+    a.B = q.B;
+    a.C = q.C;
     a.A = q.A;
     a.D = q.D;
     a.bias = q.bias;
@@ -541,7 +560,6 @@ hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
     a.dA_part = q.dA_part;
     a.dDb_part = q.dDb_part;
     a.L = q.L;
-    a.Lp = q.staged_rows;
     a.Dn = (int32_t)q.d_inner;
     a.batch = (int32_t)q.batch;
     a.n_seg = (int32_t)((q.L + S - 1) / S);

@@ -87,8 +87,6 @@ struct BwdLaunch {
     const float *A, *D, *bias, *h0, *dh_last;
     void *du, *ddelta, *dz, *dB, *dC; // activation dtype
     float *dA, *dD, *dbias, *dh0;
-    float *bc_staged;   // staged B/C (the scalar forward's layout), staged_rows rows
-    int64_t staged_rows;
     float *ckpt;        // [block][segment][n][lane]
     float *dbc_part;    // [block][t][2N]
     float *dA_part;     // [b][d][n]
