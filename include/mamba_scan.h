@@ -321,6 +321,11 @@ MAMBA_API mamba_status_t mamba_state_update_ex(float *h, const void *u, const vo
 MAMBA_API size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
                                                int64_t d_state);
 
+/* The same for explicit options (see mamba_scan_bwd_ex; opts may be NULL). */
+MAMBA_API size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t seqlen,
+                                                  int64_t d_inner, int64_t d_state,
+                                                  const mamba_scan_opts_t *opts);
+
 MAMBA_API mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A,
                                         const void *B, const void *C, const float *D,
                                         const void *z, const float *delta_bias,
@@ -330,6 +335,25 @@ MAMBA_API mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const 
                                         int64_t batch, int64_t seqlen, int64_t d_inner,
                                         int64_t d_state, mamba_dtype_t dtype, void *workspace,
                                         size_t workspace_bytes, void *stream);
+
+/* mamba_scan_bwd with explicit options (opts NULL = auto).  Only n_spans may be set:
+ * the sequence is split into that many spans (1..64) scanned in parallel and joined by
+ * carry passes for the state (forward) and for its gradient (backward in time); the
+ * automatic choice splits when the (batch row, 64-channel tile) units cannot fill the
+ * device, and depends on the current device's compute-unit count.  Any other nonzero
+ * field returns MAMBA_ERR_UNSUPPORTED.  Results agree across span counts up to float32
+ * rounding. */
+MAMBA_API mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *A,
+                                           const void *B, const void *C, const float *D,
+                                           const void *z, const float *delta_bias,
+                                           const float *h0, const void *dy,
+                                           const float *dh_last, void *du, void *ddelta,
+                                           float *dA, void *dB, void *dC, float *dD, void *dz,
+                                           float *d_delta_bias, float *dh0, int64_t batch,
+                                           int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                           mamba_dtype_t dtype, void *workspace,
+                                           size_t workspace_bytes,
+                                           const mamba_scan_opts_t *opts, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 MAMBA_API const char *mamba_status_string(mamba_status_t status);

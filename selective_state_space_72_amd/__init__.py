@@ -37,6 +37,7 @@ EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_scan_fwd_workspace_size_ex", "mamba_scan_fwd", "mamba_scan_fwd_ex",
            "mamba_state_update", "mamba_state_update_ex", "mamba_conv1d_silu_fwd",
            "mamba_conv1d_silu_update", "mamba_scan_bwd_workspace_size", "mamba_scan_bwd",
+           "mamba_scan_bwd_workspace_size_ex", "mamba_scan_bwd_ex",
            "mamba_status_string")
 
 
@@ -103,6 +104,12 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mamba_scan_bwd.restype = ctypes.c_int
     lib.mamba_scan_bwd.argtypes = [_vp] * 20 + [_i64] * 4 + [ctypes.c_int, _vp, ctypes.c_size_t,
                                                               _vp]
+    lib.mamba_scan_bwd_workspace_size_ex.restype = ctypes.c_size_t
+    lib.mamba_scan_bwd_workspace_size_ex.argtypes = [_i64] * 4 + [ctypes.POINTER(ScanOpts)]
+    lib.mamba_scan_bwd_ex.restype = ctypes.c_int
+    lib.mamba_scan_bwd_ex.argtypes = ([_vp] * 20 + [_i64] * 4 +
+                                      [ctypes.c_int, _vp, ctypes.c_size_t,
+                                       ctypes.POINTER(ScanOpts), _vp])
     lib.mamba_status_string.restype = ctypes.c_char_p
     lib.mamba_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -330,9 +337,11 @@ def mamba_conv1d_silu_update(state, x, w, conv_bias=None, *, out=None):
     return u
 
 
-def mamba_scan_bwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state: int) -> int:
+def mamba_scan_bwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state: int,
+                                  n_spans: int = 0) -> int:
     lib = load_library()
-    n = lib.mamba_scan_bwd_workspace_size(batch, seqlen, d_inner, d_state)
+    o = ScanOpts(0, 0, int(n_spans), 0, 0, 0)
+    n = lib.mamba_scan_bwd_workspace_size_ex(batch, seqlen, d_inner, d_state, ctypes.byref(o))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes for mamba_scan_bwd")
     return int(n)
@@ -342,13 +351,14 @@ GRAD_NAMES = ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0")
 
 
 def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=None,
-                   dh_last=None, *, want=GRAD_NAMES, out=None, workspace=None) -> dict:
+                   dh_last=None, *, want=GRAD_NAMES, out=None, workspace=None,
+                   n_spans: int = 0) -> dict:
     """Gradients of the selective scan (Euler); see include/mamba_scan.h.
 
     Returns a dict with the names of ``want`` (a subset of GRAD_NAMES; du and ddelta are
     always computed): du, ddelta, dz, dB, dC in the activations' dtype, dA, dD, dbias,
     dh0 in float32.  dz is None without a gate.  ``out`` may map names to preallocated
-    tensors.
+    tensors.  n_spans: sequence split (0 = automatic; see mamba_scan_bwd_ex).
     """
     torch = _torch()
     lib = load_library()
@@ -393,7 +403,9 @@ def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=No
             t = torch.empty(shape, dtype=dt, device=dev)
         res[name] = t
         ptrs[name] = _ptr(t, name, shape, dt, dev)
-    need = lib.mamba_scan_bwd_workspace_size(batch, seqlen, d_inner, d_state)
+    opts = ScanOpts(0, 0, int(n_spans), 0, 0, 0)
+    need = lib.mamba_scan_bwd_workspace_size_ex(batch, seqlen, d_inner, d_state,
+                                                ctypes.byref(opts))
     if need == ctypes.c_size_t(-1).value:
         raise MambaError(4, "mamba_scan_bwd_workspace_size")
     ws = workspace
@@ -401,10 +413,11 @@ def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=No
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     p_ws = ws.data_ptr() if ws is not None and need > 0 else None
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    st = lib.mamba_scan_bwd(p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_dy, p_dhl,
-                            ptrs["du"], ptrs["ddelta"], ptrs["dA"], ptrs["dB"], ptrs["dC"],
-                            ptrs["dD"], ptrs["dz"], ptrs["dbias"], ptrs["dh0"],
-                            batch, seqlen, d_inner, d_state, code, p_ws, ws_bytes, _stream(dev))
+    st = lib.mamba_scan_bwd_ex(p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_dy,
+                               p_dhl, ptrs["du"], ptrs["ddelta"], ptrs["dA"], ptrs["dB"],
+                               ptrs["dC"], ptrs["dD"], ptrs["dz"], ptrs["dbias"], ptrs["dh0"],
+                               batch, seqlen, d_inner, d_state, code, p_ws, ws_bytes,
+                               ctypes.byref(opts), _stream(dev))
     if st != 0:
         raise MambaError(st, "mamba_scan_bwd")
     return {k: v for k, v in res.items() if k in ("du", "ddelta") or k in want}

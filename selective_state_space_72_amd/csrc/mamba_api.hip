@@ -247,30 +247,95 @@ size_t workspace_bytes_for(int64_t batch, int64_t seqlen, int64_t d_inner, int64
     return n;
 }
 
-// Backward workspace: [segment checkpoints][dB/dC tile partials][dA partials]
-// [dD, dbias partials], each region 256-byte aligned.  Offsets in bytes; total in off[4].
-bool bwd_layout(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                size_t off[5], int *seg_len)
+// Backward launch plan: the compiled variant's segment length, and the sequence split.
+// Units of (batch row, 64-channel tile) run two blocks per compute unit.  The split costs
+// two summary passes over the whole sequence (about a third more work) whatever the span
+// count, so it is used only when the units cannot even give every compute unit one block;
+// then the sequence is cut into enough spans (a power of two, at most 64, each at least 64
+// steps) for about four full rounds of blocks.
+struct BwdPlan {
+    int seg_len;
+    int n_spans;
+    int64_t span_len;
+    int fwd_waves, fwd_chunk; // forward span-summary pass (scalar family)
+};
+
+mamba_status_t bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                        const mamba_scan_opts_t *opts, BwdPlan *plan)
 {
-    int waves = 0, S = 0;
-    if (!bwd_variant(d_state, &waves, &S))
-        return false;
-    *seg_len = S;
+    BwdPlan p{};
+    int waves = 0;
+    if (!bwd_variant(d_state, &waves, &p.seg_len))
+        return MAMBA_ERR_UNSUPPORTED;
+    if (opts && (opts->chunk_len || opts->waves || opts->kernel || opts->relay ||
+                 opts->discretization != MAMBA_DISC_EULER))
+        return MAMBA_ERR_UNSUPPORTED;
+    const bool fixed = opts && opts->n_spans;
+    if (fixed && (opts->n_spans < 1 || opts->n_spans > 64))
+        return MAMBA_ERR_UNSUPPORTED;
+    const int S = p.seg_len;
+    int n = 1;
+    if (fixed) {
+        n = opts->n_spans;
+    } else if (seqlen >= 128) {
+        const int64_t units = batch * ((d_inner + 63) / 64);
+        const int64_t cus = cu_count();
+        if (units < cus) {
+            const int64_t want = cus * 2 /*blocks each*/ * 4 /*rounds*/;
+            while (units * n < want && n < 64 && seqlen / (2 * n) >= 64)
+                n *= 2;
+        }
+    }
+    int64_t len = seqlen > 0 ? (seqlen + n - 1) / n : S;
+    len = (len + S - 1) / S * S;
+    if (len < S)
+        len = S;
+    n = seqlen > 0 ? (int)((seqlen + len - 1) / len) : 1;
+    p.fwd_waves = scalar_default_waves(d_state);
+    p.fwd_chunk = scalar_default_chunk(d_state);
+    if (n > 1 && (!scalar_variant_supported(d_state, p.fwd_waves, p.fwd_chunk) ||
+                  len % p.fwd_chunk != 0 || !scalar_span_ok(len, d_inner))) {
+        if (fixed)
+            return MAMBA_ERR_UNSUPPORTED;
+        n = 1;
+        len = (seqlen + S - 1) / S * S;
+    }
+    p.n_spans = n;
+    p.span_len = len;
+    *plan = p;
+    return MAMBA_OK;
+}
+
+// Backward workspace: [segment checkpoints][dB/dC tile partials][dA partials]
+// [dD, dbias partials] and, with spans, [staged B/C][forward span decay][forward span
+// local state][state entering each span][adjoint decay][adjoint local][adjoint entering
+// each span]; each region 256-byte aligned.  Offsets in bytes; off[11] is the total.
+void bwd_layout(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                const BwdPlan &p, size_t off[12])
+{
     auto al = [](size_t n) { return (n + 255) / 256 * 256; };
-    const size_t n_seg = (size_t)((seqlen + S - 1) / S);
+    const size_t S = (size_t)p.seg_len;
+    const size_t n_seg = (size_t)((seqlen + p.seg_len - 1) / p.seg_len);
     const size_t units = (size_t)batch * (size_t)((d_inner + 63) / 64);
     const size_t N = (size_t)d_state, f = sizeof(float);
-    size_t sz[4];
+    const size_t sp = (size_t)p.n_spans;
+    const size_t bdn = (size_t)batch * (size_t)d_inner * N;
+    size_t sz[11] = {};
     sz[0] = al(units * n_seg * N * 64 * f);
     sz[1] = al(units * (size_t)seqlen * 2 * N * f);
-    sz[2] = al((size_t)batch * (size_t)d_inner * N * f);
-    sz[3] = al((size_t)batch * (size_t)d_inner * 2 * f);
+    sz[2] = al(sp * bdn * f);
+    sz[3] = al(sp * (size_t)batch * (size_t)d_inner * 2 * f);
+    if (p.n_spans > 1) {
+        sz[4] = al((size_t)batch * ((size_t)seqlen + (size_t)p.fwd_chunk) * 2 * N * f);
+        for (int i = 5; i < 11; ++i)
+            sz[i] = al(sp * bdn * f);
+    }
+    (void)S;
     off[0] = 0;
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 11; ++i)
         off[i + 1] = off[i] + sz[i];
     if (seqlen == 0)
-        off[4] = 0;
-    return true;
+        off[11] = 0;
 }
 
 mamba_status_t hip_status(hipError_t e) { return e == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP; }
@@ -677,19 +742,26 @@ mamba_status_t mamba_conv1d_silu_update(void *state, const void *x, const float 
 }
 
 
-size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
-                                     int64_t d_state)
+size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                        int64_t d_state, const mamba_scan_opts_t *opts)
 {
     int64_t t;
     if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 ||
         !mul_ok(batch, seqlen, &t) || !mul_ok(t, d_inner, &t) || !mul_ok(t, d_state, &t) ||
         !mul_ok(t, 8, &t))
         return (size_t)-1;
-    size_t off[5];
-    int S = 0;
-    if (!bwd_layout(batch, seqlen, d_inner, d_state, off, &S))
+    BwdPlan plan;
+    if (bwd_plan(batch, seqlen, d_inner, d_state, opts, &plan) != MAMBA_OK)
         return (size_t)-1;
-    return off[4];
+    size_t off[12];
+    bwd_layout(batch, seqlen, d_inner, d_state, plan, off);
+    return off[11];
+}
+
+size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                     int64_t d_state)
+{
+    return mamba_scan_bwd_workspace_size_ex(batch, seqlen, d_inner, d_state, nullptr);
 }
 
 mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, const void *B,
@@ -701,14 +773,31 @@ mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, 
                               int64_t d_state, mamba_dtype_t dtype, void *workspace,
                               size_t workspace_bytes, void *stream)
 {
+    return mamba_scan_bwd_ex(u, delta, A, B, C, D, z, delta_bias, h0, dy, dh_last, du, ddelta,
+                             dA, dB, dC, dD, dz, d_delta_bias, dh0, batch, seqlen, d_inner,
+                             d_state, dtype, workspace, workspace_bytes, nullptr, stream);
+}
+
+mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *A,
+                                 const void *B, const void *C, const float *D, const void *z,
+                                 const float *delta_bias, const float *h0, const void *dy,
+                                 const float *dh_last, void *du, void *ddelta, float *dA,
+                                 void *dB, void *dC, float *dD, void *dz, float *d_delta_bias,
+                                 float *dh0, int64_t batch, int64_t seqlen, int64_t d_inner,
+                                 int64_t d_state, mamba_dtype_t dtype, void *workspace,
+                                 size_t workspace_bytes, const mamba_scan_opts_t *opts,
+                                 void *stream)
+{
     // ---- sizes and dtype ----
     if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0)
         return MAMBA_ERR_BAD_SHAPE;
     if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
         return MAMBA_ERR_BAD_DTYPE;
-    int waves = 0, S = 0;
-    if (!bwd_variant(d_state, &waves, &S))
-        return MAMBA_ERR_UNSUPPORTED;
+    BwdPlan plan;
+    const mamba_status_t ps = bwd_plan(batch, seqlen, d_inner, d_state, opts, &plan);
+    if (ps != MAMBA_OK)
+        return ps;
+    const int S = plan.seg_len;
     const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
     int64_t bld, bln, bdn, dn, t;
     if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, d_inner, &bld) || !mul_ok(bld, es, &t) ||
@@ -716,7 +805,7 @@ mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, 
         !mul_ok(bld, d_state, &t) || !mul_ok(t, 8, &t) || !mul_ok(batch, d_inner, &t) ||
         !mul_ok(t, d_state, &bdn) || !mul_ok(bdn, 4, &t) || !mul_ok(d_inner, d_state, &dn) ||
         !mul_ok(dn, 4, &t) || d_inner > INT32_MAX || batch > INT32_MAX ||
-        (seqlen + S - 1) / S > INT32_MAX)
+        (seqlen + S - 1) / S > INT32_MAX || plan.span_len > INT32_MAX)
         return MAMBA_ERR_BAD_SHAPE;
     if (batch == 0 || d_inner == 0)
         return MAMBA_OK;
@@ -740,9 +829,9 @@ mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, 
             return MAMBA_ERR_MISALIGNED;
 
     // ---- workspace ----
-    size_t off[5];
-    (void)bwd_layout(batch, seqlen, d_inner, d_state, off, &S);
-    const size_t need = off[4];
+    size_t off[12];
+    bwd_layout(batch, seqlen, d_inner, d_state, plan, off);
+    const size_t need = off[11];
     if (need > 0 && (!workspace || workspace_bytes < need))
         return MAMBA_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 4))
@@ -793,8 +882,53 @@ mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, 
 
     char *ws = static_cast<char *>(workspace);
     const DType dt = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+    auto region = [&](int i) { return reinterpret_cast<float *>(ws + off[i]); };
 
     BwdLaunch P{};
+    if (plan.n_spans > 1) {
+        // forward span summaries (the forward's span pass), then the state entering each span
+        ScanLaunch E{};
+        E.u = u;
+        E.delta = delta;
+        E.B = B;
+        E.C = C;
+        E.A = A;
+        E.D = D;
+        E.bias = delta_bias;
+        E.ws_decay = region(5);
+        E.ws_hloc = region(6);
+        E.batch = batch;
+        E.L = seqlen;
+        E.d_inner = d_inner;
+        E.d_state = d_state;
+        E.span_len = plan.span_len;
+        E.n_spans = plan.n_spans;
+        E.first_span = 0;
+        E.launch_spans = plan.n_spans - 1;
+        E.waves = plan.fwd_waves;
+        E.chunk = plan.fwd_chunk;
+        E.dtype = dt;
+        E.bc_staged = region(4);
+        E.staged_rows = seqlen + plan.fwd_chunk;
+        E.relay_parts = 1;
+        if (launch_stage_bc(E, st) != hipSuccess || launch_scalar_end(E, st) != hipSuccess)
+            return MAMBA_ERR_HIP;
+        CarryLaunch K{};
+        K.ws_decay = region(5);
+        K.ws_hloc = region(6);
+        K.h0 = h0;
+        K.h_in = region(7);
+        K.columns = bdn;
+        K.n_spans = plan.n_spans;
+        if (launch_carry(K, st) != hipSuccess)
+            return MAMBA_ERR_HIP;
+        P.h_in = region(7);
+        P.mu_dec = region(8);
+        P.mu_loc = region(9);
+        P.mu_in = region(10);
+    }
+    P.n_spans = plan.n_spans;
+    P.span_len = plan.span_len;
     P.u = u;
     P.delta = delta;
     P.z = z;
@@ -815,10 +949,10 @@ mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, 
     P.dD = dD;
     P.dbias = d_delta_bias;
     P.dh0 = dh0;
-    P.ckpt = reinterpret_cast<float *>(ws + off[0]);
-    P.dbc_part = reinterpret_cast<float *>(ws + off[1]);
-    P.dA_part = reinterpret_cast<float *>(ws + off[2]);
-    P.dDb_part = reinterpret_cast<float *>(ws + off[3]);
+    P.ckpt = region(0);
+    P.dbc_part = region(1);
+    P.dA_part = region(2);
+    P.dDb_part = region(3);
     P.batch = batch;
     P.L = seqlen;
     P.d_inner = d_inner;

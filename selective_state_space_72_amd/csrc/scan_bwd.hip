@@ -47,10 +47,14 @@ struct BwdArgs {
     float *dh0;
     float *ckpt;     // [block][segment][n][lane]
     float *dbc_part; // [(block * L + t) * 2N + {n, N + n}]: this tile's dB, dC
-    float *dA_part;  // [b][d][n]
-    float *dDb_part; // [b][d][2]: dD, dbias of one batch row
+    float *dA_part;  // [span][b][d][n]
+    float *dDb_part; // [span][b][d][2]: dD, dbias of one (span, batch row)
+    const float *h_in;  // [span][b][d][n]: state entering each span (spans > 0), or NULL
+    const float *mu_in; // [span][b][d][n]: adjoint entering each span from its end, or NULL
+                        // (then dh_last, a single span)
     int64_t L;
-    int32_t Dn, batch, n_seg;
+    int32_t Dn, batch, n_seg; // n_seg: segments of the whole sequence
+    int32_t span_len, n_spans; // span_len: a multiple of the segment length
 };
 
 // Value of lane (lane ^ pattern) for the butterfly's partner patterns.  Lane bits 3, 2, 1
@@ -115,9 +119,12 @@ scan_bwd_kernel(BwdArgs p)
 
     const int lane = threadIdx.x & 63;
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int bid = blockIdx.x;             // = tile * batch + b
-    const int b = bid % p.batch;
-    const int tile = bid / p.batch;
+    const int tiles = (p.Dn + 63) / 64;
+    const int units = tiles * p.batch;
+    const int unit = blockIdx.x % units;    // = tile * batch + b
+    const int span = blockIdx.x / units;
+    const int b = unit % p.batch;
+    const int tile = unit / p.batch;
     const int Dn = p.Dn;
     const int d = tile * 64 + lane;
     const bool dvalid = d < Dn;
@@ -125,13 +132,24 @@ scan_bwd_kernel(BwdArgs p)
     const int n0 = g * NQ;
     const int64_t L = p.L;
 
+    // this block's steps [t_begin, t_end) = segments [seg_lo, seg_hi)
+    const int64_t t_begin = (int64_t)span * p.span_len;
+    const int64_t t_end = min(t_begin + (int64_t)p.span_len, L);
+    const int seg_lo = (int)(t_begin / S);
+    const int seg_hi = (int)((t_end + S - 1) / S);
+
     float a2[NQ], an[NQ], h[NQ], hstart[NQ];
+    const int64_t col_c = ((int64_t)b * Dn + dc) * N + n0;       // (b, dc, n0)
+    const int64_t span_col = (int64_t)span * p.batch * Dn * N;   // span offset of [span][b][d][n]
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         const float av = p.A[(int64_t)dc * N + n0 + q];
         a2[q] = av * kLog2e;
         an[q] = av;
-        h[q] = p.h0 ? p.h0[((int64_t)b * Dn + dc) * N + n0 + q] : 0.0f;
+        if (span == 0)
+            h[q] = p.h0 ? p.h0[col_c + q] : 0.0f;
+        else
+            h[q] = p.h_in[span_col + col_c + q];
         hstart[q] = h[q];
     }
     const float bias_d = p.bias ? p.bias[dc] : 0.0f;
@@ -142,7 +160,7 @@ scan_bwd_kernel(BwdArgs p)
     const T *db = (const T *)p.delta + row0 + dc;
     const T *zb = GATED ? (const T *)p.z + row0 + dc : nullptr;
     const T *gb = (const T *)p.dy + row0 + dc;
-    float *ck = p.ckpt + (int64_t)bid * p.n_seg * N * 64;
+    float *ck = p.ckpt + (int64_t)unit * p.n_seg * N * 64; // [global segment][n][lane]
 
     // One B/C value per lane: for a segment, lane l < S*BCW holds step l / BCW, value
     // l % BCW (B for the first NQ, then C) of this wave's state indices; for a forward
@@ -159,12 +177,12 @@ scan_bwd_kernel(BwdArgs p)
         return lane < kTCF * NQ ? load_val(f_src, (t0 + f_step) * N) : 0.0f;
     };
 
-    // ---- 1. forward pass: checkpoints at the start of segments 1 .. n_seg-1 ----
+    // ---- 1. forward pass: checkpoints at the start of segments seg_lo+1 .. seg_hi-1 ----
     {
         // (Delta, Delta*u) and B of two chunks, alternating; aliases s_p
         float2 *s_f = reinterpret_cast<float2 *>(&s_p[0][0][0][0]);   // [2][kTCF][64]
         float *s_fb = reinterpret_cast<float *>(&s_p[2][0][0][0]);    // [2][NW][kTCF * NQ]
-        const int64_t LF = (int64_t)(p.n_seg - 1) * S;                 // whole segments only
+        const int64_t LF = (int64_t)(seg_hi - 1) * S;                   // whole segments only
         T fu[KF], fd[KF];
         float fb = 0.0f;
         auto ffetch = [&](int64_t t0) {
@@ -176,10 +194,10 @@ scan_bwd_kernel(BwdArgs p)
             }
             fb = b_fetch(t0);
         };
-        if (LF > 0)
-            ffetch(0);
+        if (LF > t_begin)
+            ffetch(t_begin);
         int par = 0;
-        for (int64_t t0 = 0; t0 < LF; t0 += kTCF) {
+        for (int64_t t0 = t_begin; t0 < LF; t0 += kTCF) {
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
                 const int tl = g + k * NW;
@@ -214,7 +232,12 @@ scan_bwd_kernel(BwdArgs p)
     float mu[NQ], dA[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        mu[q] = (p.dh_last && dvalid) ? p.dh_last[((int64_t)b * Dn + d) * N + n0 + q] : 0.0f;
+        if (!dvalid)
+            mu[q] = 0.0f;
+        else if (p.mu_in)
+            mu[q] = p.mu_in[span_col + col_c + q];
+        else
+            mu[q] = p.dh_last ? p.dh_last[col_c + q] : 0.0f;
         dA[q] = 0.0f;
     }
     float dD_acc = 0.0f, db_acc = 0.0f;
@@ -240,10 +263,10 @@ scan_bwd_kernel(BwdArgs p)
         bcv = bc_fetch(t0);
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
-            hnext[q] = seg == 0 ? hstart[q] : ck[((int64_t)seg * N + n0 + q) * 64 + lane];
+            hnext[q] = seg == seg_lo ? hstart[q] : ck[((int64_t)seg * N + n0 + q) * 64 + lane];
     };
-    if (p.n_seg > 0)
-        rfetch(p.n_seg - 1);
+    if (seg_hi > seg_lo)
+        rfetch(seg_hi - 1);
 
     // One segment: t0 its first step; PARTIAL when it has fewer than S steps (the last).
     auto segment = [&](auto PARTIAL_, int seg) {
@@ -281,7 +304,7 @@ scan_bwd_kernel(BwdArgs p)
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
             hin[q] = hnext[q];
-        if (seg > 0)
+        if (seg > seg_lo)
             rfetch(seg - 1);
         __syncthreads();
 
@@ -405,7 +428,7 @@ scan_bwd_kernel(BwdArgs p)
                 const int64_t t = t0 + part * RH + tlo;
                 if (writer && (!PARTIAL || t < L)) {
                     const int kind = j / NQ, q = j % NQ;
-                    p.dbc_part[((int64_t)bid * L + t) * (2 * N) + kind * N + n0 + q] = v;
+                    p.dbc_part[((int64_t)unit * L + t) * (2 * N) + kind * N + n0 + q] = v;
                 }
             }
             __syncthreads();
@@ -443,22 +466,21 @@ scan_bwd_kernel(BwdArgs p)
         }
     };
 
-    int seg = p.n_seg - 1;
-    if (seg >= 0 && L - (int64_t)seg * S < S) {
+    int seg = seg_hi - 1;
+    if (seg >= seg_lo && L - (int64_t)seg * S < S) {
         segment(std::true_type{}, seg);
         --seg;
     }
-    for (; seg >= 0; --seg)
+    for (; seg >= seg_lo; --seg)
         segment(std::false_type{}, seg);
 
     // ---- 3. per-block results ----
     if (dvalid) {
-        const int64_t col = ((int64_t)b * Dn + d) * N + n0;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            p.dA_part[col + q] = dA[q];
-            if (p.dh0)
-                p.dh0[col + q] = mu[q]; // Abar_0 mu_0
+            p.dA_part[span_col + col_c + q] = dA[q];
+            if (p.dh0 && span == 0)
+                p.dh0[col_c + q] = mu[q]; // Abar_0 mu_0
         }
     }
     __syncthreads();
@@ -472,8 +494,148 @@ scan_bwd_kernel(BwdArgs p)
             sD += s_p[0][0][w][lane];
             sb += s_p[1][0][w][lane];
         }
-        p.dDb_part[((int64_t)b * Dn + d) * 2 + 0] = sD;
-        p.dDb_part[((int64_t)b * Dn + d) * 2 + 1] = sb;
+        const int64_t o = (((int64_t)span * p.batch + b) * Dn + d) * 2;
+        p.dDb_part[o + 0] = sD;
+        p.dDb_part[o + 1] = sb;
+    }
+}
+
+// Adjoint summaries of spans 1 .. n_spans-1 (a longer sequence is split into spans so
+// that more blocks share the work): over span k, the recurrence mu <- Abar_t (mu +
+// ds_t C_t) run from the span's last step to its first is affine in the mu entering at
+// the end, mu_out = dec_k mu_in + loc_k, with dec_k = exp(A sum_{t in k} Delta_t) and
+// loc_k the result for mu_in = 0.  Layout of dec and loc: [span][b][d][n].  Same block
+// shape as the main kernel; (Delta, ds) and C are exchanged through LDS per chunk.
+struct MuSumArgs {
+    const void *delta, *z, *dy, *C;
+    const float *A, *bias;
+    float *dec, *loc;
+    int64_t L;
+    int32_t Dn, batch, span_len;
+};
+
+template <typename T, int N, int NW, bool GATED>
+__global__ void __launch_bounds__(64 * NW)
+scan_bwd_musum_kernel(MuSumArgs p)
+{
+    constexpr int NQ = N / NW;
+    constexpr int KF = kTCF / NW;
+    __shared__ float2 s_m[2][kTCF][64];          // Delta, ds per (step, channel)
+    __shared__ float s_c[2][NW][kTCF * NQ];      // C of the chunk per wave
+
+    const int lane = threadIdx.x & 63;
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tiles = (p.Dn + 63) / 64;
+    const int units = tiles * p.batch;
+    const int unit = blockIdx.x % units;
+    const int span = 1 + blockIdx.x / units;    // spans 1 .. n_spans-1
+    const int b = unit % p.batch;
+    const int tile = unit / p.batch;
+    const int Dn = p.Dn;
+    const int d = tile * 64 + lane;
+    const bool dvalid = d < Dn;
+    const int dc = dvalid ? d : Dn - 1;
+    const int n0 = g * NQ;
+    const int64_t L = p.L;
+    const int64_t t_begin = (int64_t)span * p.span_len;
+    const int64_t t_end = min(t_begin + (int64_t)p.span_len, L);
+
+    float a2[NQ], mu[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        a2[q] = p.A[(int64_t)dc * N + n0 + q] * kLog2e;
+        mu[q] = 0.0f;
+    }
+    const float bias_d = p.bias ? p.bias[dc] : 0.0f;
+    const int64_t row0 = (int64_t)b * L * Dn;
+    const T *db = (const T *)p.delta + row0 + dc;
+    const T *zb = GATED ? (const T *)p.z + row0 + dc : nullptr;
+    const T *gb = (const T *)p.dy + row0 + dc;
+    const int f_step = lane / NQ, f_q = lane % NQ;
+    const T *c_src = (const T *)p.C + (int64_t)b * L * N + n0 + f_q;
+
+    T rd[KF], rz[KF], rg[KF];
+    float cv = 0.0f;
+    auto fetch = [&](int64_t t0) {
+#pragma unroll
+        for (int k = 0; k < KF; ++k) {
+            const int64_t t = t0 + g + k * NW;
+            rd[k] = rz[k] = rg[k] = zero_val<T>();
+            if (t < t_end) {
+                rd[k] = db[t * Dn];
+                if (GATED)
+                    rz[k] = zb[t * Dn];
+                if (dvalid)
+                    rg[k] = gb[t * Dn];
+            }
+        }
+        const int64_t tc = t0 + f_step;
+        cv = (lane < kTCF * NQ && tc < t_end) ? load_val(c_src, tc * N) : 0.0f;
+    };
+
+    float sum_dt = 0.0f;
+    // chunks from the last (possibly partial) one backwards
+    const int64_t last0 = t_begin + (t_end - t_begin - 1) / kTCF * kTCF;
+    if (t_end > t_begin)
+        fetch(last0);
+    int par = 0;
+    for (int64_t t0 = last0; t0 >= t_begin; t0 -= kTCF) {
+#pragma unroll
+        for (int k = 0; k < KF; ++k) {
+            const int tl = g + k * NW;
+            const float v = widen(rd[k]) + bias_d;
+            float gate = 1.0f;
+            if (GATED) {
+                const float zz = widen(rz[k]);
+                gate = zz * hw_rcp(1.0f + hw_exp2(-zz * kLog2e));
+            }
+            s_m[par][tl][lane] = make_float2(softplus_f(v), widen(rg[k]) * gate);
+        }
+        if (lane < kTCF * NQ)
+            s_c[par][g][lane] = cv;
+        if (t0 - kTCF >= t_begin)
+            fetch(t0 - kTCF);
+        __syncthreads();
+        const int nt = (int)min((int64_t)kTCF, t_end - t0);
+#pragma unroll
+        for (int tl = kTCF - 1; tl >= 0; --tl) {
+            if (tl < nt) {
+                const float2 w = s_m[par][tl][lane];
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    mu[q] = __builtin_fmaf(w.y, s_c[par][g][tl * NQ + q], mu[q]);
+                    mu[q] *= decay_exp2(w.x, a2[q]);
+                }
+                sum_dt += w.x;
+            }
+        }
+        par ^= 1;
+    }
+    if (dvalid) {
+        const int64_t o = (((int64_t)span * p.batch + b) * Dn + d) * N + n0;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            p.dec[o + q] = hw_exp2(a2[q] * sum_dt);
+            p.loc[o + q] = mu[q];
+        }
+    }
+}
+
+// mu entering every span from its end: mu_in[n_spans-1] = dh_last (or 0), then
+// mu_in[k-1] = dec[k] mu_in[k] + loc[k].  One thread per (b, d, n) column.
+__global__ void __launch_bounds__(256)
+bwd_mu_carry_kernel(const float *__restrict__ dec, const float *__restrict__ loc,
+                    const float *__restrict__ dh_last, float *__restrict__ mu_in,
+                    int64_t columns, int32_t n_spans)
+{
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= columns)
+        return;
+    float g = dh_last ? dh_last[c] : 0.0f;
+    for (int k = n_spans - 1; k >= 0; --k) {
+        mu_in[(int64_t)k * columns + c] = g;
+        if (k > 0)
+            g = __builtin_fmaf(dec[(int64_t)k * columns + c], g, loc[(int64_t)k * columns + c]);
     }
 }
 
@@ -501,7 +663,7 @@ bwd_reduce_bc_kernel(const float *__restrict__ part, T *dB, T *dC, int64_t batch
     }
 }
 
-// dA = sum over batch rows of dA_part; dD, dbias likewise (fixed row order).
+// dA = sum over the (span, batch row) rows of dA_part; dD, dbias likewise (fixed order).
 __global__ void __launch_bounds__(256)
 bwd_reduce_params_kernel(const float *__restrict__ dA_part, const float *__restrict__ dDb_part,
                          float *dA, float *dD, float *dbias, int64_t batch, int64_t Dn, int64_t N)
@@ -539,6 +701,44 @@ bwd_reduce_params_kernel(const float *__restrict__ dA_part, const float *__restr
 template <typename T, int N, int NW, int S>
 hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
 {
+    const int64_t tiles = (q.d_inner + 63) / 64;
+    const int64_t units = tiles * q.batch;
+    if (units <= 0 || q.L <= 0)
+        return hipSuccess;
+    const bool gated = q.z != nullptr;
+    hipError_t e;
+    if (q.n_spans > 1) {
+        // adjoint summaries of spans 1 .. n_spans-1, then the reverse carry
+        MuSumArgs m{};
+        m.delta = q.delta;
+        m.z = q.z;
+        m.dy = q.dy;
+        m.C = q.C;
+        m.A = q.A;
+        m.bias = q.bias;
+        m.dec = q.mu_dec;
+        m.loc = q.mu_loc;
+        m.L = q.L;
+        m.Dn = (int32_t)q.d_inner;
+        m.batch = (int32_t)q.batch;
+        m.span_len = (int32_t)q.span_len;
+        const dim3 grid((uint32_t)(units * (q.n_spans - 1)));
+        if (gated)
+            hipLaunchKernelGGL((scan_bwd_musum_kernel<T, N, NW, true>), grid, dim3(64 * NW), 0,
+                               stream, m);
+        else
+            hipLaunchKernelGGL((scan_bwd_musum_kernel<T, N, NW, false>), grid, dim3(64 * NW), 0,
+                               stream, m);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+        const int64_t cols = q.batch * q.d_inner * N;
+        hipLaunchKernelGGL(bwd_mu_carry_kernel, dim3((uint32_t)((cols + 255) / 256)), dim3(256),
+                           0, stream, q.mu_dec, q.mu_loc, q.dh_last, q.mu_in, cols,
+                           (int32_t)q.n_spans);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+
     BwdArgs a{};
     a.u = q.u;
     a.delta = q.delta;
@@ -559,36 +759,33 @@ hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
     a.dbc_part = q.dbc_part;
     a.dA_part = q.dA_part;
     a.dDb_part = q.dDb_part;
+    a.h_in = q.n_spans > 1 ? q.h_in : nullptr;
+    a.mu_in = q.n_spans > 1 ? q.mu_in : nullptr;
     a.L = q.L;
     a.Dn = (int32_t)q.d_inner;
     a.batch = (int32_t)q.batch;
     a.n_seg = (int32_t)((q.L + S - 1) / S);
-    const int64_t tiles = (q.d_inner + 63) / 64;
-    const int64_t blocks = tiles * q.batch;
-    if (blocks <= 0 || q.L <= 0)
-        return hipSuccess;
-    if (q.z)
-        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, true>), dim3((uint32_t)blocks),
-                           dim3(64 * NW), 0, stream, a);
+    a.n_spans = (int32_t)q.n_spans;
+    a.span_len = (int32_t)(q.n_spans > 1 ? q.span_len : (q.L + S - 1) / S * S);
+    const dim3 grid((uint32_t)(units * q.n_spans));
+    if (gated)
+        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, true>), grid, dim3(64 * NW), 0, stream, a);
     else
-        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, false>), dim3((uint32_t)blocks),
-                           dim3(64 * NW), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
+        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, false>), grid, dim3(64 * NW), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const int64_t nbc = q.batch * q.L * 2 * N;
     if (q.dB || q.dC)
         hipLaunchKernelGGL((bwd_reduce_bc_kernel<T>), dim3((uint32_t)((nbc + 255) / 256)),
                            dim3(256), 0, stream, q.dbc_part, (T *)q.dB, (T *)q.dC, q.batch,
                            q.L, (int32_t)N, (int32_t)tiles);
-    e = hipGetLastError();
-    if (e != hipSuccess)
+    if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const int64_t np = q.d_inner * N + q.d_inner;
     if (q.dA || q.dD || q.dbias)
         hipLaunchKernelGGL(bwd_reduce_params_kernel, dim3((uint32_t)((np + 255) / 256)),
                            dim3(256), 0, stream, q.dA_part, q.dDb_part, q.dA, q.dD, q.dbias,
-                           q.batch, q.d_inner, (int64_t)N);
+                           q.batch * q.n_spans, q.d_inner, (int64_t)N);
     return hipGetLastError();
 }
 

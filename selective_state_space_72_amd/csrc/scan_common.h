@@ -89,8 +89,16 @@ struct BwdLaunch {
     float *dA, *dD, *dbias, *dh0;
     float *ckpt;        // [block][segment][n][lane]
     float *dbc_part;    // [block][t][2N]
-    float *dA_part;     // [b][d][n]
-    float *dDb_part;    // [b][d][2]
+    float *dA_part;     // [span][b][d][n]
+    float *dDb_part;    // [span][b][d][2]
+    // sequence split (n_spans > 1): spans of span_len steps (a multiple of the segment
+    // length); h_in = state entering each span (the forward carry pass), mu_dec / mu_loc
+    // the adjoint span summaries and mu_in the adjoint entering each span from its end,
+    // all [span][b][d][n]
+    int32_t n_spans;
+    int64_t span_len;
+    const float *h_in;
+    float *mu_dec, *mu_loc, *mu_in;
     int64_t batch, L, d_inner, d_state;
     DType dtype;
 };

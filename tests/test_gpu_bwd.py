@@ -38,14 +38,15 @@ def make_case(base: str, *, batch, seqlen, d_inner, d_state=16, gate=None, h0=No
 
 
 def gpu_bwd(inp, grads, *, use_D=True, use_bias=True, use_h0=True, use_dhl=True, want=ALL,
-            raw=False):
+            raw=False, n_spans=0):
     p = inp.params
     r = ms.mamba_scan_bwd(to_dev(inp.u), to_dev(inp.delta), to_dev(p.A), to_dev(inp.B),
                           to_dev(inp.C), to_dev(grads.dy),
                           D=to_dev(p.D) if use_D else None, z=to_dev(inp.z),
                           delta_bias=to_dev(p.bias) if use_bias else None,
                           h0=to_dev(inp.h0) if use_h0 else None,
-                          dh_last=to_dev(grads.dh_last) if use_dhl else None, want=want)
+                          dh_last=to_dev(grads.dh_last) if use_dhl else None, want=want,
+                          n_spans=n_spans)
     torch.cuda.synchronize()
     if raw:
         return r
@@ -82,10 +83,10 @@ def compare(out, ref, tol, names, label):
     log(f"{label}: " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
 
 
-def full_check(inp, grads, label, **flags):
+def full_check(inp, grads, label, n_spans=0, **flags):
     log(f"case {label}: batch {inp.cfg.batch} L {inp.cfg.seqlen} D {inp.cfg.d_inner} "
-        f"N {inp.cfg.d_state} {inp.dtype} {flags}")
-    out = gpu_bwd(inp, grads, **flags)
+        f"N {inp.cfg.d_state} {inp.dtype} spans {n_spans} {flags}")
+    out = gpu_bwd(inp, grads, n_spans=n_spans, **flags)
     ref = oracle_bwd(inp, grads, **flags)
     names = [n for n in ALL if not (n == "dz" and inp.z is None)]
     compare(out, ref, TOL[inp.dtype], names, label)
@@ -190,3 +191,52 @@ def test_bwd_c3_full_size_sampled():
     refC = sum(p["dC"] for p in parts)
     compare({"dB": out["dB"][:1], "dC": out["dC"][:1]}, {"dB": refB, "dC": refC},
             TOL[synth.BF16], ["dB", "dC"], "c3 row 0 dB/dC")
+
+
+# ---- sequence split into spans (forward and adjoint carry passes) ----------------------
+
+@pytest.mark.parametrize("n_spans,seqlen", [(2, 64), (3, 100), (5, 203), (8, 333)])
+def test_bwd_spans_fp32(n_spans, seqlen):
+    # spans of a multiple of 8 steps; the last one ragged; gate, h0 and dh_last all on
+    inp, g = make_case("c1", batch=2, seqlen=seqlen, d_inner=96, gate=True, h0=True)
+    full_check(inp, g, f"fp32 {n_spans} spans", n_spans=n_spans)
+
+
+@pytest.mark.parametrize("d_state", [4, 8, 32])
+def test_bwd_spans_d_states(d_state):
+    inp, g = make_case("c1", batch=1, seqlen=150, d_inner=70, d_state=d_state, gate=True,
+                       h0=True)
+    full_check(inp, g, f"fp32 N={d_state} 4 spans", n_spans=4)
+
+
+def test_bwd_spans_no_optional_inputs():
+    inp, g = make_case("c1", batch=2, seqlen=90, d_inner=64, gate=False, h0=False)
+    full_check(inp, g, "4 spans, no gate/D/bias/h0/dh_last", n_spans=4, use_D=False,
+               use_bias=False, use_h0=False, use_dhl=False)
+
+
+def test_bwd_auto_split_bf16():
+    # few (batch row, tile) units and a long sequence: the automatic plan splits it
+    inp, g = make_case("c4", batch=1, seqlen=8192, d_inner=256, h0=True)
+    need1 = ms.mamba_scan_bwd_workspace_size(1, 8192, 256, 16, n_spans=1)
+    assert ms.mamba_scan_bwd_workspace_size(1, 8192, 256, 16) > need1  # span buffers
+    full_check(inp, g, "bf16 auto split, 1 x 8192 x 256")
+
+
+def test_bwd_c4_full_size_sampled():
+    """The long-sequence shape (1 x 131072 x 2048, bf16, h0) with the automatic split:
+    per-channel gradients on sampled channels of every tile position."""
+    cfg = synth.CONFIGS["c4"]
+    inp = synth.make_scan_inputs(cfg)
+    g = synth.make_upstream_grads(cfg)
+    log("c4 full size: running the GPU backward")
+    r = gpu_bwd(inp, g, raw=True)
+    ds = np.array([0, 5, 63, 64, 1000, 1500, 2047])
+    di = torch.from_numpy(ds).to(DEV)
+    sub = {"du": r["du"][:, :, di], "ddelta": r["ddelta"][:, :, di],
+           "dA": r["dA"][di], "dD": r["dD"][di], "dbias": r["dbias"][di],
+           "dh0": r["dh0"][:, di]}
+    sub = {k: from_dev(v.contiguous()) for k, v in sub.items()}
+    del r
+    ref = oracle_bwd(inp, g, ds=ds)
+    compare(sub, ref, TOL[synth.BF16], list(sub), "c4 sampled channels")
