@@ -142,6 +142,46 @@ class ScanCase:
                           h_last_out=self.h_last, workspace=self.ws, **self.opts)
 
 
+class BwdCase:
+    """A backward-pass workload resident on the GPU: the scan's inputs, the upstream
+    gradients dy and dh_last, preallocated gradient outputs and workspace."""
+
+    def __init__(self, cfg, dev):
+        import torch
+        import selective_state_space_72_amd as ms
+        from selective_state_space_72_amd import synth
+        self.cfg = cfg
+        inp = synth.make_scan_inputs(cfg)
+        g = synth.make_upstream_grads(cfg)
+        p = inp.params
+        self.t = {k: to_dev(v, dev) for k, v in dict(u=inp.u, delta=inp.delta, z=inp.z, B=inp.B,
+                                                      C=inp.C, A=p.A, D=p.D, bias=p.bias,
+                                                      h0=inp.h0, dy=g.dy,
+                                                      dh_last=g.dh_last).items()}
+        nws = ms.mamba_scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state)
+        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        self.out = None
+        self.step()
+        es = 4 if cfg.dtype == synth.F32 else 2
+        bld = cfg.batch * cfg.seqlen * cfg.d_inner
+        bln = cfg.batch * cfg.seqlen * cfg.d_state
+        bdn = cfg.batch * cfg.d_inner * cfg.d_state
+        dn = cfg.d_inner * cfg.d_state
+        act = 3 if cfg.gate else 2
+        # each input read once, each gradient written once: u, delta, z, dy in and du,
+        # ddelta, dz out; B, C in and dB, dC out; A, D, bias in and their gradients out;
+        # h0 in, dh_last in, dh0 out
+        self.min_bytes = (bld * es * (act + 1) + bld * es * act + bln * es * 4 +
+                          (dn + 2 * cfg.d_inner) * 4 * 2 + bdn * 4 * (3 if cfg.h0 else 2))
+
+    def step(self):
+        import selective_state_space_72_amd as ms
+        t = self.t
+        self.out = ms.mamba_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["dy"],
+                                     D=t["D"], z=t["z"], delta_bias=t["bias"], h0=t["h0"],
+                                     dh_last=t["dh_last"], out=self.out, workspace=self.ws)
+
+
 def time_steps(fn, steps, warmup, flush=None, warm_ms=0.0):
     """Event-timed steps on the current stream.  Returns (ms/step over the back-to-back
     loop, median ms of single steps each preceded by a MALL flush, wall ms/step).
@@ -231,6 +271,22 @@ def extra_workloads(dev, flush, steps):
                      "GB_s": round(case.min_bytes / (ms_used * 1e-3) / 1e9, 1),
                      "gchan_steps_per_s": round(cfg.chan_steps / (ms_used * 1e-3) / 1e9, 2),
                      "hbm_frac": round(case.min_bytes / (ms_used * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del case
+        torch.cuda.empty_cache()
+    # backward pass (gradients of every input) on the three prefill shapes
+    for name in ("c3", "c2", "c4"):
+        cfg = synth.CONFIGS[name]
+        case = BwdCase(cfg, dev)
+        loop_ms, med, _ = time_steps(case.step, max(10, steps // 4), 3, flush, warm_ms=100.0)
+        ms_used = med if med is not None else loop_ms
+        out[name + "_bwd"] = {
+            "workload": f"backward of the {cfg.desc}: batch {cfg.batch}, L {cfg.seqlen}, "
+                        f"d_inner {cfg.d_inner}, d_state {cfg.d_state}, {cfg.dtype}; du, "
+                        "ddelta, dz, dB, dC, dA, dD, dbias, dh0 from dy and dh_last",
+            "ms": round(ms_used, 4), "ms_back_to_back": round(loop_ms, 4),
+            "GB_s": round(case.min_bytes / (ms_used * 1e-3) / 1e9, 1),
+            "gchan_steps_per_s": round(cfg.chan_steps / (ms_used * 1e-3) / 1e9, 2),
+            "hbm_frac": round(case.min_bytes / (ms_used * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del case
         torch.cuda.empty_cache()
     # causal depthwise conv1d + SiLU producing the scan's u, on the large-prefill shape

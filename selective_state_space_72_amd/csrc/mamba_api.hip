@@ -2,6 +2,7 @@
 // Declarations and the contract live in include/mamba_scan.h.
 #include "mamba_scan.h"
 #include "scan_common.h"
+#include "scan_bwd.h"
 
 #include <limits.h>
 #include <stdint.h>

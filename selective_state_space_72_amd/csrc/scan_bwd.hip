@@ -22,17 +22,24 @@
 //      through it.
 // Per (step, channel) quantities (Delta, Delta*u, ds) are computed once and shared
 // through LDS, as are B and C (a wave loads its segment's values with one load per lane,
-// a segment ahead, and reads them back as broadcasts); the per-wave partial sums over state indices (readout, sum mu B, sum
-// A mu Abar h) are summed across waves through LDS in a fixed order.  dB and dC need sums
-// over the block's 64 channels (the lanes): each wave reduces its values of 8 steps with a
-// transposed butterfly (every exchange halves the values a lane holds, so 2*NQ*8 sums
-// across 64 lanes cost about two exchanges per value) and writes one partial per
-// (tile, t, n); a second kernel sums the tiles, and dA, dD, dbias over the batch.
+// a segment ahead, and reads them back as broadcasts).  The per-wave partial sums over
+// state indices (readout, sum mu B, sum A mu Abar h) are summed across waves through LDS
+// in a fixed order.  dB and dC need sums over the block's 64 channels (the lanes): each
+// wave reduces its values of 8 steps with a transposed butterfly (every exchange halves
+// the values a lane holds, so 2*NQ*8 sums across 64 lanes cost about three VALU
+// operations per value) and writes one partial per (tile, t, n); a second kernel sums the
+// tiles, and dA, dD, dbias over the batch rows and spans.
+//
+// When the (batch row, tile) units are too few to fill the device, the sequence is split
+// into spans that run as separate blocks: the forward span pass and carry give the state
+// entering each span, the adjoint span pass below and its reverse carry give the mu
+// entering each span from its end, and each block then covers only its span's steps.
 // Nothing is accumulated with atomics: results are bitwise reproducible.
 #include <type_traits>
 
 #include "device_math.h"
 #include "scan_common.h"
+#include "scan_bwd.h"
 
 namespace mambascan {
 namespace {

@@ -81,28 +81,6 @@ struct StepLaunch {
     bool zoh;
 };
 
-// Backward pass (Euler discretisation).  Optional outputs are NULL when not wanted.
-struct BwdLaunch {
-    const void *u, *delta, *z, *dy, *B, *C;
-    const float *A, *D, *bias, *h0, *dh_last;
-    void *du, *ddelta, *dz, *dB, *dC; // activation dtype
-    float *dA, *dD, *dbias, *dh0;
-    float *ckpt;        // [block][segment][n][lane]
-    float *dbc_part;    // [block][t][2N]
-    float *dA_part;     // [span][b][d][n]
-    float *dDb_part;    // [span][b][d][2]
-    // sequence split (n_spans > 1): spans of span_len steps (a multiple of the segment
-    // length); h_in = state entering each span (the forward carry pass), mu_dec / mu_loc
-    // the adjoint span summaries and mu_in the adjoint entering each span from its end,
-    // all [span][b][d][n]
-    int32_t n_spans;
-    int64_t span_len;
-    const float *h_in;
-    float *mu_dec, *mu_loc, *mu_in;
-    int64_t batch, L, d_inner, d_state;
-    DType dtype;
-};
-
 // Returns true if the (d_state, waves, chunk) combination is compiled in.
 bool scan_variant_supported(int64_t d_state, int waves, int chunk);
 int default_waves(int64_t d_state);
@@ -123,9 +101,6 @@ hipError_t launch_carry(const CarryLaunch &p, hipStream_t stream);
 hipError_t launch_state_update(const StepLaunch &p, hipStream_t stream);
 hipError_t launch_conv1d_silu(const ConvLaunch &p, hipStream_t stream);
 hipError_t launch_conv1d_silu_update(const ConvLaunch &p, hipStream_t stream);
-// Backward pass: (waves, segment length) of the compiled variant for d_state, and launch.
-bool bwd_variant(int64_t d_state, int *waves, int *seg_len);
-hipError_t launch_scan_bwd(const BwdLaunch &p, hipStream_t stream);
 // h_last = h0 (or zeros when h0 is NULL), for empty sequences.
 hipError_t launch_copy_state(float *dst, const float *src, int64_t count, hipStream_t stream);
 
