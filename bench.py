@@ -92,6 +92,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--only-main", action="store_true", help="alias of --no-extra --no-cpu-baseline")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="time only the backward pass on the large prefill (for profiling) and "
+                         "print its JSON summary")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB device copy three times (the reference kernel for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -366,6 +369,22 @@ def main():
     torch.cuda.set_device(dev)
 
     cfg = synth.CONFIGS["c3"]
+    if args.bwd_only:
+        log("bench: backward pass on the large prefill")
+        bcase = BwdCase(cfg, dev)
+        loop_ms, _, _ = time_steps(bcase.step, args.steps, args.warmup)
+        if args.copy_calibration:
+            src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"workload": "backward of the large-model prefill scan",
+                          "steps": args.steps, "ms_per_step": round(loop_ms, 4),
+                          "min_bytes_per_step": bcase.min_bytes,
+                          "GB_s": round(bcase.min_bytes / (loop_ms * 1e-3) / 1e9, 1)}),
+              flush=True)
+        return
     log(f"bench: generating {cfg.name} inputs")
     case = ScanCase(cfg, dev)
     flush = make_flush(dev)
