@@ -104,8 +104,11 @@ __device__ __forceinline__ T zero_val()
     return T(0);
 }
 
-template <typename T, int N, int NW, int S, bool GATED>
-__global__ void __launch_bounds__(64 * NW)
+// AB: keep the segment's decay factors in registers (else recompute them in the adjoint
+// sweep, one more exp per element, to save S * NQ registers).  WPE: waves per SIMD the
+// register allocation targets.
+template <typename T, int N, int NW, int S, bool AB, int WPE, bool GATED>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 scan_bwd_kernel(BwdArgs p)
 {
     constexpr int NQ = N / NW;     // state indices per lane
@@ -316,7 +319,7 @@ scan_bwd_kernel(BwdArgs p)
         __syncthreads();
 
         // recompute the segment's states and decay factors
-        float hs[S][NQ], ab[S][NQ];
+        float hs[S][NQ], ab[AB ? S : 1][NQ];
         {
             float hc[NQ];
 #pragma unroll
@@ -330,7 +333,8 @@ scan_bwd_kernel(BwdArgs p)
                     for (int q = 0; q < NQ; ++q) {
                         const float a = decay_exp2(w.x, a2[q]);
                         hc[q] = __builtin_fmaf(a, hc[q], w.y * s_bc[g][T_ * BCW + q]);
-                        ab[T_][q] = a;
+                        if constexpr (AB)
+                            ab[T_][q] = a;
                         hs[T_][q] = hc[q];
                     }
                 }
@@ -364,7 +368,8 @@ scan_bwd_kernel(BwdArgs p)
                         xv[q] = mu[q] * w.y;                    // dB
                         xv[NQ + q] = w.z * hs[T_][q];           // dC
                         const float hp = T_ == 0 ? hin[q] : hs[T_ > 0 ? T_ - 1 : 0][q];
-                        const float m2 = mu[q] * ab[T_][q];     // Abar_t mu_t
+                        const float abq = AB ? ab[AB ? T_ : 0][q] : decay_exp2(w.x, a2[q]);
+                        const float m2 = mu[q] * abq;           // Abar_t mu_t
                         const float qv = m2 * hp;
                         p2 = __builtin_fmaf(an[q], qv, p2);
                         dA[q] = __builtin_fmaf(w.x, qv, dA[q]);
@@ -698,14 +703,18 @@ bwd_reduce_params_kernel(const float *__restrict__ dA_part, const float *__restr
     }
 }
 
-// (d_state, waves, segment length)
-#define MAMBA_BWD_VARIANTS(X) \
-    X(4, 4, 8)                \
-    X(8, 8, 8)                \
-    X(16, 8, 8)               \
-    X(32, 8, 8)
+// (d_state, waves, segment length, decay factors in registers, waves per SIMD targeted).
+// d_state 16: 4 waves of 4 state indices with the decay factors recomputed fit three
+// blocks per compute unit (167 VGPRs, 33 KB LDS), so the 640 blocks of an 8 x 5120 grid
+// are all resident: 4.01 ms against 4.50 ms for 8 waves of 2 state indices with stored
+// decay factors (119 VGPRs but 58 KB LDS: two blocks per CU) at 8 x 4096 x 5120.
+#define MAMBA_BWD_VARIANTS(X)        \
+    X(4, 4, 8, true, 4)              \
+    X(8, 8, 8, true, 4)              \
+    X(16, 4, 8, false, 3)            \
+    X(32, 8, 8, true, 2)
 
-template <typename T, int N, int NW, int S>
+template <typename T, int N, int NW, int S, bool AB, int WPE>
 hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
 {
     const int64_t tiles = (q.d_inner + 63) / 64;
@@ -776,9 +785,11 @@ hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
     a.span_len = (int32_t)(q.n_spans > 1 ? q.span_len : (q.L + S - 1) / S * S);
     const dim3 grid((uint32_t)(units * q.n_spans));
     if (gated)
-        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, true>), grid, dim3(64 * NW), 0, stream, a);
+        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, true>), grid, dim3(64 * NW), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, false>), grid, dim3(64 * NW), 0, stream, a);
+        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, false>), grid, dim3(64 * NW), 0,
+                           stream, a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const int64_t nbc = q.batch * q.L * 2 * N;
@@ -800,7 +811,7 @@ hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
 
 bool bwd_variant(int64_t d_state, int *waves, int *seg_len)
 {
-#define X(N_, W_, S_)                 \
+#define X(N_, W_, S_, AB_, WPE_)      \
     if (d_state == N_) {              \
         *waves = W_;                  \
         *seg_len = S_;                \
@@ -813,11 +824,11 @@ bool bwd_variant(int64_t d_state, int *waves, int *seg_len)
 
 hipError_t launch_scan_bwd(const BwdLaunch &q, hipStream_t stream)
 {
-#define X(N_, W_, S_)                                                  \
-    if (q.d_state == N_) {                                             \
-        if (q.dtype == DType::BF16)                                    \
-            return launch_bwd_t<uint16_t, N_, W_, S_>(q, stream);      \
-        return launch_bwd_t<float, N_, W_, S_>(q, stream);             \
+#define X(N_, W_, S_, AB_, WPE_)                                             \
+    if (q.d_state == N_) {                                                  \
+        if (q.dtype == DType::BF16)                                         \
+            return launch_bwd_t<uint16_t, N_, W_, S_, AB_, WPE_>(q, stream); \
+        return launch_bwd_t<float, N_, W_, S_, AB_, WPE_>(q, stream);        \
     }
     MAMBA_BWD_VARIANTS(X)
 #undef X
