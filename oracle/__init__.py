@@ -53,6 +53,11 @@ class Oracle:
         lib.oracle_scan.argtypes = [_dp] * 11 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int]
         lib.oracle_step.restype = ctypes.c_int
         lib.oracle_step.argtypes = [_dp] * 10 + [_i64] * 3 + [ctypes.c_int]
+        lib.oracle_scan_ext.restype = ctypes.c_int
+        lib.oracle_scan_ext.argtypes = ([_dp] * 11 + [_i64] * 4 + [ctypes.c_int, ctypes.c_int] +
+                                        [_dp] * 4)
+        lib.oracle_step_ext.restype = ctypes.c_int
+        lib.oracle_step_ext.argtypes = [_dp] * 10 + [_i64] * 3 + [ctypes.c_int] + [_dp] * 4
         lib.oracle_scan_bwd.restype = ctypes.c_int
         lib.oracle_scan_bwd.argtypes = [_dp] * 20 + [_i64] * 4 + [ctypes.c_int]
         lib.oracle_softplus.restype = ctypes.c_double
@@ -70,11 +75,15 @@ class Oracle:
 
     # -- full scan ------------------------------------------------------------
     def scan(self, u, delta, A, B, C, D=None, z=None, bias=None, h0=None,
-             nthreads: Optional[int] = None, zoh: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+             nthreads: Optional[int] = None, zoh: bool = False, lam=None, u_prev=None,
+             B_prev=None, theta=None) -> Tuple[np.ndarray, np.ndarray]:
         """Return (y, h_last) in float64 (zoh: zero-order-hold Bbar instead of Euler's).
 
         u, delta, z: (batch, L, d_inner); B, C: (batch, L, d_state);
         A: (d_inner, d_state); D, bias: (d_inner,); h0: (batch, d_inner, d_state).
+        lam (batch, L, d_inner): exponential-trapezoidal mixing coefficients, with the input
+        before t = 0 in u_prev (batch, d_inner) and B_prev (batch, d_state); theta
+        (batch, L, d_state / 2): rotation rates of the state pairs.
         """
         u = _c64(u)
         batch, L, d_inner = u.shape
@@ -90,13 +99,19 @@ class Oracle:
         _check(bias, (d_inner,), "bias")
         _check(z, u.shape, "z")
         _check(h0, (batch, d_inner, d_state), "h0")
+        lam, u_prev, B_prev, theta = _c64(lam), _c64(u_prev), _c64(B_prev), _c64(theta)
+        _check(lam, u.shape, "lam")
+        _check(u_prev, (batch, d_inner), "u_prev")
+        _check(B_prev, (batch, d_state), "B_prev")
+        _check(theta, (batch, L, d_state // 2), "theta")
         y = np.empty(u.shape, dtype=np.float64)
         h_last = np.empty((batch, d_inner, d_state), dtype=np.float64)
         if nthreads is None:
             nthreads = default_threads()
-        rc = self._lib.oracle_scan(_p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
-                                   _p(bias), _p(h0), _p(y), _p(h_last), batch, L, d_inner,
-                                   d_state, int(nthreads), int(bool(zoh)))
+        rc = self._lib.oracle_scan_ext(_p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z),
+                                       _p(bias), _p(h0), _p(y), _p(h_last), batch, L, d_inner,
+                                       d_state, int(nthreads), int(bool(zoh)), _p(lam),
+                                       _p(u_prev), _p(B_prev), _p(theta))
         if rc != 0:
             raise ValueError("oracle_scan rejected its arguments")
         return y, h_last
@@ -135,10 +150,11 @@ class Oracle:
         return out
 
     # -- one decode step ------------------------------------------------------
-    def step(self, h, u, delta, A, B, C, D=None, z=None, bias=None, zoh: bool = False
-             ) -> Tuple[np.ndarray, np.ndarray]:
-        """Return (y, h_new); h is not modified.  u, delta, z: (batch, d_inner);
-        B, C: (batch, d_state); h: (batch, d_inner, d_state)."""
+    def step(self, h, u, delta, A, B, C, D=None, z=None, bias=None, zoh: bool = False,
+             lam=None, u_prev=None, B_prev=None, theta=None) -> Tuple[np.ndarray, np.ndarray]:
+        """Return (y, h_new); h is not modified.  u, delta, z, lam, u_prev: (batch, d_inner);
+        B, C, B_prev: (batch, d_state); theta: (batch, d_state / 2);
+        h: (batch, d_inner, d_state)."""
         h_new = np.array(h, dtype=np.float64, copy=True, order="C")
         u = _c64(u)
         batch, d_inner = u.shape
@@ -151,10 +167,16 @@ class Oracle:
         _check(B, (batch, d_state), "B")
         _check(C, (batch, d_state), "C")
         _check(z, u.shape, "z")
+        lam, u_prev, B_prev, theta = _c64(lam), _c64(u_prev), _c64(B_prev), _c64(theta)
+        _check(lam, u.shape, "lam")
+        _check(u_prev, u.shape, "u_prev")
+        _check(B_prev, (batch, d_state), "B_prev")
+        _check(theta, (batch, d_state // 2), "theta")
         y = np.empty(u.shape, dtype=np.float64)
-        rc = self._lib.oracle_step(_p(h_new), _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
-                                   _p(z), _p(bias), _p(y), batch, d_inner, d_state,
-                                   int(bool(zoh)))
+        rc = self._lib.oracle_step_ext(_p(h_new), _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D),
+                                       _p(z), _p(bias), _p(y), batch, d_inner, d_state,
+                                       int(bool(zoh)), _p(lam), _p(u_prev), _p(B_prev),
+                                       _p(theta))
         if rc != 0:
             raise ValueError("oracle_step rejected its arguments")
         return y, h_new

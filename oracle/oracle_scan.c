@@ -35,7 +35,20 @@
  * Space Models and Mamba", ZOH), i.e. (exp(Delta A[d,n]) - 1) / A[d,n] * B[n] for
  * the diagonal A, with the A -> 0 limit Delta*B; y_t reads the state
  * after the update with u_t; D*u uses the raw u and is added before the gate;
- * a missing D, bias or h0 means zero and a missing z means no gate.  All
+ * a missing D, bias or h0 means zero and a missing z means no gate.
+ *
+ * Two further options of the Mamba-3 section of "State space models and the Mamba
+ * series" (jsqmd.com), sections 2.1 and 2.2, taken as the page writes them:
+ *   - exponential-trapezoidal rule (lam given): the input term is
+ *       (1 - lam_t) Delta_t B_{t-1}[n] u_{t-1} + lam_t Delta_t B_t[n] u_t
+ *     with the data-dependent mixing coefficient lam[b,t,d] in [0,1], and the input
+ *     before t = 0 taken from u_prev[b,d], B_prev[b,:] (zero when not given).  The page
+ *     writes the look-back term without a decay factor; that is what is computed.
+ *   - data-dependent rotation (theta given): h_t = exp(Delta_t A) R(Delta_t theta_t)
+ *     h_{t-1} + (input term), R the 2x2 rotation [[cos, -sin], [sin, cos]] acting on
+ *     each state pair (2k, 2k+1) with the angle Delta_t * theta[b,t,k]; the rotation
+ *     is applied before the decay, as the product exp(Delta A) R is written.
+ * All
  * arithmetic is double precision with libm exp/log1p and nothing is rounded to
  * a storage type; compile without -ffast-math.  Threads split the independent
  * (b, d) channels only, so the result does not depend on the thread count.
@@ -62,11 +75,32 @@ double oracle_silu(double z)
 
 typedef struct {
     const double *u, *delta, *A, *B, *C, *D, *z, *bias, *h0;
+    const double *lam, *u_prev, *B_prev, *theta; /* trapezoid, rotation (NULL: off) */
     double *y, *h_last;
     int64_t batch, L, Dn, N;
     int64_t chan_begin, chan_end; /* channel index c = b * Dn + d */
     int zoh;
 } scan_job;
+
+/* Rotate each state pair (2k, 2k+1) by dt * theta[k]: [[cos, -sin], [sin, cos]]. */
+static void oracle_rotate(double *h, const double *theta, double dt, int64_t N)
+{
+    for (int64_t k = 0; k < N / 2; ++k) {
+        const double phi = dt * theta[k];
+        const double c = cos(phi), s = sin(phi);
+        const double x = h[2 * k], w = h[2 * k + 1];
+        h[2 * k] = c * x - s * w;
+        h[2 * k + 1] = s * x + c * w;
+    }
+}
+
+/* Exponential-trapezoidal input term of one state index: (1 - lam) dt b_prev u_prev +
+ * lam dt b u. */
+static double oracle_trap_input(double lam, double dt, double b, double u, double b_prev,
+                                double u_prev)
+{
+    return (1.0 - lam) * dt * b_prev * u_prev + lam * dt * b * u;
+}
 
 /* Bbar[n] for step size dt, state coefficient a = A[d,n] and input coefficient b = B[n]:
  * Euler dt * b, or the zero-order hold (exp(dt a) - 1) / a * b (limit dt * b at a = 0). */
@@ -85,6 +119,9 @@ static void scan_channels(const scan_job *j)
         const int64_t b = c / Dn, d = c % Dn;
         for (int64_t n = 0; n < N; ++n)
             h[n] = j->h0 ? j->h0[(b * Dn + d) * N + n] : 0.0;
+        /* the input of the step before t = 0 (trapezoidal look-back) */
+        double u_lb = j->u_prev ? j->u_prev[b * Dn + d] : 0.0;
+        const double *B_lb = j->B_prev ? j->B_prev + b * N : NULL;
 
         for (int64_t t = 0; t < L; ++t) {
             const int64_t bld = (b * L + t) * Dn + d; /* (B, L, D) layout */
@@ -94,12 +131,22 @@ static void scan_channels(const scan_job *j)
             /* step size */
             const double dt = oracle_softplus(j->delta[bld] + (j->bias ? j->bias[d] : 0.0));
 
+            /* data-dependent rotation of the previous state, before its decay */
+            if (j->theta)
+                oracle_rotate(h, j->theta + (b * j->L + t) * (N / 2), dt, N);
+
             /* discretise and advance the state */
             for (int64_t n = 0; n < N; ++n) {
                 const double abar = exp(dt * j->A[d * N + n]);
                 const double bbar = oracle_bbar(dt, j->A[d * N + n], j->B[bln + n], j->zoh);
-                h[n] = abar * h[n] + bbar * ut;
+                if (j->lam)
+                    h[n] = abar * h[n] + oracle_trap_input(j->lam[bld], dt, j->B[bln + n], ut,
+                                                           B_lb ? B_lb[n] : 0.0, u_lb);
+                else
+                    h[n] = abar * h[n] + bbar * ut;
             }
+            u_lb = ut;
+            B_lb = j->B + bln;
 
             /* readout, skip term, gate */
             double yt = 0.0;
@@ -132,12 +179,15 @@ static void *scan_thread(void *arg)
  * zoh selects the zero-order-hold Bbar instead of Euler's.
  * Returns 0, or -1 on a bad argument.
  */
-int oracle_scan(const double *u, const double *delta, const double *A, const double *B,
-                const double *C, const double *D, const double *z, const double *bias,
-                const double *h0, double *y, double *h_last, int64_t batch, int64_t L,
-                int64_t d_inner, int64_t d_state, int nthreads, int zoh)
+int oracle_scan_ext(const double *u, const double *delta, const double *A, const double *B,
+                    const double *C, const double *D, const double *z, const double *bias,
+                    const double *h0, double *y, double *h_last, int64_t batch, int64_t L,
+                    int64_t d_inner, int64_t d_state, int nthreads, int zoh, const double *lam,
+                    const double *u_prev, const double *B_prev, const double *theta)
 {
     if (batch < 0 || L < 0 || d_inner < 0 || d_state < 0)
+        return -1;
+    if ((theta && d_state % 2 != 0) || (lam && zoh))
         return -1;
     if ((L > 0 && (!u || !delta || !B || !C || !y)) || (d_state > 0 && !A))
         return -1;
@@ -163,6 +213,7 @@ int oracle_scan(const double *u, const double *delta, const double *A, const dou
         j->chan_begin = chans * i / nthreads;
         j->chan_end = chans * (i + 1) / nthreads;
         j->zoh = zoh;
+        j->lam = lam; j->u_prev = u_prev; j->B_prev = B_prev; j->theta = theta;
     }
     for (int i = 1; i < nthreads; ++i)
         pthread_create(&tids[i], NULL, scan_thread, &jobs[i]);
@@ -174,6 +225,16 @@ int oracle_scan(const double *u, const double *delta, const double *A, const dou
     return 0;
 }
 
+/* The scan without the trapezoid and rotation options. */
+int oracle_scan(const double *u, const double *delta, const double *A, const double *B,
+                const double *C, const double *D, const double *z, const double *bias,
+                const double *h0, double *y, double *h_last, int64_t batch, int64_t L,
+                int64_t d_inner, int64_t d_state, int nthreads, int zoh)
+{
+    return oracle_scan_ext(u, delta, A, B, C, D, z, bias, h0, y, h_last, batch, L, d_inner,
+                           d_state, nthreads, zoh, NULL, NULL, NULL, NULL);
+}
+
 /*
  * One recurrent decode step: the body of the time loop above, once, for every
  * (b, d), with the state carried by the caller ("output, h = ssm(token, h)" in
@@ -181,12 +242,15 @@ int oracle_scan(const double *u, const double *delta, const double *A, const dou
  * h: (batch, d_inner, d_state), updated in place.  u, delta, z, y: (batch, d_inner);
  * B, C: (batch, d_state).
  */
-int oracle_step(double *h, const double *u, const double *delta, const double *A,
-                const double *B, const double *C, const double *D, const double *z,
-                const double *bias, double *y, int64_t batch, int64_t d_inner, int64_t d_state,
-                int zoh)
+int oracle_step_ext(double *h, const double *u, const double *delta, const double *A,
+                    const double *B, const double *C, const double *D, const double *z,
+                    const double *bias, double *y, int64_t batch, int64_t d_inner,
+                    int64_t d_state, int zoh, const double *lam, const double *u_prev,
+                    const double *B_prev, const double *theta)
 {
     if (!h || !u || !delta || !A || !B || !C || !y || batch < 0 || d_inner < 0 || d_state < 0)
+        return -1;
+    if ((theta && d_state % 2 != 0) || (lam && zoh))
         return -1;
     for (int64_t b = 0; b < batch; ++b) {
         for (int64_t d = 0; d < d_inner; ++d) {
@@ -194,10 +258,18 @@ int oracle_step(double *h, const double *u, const double *delta, const double *A
             double *hb = h + bd * d_state;
             const double ut = u[bd];
             const double dt = oracle_softplus(delta[bd] + (bias ? bias[d] : 0.0));
+            if (theta)
+                oracle_rotate(hb, theta + b * (d_state / 2), dt, d_state);
             for (int64_t n = 0; n < d_state; ++n) {
                 const double abar = exp(dt * A[d * d_state + n]);
                 const double bbar = oracle_bbar(dt, A[d * d_state + n], B[b * d_state + n], zoh);
-                hb[n] = abar * hb[n] + bbar * ut;
+                if (lam)
+                    hb[n] = abar * hb[n] +
+                            oracle_trap_input(lam[bd], dt, B[b * d_state + n], ut,
+                                              B_prev ? B_prev[b * d_state + n] : 0.0,
+                                              u_prev ? u_prev[bd] : 0.0);
+                else
+                    hb[n] = abar * hb[n] + bbar * ut;
             }
             double yt = 0.0;
             for (int64_t n = 0; n < d_state; ++n)
@@ -209,6 +281,16 @@ int oracle_step(double *h, const double *u, const double *delta, const double *A
         }
     }
     return 0;
+}
+
+/* The decode step without the trapezoid and rotation options. */
+int oracle_step(double *h, const double *u, const double *delta, const double *A,
+                const double *B, const double *C, const double *D, const double *z,
+                const double *bias, double *y, int64_t batch, int64_t d_inner, int64_t d_state,
+                int zoh)
+{
+    return oracle_step_ext(h, u, delta, A, B, C, D, z, bias, y, batch, d_inner, d_state, zoh,
+                           NULL, NULL, NULL, NULL);
 }
 
 /*

@@ -473,3 +473,213 @@ def pin_gradient_closed_forms(orc):
 
 
 PINS += [pin_gradients_finite_differences, pin_gradient_closed_forms]
+
+
+# ----------------------------------------------------------------------------
+# Mamba-3 options ("State space models and the Mamba series", jsqmd.com, sections
+# 2.1 and 2.2): exponential-trapezoidal input term and data-dependent rotation
+# ----------------------------------------------------------------------------
+
+def _shift_in_time(x, first):
+    """x_{t-1} along axis 1, with `first` at t = 0."""
+    out = np.empty_like(x)
+    out[:, 0] = first
+    out[:, 1:] = x[:, :-1]
+    return out
+
+
+def pin_trapezoid_lti_kernel(orc):
+    """Constant Delta, B, C and lam, no D, gate or h0: y is the causal convolution of u
+    with K_0 = lam Delta sum_n C_n B_n and K_k = Delta sum_n C_n B_n (lam Abar_n^k +
+    (1 - lam) Abar_n^(k-1)) for k >= 1, plus the look-back input u_prev entering as
+    (1 - lam) Delta sum_n C_n B_prev_n Abar_n^t u_prev."""
+    rng = np.random.default_rng(51)
+    L, Dn, N, lam = 40, 3, 5, 0.37
+    u = rng.standard_normal((1, L, Dn))
+    dval = rng.standard_normal(Dn)
+    delta = np.broadcast_to(dval, (1, L, Dn)).copy()
+    Bv, Cv = rng.standard_normal(N), rng.standard_normal(N)
+    B = np.broadcast_to(Bv, (1, L, N)).copy()
+    C = np.broadcast_to(Cv, (1, L, N)).copy()
+    A = -rng.uniform(0.2, 2.0, size=(Dn, N))
+    u_prev = rng.standard_normal((1, Dn))
+    B_prev = rng.standard_normal((1, N))
+    y, _ = orc.scan(u, delta, A, B, C, lam=np.full(u.shape, lam), u_prev=u_prev,
+                    B_prev=B_prev)
+    k = np.arange(L)
+    for d in range(Dn):
+        dt = ref_softplus(dval[d])
+        ab = np.exp(np.outer(k, dt * A[d]))                     # Abar^k, (L, N)
+        ab_m1 = np.vstack([np.zeros(N), ab[:-1]])                # Abar^(k-1), 0 at k = 0
+        K = dt * ((lam * ab + (1 - lam) * ab_m1) @ (Cv * Bv))
+        ref = np.convolve(u[0, :, d], K)[:L]
+        ref = ref + (1 - lam) * dt * (ab @ (Cv * B_prev[0])) * u_prev[0, d]
+        assert np.allclose(y[0, :, d], ref, rtol=1e-11, atol=1e-12), d
+
+
+def pin_trapezoid_limits(orc):
+    """lam = 1 is the Euler scan; lam = 0 is the Euler scan of the inputs shifted by one
+    step (u_{t-1}, B_{t-1}, starting from u_prev, B_prev) with the same Delta and C."""
+    rng = np.random.default_rng(52)
+    case = random_case(rng, L=23)
+    u_prev = rng.standard_normal((case["u"].shape[0], case["u"].shape[2]))
+    B_prev = rng.standard_normal((case["u"].shape[0], case["B"].shape[2]))
+    y1, h1 = orc.scan(**case)
+    yt, ht = orc.scan(**case, lam=np.ones(case["u"].shape), u_prev=u_prev, B_prev=B_prev)
+    assert np.allclose(yt, y1, rtol=1e-14, atol=0) and np.allclose(ht, h1, rtol=1e-14, atol=0)
+    c0 = dict(case, D=None)
+    y0, h0 = orc.scan(**c0, lam=np.zeros(case["u"].shape), u_prev=u_prev, B_prev=B_prev)
+    shifted = dict(c0, u=_shift_in_time(case["u"], u_prev), B=_shift_in_time(case["B"], B_prev))
+    ys, hs = orc.scan(**shifted)
+    assert np.allclose(h0, hs, rtol=1e-13, atol=1e-14)
+    # the readout uses the unshifted gate and C; with D = None y depends on h only
+    assert np.allclose(y0, ys, rtol=1e-12, atol=1e-13)
+
+
+def pin_trapezoid_affine_in_lambda(orc):
+    """The state and the output are affine in the mixing coefficients."""
+    rng = np.random.default_rng(53)
+    case = random_case(rng, L=19)
+    shp = case["u"].shape
+    l1, l2 = rng.uniform(0, 1, shp), rng.uniform(0, 1, shp)
+    a = 0.3
+    ya, ha = orc.scan(**case, lam=l1)
+    yb, hb = orc.scan(**case, lam=l2)
+    ym, hm = orc.scan(**case, lam=a * l1 + (1 - a) * l2)
+    assert np.allclose(hm, a * ha + (1 - a) * hb, rtol=1e-12, atol=1e-12)
+    assert np.allclose(ym, a * ya + (1 - a) * yb, rtol=1e-11, atol=1e-11)
+
+
+def pin_trapezoid_split_and_decode(orc):
+    """scan(0..L) == scan(0..k) then scan(k..L) continued with (h_k, u_{k-1}, B_{k-1});
+    chained decode steps reproduce the scan.  Bitwise."""
+    rng = np.random.default_rng(54)
+    case = random_case(rng, L=21)
+    lam = rng.uniform(0, 1, case["u"].shape)
+    up = rng.standard_normal((case["u"].shape[0], case["u"].shape[2]))
+    Bp = rng.standard_normal((case["u"].shape[0], case["B"].shape[2]))
+    y, h_last = orc.scan(**case, lam=lam, u_prev=up, B_prev=Bp)
+    for k in (1, 8, 20):
+        first = {key: (v[:, :k] if key in ("u", "delta", "B", "C", "z") else v)
+                 for key, v in case.items()}
+        rest = {key: (v[:, k:] if key in ("u", "delta", "B", "C", "z") else v)
+                for key, v in case.items()}
+        y1, h1 = orc.scan(**first, lam=lam[:, :k], u_prev=up, B_prev=Bp)
+        rest["h0"] = h1
+        y2, h2 = orc.scan(**rest, lam=lam[:, k:], u_prev=case["u"][:, k - 1],
+                          B_prev=case["B"][:, k - 1])
+        assert np.array_equal(np.concatenate([y1, y2], axis=1), y), k
+        assert np.array_equal(h2, h_last), k
+    h = case["h0"].copy()
+    for t in range(case["u"].shape[1]):
+        prev_u = up if t == 0 else case["u"][:, t - 1]
+        prev_B = Bp if t == 0 else case["B"][:, t - 1]
+        yt, h = orc.step(h, case["u"][:, t], case["delta"][:, t], case["A"], case["B"][:, t],
+                         case["C"][:, t], D=case["D"], z=case["z"][:, t], bias=case["bias"],
+                         lam=lam[:, t], u_prev=prev_u, B_prev=prev_B)
+        assert np.array_equal(yt, y[:, t]), t
+    assert np.array_equal(h, h_last)
+
+
+def _complex_reference(case, theta):
+    """The complex state of the pages' continuous form dh/dt = (A + i theta) h +
+    (B + i B^) x, with each state pair (2k, 2k+1) read as one complex number
+    w_k = h_2k + i h_2k+1 and A equal within a pair: w_t = exp(Delta a) exp(i Delta
+    theta_t) w_{t-1} + Delta (B_2k + i B_2k+1) u_t; y_t = sum_k C_2k Re w + C_2k+1 Im w."""
+    u, delta, A, B, C = case["u"], case["delta"], case["A"], case["B"], case["C"]
+    batch, L, Dn = u.shape
+    K = A.shape[1] // 2
+    y = np.zeros_like(u)
+    h_last = np.zeros((batch, Dn, 2 * K))
+    for b in range(batch):
+        for d in range(Dn):
+            h0 = case["h0"][b, d] if case.get("h0") is not None else np.zeros(2 * K)
+            w = h0[0::2] + 1j * h0[1::2]
+            a = A[d, 0::2]
+            for t in range(L):
+                dt = ref_softplus(delta[b, t, d] + case["bias"][d])
+                w = np.exp(dt * a) * np.exp(1j * dt * theta[b, t]) * w + \
+                    dt * (B[b, t, 0::2] + 1j * B[b, t, 1::2]) * u[b, t, d]
+                yt = np.sum(C[b, t, 0::2] * w.real + C[b, t, 1::2] * w.imag) + \
+                    case["D"][d] * u[b, t, d]
+                y[b, t, d] = yt * ref_silu(case["z"][b, t, d])
+            h_last[b, d, 0::2], h_last[b, d, 1::2] = w.real, w.imag
+    return y, h_last
+
+
+def pin_rotation_complex_form(orc):
+    """With A equal within each state pair, the rotation is multiplication of the pair,
+    read as a complex number, by exp(i Delta theta) (numpy complex arithmetic)."""
+    rng = np.random.default_rng(55)
+    case = random_case(rng, L=17, N=6)
+    case["A"][:, 1::2] = case["A"][:, 0::2]
+    theta = rng.uniform(-3, 3, (case["u"].shape[0], 17, 3))
+    y, h = orc.scan(**case, theta=theta)
+    yr, hr = _complex_reference(case, theta)
+    assert np.allclose(y, yr, rtol=1e-11, atol=1e-12)
+    assert np.allclose(h, hr, rtol=1e-11, atol=1e-12)
+
+
+def pin_rotation_pure_and_order(orc):
+    """A = 0 and u = 0: each pair turns by the accumulated angle sum_t Delta_t theta_t
+    (R(phi) e_1 = (cos phi, sin phi)); distinct decays within a pair, constant Delta and
+    theta, u = 0: h_L = (diag(exp(Delta A)) R(Delta theta))^L h0 (numpy matrix power),
+    the product in the order the page writes it."""
+    rng = np.random.default_rng(56)
+    case = random_case(rng, batch=1, L=13, Dn=2, N=4, gate=False, with_D=False)
+    case["u"] = np.zeros_like(case["u"])
+    theta = rng.uniform(-2, 2, (1, 13, 2))
+    zeroA = dict(case, A=np.zeros_like(case["A"]))
+    _, h = orc.scan(**zeroA, theta=theta)
+    for d in range(2):
+        dt = ref_softplus(case["delta"][0, :, d] + case["bias"][d])
+        for k in range(2):
+            phi = np.sum(dt * theta[0, :, k])
+            x, w = case["h0"][0, d, 2 * k], case["h0"][0, d, 2 * k + 1]
+            ref = (np.cos(phi) * x - np.sin(phi) * w, np.sin(phi) * x + np.cos(phi) * w)
+            assert np.allclose(h[0, d, 2 * k:2 * k + 2], ref, rtol=1e-12, atol=1e-13)
+    const = dict(case)
+    const["delta"] = np.broadcast_to(case["delta"][:, :1], case["delta"].shape).copy()
+    th = np.broadcast_to(theta[:, :1], theta.shape).copy()
+    _, h = orc.scan(**const, theta=th)
+    for d in range(2):
+        dt = ref_softplus(const["delta"][0, 0, d] + case["bias"][d])
+        for k in range(2):
+            phi = dt * th[0, 0, k]
+            R = np.array([[np.cos(phi), -np.sin(phi)], [np.sin(phi), np.cos(phi)]])
+            M = np.diag(np.exp(dt * case["A"][d, 2 * k:2 * k + 2])) @ R
+            ref = np.linalg.matrix_power(M, 13) @ case["h0"][0, d, 2 * k:2 * k + 2]
+            assert np.allclose(h[0, d, 2 * k:2 * k + 2], ref, rtol=1e-11, atol=1e-13)
+
+
+def pin_rotation_zero_split_decode(orc):
+    """theta = 0 is the plain scan; split invariance and decode steps, bitwise."""
+    rng = np.random.default_rng(57)
+    case = random_case(rng, L=15, N=4)
+    y0, h0 = orc.scan(**case)
+    yz, hz = orc.scan(**case, theta=np.zeros(case["u"].shape[:2] + (2,)))
+    assert np.array_equal(y0, yz) and np.array_equal(h0, hz)
+    theta = rng.uniform(-1, 1, case["u"].shape[:2] + (2,))
+    y, h_last = orc.scan(**case, theta=theta)
+    k = 6
+    first = {key: (v[:, :k] if key in ("u", "delta", "B", "C", "z") else v)
+             for key, v in case.items()}
+    rest = {key: (v[:, k:] if key in ("u", "delta", "B", "C", "z") else v)
+            for key, v in case.items()}
+    y1, h1 = orc.scan(**first, theta=theta[:, :k])
+    rest["h0"] = h1
+    y2, h2 = orc.scan(**rest, theta=theta[:, k:])
+    assert np.array_equal(np.concatenate([y1, y2], axis=1), y)
+    assert np.array_equal(h2, h_last)
+    h = case["h0"].copy()
+    for t in range(15):
+        yt, h = orc.step(h, case["u"][:, t], case["delta"][:, t], case["A"], case["B"][:, t],
+                         case["C"][:, t], D=case["D"], z=case["z"][:, t], bias=case["bias"],
+                         theta=theta[:, t])
+        assert np.array_equal(yt, y[:, t]), t
+    assert np.array_equal(h, h_last)
+
+
+PINS += [pin_trapezoid_lti_kernel, pin_trapezoid_limits, pin_trapezoid_affine_in_lambda,
+         pin_trapezoid_split_and_decode, pin_rotation_complex_form, pin_rotation_pure_and_order,
+         pin_rotation_zero_split_decode]

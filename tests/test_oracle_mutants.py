@@ -69,6 +69,29 @@ MUTANTS = [
                       "double ddt = 0.0, du = 0.0;")]),
     ("bwd_ddt_no_input_term", [("ddt += mu[n] * (a * abar * hprev + j->B[bln + n] * ut);",
                                 "ddt += mu[n] * (a * abar * hprev);")]),
+    # exponential-trapezoidal rule
+    ("trap_weights_swapped", [("return (1.0 - lam) * dt * b_prev * u_prev + lam * dt * b * u;",
+                               "return lam * dt * b_prev * u_prev + (1.0 - lam) * dt * b * u;")]),
+    ("trap_lookback_not_advanced", [("            u_lb = ut;\n", "")]),
+    ("trap_lookback_current_B", [("B_lb ? B_lb[n] : 0.0, u_lb)", "j->B[bln + n], u_lb)")]),
+    ("trap_lookback_decayed", [("return (1.0 - lam) * dt * b_prev * u_prev + lam * dt * b * u;",
+                                "return (1.0 - lam) * dt * b_prev * u_prev * exp(-dt) + "
+                                "lam * dt * b * u;")]),
+    ("trap_u_prev_ignored", [("double u_lb = j->u_prev ? j->u_prev[b * Dn + d] : 0.0;",
+                              "double u_lb = 0.0;")]),
+    ("trap_step_no_u_prev", [("u_prev ? u_prev[bd] : 0.0)", "0.0)")]),
+    # data-dependent rotation
+    ("rot_transposed", [("h[2 * k] = c * x - s * w;", "h[2 * k] = c * x + s * w;"),
+                        ("h[2 * k + 1] = s * x + c * w;", "h[2 * k + 1] = -s * x + c * w;")]),
+    ("rot_angle_without_delta", [("const double phi = dt * theta[k];",
+                                  "const double phi = theta[k];")]),
+    ("rot_previous_step_angle", [("oracle_rotate(h, j->theta + (b * j->L + t) * (N / 2), dt, N);",
+                                  "oracle_rotate(h, j->theta + (b * j->L + (t > 0 ? t - 1 : 0)) "
+                                  "* (N / 2), dt, N);")]),
+    ("rot_pairs_adjacent_halves", [("const double x = h[2 * k], w = h[2 * k + 1];",
+                                    "const double x = h[k], w = h[k + N / 2];")]),
+    ("rot_step_missing", [("                oracle_rotate(hb, theta + b * (d_state / 2), dt, d_state);\n",
+                           "")]),
 ]
 
 
