@@ -355,6 +355,65 @@ MAMBA_API mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, con
                                            size_t workspace_bytes,
                                            const mamba_scan_opts_t *opts, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Options of the Mamba-3 formulation ("State space models and the Mamba series",
+ * jsqmd.com, sections 2.1 and 2.2), taken as that page writes them.  A NULL pointer
+ * switches an option off.
+ *
+ *   lambda  (batch, seqlen, d_inner) dtype [decode: (batch, d_inner)]
+ *       exponential-trapezoidal rule: the input term of step t becomes
+ *         (1 - lambda_t) Delta_t B_{t-1}[n] u_{t-1} + lambda_t Delta_t B_t[n] u_t
+ *       (the page's look-back term carries no decay factor), with lambda_t the caller's
+ *       data-dependent mixing coefficient (in [0, 1]; not checked).  lambda = 1 is the
+ *       Euler rule.  Not combinable with the zero-order hold.
+ *   u_prev  (batch, d_inner) dtype, B_prev (batch, d_state) dtype
+ *       the input (u, B) of the step before t = 0, for continuing a sequence; NULL = 0.
+ *       Used only with lambda.
+ *   theta   (batch, seqlen, d_state/2) dtype [decode: (batch, d_state/2)]
+ *       data-dependent rotation: h_t = exp(Delta_t A) R(Delta_t theta_t) h_{t-1} + (input
+ *       term), where R turns each state pair (2k, 2k+1) by the angle
+ *       Delta_t * theta[b,t,k]: (x, w) -> (cos x - sin w, sin x + cos w), before the decay.
+ *       d_state must be even; in the scan it needs d_state 16 or 32 (state pairs within
+ *       one wave) and an unsplit sequence (n_spans 1), else MAMBA_ERR_UNSUPPORTED.
+ *
+ * Both options run in the SCALAR family (AUTO selects it; ROWS or BLOCK return
+ * MAMBA_ERR_UNSUPPORTED).  The extension inputs follow the alignment and aliasing rules
+ * of the other inputs. */
+typedef struct {
+    const void *lambda;
+    const void *u_prev;
+    const void *B_prev;
+    const void *theta;
+} mamba_scan_ext_t;
+
+/* Workspace size for mamba_scan_fwd_ext (ext and opts may be NULL). */
+MAMBA_API size_t mamba_scan_fwd_workspace_size_ext(int64_t batch, int64_t seqlen,
+                                                   int64_t d_inner, int64_t d_state,
+                                                   const mamba_scan_ext_t *ext,
+                                                   const mamba_scan_opts_t *opts);
+
+/* mamba_scan_fwd_ex with the Mamba-3 options (ext NULL = none). */
+MAMBA_API mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float *A,
+                                            const void *B, const void *C, const float *D,
+                                            const void *z, const float *delta_bias,
+                                            const float *h0, void *y, float *h_last,
+                                            int64_t batch, int64_t seqlen, int64_t d_inner,
+                                            int64_t d_state, mamba_dtype_t dtype,
+                                            void *workspace, size_t workspace_bytes,
+                                            const mamba_scan_opts_t *opts,
+                                            const mamba_scan_ext_t *ext, void *stream);
+
+/* mamba_state_update_ex with the Mamba-3 options (shapes of the decode step; ext NULL =
+ * none).  With lambda the caller passes the previous token's u and B as u_prev, B_prev. */
+MAMBA_API mamba_status_t mamba_state_update_ext(float *h, const void *u, const void *delta,
+                                                const float *A, const void *B, const void *C,
+                                                const float *D, const void *z,
+                                                const float *delta_bias, void *y,
+                                                int64_t batch, int64_t d_inner,
+                                                int64_t d_state, mamba_dtype_t dtype,
+                                                int32_t discretization,
+                                                const mamba_scan_ext_t *ext, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 MAMBA_API const char *mamba_status_string(mamba_status_t status);
 

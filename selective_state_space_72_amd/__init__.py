@@ -38,6 +38,7 @@ EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_state_update", "mamba_state_update_ex", "mamba_conv1d_silu_fwd",
            "mamba_conv1d_silu_update", "mamba_scan_bwd_workspace_size", "mamba_scan_bwd",
            "mamba_scan_bwd_workspace_size_ex", "mamba_scan_bwd_ex",
+           "mamba_scan_fwd_workspace_size_ext", "mamba_scan_fwd_ext", "mamba_state_update_ext",
            "mamba_status_string")
 
 
@@ -60,6 +61,12 @@ class ScanOpts(ctypes.Structure):
     _fields_ = [("chunk_len", ctypes.c_int32), ("waves", ctypes.c_int32),
                 ("n_spans", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("relay", ctypes.c_int32), ("discretization", ctypes.c_int32)]
+
+
+class ScanExt(ctypes.Structure):
+    """mamba_scan_ext_t: trapezoid mixing coefficients, look-back input, rotation rates."""
+    _fields_ = [("lambda_", ctypes.c_void_p), ("u_prev", ctypes.c_void_p),
+                ("B_prev", ctypes.c_void_p), ("theta", ctypes.c_void_p)]
 
 
 _vp = ctypes.c_void_p
@@ -110,6 +117,17 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mamba_scan_bwd_ex.argtypes = ([_vp] * 20 + [_i64] * 4 +
                                       [ctypes.c_int, _vp, ctypes.c_size_t,
                                        ctypes.POINTER(ScanOpts), _vp])
+    lib.mamba_scan_fwd_workspace_size_ext.restype = ctypes.c_size_t
+    lib.mamba_scan_fwd_workspace_size_ext.argtypes = ([_i64] * 4 + [ctypes.POINTER(ScanExt),
+                                                                    ctypes.POINTER(ScanOpts)])
+    lib.mamba_scan_fwd_ext.restype = ctypes.c_int
+    lib.mamba_scan_fwd_ext.argtypes = ([_vp] * 11 + [_i64] * 4 +
+                                       [ctypes.c_int, _vp, ctypes.c_size_t,
+                                        ctypes.POINTER(ScanOpts), ctypes.POINTER(ScanExt), _vp])
+    lib.mamba_state_update_ext.restype = ctypes.c_int
+    lib.mamba_state_update_ext.argtypes = ([_vp] * 10 + [_i64] * 3 +
+                                           [ctypes.c_int, ctypes.c_int32,
+                                            ctypes.POINTER(ScanExt), _vp])
     lib.mamba_status_string.restype = ctypes.c_char_p
     lib.mamba_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -176,10 +194,14 @@ def _opts(chunk_len=0, waves=0, n_spans=0, kernel="auto", relay=0, discretizatio
 def mamba_scan_fwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state: int,
                                   chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
                                   kernel: str = "auto", relay: int = 0,
-                                  discretization: str = "euler") -> int:
+                                  discretization: str = "euler", trapezoid: bool = False,
+                                  rotation: bool = False) -> int:
     lib = load_library()
     o = _opts(chunk_len, waves, n_spans, kernel, relay, discretization)
-    n = lib.mamba_scan_fwd_workspace_size_ex(batch, seqlen, d_inner, d_state, ctypes.byref(o))
+    # only the presence of the extension inputs matters for the size
+    e = ScanExt(1 if trapezoid else None, None, None, 1 if rotation else None)
+    n = lib.mamba_scan_fwd_workspace_size_ext(batch, seqlen, d_inner, d_state, ctypes.byref(e),
+                                              ctypes.byref(o))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes or options for mamba_scan_fwd")
     return int(n)
@@ -189,10 +211,13 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
                    return_last_state: bool = False, *, out=None, h_last_out=None,
                    chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
                    kernel: str = "auto", relay: int = 0, discretization: str = "euler",
-                   workspace=None) -> Tuple:
+                   workspace=None, lam=None, u_prev=None, B_prev=None, theta=None) -> Tuple:
     """Selective scan over (batch, seqlen, d_inner); see include/mamba_scan.h.
 
     Returns (y, h_last) -- h_last is None unless return_last_state (or h_last_out).
+    lam (batch, seqlen, d_inner): exponential-trapezoidal mixing coefficients, with the
+    input before t = 0 in u_prev (batch, d_inner) and B_prev (batch, d_state); theta
+    (batch, seqlen, d_state / 2): rotation rates of the state pairs (see mamba_scan_ext_t).
     """
     torch = _torch()
     lib = load_library()
@@ -221,10 +246,18 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
     if h_last is None and return_last_state:
         h_last = torch.empty((batch, d_inner, d_state), dtype=f32, device=dev)
     p_hl = _ptr(h_last, "h_last_out", (batch, d_inner, d_state), f32, dev)
+    ext = ScanExt(_ptr(lam, "lam", (batch, seqlen, d_inner), act, dev),
+                  _ptr(u_prev, "u_prev", (batch, d_inner), act, dev),
+                  _ptr(B_prev, "B_prev", (batch, d_state), act, dev),
+                  _ptr(theta, "theta", (batch, seqlen, d_state // 2), act, dev))
+    if seqlen == 0:
+        # empty tensors have no address; only the presence of an option matters here
+        ext.lambda_ = ext.lambda_ or (1 if lam is not None else None)
+        ext.theta = ext.theta or (1 if theta is not None else None)
 
     opts = _opts(chunk_len, waves, n_spans, kernel, relay, discretization)
-    need = lib.mamba_scan_fwd_workspace_size_ex(batch, seqlen, d_inner, d_state,
-                                                ctypes.byref(opts))
+    need = lib.mamba_scan_fwd_workspace_size_ext(batch, seqlen, d_inner, d_state,
+                                                 ctypes.byref(ext), ctypes.byref(opts))
     if need == ctypes.c_size_t(-1).value:
         raise MambaError(4, "mamba_scan_fwd_workspace_size")
     ws = workspace
@@ -232,17 +265,20 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     p_ws = ws.data_ptr() if ws is not None and need > 0 else None
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    st = lib.mamba_scan_fwd_ex(p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_y, p_hl,
-                               batch, seqlen, d_inner, d_state, code, p_ws, ws_bytes,
-                               ctypes.byref(opts), _stream(dev))
+    st = lib.mamba_scan_fwd_ext(p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_y,
+                                p_hl, batch, seqlen, d_inner, d_state, code, p_ws, ws_bytes,
+                                ctypes.byref(opts), ctypes.byref(ext), _stream(dev))
     if st != 0:
         raise MambaError(st, "mamba_scan_fwd")
     return y, h_last
 
 
 def mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None,
-                       discretization: str = "euler"):
-    """One decode step; h (batch, d_inner, d_state) fp32 is updated in place.  Returns y."""
+                       discretization: str = "euler", lam=None, u_prev=None, B_prev=None,
+                       theta=None):
+    """One decode step; h (batch, d_inner, d_state) fp32 is updated in place.  Returns y.
+    lam, u_prev (batch, d_inner), B_prev (batch, d_state): the trapezoid with the previous
+    token's input; theta (batch, d_state / 2): rotation rates."""
     torch = _torch()
     lib = load_library()
     if u.dim() != 2:
@@ -266,9 +302,14 @@ def mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
     p_y = _ptr(y, "out", (batch, d_inner), act, dev)
     if discretization not in DISCRETIZATIONS:
         raise ValueError(f"discretization must be one of {sorted(DISCRETIZATIONS)}")
-    st = lib.mamba_state_update_ex(p_h, p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_y,
-                                   batch, d_inner, d_state, code,
-                                   DISCRETIZATIONS[discretization], _stream(dev))
+    ext = ScanExt(_ptr(lam, "lam", (batch, d_inner), act, dev),
+                  _ptr(u_prev, "u_prev", (batch, d_inner), act, dev),
+                  _ptr(B_prev, "B_prev", (batch, d_state), act, dev),
+                  _ptr(theta, "theta", (batch, d_state // 2), act, dev))
+    st = lib.mamba_state_update_ext(p_h, p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_y,
+                                    batch, d_inner, d_state, code,
+                                    DISCRETIZATIONS[discretization], ctypes.byref(ext),
+                                    _stream(dev))
     if st != 0:
         raise MambaError(st, "mamba_state_update")
     return y

@@ -76,6 +76,18 @@ __device__ __forceinline__ float zoh_input(float x, float abar, float du, float 
     return __builtin_fabsf(x) < 0.0625f ? small : large;
 }
 
+// Rotation of a state pair by the angle phi: (x, w) <- (cos phi x - sin phi w,
+// sin phi x + cos phi w).  sincosf is the accurate library routine (a few ulp over the
+// whole range), not the hardware v_sin/v_cos approximation.
+__device__ __forceinline__ void rotate_pair(float phi, float &x, float &w) {
+    float sn, cs;
+    sincosf(phi, &sn, &cs);
+    const float nx = __builtin_fmaf(cs, x, -sn * w);
+    const float nw = __builtin_fmaf(sn, x, cs * w);
+    x = nx;
+    w = nw;
+}
+
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z); e^-z = +inf gives -0 as the limit.
 __device__ __forceinline__ float silu_f(float z) {
     return z * hw_rcp(1.0f + hw_exp2(-z * kLog2e));

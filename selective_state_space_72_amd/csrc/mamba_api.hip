@@ -78,13 +78,14 @@ struct Plan {
     int64_t relay_tiles;  // relayed (batch row, tile) units
     int64_t relay_len;    // steps per relay part (a multiple of chunk)
     bool zoh;             // zero-order-hold discretisation (scalar family only)
+    bool trap, rot;       // exponential-trapezoidal input term, pair rotation (scalar family)
 };
 
 // Launch plan.  Channel tiles of 64 lanes x `waves` waves are the unit of parallel work;
 // when a single span cannot give every SIMD a few waves, the sequence is split into spans
 // (at most 64, each at least 256 steps) joined by the carry pass.
 mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                         const mamba_scan_opts_t *opts, Plan *plan)
+                         const mamba_scan_opts_t *opts, const mamba_scan_ext_t *ext, Plan *plan)
 {
     Plan p{};
     const int cus = cu_count();
@@ -93,11 +94,15 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     if (disc != MAMBA_DISC_EULER && disc != MAMBA_DISC_ZOH)
         return MAMBA_ERR_UNSUPPORTED;
     p.zoh = disc == MAMBA_DISC_ZOH;
+    p.trap = ext && ext->lambda;
+    p.rot = ext && ext->theta;
+    if (p.trap && p.zoh)
+        return MAMBA_ERR_UNSUPPORTED; // the trapezoid replaces the input term
     Family autof = auto_family(batch, d_inner, d_state, cus);
     if (autof == Family::Scalar && !scalar_span_ok(seqlen, d_inner))
         autof = Family::Rows;
-    if (p.zoh) {
-        // the zero-order hold is implemented in the scalar-B/C family only
+    if (p.zoh || p.trap || p.rot) {
+        // these options are implemented in the scalar-B/C family only
         if (fam == MAMBA_KERNEL_ROWS || fam == MAMBA_KERNEL_BLOCK)
             return MAMBA_ERR_UNSUPPORTED;
         autof = Family::Scalar;
@@ -106,7 +111,8 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
         // an explicit block shape: the scalar family if it has it, else the block family
         const int w = opts->waves ? opts->waves : scalar_default_waves(d_state);
         const int c = opts->chunk_len ? opts->chunk_len : scalar_default_chunk(d_state);
-        autof = scalar_variant_supported(d_state, w, c) || p.zoh ? Family::Scalar : Family::Block;
+        autof = scalar_variant_supported(d_state, w, c) || p.zoh || p.trap || p.rot
+                    ? Family::Scalar : Family::Block;
     }
     if (fam == MAMBA_KERNEL_ROWS || (fam == MAMBA_KERNEL_AUTO && autof == Family::Rows)) {
         if ((opts && (opts->waves || opts->chunk_len)))
@@ -130,13 +136,17 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     } else {
         return MAMBA_ERR_UNSUPPORTED;
     }
+    // the rotation turns state pairs (2k, 2k+1), which must sit in one wave; its span
+    // summaries would be 2x2 matrices, so the sequence is never split
+    if (p.rot && (d_state % 2 != 0 || (d_state / p.waves) % 2 != 0))
+        return MAMBA_ERR_UNSUPPORTED;
     const bool fixed_spans = opts && opts->n_spans;
     int spans = 1;
     if (fixed_spans) {
-        if (opts->n_spans < 1 || opts->n_spans > 64)
+        if (opts->n_spans < 1 || opts->n_spans > 64 || (p.rot && opts->n_spans != 1))
             return MAMBA_ERR_UNSUPPORTED;
         spans = opts->n_spans;
-    } else {
+    } else if (!p.rot) {
         const int64_t tiles = batch * ((d_inner + 63) / 64);
         const int64_t waves_per_span = tiles * p.waves;
         const int64_t want = (int64_t)cus * 4 /*SIMDs*/ * 4 /*waves each*/;
@@ -161,7 +171,7 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
             len = p.chunk;
         if (p.family != Family::Scalar || scalar_span_ok(len, d_inner))
             break;
-        if (fixed_spans || spans >= 64)
+        if (fixed_spans || spans >= 64 || p.rot)
             return MAMBA_ERR_UNSUPPORTED; // span too large for the scalar kernel's addressing
         spans *= 2;
     }
@@ -217,7 +227,8 @@ size_t staged_bytes_for(int64_t batch, int64_t seqlen, int64_t d_state, const Pl
     if (p.family != Family::Scalar || seqlen <= 0)
         return 0;
     const size_t rows = (size_t)seqlen + (size_t)p.chunk;
-    const size_t bytes = (size_t)batch * rows * 2 * (size_t)d_state * sizeof(float);
+    const size_t per_row = 2 * (size_t)d_state + (p.rot ? (size_t)d_state / 2 : 0); // B, C, theta
+    const size_t bytes = (size_t)batch * rows * per_row * sizeof(float);
     return (bytes + 255) / 256 * 256;
 }
 
@@ -363,17 +374,24 @@ const char *mamba_status_string(mamba_status_t s)
 
 int32_t mamba_d_state_supported(int64_t d_state) { return d_state_ok(d_state) ? 1 : 0; }
 
-size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_inner,
-                                        int64_t d_state, const mamba_scan_opts_t *opts)
+size_t mamba_scan_fwd_workspace_size_ext(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                         int64_t d_state, const mamba_scan_ext_t *ext,
+                                         const mamba_scan_opts_t *opts)
 {
     int64_t tmp;
     if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 ||
         !mul_ok(batch, d_inner, &tmp) || !mul_ok(tmp, d_state, &tmp) || !d_state_ok(d_state))
         return (size_t)-1;
     Plan p;
-    if (make_plan(batch, seqlen, d_inner, d_state, opts, &p) != MAMBA_OK)
+    if (make_plan(batch, seqlen, d_inner, d_state, opts, ext, &p) != MAMBA_OK)
         return (size_t)-1;
     return workspace_bytes_for(batch, seqlen, d_inner, d_state, p);
+}
+
+size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                        int64_t d_state, const mamba_scan_opts_t *opts)
+{
+    return mamba_scan_fwd_workspace_size_ext(batch, seqlen, d_inner, d_state, nullptr, opts);
 }
 
 size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
@@ -390,6 +408,23 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
                                  size_t workspace_bytes, const mamba_scan_opts_t *opts,
                                  void *stream)
 {
+    return mamba_scan_fwd_ext(u, delta, A, B, C, D, z, delta_bias, h0, y, h_last, batch, seqlen,
+                              d_inner, d_state, dtype, workspace, workspace_bytes, opts, nullptr,
+                              stream);
+}
+
+mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float *A,
+                                  const void *B, const void *C, const float *D, const void *z,
+                                  const float *delta_bias, const float *h0, void *y,
+                                  float *h_last, int64_t batch, int64_t seqlen, int64_t d_inner,
+                                  int64_t d_state, mamba_dtype_t dtype, void *workspace,
+                                  size_t workspace_bytes, const mamba_scan_opts_t *opts,
+                                  const mamba_scan_ext_t *ext, void *stream)
+{
+    const void *lam = ext ? ext->lambda : nullptr;
+    const void *u_prev = lam ? ext->u_prev : nullptr; // used by the trapezoid only
+    const void *B_prev = lam ? ext->B_prev : nullptr;
+    const void *theta = ext ? ext->theta : nullptr;
     // ---- sizes and dtype ----
     if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0)
         return MAMBA_ERR_BAD_SHAPE;
@@ -414,7 +449,7 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
         return MAMBA_ERR_NULL_ARG;
 
     // ---- alignment ----
-    const void *elem_ptrs[] = {u, delta, B, C, z, y};
+    const void *elem_ptrs[] = {u, delta, B, C, z, y, lam, u_prev, B_prev, theta};
     for (const void *p : elem_ptrs)
         if (p && !aligned(p, (size_t)es))
             return MAMBA_ERR_MISALIGNED;
@@ -425,7 +460,7 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
 
     // ---- plan and workspace ----
     Plan plan;
-    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, d_state, opts, &plan);
+    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, d_state, opts, ext, &plan);
     if (ps != MAMBA_OK)
         return ps;
     const size_t need = workspace_bytes_for(batch, seqlen, d_inner, d_state, plan);
@@ -438,7 +473,10 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
     const Range r_in[] = {range_of(u, bld * es),       range_of(delta, bld * es),
                           range_of(z, bld * es),       range_of(B, bln * es),
                           range_of(C, bln * es),       range_of(A, dn * 4),
-                          range_of(D, d_inner * 4),    range_of(delta_bias, d_inner * 4)};
+                          range_of(D, d_inner * 4),    range_of(delta_bias, d_inner * 4),
+                          range_of(lam, bld * es),     range_of(u_prev, batch * d_inner * es),
+                          range_of(B_prev, batch * d_state * es),
+                          range_of(theta, bln / 2 * es)};
     const Range r_h0 = range_of(h0, bdn * 4);
     const Range r_y = range_of(has_seq ? y : nullptr, bld * es);
     const Range r_hl = range_of(h_last, bdn * 4);
@@ -483,6 +521,12 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
     L.chunk = plan.chunk;
     L.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
     L.zoh = plan.zoh;
+    L.trap = plan.trap;
+    L.rot = plan.rot;
+    L.lam = lam;
+    L.u_prev = u_prev;
+    L.B_prev = B_prev;
+    L.theta = theta;
 
     auto full = [&](const ScanLaunch &x) {
         switch (plan.family) {
@@ -588,7 +632,24 @@ mamba_status_t mamba_state_update_ex(float *h, const void *u, const void *delta,
                                      void *y, int64_t batch, int64_t d_inner, int64_t d_state,
                                      mamba_dtype_t dtype, int32_t discretization, void *stream)
 {
+    return mamba_state_update_ext(h, u, delta, A, B, C, D, z, delta_bias, y, batch, d_inner,
+                                  d_state, dtype, discretization, nullptr, stream);
+}
+
+mamba_status_t mamba_state_update_ext(float *h, const void *u, const void *delta,
+                                      const float *A, const void *B, const void *C,
+                                      const float *D, const void *z, const float *delta_bias,
+                                      void *y, int64_t batch, int64_t d_inner, int64_t d_state,
+                                      mamba_dtype_t dtype, int32_t discretization,
+                                      const mamba_scan_ext_t *ext, void *stream)
+{
+    const void *lam = ext ? ext->lambda : nullptr;
+    const void *u_prev = lam ? ext->u_prev : nullptr;
+    const void *B_prev = lam ? ext->B_prev : nullptr;
+    const void *theta = ext ? ext->theta : nullptr;
     if (discretization != MAMBA_DISC_EULER && discretization != MAMBA_DISC_ZOH)
+        return MAMBA_ERR_UNSUPPORTED;
+    if ((lam && discretization == MAMBA_DISC_ZOH) || (theta && d_state % 2 != 0))
         return MAMBA_ERR_UNSUPPORTED;
     if (batch < 0 || d_inner < 0 || d_state <= 0)
         return MAMBA_ERR_BAD_SHAPE;
@@ -607,7 +668,7 @@ mamba_status_t mamba_state_update_ex(float *h, const void *u, const void *delta,
     if (!h || !u || !delta || !A || !B || !C || !y)
         return MAMBA_ERR_NULL_ARG;
 
-    const void *elem_ptrs[] = {u, delta, B, C, z, y};
+    const void *elem_ptrs[] = {u, delta, B, C, z, y, lam, u_prev, B_prev, theta};
     for (const void *p : elem_ptrs)
         if (p && !aligned(p, (size_t)es))
             return MAMBA_ERR_MISALIGNED;
@@ -618,7 +679,9 @@ mamba_status_t mamba_state_update_ex(float *h, const void *u, const void *delta,
     const Range r_in[] = {range_of(u, bd * es),       range_of(delta, bd * es),
                           range_of(z, bd * es),       range_of(B, bn * es),
                           range_of(C, bn * es),       range_of(A, dn * 4),
-                          range_of(D, d_inner * 4),   range_of(delta_bias, d_inner * 4)};
+                          range_of(D, d_inner * 4),   range_of(delta_bias, d_inner * 4),
+                          range_of(lam, bd * es),     range_of(u_prev, bd * es),
+                          range_of(B_prev, bn * es),  range_of(theta, bn / 2 * es)};
     const Range r_h = range_of(h, bdn * 4);
     const Range r_y = range_of(y, bd * es);
     if (overlaps(r_h, r_y))
@@ -643,6 +706,12 @@ mamba_status_t mamba_state_update_ex(float *h, const void *u, const void *delta,
     S.d_state = d_state;
     S.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
     S.zoh = discretization == MAMBA_DISC_ZOH;
+    S.trap = lam != nullptr;
+    S.rot = theta != nullptr;
+    S.lam = lam;
+    S.u_prev = u_prev;
+    S.B_prev = B_prev;
+    S.theta = theta;
     return hip_status(launch_state_update(S, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -37,6 +37,12 @@ struct ScanLaunch {
     int32_t relay_tiles, relay_parts;
     int64_t relay_len;
     bool zoh; // zero-order-hold Bbar (scalar family); Euler otherwise
+    // Options of the Mamba-3 formulation (scalar family; NULL / false = off):
+    // exponential-trapezoidal input term with mixing coefficients lam (B,L,D) and the input
+    // before t = 0 in u_prev (B,D), B_prev (B,N); rotation of state pairs by Delta * theta,
+    // theta (B,L,N/2) staged next to B and C.
+    bool trap, rot;
+    const void *lam, *u_prev, *B_prev, *theta;
 };
 
 // Relay arguments as the scan kernel receives them.
@@ -79,6 +85,9 @@ struct StepLaunch {
     int64_t batch, d_inner, d_state;
     DType dtype;
     bool zoh;
+    bool trap, rot;                          // as in ScanLaunch
+    const void *lam, *u_prev, *B_prev;       // (B,D), (B,D), (B,N)
+    const void *theta;                       // (B,N/2)
 };
 
 // Returns true if the (d_state, waves, chunk) combination is compiled in.

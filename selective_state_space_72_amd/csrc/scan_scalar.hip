@@ -33,15 +33,18 @@ __device__ __forceinline__ void for_c(F &&f)
     }
 }
 
-// bcp[((b * NW + g) * Lp + t) * 2 NQ + {q, NQ + q}] = {B, C}[b, t, g * NQ + q] (0 past L).
-// Also zeroes the relay hand-off flags (n_sync words) for the scan launch that follows on
-// the same stream.
-template <typename T, int N, int NW>
+// bcp[((b * NW + g) * Lp + t) * BCW + {q, NQ + q}] = {B, C}[b, t, g * NQ + q] (0 past L),
+// BCW = 2 NQ; with rotation rates (ROT) also bcp[... + 2 NQ + q / 2] = theta[b, t, (g NQ + q)
+// / 2] for even q, BCW = 2 NQ + NQ / 2.  Also zeroes the relay hand-off flags (n_sync
+// words) for the scan launch that follows on the same stream.
+template <typename T, int N, int NW, bool ROT>
 __global__ void __launch_bounds__(256)
-stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, float *__restrict__ bcp,
-                int64_t L, int64_t Lp, int64_t total, uint32_t *__restrict__ sync, int32_t n_sync)
+stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, const T *__restrict__ th,
+                float *__restrict__ bcp, int64_t L, int64_t Lp, int64_t total,
+                uint32_t *__restrict__ sync, int32_t n_sync)
 {
     constexpr int NQ = N / NW;
+    constexpr int BCW = 2 * NQ + (ROT ? NQ / 2 : 0);
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; // over batch * Lp * N
     if (i < n_sync)
         sync[i] = 0u;
@@ -56,9 +59,13 @@ stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, float *__res
         bv = load_val(Bm, (b * L + t) * N + n);
         cv = load_val(Cm, (b * L + t) * N + n);
     }
-    float *dst = bcp + ((b * NW + g) * Lp + t) * (2 * NQ);
+    float *dst = bcp + ((b * NW + g) * Lp + t) * BCW;
     dst[q] = bv;
     dst[NQ + q] = cv;
+    if constexpr (ROT) {
+        if (q % 2 == 0)
+            dst[2 * NQ + q / 2] = t < L ? load_val(th, (b * L + t) * (N / 2) + n / 2) : 0.0f;
+    }
 }
 
 // Activations of one (batch row, span) are read and written through buffer resources
@@ -106,7 +113,15 @@ __device__ __forceinline__ void relay_wait(uint32_t *flag)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED, bool ZOH>
+// Inputs of the Mamba-3 options: trapezoid mixing coefficients lam (as u), the input
+// before t = 0 (u_prev (B,D), B_prev (B,N); NULL = 0) and B itself for the look-back at
+// a span's or relay part's first step.
+struct Mamba3Args {
+    const void *lam, *u_prev, *B_prev, *Bm;
+};
+
+// DISC: 0 Euler, 1 zero-order hold, 2 exponential-trapezoidal; ROT: rotation of state pairs.
+template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED, int DISC, bool ROT>
 __global__ void __launch_bounds__(64 * NW)
 scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                    const T *__restrict__ z, const float *__restrict__ bcp,
@@ -115,20 +130,23 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                    T *__restrict__ y, float *h_last, float *__restrict__ ws_decay,
                    float *__restrict__ ws_hloc, int64_t L, int64_t Lp, int32_t Dn,
                    int64_t span_len, int32_t n_spans, int32_t first_span, int32_t tiles,
-                   int32_t batch, RelayArgs relay)
+                   int32_t batch, RelayArgs relay, Mamba3Args m3)
 {
+    constexpr bool ZOH = DISC == 1, TRAP = DISC == 2;
     constexpr int NQ = N / NW;                 // state indices per lane
     constexpr int KPL = (TC + NW - 1) / NW;    // prologue/epilogue channel-steps per lane
-    constexpr int BCW = 2 * NQ;                // B then C, per step, in bcp
+    constexpr int BCW = 2 * NQ + (ROT ? NQ / 2 : 0); // B, C (and theta) per step, in bcp
     constexpr bool gated = FULL && GATED;
     static_assert(NQ >= 1 && N % NW == 0, "bad variant");
+    static_assert(!ROT || NQ % 2 == 0, "rotation needs whole state pairs per wave");
     static_assert(PD % 2 == 0, "ring slots double as chunk parity");
 
     // Double-buffered by chunk parity so that one barrier per chunk suffices: chunk c's
     // prologue writes s_dw[c&1]; after the barrier every wave finishes chunk c-1 from
     // s_yp[(c-1)&1] and scans chunk c into s_yp[c&1].
-    // (Delta, Delta*u) per (step, channel); with the zero-order hold also u
-    typedef typename std::conditional<ZOH, float4, float2>::type DW;
+    // (Delta, Delta*u) per (step, channel); with the zero-order hold also u; with the
+    // trapezoid (Delta, lam Delta u, (1 - lam) Delta, u)
+    typedef typename std::conditional<ZOH || TRAP, float4, float2>::type DW;
     __shared__ DW s_dw[2][TC][64];
     __shared__ float s_yp[FULL ? 2 : 1][TC][NW][64]; // partial readouts per (step, wave, channel)
 
@@ -203,6 +221,28 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     const float bias_d = bias ? bias[dc] : 0.0f;
     const float D_d = Dv ? Dv[dc] : 0.0f;
 
+    // trapezoid look-back: the input (u, B) of the step before this span's first step
+    float u_lb = 0.0f, b_lb[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+        b_lb[q] = 0.0f;
+    if constexpr (TRAP) {
+        if (t_begin > 0) {
+            u_lb = load_val(u, ((int64_t)b * L + t_begin - 1) * Dn + dc);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                b_lb[q] = load_val((const T *)m3.Bm, ((int64_t)b * L + t_begin - 1) * N + n0 + q);
+        } else {
+            if (m3.u_prev)
+                u_lb = load_val((const T *)m3.u_prev, (int64_t)b * Dn + dc);
+            if (m3.B_prev) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    b_lb[q] = load_val((const T *)m3.B_prev, (int64_t)b * N + n0 + q);
+            }
+        }
+    }
+
     // bytes per time step of one batch row; span bytes stay below 2^31 (planner)
     const uint32_t step_bytes = (uint32_t)Dn * (uint32_t)sizeof(T);
     const uint32_t vo_in = (uint32_t)dc * (uint32_t)sizeof(T);
@@ -215,6 +255,9 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     const rsrc_t r_d = make_rsrc(reinterpret_cast<const char *>(delta) + span0, span_bytes);
     const rsrc_t r_z = gated ? make_rsrc(reinterpret_cast<const char *>(z) + span0, span_bytes)
                              : r_u;
+    const rsrc_t r_l = TRAP ? make_rsrc(reinterpret_cast<const char *>(m3.lam) + span0,
+                                        span_bytes)
+                            : r_u;
     const rsrc_t r_y = FULL ? make_rsrc(reinterpret_cast<const char *>(y) + span0, span_bytes)
                             : r_u;
     // this wave's (t, B/C) rows from the span's first step
@@ -223,7 +266,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     // raw inputs of PD chunks in flight: u, delta, z for this lane's KPL channel-steps
     // (zeroed so that the prologue may process the unloaded steps of a last, partial chunk:
     // their values are computed and never used)
-    T ru[PD][KPL] = {}, rd[PD][KPL] = {}, rz[PD][KPL] = {};
+    T ru[PD][KPL] = {}, rd[PD][KPL] = {}, rz[PD][KPL] = {}, rl[PD][KPL] = {};
     auto fetch = [&](auto BUF, int t0) {
         constexpr int j = decltype(BUF)::value;
 #pragma unroll
@@ -236,6 +279,8 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                 rd[j][k] = buf_load(r_d, vo_in, so, (T *)nullptr);
                 if (gated)
                     rz[j][k] = buf_load(r_z, vo_in, so, (T *)nullptr);
+                if (TRAP)
+                    rl[j][k] = buf_load(r_l, vo_in, so, (T *)nullptr);
             }
         }
     };
@@ -308,10 +353,14 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
             du[k] = FULL ? D_d * uu : 0.0f;
             gz[k] = gated ? silu_f(widen(rz[j][k])) : 1.0f;
             if (tl < TC) {
-                if constexpr (ZOH)
+                if constexpr (ZOH) {
                     s_dw[pp][tl][lane] = make_float4(dl, dl * uu, uu, 0.0f);
-                else
+                } else if constexpr (TRAP) {
+                    const float lm = widen(rl[j][k]);
+                    s_dw[pp][tl][lane] = make_float4(dl, lm * dl * uu, (1.0f - lm) * dl, uu);
+                } else {
                     s_dw[pp][tl][lane] = make_float2(dl, dl * uu);
+                }
             }
         }
         if (t0 + PD * TC < n_loc)
@@ -330,13 +379,28 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
         // ---- recurrence over the chunk ----
         auto step = [&](int tl) {
             float yp = 0.0f;
+            if constexpr (ROT) {
+                // rotate each state pair by Delta * theta before the decay
+#pragma unroll
+                for (int k = 0; k < NQ / 2; ++k)
+                    rotate_pair(dw[tl].x * bcs[tl][2 * NQ + k], h[2 * k], h[2 * k + 1]);
+            }
+            // trapezoid: (1 - lam) Delta u_{t-1}, from the previous step (or the carry)
+            float p_lb = 0.0f;
+            if constexpr (TRAP)
+                p_lb = dw[tl].z * (tl == 0 ? u_lb : dw[tl > 0 ? tl - 1 : 0].w);
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const float a = decay_exp2(dw[tl].x, a2[q]);
-                float bu = dw[tl].y; // Bbar u / B: Euler Delta u
+                float bu = dw[tl].y; // Bbar u / B: Euler Delta u (trapezoid: lam Delta u)
                 if constexpr (ZOH)
                     bu = zoh_input(dw[tl].x * an[q], a, dw[tl].y, dw[tl].z * ia[q]);
-                h[q] = __builtin_fmaf(a, h[q], bu * bcs[tl][q]);
+                if constexpr (TRAP) {
+                    const float bp = tl == 0 ? b_lb[q] : bcs[tl > 0 ? tl - 1 : 0][q];
+                    h[q] = __builtin_fmaf(a, h[q], __builtin_fmaf(p_lb, bp, bu * bcs[tl][q]));
+                } else {
+                    h[q] = __builtin_fmaf(a, h[q], bu * bcs[tl][q]);
+                }
                 if (FULL)
                     yp = __builtin_fmaf(bcs[tl][NQ + q], h[q], yp);
             }
@@ -354,6 +418,13 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
             for (int tl = 0; tl < TC; ++tl)
                 if (tl < nt)
                     step(tl);
+        }
+        if constexpr (TRAP) {
+            // look-back of the next chunk's first step (only a full chunk has a next one)
+            u_lb = dw[TC - 1].w;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                b_lb[q] = bcs[TC - 1][q];
         }
         __builtin_amdgcn_sched_barrier(0);
         if (t0 + TC < n_loc)
@@ -435,7 +506,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     X(16, 8, 8, 2)               \
     X(32, 8, 4, 2)
 
-template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED, bool ZOH>
+template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED, int DISC, bool ROT>
 hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
 {
     const int32_t tiles = (int32_t)((p.d_inner + 63) / 64);
@@ -453,12 +524,13 @@ hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
     }
     if (blocks <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL((scan_scalar_kernel<T, N, NW, TC, PD, FULL, GATED, ZOH>),
+    Mamba3Args m3{p.lam, p.u_prev, p.B_prev, p.B};
+    hipLaunchKernelGGL((scan_scalar_kernel<T, N, NW, TC, PD, FULL, GATED, DISC, ROT>),
                        dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, (const T *)p.u,
                        (const T *)p.delta, (const T *)p.z, p.bc_staged, p.A, p.D, p.bias,
                        p.h_init, p.h_init_span_stride, (T *)p.y, p.h_last, p.ws_decay,
                        p.ws_hloc, p.L, p.staged_rows, (int32_t)p.d_inner, p.span_len,
-                       p.n_spans, p.first_span, tiles, (int32_t)p.batch, relay);
+                       p.n_spans, p.first_span, tiles, (int32_t)p.batch, relay, m3);
     return hipGetLastError();
 }
 
@@ -470,21 +542,47 @@ hipError_t launch_stage(const ScanLaunch &p, hipStream_t stream)
     const int64_t blocks = (max(total, (int64_t)n_sync) + 255) / 256;
     if (blocks <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL((stage_bc_kernel<T, N, NW>), dim3((uint32_t)blocks), dim3(256), 0,
-                       stream, (const T *)p.B, (const T *)p.C, p.bc_staged, p.L, p.staged_rows,
-                       total, p.relay_sync, n_sync);
+    if (p.rot) {
+        if constexpr ((N / NW) % 2 == 0)
+            hipLaunchKernelGGL((stage_bc_kernel<T, N, NW, true>), dim3((uint32_t)blocks),
+                               dim3(256), 0, stream, (const T *)p.B, (const T *)p.C,
+                               (const T *)p.theta, p.bc_staged, p.L, p.staged_rows, total,
+                               p.relay_sync, n_sync);
+        else
+            return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((stage_bc_kernel<T, N, NW, false>), dim3((uint32_t)blocks), dim3(256),
+                           0, stream, (const T *)p.B, (const T *)p.C, (const T *)nullptr,
+                           p.bc_staged, p.L, p.staged_rows, total, p.relay_sync, n_sync);
+    }
     return hipGetLastError();
+}
+
+// Rotation is compiled for the full-output pass of variants whose waves hold whole state
+// pairs (the span summaries of the split sequence have no rotation form).
+template <typename T, int N, int NW, int TC, int PD, bool FULL, int DISC>
+hipError_t launch_scalar_disc(const ScanLaunch &p, hipStream_t stream)
+{
+    const bool g = FULL && p.z != nullptr;
+    if (p.rot) {
+        if constexpr (FULL && (N / NW) % 2 == 0)
+            return g ? launch_scalar_variant<T, N, NW, TC, PD, FULL, true, DISC, true>(p, stream)
+                     : launch_scalar_variant<T, N, NW, TC, PD, FULL, false, DISC, true>(p, stream);
+        else
+            return hipErrorInvalidValue;
+    }
+    return g ? launch_scalar_variant<T, N, NW, TC, PD, FULL, true, DISC, false>(p, stream)
+             : launch_scalar_variant<T, N, NW, TC, PD, FULL, false, DISC, false>(p, stream);
 }
 
 template <typename T, int N, int NW, int TC, int PD, bool FULL>
 hipError_t launch_scalar_opts(const ScanLaunch &p, hipStream_t stream)
 {
-    const bool g = FULL && p.z != nullptr;
+    if (p.trap)
+        return launch_scalar_disc<T, N, NW, TC, PD, FULL, 2>(p, stream);
     if (p.zoh)
-        return g ? launch_scalar_variant<T, N, NW, TC, PD, FULL, true, true>(p, stream)
-                 : launch_scalar_variant<T, N, NW, TC, PD, FULL, false, true>(p, stream);
-    return g ? launch_scalar_variant<T, N, NW, TC, PD, FULL, true, false>(p, stream)
-             : launch_scalar_variant<T, N, NW, TC, PD, FULL, false, false>(p, stream);
+        return launch_scalar_disc<T, N, NW, TC, PD, FULL, 1>(p, stream);
+    return launch_scalar_disc<T, N, NW, TC, PD, FULL, 0>(p, stream);
 }
 
 template <bool FULL>

@@ -11,18 +11,30 @@
 // consecutive addresses.  The N/4 lanes of a channel each compute the per-channel softplus
 // and gate (spare VALU in a memory-bound kernel) and combine their partial readouts with a
 // butterfly over N/4 lanes in a fixed order; the first lane of the channel stores y.
+//
+// Options (the Mamba-3 section of "State space models and the Mamba series", jsqmd.com,
+// sections 2.1 and 2.2): the exponential-trapezoidal input term (1 - lam) Delta
+// B_prev u_prev + lam Delta B u, with the previous token's u and B supplied by the caller,
+// and the rotation of each state pair (2k, 2k+1) by Delta theta[k] before the decay (the
+// pairs of a lane's 4 states are its own).
 #include "device_math.h"
 #include "scan_common.h"
 
 namespace mambascan {
 
-template <typename T, int N, bool ZOH>
+struct StepExt {
+    const void *lam, *u_prev, *B_prev, *theta; // (B,D), (B,D), (B,N), (B,N/2); rows of this launch
+};
+
+// DISC: 0 Euler, 1 zero-order hold, 2 exponential-trapezoidal; ROT: pair rotation.
+template <typename T, int N, int DISC, bool ROT>
 __global__ void __launch_bounds__(256)
 state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__restrict__ delta,
                     const T *__restrict__ z, const T *__restrict__ Bm, const T *__restrict__ Cm,
                     const float *__restrict__ A, const float *__restrict__ Dv,
-                    const float *__restrict__ bias, T *__restrict__ y, int32_t Dn)
+                    const float *__restrict__ bias, T *__restrict__ y, int32_t Dn, StepExt ext)
 {
+    constexpr bool ZOH = DISC == 1, TRAP = DISC == 2;
     constexpr int LPC = N / 4; // lanes per channel
     static_assert(N % 4 == 0 && LPC <= 64, "bad d_state");
     const int b = blockIdx.y;
@@ -42,8 +54,19 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
     const int64_t bn = (int64_t)b * N + 4 * q;
 
     float hn[4];
-    const float hin[4] = {hv.x, hv.y, hv.z, hv.w};
+    float hin[4] = {hv.x, hv.y, hv.z, hv.w};
     const float ain[4] = {av.x, av.y, av.z, av.w};
+    if constexpr (ROT) {
+#pragma unroll
+        for (int k = 0; k < 4; k += 2)
+            rotate_pair(dl * load_val((const T *)ext.theta, ((int64_t)b * N + 4 * q + k) / 2),
+                        hin[k], hin[k + 1]);
+    }
+    float lm = 1.0f, p_lb = 0.0f;
+    if constexpr (TRAP) {
+        lm = load_val((const T *)ext.lam, c);
+        p_lb = (1.0f - lm) * dl * (ext.u_prev ? load_val((const T *)ext.u_prev, c) : 0.0f);
+    }
     float yp = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -51,7 +74,13 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
         float bu = w; // Bbar u / B: Euler Delta u, or the zero-order hold
         if constexpr (ZOH)
             bu = zoh_input(dl * ain[k], a, w, uu / ain[k]);
-        hn[k] = __builtin_fmaf(a, hin[k], bu * load_val(Bm, bn + k));
+        if constexpr (TRAP) {
+            const float bp = ext.B_prev ? load_val((const T *)ext.B_prev, bn + k) : 0.0f;
+            hn[k] = __builtin_fmaf(a, hin[k],
+                                   __builtin_fmaf(p_lb, bp, lm * w * load_val(Bm, bn + k)));
+        } else {
+            hn[k] = __builtin_fmaf(a, hin[k], bu * load_val(Bm, bn + k));
+        }
         yp = __builtin_fmaf(load_val(Cm, bn + k), hn[k], yp);
     }
 #pragma unroll
@@ -69,7 +98,7 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
     }
 }
 
-template <typename T, int N, bool ZOH>
+template <typename T, int N, int DISC, bool ROT>
 static hipError_t launch_step(const StepLaunch &p, hipStream_t stream)
 {
     constexpr int LPC = N / 4;
@@ -79,17 +108,40 @@ static hipError_t launch_step(const StepLaunch &p, hipStream_t stream)
     for (int64_t b0 = 0; b0 < p.batch; b0 += 65535) {
         const int64_t nb = p.batch - b0 < 65535 ? p.batch - b0 : 65535;
         const int64_t off_bd = b0 * p.d_inner, off_bn = b0 * N;
-        hipLaunchKernelGGL((state_update_kernel<T, N, ZOH>), dim3(gx, (uint32_t)nb), dim3(256), 0,
-                           stream, p.h + off_bd * N, (const T *)p.u + off_bd,
+        StepExt ext{};
+        ext.lam = p.lam ? (const T *)p.lam + off_bd : nullptr;
+        ext.u_prev = p.u_prev ? (const T *)p.u_prev + off_bd : nullptr;
+        ext.B_prev = p.B_prev ? (const T *)p.B_prev + off_bn : nullptr;
+        ext.theta = p.theta ? (const T *)p.theta + b0 * (N / 2) : nullptr;
+        hipLaunchKernelGGL((state_update_kernel<T, N, DISC, ROT>), dim3(gx, (uint32_t)nb),
+                           dim3(256), 0, stream, p.h + off_bd * N, (const T *)p.u + off_bd,
                            (const T *)p.delta + off_bd,
                            p.z ? (const T *)p.z + off_bd : nullptr, (const T *)p.B + off_bn,
                            (const T *)p.C + off_bn, p.A, p.D, p.bias, (T *)p.y + off_bd,
-                           (int32_t)p.d_inner);
+                           (int32_t)p.d_inner, ext);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
     return hipSuccess;
+}
+
+template <typename T, int N>
+static hipError_t launch_step_opts(const StepLaunch &p, hipStream_t stream)
+{
+    const int disc = p.trap ? 2 : p.zoh ? 1 : 0;
+    if (p.rot) {
+        switch (disc) {
+        case 2: return launch_step<T, N, 2, true>(p, stream);
+        case 1: return launch_step<T, N, 1, true>(p, stream);
+        default: return launch_step<T, N, 0, true>(p, stream);
+        }
+    }
+    switch (disc) {
+    case 2: return launch_step<T, N, 2, false>(p, stream);
+    case 1: return launch_step<T, N, 1, false>(p, stream);
+    default: return launch_step<T, N, 0, false>(p, stream);
+    }
 }
 
 hipError_t launch_state_update(const StepLaunch &p, hipStream_t stream)
@@ -99,10 +151,8 @@ hipError_t launch_state_update(const StepLaunch &p, hipStream_t stream)
 #define STEP_CASE(N_)                                                   \
     if (p.d_state == N_) {                                              \
         if (p.dtype == DType::BF16)                                     \
-            return p.zoh ? launch_step<uint16_t, N_, true>(p, stream)   \
-                         : launch_step<uint16_t, N_, false>(p, stream); \
-        return p.zoh ? launch_step<float, N_, true>(p, stream)          \
-                     : launch_step<float, N_, false>(p, stream);        \
+            return launch_step_opts<uint16_t, N_>(p, stream);           \
+        return launch_step_opts<float, N_>(p, stream);                  \
     }
     STEP_CASE(4)
     STEP_CASE(8)

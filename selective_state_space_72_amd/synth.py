@@ -317,3 +317,40 @@ def make_upstream_grads(cfg: ScanConfig, with_dh_last: bool = True) -> UpstreamG
     dhl = (_normal(cfg.seed, (7,), (cfg.batch, cfg.d_inner, cfg.d_state), F32)
            if with_dh_last else None)
     return UpstreamGrads(dy=dy, dh_last=dhl)
+
+
+# ----------------------------------------------------------------------------
+# inputs of the Mamba-3 options (exponential-trapezoidal rule, rotation)
+# ----------------------------------------------------------------------------
+
+def _uniform01(seed: int, key: tuple, shape, dtype: str) -> np.ndarray:
+    """U(0, 1) float32 draws for tensor `key`, blocked and seeded like _normal."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16 if dtype == BF16 else np.float32)
+    for j in range((n + BLOCK - 1) // BLOCK):
+        lo, hi = j * BLOCK, min(n, (j + 1) * BLOCK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=tuple(key) + (j,))))
+        x = g.random(hi - lo, dtype=np.float32)
+        out[lo:hi] = f32_to_bf16_bits(x) if dtype == BF16 else x
+    return out.reshape(shape)
+
+
+@dataclasses.dataclass
+class Mamba3Inputs:
+    lam: np.ndarray      # (batch, L, d_inner) stored dtype: trapezoid mixing, U(0, 1)
+    theta: np.ndarray    # (batch, L, d_state // 2) stored dtype: rotation rates, N(0, 1)
+    u_prev: np.ndarray   # (batch, d_inner) stored dtype: input before t = 0, N(0, 1)
+    B_prev: np.ndarray   # (batch, d_state) stored dtype: its B, N(0, 1)
+
+
+def make_mamba3_inputs(cfg: ScanConfig) -> Mamba3Inputs:
+    """Tensor ids 8 (lam), 9 (theta), 10 (u_prev), 11 (B_prev) of the config's seed.  The
+    page gives lam in [0, 1] (initial value 0.5) and no scale for theta; theta is drawn
+    like the other projections (standard normal), so Delta * theta spans small and large
+    angles over the configs' Delta range."""
+    sd = cfg.seed
+    return Mamba3Inputs(
+        lam=_uniform01(sd, (8,), (cfg.batch, cfg.seqlen, cfg.d_inner), cfg.dtype),
+        theta=_normal(sd, (9,), (cfg.batch, cfg.seqlen, cfg.d_state // 2), cfg.dtype),
+        u_prev=_normal(sd, (10,), (cfg.batch, cfg.d_inner), cfg.dtype),
+        B_prev=_normal(sd, (11,), (cfg.batch, cfg.d_state), cfg.dtype))

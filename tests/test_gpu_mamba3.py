@@ -1,0 +1,178 @@
+"""GPU parity of the Mamba-3 options against the fp64 oracle: the exponential-trapezoidal
+input term (mixing coefficients lam, look-back input u_prev/B_prev) and the data-dependent
+rotation of state pairs (theta), in the scan and in the decode step.
+
+Shapes span several chunks and 64-channel tiles with ragged tails; the trapezoid is also
+run with the sequence split into spans and with the relay (its look-back crosses those
+boundaries), the rotation with the relay.  Tolerances as for the scan: metric M of
+gpu_helpers, 1e-5 for fp32 inputs, 2e-2 for bf16 inputs.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_72_amd as ms
+from selective_state_space_72_amd import synth
+from gpu_helpers import TOL, from_dev, log, metric, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def make_case(base, *, batch, seqlen, d_inner, d_state=16, gate=None, h0=None):
+    cfg = synth.CONFIGS[base]
+    cfg = dataclasses.replace(cfg, batch=batch, seqlen=seqlen, d_inner=d_inner, d_state=d_state,
+                              gate=cfg.gate if gate is None else gate,
+                              h0=cfg.h0 if h0 is None else h0)
+    inp = synth.make_scan_inputs(cfg)
+    return inp, synth.make_mamba3_inputs(inp.cfg)
+
+
+def run_gpu(inp, m3, *, trap, rot, prev=True, **opts):
+    p = inp.params
+    y, h = ms.mamba_scan_fwd(to_dev(inp.u), to_dev(inp.delta), to_dev(p.A), to_dev(inp.B),
+                             to_dev(inp.C), D=to_dev(p.D), z=to_dev(inp.z),
+                             delta_bias=to_dev(p.bias), h0=to_dev(inp.h0),
+                             return_last_state=True,
+                             lam=to_dev(m3.lam) if trap else None,
+                             u_prev=to_dev(m3.u_prev) if (trap and prev) else None,
+                             B_prev=to_dev(m3.B_prev) if (trap and prev) else None,
+                             theta=to_dev(m3.theta) if rot else None, **opts)
+    torch.cuda.synchronize()
+    return from_dev(y), from_dev(h)
+
+
+def run_oracle(inp, m3, *, trap, rot, prev=True, zoh=False):
+    f = lambda a: synth.to_f64(a, inp.dtype)  # noqa: E731
+    p = inp.params
+    return oracle.load().scan(
+        f(inp.u), f(inp.delta), p.A.astype(np.float64), f(inp.B), f(inp.C),
+        D=p.D.astype(np.float64), z=f(inp.z), bias=p.bias.astype(np.float64),
+        h0=inp.h0.astype(np.float64) if inp.h0 is not None else None, zoh=zoh,
+        lam=f(m3.lam) if trap else None,
+        u_prev=f(m3.u_prev) if (trap and prev) else None,
+        B_prev=f(m3.B_prev) if (trap and prev) else None,
+        theta=f(m3.theta) if rot else None)
+
+
+def check(inp, m3, label, *, trap, rot, prev=True, **opts):
+    log(f"case {label}: batch {inp.cfg.batch} L {inp.cfg.seqlen} D {inp.cfg.d_inner} "
+        f"N {inp.cfg.d_state} {inp.dtype} trap {trap} rot {rot} {opts}")
+    y, h = run_gpu(inp, m3, trap=trap, rot=rot, prev=prev, **opts)
+    yr, hr = run_oracle(inp, m3, trap=trap, rot=rot, prev=prev,
+                        zoh=opts.get("discretization") == "zoh")
+    ey, eh = metric(y, yr), metric(h, hr)
+    log(f"{label}: y {ey:.2e}, h_last {eh:.2e}")
+    tol = TOL[inp.dtype]
+    assert np.all(np.isfinite(y)) and ey <= tol and eh <= tol, (label, ey, eh)
+
+
+# ---- exponential-trapezoidal rule ---------------------------------------------------
+
+@pytest.mark.parametrize("d_state", [4, 8, 16, 32])
+def test_trapezoid_fp32(d_state):
+    inp, m3 = make_case("c1", batch=2, seqlen=77, d_inner=96, d_state=d_state, gate=True,
+                        h0=True)
+    check(inp, m3, f"trapezoid fp32 N={d_state}", trap=True, rot=False)
+
+
+def test_trapezoid_without_prev_bf16():
+    inp, m3 = make_case("c3", batch=2, seqlen=300, d_inner=160)
+    check(inp, m3, "trapezoid bf16, zero look-back at t = 0", trap=True, rot=False, prev=False)
+
+
+@pytest.mark.parametrize("n_spans", [2, 5])
+def test_trapezoid_spans(n_spans):
+    inp, m3 = make_case("c1", batch=1, seqlen=203, d_inner=70, gate=True, h0=True)
+    check(inp, m3, f"trapezoid fp32, {n_spans} spans", trap=True, rot=False, n_spans=n_spans)
+
+
+def test_trapezoid_relay():
+    inp, m3 = make_case("c1", batch=2, seqlen=130, d_inner=130, gate=True, h0=True)
+    check(inp, m3, "trapezoid fp32, relay in 3 parts", trap=True, rot=False, relay=3)
+
+
+# ---- rotation ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("d_state", [16, 32])
+def test_rotation_fp32(d_state):
+    inp, m3 = make_case("c1", batch=2, seqlen=77, d_inner=96, d_state=d_state, gate=True,
+                        h0=True)
+    check(inp, m3, f"rotation fp32 N={d_state}", trap=False, rot=True)
+
+
+def test_rotation_relay_bf16():
+    inp, m3 = make_case("c3", batch=2, seqlen=260, d_inner=200, h0=True)
+    check(inp, m3, "rotation bf16, relay in 2 parts", trap=False, rot=True, relay=2)
+
+
+def test_rotation_with_trapezoid_and_zoh():
+    inp, m3 = make_case("c1", batch=2, seqlen=90, d_inner=64, gate=True, h0=True)
+    check(inp, m3, "rotation + trapezoid fp32", trap=True, rot=True)
+    check(inp, m3, "rotation + zero-order hold fp32", trap=False, rot=True,
+          discretization="zoh")
+
+
+def test_unsupported_combinations():
+    inp, m3 = make_case("c1", batch=1, seqlen=32, d_inner=64, d_state=8, h0=True)
+    with pytest.raises(ms.MambaError, match="UNSUPPORTED"):
+        run_gpu(inp, m3, trap=False, rot=True)               # pairs split across waves
+    inp, m3 = make_case("c1", batch=1, seqlen=64, d_inner=64, h0=True)
+    with pytest.raises(ms.MambaError, match="UNSUPPORTED"):
+        run_gpu(inp, m3, trap=False, rot=True, n_spans=2)    # no split with rotation
+    with pytest.raises(ms.MambaError, match="UNSUPPORTED"):
+        run_gpu(inp, m3, trap=True, rot=False, discretization="zoh")
+    with pytest.raises(ms.MambaError, match="UNSUPPORTED"):
+        run_gpu(inp, m3, trap=True, rot=False, kernel="rows")
+
+
+def test_large_prefill_sampled():
+    """The large prefill shape with both options, in the configuration the benchmark
+    times: sampled channels of every tile position against the oracle."""
+    cfg = synth.CONFIGS["c3"]
+    inp = synth.make_scan_inputs(cfg)
+    m3 = synth.make_mamba3_inputs(cfg)
+    y, h = run_gpu(inp, m3, trap=True, rot=True)
+    ds = np.array([0, 1, 63, 64, 2600, 5056, 5119])
+    sub = dataclasses.replace(inp, u=inp.u[:, :, ds], delta=inp.delta[:, :, ds], z=inp.z[:, :, ds],
+                              params=synth.Params(A=inp.params.A[ds], D=inp.params.D[ds],
+                                                  bias=inp.params.bias[ds]),
+                              cfg=dataclasses.replace(cfg, d_inner=len(ds)))
+    m3s = dataclasses.replace(m3, lam=m3.lam[:, :, ds], u_prev=m3.u_prev[:, ds])
+    yr, hr = run_oracle(sub, m3s, trap=True, rot=True)
+    ey, eh = metric(y[:, :, ds], yr), metric(h[:, ds], hr)
+    log(f"large prefill, trapezoid + rotation, sampled: y {ey:.2e}, h_last {eh:.2e}")
+    assert ey <= TOL[synth.BF16] and eh <= TOL[synth.BF16]
+
+
+# ---- decode step --------------------------------------------------------------------
+
+@pytest.mark.parametrize("trap,rot", [(True, False), (False, True), (True, True)])
+def test_decode_chain_matches_scan(trap, rot):
+    """Chained decode steps (each given the previous token's u and B) against the oracle's
+    scan of the same tokens, fp32."""
+    inp, m3 = make_case("c1", batch=3, seqlen=20, d_inner=40, gate=True, h0=True)
+    p = inp.params
+    dev = lambda a: to_dev(np.ascontiguousarray(a))  # noqa: E731
+    h = to_dev(inp.h0).clone()
+    ys = []
+    for t in range(20):
+        up = m3.u_prev if t == 0 else inp.u[:, t - 1]
+        bp = m3.B_prev if t == 0 else inp.B[:, t - 1]
+        y = ms.mamba_state_update(h, dev(inp.u[:, t]), dev(inp.delta[:, t]), to_dev(p.A),
+                                  dev(inp.B[:, t]), dev(inp.C[:, t]), D=to_dev(p.D),
+                                  z=dev(inp.z[:, t]), delta_bias=to_dev(p.bias),
+                                  lam=dev(m3.lam[:, t]) if trap else None,
+                                  u_prev=dev(up) if trap else None,
+                                  B_prev=dev(bp) if trap else None,
+                                  theta=dev(m3.theta[:, t]) if rot else None)
+        ys.append(from_dev(y))
+    torch.cuda.synchronize()
+    yr, hr = run_oracle(inp, m3, trap=trap, rot=rot)
+    ey, eh = metric(np.stack(ys, axis=1), yr), metric(from_dev(h), hr)
+    log(f"decode chain trap {trap} rot {rot}: y {ey:.2e}, h {eh:.2e}")
+    assert ey <= TOL[synth.F32] and eh <= TOL[synth.F32]
