@@ -115,7 +115,7 @@ def to_dev(a, dev):
 class ScanCase:
     """A scan workload resident on the GPU with preallocated outputs and workspace."""
 
-    def __init__(self, cfg, dev, with_h_last=True, **opts):
+    def __init__(self, cfg, dev, with_h_last=True, trapezoid=False, rotation=False, **opts):
         import torch
         import selective_state_space_72_amd as ms
         from selective_state_space_72_amd import synth
@@ -126,15 +126,28 @@ class ScanCase:
         self.t = {k: to_dev(v, dev) for k, v in dict(u=inp.u, delta=inp.delta, z=inp.z, B=inp.B,
                                                       C=inp.C, A=p.A, D=p.D, bias=p.bias,
                                                       h0=inp.h0).items()}
+        self.ext = {}
+        extra_bytes = 0
+        if trapezoid or rotation:
+            m3 = synth.make_mamba3_inputs(cfg)
+            es = 4 if cfg.dtype == synth.F32 else 2
+            if trapezoid:
+                self.ext.update(lam=to_dev(m3.lam, dev), u_prev=to_dev(m3.u_prev, dev),
+                                B_prev=to_dev(m3.B_prev, dev))
+                extra_bytes += m3.lam.size * es + m3.u_prev.size * es + m3.B_prev.size * es
+            if rotation:
+                self.ext["theta"] = to_dev(m3.theta, dev)
+                extra_bytes += m3.theta.size * es
         act = self.t["u"].dtype
         self.y = torch.empty((cfg.batch, cfg.seqlen, cfg.d_inner), dtype=act, device=dev)
         self.h_last = (torch.empty((cfg.batch, cfg.d_inner, cfg.d_state), dtype=torch.float32,
                                    device=dev) if with_h_last else None)
         nws = ms.mamba_scan_fwd_workspace_size(cfg.batch, cfg.seqlen, cfg.d_inner,
-                                               cfg.d_state, **opts)
+                                               cfg.d_state, trapezoid=trapezoid,
+                                               rotation=rotation, **opts)
         self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
         self.n_spans_auto = nws > 0
-        self.min_bytes = cfg.min_bytes(with_h_last=with_h_last)
+        self.min_bytes = cfg.min_bytes(with_h_last=with_h_last) + extra_bytes
         self.inp = inp
 
     def step(self):
@@ -142,7 +155,7 @@ class ScanCase:
         t = self.t
         ms.mamba_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                           delta_bias=t["bias"], h0=t["h0"], out=self.y,
-                          h_last_out=self.h_last, workspace=self.ws, **self.opts)
+                          h_last_out=self.h_last, workspace=self.ws, **self.ext, **self.opts)
 
 
 class BwdCase:
@@ -262,14 +275,19 @@ def extra_workloads(dev, flush, steps):
     import selective_state_space_72_amd as ms
     from selective_state_space_72_amd import synth
     out = {}
-    for name, opts in (("c2", {}), ("c4", {}), ("c3_zoh", dict(discretization="zoh"))):
+    variants = (("c2", {}), ("c4", {}), ("c3_zoh", dict(discretization="zoh")),
+                ("c3_trapezoid", dict(trapezoid=True)), ("c3_rotation", dict(rotation=True)))
+    labels = {"discretization": ", zero-order-hold discretisation",
+              "trapezoid": ", exponential-trapezoidal rule (lam, u_prev, B_prev)",
+              "rotation": ", data-dependent rotation of state pairs (theta)"}
+    for name, opts in variants:
         cfg = synth.CONFIGS[name.split("_")[0]]
         case = ScanCase(cfg, dev, **opts)
         loop_ms, med, _ = time_steps(case.step, steps, 10, flush, warm_ms=100.0)
         ms_used = med if med is not None else loop_ms
         out[name] = {"workload": f"{cfg.desc}: batch {cfg.batch}, L {cfg.seqlen}, d_inner "
                                  f"{cfg.d_inner}, d_state {cfg.d_state}, {cfg.dtype}"
-                                 + (", zero-order-hold discretisation" if opts else ""),
+                                 + "".join(labels[k] for k in opts),
                      "ms": round(ms_used, 4), "ms_back_to_back": round(loop_ms, 4),
                      "GB_s": round(case.min_bytes / (ms_used * 1e-3) / 1e9, 1),
                      "gchan_steps_per_s": round(cfg.chan_steps / (ms_used * 1e-3) / 1e9, 2),

@@ -347,3 +347,57 @@ def test_bwd_validation(lib):
     assert bwd(lib, dB=BASE + 132 * MB) == ALIAS
     assert bwd(lib, dh0=BASE + 1024 * MB + 4096) == ALIAS
     assert bwd(lib, dA=BASE + 160 * MB) == ALIAS
+
+
+# ---- Mamba-3 options (mamba_scan_ext_t) ---------------------------------------------
+
+def scan_ext(lib, *, lam=None, u_prev=None, B_prev=None, theta=None, N=16, L=64, opts=None,
+             y=BASE + 256 * MB, ws=BASE + 1024 * MB, ws_bytes=1 << 30):
+    e = ms.ScanExt(lam, u_prev, B_prev, theta)
+    o = ctypes.byref(opts) if opts is not None else None
+    return lib.mamba_scan_fwd_ext(BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 132 * MB,
+                                  BASE + 136 * MB, None, None, None, None, y, None, 2, L, 128,
+                                  N, BF16, ws, ws_bytes, o, ctypes.byref(e), None)
+
+
+def test_ext_validation(lib):
+    LAM, TH = BASE + 400 * MB, BASE + 500 * MB
+    # rotation needs state pairs within a wave and an unsplit sequence
+    assert scan_ext(lib, theta=TH, N=8) == UNSUP
+    assert scan_ext(lib, theta=TH, opts=ms.ScanOpts(0, 0, 2, 0, 0, 0)) == UNSUP
+    assert scan_ext(lib, theta=TH, opts=ms.ScanOpts(0, 0, 0, ms.MAMBA_KERNEL_ROWS, 0, 0)) == UNSUP
+    # the trapezoid replaces the input term: not with the zero-order hold
+    assert scan_ext(lib, lam=LAM, opts=ms.ScanOpts(0, 0, 0, 0, 0, ms.MAMBA_DISC_ZOH)) == UNSUP
+    assert scan_ext(lib, lam=LAM + 1) == ALIGN
+    assert scan_ext(lib, theta=TH + 1) == ALIGN
+    assert scan_ext(lib, lam=LAM, u_prev=BASE + 600 * MB + 1) == ALIGN
+    # outputs may not overlap the extension inputs
+    assert scan_ext(lib, lam=LAM, y=LAM + 64) == ALIAS
+    assert scan_ext(lib, theta=TH, ws=TH + 64) == ALIAS
+
+
+def test_ext_workspace(lib):
+    plain = lib.mamba_scan_fwd_workspace_size_ext(8, 4096, 5120, 16, None, None)
+    assert plain == lib.mamba_scan_fwd_workspace_size(8, 4096, 5120, 16)
+    rot = lib.mamba_scan_fwd_workspace_size_ext(8, 4096, 5120, 16,
+                                                ctypes.byref(ms.ScanExt(None, None, None, 1)),
+                                                None)
+    assert rot > plain   # theta staged next to B and C
+    bad = ctypes.c_size_t(-1).value
+    assert lib.mamba_scan_fwd_workspace_size_ext(
+        8, 4096, 5120, 8, ctypes.byref(ms.ScanExt(None, None, None, 1)), None) == bad
+
+
+def test_decode_ext_validation(lib):
+    e = ms.ScanExt(BASE + 400 * MB, None, None, None)
+    st = lib.mamba_state_update_ext(BASE, BASE + 64 * MB, BASE + 65 * MB, BASE + 128 * MB,
+                                    BASE + 132 * MB, BASE + 133 * MB, None, None, None,
+                                    BASE + 256 * MB, 4, 128, 16, BF16, ms.MAMBA_DISC_ZOH,
+                                    ctypes.byref(e), None)
+    assert st == UNSUP
+    e = ms.ScanExt(BASE + 256 * MB, None, None, None)   # lam overlapping y
+    st = lib.mamba_state_update_ext(BASE, BASE + 64 * MB, BASE + 65 * MB, BASE + 128 * MB,
+                                    BASE + 132 * MB, BASE + 133 * MB, None, None, None,
+                                    BASE + 256 * MB, 4, 128, 16, BF16, ms.MAMBA_DISC_EULER,
+                                    ctypes.byref(e), None)
+    assert st == ALIAS
