@@ -414,6 +414,41 @@ MAMBA_API mamba_status_t mamba_state_update_ext(float *h, const void *u, const v
                                                 int32_t discretization,
                                                 const mamba_scan_ext_t *ext, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Mamba-2 SSD scan: the state-space-duality form of "Understanding Mamba"
+ * (aiattnstudio.link) section 6 -- y_t = sum_{s<=t} C_t . B_s (prod_{l=s+1..t} Abar_l)
+ * Bbar_s x_s -- with the scalar state transition per head of Mamba-2 ("State space models
+ * and the Mamba series", jsqmd.com, section 1.2: A = diag(a)), computed in chunks with
+ * matrix products on the matrix cores.  d_inner = n_heads * head_dim channels; head h owns
+ * channels [h * head_dim, (h+1) * head_dim).  For every b, h, channel p of the head and n:
+ *
+ *   Delta_t   = softplus(dt[b,t,h] + dt_bias[h])
+ *   h_t[p,n]  = exp(Delta_t * A[h]) * h_{t-1}[p,n] + Delta_t * B[b,t,n] * x[b,t,h*P+p]
+ *   y[b,t,h*P+p] = (sum_n C[b,t,n] * h_t[p,n] + D[h] * x[b,t,h*P+p]) * silu(z[b,t,h*P+p])
+ *
+ * i.e. the selective scan above with Delta and A shared by the channels of a head.
+ *
+ *   x, z, y   (batch, seqlen, n_heads * head_dim) dtype   z nullable (no gate)
+ *   dt        (batch, seqlen, n_heads) dtype
+ *   A         (n_heads) float32 (normally < 0)         D, dt_bias (n_heads) float32 nullable
+ *   B, C      (batch, seqlen, d_state) dtype (shared by all heads)
+ *   h0, h_last (batch, n_heads * head_dim, d_state) float32, nullable
+ *
+ * head_dim must be 64 and d_state 64 or 128 (mamba_ssd_supported), else
+ * MAMBA_ERR_UNSUPPORTED.  Arithmetic: bf16 inputs use bf16 matrix-core products with fp32
+ * accumulation (the chunk's decay-weighted C.B^T, decay-weighted B and the state copy read
+ * by C h are rounded to bf16; the carried state is fp32); fp32 inputs use fp32 products.
+ * No workspace.  y and h_last must not overlap any input or each other (h_last may not be
+ * h0).  Other conventions as for every entry point. */
+MAMBA_API int32_t mamba_ssd_supported(int64_t head_dim, int64_t d_state);
+
+MAMBA_API mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A,
+                                       const void *B, const void *C, const float *D,
+                                       const void *z, const float *dt_bias, const float *h0,
+                                       void *y, float *h_last, int64_t batch, int64_t seqlen,
+                                       int64_t n_heads, int64_t head_dim, int64_t d_state,
+                                       mamba_dtype_t dtype, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 MAMBA_API const char *mamba_status_string(mamba_status_t status);
 

@@ -39,6 +39,7 @@ EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_conv1d_silu_update", "mamba_scan_bwd_workspace_size", "mamba_scan_bwd",
            "mamba_scan_bwd_workspace_size_ex", "mamba_scan_bwd_ex",
            "mamba_scan_fwd_workspace_size_ext", "mamba_scan_fwd_ext", "mamba_state_update_ext",
+           "mamba_ssd_supported", "mamba_ssd_fwd",
            "mamba_status_string")
 
 
@@ -128,6 +129,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mamba_state_update_ext.argtypes = ([_vp] * 10 + [_i64] * 3 +
                                            [ctypes.c_int, ctypes.c_int32,
                                             ctypes.POINTER(ScanExt), _vp])
+    lib.mamba_ssd_supported.restype = ctypes.c_int32
+    lib.mamba_ssd_supported.argtypes = [_i64, _i64]
+    lib.mamba_ssd_fwd.restype = ctypes.c_int
+    lib.mamba_ssd_fwd.argtypes = [_vp] * 11 + [_i64] * 5 + [ctypes.c_int, _vp]
     lib.mamba_status_string.restype = ctypes.c_char_p
     lib.mamba_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -462,3 +467,44 @@ def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=No
     if st != 0:
         raise MambaError(st, "mamba_scan_bwd")
     return {k: v for k, v in res.items() if k in ("du", "ddelta") or k in want}
+
+
+def mamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None,
+                  return_last_state: bool = False, *, out=None, h_last_out=None,
+                  head_dim: int = 64) -> Tuple:
+    """Mamba-2 SSD scan (see include/mamba_scan.h): x (batch, seqlen, n_heads * head_dim),
+    dt (batch, seqlen, n_heads), A/D/dt_bias (n_heads,) fp32, B/C (batch, seqlen, d_state),
+    h0 (batch, n_heads * head_dim, d_state) fp32.  Returns (y, h_last)."""
+    torch = _torch()
+    lib = load_library()
+    if x.dim() != 3 or dt.dim() != 3:
+        raise ValueError("x must be (batch, seqlen, d_inner) and dt (batch, seqlen, n_heads)")
+    batch, seqlen, d_inner = x.shape
+    n_heads = dt.shape[2]
+    if n_heads * head_dim != d_inner:
+        raise ValueError("d_inner must be n_heads * head_dim")
+    d_state = B.shape[2]
+    dev, act = x.device, x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    bld = (batch, seqlen, d_inner)
+    p_x = _ptr(x, "x", bld, act, dev)
+    p_dt = _ptr(dt, "dt", (batch, seqlen, n_heads), act, dev)
+    p_A = _ptr(A, "A", (n_heads,), f32, dev)
+    p_B = _ptr(B, "B", (batch, seqlen, d_state), act, dev)
+    p_C = _ptr(C, "C", (batch, seqlen, d_state), act, dev)
+    p_D = _ptr(D, "D", (n_heads,), f32, dev)
+    p_z = _ptr(z, "z", bld, act, dev)
+    p_bias = _ptr(dt_bias, "dt_bias", (n_heads,), f32, dev)
+    p_h0 = _ptr(h0, "h0", (batch, d_inner, d_state), f32, dev)
+    y = out if out is not None else torch.empty(bld, dtype=act, device=dev)
+    p_y = _ptr(y, "out", bld, act, dev)
+    h_last = h_last_out
+    if h_last is None and return_last_state:
+        h_last = torch.empty((batch, d_inner, d_state), dtype=f32, device=dev)
+    p_hl = _ptr(h_last, "h_last_out", (batch, d_inner, d_state), f32, dev)
+    st = lib.mamba_ssd_fwd(p_x, p_dt, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_y, p_hl, batch,
+                           seqlen, n_heads, head_dim, d_state, code, _stream(dev))
+    if st != 0:
+        raise MambaError(st, "mamba_ssd_fwd")
+    return y, h_last

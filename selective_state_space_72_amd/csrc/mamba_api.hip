@@ -3,6 +3,7 @@
 #include "mamba_scan.h"
 #include "scan_common.h"
 #include "scan_bwd.h"
+#include "ssd.h"
 
 #include <limits.h>
 #include <stdint.h>
@@ -1029,6 +1030,84 @@ mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *
     P.d_state = d_state;
     P.dtype = dt;
     return hip_status(launch_scan_bwd(P, st));
+}
+
+
+int32_t mamba_ssd_supported(int64_t head_dim, int64_t d_state)
+{
+    return ssd_supported(head_dim, d_state) ? 1 : 0;
+}
+
+mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A, const void *B,
+                             const void *C, const float *D, const void *z,
+                             const float *dt_bias, const float *h0, void *y, float *h_last,
+                             int64_t batch, int64_t seqlen, int64_t n_heads, int64_t head_dim,
+                             int64_t d_state, mamba_dtype_t dtype, void *stream)
+{
+    if (batch < 0 || seqlen < 0 || n_heads < 0 || head_dim <= 0 || d_state <= 0)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
+        return MAMBA_ERR_BAD_DTYPE;
+    if (!ssd_supported(head_dim, d_state))
+        return MAMBA_ERR_UNSUPPORTED;
+    const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
+    int64_t dn, bld, blh, bln, bdn, t;
+    if (!mul_ok(n_heads, head_dim, &dn) || !mul_ok(batch, seqlen, &t) ||
+        !mul_ok(t, dn, &bld) || !mul_ok(bld, es, &t) || !mul_ok(batch * seqlen, n_heads, &blh) ||
+        !mul_ok(blh, es, &t) || !mul_ok(batch * seqlen, d_state, &bln) || !mul_ok(bln, es, &t) ||
+        !mul_ok(batch, dn, &t) || !mul_ok(t, d_state, &bdn) || !mul_ok(bdn, 4, &t) ||
+        dn > INT32_MAX || batch * n_heads > INT32_MAX)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (batch == 0 || n_heads == 0)
+        return MAMBA_OK;
+    const bool has_seq = seqlen > 0;
+    if (!A || (has_seq && (!x || !dt || !B || !C || !y)))
+        return MAMBA_ERR_NULL_ARG;
+    const void *elem_ptrs[] = {x, dt, B, C, z, y};
+    for (const void *p : elem_ptrs)
+        if (p && !aligned(p, (size_t)es))
+            return MAMBA_ERR_MISALIGNED;
+    const void *f32_ptrs[] = {A, D, dt_bias, h0, h_last};
+    for (const void *p : f32_ptrs)
+        if (p && !aligned(p, 4))
+            return MAMBA_ERR_MISALIGNED;
+    const Range r_in[] = {range_of(x, bld * es),         range_of(dt, blh * es),
+                          range_of(B, bln * es),         range_of(C, bln * es),
+                          range_of(z, bld * es),         range_of(A, n_heads * 4),
+                          range_of(D, n_heads * 4),      range_of(dt_bias, n_heads * 4)};
+    const Range r_h0 = range_of(h0, bdn * 4);
+    const Range r_y = range_of(has_seq ? y : nullptr, bld * es);
+    const Range r_hl = range_of(h_last, bdn * 4);
+    for (const Range &r : r_in)
+        if (overlaps(r_y, r) || overlaps(r_hl, r))
+            return MAMBA_ERR_ALIASING;
+    if (overlaps(r_y, r_h0) || overlaps(r_y, r_hl) || overlaps(r_hl, r_h0))
+        return MAMBA_ERR_ALIASING; // (h_last is written while h0 is still being read)
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (!has_seq) {
+        if (h_last)
+            return hip_status(launch_copy_state(h_last, h0, bdn, st));
+        return MAMBA_OK;
+    }
+    SsdLaunch q{};
+    q.x = x;
+    q.dt = dt;
+    q.B = B;
+    q.C = C;
+    q.z = z;
+    q.A = A;
+    q.D = D;
+    q.dt_bias = dt_bias;
+    q.h0 = h0;
+    q.y = y;
+    q.h_last = h_last;
+    q.batch = batch;
+    q.L = seqlen;
+    q.n_heads = n_heads;
+    q.head_dim = head_dim;
+    q.d_state = d_state;
+    q.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+    return hip_status(launch_ssd(q, st));
 }
 
 } // extern "C"

@@ -354,3 +354,51 @@ def make_mamba3_inputs(cfg: ScanConfig) -> Mamba3Inputs:
         theta=_normal(sd, (9,), (cfg.batch, cfg.seqlen, cfg.d_state // 2), cfg.dtype),
         u_prev=_normal(sd, (10,), (cfg.batch, cfg.d_inner), cfg.dtype),
         B_prev=_normal(sd, (11,), (cfg.batch, cfg.d_state), cfg.dtype))
+
+
+# ----------------------------------------------------------------------------
+# Mamba-2 SSD workloads (scalar A per head, one step size per token and head)
+# ----------------------------------------------------------------------------
+
+# large SSD prefill: the large prefill's tokens and channels as 80 heads of 64, d_state 128
+# (the Mamba-2 block of "State Space Models and Mamba" uses d_state 128)
+SSD_LARGE = dict(batch=8, seqlen=4096, n_heads=80, head_dim=64, d_state=128, dtype=BF16,
+                 gate=True, h0=False, seed=7210)
+
+
+@dataclasses.dataclass
+class SsdInputs:
+    x: np.ndarray          # (batch, L, H * P) stored dtype
+    dt: np.ndarray         # (batch, L, H) stored dtype
+    B: np.ndarray          # (batch, L, N)
+    C: np.ndarray          # (batch, L, N)
+    z: Optional[np.ndarray]
+    h0: Optional[np.ndarray]   # (batch, H * P, N) float32
+    A: np.ndarray          # (H,) float32
+    D: np.ndarray          # (H,) float32
+    dt_bias: np.ndarray    # (H,) float32
+    head_dim: int
+    dtype: str
+
+
+def make_ssd_inputs(batch: int, seqlen: int, n_heads: int, head_dim: int = 64,
+                    d_state: int = 128, dtype: str = BF16, gate: bool = True, h0: bool = False,
+                    seed: int = 7210) -> SsdInputs:
+    """Activations x, dt, B, C, z ~ N(0, 1) (tensor ids 20..24), h0 ~ N(0, 1) fp32 (25);
+    per head: A = -exp(A_log), A_log ~ U(log 1, log 16) (the 1..16 range of the Mamba-1
+    recipe's A = -(n + 1)), dt bias = inverse softplus of dt log-uniform in [1e-3, 1e-1],
+    D ~ U(0.5, 1.5); drawn in float64 from default_rng(seed) in that order, rounded once."""
+    rng = np.random.default_rng(seed)
+    A = (-np.exp(rng.uniform(0.0, np.log(16.0), size=n_heads))).astype(np.float32)
+    dtv = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=n_heads))
+    dt_bias = np.log(np.expm1(dtv)).astype(np.float32)
+    D = rng.uniform(0.5, 1.5, size=n_heads).astype(np.float32)
+    d_inner = n_heads * head_dim
+    x = _normal(seed, (20,), (batch, seqlen, d_inner), dtype)
+    dt = _normal(seed, (21,), (batch, seqlen, n_heads), dtype)
+    Bm = _normal(seed, (22,), (batch, seqlen, d_state), dtype)
+    Cm = _normal(seed, (23,), (batch, seqlen, d_state), dtype)
+    z = _normal(seed, (24,), (batch, seqlen, d_inner), dtype) if gate else None
+    hz = _normal(seed, (25,), (batch, d_inner, d_state), F32) if h0 else None
+    return SsdInputs(x=x, dt=dt, B=Bm, C=Cm, z=z, h0=hz, A=A, D=D, dt_bias=dt_bias,
+                     head_dim=head_dim, dtype=dtype)
