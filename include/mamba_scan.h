@@ -434,12 +434,15 @@ MAMBA_API mamba_status_t mamba_state_update_ext(float *h, const void *u, const v
  *   B, C      (batch, seqlen, d_state) dtype (shared by all heads)
  *   h0, h_last (batch, n_heads * head_dim, d_state) float32, nullable
  *
- * head_dim must be 64 and d_state 64 or 128 (mamba_ssd_supported), else
+ * head_dim must be 64 and d_state 64 or 128 (mamba_ssd_supported), and 64 rows of x must
+ * span fewer than 2^31 bytes (n_heads * head_dim * element size * 64), else
  * MAMBA_ERR_UNSUPPORTED.  Arithmetic: bf16 inputs use bf16 matrix-core products with fp32
- * accumulation (the chunk's decay-weighted C.B^T, decay-weighted B and the state copy read
- * by C h are rounded to bf16; the carried state is fp32); fp32 inputs use fp32 products.
- * No workspace.  y and h_last must not overlap any input or each other (h_last may not be
- * h0).  Other conventions as for every entry point. */
+ * accumulation; the operands computed in fp32 (the chunk's decay-weighted C.B^T, the
+ * decay-weighted x and the state read by C h) enter as a bf16 pair hi + lo, about 16
+ * significant bits; the carried state is fp32.  fp32 inputs use fp32 products.
+ * No workspace.  x, z, B and C must be 16-byte aligned (they are read as 16-byte vectors;
+ * MAMBA_ERR_MISALIGNED otherwise).  y and h_last must not overlap any input or each other
+ * (h_last may not be h0).  Other conventions as for every entry point. */
 MAMBA_API int32_t mamba_ssd_supported(int64_t head_dim, int64_t d_state);
 
 MAMBA_API mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A,

@@ -1058,14 +1058,20 @@ mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A, cons
         !mul_ok(batch, dn, &t) || !mul_ok(t, d_state, &bdn) || !mul_ok(bdn, 4, &t) ||
         dn > INT32_MAX || batch * n_heads > INT32_MAX)
         return MAMBA_ERR_BAD_SHAPE;
+    if (dn * es * 64 > INT32_MAX) // a chunk of 64 rows is addressed with 32-bit offsets
+        return MAMBA_ERR_UNSUPPORTED;
     if (batch == 0 || n_heads == 0)
         return MAMBA_OK;
     const bool has_seq = seqlen > 0;
     if (!A || (has_seq && (!x || !dt || !B || !C || !y)))
         return MAMBA_ERR_NULL_ARG;
-    const void *elem_ptrs[] = {x, dt, B, C, z, y};
+    const void *elem_ptrs[] = {dt, y};
     for (const void *p : elem_ptrs)
         if (p && !aligned(p, (size_t)es))
+            return MAMBA_ERR_MISALIGNED;
+    const void *vec_ptrs[] = {x, B, C, z}; // read as 16-byte vectors
+    for (const void *p : vec_ptrs)
+        if (p && !aligned(p, 16))
             return MAMBA_ERR_MISALIGNED;
     const void *f32_ptrs[] = {A, D, dt_bias, h0, h_last};
     for (const void *p : f32_ptrs)

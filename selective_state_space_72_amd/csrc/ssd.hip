@@ -13,21 +13,36 @@
 // Chunked evaluation (chunks of Q = 64 steps; cs = inclusive cumulative sum of Delta A
 // within the chunk, in log2 units): per chunk,
 //   S      = C B^T                                   (Q x Q, contraction over N)
-//   M[t,s] = S[t,s] exp(cs_t - cs_s) Delta_s  (s <= t, else 0)
-//   Y      = M X + diag(exp(cs)) C H_in + D X        (Q x P)
-//   H_out  = exp(cs_{Q-1}) H_in + Btil^T X,   Btil[s,n] = B[s,n] exp(cs_{Q-1} - cs_s) Delta_s
-// One block per (batch row, head) walks the chunks in order and keeps H in the MFMA
-// accumulators (fp32) from chunk to chunk, so nothing of the chunk states goes to HBM.
-// The four products use v_mfma_f32_32x32x16_bf16 for bf16 inputs and v_mfma_f32_32x32x2f32
-// for fp32 inputs.  With bf16 inputs, X, B and C are exact bf16 values, but M, Btil and
-// the copy of H read by C H are computed in fp32: each is split as hi + lo (hi = its bf16
+//   M[t,s] = S[t,s] exp(cs_t - cs_s) Delta_s  (s <= t, else 0),  plus D on the diagonal
+//   Y      = M X + diag(exp(cs)) C H_in               (Q x P)
+//   H_out  = exp(cs_{Q-1}) H_in + B^T Xtil,   Xtil[s,p] = exp(cs_{Q-1} - cs_s) Delta_s X[s,p]
+// One block per (batch row, head) walks the chunks in order; nothing of the chunk states
+// goes to HBM.
+//
+// Work split.  Wave w of the block's four owns the columns p in [16w, 16w + 16) of Y and of
+// H, and keeps its N x 16 slab of H in MFMA accumulators (16 x 16 tiles) from chunk to
+// chunk.  That slab is also the right operand of C H_in: the contraction index of an MFMA
+// may be permuted freely as long as both operands agree, and the accumulator rows a lane
+// holds (4 consecutive n in each of two tiles) are exactly as many as an operand lane
+// takes, so C is read from LDS in the same permuted order and H never passes through LDS.
+// The causal tiles of S (10 of the 16 tiles of 16 x 16) are shared out among the waves
+// and M goes through LDS; the Xtil operand is formed in registers from X^T.
+//
+// Precision.  The products use v_mfma_f32_16x16x32_bf16 for bf16 inputs and
+// v_mfma_f32_16x16x4f32 for fp32 inputs.  With bf16 inputs, X, B and C are exact bf16
+// values, but M, Xtil and H are computed in fp32: each is split as hi + lo (hi = its bf16
 // rounding, lo = the bf16 rounding of the remainder) and enters as two products, which
 // keeps about 16 significant bits (a single bf16 operand measured 1.4e-2 relative error in
-// y and in the state on a CPU emulation of this arithmetic).  Each wave of the block owns
-// one 32 x 32 tile of S and of Y and N/64 tiles of H.  Every operand is read from an LDS matrix stored with
-// its contraction index contiguous (rows padded by 16 bytes against bank conflicts).
-#include <type_traits>
-
+// y and in the state on a CPU emulation of this arithmetic).
+//
+// Memory.  Inputs are read with 16-byte buffer loads through descriptors that end at the
+// chunk's last row, so rows past the end of the sequence read as zero and stores to them
+// are dropped.  The loads of the next chunk are issued before the current chunk's products
+// and land in registers; the block barriers wait only for LDS traffic, so those loads stay
+// in flight across them.  LDS matrices are unpadded, with their 16-byte granules permuted
+// per row (an XOR key) so that the 16 rows of one operand load fall in distinct banks.
+// Blocks are numbered so that each XCD takes a contiguous range of (batch row, head) pairs:
+// the heads of one batch row share B and C in that XCD's L2.
 #include "device_math.h"
 #include "scan_common.h"
 #include "ssd.h"
@@ -36,57 +51,85 @@ namespace mambascan {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int kQ = 64;       // chunk length
-constexpr int kP = 64;       // head dimension
+constexpr int kQ = 64;        // chunk length
+constexpr int kP = 64;        // head dimension
 constexpr int kThreads = 256; // 4 waves
+constexpr int kRsrcWord3 = 0x00020000; // gfx9 raw-buffer descriptor word 3
 
-// The MFMA used for an element type, its K, and the LDS element type.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+// Block barrier that waits for this wave's LDS accesses only (a __syncthreads also waits
+// for every outstanding global load, which would drain the prefetch).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The MFMA used for an element type: k per instruction (KI) and per lane (KL).
 template <typename T> struct Mma;
 template <> struct Mma<uint16_t> {
-    static constexpr int K = 16;   // contraction per instruction
-    static constexpr int KL = 8;   // contiguous k values per lane
-    static constexpr int PAD = 8;  // row padding (elements)
+    static constexpr int KI = 32, KL = 8;
+    static constexpr bool SPLIT = true; // computed operands as hi + lo
     typedef __bf16 E;
     typedef bf16x8 Frag;
-    static __device__ __forceinline__ Frag load(const E *p) { return *reinterpret_cast<const Frag *>(p); }
-    static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c)
+    static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c)
     {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ E from_float(float v) { return static_cast<__bf16>(v); }
-    static __device__ __forceinline__ E from_raw(uint16_t v) { return __builtin_bit_cast(__bf16, v); }
     static __device__ __forceinline__ float to_float(E v) { return static_cast<float>(v); }
-    static constexpr bool SPLIT = true; // computed operands as hi + lo
 };
 template <> struct Mma<float> {
-    static constexpr int K = 2;
-    static constexpr int KL = 1;
-    static constexpr int PAD = 1;
+    static constexpr int KI = 4, KL = 1;
+    static constexpr bool SPLIT = false;
     typedef float E;
     typedef float Frag;
-    static __device__ __forceinline__ Frag load(const E *p) { return *p; }
-    static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c)
+    static __device__ __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c)
     {
-        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ E from_float(float v) { return v; }
-    static __device__ __forceinline__ E from_raw(float v) { return v; }
     static __device__ __forceinline__ float to_float(E v) { return v; }
-    static constexpr bool SPLIT = false;
 };
 
-// Store v at hi[i] (and its rounding remainder at lo[i] when operands are split).
-template <typename T>
-__device__ __forceinline__ void put_split(typename Mma<T>::E *hi, typename Mma<T>::E *lo, int i,
-                                          float v)
+// Index of element (r, c) of an LDS matrix of RL elements per row (ES bytes each): rows
+// are unpadded and the 16-byte granules of row r are XOR-permuted by a key of r, so that
+// 16 consecutive rows read at one column land in distinct banks.
+template <int RL, int ES>
+__device__ __forceinline__ int sw(int r, int c)
 {
-    typedef Mma<T> M;
-    const typename M::E h = M::from_float(v);
-    hi[i] = h;
-    if constexpr (M::SPLIT)
-        lo[i] = M::from_float(v - M::to_float(h));
+    constexpr int G = 16 / ES, RB = RL * ES;
+    static_assert(RB % 128 == 0, "row bytes");
+    const int key = RB == 128 ? (r >> 1) & 7 : r & 15;
+    return r * RL + (((c / G) ^ key) * G) + (c % G);
+}
+
+// MFMA operand of KL contiguous elements at index i of an LDS matrix.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::Frag frag(const typename Mma<T>::E *m, int i)
+{
+    if constexpr (Mma<T>::KL == 8)
+        return *reinterpret_cast<const bf16x8 *>(m + i);
+    else
+        return m[i];
+}
+
+// Split v into hi (its bf16 rounding) and lo (the bf16 rounding of v - hi).
+__device__ __forceinline__ void split_bf16(float v, __bf16 &hi, __bf16 &lo)
+{
+    hi = static_cast<__bf16>(v);
+    lo = static_cast<__bf16>(v - static_cast<float>(hi));
 }
 
 // a + b = s + e exactly (Knuth's TwoSum; no reassociation, no FMA is involved).
@@ -97,47 +140,14 @@ __device__ __forceinline__ void two_sum(float a, float b, float &s, float &e)
     e = (a - (s - bb)) + (b - bb);
 }
 
-// Row and column of accumulator element v of this lane in a 32 x 32 tile.
-__device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
-__device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
-
-// acc += A B over k in [0, KTOT): A rows [i0, i0+32) of a [.][k] matrix with row stride ra,
-// B columns [j0, j0+32) of a [j][k] matrix (stored transposed) with row stride rb.
-template <typename T, int KTOT>
-__device__ __forceinline__ void tile_mma(f32x16 &acc, const typename Mma<T>::E *a, int ra, int i0,
-                                         const typename Mma<T>::E *b, int rb, int j0, int lane)
+// Raw bits of element j of a 16-byte vector of bf16 or fp32 values.
+template <int ES>
+__device__ __forceinline__ uint32_t vec_elem(const u32x4 &v, int j)
 {
-    typedef Mma<T> M;
-    const int r = lane & 31, kh = (lane >> 5) * M::KL;
-    const typename M::E *pa = a + (i0 + r) * ra + kh;
-    const typename M::E *pb = b + (j0 + r) * rb + kh;
-#pragma unroll
-    for (int k = 0; k < KTOT; k += M::K)
-        acc = M::mma(M::load(pa + k), M::load(pb + k), acc);
-}
-
-// acc += (A_hi + A_lo) B, or acc += A (B_hi + B_lo): the split side given twice (lo
-// ignored when operands are not split).
-template <typename T, int KTOT>
-__device__ __forceinline__ void tile_mma_split_a(f32x16 &acc, const typename Mma<T>::E *ahi,
-                                                 const typename Mma<T>::E *alo, int ra, int i0,
-                                                 const typename Mma<T>::E *b, int rb, int j0,
-                                                 int lane)
-{
-    tile_mma<T, KTOT>(acc, ahi, ra, i0, b, rb, j0, lane);
-    if constexpr (Mma<T>::SPLIT)
-        tile_mma<T, KTOT>(acc, alo, ra, i0, b, rb, j0, lane);
-}
-
-template <typename T, int KTOT>
-__device__ __forceinline__ void tile_mma_split_b(f32x16 &acc, const typename Mma<T>::E *a,
-                                                 int ra, int i0, const typename Mma<T>::E *bhi,
-                                                 const typename Mma<T>::E *blo, int rb, int j0,
-                                                 int lane)
-{
-    tile_mma<T, KTOT>(acc, a, ra, i0, bhi, rb, j0, lane);
-    if constexpr (Mma<T>::SPLIT)
-        tile_mma<T, KTOT>(acc, a, ra, i0, blo, rb, j0, lane);
+    if constexpr (ES == 2)
+        return (v[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+    else
+        return v[j];
 }
 
 struct SsdArgs {
@@ -149,83 +159,175 @@ struct SsdArgs {
     int32_t H; // heads
 };
 
+// bf16: two blocks per CU (75 KB of LDS each at N = 128), so registers are held to 256
 template <typename T, int N, bool GATED>
 __global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
 ssd_chunk_kernel(SsdArgs p)
 {
     typedef Mma<T> M;
     typedef typename M::E E;
-    constexpr int Q = kQ, P = kP;
-    constexpr int RQ = Q + M::PAD, RN = N + M::PAD; // row strides
-    constexpr int HT = N / 64;                       // H tiles per wave (N/32 x 2 tiles / 4 waves)
-    static_assert(N % 64 == 0 && Q == 64 && P == 64, "shape");
-
-    // LDS: X^T [P][RQ]; B [Q][RN], then M [Q][RQ] (hi, lo) in the same place; C [Q][RN];
-    // Btil^T [N][RQ] (hi, lo); H^T [P][RN] (hi, lo); cumulative decay and Delta per step.
+    typedef typename M::Frag F;
+    constexpr int Q = kQ, P = kP, ES = (int)sizeof(T);
+    constexpr int G = 16 / ES;           // elements per 16-byte vector
+    constexpr int KI = M::KI, KL = M::KL;
+    constexpr int NT = N / 16;           // 16-row tiles of this wave's H slab
     constexpr int NS = M::SPLIT ? 2 : 1;
-    constexpr int BM = Q * RN > NS * Q * RQ ? Q * RN : NS * Q * RQ;
-    __shared__ __attribute__((aligned(16))) E s_xt[P * RQ];
-    __shared__ __attribute__((aligned(16))) E s_bm[BM];
-    __shared__ __attribute__((aligned(16))) E s_c[Q * RN];
-    __shared__ __attribute__((aligned(16))) E s_bt[NS * N * RQ];
-    __shared__ __attribute__((aligned(16))) E s_ht[NS * P * RN];
-    // cumulative decay cs = cs_hi + cs_lo (a compensated sum: the weights use differences
-    // cs_t - cs_s, which a plain fp32 sum would lose when |cs| is large), Delta per step
-    __shared__ float s_cs[Q], s_csl[Q], s_dl[Q];
-    E *const s_ml = s_bm + (NS - 1) * Q * RQ;     // lo parts (alias the hi arrays when unsplit)
-    E *const s_btl = s_bt + (NS - 1) * N * RQ;
-    E *const s_htl = s_ht + (NS - 1) * P * RN;
+    static_assert(N % 32 == 0 && Q == 64 && P == 64, "shape");
+
+    // X^T [p][t], B [s][n], B^T [n][s], C [t][n], M [t][s] (hi, then lo when split)
+    __shared__ __attribute__((aligned(16))) E s_xt[P * Q];
+    __shared__ __attribute__((aligned(16))) E s_b[Q * N];
+    __shared__ __attribute__((aligned(16))) E s_bt[N * Q];
+    __shared__ __attribute__((aligned(16))) E s_c[Q * N];
+    __shared__ __attribute__((aligned(16))) E s_m[NS * Q * Q];
+    // per step: cumulative decay cs = cs_hi + cs_lo (a compensated sum: M uses differences
+    // cs_t - cs_s, which a plain fp32 sum would lose when |cs| is large), Delta, the weight
+    // of Xtil, exp(cs); and the chunk's total decay
+    __shared__ __attribute__((aligned(16))) float s_cs[Q], s_csl[Q], s_dl[Q], s_w[Q], s_e[Q];
+    __shared__ float s_dec;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    const int lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int bh = blockIdx.x;
+    const int nblk = (int)gridDim.x;
+    int bh = (int)blockIdx.x;
+    if (nblk % 8 == 0) // blocks go round-robin over the 8 XCDs: give each a contiguous range
+        bh = (bh % 8) * (nblk / 8) + bh / 8;
     const int b = bh / p.H, h = bh % p.H;
     const int64_t L = p.L;
     const int64_t Dn = (int64_t)p.H * P;
+    const int pc = 16 * w + r16; // this lane's column of Y and of H
 
-    const T *xg = (const T *)p.x + (int64_t)b * L * Dn + (int64_t)h * P;
-    const T *zg = GATED ? (const T *)p.z + (int64_t)b * L * Dn + (int64_t)h * P : nullptr;
-    T *yg = (T *)p.y + (int64_t)b * L * Dn + (int64_t)h * P;
-    const T *bg = (const T *)p.B + (int64_t)b * L * N;
-    const T *cg = (const T *)p.C + (int64_t)b * L * N;
-    const T *dtg = (const T *)p.dt + (int64_t)b * L * p.H + h;
+    const char *xb = (const char *)p.x + ((int64_t)b * L * Dn + (int64_t)h * P) * ES;
+    const char *zb = GATED ? (const char *)p.z + ((int64_t)b * L * Dn + (int64_t)h * P) * ES
+                           : nullptr;
+    char *yb = (char *)p.y + ((int64_t)b * L * Dn + (int64_t)h * P) * ES;
+    const char *bb = (const char *)p.B + (int64_t)b * L * N * ES;
+    const char *cb = (const char *)p.C + (int64_t)b * L * N * ES;
+    const char *db = (const char *)p.dt + ((int64_t)b * L * p.H + h) * ES;
     const float a2 = p.A[h] * kLog2e;
     const float dtb = p.dt_bias ? p.dt_bias[h] : 0.0f;
     const float Dh = p.D ? p.D[h] : 0.0f;
+    const uint32_t row_x = (uint32_t)(Dn * ES), row_b = (uint32_t)(N * ES);
 
-    // state tiles of this wave: tile tau = w * HT + m -> rows 32 (tau / 2) (n), cols 32 (tau % 2) (p)
-    f32x16 hacc[HT];
-    const float *h0 = p.h0 ? p.h0 + ((int64_t)b * Dn + (int64_t)h * P) * N : nullptr;
+    // ---- state slab: tile m holds rows n = 16m + 4g + v, column pc ----
+    f32x4 hacc[NT];
+    const int64_t hrow = ((int64_t)b * Dn + (int64_t)h * P + pc) * N;
+    if (p.h0) {
 #pragma unroll
-    for (int m = 0; m < HT; ++m) {
-        const int tau = w * HT + m, n0 = 32 * (tau >> 1), p0 = 32 * (tau & 1);
+        for (int m = 0; m < NT; ++m)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int n = n0 + acc_row(v, lane), pc = p0 + acc_col(lane);
-            const float hv = h0 ? h0[(int64_t)pc * N + n] : 0.0f;
-            hacc[m][v] = hv;
-            put_split<T>(s_ht, s_htl, pc * RN + n, hv);
-        }
+            for (int v = 0; v < 4; ++v)
+                hacc[m][v] = p.h0[hrow + 16 * m + 4 * g + v];
+    } else {
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+            hacc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    // M's tiles above the diagonal stay zero; the causal tiles are rewritten every chunk
+    for (int e = tid; e < NS * Q * Q; e += kThreads)
+        s_m[e] = M::from_float(0.0f);
 
-    const int ti0 = 32 * (w >> 1), tj0 = 32 * (w & 1); // this wave's tile of S and Y
-    for (int64_t t0 = 0; t0 < L; t0 += Q) {
-        const int nt = (int)min((int64_t)Q, L - t0);
-        // ---- load the chunk: X^T, B, C; Delta and the cumulative decay ----
-        for (int e = tid; e < Q * P; e += kThreads) {
-            const int t = e / P, pc = e % P;
-            s_xt[pc * RQ + t] = t < nt ? M::from_raw(xg[(t0 + t) * Dn + pc]) : M::from_float(0.0f);
+    // ---- loads of one chunk into registers; a unit is rows (2 rp, 2 rp + 1) x one 16-byte
+    // column group ----
+    constexpr int XU = (Q / 2) * (P / G) / kThreads; // X units per thread
+    constexpr int BU = (Q / 2) * (N / G) / kThreads; // B and C units per thread
+    static_assert(XU * kThreads == (Q / 2) * (P / G) && BU * kThreads == (Q / 2) * (N / G),
+                  "units");
+    u32x4 fx[XU][2], fb[BU][2], fc[BU][2];
+    uint32_t fdt = 0;
+    auto fetch = [&](int64_t c0) {
+        const int nok = (int)min((int64_t)Q, L - c0);
+        const rsrc_t rx = make_rsrc(xb + c0 * row_x, (uint32_t)(nok - 1) * row_x + P * ES);
+        const rsrc_t rb = make_rsrc(bb + c0 * row_b, (uint32_t)nok * row_b);
+        const rsrc_t rc = make_rsrc(cb + c0 * row_b, (uint32_t)nok * row_b);
+#pragma unroll
+        for (int k = 0; k < XU; ++k) {
+            const int u = tid + k * kThreads, rp = u / (P / G), cg = u % (P / G);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                fx[k][i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rx, (int)((2 * rp + i) * row_x + cg * 16), 0, 0);
         }
-        for (int e = tid; e < Q * N; e += kThreads) {
-            const int t = e / N, n = e % N;
-            const bool ok = t < nt;
-            s_bm[t * RN + n] = ok ? M::from_raw(bg[(t0 + t) * N + n]) : M::from_float(0.0f);
-            s_c[t * RN + n] = ok ? M::from_raw(cg[(t0 + t) * N + n]) : M::from_float(0.0f);
+#pragma unroll
+        for (int k = 0; k < BU; ++k) {
+            const int u = tid + k * kThreads, rp = u / (N / G), cg = u % (N / G);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int off = (int)((2 * rp + i) * row_b + cg * 16);
+                fb[k][i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+                fc[k][i] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+            }
         }
         if (w == 0) {
+            const rsrc_t rd = make_rsrc(db + c0 * p.H * ES, (uint32_t)((nok - 1) * p.H + 1) * ES);
+            if constexpr (ES == 2)
+                fdt = __builtin_amdgcn_raw_buffer_load_b16(rd, lane * p.H * ES, 0, 0);
+            else
+                fdt = __builtin_amdgcn_raw_buffer_load_b32(rd, lane * p.H * ES, 0, 0);
+        }
+    };
+    // the registers into LDS: X transposed, B as rows and transposed, C as rows
+    auto stage = [&]() {
+#pragma unroll
+        for (int k = 0; k < XU; ++k) {
+            const int u = tid + k * kThreads, rp = u / (P / G), cg = u % (P / G);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int i = sw<Q, ES>(cg * G + j, 2 * rp);
+                const uint32_t a0 = vec_elem<ES>(fx[k][0], j), a1 = vec_elem<ES>(fx[k][1], j);
+                if constexpr (ES == 2)
+                    *reinterpret_cast<uint32_t *>(s_xt + i) = a0 | (a1 << 16);
+                else
+                    *reinterpret_cast<uint2 *>(s_xt + i) = make_uint2(a0, a1);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < BU; ++k) {
+            const int u = tid + k * kThreads, rp = u / (N / G), cg = u % (N / G);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                *reinterpret_cast<u32x4 *>(s_b + sw<N, ES>(2 * rp + i, cg * G)) = fb[k][i];
+                *reinterpret_cast<u32x4 *>(s_c + sw<N, ES>(2 * rp + i, cg * G)) = fc[k][i];
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int i = sw<Q, ES>(cg * G + j, 2 * rp);
+                const uint32_t a0 = vec_elem<ES>(fb[k][0], j), a1 = vec_elem<ES>(fb[k][1], j);
+                if constexpr (ES == 2)
+                    *reinterpret_cast<uint32_t *>(s_bt + i) = a0 | (a1 << 16);
+                else
+                    *reinterpret_cast<uint2 *>(s_bt + i) = make_uint2(a0, a1);
+            }
+        }
+    };
+
+    if (L > 0)
+        fetch(0);
+    for (int64_t t0 = 0; t0 < L; t0 += Q) {
+        const int nt = (int)min((int64_t)Q, L - t0);
+        const uint32_t ybytes = (uint32_t)(nt - 1) * row_x + P * ES;
+        // gate of this lane's outputs (rows 16 rt + 4g + v), wanted at the end of the chunk
+        uint32_t fz[16];
+        if constexpr (GATED) {
+            const rsrc_t rz = make_rsrc(zb + t0 * row_x, ybytes);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int off = (int)((16 * (q >> 2) + 4 * g + (q & 3)) * row_x + pc * ES);
+                if constexpr (ES == 2)
+                    fz[q] = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
+                else
+                    fz[q] = __builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0);
+            }
+        }
+
+        // ---- the chunk into LDS; Delta and the decays; the next chunk's loads ----
+        stage();
+        if (w == 0) {
             const int t = lane;
-            const float dl = t < nt ? softplus_f(load_val(dtg, (t0 + t) * p.H) + dtb) : 0.0f;
+            const float dv = ES == 2 ? __uint_as_float(fdt << 16) : __uint_as_float(fdt);
+            const float dl = t < nt ? softplus_f(dv + dtb) : 0.0f;
             float cs = dl * a2, csl = 0.0f;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) { // inclusive prefix sum over the 64 steps
@@ -234,87 +336,164 @@ ssd_chunk_kernel(SsdArgs p)
                     float sh, e;
                     two_sum(cs, vh, sh, e);
                     const float l = csl + vl + e;
-                    cs = sh + l;               // renormalise (|sh| >= |l|)
+                    cs = sh + l; // renormalise (|sh| >= |l|)
                     csl = l - (cs - sh);
                 }
             }
+            const float ce = __shfl(cs, 63, 64), cel = __shfl(csl, 63, 64);
             s_cs[t] = cs;
             s_csl[t] = csl;
             s_dl[t] = dl;
+            s_w[t] = hw_exp2((ce - cs) + (cel - csl)) * dl;
+            s_e[t] = hw_exp2(cs + csl);
+            if (lane == 0)
+                s_dec = hw_exp2(ce + cel);
         }
-        __syncthreads();
+        if (t0 + Q < L)
+            fetch(t0 + Q);
+        lds_barrier();
 
-        // ---- S = C B^T (this wave's tile), the weights of M; Btil^T ----
-        f32x16 sacc = {};
-        tile_mma<T, N>(sacc, s_c, RN, ti0, s_bm, RN, tj0, lane);
-        float mv[16];
+        // ---- the causal tiles of S = C B^T given to this wave, weighted into M ----
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int i = ti0 + acc_row(v, lane), j = tj0 + acc_col(lane);
-            mv[v] = j <= i ? sacc[v] * hw_exp2((s_cs[i] - s_cs[j]) + (s_csl[i] - s_csl[j])) * s_dl[j]
-                           : 0.0f;
-        }
-        const float cs_end = s_cs[Q - 1], cs_endl = s_csl[Q - 1];
-        for (int e = tid; e < Q * N; e += kThreads) {
-            const int t = e % Q, n = e / Q;
-            const float wgt = hw_exp2((cs_end - s_cs[t]) + (cs_endl - s_csl[t])) * s_dl[t];
-            put_split<T>(s_bt, s_btl, n * RQ + t, M::to_float(s_bm[t * RN + n]) * wgt);
-        }
-        __syncthreads(); // B is no longer read: M takes its place
+        for (int q = 0; q < 3; ++q) {
+            const int k = w + 4 * q; // tiles in row order: (0,0) (1,0) (1,1) (2,0) ...
+            if (k < 10) {
+                const int r = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3, c = k - r * (r + 1) / 2;
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int i = ti0 + acc_row(v, lane), j = tj0 + acc_col(lane);
-            put_split<T>(s_bm, s_ml, i * RQ + j, mv[v]);
-        }
-        __syncthreads();
-
-        // ---- Y = M X + diag(exp(cs)) C H_in + D X, gate, store ----
-        f32x16 yacc = {}, oacc = {};
-        tile_mma_split_a<T, Q>(yacc, s_bm, s_ml, RQ, ti0, s_xt, RQ, tj0, lane);
-        tile_mma_split_b<T, N>(oacc, s_c, RN, ti0, s_ht, s_htl, RN, tj0, lane);
+                for (int ks = 0; ks < N / KI; ++ks)
+                    acc = M::mma(frag<T>(s_c, sw<N, ES>(16 * r + r16, KI * ks + KL * g)),
+                                 frag<T>(s_b, sw<N, ES>(16 * c + r16, KI * ks + KL * g)), acc);
+                const int s = 16 * c + r16;
+                const float css = s_cs[s], csls = s_csl[s], dls = s_dl[s];
+                const f32x4 cst = *reinterpret_cast<const f32x4 *>(s_cs + 16 * r + 4 * g);
+                const f32x4 cstl = *reinterpret_cast<const f32x4 *>(s_csl + 16 * r + 4 * g);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int i = ti0 + acc_row(v, lane), pc = tj0 + acc_col(lane);
-            if (i < nt) {
-                const float xv = M::to_float(s_xt[pc * RQ + i]);
-                float yv = yacc[v] + hw_exp2(s_cs[i] + s_csl[i]) * oacc[v] + Dh * xv;
-                if (GATED)
-                    yv *= silu_f(load_val(zg, (t0 + i) * Dn + pc));
-                store_val(yg, (t0 + i) * Dn + pc, yv);
+                for (int v = 0; v < 4; ++v) {
+                    const int t = 16 * r + 4 * g + v;
+                    float m = s <= t ? acc[v] * hw_exp2((cst[v] - css) + (cstl[v] - csls)) * dls
+                                     : 0.0f;
+                    if (s == t)
+                        m += Dh;
+                    const int i = sw<Q, ES>(t, s);
+                    if constexpr (M::SPLIT)
+                        split_bf16(m, s_m[i], s_m[Q * Q + i]);
+                    else
+                        s_m[i] = m;
+                }
             }
         }
 
-        // ---- H_out = exp(cs_end) H_in + Btil^T X ----
-        const float dec = hw_exp2(cs_end + cs_endl);
+        // ---- Y = diag(exp(cs)) C H_in on this wave's columns ----
+        f32x4 yacc[4];
 #pragma unroll
-        for (int m = 0; m < HT; ++m) {
-            const int tau = w * HT + m;
+        for (int rt = 0; rt < 4; ++rt)
+            yacc[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                hacc[m][v] *= dec;
-            tile_mma_split_a<T, Q>(hacc[m], s_bt, s_btl, RQ, 32 * (tau >> 1), s_xt, RQ,
-                                   32 * (tau & 1), lane);
+        for (int ks = 0; ks < N / KI; ++ks) {
+            if constexpr (KL == 8) {
+                // operand slot (g, e) <-> n = 32 ks + 16 (e / 4) + 4 g + e % 4
+                bf16x8 hh, hl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    __bf16 a, c;
+                    split_bf16(hacc[2 * ks + e / 4][e % 4], a, c);
+                    hh[e] = a;
+                    hl[e] = c;
+                }
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int t = 16 * rt + r16;
+                    const bf16x4 c0 =
+                        *reinterpret_cast<const bf16x4 *>(s_c + sw<N, ES>(t, 32 * ks + 4 * g));
+                    const bf16x4 c1 =
+                        *reinterpret_cast<const bf16x4 *>(s_c + sw<N, ES>(t, 32 * ks + 16 + 4 * g));
+                    const bf16x8 cf = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    yacc[rt] = M::mma(cf, hh, yacc[rt]);
+                    yacc[rt] = M::mma(cf, hl, yacc[rt]);
+                }
+            } else {
+                // operand slot g <-> n = 16 (ks / 4) + 4 g + ks % 4
+                const float hv = hacc[ks / 4][ks % 4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    yacc[rt] = M::mma(s_c[sw<N, ES>(16 * rt + r16, 16 * (ks / 4) + 4 * g + ks % 4)],
+                                      hv, yacc[rt]);
+            }
         }
-        __syncthreads(); // every wave has read H_in (and X, C, M, Btil)
 #pragma unroll
-        for (int m = 0; m < HT; ++m) {
-            const int tau = w * HT + m, n0 = 32 * (tau >> 1), p0 = 32 * (tau & 1);
+        for (int rt = 0; rt < 4; ++rt)
+            yacc[rt] *= *reinterpret_cast<const f32x4 *>(s_e + 16 * rt + 4 * g);
+
+        // ---- H_out = exp(cs_end) H_in + B^T Xtil on this wave's columns ----
+        F xf[Q / KI]; // X^T operands of this lane's column, also used by M X below
+        {
+            const float dec = s_dec;
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                put_split<T>(s_ht, s_htl, (p0 + acc_col(lane)) * RN + n0 + acc_row(v, lane),
-                             hacc[m][v]);
+            for (int m = 0; m < NT; ++m)
+                hacc[m] *= dec;
+#pragma unroll
+            for (int js = 0; js < Q / KI; ++js) {
+                const int tk = KI * js + KL * g;
+                xf[js] = frag<T>(s_xt, sw<Q, ES>(pc, tk));
+                F xh, xl;
+                if constexpr (KL == 8) {
+                    const f32x4 w0 = *reinterpret_cast<const f32x4 *>(s_w + tk);
+                    const f32x4 w1 = *reinterpret_cast<const f32x4 *>(s_w + tk + 4);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        __bf16 a, c;
+                        split_bf16(M::to_float(xf[js][e]) * (e < 4 ? w0[e] : w1[e - 4]), a, c);
+                        xh[e] = a;
+                        xl[e] = c;
+                    }
+                } else {
+                    xh = xf[js] * s_w[tk];
+                    xl = 0.0f;
+                }
+#pragma unroll
+                for (int m = 0; m < NT; ++m) {
+                    const F a = frag<T>(s_bt, sw<Q, ES>(16 * m + r16, tk));
+                    hacc[m] = M::mma(a, xh, hacc[m]);
+                    if constexpr (M::SPLIT)
+                        hacc[m] = M::mma(a, xl, hacc[m]);
+                }
+            }
+        }
+        lds_barrier(); // M complete
+
+        // ---- Y += M X (D included), gate, store ----
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int js = 0; js <= (16 * rt + 15) / KI; ++js) {
+                const int i = sw<Q, ES>(16 * rt + r16, KI * js + KL * g);
+                yacc[rt] = M::mma(frag<T>(s_m, i), xf[js], yacc[rt]);
+                if constexpr (M::SPLIT)
+                    yacc[rt] = M::mma(frag<T>(s_m + Q * Q, i), xf[js], yacc[rt]);
+            }
+        }
+        const rsrc_t ry = make_rsrc(yb + t0 * row_x, ybytes);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            float yv = yacc[q >> 2][q & 3];
+            if constexpr (GATED)
+                yv *= silu_f(ES == 2 ? __uint_as_float(fz[q] << 16) : __uint_as_float(fz[q]));
+            const int off = (int)((16 * (q >> 2) + 4 * g + (q & 3)) * row_x + pc * ES);
+            if constexpr (ES == 2)
+                __builtin_amdgcn_raw_buffer_store_b16(
+                    __builtin_bit_cast(uint16_t, static_cast<__bf16>(yv)), ry, off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), ry, off, 0, 0);
         }
     }
 
     if (p.h_last) {
-        float *hl = p.h_last + ((int64_t)b * Dn + (int64_t)h * P) * N;
 #pragma unroll
-        for (int m = 0; m < HT; ++m) {
-            const int tau = w * HT + m, n0 = 32 * (tau >> 1), p0 = 32 * (tau & 1);
+        for (int m = 0; m < NT; ++m)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                hl[(int64_t)(p0 + acc_col(lane)) * N + n0 + acc_row(v, lane)] = hacc[m][v];
-        }
+            for (int v = 0; v < 4; ++v)
+                p.h_last[hrow + 16 * m + 4 * g + v] = hacc[m][v];
     }
 }
 
