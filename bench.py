@@ -95,6 +95,9 @@ def parse():
     ap.add_argument("--bwd-only", action="store_true",
                     help="time only the backward pass on the large prefill (for profiling) and "
                          "print its JSON summary")
+    ap.add_argument("--ssd-only", action="store_true",
+                    help="time only the Mamba-2 SSD scan on its large shape (for profiling) and "
+                         "print its JSON summary")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB device copy three times (the reference kernel for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -364,7 +367,45 @@ def extra_workloads(dev, flush, steps):
                  "GB_s_chained_cache_warm": round(dbytes / (loop_ms * 1e-3) / 1e9, 1),
                  "gchan_steps_per_s": round(bd / (med * 1e-3) / 1e9, 2),
                  "hbm_frac": round(dbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del t, y
+    torch.cuda.empty_cache()
+    # Mamba-2 SSD scan (chunked, on the matrix cores) on its large shape
+    out["ssd_large"] = ssd_workload(dev, flush, steps)
     return out
+
+
+def ssd_workload(dev, flush, steps):
+    """The SSD scan on the large shape: batch 8, L 4096, 80 heads of 64 channels, d_state
+    128, bf16 activations, gated, final state returned.  Bytes: x, z and y once each, dt, B
+    and C once, the final state; flops: the chunked form's products over their causal
+    part (C B^T and M X over s <= t, C H_in and B^T X in full), 64-step chunks."""
+    import torch
+    import selective_state_space_72_amd as ms
+    from selective_state_space_72_amd import synth
+    sc = synth.SSD_LARGE
+    si = synth.make_ssd_inputs(sc["batch"], sc["seqlen"], sc["n_heads"], sc["head_dim"],
+                               sc["d_state"], sc["dtype"], sc["gate"], sc["h0"], sc["seed"])
+    sa = [to_dev(v, dev) for v in (si.x, si.dt, si.A, si.B, si.C)]
+    kw = dict(D=to_dev(si.D, dev), z=to_dev(si.z, dev), dt_bias=to_dev(si.dt_bias, dev))
+    y, h = ms.mamba_ssd_fwd(*sa, **kw, return_last_state=True)
+
+    def sstep():
+        ms.mamba_ssd_fwd(*sa, **kw, out=y, h_last_out=h)
+    loop_ms, med, _ = time_steps(sstep, steps, 10, flush, warm_ms=100.0)
+    ms_used = med if med is not None else loop_ms
+    tok, H, P, N, Q = sc["batch"] * sc["seqlen"], sc["n_heads"], sc["head_dim"], sc["d_state"], 64
+    es = 2
+    nbytes = tok * (3 * H * P * es + H * es + 2 * N * es) + sc["batch"] * H * P * N * 4
+    flop = tok * H * ((Q + 1) * (N + P) + 4 * N * P)
+    tf = flop / (ms_used * 1e-3) / 1e12
+    gbs = nbytes / (ms_used * 1e-3) / 1e9
+    return {"workload": "Mamba-2 SSD scan: batch 8, L 4096, 80 heads x head_dim 64, d_state "
+                        "128, bf16 x/dt/B/C/z and y, fp32 A/D/dt_bias and state, gated, final "
+                        "state returned",
+            "ms": round(ms_used, 4), "ms_back_to_back": round(loop_ms, 4),
+            "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "TFLOP_s": round(tf, 1), "mfma_bf16_frac": round(tf / 2500.0, 4),
+            "bytes_per_step": nbytes, "flop_per_step": flop}
 
 
 def main():
@@ -387,6 +428,10 @@ def main():
     torch.cuda.set_device(dev)
 
     cfg = synth.CONFIGS["c3"]
+    if args.ssd_only:
+        log("bench: SSD scan on its large shape")
+        print(json.dumps(ssd_workload(dev, make_flush(dev), args.steps)), flush=True)
+        return
     if args.bwd_only:
         log("bench: backward pass on the large prefill")
         bcase = BwdCase(cfg, dev)

@@ -39,8 +39,10 @@
 // chunk's last row, so rows past the end of the sequence read as zero and stores to them
 // are dropped.  The loads of the next chunk are issued before the current chunk's products
 // and land in registers; the block barriers wait only for LDS traffic, so those loads stay
-// in flight across them.  LDS matrices are unpadded, with their 16-byte granules permuted
-// per row (an XOR key) so that the 16 rows of one operand load fall in distinct banks.
+// in flight across them.  LDS rows are padded by 16 bytes, which puts the 16 rows of one
+// operand load in distinct banks and keeps every address an immediate offset from a
+// per-lane base; M, which has no room for padding, permutes its 16-byte granules per row
+// with an XOR key instead.
 // Blocks are numbered so that each XCD takes a contiguous range of (batch row, head) pairs:
 // the heads of one batch row share B and C in that XCD's L2.
 #include "device_math.h"
@@ -103,9 +105,18 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ float to_float(E v) { return v; }
 };
 
-// Index of element (r, c) of an LDS matrix of RL elements per row (ES bytes each): rows
-// are unpadded and the 16-byte granules of row r are XOR-permuted by a key of r, so that
-// 16 consecutive rows read at one column land in distinct banks.
+// Index of element (r, c) of an LDS matrix of RL elements per row (ES bytes each), rows
+// padded by 16 bytes.
+template <int RL, int ES>
+__device__ __forceinline__ constexpr int pd(int r, int c)
+{
+    return r * (RL + 16 / ES) + c;
+}
+template <int RL, int ES> constexpr int pd_size(int rows) { return rows * (RL + 16 / ES); }
+
+// Index of element (r, c) of an unpadded LDS matrix whose 16-byte granules in row r are
+// XOR-permuted by a key of r, so that 16 consecutive rows read at one column land in
+// distinct banks.
 template <int RL, int ES>
 __device__ __forceinline__ int sw(int r, int c)
 {
@@ -138,6 +149,18 @@ __device__ __forceinline__ void two_sum(float a, float b, float &s, float &e)
     s = a + b;
     const float bb = s - a;
     e = (a - (s - bb)) + (b - bb);
+}
+
+// v from the lane that DPP control CTRL names, in the rows of ROWS; 0 where there is none.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp0(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+
+__device__ __forceinline__ float lane_63(float v)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Raw bits of element j of a 16-byte vector of bf16 or fp32 values.
@@ -176,10 +199,10 @@ ssd_chunk_kernel(SsdArgs p)
     static_assert(N % 32 == 0 && Q == 64 && P == 64, "shape");
 
     // X^T [p][t], B [s][n], B^T [n][s], C [t][n], M [t][s] (hi, then lo when split)
-    __shared__ __attribute__((aligned(16))) E s_xt[P * Q];
-    __shared__ __attribute__((aligned(16))) E s_b[Q * N];
-    __shared__ __attribute__((aligned(16))) E s_bt[N * Q];
-    __shared__ __attribute__((aligned(16))) E s_c[Q * N];
+    __shared__ __attribute__((aligned(16))) E s_xt[pd_size<Q, ES>(P)];
+    __shared__ __attribute__((aligned(16))) E s_b[pd_size<N, ES>(Q)];
+    __shared__ __attribute__((aligned(16))) E s_bt[pd_size<Q, ES>(N)];
+    __shared__ __attribute__((aligned(16))) E s_c[pd_size<N, ES>(Q)];
     __shared__ __attribute__((aligned(16))) E s_m[NS * Q * Q];
     // per step: cumulative decay cs = cs_hi + cs_lo (a compensated sum: M uses differences
     // cs_t - cs_s, which a plain fp32 sum would lose when |cs| is large), Delta, the weight
@@ -230,11 +253,12 @@ ssd_chunk_kernel(SsdArgs p)
         s_m[e] = M::from_float(0.0f);
 
     // ---- loads of one chunk into registers; a unit is rows (2 rp, 2 rp + 1) x one 16-byte
-    // column group ----
-    constexpr int XU = (Q / 2) * (P / G) / kThreads; // X units per thread
-    constexpr int BU = (Q / 2) * (N / G) / kThreads; // B and C units per thread
-    static_assert(XU * kThreads == (Q / 2) * (P / G) && BU * kThreads == (Q / 2) * (N / G),
-                  "units");
+    // column group cg: rp = tid / 8, cg = tid % 8 + 8k for the thread's k-th unit (8 lanes
+    // cover 128 contiguous bytes of a row) ----
+    constexpr int XU = P / G / 8; // X units per thread
+    constexpr int BU = N / G / 8; // B and C units per thread
+    static_assert(XU >= 1 && BU >= 1 && (Q / 2) * 8 == kThreads, "units");
+    const int rp = tid >> 3;
     u32x4 fx[XU][2], fb[BU][2], fc[BU][2];
     uint32_t fdt = 0;
     auto fetch = [&](int64_t c0) {
@@ -244,7 +268,7 @@ ssd_chunk_kernel(SsdArgs p)
         const rsrc_t rc = make_rsrc(cb + c0 * row_b, (uint32_t)nok * row_b);
 #pragma unroll
         for (int k = 0; k < XU; ++k) {
-            const int u = tid + k * kThreads, rp = u / (P / G), cg = u % (P / G);
+            const int cg = (tid & 7) + 8 * k;
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 fx[k][i] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -252,7 +276,7 @@ ssd_chunk_kernel(SsdArgs p)
         }
 #pragma unroll
         for (int k = 0; k < BU; ++k) {
-            const int u = tid + k * kThreads, rp = u / (N / G), cg = u % (N / G);
+            const int cg = (tid & 7) + 8 * k;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int off = (int)((2 * rp + i) * row_b + cg * 16);
@@ -260,7 +284,7 @@ ssd_chunk_kernel(SsdArgs p)
                 fc[k][i] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
             }
         }
-        if (w == 0) {
+        if (w == 3) {
             const rsrc_t rd = make_rsrc(db + c0 * p.H * ES, (uint32_t)((nok - 1) * p.H + 1) * ES);
             if constexpr (ES == 2)
                 fdt = __builtin_amdgcn_raw_buffer_load_b16(rd, lane * p.H * ES, 0, 0);
@@ -272,10 +296,10 @@ ssd_chunk_kernel(SsdArgs p)
     auto stage = [&]() {
 #pragma unroll
         for (int k = 0; k < XU; ++k) {
-            const int u = tid + k * kThreads, rp = u / (P / G), cg = u % (P / G);
+            const int cg = (tid & 7) + 8 * k;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const int i = sw<Q, ES>(cg * G + j, 2 * rp);
+                const int i = pd<Q, ES>(cg * G + j, 2 * rp);
                 const uint32_t a0 = vec_elem<ES>(fx[k][0], j), a1 = vec_elem<ES>(fx[k][1], j);
                 if constexpr (ES == 2)
                     *reinterpret_cast<uint32_t *>(s_xt + i) = a0 | (a1 << 16);
@@ -285,15 +309,15 @@ ssd_chunk_kernel(SsdArgs p)
         }
 #pragma unroll
         for (int k = 0; k < BU; ++k) {
-            const int u = tid + k * kThreads, rp = u / (N / G), cg = u % (N / G);
+            const int cg = (tid & 7) + 8 * k;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                *reinterpret_cast<u32x4 *>(s_b + sw<N, ES>(2 * rp + i, cg * G)) = fb[k][i];
-                *reinterpret_cast<u32x4 *>(s_c + sw<N, ES>(2 * rp + i, cg * G)) = fc[k][i];
+                *reinterpret_cast<u32x4 *>(s_b + pd<N, ES>(2 * rp + i, cg * G)) = fb[k][i];
+                *reinterpret_cast<u32x4 *>(s_c + pd<N, ES>(2 * rp + i, cg * G)) = fc[k][i];
             }
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const int i = sw<Q, ES>(cg * G + j, 2 * rp);
+                const int i = pd<Q, ES>(cg * G + j, 2 * rp);
                 const uint32_t a0 = vec_elem<ES>(fb[k][0], j), a1 = vec_elem<ES>(fb[k][1], j);
                 if constexpr (ES == 2)
                     *reinterpret_cast<uint32_t *>(s_bt + i) = a0 | (a1 << 16);
@@ -303,8 +327,47 @@ ssd_chunk_kernel(SsdArgs p)
         }
     };
 
-    if (L > 0)
+    // Delta and the decays of the chunk at c0 (wave 3, which has one causal tile of S fewer
+    // than waves 0 and 1): an inclusive, compensated prefix sum
+    // over the 64 steps by DPP row shifts, then row broadcasts across the 16-lane rows
+    auto decays = [&](int64_t c0) {
+        const int nn = (int)min((int64_t)Q, L - c0);
+        const float dv = ES == 2 ? __uint_as_float(fdt << 16) : __uint_as_float(fdt);
+        const float dl = lane < nn ? softplus_f(dv + dtb) : 0.0f;
+        float cs = dl * a2, csl = 0.0f;
+        auto add = [&](float vh, float vl) {
+            float sh, e;
+            two_sum(cs, vh, sh, e);
+            const float l = csl + vl + e;
+            cs = sh + l; // renormalise (|sh| >= |l|)
+            csl = l - (cs - sh);
+        };
+        add(dpp0<0x111, 0xf>(cs), dpp0<0x111, 0xf>(csl)); // row_shr:1
+        add(dpp0<0x112, 0xf>(cs), dpp0<0x112, 0xf>(csl)); // row_shr:2
+        add(dpp0<0x114, 0xf>(cs), dpp0<0x114, 0xf>(csl)); // row_shr:4
+        add(dpp0<0x118, 0xf>(cs), dpp0<0x118, 0xf>(csl)); // row_shr:8
+        add(dpp0<0x142, 0xa>(cs), dpp0<0x142, 0xa>(csl)); // row_bcast:15 into rows 1 and 3
+        add(dpp0<0x143, 0xc>(cs), dpp0<0x143, 0xc>(csl)); // row_bcast:31 into rows 2 and 3
+        const float ce = lane_63(cs), cel = lane_63(csl);
+        s_cs[lane] = cs;
+        s_csl[lane] = csl;
+        s_dl[lane] = dl;
+        s_w[lane] = hw_exp2((ce - cs) + (cel - csl)) * dl;
+        s_e[lane] = hw_exp2(cs + csl);
+        if (lane == 0)
+            s_dec = hw_exp2(ce + cel);
+    };
+
+    // Pipeline: chunk c is staged into LDS while chunk c - 1 finishes (M X and the stores),
+    // and its global loads were issued while chunk c - 2 did.
+    if (L > 0) {
         fetch(0);
+        stage();
+        if (w == 3)
+            decays(0);
+        if (Q < L)
+            fetch(Q);
+    }
     for (int64_t t0 = 0; t0 < L; t0 += Q) {
         const int nt = (int)min((int64_t)Q, L - t0);
         const uint32_t ybytes = (uint32_t)(nt - 1) * row_x + P * ES;
@@ -321,37 +384,7 @@ ssd_chunk_kernel(SsdArgs p)
                     fz[q] = __builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0);
             }
         }
-
-        // ---- the chunk into LDS; Delta and the decays; the next chunk's loads ----
-        stage();
-        if (w == 0) {
-            const int t = lane;
-            const float dv = ES == 2 ? __uint_as_float(fdt << 16) : __uint_as_float(fdt);
-            const float dl = t < nt ? softplus_f(dv + dtb) : 0.0f;
-            float cs = dl * a2, csl = 0.0f;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) { // inclusive prefix sum over the 64 steps
-                const float vh = __shfl_up(cs, o, 64), vl = __shfl_up(csl, o, 64);
-                if (lane >= o) {
-                    float sh, e;
-                    two_sum(cs, vh, sh, e);
-                    const float l = csl + vl + e;
-                    cs = sh + l; // renormalise (|sh| >= |l|)
-                    csl = l - (cs - sh);
-                }
-            }
-            const float ce = __shfl(cs, 63, 64), cel = __shfl(csl, 63, 64);
-            s_cs[t] = cs;
-            s_csl[t] = csl;
-            s_dl[t] = dl;
-            s_w[t] = hw_exp2((ce - cs) + (cel - csl)) * dl;
-            s_e[t] = hw_exp2(cs + csl);
-            if (lane == 0)
-                s_dec = hw_exp2(ce + cel);
-        }
-        if (t0 + Q < L)
-            fetch(t0 + Q);
-        lds_barrier();
+        lds_barrier(); // this chunk is in LDS; the previous chunk's M is no longer read
 
         // ---- the causal tiles of S = C B^T given to this wave, weighted into M ----
 #pragma unroll
@@ -362,8 +395,8 @@ ssd_chunk_kernel(SsdArgs p)
                 f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ks = 0; ks < N / KI; ++ks)
-                    acc = M::mma(frag<T>(s_c, sw<N, ES>(16 * r + r16, KI * ks + KL * g)),
-                                 frag<T>(s_b, sw<N, ES>(16 * c + r16, KI * ks + KL * g)), acc);
+                    acc = M::mma(frag<T>(s_c, pd<N, ES>(16 * r + r16, KI * ks + KL * g)),
+                                 frag<T>(s_b, pd<N, ES>(16 * c + r16, KI * ks + KL * g)), acc);
                 const int s = 16 * c + r16;
                 const float css = s_cs[s], csls = s_csl[s], dls = s_dl[s];
                 const f32x4 cst = *reinterpret_cast<const f32x4 *>(s_cs + 16 * r + 4 * g);
@@ -405,9 +438,9 @@ ssd_chunk_kernel(SsdArgs p)
                 for (int rt = 0; rt < 4; ++rt) {
                     const int t = 16 * rt + r16;
                     const bf16x4 c0 =
-                        *reinterpret_cast<const bf16x4 *>(s_c + sw<N, ES>(t, 32 * ks + 4 * g));
+                        *reinterpret_cast<const bf16x4 *>(s_c + pd<N, ES>(t, 32 * ks + 4 * g));
                     const bf16x4 c1 =
-                        *reinterpret_cast<const bf16x4 *>(s_c + sw<N, ES>(t, 32 * ks + 16 + 4 * g));
+                        *reinterpret_cast<const bf16x4 *>(s_c + pd<N, ES>(t, 32 * ks + 16 + 4 * g));
                     const bf16x8 cf = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
                     yacc[rt] = M::mma(cf, hh, yacc[rt]);
                     yacc[rt] = M::mma(cf, hl, yacc[rt]);
@@ -417,7 +450,7 @@ ssd_chunk_kernel(SsdArgs p)
                 const float hv = hacc[ks / 4][ks % 4];
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
-                    yacc[rt] = M::mma(s_c[sw<N, ES>(16 * rt + r16, 16 * (ks / 4) + 4 * g + ks % 4)],
+                    yacc[rt] = M::mma(s_c[pd<N, ES>(16 * rt + r16, 16 * (ks / 4) + 4 * g + ks % 4)],
                                       hv, yacc[rt]);
             }
         }
@@ -435,7 +468,7 @@ ssd_chunk_kernel(SsdArgs p)
 #pragma unroll
             for (int js = 0; js < Q / KI; ++js) {
                 const int tk = KI * js + KL * g;
-                xf[js] = frag<T>(s_xt, sw<Q, ES>(pc, tk));
+                xf[js] = frag<T>(s_xt, pd<Q, ES>(pc, tk));
                 F xh, xl;
                 if constexpr (KL == 8) {
                     const f32x4 w0 = *reinterpret_cast<const f32x4 *>(s_w + tk);
@@ -453,14 +486,23 @@ ssd_chunk_kernel(SsdArgs p)
                 }
 #pragma unroll
                 for (int m = 0; m < NT; ++m) {
-                    const F a = frag<T>(s_bt, sw<Q, ES>(16 * m + r16, tk));
+                    const F a = frag<T>(s_bt, pd<Q, ES>(16 * m + r16, tk));
                     hacc[m] = M::mma(a, xh, hacc[m]);
                     if constexpr (M::SPLIT)
                         hacc[m] = M::mma(a, xl, hacc[m]);
                 }
             }
         }
-        lds_barrier(); // M complete
+        lds_barrier(); // M complete; X, B, C and the decays of this chunk no longer read
+
+        // ---- the next chunk into LDS and its decays; the loads of the one after ----
+        if (t0 + Q < L) {
+            stage();
+            if (w == 3)
+                decays(t0 + Q);
+            if (t0 + 2 * Q < L)
+                fetch(t0 + 2 * Q);
+        }
 
         // ---- Y += M X (D included), gate, store ----
 #pragma unroll
