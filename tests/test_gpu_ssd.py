@@ -1,8 +1,8 @@
 """GPU parity of the Mamba-2 SSD scan (chunked, matrix cores) against the fp64 oracle.
 
 The SSD recurrence is the selective scan with the step size and A shared by the channels
-of a head, so the reference is the scan oracle on inputs expanded per channel (dt and its
-bias per head -> per channel, A[h] -> A[d, n] for all n, D[h] -> D[d]).  Shapes cover
+of a head, so the reference is the scan oracle on inputs expanded per channel
+(tests/ssd_reference.py, pinned against the dual form in tests/test_ssd_reference.py).  Shapes cover
 several 64-step chunks with a ragged last chunk, several heads, both compiled d_state
 values, h0 and the gate; the large shape in the benchmark's configuration is checked on
 sampled heads.  Metric and bounds as for the scan (1e-5 fp32, 2e-2 bf16 inputs).
@@ -13,10 +13,10 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 import selective_state_space_72_amd as ms
 from selective_state_space_72_amd import synth
 from gpu_helpers import TOL, from_dev, log, metric, to_dev
+from ssd_reference import ssd_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -31,23 +31,8 @@ def run_gpu(s, *, use_D=True, use_bias=True, use_h0=True):
     return y, h
 
 
-def run_oracle(s, heads=None, *, use_D=True, use_bias=True, use_h0=True):
-    """Oracle on the channels of `heads` (all if None)."""
-    f = lambda a: synth.to_f64(a, s.dtype)  # noqa: E731
-    P = s.head_dim
-    H = s.dt.shape[2]
-    heads = np.arange(H) if heads is None else np.asarray(heads)
-    ch = (heads[:, None] * P + np.arange(P)[None, :]).reshape(-1)     # channels of the heads
-    hd = np.repeat(heads, P)                                          # head of each channel
-    N = s.B.shape[2]
-    x = f(np.ascontiguousarray(s.x[:, :, ch]))
-    delta = np.ascontiguousarray(f(s.dt)[:, :, hd])
-    A = np.repeat(s.A[hd].astype(np.float64)[:, None], N, axis=1)
-    return oracle.load().scan(
-        x, delta, A, f(s.B), f(s.C), D=s.D[hd].astype(np.float64) if use_D else None,
-        z=f(np.ascontiguousarray(s.z[:, :, ch])) if s.z is not None else None,
-        bias=s.dt_bias[hd].astype(np.float64) if use_bias else None,
-        h0=s.h0[:, ch].astype(np.float64) if (use_h0 and s.h0 is not None) else None), ch
+def run_oracle(s, heads=None, **flags):
+    return ssd_oracle(s, heads, **flags)
 
 
 def check(s, label, **flags):
