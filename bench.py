@@ -408,6 +408,18 @@ def ssd_workload(dev, flush, steps):
             "bytes_per_step": nbytes, "flop_per_step": flop}
 
 
+def copy_calibration(dev):
+    """Three 512 MiB device copies: the reference kernel that FETCH_SIZE / WRITE_SIZE
+    counters of the measured kernels are scaled by."""
+    import torch
+    src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     args = parse()
     if args.only_main:
@@ -430,18 +442,17 @@ def main():
     cfg = synth.CONFIGS["c3"]
     if args.ssd_only:
         log("bench: SSD scan on its large shape")
-        print(json.dumps(ssd_workload(dev, make_flush(dev), args.steps)), flush=True)
+        res = ssd_workload(dev, make_flush(dev), args.steps)
+        if args.copy_calibration:
+            copy_calibration(dev)
+        print(json.dumps(res), flush=True)
         return
     if args.bwd_only:
         log("bench: backward pass on the large prefill")
         bcase = BwdCase(cfg, dev)
         loop_ms, _, _ = time_steps(bcase.step, args.steps, args.warmup)
         if args.copy_calibration:
-            src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
-            dst = torch.empty_like(src)
-            for _ in range(3):
-                dst.copy_(src)
-            torch.cuda.synchronize()
+            copy_calibration(dev)
         print(json.dumps({"workload": "backward of the large-model prefill scan",
                           "steps": args.steps, "ms_per_step": round(loop_ms, 4),
                           "min_bytes_per_step": bcase.min_bytes,
@@ -491,12 +502,7 @@ def main():
     del case
     torch.cuda.empty_cache()
     if args.copy_calibration:
-        src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(dev)
     if not args.no_extra:
         log("bench: other workloads")
         line["other_workloads"] = extra_workloads(dev, flush, args.steps)

@@ -105,26 +105,25 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ float to_float(E v) { return v; }
 };
 
-// Index of element (r, c) of an LDS matrix of RL elements per row (ES bytes each), rows
-// padded by 16 bytes.
-template <int RL, int ES>
-__device__ __forceinline__ constexpr int pd(int r, int c)
-{
-    return r * (RL + 16 / ES) + c;
-}
-template <int RL, int ES> constexpr int pd_size(int rows) { return rows * (RL + 16 / ES); }
-
-// Index of element (r, c) of an unpadded LDS matrix whose 16-byte granules in row r are
-// XOR-permuted by a key of r, so that 16 consecutive rows read at one column land in
-// distinct banks.
-template <int RL, int ES>
-__device__ __forceinline__ int sw(int r, int c)
-{
-    constexpr int G = 16 / ES, RB = RL * ES;
-    static_assert(RB % 128 == 0, "row bytes");
-    const int key = RB == 128 ? (r >> 1) & 7 : r & 15;
-    return r * RL + (((c / G) ^ key) * G) + (c % G);
-}
+// Layout of an LDS matrix of RL elements per row (ES bytes each).  Padded: rows padded by
+// 16 bytes (addresses stay affine, so unrolled accesses are immediate offsets).  XOR: rows
+// unpadded, the 16-byte granules of row r permuted by a key of r.  Either puts the 16 rows
+// of one operand load (one column) in distinct banks.
+template <int RL, int ES, bool XOR> struct Lay;
+template <int RL, int ES> struct Lay<RL, ES, false> {
+    static constexpr int size(int rows) { return rows * (RL + 16 / ES); }
+    static __device__ __forceinline__ int idx(int r, int c) { return r * (RL + 16 / ES) + c; }
+};
+template <int RL, int ES> struct Lay<RL, ES, true> {
+    static constexpr int size(int rows) { return rows * RL; }
+    static __device__ __forceinline__ int idx(int r, int c)
+    {
+        constexpr int G = 16 / ES, RB = RL * ES;
+        static_assert(RB % 128 == 0, "row bytes");
+        const int key = RB == 128 ? (r >> 1) & 7 : r & 15;
+        return r * RL + (((c / G) ^ key) * G) + (c % G);
+    }
+};
 
 // MFMA operand of KL contiguous elements at index i of an LDS matrix.
 template <typename T>
@@ -199,11 +198,16 @@ ssd_chunk_kernel(SsdArgs p)
     static_assert(N % 32 == 0 && Q == 64 && P == 64, "shape");
 
     // X^T [p][t], B [s][n], B^T [n][s], C [t][n], M [t][s] (hi, then lo when split)
-    __shared__ __attribute__((aligned(16))) E s_xt[pd_size<Q, ES>(P)];
-    __shared__ __attribute__((aligned(16))) E s_b[pd_size<N, ES>(Q)];
-    __shared__ __attribute__((aligned(16))) E s_bt[pd_size<Q, ES>(N)];
-    __shared__ __attribute__((aligned(16))) E s_c[pd_size<N, ES>(Q)];
-    __shared__ __attribute__((aligned(16))) E s_m[NS * Q * Q];
+    typedef Lay<Q, ES, false> LXT;
+    typedef Lay<N, ES, false> LB;
+    typedef Lay<Q, ES, false> LBT;
+    typedef Lay<N, ES, false> LC;
+    typedef Lay<Q, ES, true> LM; // no room for padding
+    __shared__ __attribute__((aligned(16))) E s_xt[LXT::size(P)];
+    __shared__ __attribute__((aligned(16))) E s_b[LB::size(Q)];
+    __shared__ __attribute__((aligned(16))) E s_bt[LBT::size(N)];
+    __shared__ __attribute__((aligned(16))) E s_c[LC::size(Q)];
+    __shared__ __attribute__((aligned(16))) E s_m[NS * LM::size(Q)];
     // per step: cumulative decay cs = cs_hi + cs_lo (a compensated sum: M uses differences
     // cs_t - cs_s, which a plain fp32 sum would lose when |cs| is large), Delta, the weight
     // of Xtil, exp(cs); and the chunk's total decay
@@ -249,7 +253,7 @@ ssd_chunk_kernel(SsdArgs p)
             hacc[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     // M's tiles above the diagonal stay zero; the causal tiles are rewritten every chunk
-    for (int e = tid; e < NS * Q * Q; e += kThreads)
+    for (int e = tid; e < NS * LM::size(Q); e += kThreads)
         s_m[e] = M::from_float(0.0f);
 
     // ---- loads of one chunk into registers; a unit is rows (2 rp, 2 rp + 1) x one 16-byte
@@ -299,7 +303,7 @@ ssd_chunk_kernel(SsdArgs p)
             const int cg = (tid & 7) + 8 * k;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const int i = pd<Q, ES>(cg * G + j, 2 * rp);
+                const int i = LXT::idx(cg * G + j, 2 * rp);
                 const uint32_t a0 = vec_elem<ES>(fx[k][0], j), a1 = vec_elem<ES>(fx[k][1], j);
                 if constexpr (ES == 2)
                     *reinterpret_cast<uint32_t *>(s_xt + i) = a0 | (a1 << 16);
@@ -312,12 +316,12 @@ ssd_chunk_kernel(SsdArgs p)
             const int cg = (tid & 7) + 8 * k;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                *reinterpret_cast<u32x4 *>(s_b + pd<N, ES>(2 * rp + i, cg * G)) = fb[k][i];
-                *reinterpret_cast<u32x4 *>(s_c + pd<N, ES>(2 * rp + i, cg * G)) = fc[k][i];
+                *reinterpret_cast<u32x4 *>(s_b + LB::idx(2 * rp + i, cg * G)) = fb[k][i];
+                *reinterpret_cast<u32x4 *>(s_c + LC::idx(2 * rp + i, cg * G)) = fc[k][i];
             }
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const int i = pd<Q, ES>(cg * G + j, 2 * rp);
+                const int i = LBT::idx(cg * G + j, 2 * rp);
                 const uint32_t a0 = vec_elem<ES>(fb[k][0], j), a1 = vec_elem<ES>(fb[k][1], j);
                 if constexpr (ES == 2)
                     *reinterpret_cast<uint32_t *>(s_bt + i) = a0 | (a1 << 16);
@@ -395,8 +399,8 @@ ssd_chunk_kernel(SsdArgs p)
                 f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ks = 0; ks < N / KI; ++ks)
-                    acc = M::mma(frag<T>(s_c, pd<N, ES>(16 * r + r16, KI * ks + KL * g)),
-                                 frag<T>(s_b, pd<N, ES>(16 * c + r16, KI * ks + KL * g)), acc);
+                    acc = M::mma(frag<T>(s_c, LC::idx(16 * r + r16, KI * ks + KL * g)),
+                                 frag<T>(s_b, LB::idx(16 * c + r16, KI * ks + KL * g)), acc);
                 const int s = 16 * c + r16;
                 const float css = s_cs[s], csls = s_csl[s], dls = s_dl[s];
                 const f32x4 cst = *reinterpret_cast<const f32x4 *>(s_cs + 16 * r + 4 * g);
@@ -408,9 +412,9 @@ ssd_chunk_kernel(SsdArgs p)
                                      : 0.0f;
                     if (s == t)
                         m += Dh;
-                    const int i = sw<Q, ES>(t, s);
+                    const int i = LM::idx(t, s);
                     if constexpr (M::SPLIT)
-                        split_bf16(m, s_m[i], s_m[Q * Q + i]);
+                        split_bf16(m, s_m[i], s_m[LM::size(Q) + i]);
                     else
                         s_m[i] = m;
                 }
@@ -438,9 +442,9 @@ ssd_chunk_kernel(SsdArgs p)
                 for (int rt = 0; rt < 4; ++rt) {
                     const int t = 16 * rt + r16;
                     const bf16x4 c0 =
-                        *reinterpret_cast<const bf16x4 *>(s_c + pd<N, ES>(t, 32 * ks + 4 * g));
+                        *reinterpret_cast<const bf16x4 *>(s_c + LC::idx(t, 32 * ks + 4 * g));
                     const bf16x4 c1 =
-                        *reinterpret_cast<const bf16x4 *>(s_c + pd<N, ES>(t, 32 * ks + 16 + 4 * g));
+                        *reinterpret_cast<const bf16x4 *>(s_c + LC::idx(t, 32 * ks + 16 + 4 * g));
                     const bf16x8 cf = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
                     yacc[rt] = M::mma(cf, hh, yacc[rt]);
                     yacc[rt] = M::mma(cf, hl, yacc[rt]);
@@ -450,7 +454,7 @@ ssd_chunk_kernel(SsdArgs p)
                 const float hv = hacc[ks / 4][ks % 4];
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
-                    yacc[rt] = M::mma(s_c[pd<N, ES>(16 * rt + r16, 16 * (ks / 4) + 4 * g + ks % 4)],
+                    yacc[rt] = M::mma(s_c[LC::idx(16 * rt + r16, 16 * (ks / 4) + 4 * g + ks % 4)],
                                       hv, yacc[rt]);
             }
         }
@@ -468,7 +472,7 @@ ssd_chunk_kernel(SsdArgs p)
 #pragma unroll
             for (int js = 0; js < Q / KI; ++js) {
                 const int tk = KI * js + KL * g;
-                xf[js] = frag<T>(s_xt, pd<Q, ES>(pc, tk));
+                xf[js] = frag<T>(s_xt, LXT::idx(pc, tk));
                 F xh, xl;
                 if constexpr (KL == 8) {
                     const f32x4 w0 = *reinterpret_cast<const f32x4 *>(s_w + tk);
@@ -486,7 +490,7 @@ ssd_chunk_kernel(SsdArgs p)
                 }
 #pragma unroll
                 for (int m = 0; m < NT; ++m) {
-                    const F a = frag<T>(s_bt, pd<Q, ES>(16 * m + r16, tk));
+                    const F a = frag<T>(s_bt, LBT::idx(16 * m + r16, tk));
                     hacc[m] = M::mma(a, xh, hacc[m]);
                     if constexpr (M::SPLIT)
                         hacc[m] = M::mma(a, xl, hacc[m]);
@@ -509,10 +513,10 @@ ssd_chunk_kernel(SsdArgs p)
         for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
             for (int js = 0; js <= (16 * rt + 15) / KI; ++js) {
-                const int i = sw<Q, ES>(16 * rt + r16, KI * js + KL * g);
+                const int i = LM::idx(16 * rt + r16, KI * js + KL * g);
                 yacc[rt] = M::mma(frag<T>(s_m, i), xf[js], yacc[rt]);
                 if constexpr (M::SPLIT)
-                    yacc[rt] = M::mma(frag<T>(s_m + Q * Q, i), xf[js], yacc[rt]);
+                    yacc[rt] = M::mma(frag<T>(s_m + LM::size(Q), i), xf[js], yacc[rt]);
             }
         }
         const rsrc_t ry = make_rsrc(yb + t0 * row_x, ybytes);

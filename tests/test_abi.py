@@ -401,3 +401,35 @@ def test_decode_ext_validation(lib):
                                     BASE + 256 * MB, 4, 128, 16, BF16, ms.MAMBA_DISC_EULER,
                                     ctypes.byref(e), None)
     assert st == ALIAS
+
+
+def ssd(lib, **kw):
+    a = dict(x=BASE, dt=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB,
+             C=BASE + 400 * MB, D=BASE + 500 * MB, z=BASE + 600 * MB, bias=BASE + 700 * MB,
+             h0=None, y=BASE + 800 * MB, hl=None, batch=2, L=64, H=4, P=64, N=128, dtype=BF16)
+    a.update(kw)
+    return lib.mamba_ssd_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                             a["bias"], a["h0"], a["y"], a["hl"], a["batch"], a["L"], a["H"],
+                             a["P"], a["N"], a["dtype"], None)
+
+
+def test_ssd_validation(lib):
+    assert lib.mamba_ssd_supported(64, 64) == 1 and lib.mamba_ssd_supported(64, 128) == 1
+    for p, n in ((32, 64), (128, 128), (64, 16), (64, 256), (0, 64)):
+        assert lib.mamba_ssd_supported(p, n) == 0
+    assert ssd(lib, P=32) == UNSUP and ssd(lib, N=16) == UNSUP
+    assert ssd(lib, dtype=7) == DTYPE
+    assert ssd(lib, batch=-1) == SHAPE and ssd(lib, P=0) == SHAPE and ssd(lib, L=-3) == SHAPE
+    # 64 rows of x must span fewer than 2^31 bytes (32-bit offsets within a chunk)
+    assert ssd(lib, batch=1, L=1, H=1 << 20) == UNSUP
+    assert ssd(lib, x=None) == NULL and ssd(lib, A=None) == NULL and ssd(lib, y=None) == NULL
+    assert ssd(lib, B=None) == NULL and ssd(lib, dt=None) == NULL
+    assert ssd(lib, x=BASE + 2) == ALIGN                   # x, z, B, C: 16-byte vectors
+    assert ssd(lib, C=BASE + 400 * MB + 8) == ALIGN
+    assert ssd(lib, dt=BASE + 100 * MB + 1) == ALIGN
+    assert ssd(lib, A=BASE + 200 * MB + 2) == ALIGN
+    assert ssd(lib, y=BASE + 64) == ALIAS                   # y over x
+    assert ssd(lib, hl=BASE + 300 * MB) == ALIAS            # h_last over B
+    assert ssd(lib, h0=BASE + 900 * MB, hl=BASE + 900 * MB) == ALIAS
+    assert ssd(lib, batch=0) == OK and ssd(lib, H=0) == OK
+    assert ssd(lib, L=0) == OK                              # no state asked for: nothing to do

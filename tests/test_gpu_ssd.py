@@ -102,3 +102,22 @@ def test_ssd_large_sampled():
     eh = metric(from_dev(h[:, chd].contiguous()), hr)
     log(f"ssd large, heads {heads}: y {ey:.2e}, h_last {eh:.2e}")
     assert ey <= TOL[synth.BF16] and eh <= TOL[synth.BF16]
+
+
+def test_ssd_bf16_d_state_64():
+    """bf16 with d_state 64, h0, no gate; 3 x 8 = 24 blocks (a multiple of 8: the blocks
+    are renumbered so each XCD takes a contiguous range) and a ragged last chunk."""
+    s = synth.make_ssd_inputs(3, 130, 8, d_state=64, dtype=synth.BF16, gate=False, h0=True)
+    check(s, "ssd bf16 N=64, 24 blocks")
+
+
+def test_ssd_fp32_remapped_grid():
+    s = synth.make_ssd_inputs(2, 70, 4, d_state=128, dtype=synth.F32, h0=True)
+    check(s, "ssd fp32 N=128, 8 blocks")
+
+
+def test_ssd_empty_sequence_returns_h0():
+    s = synth.make_ssd_inputs(2, 0, 3, d_state=64, dtype=synth.BF16, h0=True)
+    y, h = run_gpu(s)
+    assert y.shape == (2, 0, 3 * 64)
+    assert torch.equal(h.cpu(), torch.from_numpy(s.h0))
