@@ -201,6 +201,50 @@ class BwdCase:
                                      dh_last=t["dh_last"], out=self.out, workspace=self.ws)
 
 
+class CkptTrainCase(BwdCase):
+    """The training path with checkpoints: the forward scan also stores the state entering
+    every 8-step segment (mamba_scan_fwd(..., ckpt=)), and the backward reads them instead of
+    running a forward pass of its own (mamba_scan_bwd(..., ckpt=))."""
+
+    def __init__(self, cfg, dev):
+        import ctypes
+        import torch
+        import selective_state_space_72_amd as ms
+        self.ck = ms.mamba_scan_ckpt_buffer(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state, dev)
+        lib = ms.load_library()
+        ext = ms.ScanExt(None, None, None, None, 1)  # (only the option's presence matters)
+        nf = lib.mamba_scan_fwd_workspace_size_ext(cfg.batch, cfg.seqlen, cfg.d_inner,
+                                                   cfg.d_state, ctypes.byref(ext), None)
+        self.fws = torch.empty(max(int(nf), 1), dtype=torch.uint8, device=dev)
+        self._dev = dev
+        self.y = self.hl = None
+        super().__init__(cfg, dev)
+        nws = ms.mamba_scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state,
+                                               with_ckpt=True)
+        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        self.forward()
+        self.step()
+
+    def forward(self):
+        import selective_state_space_72_amd as ms
+        t = self.t
+        self.y, self.hl = ms.mamba_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"],
+                                            D=t["D"], z=t["z"], delta_bias=t["bias"],
+                                            h0=t["h0"], return_last_state=True, out=self.y,
+                                            h_last_out=self.hl, workspace=self.fws,
+                                            ckpt=self.ck)
+
+    def step(self):
+        import selective_state_space_72_amd as ms
+        if self.y is None:  # (the base class's first step: checkpoints not written yet)
+            self.forward()
+        t = self.t
+        self.out = ms.mamba_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["dy"],
+                                     D=t["D"], z=t["z"], delta_bias=t["bias"], h0=t["h0"],
+                                     dh_last=t["dh_last"], out=self.out, workspace=self.ws,
+                                     ckpt=self.ck)
+
+
 def time_steps(fn, steps, warmup, flush=None, warm_ms=0.0):
     """Event-timed steps on the current stream.  Returns (ms/step over the back-to-back
     loop, median ms of single steps each preceded by a MALL flush, wall ms/step).
@@ -313,6 +357,24 @@ def extra_workloads(dev, flush, steps):
             "hbm_frac": round(case.min_bytes / (ms_used * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del case
         torch.cuda.empty_cache()
+    # training path with checkpoints on the large prefill: forward storing them, backward
+    # reading them
+    cfg = synth.CONFIGS["c3"]
+    case = CkptTrainCase(cfg, dev)
+    f_loop, f_med, _ = time_steps(case.forward, max(10, steps // 4), 3, flush, warm_ms=100.0)
+    b_loop, b_med, _ = time_steps(case.step, max(10, steps // 4), 3, flush, warm_ms=100.0)
+    fm = f_med if f_med is not None else f_loop
+    bm = b_med if b_med is not None else b_loop
+    out["c3_train_ckpt"] = {
+        "workload": f"training path of the {cfg.desc} (batch {cfg.batch}, L {cfg.seqlen}, "
+                    f"d_inner {cfg.d_inner}, d_state {cfg.d_state}, {cfg.dtype}): the forward "
+                    "storing a state every 8 steps, then the backward reading them",
+        "fwd_ckpt_ms": round(fm, 4), "fwd_ckpt_ms_back_to_back": round(f_loop, 4),
+        "bwd_from_ckpt_ms": round(bm, 4), "bwd_from_ckpt_ms_back_to_back": round(b_loop, 4),
+        "train_step_ms": round(fm + bm, 4),
+        "ckpt_bytes": int(case.ck.numel() * 4)}
+    del case
+    torch.cuda.empty_cache()
     # causal depthwise conv1d + SiLU producing the scan's u, on the large-prefill shape
     ci = synth.make_conv_inputs(8, 4096, 5120, 4, synth.BF16)
     cx, cw, cb = to_dev(ci.x, dev), to_dev(ci.w, dev), to_dev(ci.bias, dev)

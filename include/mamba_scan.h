@@ -355,6 +355,38 @@ MAMBA_API mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, con
                                            size_t workspace_bytes,
                                            const mamba_scan_opts_t *opts, void *stream);
 
+/* Bytes of the checkpoint buffer that mamba_scan_fwd_ext writes (ext->ckpt) and
+ * mamba_scan_bwd_ckpt reads: (batch * ceil(d_inner / 64)) * ceil(seqlen / 8) * d_state *
+ * 64 * 4.  SIZE_MAX for negative sizes, overflow or a d_state other than 4, 8, 16, 32. */
+MAMBA_API size_t mamba_scan_ckpt_size(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                      int64_t d_state);
+
+/* Workspace size for mamba_scan_bwd_ckpt (opts may be NULL): mamba_scan_bwd_workspace_size
+ * without the checkpoint region and, on a split sequence, without the forward span
+ * summaries. */
+MAMBA_API size_t mamba_scan_bwd_ckpt_workspace_size(int64_t batch, int64_t seqlen,
+                                                    int64_t d_inner, int64_t d_state,
+                                                    const mamba_scan_opts_t *opts);
+
+/* mamba_scan_bwd_ex reading the states from ckpt, written by mamba_scan_fwd_ext (ext->ckpt)
+ * on the same inputs, instead of running a forward pass of its own.  ckpt is required when
+ * seqlen > 0 (MAMBA_ERR_NULL_ARG) and read only; it must not overlap an output or the
+ * workspace.  Results equal mamba_scan_bwd_ex's up to float32 rounding (the states are the
+ * forward scan's rather than the backward's own recomputation).  Other arguments and
+ * conventions as for mamba_scan_bwd_ex. */
+MAMBA_API mamba_status_t mamba_scan_bwd_ckpt(const void *u, const void *delta, const float *A,
+                                             const void *B, const void *C, const float *D,
+                                             const void *z, const float *delta_bias,
+                                             const float *h0, const void *dy,
+                                             const float *dh_last, const float *ckpt, void *du,
+                                             void *ddelta, float *dA, void *dB, void *dC,
+                                             float *dD, void *dz, float *d_delta_bias,
+                                             float *dh0, int64_t batch, int64_t seqlen,
+                                             int64_t d_inner, int64_t d_state,
+                                             mamba_dtype_t dtype, void *workspace,
+                                             size_t workspace_bytes,
+                                             const mamba_scan_opts_t *opts, void *stream);
+
 /* ------------------------------------------------------------------------
  * Options of the Mamba-3 formulation ("State space models and the Mamba series",
  * jsqmd.com, sections 2.1 and 2.2), taken as that page writes them.  A NULL pointer
@@ -378,12 +410,23 @@ MAMBA_API mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, con
  *
  * Both options run in the SCALAR family (AUTO selects it; ROWS or BLOCK return
  * MAMBA_ERR_UNSUPPORTED).  The extension inputs follow the alignment and aliasing rules
- * of the other inputs. */
+ * of the other inputs.
+ *
+ *   ckpt    float32 output of mamba_scan_ckpt_size bytes, nullable
+ *       the states the backward pass needs ("Understanding Mamba" section 7.3: the
+ *       backward recomputes states from stored checkpoints rather than storing every
+ *       step): the state h entering every 8-step segment s >= 1 of each (batch row,
+ *       64-channel tile), for mamba_scan_bwd_ckpt.  Its layout is internal to the
+ *       library; it is written only, 4-byte aligned, and overlaps no other argument or
+ *       the workspace (MAMBA_ERR_ALIASING).  Needs the Euler rule without lambda or
+ *       theta and d_state 4, 8, 16 or 32, and runs in the SCALAR family (else
+ *       MAMBA_ERR_UNSUPPORTED).  It does not change y or h_last. */
 typedef struct {
     const void *lambda;
     const void *u_prev;
     const void *B_prev;
     const void *theta;
+    float *ckpt;
 } mamba_scan_ext_t;
 
 /* Workspace size for mamba_scan_fwd_ext (ext and opts may be NULL). */
@@ -404,7 +447,8 @@ MAMBA_API mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, co
                                             const mamba_scan_ext_t *ext, void *stream);
 
 /* mamba_state_update_ex with the Mamba-3 options (shapes of the decode step; ext NULL =
- * none).  With lambda the caller passes the previous token's u and B as u_prev, B_prev. */
+ * none).  With lambda the caller passes the previous token's u and B as u_prev, B_prev.
+ * ext->ckpt must be NULL (MAMBA_ERR_UNSUPPORTED otherwise). */
 MAMBA_API mamba_status_t mamba_state_update_ext(float *h, const void *u, const void *delta,
                                                 const float *A, const void *B, const void *C,
                                                 const float *D, const void *z,

@@ -40,6 +40,7 @@ EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_scan_bwd_workspace_size_ex", "mamba_scan_bwd_ex",
            "mamba_scan_fwd_workspace_size_ext", "mamba_scan_fwd_ext", "mamba_state_update_ext",
            "mamba_ssd_supported", "mamba_ssd_fwd",
+           "mamba_scan_ckpt_size", "mamba_scan_bwd_ckpt_workspace_size", "mamba_scan_bwd_ckpt",
            "mamba_status_string")
 
 
@@ -65,9 +66,11 @@ class ScanOpts(ctypes.Structure):
 
 
 class ScanExt(ctypes.Structure):
-    """mamba_scan_ext_t: trapezoid mixing coefficients, look-back input, rotation rates."""
+    """mamba_scan_ext_t: trapezoid mixing coefficients, look-back input, rotation rates,
+    checkpoint output for the backward pass."""
     _fields_ = [("lambda_", ctypes.c_void_p), ("u_prev", ctypes.c_void_p),
-                ("B_prev", ctypes.c_void_p), ("theta", ctypes.c_void_p)]
+                ("B_prev", ctypes.c_void_p), ("theta", ctypes.c_void_p),
+                ("ckpt", ctypes.c_void_p)]
 
 
 _vp = ctypes.c_void_p
@@ -133,6 +136,14 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mamba_ssd_supported.argtypes = [_i64, _i64]
     lib.mamba_ssd_fwd.restype = ctypes.c_int
     lib.mamba_ssd_fwd.argtypes = [_vp] * 11 + [_i64] * 5 + [ctypes.c_int, _vp]
+    lib.mamba_scan_ckpt_size.restype = ctypes.c_size_t
+    lib.mamba_scan_ckpt_size.argtypes = [_i64] * 4
+    lib.mamba_scan_bwd_ckpt_workspace_size.restype = ctypes.c_size_t
+    lib.mamba_scan_bwd_ckpt_workspace_size.argtypes = [_i64] * 4 + [ctypes.POINTER(ScanOpts)]
+    lib.mamba_scan_bwd_ckpt.restype = ctypes.c_int
+    lib.mamba_scan_bwd_ckpt.argtypes = ([_vp] * 21 + [_i64] * 4 + [ctypes.c_int, _vp,
+                                                                     ctypes.c_size_t,
+                                                                     ctypes.POINTER(ScanOpts), _vp])
     lib.mamba_status_string.restype = ctypes.c_char_p
     lib.mamba_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -216,13 +227,16 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
                    return_last_state: bool = False, *, out=None, h_last_out=None,
                    chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
                    kernel: str = "auto", relay: int = 0, discretization: str = "euler",
-                   workspace=None, lam=None, u_prev=None, B_prev=None, theta=None) -> Tuple:
+                   workspace=None, lam=None, u_prev=None, B_prev=None, theta=None,
+                   ckpt=None) -> Tuple:
     """Selective scan over (batch, seqlen, d_inner); see include/mamba_scan.h.
 
     Returns (y, h_last) -- h_last is None unless return_last_state (or h_last_out).
     lam (batch, seqlen, d_inner): exponential-trapezoidal mixing coefficients, with the
     input before t = 0 in u_prev (batch, d_inner) and B_prev (batch, d_state); theta
     (batch, seqlen, d_state / 2): rotation rates of the state pairs (see mamba_scan_ext_t).
+    ckpt: a float32 tensor of mamba_scan_ckpt_size(...) bytes that receives the states the
+    backward pass needs (for mamba_scan_bwd(..., ckpt=...)).
     """
     torch = _torch()
     lib = load_library()
@@ -254,11 +268,13 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
     ext = ScanExt(_ptr(lam, "lam", (batch, seqlen, d_inner), act, dev),
                   _ptr(u_prev, "u_prev", (batch, d_inner), act, dev),
                   _ptr(B_prev, "B_prev", (batch, d_state), act, dev),
-                  _ptr(theta, "theta", (batch, seqlen, d_state // 2), act, dev))
+                  _ptr(theta, "theta", (batch, seqlen, d_state // 2), act, dev),
+                  _ckpt_ptr(ckpt, batch, seqlen, d_inner, d_state, dev))
     if seqlen == 0:
         # empty tensors have no address; only the presence of an option matters here
         ext.lambda_ = ext.lambda_ or (1 if lam is not None else None)
         ext.theta = ext.theta or (1 if theta is not None else None)
+        ext.ckpt = ext.ckpt or (1 if ckpt is not None else None)
 
     opts = _opts(chunk_len, waves, n_spans, kernel, relay, discretization)
     need = lib.mamba_scan_fwd_workspace_size_ext(batch, seqlen, d_inner, d_state,
@@ -384,13 +400,43 @@ def mamba_conv1d_silu_update(state, x, w, conv_bias=None, *, out=None):
 
 
 def mamba_scan_bwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state: int,
-                                  n_spans: int = 0) -> int:
+                                  n_spans: int = 0, with_ckpt: bool = False) -> int:
+    """Workspace bytes of mamba_scan_bwd (with_ckpt: of the variant that reads the forward
+    pass's checkpoints)."""
     lib = load_library()
     o = ScanOpts(0, 0, int(n_spans), 0, 0, 0)
-    n = lib.mamba_scan_bwd_workspace_size_ex(batch, seqlen, d_inner, d_state, ctypes.byref(o))
+    f = lib.mamba_scan_bwd_ckpt_workspace_size if with_ckpt else lib.mamba_scan_bwd_workspace_size_ex
+    n = f(batch, seqlen, d_inner, d_state, ctypes.byref(o))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid sizes for mamba_scan_bwd")
     return int(n)
+
+
+def mamba_scan_ckpt_size(batch: int, seqlen: int, d_inner: int, d_state: int) -> int:
+    """Bytes of the checkpoint buffer (mamba_scan_fwd(..., ckpt=) / mamba_scan_bwd(..., ckpt=))."""
+    n = load_library().mamba_scan_ckpt_size(batch, seqlen, d_inner, d_state)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes or d_state for checkpoints")
+    return int(n)
+
+
+def mamba_scan_ckpt_buffer(batch: int, seqlen: int, d_inner: int, d_state: int, device):
+    """A float32 tensor of the checkpoint buffer's size."""
+    torch = _torch()
+    n = mamba_scan_ckpt_size(batch, seqlen, d_inner, d_state)
+    return torch.empty(max(n // 4, 1), dtype=torch.float32, device=device)
+
+
+def _ckpt_ptr(ckpt, batch, seqlen, d_inner, d_state, dev):
+    if ckpt is None:
+        return None
+    torch = _torch()
+    need = mamba_scan_ckpt_size(batch, seqlen, d_inner, d_state)
+    if ckpt.dtype != torch.float32 or ckpt.device != dev or not ckpt.is_contiguous() or \
+            ckpt.numel() * 4 < need:
+        raise ValueError(f"ckpt must be a contiguous float32 tensor of at least {need} bytes "
+                         f"on {dev}")
+    return ckpt.data_ptr() if need > 0 else None
 
 
 GRAD_NAMES = ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0")
@@ -398,13 +444,15 @@ GRAD_NAMES = ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0")
 
 def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=None,
                    dh_last=None, *, want=GRAD_NAMES, out=None, workspace=None,
-                   n_spans: int = 0) -> dict:
+                   n_spans: int = 0, ckpt=None) -> dict:
     """Gradients of the selective scan (Euler); see include/mamba_scan.h.
 
     Returns a dict with the names of ``want`` (a subset of GRAD_NAMES; du and ddelta are
     always computed): du, ddelta, dz, dB, dC in the activations' dtype, dA, dD, dbias,
     dh0 in float32.  dz is None without a gate.  ``out`` may map names to preallocated
-    tensors.  n_spans: sequence split (0 = automatic; see mamba_scan_bwd_ex).
+    tensors.  n_spans: sequence split (0 = automatic; see mamba_scan_bwd_ex).  ckpt: the
+    checkpoints written by mamba_scan_fwd(..., ckpt=) on the same inputs
+    (mamba_scan_bwd_ckpt: no forward pass of its own).
     """
     torch = _torch()
     lib = load_library()
@@ -450,8 +498,10 @@ def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=No
         res[name] = t
         ptrs[name] = _ptr(t, name, shape, dt, dev)
     opts = ScanOpts(0, 0, int(n_spans), 0, 0, 0)
-    need = lib.mamba_scan_bwd_workspace_size_ex(batch, seqlen, d_inner, d_state,
-                                                ctypes.byref(opts))
+    p_ck = _ckpt_ptr(ckpt, batch, seqlen, d_inner, d_state, dev)
+    size_f = (lib.mamba_scan_bwd_ckpt_workspace_size if ckpt is not None
+              else lib.mamba_scan_bwd_workspace_size_ex)
+    need = size_f(batch, seqlen, d_inner, d_state, ctypes.byref(opts))
     if need == ctypes.c_size_t(-1).value:
         raise MambaError(4, "mamba_scan_bwd_workspace_size")
     ws = workspace
@@ -459,11 +509,19 @@ def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=No
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
     p_ws = ws.data_ptr() if ws is not None and need > 0 else None
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    st = lib.mamba_scan_bwd_ex(p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_dy,
-                               p_dhl, ptrs["du"], ptrs["ddelta"], ptrs["dA"], ptrs["dB"],
-                               ptrs["dC"], ptrs["dD"], ptrs["dz"], ptrs["dbias"], ptrs["dh0"],
-                               batch, seqlen, d_inner, d_state, code, p_ws, ws_bytes,
-                               ctypes.byref(opts), _stream(dev))
+    if ckpt is not None:
+        st = lib.mamba_scan_bwd_ckpt(p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_dy,
+                                     p_dhl, p_ck, ptrs["du"], ptrs["ddelta"], ptrs["dA"],
+                                     ptrs["dB"], ptrs["dC"], ptrs["dD"], ptrs["dz"],
+                                     ptrs["dbias"], ptrs["dh0"], batch, seqlen, d_inner,
+                                     d_state, code, p_ws, ws_bytes, ctypes.byref(opts),
+                                     _stream(dev))
+    else:
+        st = lib.mamba_scan_bwd_ex(p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_dy,
+                                   p_dhl, ptrs["du"], ptrs["ddelta"], ptrs["dA"], ptrs["dB"],
+                                   ptrs["dC"], ptrs["dD"], ptrs["dz"], ptrs["dbias"],
+                                   ptrs["dh0"], batch, seqlen, d_inner, d_state, code, p_ws,
+                                   ws_bytes, ctypes.byref(opts), _stream(dev))
     if st != 0:
         raise MambaError(st, "mamba_scan_bwd")
     return {k: v for k, v in res.items() if k in ("du", "ddelta") or k in want}

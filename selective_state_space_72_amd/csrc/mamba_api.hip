@@ -58,6 +58,18 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
 
 bool d_state_ok(int64_t n) { return n == 4 || n == 8 || n == 16 || n == 32 || n == 64; }
+bool bwd_d_state_ok(int64_t n) { return n == 4 || n == 8 || n == 16 || n == 32; }
+
+// Bytes of the backward-pass checkpoints: (batch * channel tiles) x ceil(L / 8) segments x
+// d_state x 64 lanes, fp32; -1 on overflow.
+int64_t ckpt_bytes(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state)
+{
+    int64_t t;
+    const int64_t units = batch * ((d_inner + 63) / 64), nseg = (seqlen + 7) / 8;
+    if (!mul_ok(units, nseg, &t) || !mul_ok(t, d_state * 64 * 4, &t))
+        return -1;
+    return t;
+}
 
 int cu_count()
 {
@@ -80,6 +92,7 @@ struct Plan {
     int64_t relay_len;    // steps per relay part (a multiple of chunk)
     bool zoh;             // zero-order-hold discretisation (scalar family only)
     bool trap, rot;       // exponential-trapezoidal input term, pair rotation (scalar family)
+    bool ckpt;            // backward-pass checkpoints written (scalar family, Euler)
 };
 
 // Launch plan.  Channel tiles of 64 lanes x `waves` waves are the unit of parallel work;
@@ -97,12 +110,15 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     p.zoh = disc == MAMBA_DISC_ZOH;
     p.trap = ext && ext->lambda;
     p.rot = ext && ext->theta;
+    p.ckpt = ext && ext->ckpt;
     if (p.trap && p.zoh)
         return MAMBA_ERR_UNSUPPORTED; // the trapezoid replaces the input term
+    if (p.ckpt && (p.zoh || p.trap || p.rot || !bwd_d_state_ok(d_state)))
+        return MAMBA_ERR_UNSUPPORTED; // the backward pass is built for Euler only
     Family autof = auto_family(batch, d_inner, d_state, cus);
     if (autof == Family::Scalar && !scalar_span_ok(seqlen, d_inner))
         autof = Family::Rows;
-    if (p.zoh || p.trap || p.rot) {
+    if (p.zoh || p.trap || p.rot || p.ckpt) {
         // these options are implemented in the scalar-B/C family only
         if (fam == MAMBA_KERNEL_ROWS || fam == MAMBA_KERNEL_BLOCK)
             return MAMBA_ERR_UNSUPPORTED;
@@ -112,7 +128,7 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
         // an explicit block shape: the scalar family if it has it, else the block family
         const int w = opts->waves ? opts->waves : scalar_default_waves(d_state);
         const int c = opts->chunk_len ? opts->chunk_len : scalar_default_chunk(d_state);
-        autof = scalar_variant_supported(d_state, w, c) || p.zoh || p.trap || p.rot
+        autof = scalar_variant_supported(d_state, w, c) || p.zoh || p.trap || p.rot || p.ckpt
                     ? Family::Scalar : Family::Block;
     }
     if (fam == MAMBA_KERNEL_ROWS || (fam == MAMBA_KERNEL_AUTO && autof == Family::Rows)) {
@@ -323,8 +339,10 @@ mamba_status_t bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t 
 // [dD, dbias partials] and, with spans, [staged B/C][forward span decay][forward span
 // local state][state entering each span][adjoint decay][adjoint local][adjoint entering
 // each span]; each region 256-byte aligned.  Offsets in bytes; off[11] is the total.
+// With checkpoints from the forward pass (ext_ck) the checkpoint region and the forward
+// span regions are empty.
 void bwd_layout(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                const BwdPlan &p, size_t off[12])
+                const BwdPlan &p, bool ext_ck, size_t off[12])
 {
     auto al = [](size_t n) { return (n + 255) / 256 * 256; };
     const size_t S = (size_t)p.seg_len;
@@ -343,6 +361,8 @@ void bwd_layout(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
         for (int i = 5; i < 11; ++i)
             sz[i] = al(sp * bdn * f);
     }
+    if (ext_ck)
+        sz[0] = sz[4] = sz[5] = sz[6] = sz[7] = 0;
     (void)S;
     off[0] = 0;
     for (int i = 0; i < 11; ++i)
@@ -426,6 +446,7 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     const void *u_prev = lam ? ext->u_prev : nullptr; // used by the trapezoid only
     const void *B_prev = lam ? ext->B_prev : nullptr;
     const void *theta = ext ? ext->theta : nullptr;
+    float *ckpt = ext ? ext->ckpt : nullptr;
     // ---- sizes and dtype ----
     if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0)
         return MAMBA_ERR_BAD_SHAPE;
@@ -454,7 +475,7 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     for (const void *p : elem_ptrs)
         if (p && !aligned(p, (size_t)es))
             return MAMBA_ERR_MISALIGNED;
-    const void *f32_ptrs[] = {A, D, delta_bias, h0, h_last};
+    const void *f32_ptrs[] = {A, D, delta_bias, h0, h_last, ckpt};
     for (const void *p : f32_ptrs)
         if (p && !aligned(p, 4))
             return MAMBA_ERR_MISALIGNED;
@@ -482,12 +503,17 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     const Range r_y = range_of(has_seq ? y : nullptr, bld * es);
     const Range r_hl = range_of(h_last, bdn * 4);
     const Range r_ws = range_of(need > 0 ? workspace : nullptr, (int64_t)need);
+    const int64_t ckb = ckpt ? ckpt_bytes(batch, seqlen, d_inner, d_state) : 0;
+    if (ckb < 0)
+        return MAMBA_ERR_BAD_SHAPE;
+    const Range r_ck = range_of(has_seq ? ckpt : nullptr, ckb);
     for (const Range &r : r_in) {
-        if (overlaps(r_y, r) || overlaps(r_hl, r) || overlaps(r_ws, r))
+        if (overlaps(r_y, r) || overlaps(r_hl, r) || overlaps(r_ws, r) || overlaps(r_ck, r))
             return MAMBA_ERR_ALIASING;
     }
     if (overlaps(r_y, r_h0) || overlaps(r_y, r_hl) || overlaps(r_y, r_ws) ||
-        overlaps(r_ws, r_h0) || overlaps(r_ws, r_hl))
+        overlaps(r_ws, r_h0) || overlaps(r_ws, r_hl) || overlaps(r_ck, r_y) ||
+        overlaps(r_ck, r_h0) || overlaps(r_ck, r_hl) || overlaps(r_ck, r_ws))
         return MAMBA_ERR_ALIASING;
     if (overlaps(r_hl, r_h0) && (const void *)h_last != (const void *)h0)
         return MAMBA_ERR_ALIASING;
@@ -528,6 +554,7 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     L.u_prev = u_prev;
     L.B_prev = B_prev;
     L.theta = theta;
+    L.ckpt = plan.ckpt ? ckpt : nullptr;
 
     auto full = [&](const ScanLaunch &x) {
         switch (plan.family) {
@@ -579,6 +606,7 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     ScanLaunch E = L;
     E.h_init = nullptr;
     E.h_init_span_stride = 0;
+    E.ckpt = nullptr; // span summaries hold local states: no checkpoints
     E.ws_decay = ws_decay;
     E.ws_hloc = ws_hloc;
     E.first_span = 0;
@@ -650,8 +678,9 @@ mamba_status_t mamba_state_update_ext(float *h, const void *u, const void *delta
     const void *theta = ext ? ext->theta : nullptr;
     if (discretization != MAMBA_DISC_EULER && discretization != MAMBA_DISC_ZOH)
         return MAMBA_ERR_UNSUPPORTED;
-    if ((lam && discretization == MAMBA_DISC_ZOH) || (theta && d_state % 2 != 0))
-        return MAMBA_ERR_UNSUPPORTED;
+    if ((lam && discretization == MAMBA_DISC_ZOH) || (theta && d_state % 2 != 0) ||
+        (ext && ext->ckpt))
+        return MAMBA_ERR_UNSUPPORTED; // (checkpoints belong to the scan)
     if (batch < 0 || d_inner < 0 || d_state <= 0)
         return MAMBA_ERR_BAD_SHAPE;
     if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
@@ -813,8 +842,8 @@ mamba_status_t mamba_conv1d_silu_update(void *state, const void *x, const float 
 }
 
 
-size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_inner,
-                                        int64_t d_state, const mamba_scan_opts_t *opts)
+static size_t bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                 int64_t d_state, const mamba_scan_opts_t *opts, bool ext_ck)
 {
     int64_t t;
     if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 ||
@@ -825,8 +854,28 @@ size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d
     if (bwd_plan(batch, seqlen, d_inner, d_state, opts, &plan) != MAMBA_OK)
         return (size_t)-1;
     size_t off[12];
-    bwd_layout(batch, seqlen, d_inner, d_state, plan, off);
+    bwd_layout(batch, seqlen, d_inner, d_state, plan, ext_ck, off);
     return off[11];
+}
+
+size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                        int64_t d_state, const mamba_scan_opts_t *opts)
+{
+    return bwd_workspace_size(batch, seqlen, d_inner, d_state, opts, false);
+}
+
+size_t mamba_scan_bwd_ckpt_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                          int64_t d_state, const mamba_scan_opts_t *opts)
+{
+    return bwd_workspace_size(batch, seqlen, d_inner, d_state, opts, true);
+}
+
+size_t mamba_scan_ckpt_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state)
+{
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || !bwd_d_state_ok(d_state))
+        return (size_t)-1;
+    const int64_t b = ckpt_bytes(batch, seqlen, d_inner, d_state);
+    return b < 0 ? (size_t)-1 : (size_t)b;
 }
 
 size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
@@ -849,15 +898,17 @@ mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const float *A, 
                              d_state, dtype, workspace, workspace_bytes, nullptr, stream);
 }
 
-mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *A,
-                                 const void *B, const void *C, const float *D, const void *z,
-                                 const float *delta_bias, const float *h0, const void *dy,
-                                 const float *dh_last, void *du, void *ddelta, float *dA,
-                                 void *dB, void *dC, float *dD, void *dz, float *d_delta_bias,
-                                 float *dh0, int64_t batch, int64_t seqlen, int64_t d_inner,
-                                 int64_t d_state, mamba_dtype_t dtype, void *workspace,
-                                 size_t workspace_bytes, const mamba_scan_opts_t *opts,
-                                 void *stream)
+// The backward pass; ckpt: checkpoints written by the forward pass, or NULL (then the
+// backward runs its own forward pass into the workspace).
+static mamba_status_t bwd_impl(const void *u, const void *delta, const float *A, const void *B,
+                               const void *C, const float *D, const void *z,
+                               const float *delta_bias, const float *h0, const void *dy,
+                               const float *dh_last, const float *ckpt, void *du, void *ddelta,
+                               float *dA, void *dB, void *dC, float *dD, void *dz,
+                               float *d_delta_bias, float *dh0, int64_t batch, int64_t seqlen,
+                               int64_t d_inner, int64_t d_state, mamba_dtype_t dtype,
+                               void *workspace, size_t workspace_bytes,
+                               const mamba_scan_opts_t *opts, void *stream)
 {
     // ---- sizes and dtype ----
     if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0)
@@ -883,6 +934,7 @@ mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *
 
     // ---- required pointers ----
     const bool has_seq = seqlen > 0;
+    const bool ext_ck = ckpt != nullptr;
     if (!A || (has_seq && (!u || !delta || !B || !C || !dy || !du || !ddelta)) ||
         (has_seq && z && !dz))
         return MAMBA_ERR_NULL_ARG;
@@ -894,14 +946,19 @@ mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *
     for (const void *p : elem_ptrs)
         if (p && !aligned(p, (size_t)es))
             return MAMBA_ERR_MISALIGNED;
-    const void *f32_ptrs[] = {A, D, delta_bias, h0, dh_last, dA, dD, d_delta_bias, dh0};
+    const void *f32_ptrs[] = {A, D, delta_bias, h0, dh_last, dA, dD, d_delta_bias, dh0, ckpt};
     for (const void *p : f32_ptrs)
         if (p && !aligned(p, 4))
             return MAMBA_ERR_MISALIGNED;
+    const int64_t ckb = ext_ck ? ckpt_bytes(batch, seqlen, d_inner, d_state) : 0;
+    if (ckb < 0)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (ext_ck && S != 8)
+        return MAMBA_ERR_UNSUPPORTED; // the forward stores the state every 8 steps
 
     // ---- workspace ----
     size_t off[12];
-    bwd_layout(batch, seqlen, d_inner, d_state, plan, off);
+    bwd_layout(batch, seqlen, d_inner, d_state, plan, ext_ck, off);
     const size_t need = off[11];
     if (need > 0 && (!workspace || workspace_bytes < need))
         return MAMBA_ERR_WORKSPACE;
@@ -914,7 +971,8 @@ mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *
                           range_of(B, bln * es),       range_of(C, bln * es),
                           range_of(A, dn * 4),         range_of(D, d_inner * 4),
                           range_of(delta_bias, d_inner * 4), range_of(h0, bdn * 4),
-                          range_of(dh_last, bdn * 4)};
+                          range_of(dh_last, bdn * 4),
+                          range_of(has_seq ? ckpt : nullptr, ckb)};
     const Range r_out[] = {range_of(has_seq ? du : nullptr, bld * es),
                            range_of(has_seq ? ddelta : nullptr, bld * es),
                            range_of(has_seq ? dz : nullptr, bld * es),
@@ -956,7 +1014,12 @@ mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *
     auto region = [&](int i) { return reinterpret_cast<float *>(ws + off[i]); };
 
     BwdLaunch P{};
-    if (plan.n_spans > 1) {
+    if (plan.n_spans > 1 && ext_ck) {
+        // the state entering each span is a checkpoint; only the adjoint carries are needed
+        P.mu_dec = region(8);
+        P.mu_loc = region(9);
+        P.mu_in = region(10);
+    } else if (plan.n_spans > 1) {
         // forward span summaries (the forward's span pass), then the state entering each span
         ScanLaunch E{};
         E.u = u;
@@ -1020,7 +1083,8 @@ mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *
     P.dD = dD;
     P.dbias = d_delta_bias;
     P.dh0 = dh0;
-    P.ckpt = region(0);
+    P.ckpt = ext_ck ? const_cast<float *>(ckpt) : region(0);
+    P.ck_ext = ext_ck;
     P.dbc_part = region(1);
     P.dA_part = region(2);
     P.dDb_part = region(3);
@@ -1030,6 +1094,39 @@ mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *
     P.d_state = d_state;
     P.dtype = dt;
     return hip_status(launch_scan_bwd(P, st));
+}
+
+mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *A,
+                                 const void *B, const void *C, const float *D, const void *z,
+                                 const float *delta_bias, const float *h0, const void *dy,
+                                 const float *dh_last, void *du, void *ddelta, float *dA,
+                                 void *dB, void *dC, float *dD, void *dz, float *d_delta_bias,
+                                 float *dh0, int64_t batch, int64_t seqlen, int64_t d_inner,
+                                 int64_t d_state, mamba_dtype_t dtype, void *workspace,
+                                 size_t workspace_bytes, const mamba_scan_opts_t *opts,
+                                 void *stream)
+{
+    return bwd_impl(u, delta, A, B, C, D, z, delta_bias, h0, dy, dh_last, nullptr, du, ddelta,
+                    dA, dB, dC, dD, dz, d_delta_bias, dh0, batch, seqlen, d_inner, d_state,
+                    dtype, workspace, workspace_bytes, opts, stream);
+}
+
+mamba_status_t mamba_scan_bwd_ckpt(const void *u, const void *delta, const float *A,
+                                   const void *B, const void *C, const float *D, const void *z,
+                                   const float *delta_bias, const float *h0, const void *dy,
+                                   const float *dh_last, const float *ckpt, void *du,
+                                   void *ddelta, float *dA, void *dB, void *dC, float *dD,
+                                   void *dz, float *d_delta_bias, float *dh0, int64_t batch,
+                                   int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                   mamba_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                   const mamba_scan_opts_t *opts, void *stream)
+{
+    if (!ckpt && seqlen > 0)
+        return MAMBA_ERR_NULL_ARG;
+    return bwd_impl(u, delta, A, B, C, D, z, delta_bias, h0, dy, dh_last,
+                    seqlen > 0 ? ckpt : nullptr, du, ddelta, dA, dB, dC, dD, dz, d_delta_bias,
+                    dh0, batch, seqlen, d_inner, d_state, dtype, workspace, workspace_bytes, opts,
+                    stream);
 }
 
 

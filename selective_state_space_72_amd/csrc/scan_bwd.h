@@ -13,6 +13,7 @@ struct BwdLaunch {
     void *du, *ddelta, *dz, *dB, *dC; // activation dtype
     float *dA, *dD, *dbias, *dh0;
     float *ckpt;        // [block][segment][n][lane]
+    bool ck_ext;        // ckpt written by the forward pass: no forward pass here
     float *dbc_part;    // [block][t][2N]
     float *dA_part;     // [span][b][d][n]
     float *dDb_part;    // [span][b][d][2]

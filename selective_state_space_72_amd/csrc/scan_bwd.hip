@@ -106,8 +106,10 @@ __device__ __forceinline__ T zero_val()
 
 // AB: keep the segment's decay factors in registers (else recompute them in the adjoint
 // sweep, one more exp per element, to save S * NQ registers).  WPE: waves per SIMD the
-// register allocation targets.
-template <typename T, int N, int NW, int S, bool AB, int WPE, bool GATED>
+// register allocation targets.  CKE: the checkpoints hold every segment's entering state
+// already (written by the forward scan): no forward pass here, and a later span's entering
+// state is its first checkpoint.
+template <typename T, int N, int NW, int S, bool AB, int WPE, bool GATED, bool CKE = false>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 scan_bwd_kernel(BwdArgs p)
 {
@@ -158,6 +160,8 @@ scan_bwd_kernel(BwdArgs p)
         an[q] = av;
         if (span == 0)
             h[q] = p.h0 ? p.h0[col_c + q] : 0.0f;
+        else if constexpr (CKE) // unused: the span's first segment reads its checkpoint
+            h[q] = 0.0f;
         else
             h[q] = p.h_in[span_col + col_c + q];
         hstart[q] = h[q];
@@ -188,7 +192,7 @@ scan_bwd_kernel(BwdArgs p)
     };
 
     // ---- 1. forward pass: checkpoints at the start of segments seg_lo+1 .. seg_hi-1 ----
-    {
+    if constexpr (!CKE) {
         // (Delta, Delta*u) and B of two chunks, alternating; aliases s_p
         float2 *s_f = reinterpret_cast<float2 *>(&s_p[0][0][0][0]);   // [2][kTCF][64]
         float *s_fb = reinterpret_cast<float *>(&s_p[2][0][0][0]);    // [2][NW][kTCF * NQ]
@@ -273,7 +277,8 @@ scan_bwd_kernel(BwdArgs p)
         bcv = bc_fetch(t0);
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
-            hnext[q] = seg == seg_lo ? hstart[q] : ck[((int64_t)seg * N + n0 + q) * 64 + lane];
+            hnext[q] = (CKE ? seg == 0 : seg == seg_lo)
+                           ? hstart[q] : ck[((int64_t)seg * N + n0 + q) * 64 + lane];
     };
     if (seg_hi > seg_lo)
         rfetch(seg_hi - 1);
@@ -784,12 +789,20 @@ hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
     a.n_spans = (int32_t)q.n_spans;
     a.span_len = (int32_t)(q.n_spans > 1 ? q.span_len : (q.L + S - 1) / S * S);
     const dim3 grid((uint32_t)(units * q.n_spans));
-    if (gated)
+    if (q.ck_ext) {
+        if (gated)
+            hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, true, true>), grid,
+                               dim3(64 * NW), 0, stream, a);
+        else
+            hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, false, true>), grid,
+                               dim3(64 * NW), 0, stream, a);
+    } else if (gated) {
         hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, true>), grid, dim3(64 * NW), 0,
                            stream, a);
-    else
+    } else {
         hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, false>), grid, dim3(64 * NW), 0,
                            stream, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const int64_t nbc = q.batch * q.L * 2 * N;

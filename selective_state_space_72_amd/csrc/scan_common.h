@@ -43,6 +43,10 @@ struct ScanLaunch {
     // theta (B,L,N/2) staged next to B and C.
     bool trap, rot;
     const void *lam, *u_prev, *B_prev, *theta;
+    // Checkpoints for the backward pass (scalar family, Euler, full-output pass; NULL = off):
+    // the state entering every 8-step segment s >= 1, at ckpt[((unit * n_seg + s) * N + n)
+    // * 64 + lane], unit = channel tile * batch + b, n_seg = ceil(L / 8).
+    float *ckpt;
 };
 
 // Relay arguments as the scan kernel receives them.

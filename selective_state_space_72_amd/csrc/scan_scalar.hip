@@ -115,13 +115,17 @@ __device__ __forceinline__ void relay_wait(uint32_t *flag)
 
 // Inputs of the Mamba-3 options: trapezoid mixing coefficients lam (as u), the input
 // before t = 0 (u_prev (B,D), B_prev (B,N); NULL = 0) and B itself for the look-back at
-// a span's or relay part's first step.
+// a span's or relay part's first step.  Also the checkpoint output of the CK variants.
 struct Mamba3Args {
     const void *lam, *u_prev, *B_prev, *Bm;
+    float *ck;       // checkpoints for the backward pass (CK variants)
+    int32_t ck_nseg; // 8-step segments of the whole sequence
 };
 
-// DISC: 0 Euler, 1 zero-order hold, 2 exponential-trapezoidal; ROT: rotation of state pairs.
-template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED, int DISC, bool ROT>
+// DISC: 0 Euler, 1 zero-order hold, 2 exponential-trapezoidal; ROT: rotation of state pairs;
+// CK: also store the state entering every 8-step segment (the backward pass's checkpoints).
+template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED, int DISC, bool ROT,
+          bool CK = false>
 __global__ void __launch_bounds__(64 * NW)
 scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                    const T *__restrict__ z, const float *__restrict__ bcp,
@@ -408,6 +412,20 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                 s_yp[FULL ? pp : 0][tl][g][lane] = yp;
             else
                 sum_dt += dw[tl].x;
+            if constexpr (CK) {
+                // the state after absolute step tn - 1 enters segment tn / 8 (every lane,
+                // tail lanes included: they hold a valid channel's finite state).  Spans and
+                // relay parts start at multiples of the chunk, so with chunks of a multiple
+                // of 8 steps the boundaries are known steps of the chunk.
+                const int64_t tn = t_begin + t0 + tl + 1;
+                if ((TC % 8 == 0 ? (tl & 7) == 7 : (tn & 7) == 0) && tn < L) {
+                    float *ckp = m3.ck + ((((int64_t)tile * batch + b) * m3.ck_nseg + (tn >> 3)) * N +
+                                          n0) * 64 + lane;
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q)
+                        ckp[q * 64] = h[q];
+                }
+            }
         };
         if (nt == TC) {
 #pragma unroll
@@ -506,7 +524,8 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     X(16, 8, 8, 2)               \
     X(32, 8, 4, 2)
 
-template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED, int DISC, bool ROT>
+template <typename T, int N, int NW, int TC, int PD, bool FULL, bool GATED, int DISC, bool ROT,
+          bool CK = false>
 hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
 {
     const int32_t tiles = (int32_t)((p.d_inner + 63) / 64);
@@ -524,8 +543,8 @@ hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
     }
     if (blocks <= 0)
         return hipSuccess;
-    Mamba3Args m3{p.lam, p.u_prev, p.B_prev, p.B};
-    hipLaunchKernelGGL((scan_scalar_kernel<T, N, NW, TC, PD, FULL, GATED, DISC, ROT>),
+    Mamba3Args m3{p.lam, p.u_prev, p.B_prev, p.B, p.ckpt, (int32_t)((p.L + 7) / 8)};
+    hipLaunchKernelGGL((scan_scalar_kernel<T, N, NW, TC, PD, FULL, GATED, DISC, ROT, CK>),
                        dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, (const T *)p.u,
                        (const T *)p.delta, (const T *)p.z, p.bc_staged, p.A, p.D, p.bias,
                        p.h_init, p.h_init_span_stride, (T *)p.y, p.h_last, p.ws_decay,
@@ -564,6 +583,14 @@ template <typename T, int N, int NW, int TC, int PD, bool FULL, int DISC>
 hipError_t launch_scalar_disc(const ScanLaunch &p, hipStream_t stream)
 {
     const bool g = FULL && p.z != nullptr;
+    if (p.ckpt) {
+        // checkpoints: Euler without rotation, written by the full-output pass
+        if constexpr (FULL && DISC == 0)
+            return g ? launch_scalar_variant<T, N, NW, TC, PD, FULL, true, 0, false, true>(p, stream)
+                     : launch_scalar_variant<T, N, NW, TC, PD, FULL, false, 0, false, true>(p, stream);
+        else
+            return hipErrorInvalidValue;
+    }
     if (p.rot) {
         if constexpr (FULL && (N / NW) % 2 == 0)
             return g ? launch_scalar_variant<T, N, NW, TC, PD, FULL, true, DISC, true>(p, stream)

@@ -433,3 +433,74 @@ def test_ssd_validation(lib):
     assert ssd(lib, h0=BASE + 900 * MB, hl=BASE + 900 * MB) == ALIAS
     assert ssd(lib, batch=0) == OK and ssd(lib, H=0) == OK
     assert ssd(lib, L=0) == OK                              # no state asked for: nothing to do
+
+
+# ---- checkpoints written by the forward pass for the backward pass ----------------
+
+def test_ckpt_size(lib):
+    assert lib.mamba_scan_ckpt_size(8, 4096, 5120, 16) == 8 * 80 * 512 * 16 * 64 * 4
+    assert lib.mamba_scan_ckpt_size(2, 65, 100, 8) == 2 * 2 * 9 * 8 * 64 * 4   # ragged
+    assert lib.mamba_scan_ckpt_size(2, 0, 100, 8) == 0
+    bad = ctypes.c_size_t(-1).value
+    for n in (64, 12, 0):
+        assert lib.mamba_scan_ckpt_size(2, 64, 64, n) == bad       # no backward pass there
+    assert lib.mamba_scan_ckpt_size(-1, 64, 64, 16) == bad
+    # the backward's workspace without its own checkpoints (and forward span summaries)
+    o = ms.ScanOpts()
+    full = lib.mamba_scan_bwd_workspace_size_ex(8, 4096, 5120, 16, ctypes.byref(o))
+    lean = lib.mamba_scan_bwd_ckpt_workspace_size(8, 4096, 5120, 16, ctypes.byref(o))
+    assert full - lean == lib.mamba_scan_ckpt_size(8, 4096, 5120, 16)
+    long_full = lib.mamba_scan_bwd_workspace_size_ex(1, 131072, 2048, 16, ctypes.byref(o))
+    long_lean = lib.mamba_scan_bwd_ckpt_workspace_size(1, 131072, 2048, 16, ctypes.byref(o))
+    assert long_full - long_lean > lib.mamba_scan_ckpt_size(1, 131072, 2048, 16)
+
+
+def fwd_ck(lib, *, ckpt=BASE + 2048 * MB, opts=None, lam=None, N=16, u=BASE,
+           y=BASE + 256 * MB, batch=2, L=64, Dn=128, dtype=BF16, ws=BASE + 1024 * MB):
+    ext = ms.ScanExt(lam, None, None, None, ckpt)
+    o = ctypes.byref(opts) if opts is not None else None
+    need = lib.mamba_scan_fwd_workspace_size_ext(batch, L, Dn, N, ctypes.byref(ext), o)
+    need = 0 if need == ctypes.c_size_t(-1).value else need
+    return lib.mamba_scan_fwd_ext(u, BASE + 64 * MB, BASE + 128 * MB, BASE + 132 * MB,
+                                  BASE + 136 * MB, None, None, None, None, y, None, batch, L,
+                                  Dn, N, dtype, ws, need, o, ctypes.byref(ext), None)
+
+
+def test_fwd_ckpt_validation(lib):
+    # Euler only, the scalar family, d_state 4..32 (every call fails before a launch)
+    assert fwd_ck(lib, opts=ms.ScanOpts(0, 0, 0, 0, 0, 1)) == UNSUP          # zero-order hold
+    assert fwd_ck(lib, opts=ms.ScanOpts(0, 0, 0, 2, 0, 0)) == UNSUP          # rows family
+    assert fwd_ck(lib, opts=ms.ScanOpts(0, 0, 0, 1, 0, 0)) == UNSUP          # block family
+    assert fwd_ck(lib, lam=BASE + 300 * MB) == UNSUP                          # trapezoid
+    assert fwd_ck(lib, N=64) == UNSUP
+    assert fwd_ck(lib, ckpt=BASE + 2048 * MB + 2) == ALIGN
+    assert fwd_ck(lib, ckpt=BASE + 4096) == ALIAS                            # over u
+    assert fwd_ck(lib, ckpt=BASE + 256 * MB - 4096) == ALIAS                 # over y
+    assert fwd_ck(lib, ckpt=BASE + 1024 * MB + 64) == ALIAS                  # over the workspace
+    # the decode step takes the same struct but has no checkpoints
+    ext = ms.ScanExt(None, None, None, None, BASE + 2048 * MB)
+    assert lib.mamba_state_update_ext(BASE, BASE + 100 * MB, BASE + 110 * MB, BASE + 120 * MB,
+                                      BASE + 130 * MB, BASE + 131 * MB, None, None, None,
+                                      BASE + 140 * MB, 4, 256, 16, BF16, 0,
+                                      ctypes.byref(ext), None) == UNSUP
+
+
+def bwd_ck(lib, *, ckpt=BASE + 2048 * MB, du=BASE + 256 * MB, ws=BASE + 1024 * MB,
+           ws_bytes=None, batch=2, L=64, Dn=128, N=16):
+    o = ms.ScanOpts()
+    if ws_bytes is None:
+        ws_bytes = lib.mamba_scan_bwd_ckpt_workspace_size(batch, L, Dn, N, ctypes.byref(o))
+    return lib.mamba_scan_bwd_ckpt(BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 132 * MB,
+                                   BASE + 136 * MB, None, None, None, None, BASE + 160 * MB,
+                                   None, ckpt, du, BASE + 320 * MB, None, None, None, None,
+                                   None, None, None, batch, L, Dn, N, BF16, ws, ws_bytes,
+                                   ctypes.byref(o), None)
+
+
+def test_bwd_ckpt_validation(lib):
+    assert bwd_ck(lib, ckpt=None) == NULL
+    assert bwd_ck(lib, ckpt=BASE + 2048 * MB + 1) == ALIGN
+    assert bwd_ck(lib, du=BASE + 2048 * MB + 4096) == ALIAS                  # du over ckpt
+    assert bwd_ck(lib, ckpt=BASE + 1024 * MB) == ALIAS                       # ckpt over ws
+    assert bwd_ck(lib, ws_bytes=16) == WS
+    assert bwd_ck(lib, N=64) == UNSUP
