@@ -183,17 +183,16 @@ scan_bwd_kernel(BwdArgs p)
     // (steps past its end and lanes past the values are never used; the tail lanes' dy is
     // masked where it is used): a load inside a branch makes the compiler wait for every
     // outstanding memory operation where the branch joins (measured 4 % / 8 % faster for
-    // the backward without / with stored checkpoints at the large prefill).
+    // the backward without / with stored checkpoints at the large prefill).  They return
+    // the raw element, widened where it is stored to LDS: widening at the load made the
+    // compiler wait for it, and for every load issued before it, right after the issue
+    // (9 % / 5 % faster).
     const int r_step = lane / BCW, r_i = lane % BCW;
     const T *r_src = (const T *)(r_i < NQ ? p.B : p.C) + (int64_t)b * L * N + n0 + r_i % NQ;
-    auto bc_fetch = [&](int64_t t0) -> float {
-        return load_val(r_src, min(t0 + r_step, L - 1) * N);
-    };
+    auto bc_fetch = [&](int64_t t0) -> T { return r_src[min(t0 + r_step, L - 1) * N]; };
     const int f_step = lane / NQ, f_q = lane % NQ;
     const T *f_src = (const T *)p.B + (int64_t)b * L * N + n0 + f_q;
-    auto b_fetch = [&](int64_t t0) -> float {
-        return load_val(f_src, min(t0 + f_step, L - 1) * N);
-    };
+    auto b_fetch = [&](int64_t t0) -> T { return f_src[min(t0 + f_step, L - 1) * N]; };
 
     // ---- 1. forward pass: checkpoints at the start of segments seg_lo+1 .. seg_hi-1 ----
     if constexpr (!CKE) {
@@ -202,7 +201,7 @@ scan_bwd_kernel(BwdArgs p)
         float *s_fb = reinterpret_cast<float *>(&s_p[2][0][0][0]);    // [2][NW][kTCF * NQ]
         const int64_t LF = (int64_t)(seg_hi - 1) * S;                   // whole segments only
         T fu[KF], fd[KF];
-        float fb = 0.0f;
+        T fb = 0;
         auto ffetch = [&](int64_t t0) {
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
@@ -223,7 +222,7 @@ scan_bwd_kernel(BwdArgs p)
                 s_f[(par * kTCF + tl) * 64 + lane] = make_float2(dl, dl * widen(fu[k]));
             }
             if (lane < kTCF * NQ)
-                s_fb[(par * NW + g) * (kTCF * NQ) + lane] = fb;
+                s_fb[(par * NW + g) * (kTCF * NQ) + lane] = widen(fb);
             if (t0 + kTCF < LF)
                 ffetch(t0 + kTCF);
             __syncthreads();
@@ -262,7 +261,8 @@ scan_bwd_kernel(BwdArgs p)
 
     // inputs of the next segment to process, loaded one segment ahead
     T ru[KP], rd[KP], rz[KP], rg[KP];
-    float bcv = 0.0f, hnext[NQ];
+    T bcv = 0;
+    float hnext[NQ];
     auto rfetch = [&](int seg) {
         const int64_t t0 = (int64_t)seg * S;
 #pragma unroll
@@ -315,7 +315,7 @@ scan_bwd_kernel(BwdArgs p)
             s_in[tl][lane] = make_float4(dl, dl * uu, ds, 0.0f);
         }
         if (lane < S * BCW)
-            s_bc[g][lane] = bcv;
+            s_bc[g][lane] = widen(bcv);
         float hin[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
