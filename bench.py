@@ -449,6 +449,10 @@ def ssd_workload(dev, flush, steps):
                                sc["d_state"], sc["dtype"], sc["gate"], sc["h0"], sc["seed"])
     sa = [to_dev(v, dev) for v in (si.x, si.dt, si.A, si.B, si.C)]
     kw = dict(D=to_dev(si.D, dev), z=to_dev(si.z, dev), dt_bias=to_dev(si.dt_bias, dev))
+    need = ms.mamba_ssd_workspace_size(sc["batch"], sc["seqlen"], sc["n_heads"],
+                                       sc["head_dim"], sc["d_state"], sc["dtype"])
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    kw["workspace"] = ws
     y, h = ms.mamba_ssd_fwd(*sa, **kw, return_last_state=True)
 
     def sstep():
@@ -467,7 +471,8 @@ def ssd_workload(dev, flush, steps):
             "ms": round(ms_used, 4), "ms_back_to_back": round(loop_ms, 4),
             "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "TFLOP_s": round(tf, 1), "mfma_bf16_frac": round(tf / 2500.0, 4),
-            "bytes_per_step": nbytes, "flop_per_step": flop}
+            "bytes_per_step": nbytes, "flop_per_step": flop,
+            "relayed_units": need // (sc["head_dim"] * sc["d_state"] * 4)}
 
 
 def copy_calibration(dev):

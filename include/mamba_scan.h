@@ -484,9 +484,10 @@ MAMBA_API mamba_status_t mamba_state_update_ext(float *h, const void *u, const v
  * accumulation; the operands computed in fp32 (the chunk's decay-weighted C.B^T, the
  * decay-weighted x and the state read by C h) enter as a bf16 pair hi + lo, about 16
  * significant bits; the carried state is fp32.  fp32 inputs use fp32 products.
- * No workspace.  x, z, B and C must be 16-byte aligned (they are read as 16-byte vectors;
- * MAMBA_ERR_MISALIGNED otherwise).  y and h_last must not overlap any input or each other
- * (h_last may not be h0).  Other conventions as for every entry point. */
+ * mamba_ssd_fwd needs no workspace; mamba_ssd_fwd_ex may (below).  x, z, B and C must be
+ * 16-byte aligned (they are read as 16-byte vectors; MAMBA_ERR_MISALIGNED otherwise).  y and
+ * h_last must not overlap any input or each other (h_last may not be h0).  Other
+ * conventions as for every entry point. */
 MAMBA_API int32_t mamba_ssd_supported(int64_t head_dim, int64_t d_state);
 
 MAMBA_API mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A,
@@ -495,6 +496,39 @@ MAMBA_API mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const floa
                                        void *y, float *h_last, int64_t batch, int64_t seqlen,
                                        int64_t n_heads, int64_t head_dim, int64_t d_state,
                                        mamba_dtype_t dtype, void *stream);
+
+/*
+ * mamba_ssd_fwd with load balancing across the device (same results, bitwise).
+ * The (batch row, head) units run one block each, a fixed number at a time (blocks per
+ * compute unit x compute units, the "slots").  When the units overflow the slots by a
+ * partial round, the units of that round would run on a mostly idle device; with the
+ * relay they run in two parts each instead -- the first half of the sequence (whole
+ * 64-step chunks) in the first round, the second half, continuing from the first's final
+ * state, in the slots the last full round frees -- the balance the scan's relay gives
+ * (mamba_scan_opts_t.relay).
+ *   relay: 0 automatic (relay when units exceed the slots, the overflow is at most half
+ *          of them and the sequence has at least 8 chunks); 1 off; 2 force two parts
+ *          (sequences of at least 2 chunks) on the overflow units, or on every unit when
+ *          they fit the slots (testing).  Other values: MAMBA_ERR_UNSUPPORTED.
+ * Workspace (caller-owned device memory, 4-byte aligned, not overlapping any argument):
+ * one flag and one head_dim x d_state fp32 state per relayed unit, size from
+ * mamba_ssd_workspace_size for the same arguments on the same device (0: none needed, NULL
+ * allowed; (size_t)-1 for arguments mamba_ssd_fwd_ex would reject); MAMBA_ERR_WORKSPACE
+ * when missing or too small.  Its contents on entry do not matter and are overwritten.
+ * Concurrent calls must not share a workspace.
+ */
+MAMBA_API size_t mamba_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
+                                          int64_t head_dim, int64_t d_state,
+                                          mamba_dtype_t dtype, int32_t relay);
+
+MAMBA_API mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const float *A,
+                                          const void *B, const void *C, const float *D,
+                                          const void *z, const float *dt_bias, const float *h0,
+                                          void *y, float *h_last, int64_t batch,
+                                          int64_t seqlen, int64_t n_heads, int64_t head_dim,
+                                          int64_t d_state, mamba_dtype_t dtype,
+                                          void *workspace, size_t workspace_bytes,
+                                          int32_t relay, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 MAMBA_API const char *mamba_status_string(mamba_status_t status);

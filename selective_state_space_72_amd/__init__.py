@@ -39,7 +39,7 @@ EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_conv1d_silu_update", "mamba_scan_bwd_workspace_size", "mamba_scan_bwd",
            "mamba_scan_bwd_workspace_size_ex", "mamba_scan_bwd_ex",
            "mamba_scan_fwd_workspace_size_ext", "mamba_scan_fwd_ext", "mamba_state_update_ext",
-           "mamba_ssd_supported", "mamba_ssd_fwd",
+           "mamba_ssd_supported", "mamba_ssd_fwd", "mamba_ssd_workspace_size", "mamba_ssd_fwd_ex",
            "mamba_scan_ckpt_size", "mamba_scan_bwd_ckpt_workspace_size", "mamba_scan_bwd_ckpt",
            "mamba_status_string")
 
@@ -136,6 +136,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mamba_ssd_supported.argtypes = [_i64, _i64]
     lib.mamba_ssd_fwd.restype = ctypes.c_int
     lib.mamba_ssd_fwd.argtypes = [_vp] * 11 + [_i64] * 5 + [ctypes.c_int, _vp]
+    lib.mamba_ssd_workspace_size.restype = ctypes.c_size_t
+    lib.mamba_ssd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int, ctypes.c_int32]
+    lib.mamba_ssd_fwd_ex.restype = ctypes.c_int
+    lib.mamba_ssd_fwd_ex.argtypes = ([_vp] * 11 + [_i64] * 5 + [ctypes.c_int, _vp,
+                                     ctypes.c_size_t, ctypes.c_int32, _vp])
     lib.mamba_scan_ckpt_size.restype = ctypes.c_size_t
     lib.mamba_scan_ckpt_size.argtypes = [_i64] * 4
     lib.mamba_scan_bwd_ckpt_workspace_size.restype = ctypes.c_size_t
@@ -172,6 +177,22 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.float32:
         return MAMBA_DTYPE_F32
     raise TypeError(f"activations must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dtype_code_of(dtype) -> int:
+    """Code of an activation dtype given as a torch dtype or a name ("bf16", "f32")."""
+    if isinstance(dtype, str):
+        codes = {"bf16": MAMBA_DTYPE_BF16, "bfloat16": MAMBA_DTYPE_BF16,
+                 "f32": MAMBA_DTYPE_F32, "fp32": MAMBA_DTYPE_F32, "float32": MAMBA_DTYPE_F32}
+        if dtype not in codes:
+            raise TypeError(f"unknown activation dtype {dtype!r}")
+        return codes[dtype]
+    torch = _torch()
+    if dtype == torch.bfloat16:
+        return MAMBA_DTYPE_BF16
+    if dtype == torch.float32:
+        return MAMBA_DTYPE_F32
+    raise TypeError(f"activations must be bfloat16 or float32, got {dtype}")
 
 
 def _ptr(t, name, shape=None, dtype=None, device=None) -> Optional[int]:
@@ -527,12 +548,28 @@ def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=No
     return {k: v for k, v in res.items() if k in ("du", "ddelta") or k in want}
 
 
+_SSD_RELAY = {"auto": 0, "off": 1, "force": 2}
+
+
+def mamba_ssd_workspace_size(batch: int, seqlen: int, n_heads: int, head_dim: int,
+                             d_state: int, dtype, relay: str = "auto") -> int:
+    """Workspace bytes of mamba_ssd_fwd_ex on the current device (0: none needed)."""
+    lib = load_library()
+    n = lib.mamba_ssd_workspace_size(batch, seqlen, n_heads, head_dim, d_state,
+                                     _dtype_code_of(dtype), _SSD_RELAY[relay])
+    if n == ctypes.c_size_t(-1).value:
+        raise MambaError(4, "mamba_ssd_workspace_size")
+    return n
+
+
 def mamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None,
                   return_last_state: bool = False, *, out=None, h_last_out=None,
-                  head_dim: int = 64) -> Tuple:
+                  head_dim: int = 64, relay: str = "auto", workspace=None) -> Tuple:
     """Mamba-2 SSD scan (see include/mamba_scan.h): x (batch, seqlen, n_heads * head_dim),
     dt (batch, seqlen, n_heads), A/D/dt_bias (n_heads,) fp32, B/C (batch, seqlen, d_state),
-    h0 (batch, n_heads * head_dim, d_state) fp32.  Returns (y, h_last)."""
+    h0 (batch, n_heads * head_dim, d_state) fp32.  Returns (y, h_last).  relay: "auto"
+    (load balancing when the device needs it), "off" (mamba_ssd_fwd itself) or "force";
+    the workspace it needs is allocated unless given."""
     torch = _torch()
     lib = load_library()
     if x.dim() != 3 or dt.dim() != 3:
@@ -561,8 +598,26 @@ def mamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None,
     if h_last is None and return_last_state:
         h_last = torch.empty((batch, d_inner, d_state), dtype=f32, device=dev)
     p_hl = _ptr(h_last, "h_last_out", (batch, d_inner, d_state), f32, dev)
-    st = lib.mamba_ssd_fwd(p_x, p_dt, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_y, p_hl, batch,
-                           seqlen, n_heads, head_dim, d_state, code, _stream(dev))
+    if relay not in _SSD_RELAY:
+        raise ValueError(f"relay must be one of {sorted(_SSD_RELAY)}")
+    if relay == "off" and workspace is None:
+        st = lib.mamba_ssd_fwd(p_x, p_dt, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_y, p_hl,
+                               batch, seqlen, n_heads, head_dim, d_state, code, _stream(dev))
+        if st != 0:
+            raise MambaError(st, "mamba_ssd_fwd")
+        return y, h_last
+    need = lib.mamba_ssd_workspace_size(batch, seqlen, n_heads, head_dim, d_state, code,
+                                        _SSD_RELAY[relay])
+    if need == ctypes.c_size_t(-1).value:
+        need = 0  # the call itself reports what is wrong
+    ws = workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    p_ws = ws.data_ptr() if ws is not None and ws.numel() > 0 else None
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = lib.mamba_ssd_fwd_ex(p_x, p_dt, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_y, p_hl,
+                              batch, seqlen, n_heads, head_dim, d_state, code, p_ws, ws_bytes,
+                              _SSD_RELAY[relay], _stream(dev))
     if st != 0:
-        raise MambaError(st, "mamba_ssd_fwd")
+        raise MambaError(st, "mamba_ssd_fwd_ex")
     return y, h_last

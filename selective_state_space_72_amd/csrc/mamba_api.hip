@@ -1135,11 +1135,14 @@ int32_t mamba_ssd_supported(int64_t head_dim, int64_t d_state)
     return ssd_supported(head_dim, d_state) ? 1 : 0;
 }
 
-mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A, const void *B,
-                             const void *C, const float *D, const void *z,
-                             const float *dt_bias, const float *h0, void *y, float *h_last,
-                             int64_t batch, int64_t seqlen, int64_t n_heads, int64_t head_dim,
-                             int64_t d_state, mamba_dtype_t dtype, void *stream)
+// SSD relay plan (mamba_ssd_fwd_ex): the units of a partial last round run in two parts,
+// the second from step `mid` (whole chunks before it).
+struct SsdRelay {
+    int64_t units = 0, mid = 0;
+};
+
+static mamba_status_t ssd_check_shape(int64_t batch, int64_t seqlen, int64_t n_heads,
+                                      int64_t head_dim, int64_t d_state, mamba_dtype_t dtype)
 {
     if (batch < 0 || seqlen < 0 || n_heads < 0 || head_dim <= 0 || d_state <= 0)
         return MAMBA_ERR_BAD_SHAPE;
@@ -1157,8 +1160,84 @@ mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A, cons
         return MAMBA_ERR_BAD_SHAPE;
     if (dn * es * 64 > INT32_MAX) // a chunk of 64 rows is addressed with 32-bit offsets
         return MAMBA_ERR_UNSUPPORTED;
+    return MAMBA_OK;
+}
+
+// (shapes already checked)
+static mamba_status_t ssd_relay_plan(int64_t batch, int64_t seqlen, int64_t n_heads,
+                                     int64_t d_state, mamba_dtype_t dtype, int32_t relay,
+                                     SsdRelay *r)
+{
+    *r = SsdRelay{};
+    if (relay < 0 || relay > 2)
+        return MAMBA_ERR_UNSUPPORTED;
+    const int64_t units = batch * n_heads;
+    const int64_t chunks = (seqlen + 63) / 64;
+    if (relay == 1 || units <= 0 || chunks < 2)
+        return MAMBA_OK;
+    const int64_t slots =
+        ssd_block_slots(d_state, dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32);
+    int64_t rem = slots > 0 ? units % slots : 0;
+    if (relay == 2) {
+        if (rem == 0)
+            rem = units;
+    } else if (!(slots > 0 && units > slots && rem > 0 && 2 * rem <= slots && chunks >= 8)) {
+        return MAMBA_OK;
+    }
+    if (rem > INT32_MAX - units) // the grid holds units + rem blocks
+        return MAMBA_OK;
+    r->units = rem;
+    r->mid = (chunks + 1) / 2 * 64;
+    return MAMBA_OK;
+}
+
+// Workspace: [one flag per relayed unit, 256-byte aligned][head_dim x d_state fp32 each]
+static size_t ssd_sync_bytes(const SsdRelay &r)
+{
+    return r.units > 0 ? ((size_t)r.units * sizeof(uint32_t) + 255) / 256 * 256 : 0;
+}
+
+static size_t ssd_workspace_bytes(const SsdRelay &r, int64_t head_dim, int64_t d_state)
+{
+    if (r.units <= 0)
+        return 0;
+    return ssd_sync_bytes(r) + (size_t)r.units * (size_t)head_dim * (size_t)d_state * sizeof(float);
+}
+
+size_t mamba_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
+                                int64_t head_dim, int64_t d_state, mamba_dtype_t dtype,
+                                int32_t relay)
+{
+    SsdRelay r;
+    if (ssd_check_shape(batch, seqlen, n_heads, head_dim, d_state, dtype) != MAMBA_OK ||
+        ssd_relay_plan(batch, seqlen, n_heads, d_state, dtype, relay, &r) != MAMBA_OK)
+        return (size_t)-1;
+    return ssd_workspace_bytes(r, head_dim, d_state);
+}
+
+mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const float *A, const void *B,
+                                const void *C, const float *D, const void *z,
+                                const float *dt_bias, const float *h0, void *y, float *h_last,
+                                int64_t batch, int64_t seqlen, int64_t n_heads,
+                                int64_t head_dim, int64_t d_state, mamba_dtype_t dtype,
+                                void *workspace, size_t workspace_bytes, int32_t relay,
+                                void *stream)
+{
+    const mamba_status_t shape_st =
+        ssd_check_shape(batch, seqlen, n_heads, head_dim, d_state, dtype);
+    if (shape_st != MAMBA_OK)
+        return shape_st;
+    SsdRelay plan;
+    const mamba_status_t plan_st =
+        ssd_relay_plan(batch, seqlen, n_heads, d_state, dtype, relay, &plan);
+    if (plan_st != MAMBA_OK)
+        return plan_st;
     if (batch == 0 || n_heads == 0)
         return MAMBA_OK;
+    const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
+    const int64_t dn = n_heads * head_dim;
+    const int64_t bld = batch * seqlen * dn, blh = batch * seqlen * n_heads;
+    const int64_t bln = batch * seqlen * d_state, bdn = batch * dn * d_state;
     const bool has_seq = seqlen > 0;
     if (!A || (has_seq && (!x || !dt || !B || !C || !y)))
         return MAMBA_ERR_NULL_ARG;
@@ -1174,6 +1253,11 @@ mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A, cons
     for (const void *p : f32_ptrs)
         if (p && !aligned(p, 4))
             return MAMBA_ERR_MISALIGNED;
+    const size_t need = ssd_workspace_bytes(plan, head_dim, d_state);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return MAMBA_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 4))
+        return MAMBA_ERR_MISALIGNED;
     const Range r_in[] = {range_of(x, bld * es),         range_of(dt, blh * es),
                           range_of(B, bln * es),         range_of(C, bln * es),
                           range_of(z, bld * es),         range_of(A, n_heads * 4),
@@ -1181,11 +1265,14 @@ mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A, cons
     const Range r_h0 = range_of(h0, bdn * 4);
     const Range r_y = range_of(has_seq ? y : nullptr, bld * es);
     const Range r_hl = range_of(h_last, bdn * 4);
+    const Range r_ws = range_of(need > 0 ? workspace : nullptr, (int64_t)need);
     for (const Range &r : r_in)
-        if (overlaps(r_y, r) || overlaps(r_hl, r))
+        if (overlaps(r_y, r) || overlaps(r_hl, r) || overlaps(r_ws, r))
             return MAMBA_ERR_ALIASING;
     if (overlaps(r_y, r_h0) || overlaps(r_y, r_hl) || overlaps(r_hl, r_h0))
         return MAMBA_ERR_ALIASING; // (h_last is written while h0 is still being read)
+    if (overlaps(r_ws, r_h0) || overlaps(r_ws, r_y) || overlaps(r_ws, r_hl))
+        return MAMBA_ERR_ALIASING;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (!has_seq) {
         if (h_last)
@@ -1210,7 +1297,24 @@ mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A, cons
     q.head_dim = head_dim;
     q.d_state = d_state;
     q.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+    if (plan.units > 0) {
+        char *ws = static_cast<char *>(workspace);
+        q.relay_units = plan.units;
+        q.relay_mid = plan.mid;
+        q.relay_sync = reinterpret_cast<uint32_t *>(ws);
+        q.relay_state = reinterpret_cast<float *>(ws + ssd_sync_bytes(plan));
+    }
     return hip_status(launch_ssd(q, st));
+}
+
+mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A, const void *B,
+                             const void *C, const float *D, const void *z,
+                             const float *dt_bias, const float *h0, void *y, float *h_last,
+                             int64_t batch, int64_t seqlen, int64_t n_heads, int64_t head_dim,
+                             int64_t d_state, mamba_dtype_t dtype, void *stream)
+{
+    return mamba_ssd_fwd_ex(x, dt, A, B, C, D, z, dt_bias, h0, y, h_last, batch, seqlen,
+                            n_heads, head_dim, d_state, dtype, nullptr, 0, 1, stream);
 }
 
 } // extern "C"

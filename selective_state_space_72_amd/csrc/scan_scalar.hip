@@ -17,6 +17,7 @@
 #include <type_traits>
 
 #include "device_math.h"
+#include "relay.h"
 #include "scan_common.h"
 
 namespace mambascan {
@@ -97,20 +98,6 @@ __device__ __forceinline__ void buf_store(float v, rsrc_t r, uint32_t vo, uint32
 __device__ __forceinline__ void buf_store(float v, rsrc_t r, uint32_t vo, uint32_t so, float *)
 {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, vo, so, 0);
-}
-
-// Bounded wait for a relay flag.  Polls with relaxed device-scope loads (no cache
-// invalidation per poll, which would disturb every other wave on the XCD) and long
-// sleeps, then acquires once; gives up after 2^20 polls (a few seconds), so a missing
-// hand-off can never hang the device.
-__device__ __forceinline__ void relay_wait(uint32_t *flag)
-{
-    for (uint32_t i = 0; i < (1u << 20); ++i) {
-        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
-            break;
-        __builtin_amdgcn_s_sleep(127);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 // Inputs of the Mamba-3 options: trapezoid mixing coefficients lam (as u), the input
@@ -214,10 +201,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     if (relayed && part > 0) {
         // the previous part's final state: wait for its flag, then read it
         const int slot = r_unit * (relay.parts - 1) + part - 1;
-        if (threadIdx.x == 0)
-            relay_wait(relay.sync + slot);
-        __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        relay_receive(relay.sync + slot);
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
             h[q] = relay.state[((int64_t)slot * N + n0 + q) * 64 + lane];
@@ -490,11 +474,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
             relay.state[((int64_t)slot * N + n0 + q) * 64 + lane] = h[q];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (threadIdx.x == 0)
-            __hip_atomic_store(relay.sync + slot, 1u, __ATOMIC_RELEASE,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        relay_signal(relay.sync + slot);
         return;
     }
     if (!dvalid)

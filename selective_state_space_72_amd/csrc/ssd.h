@@ -14,10 +14,20 @@ struct SsdLaunch {
     float *h_last;                  // nullable
     int64_t batch, L, n_heads, head_dim, d_state;
     DType dtype;
+    // Relay: the last relay_units (batch row, head) units run as two blocks each, the
+    // second continuing from step relay_mid (a multiple of the chunk) with the first's
+    // final state, handed over through relay_state (head_dim x d_state fp32 per unit) and
+    // relay_sync (one flag per unit).  relay_units = 0: no relay.
+    int64_t relay_units, relay_mid;
+    uint32_t *relay_sync;
+    float *relay_state;
 };
 
 // True if (head_dim, d_state) is compiled in.
 bool ssd_supported(int64_t head_dim, int64_t d_state);
+// Blocks of the SSD kernel for (d_state, dtype) that the current device runs at once
+// (blocks per compute unit x compute units); 0 if unknown.
+int64_t ssd_block_slots(int64_t d_state, DType dtype);
 hipError_t launch_ssd(const SsdLaunch &p, hipStream_t stream);
 
 } // namespace mambascan

@@ -45,6 +45,7 @@
 // Blocks are numbered so that each XCD takes a contiguous range of (batch row, head) pairs:
 // the heads of one batch row share B and C in that XCD's L2.
 #include "device_math.h"
+#include "relay.h"
 #include "scan_common.h"
 #include "ssd.h"
 
@@ -178,6 +179,12 @@ struct SsdArgs {
     float *h_last;
     int64_t L;
     int32_t H; // heads
+    // relay: units = batch * heads; the last r_units of them run in two parts, the second
+    // from step r_mid; 0 = none
+    int32_t units, r_units;
+    int64_t r_mid;
+    uint32_t *r_sync;
+    float *r_state;
 };
 
 // bf16: two blocks per CU (75 KB of LDS each at N = 128), so registers are held to 256
@@ -216,12 +223,32 @@ ssd_chunk_kernel(SsdArgs p)
     const int tid = threadIdx.x;
     const int lane = tid & 63, g = lane >> 4, r16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nblk = (int)gridDim.x;
-    int bh = (int)blockIdx.x;
-    if (nblk % 8 == 0) // blocks go round-robin over the 8 XCDs: give each a contiguous range
-        bh = (bh % 8) * (nblk / 8) + bh / 8;
-    const int b = bh / p.H, h = bh % p.H;
+
+    // Work unit (batch row, head) and steps [t_begin, L) of this block.  Blocks go
+    // round-robin over the 8 XCDs; the whole units are renumbered so each XCD takes a
+    // contiguous range (the heads of a batch row share B and C in one L2).  With relay the
+    // grid is [part 0 of each relayed unit][whole units][part 1 of each relayed unit]:
+    // workgroups are dispatched in index order, so the part-0 blocks start in the first
+    // round, the part-1 blocks take the slots the whole units' last round frees, and a
+    // part 1 waits only for a block of smaller index.
+    const int idx = (int)blockIdx.x;
+    const int whole = p.units - p.r_units;
+    int bh = idx - p.r_units, part = -1;
     const int64_t L = p.L;
+    int64_t t_begin = 0, t_end = L;
+    if (idx < p.r_units) {
+        bh = whole + idx;
+        part = 0;
+        t_end = p.r_mid;
+    } else if (idx >= p.units) {
+        bh = whole + (idx - p.units);
+        part = 1;
+        t_begin = p.r_mid;
+    } else if (whole % 8 == 0 && p.r_units % 8 == 0) {
+        bh = (bh % 8) * (whole / 8) + bh / 8;
+    }
+    const int slot = bh - whole; // relay slot of a relayed unit
+    const int b = bh / p.H, h = bh % p.H;
     const int64_t Dn = (int64_t)p.H * P;
     const int pc = 16 * w + r16; // this lane's column of Y and of H
 
@@ -240,7 +267,7 @@ ssd_chunk_kernel(SsdArgs p)
     // ---- state slab: tile m holds rows n = 16m + 4g + v, column pc ----
     f32x4 hacc[NT];
     const int64_t hrow = ((int64_t)b * Dn + (int64_t)h * P + pc) * N;
-    if (p.h0) {
+    if (p.h0 && part != 1) {
 #pragma unroll
         for (int m = 0; m < NT; ++m)
 #pragma unroll
@@ -265,7 +292,7 @@ ssd_chunk_kernel(SsdArgs p)
     u32x4 fx[XU][2], fb[BU][2], fc[BU][2];
     uint32_t fdt = 0;
     auto fetch = [&](int64_t c0) {
-        const int nok = (int)min((int64_t)Q, L - c0);
+        const int nok = (int)min((int64_t)Q, t_end - c0);
         const rsrc_t rx = make_rsrc(xb + c0 * row_x, (uint32_t)(nok - 1) * row_x + P * ES);
         const rsrc_t rb = make_rsrc(bb + c0 * row_b, (uint32_t)nok * row_b);
         const rsrc_t rc = make_rsrc(cb + c0 * row_b, (uint32_t)nok * row_b);
@@ -334,7 +361,7 @@ ssd_chunk_kernel(SsdArgs p)
     // than waves 0 and 1): an inclusive, compensated prefix sum
     // over the 64 steps by DPP row shifts, then row broadcasts across the 16-lane rows
     auto decays = [&](int64_t c0) {
-        const int nn = (int)min((int64_t)Q, L - c0);
+        const int nn = (int)min((int64_t)Q, t_end - c0);
         const float dv = ES == 2 ? __uint_as_float(fdt << 16) : __uint_as_float(fdt);
         const float dl = lane < nn ? softplus_f(dv + dtb) : 0.0f;
         float cs = dl * a2, csl = 0.0f;
@@ -363,16 +390,25 @@ ssd_chunk_kernel(SsdArgs p)
 
     // Pipeline: chunk c is staged into LDS while chunk c - 1 finishes (M X and the stores),
     // and its global loads were issued while chunk c - 2 did.
-    if (L > 0) {
-        fetch(0);
+    if (t_begin < t_end) {
+        fetch(t_begin);
         stage();
         if (w == 3)
-            decays(0);
-        if (Q < L)
-            fetch(Q);
+            decays(t_begin);
+        if (t_begin + Q < t_end)
+            fetch(t_begin + Q);
     }
-    for (int64_t t0 = 0; t0 < L; t0 += Q) {
-        const int nt = (int)min((int64_t)Q, L - t0);
+    if (part == 1) {
+        // part 0's final state, once its first chunk is on the way
+        relay_receive(p.r_sync + slot);
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                hacc[m][v] = p.r_state[((int64_t)slot * P + pc) * N + 16 * m + 4 * g + v];
+    }
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += Q) {
+        const int nt = (int)min((int64_t)Q, t_end - t0);
         const uint32_t ybytes = (uint32_t)(nt - 1) * row_x + P * ES;
         // gate of this lane's outputs (rows 16 rt + 4g + v), wanted at the end of the chunk
         uint32_t fz[16];
@@ -499,11 +535,11 @@ ssd_chunk_kernel(SsdArgs p)
         lds_barrier(); // M complete; X, B, C and the decays of this chunk no longer read
 
         // ---- the next chunk into LDS and its decays; the loads of the one after ----
-        if (t0 + Q < L) {
+        if (t0 + Q < t_end) {
             stage();
             if (w == 3)
                 decays(t0 + Q);
-            if (t0 + 2 * Q < L)
+            if (t0 + 2 * Q < t_end)
                 fetch(t0 + 2 * Q);
         }
 
@@ -533,6 +569,16 @@ ssd_chunk_kernel(SsdArgs p)
         }
     }
 
+    if (part == 0) {
+        // hand the final state to part 1 (the part covers whole chunks: no tail rows)
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                p.r_state[((int64_t)slot * P + pc) * N + 16 * m + 4 * g + v] = hacc[m][v];
+        relay_signal(p.r_sync + slot);
+        return;
+    }
     if (p.h_last) {
 #pragma unroll
         for (int m = 0; m < NT; ++m)
@@ -540,6 +586,15 @@ ssd_chunk_kernel(SsdArgs p)
             for (int v = 0; v < 4; ++v)
                 p.h_last[hrow + 16 * m + 4 * g + v] = hacc[m][v];
     }
+}
+
+// Zeroes the relay flags before a relayed launch (a kernel, not a memset: the launch
+// sequence stays capturable in a graph).
+__global__ void ssd_relay_clear_kernel(uint32_t *sync, int32_t n)
+{
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n)
+        sync[i] = 0u;
 }
 
 template <typename T, int N>
@@ -559,9 +614,23 @@ hipError_t launch_ssd_t(const SsdLaunch &q, hipStream_t stream)
     a.h_last = q.h_last;
     a.L = q.L;
     a.H = (int32_t)q.n_heads;
-    const int64_t blocks = q.batch * q.n_heads;
-    if (blocks <= 0)
+    const int64_t units = q.batch * q.n_heads;
+    if (units <= 0)
         return hipSuccess;
+    a.units = (int32_t)units;
+    a.r_units = (int32_t)q.relay_units;
+    a.r_mid = q.relay_mid;
+    a.r_sync = q.relay_sync;
+    a.r_state = q.relay_state;
+    const int64_t blocks = units + q.relay_units;
+    if (q.relay_units > 0) {
+        const int32_t n = (int32_t)q.relay_units;
+        hipLaunchKernelGGL(ssd_relay_clear_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256),
+                           0, stream, q.relay_sync, n);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     if (q.z)
         hipLaunchKernelGGL((ssd_chunk_kernel<T, N, true>), dim3((uint32_t)blocks), dim3(kThreads),
                            0, stream, a);
@@ -576,6 +645,34 @@ hipError_t launch_ssd_t(const SsdLaunch &q, hipStream_t stream)
 bool ssd_supported(int64_t head_dim, int64_t d_state)
 {
     return head_dim == kP && (d_state == 64 || d_state == 128);
+}
+
+namespace {
+template <typename T, int N>
+int64_t block_slots_t()
+{
+    int dev = 0, cu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(ssd_chunk_kernel<T, N, true>), kThreads,
+            0) != hipSuccess ||
+        cu <= 0 || per_cu <= 0) {
+        (void)hipGetLastError(); // do not leave a sticky error behind
+        return 0;
+    }
+    return (int64_t)cu * per_cu;
+}
+} // namespace
+
+int64_t ssd_block_slots(int64_t d_state, DType dtype)
+{
+    const bool bf = dtype == DType::BF16;
+    switch (d_state) {
+    case 64: return bf ? block_slots_t<uint16_t, 64>() : block_slots_t<float, 64>();
+    case 128: return bf ? block_slots_t<uint16_t, 128>() : block_slots_t<float, 128>();
+    default: return 0;
+    }
 }
 
 hipError_t launch_ssd(const SsdLaunch &q, hipStream_t stream)

@@ -435,6 +435,46 @@ def test_ssd_validation(lib):
     assert ssd(lib, L=0) == OK                              # no state asked for: nothing to do
 
 
+def ssd_ex(lib, *, ws=None, ws_bytes=0, relay=2, **kw):
+    a = dict(x=BASE, dt=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB,
+             C=BASE + 400 * MB, D=BASE + 500 * MB, z=BASE + 600 * MB, bias=BASE + 700 * MB,
+             h0=None, y=BASE + 800 * MB, hl=None, batch=2, L=200, H=4, P=64, N=128, dtype=BF16)
+    a.update(kw)
+    return lib.mamba_ssd_fwd_ex(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                a["bias"], a["h0"], a["y"], a["hl"], a["batch"], a["L"],
+                                a["H"], a["P"], a["N"], a["dtype"], ws, ws_bytes, relay, None)
+
+
+def test_ssd_relay_workspace(lib):
+    """Forced relay: one flag (256-byte aligned block) and one head_dim x d_state fp32 state
+    per relayed unit -- every unit when they fit the device; none for a single chunk or
+    with the relay off; invalid options and shapes give (size_t)-1 and errors."""
+    bad = ctypes.c_size_t(-1).value
+    size = lib.mamba_ssd_workspace_size
+    assert size(2, 200, 4, 64, 128, BF16, 2) == 256 + 8 * 64 * 128 * 4
+    assert size(3, 130, 100, 64, 64, F32, 2) == 1280 + 300 * 64 * 64 * 4   # 300 flags
+    assert size(2, 64, 4, 64, 128, BF16, 2) == 0          # one chunk: nothing to split
+    assert size(2, 200, 4, 64, 128, BF16, 1) == 0         # off
+    assert size(2, 0, 4, 64, 128, BF16, 2) == 0
+    for relay in (-1, 3):
+        assert size(2, 200, 4, 64, 128, BF16, relay) == bad
+    assert size(2, 200, 4, 32, 128, BF16, 0) == bad       # head_dim not compiled in
+    assert size(-1, 200, 4, 64, 128, BF16, 0) == bad
+    assert size(2, 200, 4, 64, 128, 7, 0) == bad
+    need = size(2, 200, 4, 64, 128, BF16, 2)
+    ws = BASE + 2048 * MB
+    assert ssd_ex(lib, relay=3) == UNSUP and ssd_ex(lib, relay=-1) == UNSUP
+    assert ssd_ex(lib) == WS                                 # no workspace
+    assert ssd_ex(lib, ws=ws, ws_bytes=need - 4) == WS
+    assert ssd_ex(lib, ws=ws + 2, ws_bytes=need) == ALIGN
+    assert ssd_ex(lib, ws=BASE + 64, ws_bytes=need) == ALIAS              # over x
+    assert ssd_ex(lib, ws=BASE + 800 * MB, ws_bytes=need) == ALIAS        # over y
+    assert ssd_ex(lib, ws=ws, ws_bytes=need, hl=ws + 4096) == ALIAS       # over h_last
+    assert ssd_ex(lib, ws=ws, ws_bytes=need, P=32) == UNSUP
+    assert ssd_ex(lib, ws=ws, ws_bytes=need, x=None) == NULL
+    assert ssd_ex(lib, batch=0) == OK                        # nothing to do, no workspace
+
+
 # ---- checkpoints written by the forward pass for the backward pass ----------------
 
 def test_ckpt_size(lib):

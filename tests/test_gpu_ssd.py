@@ -21,12 +21,12 @@ from ssd_reference import ssd_oracle
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(s, *, use_D=True, use_bias=True, use_h0=True):
+def run_gpu(s, *, use_D=True, use_bias=True, use_h0=True, relay="auto"):
     y, h = ms.mamba_ssd_fwd(to_dev(s.x), to_dev(s.dt), to_dev(s.A), to_dev(s.B), to_dev(s.C),
                             D=to_dev(s.D) if use_D else None, z=to_dev(s.z),
                             dt_bias=to_dev(s.dt_bias) if use_bias else None,
                             h0=to_dev(s.h0) if use_h0 else None, return_last_state=True,
-                            head_dim=s.head_dim)
+                            head_dim=s.head_dim, relay=relay)
     torch.cuda.synchronize()
     return y, h
 
@@ -114,6 +114,64 @@ def test_ssd_bf16_d_state_64():
 def test_ssd_fp32_remapped_grid():
     s = synth.make_ssd_inputs(2, 70, 4, d_state=128, dtype=synth.F32, h0=True)
     check(s, "ssd fp32 N=128, 8 blocks")
+
+
+@pytest.mark.parametrize("dtype,d_state,seqlen,gate,h0", [
+    (synth.F32, 64, 200, True, True),      # 4 chunks, ragged last
+    (synth.BF16, 128, 130, False, False),  # 3 chunks: parts of 2 and 1
+    (synth.BF16, 64, 128, True, True),     # 2 whole chunks: one each
+])
+def test_ssd_relay_forced(dtype, d_state, seqlen, gate, h0):
+    """Every unit in two parts (the second from the middle chunk, continuing from the
+    first's final state handed over through the workspace): against the oracle, and
+    bitwise equal to the call without relay."""
+    s = synth.make_ssd_inputs(2, seqlen, 3, d_state=d_state, dtype=dtype, gate=gate, h0=h0)
+    need = ms.mamba_ssd_workspace_size(2, seqlen, 3, 64, d_state, dtype, relay="force")
+    assert need == 256 + 6 * 64 * d_state * 4
+    label = f"ssd relay forced, {dtype} N={d_state} L={seqlen}"
+    log(f"case {label}")
+    y, h = run_gpu(s, relay="force")
+    (yr, hr), _ = run_oracle(s)
+    ey, eh = metric(from_dev(y), yr), metric(from_dev(h), hr)
+    log(f"{label}: y {ey:.2e}, h_last {eh:.2e}")
+    assert ey <= TOL[dtype] and eh <= TOL[dtype]
+    y0, h0_ = run_gpu(s, relay="off")
+    assert torch.equal(y, y0) and torch.equal(h, h0_)
+
+
+def test_ssd_relay_mixed_grid():
+    """576 units (8 batch rows x 72 heads), 8 chunks: on a device with 512 block slots
+    (MI355X, two blocks per compute unit) the 64 units past the full round run in two
+    parts beside 512 whole units.  Bitwise equal to the call without relay; sampled heads
+    (whole and relayed units) against the oracle."""
+    s = synth.make_ssd_inputs(8, 512, 72, d_state=128, dtype=synth.BF16, gate=True, h0=True)
+    need = ms.mamba_ssd_workspace_size(8, 512, 72, 64, 128, synth.BF16)
+    log(f"ssd 576 units: relay workspace {need} bytes")
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert need == 256 + 64 * 64 * 128 * 4
+    y, h = run_gpu(s)
+    y0, h0_ = run_gpu(s, relay="off")
+    assert torch.equal(y, y0) and torch.equal(h, h0_)
+    heads = [0, 35, 71]  # head 35 and 71 of batch row 7 are relayed units
+    (yr, hr), ch = run_oracle(s, heads)
+    chd = torch.from_numpy(ch).to(y.device)
+    ey = metric(from_dev(y[:, :, chd].contiguous()), yr)
+    eh = metric(from_dev(h[:, chd].contiguous()), hr)
+    log(f"ssd 576 units, heads {heads}: y {ey:.2e}, h_last {eh:.2e}")
+    assert ey <= TOL[synth.BF16] and eh <= TOL[synth.BF16]
+
+
+def test_ssd_large_relay_equals_unrelayed():
+    """The large shape (640 units; relayed on MI355X) equals the unrelayed call bitwise."""
+    c = synth.SSD_LARGE
+    s = synth.make_ssd_inputs(c["batch"], c["seqlen"], c["n_heads"], c["head_dim"],
+                              c["d_state"], c["dtype"], c["gate"], c["h0"], c["seed"])
+    need = ms.mamba_ssd_workspace_size(c["batch"], c["seqlen"], c["n_heads"], c["head_dim"],
+                                       c["d_state"], c["dtype"])
+    log(f"ssd large: relay workspace {need} bytes")
+    y, h = run_gpu(s)
+    y0, h0_ = run_gpu(s, relay="off")
+    assert torch.equal(y, y0) and torch.equal(h, h0_)
 
 
 def test_ssd_empty_sequence_returns_h0():
