@@ -515,15 +515,22 @@ def main():
         print(json.dumps(res), flush=True)
         return
     if args.bwd_only:
-        log("bench: backward pass on the large prefill")
+        log("bench: backward pass on the large prefill (own states, then from checkpoints)")
         bcase = BwdCase(cfg, dev)
         loop_ms, _, _ = time_steps(bcase.step, args.steps, args.warmup)
+        min_bytes = bcase.min_bytes
+        del bcase
+        torch.cuda.empty_cache()
+        ccase = CkptTrainCase(cfg, dev)
+        f_ms, _, _ = time_steps(ccase.forward, args.steps, args.warmup)
+        b_ms, _, _ = time_steps(ccase.step, args.steps, args.warmup)
         if args.copy_calibration:
             copy_calibration(dev)
         print(json.dumps({"workload": "backward of the large-model prefill scan",
                           "steps": args.steps, "ms_per_step": round(loop_ms, 4),
-                          "min_bytes_per_step": bcase.min_bytes,
-                          "GB_s": round(bcase.min_bytes / (loop_ms * 1e-3) / 1e9, 1)}),
+                          "min_bytes_per_step": min_bytes,
+                          "GB_s": round(min_bytes / (loop_ms * 1e-3) / 1e9, 1),
+                          "fwd_ckpt_ms": round(f_ms, 4), "bwd_from_ckpt_ms": round(b_ms, 4)}),
               flush=True)
         return
     log(f"bench: generating {cfg.name} inputs")
