@@ -17,7 +17,9 @@
 //   Y      = M X + diag(exp(cs)) C H_in               (Q x P)
 //   H_out  = exp(cs_{Q-1}) H_in + B^T Xtil,   Xtil[s,p] = exp(cs_{Q-1} - cs_s) Delta_s X[s,p]
 // One block per (batch row, head) walks the chunks in order; nothing of the chunk states
-// goes to HBM.
+// goes to HBM.  When the units overflow the device's block slots by a partial round, the
+// units of that round are relayed: each runs as two blocks, the second continuing from
+// the first's final state (relay.h), so the last round is not left mostly idle.
 //
 // Work split.  Wave w of the block's four owns the columns p in [16w, 16w + 16) of Y and of
 // H, and keeps its N x 16 slab of H in MFMA accumulators (16 x 16 tiles) from chunk to
@@ -32,8 +34,8 @@
 // v_mfma_f32_16x16x4f32 for fp32 inputs.  With bf16 inputs, X, B and C are exact bf16
 // values, but M, Xtil and H are computed in fp32: each is split as hi + lo (hi = its bf16
 // rounding, lo = the bf16 rounding of the remainder) and enters as two products, which
-// keeps about 16 significant bits (a single bf16 operand measured 1.4e-2 relative error in
-// y and in the state on a CPU emulation of this arithmetic).
+// keeps about 16 significant bits (rounding any one of them to a single bf16 measured
+// 2.2e-2 to 4.4e-2 relative error in y on a CPU emulation of this arithmetic).
 //
 // Memory.  Inputs are read with 16-byte buffer loads through descriptors that end at the
 // chunk's last row, so rows past the end of the sequence read as zero and stores to them
