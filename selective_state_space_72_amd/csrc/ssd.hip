@@ -46,6 +46,8 @@
 // banks (measured 7 % faster than 16-byte row padding, which keeps addresses affine).
 // Blocks are numbered so that each XCD takes a contiguous range of (batch row, head) pairs:
 // the heads of one batch row share B and C in that XCD's L2.
+#include <atomic>
+
 #include "device_math.h"
 #include "relay.h"
 #include "scan_common.h"
@@ -651,11 +653,10 @@ bool ssd_supported(int64_t head_dim, int64_t d_state)
 
 namespace {
 template <typename T, int N>
-int64_t block_slots_t()
+int64_t block_slots_t(int dev)
 {
-    int dev = 0, cu = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+    int cu = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, reinterpret_cast<const void *>(ssd_chunk_kernel<T, N, true>), kThreads,
             0) != hipSuccess ||
@@ -665,16 +666,38 @@ int64_t block_slots_t()
     }
     return (int64_t)cu * per_cu;
 }
+
+// Per device and kernel variant, queried once (the planner asks on every call).
+constexpr int kSlotDevices = 64;
+std::atomic<int64_t> g_slots[kSlotDevices][4];
 } // namespace
 
 int64_t ssd_block_slots(int64_t d_state, DType dtype)
 {
     const bool bf = dtype == DType::BF16;
-    switch (d_state) {
-    case 64: return bf ? block_slots_t<uint16_t, 64>() : block_slots_t<float, 64>();
-    case 128: return bf ? block_slots_t<uint16_t, 128>() : block_slots_t<float, 128>();
-    default: return 0;
+    if (d_state != 64 && d_state != 128)
+        return 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
     }
+    const int v = (d_state == 128 ? 2 : 0) + (bf ? 1 : 0);
+    if (dev >= 0 && dev < kSlotDevices) {
+        const int64_t c = g_slots[dev][v].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int64_t n = 0;
+    switch (v) {
+    case 0: n = block_slots_t<float, 64>(dev); break;
+    case 1: n = block_slots_t<uint16_t, 64>(dev); break;
+    case 2: n = block_slots_t<float, 128>(dev); break;
+    default: n = block_slots_t<uint16_t, 128>(dev); break;
+    }
+    if (n > 0 && dev >= 0 && dev < kSlotDevices)
+        g_slots[dev][v].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 hipError_t launch_ssd(const SsdLaunch &q, hipStream_t stream)
