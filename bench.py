@@ -431,8 +431,9 @@ def extra_workloads(dev, flush, steps):
                  "hbm_frac": round(dbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del t, y
     torch.cuda.empty_cache()
-    # Mamba-2 SSD scan (chunked, on the matrix cores) on its large shape
+    # Mamba-2 SSD scan (chunked, on the matrix cores) on its large shape, and its decode token
     out["ssd_large"] = ssd_workload(dev, flush, steps)
+    out["ssd_decode"] = ssd_decode_workload(dev, flush, steps)
     return out
 
 
@@ -473,6 +474,36 @@ def ssd_workload(dev, flush, steps):
             "TFLOP_s": round(tf, 1), "mfma_bf16_frac": round(tf / 2500.0, 4),
             "bytes_per_step": nbytes, "flop_per_step": flop,
             "relayed_units": need // (sc["head_dim"] * sc["d_state"] * 4)}
+
+
+def ssd_decode_workload(dev, flush, steps):
+    """One Mamba-2 decode token on a persistent fp32 state of 64 rows x 80 heads x 64 x
+    d_state 128 (the SSD large shape's heads), bf16 token inputs, gated.  Bytes: the
+    state read and written, the token's x, z, y, dt, B, C and the per-head parameters."""
+    import torch
+    import selective_state_space_72_amd as ms
+    from selective_state_space_72_amd import synth
+    batch, H, P, N = 64, 80, 64, 128
+    si = synth.make_ssd_inputs(batch, 1, H, P, N, synth.BF16, True, True, 7220)
+    t = {k: to_dev(v, dev) for k, v in dict(x=si.x[:, 0], dt=si.dt[:, 0], B=si.B[:, 0],
+                                              C=si.C[:, 0], z=si.z[:, 0], A=si.A, D=si.D,
+                                              bias=si.dt_bias, h=si.h0).items()}
+    y = torch.empty((batch, H * P), dtype=torch.bfloat16, device=dev)
+
+    def dstep():
+        ms.mamba_ssd_state_update(t["h"], t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"],
+                                  z=t["z"], dt_bias=t["bias"], out=y, head_dim=P)
+    loop_ms, med, _ = time_steps(dstep, max(steps, 50), 10, flush, warm_ms=100.0)
+    nbytes = batch * H * P * N * 8 + batch * H * P * 2 * 3 + batch * H * 2 + \
+        batch * N * 2 * 2 + H * 4 * 3
+    del t, y
+    torch.cuda.empty_cache()
+    return {"workload": "Mamba-2 SSD decode token: state (64, 80 x 64, 128) fp32, bf16 token "
+                        "inputs, gated",
+            "ms": round(med, 5), "ms_chained_cache_warm": round(loop_ms, 5),
+            "GB_s": round(nbytes / (med * 1e-3) / 1e9, 1),
+            "GB_s_chained_cache_warm": round(nbytes / (loop_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def copy_calibration(dev):

@@ -530,6 +530,32 @@ MAMBA_API mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const f
                                           void *workspace, size_t workspace_bytes,
                                           int32_t relay, void *stream);
 
+/*
+ * One decode token of the Mamba-2 SSD on a persistent fp32 state: the recurrence of
+ * mamba_ssd_fwd for a single step ("Understanding Mamba" section 6, "State space models and
+ * the Mamba series" section 1.2, in their recurrent form), with Delta = softplus(dt[b,h] +
+ * dt_bias[h]) and exp(Delta A[h]) shared by the head's channels and state indices:
+ *   h[b,h*P+p,n] <- exp(Delta A[h]) h[b,h*P+p,n] + Delta B[b,n] x[b,h*P+p]
+ *   y[b,h*P+p]    = (sum_n C[b,n] h[b,h*P+p,n] + D[h] x[b,h*P+p]) * silu(z[b,h*P+p])
+ *   h          (batch, n_heads * head_dim, d_state) float32, updated in place, 16-byte
+ *              aligned (moved as 16-byte vectors)
+ *   x, z, y    (batch, n_heads * head_dim) dtype        z nullable (no gate)
+ *   dt         (batch, n_heads) dtype
+ *   B, C       (batch, d_state) dtype
+ *   A          (n_heads) float32        D, dt_bias (n_heads) float32 nullable
+ * Sizes, dtypes and supported (head_dim, d_state) as for mamba_ssd_fwd.  y must not overlap
+ * h or any input, and h no input.  fp32 arithmetic throughout; chained steps follow the
+ * scan's recurrence exactly, while mamba_ssd_fwd evaluates it in chunked matrix form (equal
+ * within the stated bounds, not bitwise).  No workspace.
+ */
+MAMBA_API mamba_status_t mamba_ssd_state_update(float *h, const void *x, const void *dt,
+                                                const float *A, const void *B, const void *C,
+                                                const float *D, const void *z,
+                                                const float *dt_bias, void *y, int64_t batch,
+                                                int64_t n_heads, int64_t head_dim,
+                                                int64_t d_state, mamba_dtype_t dtype,
+                                                void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 MAMBA_API const char *mamba_status_string(mamba_status_t status);
 

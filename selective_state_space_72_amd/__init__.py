@@ -40,6 +40,7 @@ EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_scan_bwd_workspace_size_ex", "mamba_scan_bwd_ex",
            "mamba_scan_fwd_workspace_size_ext", "mamba_scan_fwd_ext", "mamba_state_update_ext",
            "mamba_ssd_supported", "mamba_ssd_fwd", "mamba_ssd_workspace_size", "mamba_ssd_fwd_ex",
+           "mamba_ssd_state_update",
            "mamba_scan_ckpt_size", "mamba_scan_bwd_ckpt_workspace_size", "mamba_scan_bwd_ckpt",
            "mamba_status_string")
 
@@ -136,6 +137,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mamba_ssd_supported.argtypes = [_i64, _i64]
     lib.mamba_ssd_fwd.restype = ctypes.c_int
     lib.mamba_ssd_fwd.argtypes = [_vp] * 11 + [_i64] * 5 + [ctypes.c_int, _vp]
+    lib.mamba_ssd_state_update.restype = ctypes.c_int
+    lib.mamba_ssd_state_update.argtypes = [_vp] * 10 + [_i64] * 4 + [ctypes.c_int, _vp]
     lib.mamba_ssd_workspace_size.restype = ctypes.c_size_t
     lib.mamba_ssd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int, ctypes.c_int32]
     lib.mamba_ssd_fwd_ex.restype = ctypes.c_int
@@ -621,3 +624,40 @@ def mamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None,
     if st != 0:
         raise MambaError(st, "mamba_ssd_fwd_ex")
     return y, h_last
+
+
+def mamba_ssd_state_update(h, x, dt, A, B, C, D=None, z=None, dt_bias=None, *, out=None,
+                           head_dim: int = 64):
+    """One Mamba-2 SSD decode token (see include/mamba_scan.h): h (batch, n_heads * head_dim,
+    d_state) fp32 is updated in place; x, z (batch, n_heads * head_dim), dt (batch, n_heads),
+    B, C (batch, d_state), A/D/dt_bias (n_heads,) fp32.  Returns y (batch, n_heads *
+    head_dim)."""
+    torch = _torch()
+    lib = load_library()
+    if x.dim() != 2 or dt.dim() != 2 or h.dim() != 3:
+        raise ValueError("x must be (batch, d_inner), dt (batch, n_heads), h (batch, d_inner, "
+                         "d_state)")
+    batch, d_inner = x.shape
+    n_heads = dt.shape[1]
+    if n_heads * head_dim != d_inner:
+        raise ValueError("d_inner must be n_heads * head_dim")
+    d_state = h.shape[2]
+    dev, act = x.device, x.dtype
+    code = _dtype_code(x)
+    f32 = torch.float32
+    p_h = _ptr(h, "h", (batch, d_inner, d_state), f32, dev)
+    p_x = _ptr(x, "x", (batch, d_inner), act, dev)
+    p_dt = _ptr(dt, "dt", (batch, n_heads), act, dev)
+    p_A = _ptr(A, "A", (n_heads,), f32, dev)
+    p_B = _ptr(B, "B", (batch, d_state), act, dev)
+    p_C = _ptr(C, "C", (batch, d_state), act, dev)
+    p_D = _ptr(D, "D", (n_heads,), f32, dev)
+    p_z = _ptr(z, "z", (batch, d_inner), act, dev)
+    p_bias = _ptr(dt_bias, "dt_bias", (n_heads,), f32, dev)
+    y = out if out is not None else torch.empty((batch, d_inner), dtype=act, device=dev)
+    p_y = _ptr(y, "out", (batch, d_inner), act, dev)
+    st = lib.mamba_ssd_state_update(p_h, p_x, p_dt, p_A, p_B, p_C, p_D, p_z, p_bias, p_y,
+                                    batch, n_heads, head_dim, d_state, code, _stream(dev))
+    if st != 0:
+        raise MambaError(st, "mamba_ssd_state_update")
+    return y

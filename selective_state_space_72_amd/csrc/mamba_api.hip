@@ -1307,6 +1307,62 @@ mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const float *A, c
     return hip_status(launch_ssd(q, st));
 }
 
+mamba_status_t mamba_ssd_state_update(float *h, const void *x, const void *dt, const float *A,
+                                      const void *B, const void *C, const float *D,
+                                      const void *z, const float *dt_bias, void *y,
+                                      int64_t batch, int64_t n_heads, int64_t head_dim,
+                                      int64_t d_state, mamba_dtype_t dtype, void *stream)
+{
+    const mamba_status_t shape_st = ssd_check_shape(batch, 1, n_heads, head_dim, d_state, dtype);
+    if (shape_st != MAMBA_OK)
+        return shape_st;
+    if (batch == 0 || n_heads == 0)
+        return MAMBA_OK;
+    if (!h || !x || !dt || !A || !B || !C || !y)
+        return MAMBA_ERR_NULL_ARG;
+    const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
+    const int64_t dn = n_heads * head_dim, bd = batch * dn, bh = batch * n_heads;
+    const int64_t bn = batch * d_state, bdn = bd * d_state;
+    const void *elem_ptrs[] = {x, dt, B, C, z, y};
+    for (const void *p : elem_ptrs)
+        if (p && !aligned(p, (size_t)es))
+            return MAMBA_ERR_MISALIGNED;
+    const void *f32_ptrs[] = {A, D, dt_bias};
+    for (const void *p : f32_ptrs)
+        if (p && !aligned(p, 4))
+            return MAMBA_ERR_MISALIGNED;
+    if (!aligned(h, 16)) // moved as 16-byte vectors
+        return MAMBA_ERR_MISALIGNED;
+    const Range r_in[] = {range_of(x, bd * es),          range_of(dt, bh * es),
+                          range_of(z, bd * es),          range_of(B, bn * es),
+                          range_of(C, bn * es),          range_of(A, n_heads * 4),
+                          range_of(D, n_heads * 4),      range_of(dt_bias, n_heads * 4)};
+    const Range r_h = range_of(h, bdn * 4);
+    const Range r_y = range_of(y, bd * es);
+    if (overlaps(r_h, r_y))
+        return MAMBA_ERR_ALIASING;
+    for (const Range &r : r_in)
+        if (overlaps(r_h, r) || overlaps(r_y, r))
+            return MAMBA_ERR_ALIASING;
+    SsdStepLaunch S{};
+    S.h = h;
+    S.x = x;
+    S.dt = dt;
+    S.B = B;
+    S.C = C;
+    S.z = z;
+    S.A = A;
+    S.D = D;
+    S.dt_bias = dt_bias;
+    S.y = y;
+    S.batch = batch;
+    S.n_heads = n_heads;
+    S.head_dim = head_dim;
+    S.d_state = d_state;
+    S.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+    return hip_status(launch_ssd_step(S, reinterpret_cast<hipStream_t>(stream)));
+}
+
 mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A, const void *B,
                              const void *C, const float *D, const void *z,
                              const float *dt_bias, const float *h0, void *y, float *h_last,

@@ -23,8 +23,19 @@ struct SsdLaunch {
     float *relay_state;
 };
 
+// One decode token of the SSD (ssd_step.hip).
+struct SsdStepLaunch {
+    float *h;                       // (batch, n_heads * head_dim, d_state) fp32, in place
+    const void *x, *dt, *B, *C, *z; // (batch, H*P), (batch, H), (batch, N) x2, (batch, H*P)
+    const float *A, *D, *dt_bias;   // (n_heads); D, dt_bias nullable
+    void *y;                        // (batch, n_heads * head_dim)
+    int64_t batch, n_heads, head_dim, d_state;
+    DType dtype;
+};
+
 // True if (head_dim, d_state) is compiled in.
 bool ssd_supported(int64_t head_dim, int64_t d_state);
+hipError_t launch_ssd_step(const SsdStepLaunch &p, hipStream_t stream);
 // Blocks of the SSD kernel for (d_state, dtype) that the current device runs at once
 // (blocks per compute unit x compute units); 0 if unknown.
 int64_t ssd_block_slots(int64_t d_state, DType dtype);

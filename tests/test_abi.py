@@ -475,6 +475,32 @@ def test_ssd_relay_workspace(lib):
     assert ssd_ex(lib, batch=0) == OK                        # nothing to do, no workspace
 
 
+def ssd_step(lib, **kw):
+    a = dict(h=BASE + 1000 * MB, x=BASE, dt=BASE + 100 * MB, A=BASE + 200 * MB,
+             B=BASE + 300 * MB, C=BASE + 400 * MB, D=BASE + 500 * MB, z=BASE + 600 * MB,
+             bias=BASE + 700 * MB, y=BASE + 800 * MB, batch=2, H=4, P=64, N=128, dtype=BF16)
+    a.update(kw)
+    return lib.mamba_ssd_state_update(a["h"], a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"],
+                                      a["z"], a["bias"], a["y"], a["batch"], a["H"], a["P"],
+                                      a["N"], a["dtype"], None)
+
+
+def test_ssd_state_update_validation(lib):
+    assert ssd_step(lib, P=32) == UNSUP and ssd_step(lib, N=16) == UNSUP
+    assert ssd_step(lib, dtype=7) == DTYPE
+    assert ssd_step(lib, batch=-1) == SHAPE and ssd_step(lib, H=-1) == SHAPE
+    for name in ("h", "x", "dt", "A", "B", "C", "y"):
+        assert ssd_step(lib, **{name: None}) == NULL, name
+    assert ssd_step(lib, h=BASE + 1000 * MB + 4) == ALIGN      # h moves as 16-byte vectors
+    assert ssd_step(lib, x=BASE + 1) == ALIGN
+    assert ssd_step(lib, dt=BASE + 100 * MB + 1) == ALIGN
+    assert ssd_step(lib, A=BASE + 200 * MB + 2) == ALIGN
+    assert ssd_step(lib, y=BASE + 64) == ALIAS                 # y over x
+    assert ssd_step(lib, y=BASE + 1000 * MB + 64) == ALIAS     # y over h
+    assert ssd_step(lib, h=BASE + 300 * MB) == ALIAS           # h over B
+    assert ssd_step(lib, batch=0) == OK and ssd_step(lib, H=0) == OK
+
+
 # ---- checkpoints written by the forward pass for the backward pass ----------------
 
 def test_ckpt_size(lib):

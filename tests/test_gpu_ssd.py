@@ -179,3 +179,68 @@ def test_ssd_empty_sequence_returns_h0():
     y, h = run_gpu(s)
     assert y.shape == (2, 0, 3 * 64)
     assert torch.equal(h.cpu(), torch.from_numpy(s.h0))
+
+
+# ---- the decode token (mamba_ssd_state_update) ----------------------------------------
+
+def step_gpu(s, t, h, *, use_D=True, use_bias=True, use_z=True):
+    """Token t of the inputs s through mamba_ssd_state_update on the device state h."""
+    sl = lambda a: to_dev(a[:, t]) if a is not None else None  # noqa: E731
+    return ms.mamba_ssd_state_update(h, sl(s.x), sl(s.dt), to_dev(s.A), sl(s.B), sl(s.C),
+                                     D=to_dev(s.D) if use_D else None,
+                                     z=sl(s.z) if use_z else None,
+                                     dt_bias=to_dev(s.dt_bias) if use_bias else None,
+                                     head_dim=s.head_dim)
+
+
+@pytest.mark.parametrize("dtype,d_state,gate,opt", [
+    (synth.F32, 64, True, True),
+    (synth.F32, 128, False, False),
+    (synth.BF16, 128, True, True),
+    (synth.BF16, 64, True, False),
+])
+def test_ssd_step_one_token(dtype, d_state, gate, opt):
+    """One token on a nonzero state against the oracle's one-step scan from that state."""
+    s = synth.make_ssd_inputs(3, 1, 5, d_state=d_state, dtype=dtype, gate=gate, h0=True)
+    h = to_dev(s.h0)
+    y = step_gpu(s, 0, h, use_D=opt, use_bias=opt)
+    torch.cuda.synchronize()
+    (yr, hr), _ = run_oracle(s, use_D=opt, use_bias=opt)
+    ey, eh = metric(from_dev(y), yr[:, 0]), metric(from_dev(h), hr)
+    log(f"ssd step {dtype} N={d_state} gate={gate} D/bias={opt}: y {ey:.2e}, h {eh:.2e}")
+    assert ey <= TOL[dtype] and eh <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_ssd_step_chain_equals_scan(dtype):
+    """200 chained tokens against the oracle's scan of the same 200 steps (every output
+    and the final state), and against the chunked scan on the device (same bounds)."""
+    L = 200
+    s = synth.make_ssd_inputs(2, L, 3, d_state=128, dtype=dtype, gate=True, h0=True)
+    h = to_dev(s.h0)
+    ys = [step_gpu(s, t, h) for t in range(L)]
+    torch.cuda.synchronize()
+    y = torch.stack(ys, dim=1)
+    (yr, hr), _ = run_oracle(s)
+    ey, eh = metric(from_dev(y), yr), metric(from_dev(h), hr)
+    yc, hc = run_gpu(s)
+    ec = metric(from_dev(y), from_dev(yc))
+    log(f"ssd {dtype} 200 chained tokens: y {ey:.2e}, h {eh:.2e}; against the chunked scan "
+        f"{ec:.2e}")
+    assert ey <= TOL[dtype] and eh <= TOL[dtype] and ec <= TOL[dtype]
+
+
+def test_ssd_step_large_sampled():
+    """The decode shape of the benchmark (64 rows x 80 heads x 64, d_state 128, bf16):
+    sampled heads against the oracle."""
+    s = synth.make_ssd_inputs(64, 1, 80, d_state=128, dtype=synth.BF16, gate=True, h0=True)
+    h = to_dev(s.h0)
+    y = step_gpu(s, 0, h)
+    torch.cuda.synchronize()
+    heads = [0, 41, 79]
+    (yr, hr), ch = run_oracle(s, heads)
+    chd = torch.from_numpy(ch).to(y.device)
+    ey = metric(from_dev(y[:, chd].contiguous()), yr[:, 0])
+    eh = metric(from_dev(h[:, chd].contiguous()), hr)
+    log(f"ssd step 64 x 80 heads, heads {heads}: y {ey:.2e}, h {eh:.2e}")
+    assert ey <= TOL[synth.BF16] and eh <= TOL[synth.BF16]
