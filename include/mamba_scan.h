@@ -498,28 +498,41 @@ MAMBA_API mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const floa
                                        mamba_dtype_t dtype, void *stream);
 
 /*
- * mamba_ssd_fwd with load balancing across the device (same results, bitwise).
- * The (batch row, head) units run one block each, a fixed number at a time (blocks per
- * compute unit x compute units, the "slots").  When the units overflow the slots by a
- * partial round, the units of that round would run on a mostly idle device; with the
- * relay they run in two parts each instead -- the first half of the sequence (whole
- * 64-step chunks) in the first round, the second half, continuing from the first's final
- * state, in the slots the last full round frees -- the balance the scan's relay gives
- * (mamba_scan_opts_t.relay).
- *   relay: 0 automatic (relay when units exceed the slots, the overflow is at most half
- *          of them and the sequence has at least 8 chunks); 1 off; 2 force two parts
- *          (sequences of at least 2 chunks) on the overflow units, or on every unit when
- *          they fit the slots (testing).  Other values: MAMBA_ERR_UNSUPPORTED.
- * Workspace (caller-owned device memory, 4-byte aligned, not overlapping any argument):
- * one flag and one head_dim x d_state fp32 state per relayed unit, size from
- * mamba_ssd_workspace_size for the same arguments on the same device (0: none needed, NULL
- * allowed; (size_t)-1 for arguments mamba_ssd_fwd_ex would reject); MAMBA_ERR_WORKSPACE
- * when missing or too small.  Its contents on entry do not matter and are overwritten.
- * Concurrent calls must not share a workspace.
+ * mamba_ssd_fwd with the device kept busy.  The (batch row, head) units run one block each,
+ * a fixed number at a time (blocks per compute unit x compute units, the "slots"):
+ *  - relay: when the units overflow the slots by a partial round, the units of that round
+ *    would run on a mostly idle device; instead each runs in two parts -- the first half of
+ *    the sequence (whole 64-step chunks) in the first round, the second, continuing from
+ *    the first's final state, in the slots the last full round frees (the balance the
+ *    scan's relay gives, mamba_scan_opts_t.relay).  Results equal mamba_ssd_fwd bitwise.
+ *  - split: when the units fill at most half of the slots, the sequence is cut into spans
+ *    (whole chunks) that run in parallel: a first pass gives each span's final state from
+ *    zero and its total decay, a carry turns them into the state entering each span, and
+ *    the output pass runs every span from its true state (the scan's span split).  Results
+ *    equal mamba_ssd_fwd within the stated bounds (the carry rounds differently).
+ * Options (NULL = automatic):
+ *   relay:   0 automatic (the overflow is at most half of the slots and the sequence has at
+ *            least 8 chunks); 1 off; 2 force two parts on the overflow units, or on every
+ *            unit when they fit the slots (testing; sequences of at least 2 chunks).
+ *   n_spans: 0 automatic (as many spans as fill one round, each of at least 8 chunks); 1 no
+ *            split; k in [2, 64] force k spans (fewer when the sequence has fewer chunks).
+ *   A split takes precedence over the relay; forcing both is MAMBA_ERR_UNSUPPORTED, as are
+ *   values out of range.
+ * Workspace (caller-owned device memory, 4-byte aligned, not overlapping any argument),
+ * size from mamba_ssd_workspace_size for the same arguments on the same device (0: none
+ * needed, NULL allowed; (size_t)-1 for arguments mamba_ssd_fwd_ex would reject): relay, one
+ * flag and one head_dim x d_state fp32 state per relayed unit; split, (n_spans - 1) states
+ * and decays per unit.  MAMBA_ERR_WORKSPACE when missing or too small.  Its contents on
+ * entry do not matter and are overwritten.  Concurrent calls must not share a workspace.
  */
+typedef struct {
+    int32_t relay;
+    int32_t n_spans;
+} mamba_ssd_opts_t;
+
 MAMBA_API size_t mamba_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
                                           int64_t head_dim, int64_t d_state,
-                                          mamba_dtype_t dtype, int32_t relay);
+                                          mamba_dtype_t dtype, const mamba_ssd_opts_t *opts);
 
 MAMBA_API mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const float *A,
                                           const void *B, const void *C, const float *D,
@@ -528,7 +541,7 @@ MAMBA_API mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const f
                                           int64_t seqlen, int64_t n_heads, int64_t head_dim,
                                           int64_t d_state, mamba_dtype_t dtype,
                                           void *workspace, size_t workspace_bytes,
-                                          int32_t relay, void *stream);
+                                          const mamba_ssd_opts_t *opts, void *stream);
 
 /*
  * One decode token of the Mamba-2 SSD on a persistent fp32 state: the recurrence of

@@ -66,6 +66,11 @@ class ScanOpts(ctypes.Structure):
                 ("relay", ctypes.c_int32), ("discretization", ctypes.c_int32)]
 
 
+class SsdOpts(ctypes.Structure):
+    """mamba_ssd_opts_t: relay (0 auto, 1 off, 2 force), n_spans (0 auto, 1 none, k)."""
+    _fields_ = [("relay", ctypes.c_int32), ("n_spans", ctypes.c_int32)]
+
+
 class ScanExt(ctypes.Structure):
     """mamba_scan_ext_t: trapezoid mixing coefficients, look-back input, rotation rates,
     checkpoint output for the backward pass."""
@@ -140,10 +145,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mamba_ssd_state_update.restype = ctypes.c_int
     lib.mamba_ssd_state_update.argtypes = [_vp] * 10 + [_i64] * 4 + [ctypes.c_int, _vp]
     lib.mamba_ssd_workspace_size.restype = ctypes.c_size_t
-    lib.mamba_ssd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int, ctypes.c_int32]
+    lib.mamba_ssd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int,
+                                                          ctypes.POINTER(SsdOpts)]
     lib.mamba_ssd_fwd_ex.restype = ctypes.c_int
     lib.mamba_ssd_fwd_ex.argtypes = ([_vp] * 11 + [_i64] * 5 + [ctypes.c_int, _vp,
-                                     ctypes.c_size_t, ctypes.c_int32, _vp])
+                                     ctypes.c_size_t, ctypes.POINTER(SsdOpts), _vp])
     lib.mamba_scan_ckpt_size.restype = ctypes.c_size_t
     lib.mamba_scan_ckpt_size.argtypes = [_i64] * 4
     lib.mamba_scan_bwd_ckpt_workspace_size.restype = ctypes.c_size_t
@@ -554,12 +560,19 @@ def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=No
 _SSD_RELAY = {"auto": 0, "off": 1, "force": 2}
 
 
+def _ssd_opts(relay: str, n_spans: int):
+    if relay not in _SSD_RELAY:
+        raise ValueError(f"relay must be one of {sorted(_SSD_RELAY)}")
+    return SsdOpts(_SSD_RELAY[relay], n_spans)
+
+
 def mamba_ssd_workspace_size(batch: int, seqlen: int, n_heads: int, head_dim: int,
-                             d_state: int, dtype, relay: str = "auto") -> int:
+                             d_state: int, dtype, relay: str = "auto", n_spans: int = 0) -> int:
     """Workspace bytes of mamba_ssd_fwd_ex on the current device (0: none needed)."""
     lib = load_library()
+    o = _ssd_opts(relay, n_spans)
     n = lib.mamba_ssd_workspace_size(batch, seqlen, n_heads, head_dim, d_state,
-                                     _dtype_code_of(dtype), _SSD_RELAY[relay])
+                                     _dtype_code_of(dtype), ctypes.byref(o))
     if n == ctypes.c_size_t(-1).value:
         raise MambaError(4, "mamba_ssd_workspace_size")
     return n
@@ -567,12 +580,14 @@ def mamba_ssd_workspace_size(batch: int, seqlen: int, n_heads: int, head_dim: in
 
 def mamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None,
                   return_last_state: bool = False, *, out=None, h_last_out=None,
-                  head_dim: int = 64, relay: str = "auto", workspace=None) -> Tuple:
+                  head_dim: int = 64, relay: str = "auto", n_spans: int = 0,
+                  workspace=None) -> Tuple:
     """Mamba-2 SSD scan (see include/mamba_scan.h): x (batch, seqlen, n_heads * head_dim),
     dt (batch, seqlen, n_heads), A/D/dt_bias (n_heads,) fp32, B/C (batch, seqlen, d_state),
-    h0 (batch, n_heads * head_dim, d_state) fp32.  Returns (y, h_last).  relay: "auto"
-    (load balancing when the device needs it), "off" (mamba_ssd_fwd itself) or "force";
-    the workspace it needs is allocated unless given."""
+    h0 (batch, n_heads * head_dim, d_state) fp32.  Returns (y, h_last).  relay ("auto",
+    "off", "force") and n_spans (0 automatic, 1 none, k spans) as mamba_ssd_opts_t; with
+    relay "off" and n_spans 1 this is mamba_ssd_fwd itself.  The workspace they need is
+    allocated unless given."""
     torch = _torch()
     lib = load_library()
     if x.dim() != 3 or dt.dim() != 3:
@@ -601,16 +616,15 @@ def mamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None,
     if h_last is None and return_last_state:
         h_last = torch.empty((batch, d_inner, d_state), dtype=f32, device=dev)
     p_hl = _ptr(h_last, "h_last_out", (batch, d_inner, d_state), f32, dev)
-    if relay not in _SSD_RELAY:
-        raise ValueError(f"relay must be one of {sorted(_SSD_RELAY)}")
-    if relay == "off" and workspace is None:
+    opts = _ssd_opts(relay, n_spans)
+    if relay == "off" and n_spans == 1 and workspace is None:
         st = lib.mamba_ssd_fwd(p_x, p_dt, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_y, p_hl,
                                batch, seqlen, n_heads, head_dim, d_state, code, _stream(dev))
         if st != 0:
             raise MambaError(st, "mamba_ssd_fwd")
         return y, h_last
     need = lib.mamba_ssd_workspace_size(batch, seqlen, n_heads, head_dim, d_state, code,
-                                        _SSD_RELAY[relay])
+                                        ctypes.byref(opts))
     if need == ctypes.c_size_t(-1).value:
         need = 0  # the call itself reports what is wrong
     ws = workspace
@@ -620,7 +634,7 @@ def mamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None,
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     st = lib.mamba_ssd_fwd_ex(p_x, p_dt, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_y, p_hl,
                               batch, seqlen, n_heads, head_dim, d_state, code, p_ws, ws_bytes,
-                              _SSD_RELAY[relay], _stream(dev))
+                              ctypes.byref(opts), _stream(dev))
     if st != 0:
         raise MambaError(st, "mamba_ssd_fwd_ex")
     return y, h_last

@@ -1,10 +1,12 @@
 // C ABI of libmambascan: argument validation, launch planning and dispatch.
 // Declarations and the contract live in include/mamba_scan.h.
 #include "mamba_scan.h"
+
 #include "scan_common.h"
 #include "scan_bwd.h"
 #include "ssd.h"
 
+#include <algorithm>
 #include <limits.h>
 #include <stdint.h>
 
@@ -1135,10 +1137,12 @@ int32_t mamba_ssd_supported(int64_t head_dim, int64_t d_state)
     return ssd_supported(head_dim, d_state) ? 1 : 0;
 }
 
-// SSD relay plan (mamba_ssd_fwd_ex): the units of a partial last round run in two parts,
-// the second from step `mid` (whole chunks before it).
-struct SsdRelay {
-    int64_t units = 0, mid = 0;
+// SSD launch plan (mamba_ssd_fwd_ex): a sequence split into spans when the units are too few
+// for the device, else the relay of a partial last round (the second parts from step
+// relay_mid, whole chunks before it).
+struct SsdPlan {
+    int64_t relay_units = 0, relay_mid = 0;
+    int64_t n_spans = 1, span_len = 0;
 };
 
 static mamba_status_t ssd_check_shape(int64_t batch, int64_t seqlen, int64_t n_heads,
@@ -1164,19 +1168,39 @@ static mamba_status_t ssd_check_shape(int64_t batch, int64_t seqlen, int64_t n_h
 }
 
 // (shapes already checked)
-static mamba_status_t ssd_relay_plan(int64_t batch, int64_t seqlen, int64_t n_heads,
-                                     int64_t d_state, mamba_dtype_t dtype, int32_t relay,
-                                     SsdRelay *r)
+static mamba_status_t ssd_make_plan(int64_t batch, int64_t seqlen, int64_t n_heads,
+                                    int64_t d_state, mamba_dtype_t dtype,
+                                    const mamba_ssd_opts_t *opts, SsdPlan *r)
 {
-    *r = SsdRelay{};
-    if (relay < 0 || relay > 2)
+    *r = SsdPlan{};
+    const int32_t relay = opts ? opts->relay : 0;
+    const int32_t spans = opts ? opts->n_spans : 0;
+    if (relay < 0 || relay > 2 || spans < 0 || spans > 64 || (relay == 2 && spans >= 2))
         return MAMBA_ERR_UNSUPPORTED;
     const int64_t units = batch * n_heads;
     const int64_t chunks = (seqlen + 63) / 64;
-    if (relay == 1 || units <= 0 || chunks < 2)
+    if (units <= 0 || chunks < 2)
         return MAMBA_OK;
     const int64_t slots =
         ssd_block_slots(d_state, dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32);
+
+    // Split: as many spans as fill one round of the slots, of at least 8 chunks each.
+    int64_t k = 1;
+    if (spans >= 2)
+        k = spans;
+    else if (spans == 0 && relay == 0 && slots > 0 && 2 * units <= slots)
+        k = std::min(slots / units, chunks / 8);
+    if (k >= 2) {
+        const int64_t per = (chunks + k - 1) / k; // chunks per span
+        k = (chunks + per - 1) / per;             // every span non-empty
+        if (k >= 2 && units * k <= INT32_MAX) {
+            r->n_spans = k;
+            r->span_len = per * 64;
+            return MAMBA_OK;
+        }
+    }
+    if (relay == 1)
+        return MAMBA_OK;
     int64_t rem = slots > 0 ? units % slots : 0;
     if (relay == 2) {
         if (rem == 0)
@@ -1186,33 +1210,49 @@ static mamba_status_t ssd_relay_plan(int64_t batch, int64_t seqlen, int64_t n_he
     }
     if (rem > INT32_MAX - units) // the grid holds units + rem blocks
         return MAMBA_OK;
-    r->units = rem;
-    r->mid = (chunks + 1) / 2 * 64;
+    r->relay_units = rem;
+    r->relay_mid = (chunks + 1) / 2 * 64;
     return MAMBA_OK;
 }
 
-// Workspace: [one flag per relayed unit, 256-byte aligned][head_dim x d_state fp32 each]
-static size_t ssd_sync_bytes(const SsdRelay &r)
+// Workspace: relay [one flag per relayed unit, 256-byte aligned][head_dim x d_state fp32
+// each]; split [(n_spans - 1) x units states of head_dim x d_state fp32][(n_spans - 1) x
+// units decays, fp32].
+static size_t ssd_sync_bytes(const SsdPlan &r)
 {
-    return r.units > 0 ? ((size_t)r.units * sizeof(uint32_t) + 255) / 256 * 256 : 0;
+    return r.relay_units > 0 ? ((size_t)r.relay_units * sizeof(uint32_t) + 255) / 256 * 256 : 0;
 }
 
-static size_t ssd_workspace_bytes(const SsdRelay &r, int64_t head_dim, int64_t d_state)
+static size_t ssd_span_state_bytes(const SsdPlan &r, int64_t units, int64_t head_dim,
+                                   int64_t d_state)
 {
-    if (r.units <= 0)
+    if (r.n_spans < 2)
         return 0;
-    return ssd_sync_bytes(r) + (size_t)r.units * (size_t)head_dim * (size_t)d_state * sizeof(float);
+    return (size_t)(r.n_spans - 1) * (size_t)units * (size_t)head_dim * (size_t)d_state *
+           sizeof(float);
+}
+
+static size_t ssd_workspace_bytes(const SsdPlan &r, int64_t units, int64_t head_dim,
+                                  int64_t d_state)
+{
+    if (r.n_spans >= 2)
+        return ssd_span_state_bytes(r, units, head_dim, d_state) +
+               (size_t)(r.n_spans - 1) * (size_t)units * sizeof(float);
+    if (r.relay_units <= 0)
+        return 0;
+    return ssd_sync_bytes(r) +
+           (size_t)r.relay_units * (size_t)head_dim * (size_t)d_state * sizeof(float);
 }
 
 size_t mamba_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t n_heads,
                                 int64_t head_dim, int64_t d_state, mamba_dtype_t dtype,
-                                int32_t relay)
+                                const mamba_ssd_opts_t *opts)
 {
-    SsdRelay r;
+    SsdPlan r;
     if (ssd_check_shape(batch, seqlen, n_heads, head_dim, d_state, dtype) != MAMBA_OK ||
-        ssd_relay_plan(batch, seqlen, n_heads, d_state, dtype, relay, &r) != MAMBA_OK)
+        ssd_make_plan(batch, seqlen, n_heads, d_state, dtype, opts, &r) != MAMBA_OK)
         return (size_t)-1;
-    return ssd_workspace_bytes(r, head_dim, d_state);
+    return ssd_workspace_bytes(r, batch * n_heads, head_dim, d_state);
 }
 
 mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const float *A, const void *B,
@@ -1220,16 +1260,16 @@ mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const float *A, c
                                 const float *dt_bias, const float *h0, void *y, float *h_last,
                                 int64_t batch, int64_t seqlen, int64_t n_heads,
                                 int64_t head_dim, int64_t d_state, mamba_dtype_t dtype,
-                                void *workspace, size_t workspace_bytes, int32_t relay,
-                                void *stream)
+                                void *workspace, size_t workspace_bytes,
+                                const mamba_ssd_opts_t *opts, void *stream)
 {
     const mamba_status_t shape_st =
         ssd_check_shape(batch, seqlen, n_heads, head_dim, d_state, dtype);
     if (shape_st != MAMBA_OK)
         return shape_st;
-    SsdRelay plan;
+    SsdPlan plan;
     const mamba_status_t plan_st =
-        ssd_relay_plan(batch, seqlen, n_heads, d_state, dtype, relay, &plan);
+        ssd_make_plan(batch, seqlen, n_heads, d_state, dtype, opts, &plan);
     if (plan_st != MAMBA_OK)
         return plan_st;
     if (batch == 0 || n_heads == 0)
@@ -1253,7 +1293,7 @@ mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const float *A, c
     for (const void *p : f32_ptrs)
         if (p && !aligned(p, 4))
             return MAMBA_ERR_MISALIGNED;
-    const size_t need = ssd_workspace_bytes(plan, head_dim, d_state);
+    const size_t need = ssd_workspace_bytes(plan, batch * n_heads, head_dim, d_state);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return MAMBA_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 4))
@@ -1297,10 +1337,16 @@ mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const float *A, c
     q.head_dim = head_dim;
     q.d_state = d_state;
     q.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
-    if (plan.units > 0) {
-        char *ws = static_cast<char *>(workspace);
-        q.relay_units = plan.units;
-        q.relay_mid = plan.mid;
+    char *ws = static_cast<char *>(workspace);
+    if (plan.n_spans >= 2) {
+        q.n_spans = plan.n_spans;
+        q.span_len = plan.span_len;
+        q.span_state = reinterpret_cast<float *>(ws);
+        q.span_decay = reinterpret_cast<float *>(
+            ws + ssd_span_state_bytes(plan, batch * n_heads, head_dim, d_state));
+    } else if (plan.relay_units > 0) {
+        q.relay_units = plan.relay_units;
+        q.relay_mid = plan.relay_mid;
         q.relay_sync = reinterpret_cast<uint32_t *>(ws);
         q.relay_state = reinterpret_cast<float *>(ws + ssd_sync_bytes(plan));
     }
@@ -1369,8 +1415,9 @@ mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const float *A, cons
                              int64_t batch, int64_t seqlen, int64_t n_heads, int64_t head_dim,
                              int64_t d_state, mamba_dtype_t dtype, void *stream)
 {
+    const mamba_ssd_opts_t plain = {1, 1}; // no relay, no split
     return mamba_ssd_fwd_ex(x, dt, A, B, C, D, z, dt_bias, h0, y, h_last, batch, seqlen,
-                            n_heads, head_dim, d_state, dtype, nullptr, 0, 1, stream);
+                            n_heads, head_dim, d_state, dtype, nullptr, 0, &plain, stream);
 }
 
 } // extern "C"

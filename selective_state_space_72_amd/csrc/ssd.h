@@ -21,6 +21,12 @@ struct SsdLaunch {
     int64_t relay_units, relay_mid;
     uint32_t *relay_sync;
     float *relay_state;
+    // Sequence split (no relay then): n_spans spans of span_len steps (a multiple of the
+    // chunk), the spans after the first starting from the state the carry gives them;
+    // span_state (n_spans - 1) x units x head_dim x d_state fp32, span_decay (n_spans - 1) x
+    // units fp32.  n_spans <= 1: no split.
+    int64_t n_spans, span_len;
+    float *span_state, *span_decay;
 };
 
 // One decode token of the SSD (ssd_step.hip).

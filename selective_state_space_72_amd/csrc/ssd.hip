@@ -189,10 +189,18 @@ struct SsdArgs {
     int64_t r_mid;
     uint32_t *r_sync;
     float *r_state;
+    // sequence split into n_spans spans of span_len steps (a multiple of the chunk); sp holds
+    // per span s < n_spans - 1 and unit its final state (END pass, from h0 for span 0 and
+    // from zero otherwise), turned by the carry into the state entering span s + 1; sp_dec
+    // the span's total decay
+    int32_t n_spans;
+    int64_t span_len;
+    float *sp, *sp_dec;
 };
 
-// bf16: two blocks per CU (75 KB of LDS each at N = 128), so registers are held to 256
-template <typename T, int N, bool GATED>
+// bf16: two blocks per CU (75 KB of LDS each at N = 128), so registers are held to 256.
+// END: the span pass of a split sequence, which only carries the state (no outputs).
+template <typename T, int N, bool GATED, bool END = false>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
 ssd_chunk_kernel(SsdArgs p)
@@ -237,10 +245,17 @@ ssd_chunk_kernel(SsdArgs p)
     // part 1 waits only for a block of smaller index.
     const int idx = (int)blockIdx.x;
     const int whole = p.units - p.r_units;
-    int bh = idx - p.r_units, part = -1;
+    int bh = idx - p.r_units, part = -1, span = 0;
     const int64_t L = p.L;
     int64_t t_begin = 0, t_end = L;
-    if (idx < p.r_units) {
+    if (p.n_spans > 1) { // split sequence: block = (span, unit), no relay
+        span = idx / p.units;
+        bh = idx % p.units;
+        if (p.units % 8 == 0)
+            bh = (bh % 8) * (p.units / 8) + bh / 8;
+        t_begin = (int64_t)span * p.span_len;
+        t_end = min(t_begin + p.span_len, L);
+    } else if (idx < p.r_units) {
         bh = whole + idx;
         part = 0;
         t_end = p.r_mid;
@@ -271,12 +286,21 @@ ssd_chunk_kernel(SsdArgs p)
     // ---- state slab: tile m holds rows n = 16m + 4g + v, column pc ----
     f32x4 hacc[NT];
     const int64_t hrow = ((int64_t)b * Dn + (int64_t)h * P + pc) * N;
-    if (p.h0 && part != 1) {
+    // (the span arrays share this layout: unit bh = b * H + h holds P rows of N at hrow)
+    const int64_t sp_stride = (int64_t)p.units * P * N;
+    if (p.h0 && part != 1 && span == 0) {
 #pragma unroll
         for (int m = 0; m < NT; ++m)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 hacc[m][v] = p.h0[hrow + 16 * m + 4 * g + v];
+    } else if (!END && span > 0) { // the state entering this span, from the carry
+        const float *src = p.sp + (int64_t)(span - 1) * sp_stride + hrow;
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                hacc[m][v] = src[16 * m + 4 * g + v];
     } else {
 #pragma unroll
         for (int m = 0; m < NT; ++m)
@@ -411,6 +435,7 @@ ssd_chunk_kernel(SsdArgs p)
             for (int v = 0; v < 4; ++v)
                 hacc[m][v] = p.r_state[((int64_t)slot * P + pc) * N + 16 * m + 4 * g + v];
     }
+    float decp = 1.0f; // END: the span's total decay, the product of its chunks'
     for (int64_t t0 = t_begin; t0 < t_end; t0 += Q) {
         const int nt = (int)min((int64_t)Q, t_end - t0);
         const uint32_t ybytes = (uint32_t)(nt - 1) * row_x + P * ES;
@@ -430,81 +455,87 @@ ssd_chunk_kernel(SsdArgs p)
         lds_barrier(); // this chunk is in LDS; the previous chunk's M is no longer read
 
         // ---- the causal tiles of S = C B^T given to this wave, weighted into M ----
+        if constexpr (!END) {
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const int k = w + 4 * q; // tiles in row order: (0,0) (1,0) (1,1) (2,0) ...
-            if (k < 10) {
-                const int r = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3, c = k - r * (r + 1) / 2;
-                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int q = 0; q < 3; ++q) {
+                const int k = w + 4 * q; // tiles in row order: (0,0) (1,0) (1,1) (2,0) ...
+                if (k < 10) {
+                    const int r = k < 1 ? 0 : k < 3 ? 1 : k < 6 ? 2 : 3, c = k - r * (r + 1) / 2;
+                    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int ks = 0; ks < N / KI; ++ks)
-                    acc = M::mma(frag<T>(s_c, LC::idx(16 * r + r16, KI * ks + KL * g)),
-                                 frag<T>(s_b, LB::idx(16 * c + r16, KI * ks + KL * g)), acc);
-                const int s = 16 * c + r16;
-                const float css = s_cs[s], csls = s_csl[s], dls = s_dl[s];
-                const f32x4 cst = *reinterpret_cast<const f32x4 *>(s_cs + 16 * r + 4 * g);
-                const f32x4 cstl = *reinterpret_cast<const f32x4 *>(s_csl + 16 * r + 4 * g);
+                    for (int ks = 0; ks < N / KI; ++ks)
+                        acc = M::mma(frag<T>(s_c, LC::idx(16 * r + r16, KI * ks + KL * g)),
+                                     frag<T>(s_b, LB::idx(16 * c + r16, KI * ks + KL * g)), acc);
+                    const int s = 16 * c + r16;
+                    const float css = s_cs[s], csls = s_csl[s], dls = s_dl[s];
+                    const f32x4 cst = *reinterpret_cast<const f32x4 *>(s_cs + 16 * r + 4 * g);
+                    const f32x4 cstl = *reinterpret_cast<const f32x4 *>(s_csl + 16 * r + 4 * g);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int t = 16 * r + 4 * g + v;
-                    float m = s <= t ? acc[v] * hw_exp2((cst[v] - css) + (cstl[v] - csls)) * dls
-                                     : 0.0f;
-                    if (s == t)
-                        m += Dh;
-                    const int i = LM::idx(t, s);
-                    if constexpr (M::SPLIT)
-                        split_bf16(m, s_m[i], s_m[LM::size(Q) + i]);
-                    else
-                        s_m[i] = m;
+                    for (int v = 0; v < 4; ++v) {
+                        const int t = 16 * r + 4 * g + v;
+                        float m = s <= t ? acc[v] * hw_exp2((cst[v] - css) + (cstl[v] - csls)) * dls
+                                         : 0.0f;
+                        if (s == t)
+                            m += Dh;
+                        const int i = LM::idx(t, s);
+                        if constexpr (M::SPLIT)
+                            split_bf16(m, s_m[i], s_m[LM::size(Q) + i]);
+                        else
+                            s_m[i] = m;
+                    }
                 }
             }
         }
 
         // ---- Y = diag(exp(cs)) C H_in on this wave's columns ----
         f32x4 yacc[4];
+        if constexpr (!END) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-            yacc[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int rt = 0; rt < 4; ++rt)
+                yacc[rt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int ks = 0; ks < N / KI; ++ks) {
-            if constexpr (KL == 8) {
-                // operand slot (g, e) <-> n = 32 ks + 16 (e / 4) + 4 g + e % 4
-                bf16x8 hh, hl;
+            for (int ks = 0; ks < N / KI; ++ks) {
+                if constexpr (KL == 8) {
+                    // operand slot (g, e) <-> n = 32 ks + 16 (e / 4) + 4 g + e % 4
+                    bf16x8 hh, hl;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    __bf16 a, c;
-                    split_bf16(hacc[2 * ks + e / 4][e % 4], a, c);
-                    hh[e] = a;
-                    hl[e] = c;
+                    for (int e = 0; e < 8; ++e) {
+                        __bf16 a, c;
+                        split_bf16(hacc[2 * ks + e / 4][e % 4], a, c);
+                        hh[e] = a;
+                        hl[e] = c;
+                    }
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        const int t = 16 * rt + r16;
+                        const bf16x4 c0 =
+                            *reinterpret_cast<const bf16x4 *>(s_c + LC::idx(t, 32 * ks + 4 * g));
+                        const bf16x4 c1 =
+                            *reinterpret_cast<const bf16x4 *>(s_c + LC::idx(t, 32 * ks + 16 + 4 * g));
+                        const bf16x8 cf = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        yacc[rt] = M::mma(cf, hh, yacc[rt]);
+                        yacc[rt] = M::mma(cf, hl, yacc[rt]);
+                    }
+                } else {
+                    // operand slot g <-> n = 16 (ks / 4) + 4 g + ks % 4
+                    const float hv = hacc[ks / 4][ks % 4];
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt)
+                        yacc[rt] = M::mma(s_c[LC::idx(16 * rt + r16, 16 * (ks / 4) + 4 * g + ks % 4)],
+                                          hv, yacc[rt]);
                 }
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    const int t = 16 * rt + r16;
-                    const bf16x4 c0 =
-                        *reinterpret_cast<const bf16x4 *>(s_c + LC::idx(t, 32 * ks + 4 * g));
-                    const bf16x4 c1 =
-                        *reinterpret_cast<const bf16x4 *>(s_c + LC::idx(t, 32 * ks + 16 + 4 * g));
-                    const bf16x8 cf = __builtin_shufflevector(c0, c1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    yacc[rt] = M::mma(cf, hh, yacc[rt]);
-                    yacc[rt] = M::mma(cf, hl, yacc[rt]);
-                }
-            } else {
-                // operand slot g <-> n = 16 (ks / 4) + 4 g + ks % 4
-                const float hv = hacc[ks / 4][ks % 4];
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    yacc[rt] = M::mma(s_c[LC::idx(16 * rt + r16, 16 * (ks / 4) + 4 * g + ks % 4)],
-                                      hv, yacc[rt]);
             }
-        }
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-            yacc[rt] *= *reinterpret_cast<const f32x4 *>(s_e + 16 * rt + 4 * g);
+            for (int rt = 0; rt < 4; ++rt)
+                yacc[rt] *= *reinterpret_cast<const f32x4 *>(s_e + 16 * rt + 4 * g);
+        }
 
         // ---- H_out = exp(cs_end) H_in + B^T Xtil on this wave's columns ----
         F xf[Q / KI]; // X^T operands of this lane's column, also used by M X below
         {
             const float dec = s_dec;
+            if constexpr (END)
+                decp *= dec;
 #pragma unroll
             for (int m = 0; m < NT; ++m)
                 hacc[m] *= dec;
@@ -548,31 +579,45 @@ ssd_chunk_kernel(SsdArgs p)
         }
 
         // ---- Y += M X (D included), gate, store ----
+        if constexpr (!END) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+            for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
-            for (int js = 0; js <= (16 * rt + 15) / KI; ++js) {
-                const int i = LM::idx(16 * rt + r16, KI * js + KL * g);
-                yacc[rt] = M::mma(frag<T>(s_m, i), xf[js], yacc[rt]);
-                if constexpr (M::SPLIT)
-                    yacc[rt] = M::mma(frag<T>(s_m + LM::size(Q), i), xf[js], yacc[rt]);
+                for (int js = 0; js <= (16 * rt + 15) / KI; ++js) {
+                    const int i = LM::idx(16 * rt + r16, KI * js + KL * g);
+                    yacc[rt] = M::mma(frag<T>(s_m, i), xf[js], yacc[rt]);
+                    if constexpr (M::SPLIT)
+                        yacc[rt] = M::mma(frag<T>(s_m + LM::size(Q), i), xf[js], yacc[rt]);
+                }
             }
-        }
-        const rsrc_t ry = make_rsrc(yb + t0 * row_x, ybytes);
+            const rsrc_t ry = make_rsrc(yb + t0 * row_x, ybytes);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            float yv = yacc[q >> 2][q & 3];
-            if constexpr (GATED)
-                yv *= silu_f(ES == 2 ? __uint_as_float(fz[q] << 16) : __uint_as_float(fz[q]));
-            const int off = (int)((16 * (q >> 2) + 4 * g + (q & 3)) * row_x + pc * ES);
-            if constexpr (ES == 2)
-                __builtin_amdgcn_raw_buffer_store_b16(
-                    __builtin_bit_cast(uint16_t, static_cast<__bf16>(yv)), ry, off, 0, 0);
-            else
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), ry, off, 0, 0);
+            for (int q = 0; q < 16; ++q) {
+                float yv = yacc[q >> 2][q & 3];
+                if constexpr (GATED)
+                    yv *= silu_f(ES == 2 ? __uint_as_float(fz[q] << 16) : __uint_as_float(fz[q]));
+                const int off = (int)((16 * (q >> 2) + 4 * g + (q & 3)) * row_x + pc * ES);
+                if constexpr (ES == 2)
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        __builtin_bit_cast(uint16_t, static_cast<__bf16>(yv)), ry, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), ry, off, 0, 0);
+            }
         }
     }
 
+    if constexpr (END) {
+        // the span's final state and total decay, for the carry
+        float *dst = p.sp + (int64_t)span * sp_stride + hrow;
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                dst[16 * m + 4 * g + v] = hacc[m][v];
+        if (tid == 0)
+            p.sp_dec[(int64_t)span * p.units + bh] = decp;
+        return;
+    }
     if (part == 0) {
         // hand the final state to part 1 (the part covers whole chunks: no tail rows)
 #pragma unroll
@@ -583,12 +628,29 @@ ssd_chunk_kernel(SsdArgs p)
         relay_signal(p.r_sync + slot);
         return;
     }
-    if (p.h_last) {
+    if (p.h_last && span == p.n_spans - 1) {
 #pragma unroll
         for (int m = 0; m < NT; ++m)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
                 p.h_last[hrow + 16 * m + 4 * g + v] = hacc[m][v];
+    }
+}
+
+// Carry over the spans of a split sequence, per unit and state element (in place): the END
+// pass left span s's final state from zero (span 0: from h0) and total decay; the state
+// entering span s + 1 is decay(s) * (state entering s) + (final state of s from zero).
+__global__ void ssd_span_carry_kernel(float *sp, const float *sp_dec, int64_t units,
+                                      int32_t n_spans, int32_t pn)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; // unit * pn + element
+    if (i >= units * pn)
+        return;
+    const int64_t u = i / pn, stride = units * pn;
+    float run = sp[i];
+    for (int s = 1; s < n_spans - 1; ++s) {
+        run = __builtin_fmaf(sp_dec[(int64_t)s * units + u], run, sp[s * stride + i]);
+        sp[s * stride + i] = run;
     }
 }
 
@@ -626,7 +688,24 @@ hipError_t launch_ssd_t(const SsdLaunch &q, hipStream_t stream)
     a.r_mid = q.relay_mid;
     a.r_sync = q.relay_sync;
     a.r_state = q.relay_state;
-    const int64_t blocks = units + q.relay_units;
+    a.n_spans = q.n_spans > 1 ? (int32_t)q.n_spans : 1;
+    a.span_len = q.span_len;
+    a.sp = q.span_state;
+    a.sp_dec = q.span_decay;
+    if (a.n_spans > 1) {
+        // the spans' final states from zero, the carry, then the outputs from the true states
+        hipLaunchKernelGGL((ssd_chunk_kernel<T, N, false, true>),
+                           dim3((uint32_t)(units * (a.n_spans - 1))), dim3(kThreads), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        const int64_t n = units * kP * N;
+        hipLaunchKernelGGL(ssd_span_carry_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0,
+                           stream, a.sp, a.sp_dec, units, a.n_spans, (int32_t)(kP * N));
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    const int64_t blocks = units * a.n_spans + q.relay_units;
     if (q.relay_units > 0) {
         const int32_t n = (int32_t)q.relay_units;
         hipLaunchKernelGGL(ssd_relay_clear_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256),

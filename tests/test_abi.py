@@ -435,14 +435,21 @@ def test_ssd_validation(lib):
     assert ssd(lib, L=0) == OK                              # no state asked for: nothing to do
 
 
-def ssd_ex(lib, *, ws=None, ws_bytes=0, relay=2, **kw):
+def ssd_ex(lib, *, ws=None, ws_bytes=0, relay=2, n_spans=0, **kw):
     a = dict(x=BASE, dt=BASE + 100 * MB, A=BASE + 200 * MB, B=BASE + 300 * MB,
              C=BASE + 400 * MB, D=BASE + 500 * MB, z=BASE + 600 * MB, bias=BASE + 700 * MB,
              h0=None, y=BASE + 800 * MB, hl=None, batch=2, L=200, H=4, P=64, N=128, dtype=BF16)
     a.update(kw)
+    o = ms.SsdOpts(relay, n_spans)
     return lib.mamba_ssd_fwd_ex(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["z"],
                                 a["bias"], a["h0"], a["y"], a["hl"], a["batch"], a["L"],
-                                a["H"], a["P"], a["N"], a["dtype"], ws, ws_bytes, relay, None)
+                                a["H"], a["P"], a["N"], a["dtype"], ws, ws_bytes,
+                                ctypes.byref(o), None)
+
+
+def ssd_size(lib, batch, L, H, P, N, dtype, relay=0, n_spans=0):
+    return lib.mamba_ssd_workspace_size(batch, L, H, P, N, dtype,
+                                        ctypes.byref(ms.SsdOpts(relay, n_spans)))
 
 
 def test_ssd_relay_workspace(lib):
@@ -450,29 +457,49 @@ def test_ssd_relay_workspace(lib):
     per relayed unit -- every unit when they fit the device; none for a single chunk or
     with the relay off; invalid options and shapes give (size_t)-1 and errors."""
     bad = ctypes.c_size_t(-1).value
-    size = lib.mamba_ssd_workspace_size
-    assert size(2, 200, 4, 64, 128, BF16, 2) == 256 + 8 * 64 * 128 * 4
-    assert size(3, 130, 100, 64, 64, F32, 2) == 1280 + 300 * 64 * 64 * 4   # 300 flags
-    assert size(2, 64, 4, 64, 128, BF16, 2) == 0          # one chunk: nothing to split
-    assert size(2, 200, 4, 64, 128, BF16, 1) == 0         # off
-    assert size(2, 0, 4, 64, 128, BF16, 2) == 0
+    size = lambda *a, relay=2: ssd_size(lib, *a, relay=relay, n_spans=1)  # noqa: E731
+    assert size(2, 200, 4, 64, 128, BF16) == 256 + 8 * 64 * 128 * 4
+    assert size(3, 130, 100, 64, 64, F32) == 1280 + 300 * 64 * 64 * 4   # 300 flags
+    assert size(2, 64, 4, 64, 128, BF16) == 0          # one chunk: nothing to split
+    assert size(2, 200, 4, 64, 128, BF16, relay=1) == 0  # off
+    assert size(2, 0, 4, 64, 128, BF16) == 0
     for relay in (-1, 3):
-        assert size(2, 200, 4, 64, 128, BF16, relay) == bad
-    assert size(2, 200, 4, 32, 128, BF16, 0) == bad       # head_dim not compiled in
-    assert size(-1, 200, 4, 64, 128, BF16, 0) == bad
-    assert size(2, 200, 4, 64, 128, 7, 0) == bad
-    need = size(2, 200, 4, 64, 128, BF16, 2)
+        assert size(2, 200, 4, 64, 128, BF16, relay=relay) == bad
+    assert size(2, 200, 4, 32, 128, BF16) == bad       # head_dim not compiled in
+    assert size(-1, 200, 4, 64, 128, BF16) == bad
+    assert size(2, 200, 4, 64, 128, 7) == bad
+    need = size(2, 200, 4, 64, 128, BF16)
     ws = BASE + 2048 * MB
     assert ssd_ex(lib, relay=3) == UNSUP and ssd_ex(lib, relay=-1) == UNSUP
-    assert ssd_ex(lib) == WS                                 # no workspace
-    assert ssd_ex(lib, ws=ws, ws_bytes=need - 4) == WS
-    assert ssd_ex(lib, ws=ws + 2, ws_bytes=need) == ALIGN
-    assert ssd_ex(lib, ws=BASE + 64, ws_bytes=need) == ALIAS              # over x
-    assert ssd_ex(lib, ws=BASE + 800 * MB, ws_bytes=need) == ALIAS        # over y
-    assert ssd_ex(lib, ws=ws, ws_bytes=need, hl=ws + 4096) == ALIAS       # over h_last
-    assert ssd_ex(lib, ws=ws, ws_bytes=need, P=32) == UNSUP
-    assert ssd_ex(lib, ws=ws, ws_bytes=need, x=None) == NULL
+    assert ssd_ex(lib, n_spans=1) == WS                      # no workspace
+    assert ssd_ex(lib, n_spans=1, ws=ws, ws_bytes=need - 4) == WS
+    assert ssd_ex(lib, n_spans=1, ws=ws + 2, ws_bytes=need) == ALIGN
+    assert ssd_ex(lib, n_spans=1, ws=BASE + 64, ws_bytes=need) == ALIAS          # over x
+    assert ssd_ex(lib, n_spans=1, ws=BASE + 800 * MB, ws_bytes=need) == ALIAS    # over y
+    assert ssd_ex(lib, n_spans=1, ws=ws, ws_bytes=need, hl=ws + 4096) == ALIAS   # h_last
+    assert ssd_ex(lib, n_spans=1, ws=ws, ws_bytes=need, P=32) == UNSUP
+    assert ssd_ex(lib, n_spans=1, ws=ws, ws_bytes=need, x=None) == NULL
     assert ssd_ex(lib, batch=0) == OK                        # nothing to do, no workspace
+
+
+def test_ssd_split_workspace(lib):
+    """Forced split: (n_spans - 1) states of head_dim x d_state fp32 and as many decays per
+    unit, the span count cut to the chunks there are; invalid options rejected."""
+    bad = ctypes.c_size_t(-1).value
+    units, pn = 2 * 4, 64 * 128
+    assert ssd_size(lib, 2, 1024, 4, 64, 128, BF16, relay=1, n_spans=4) == 3 * units * (pn + 1) * 4
+    # 200 steps are 4 chunks: 8 spans become 4
+    assert ssd_size(lib, 2, 200, 4, 64, 128, BF16, relay=1, n_spans=8) == 3 * units * (pn + 1) * 4
+    # 1000 steps, 5 spans: 16 chunks, 4 per span -> 4 spans
+    assert ssd_size(lib, 2, 1000, 4, 64, 128, BF16, relay=1, n_spans=5) == 3 * units * (pn + 1) * 4
+    assert ssd_size(lib, 2, 64, 4, 64, 128, BF16, relay=1, n_spans=4) == 0     # one chunk
+    assert ssd_size(lib, 2, 1024, 4, 64, 128, BF16, relay=0, n_spans=4) == 3 * units * (pn + 1) * 4
+    for relay, n in ((2, 2), (0, 65), (0, -1)):
+        assert ssd_size(lib, 2, 1024, 4, 64, 128, BF16, relay=relay, n_spans=n) == bad
+        assert ssd_ex(lib, relay=relay, n_spans=n) == UNSUP
+    need = ssd_size(lib, 2, 1024, 4, 64, 128, BF16, relay=1, n_spans=4)
+    assert ssd_ex(lib, L=1024, relay=1, n_spans=4) == WS
+    assert ssd_ex(lib, L=1024, relay=1, n_spans=4, ws=BASE + 2048 * MB, ws_bytes=need - 4) == WS
 
 
 def ssd_step(lib, **kw):

@@ -21,12 +21,12 @@ from ssd_reference import ssd_oracle
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(s, *, use_D=True, use_bias=True, use_h0=True, relay="auto"):
+def run_gpu(s, *, use_D=True, use_bias=True, use_h0=True, relay="auto", n_spans=0):
     y, h = ms.mamba_ssd_fwd(to_dev(s.x), to_dev(s.dt), to_dev(s.A), to_dev(s.B), to_dev(s.C),
                             D=to_dev(s.D) if use_D else None, z=to_dev(s.z),
                             dt_bias=to_dev(s.dt_bias) if use_bias else None,
                             h0=to_dev(s.h0) if use_h0 else None, return_last_state=True,
-                            head_dim=s.head_dim, relay=relay)
+                            head_dim=s.head_dim, relay=relay, n_spans=n_spans)
     torch.cuda.synchronize()
     return y, h
 
@@ -130,12 +130,12 @@ def test_ssd_relay_forced(dtype, d_state, seqlen, gate, h0):
     assert need == 256 + 6 * 64 * d_state * 4
     label = f"ssd relay forced, {dtype} N={d_state} L={seqlen}"
     log(f"case {label}")
-    y, h = run_gpu(s, relay="force")
+    y, h = run_gpu(s, relay="force", n_spans=1)
     (yr, hr), _ = run_oracle(s)
     ey, eh = metric(from_dev(y), yr), metric(from_dev(h), hr)
     log(f"{label}: y {ey:.2e}, h_last {eh:.2e}")
     assert ey <= TOL[dtype] and eh <= TOL[dtype]
-    y0, h0_ = run_gpu(s, relay="off")
+    y0, h0_ = run_gpu(s, relay="off", n_spans=1)
     assert torch.equal(y, y0) and torch.equal(h, h0_)
 
 
@@ -150,7 +150,7 @@ def test_ssd_relay_mixed_grid():
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
         assert need == 256 + 64 * 64 * 128 * 4
     y, h = run_gpu(s)
-    y0, h0_ = run_gpu(s, relay="off")
+    y0, h0_ = run_gpu(s, relay="off", n_spans=1)
     assert torch.equal(y, y0) and torch.equal(h, h0_)
     heads = [0, 35, 71]  # head 35 and 71 of batch row 7 are relayed units
     (yr, hr), ch = run_oracle(s, heads)
@@ -170,8 +170,45 @@ def test_ssd_large_relay_equals_unrelayed():
                                        c["d_state"], c["dtype"])
     log(f"ssd large: relay workspace {need} bytes")
     y, h = run_gpu(s)
-    y0, h0_ = run_gpu(s, relay="off")
+    y0, h0_ = run_gpu(s, relay="off", n_spans=1)
     assert torch.equal(y, y0) and torch.equal(h, h0_)
+
+
+@pytest.mark.parametrize("dtype,d_state,seqlen,n_spans,gate,h0", [
+    (synth.F32, 64, 200, 3, True, True),      # 4 chunks: spans of 2, 2
+    (synth.F32, 128, 1000, 5, False, True),   # 16 chunks, 4 per span, ragged last chunk
+    (synth.BF16, 128, 1000, 4, True, False),
+    (synth.BF16, 64, 130, 8, True, True),     # 3 chunks: 3 spans of one
+])
+def test_ssd_split_forced(dtype, d_state, seqlen, n_spans, gate, h0):
+    """The sequence split into spans (span passes from zero, the carry, the output pass
+    from each span's true state): against the oracle, and against the unsplit call within
+    the same bounds."""
+    s = synth.make_ssd_inputs(2, seqlen, 3, d_state=d_state, dtype=dtype, gate=gate, h0=h0)
+    label = f"ssd split {n_spans} spans, {dtype} N={d_state} L={seqlen}"
+    log(f"case {label}")
+    y, h = run_gpu(s, relay="off", n_spans=n_spans)
+    (yr, hr), _ = run_oracle(s)
+    ey, eh = metric(from_dev(y), yr), metric(from_dev(h), hr)
+    y0, h0_ = run_gpu(s, relay="off", n_spans=1)
+    e0 = max(metric(from_dev(y), from_dev(y0)), metric(from_dev(h), from_dev(h0_)))
+    log(f"{label}: y {ey:.2e}, h_last {eh:.2e}; against unsplit {e0:.2e}")
+    assert ey <= TOL[dtype] and eh <= TOL[dtype] and e0 <= TOL[dtype]
+
+
+def test_ssd_split_auto_few_units():
+    """One batch row of 4 heads over 2048 steps: 4 units on a device of 512 block slots
+    (MI355X) are split automatically (4 spans of 8 chunks); against the oracle."""
+    s = synth.make_ssd_inputs(1, 2048, 4, d_state=128, dtype=synth.BF16, gate=True, h0=True)
+    need = ms.mamba_ssd_workspace_size(1, 2048, 4, 64, 128, synth.BF16)
+    log(f"ssd 4 units x 2048 steps: workspace {need} bytes")
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert need == 3 * 4 * (64 * 128 + 1) * 4
+    y, h = run_gpu(s)
+    (yr, hr), _ = run_oracle(s)
+    ey, eh = metric(from_dev(y), yr), metric(from_dev(h), hr)
+    log(f"ssd 4 units auto split: y {ey:.2e}, h_last {eh:.2e}")
+    assert ey <= TOL[synth.BF16] and eh <= TOL[synth.BF16]
 
 
 def test_ssd_empty_sequence_returns_h0():
