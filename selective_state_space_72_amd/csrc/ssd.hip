@@ -19,7 +19,10 @@
 // One block per (batch row, head) walks the chunks in order; nothing of the chunk states
 // goes to HBM.  When the units overflow the device's block slots by a partial round, the
 // units of that round are relayed: each runs as two blocks, the second continuing from
-// the first's final state (relay.h), so the last round is not left mostly idle.
+// the first's final state (relay.h), so the last round is not left mostly idle.  When the
+// units are too few for the device, the sequence is split into spans instead: a span pass
+// (END) gives each span's final state from zero and its total decay, a carry kernel folds
+// them into the state entering each span, and the output pass runs the spans in parallel.
 //
 // Work split.  Wave w of the block's four owns the columns p in [16w, 16w + 16) of Y and of
 // H, and keeps its N x 16 slab of H in MFMA accumulators (16 x 16 tiles) from chunk to
