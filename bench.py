@@ -433,19 +433,23 @@ def extra_workloads(dev, flush, steps):
     torch.cuda.empty_cache()
     # Mamba-2 SSD scan (chunked, on the matrix cores) on its large shape, and its decode token
     out["ssd_large"] = ssd_workload(dev, flush, steps)
+    out["ssd_one_row"] = ssd_workload(dev, flush, steps, batch=1, seqlen=16384)
     out["ssd_decode"] = ssd_decode_workload(dev, flush, steps)
     return out
 
 
-def ssd_workload(dev, flush, steps):
+def ssd_workload(dev, flush, steps, batch=None, seqlen=None):
     """The SSD scan on the large shape: batch 8, L 4096, 80 heads of 64 channels, d_state
-    128, bf16 activations, gated, final state returned.  Bytes: x, z and y once each, dt, B
-    and C once, the final state; flops: the chunked form's products over their causal
-    part (C B^T and M X over s <= t, C H_in and B^T X in full), 64-step chunks."""
+    128, bf16 activations, gated, final state returned (or another batch and length of the
+    same heads).  Bytes: x, z and y once each, dt, B and C once, the final state; flops: the
+    chunked form's products over their causal part (C B^T and M X over s <= t, C H_in and
+    B^T X in full), 64-step chunks."""
     import torch
     import selective_state_space_72_amd as ms
     from selective_state_space_72_amd import synth
-    sc = synth.SSD_LARGE
+    sc = dict(synth.SSD_LARGE)
+    if batch is not None:
+        sc["batch"], sc["seqlen"] = batch, seqlen
     si = synth.make_ssd_inputs(sc["batch"], sc["seqlen"], sc["n_heads"], sc["head_dim"],
                                sc["d_state"], sc["dtype"], sc["gate"], sc["h0"], sc["seed"])
     sa = [to_dev(v, dev) for v in (si.x, si.dt, si.A, si.B, si.C)]
@@ -466,14 +470,14 @@ def ssd_workload(dev, flush, steps):
     flop = tok * H * ((Q + 1) * (N + P) + 4 * N * P)
     tf = flop / (ms_used * 1e-3) / 1e12
     gbs = nbytes / (ms_used * 1e-3) / 1e9
-    return {"workload": "Mamba-2 SSD scan: batch 8, L 4096, 80 heads x head_dim 64, d_state "
-                        "128, bf16 x/dt/B/C/z and y, fp32 A/D/dt_bias and state, gated, final "
-                        "state returned",
+    return {"workload": f"Mamba-2 SSD scan: batch {sc['batch']}, L {sc['seqlen']}, 80 heads x "
+                        "head_dim 64, d_state 128, bf16 x/dt/B/C/z and y, fp32 A/D/dt_bias and "
+                        "state, gated, final state returned",
             "ms": round(ms_used, 4), "ms_back_to_back": round(loop_ms, 4),
             "GB_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "TFLOP_s": round(tf, 1), "mfma_bf16_frac": round(tf / 2500.0, 4),
             "bytes_per_step": nbytes, "flop_per_step": flop,
-            "relayed_units": need // (sc["head_dim"] * sc["d_state"] * 4)}
+            "workspace_bytes": need}
 
 
 def ssd_decode_workload(dev, flush, steps):
