@@ -1188,7 +1188,7 @@ static mamba_status_t ssd_make_plan(int64_t batch, int64_t seqlen, int64_t n_hea
     int64_t k = 1;
     if (spans >= 2)
         k = spans;
-    else if (spans == 0 && relay == 0 && slots > 0 && 2 * units <= slots)
+    else if (spans == 0 && relay != 2 && slots > 0 && 2 * units <= slots)
         k = std::min(slots / units, chunks / 8);
     if (k >= 2) {
         const int64_t per = (chunks + k - 1) / k; // chunks per span
