@@ -703,6 +703,8 @@ hipError_t launch_ssd_t(const SsdLaunch &q, hipStream_t stream)
         if (e != hipSuccess)
             return e;
         const int64_t n = units * kP * N;
+        if ((n + 255) / 256 > (int64_t)UINT32_MAX)
+            return hipErrorInvalidValue;
         hipLaunchKernelGGL(ssd_span_carry_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0,
                            stream, a.sp, a.sp_dec, units, a.n_spans, (int32_t)(kP * N));
         if ((e = hipGetLastError()) != hipSuccess)
