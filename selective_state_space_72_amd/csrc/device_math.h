@@ -100,16 +100,19 @@ __device__ __forceinline__ void sincos_fast(float x, float &sn, float &cs) {
     cs = __int_as_float(__float_as_int(c1) ^ (((q + 1) & 2) << 30));
 }
 
-// Rotation of a state pair by the angle phi: (x, w) <- (cos phi x - sin phi w,
-// sin phi x + cos phi w), with sincos_fast (accurate to about 1.5 * 2^-24, not the hardware
-// v_sin/v_cos approximation).
-__device__ __forceinline__ void rotate_pair(float phi, float &x, float &w) {
-    float sn, cs;
-    sincos_fast(phi, sn, cs);
+// Rotation of a state pair: (x, w) <- (cos phi x - sin phi w, sin phi x + cos phi w), given
+// (sin phi, cos phi) (turn_pair) or the angle phi (rotate_pair, with sincos_fast: accurate to
+// about 1.5 * 2^-24, not the hardware v_sin/v_cos approximation).
+__device__ __forceinline__ void turn_pair(float sn, float cs, float &x, float &w) {
     const float nx = __builtin_fmaf(cs, x, -sn * w);
     const float nw = __builtin_fmaf(sn, x, cs * w);
     x = nx;
     w = nw;
+}
+__device__ __forceinline__ void rotate_pair(float phi, float &x, float &w) {
+    float sn, cs;
+    sincos_fast(phi, sn, cs);
+    turn_pair(sn, cs, x, w);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z); e^-z = +inf gives -0 as the limit.

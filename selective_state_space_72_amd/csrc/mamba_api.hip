@@ -155,17 +155,17 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     } else {
         return MAMBA_ERR_UNSUPPORTED;
     }
-    // the rotation turns state pairs (2k, 2k+1), which must sit in one wave; its span
-    // summaries would be 2x2 matrices, so the sequence is never split
+    // the rotation turns state pairs (2k, 2k+1), which must sit in one wave (its span
+    // summaries are the pairs' 2x2 transitions)
     if (p.rot && (d_state % 2 != 0 || (d_state / p.waves) % 2 != 0))
         return MAMBA_ERR_UNSUPPORTED;
     const bool fixed_spans = opts && opts->n_spans;
     int spans = 1;
     if (fixed_spans) {
-        if (opts->n_spans < 1 || opts->n_spans > 64 || (p.rot && opts->n_spans != 1))
+        if (opts->n_spans < 1 || opts->n_spans > 64)
             return MAMBA_ERR_UNSUPPORTED;
         spans = opts->n_spans;
-    } else if (!p.rot) {
+    } else {
         const int64_t tiles = batch * ((d_inner + 63) / 64);
         const int64_t waves_per_span = tiles * p.waves;
         const int64_t want = (int64_t)cus * 4 /*SIMDs*/ * 4 /*waves each*/;
@@ -190,7 +190,7 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
             len = p.chunk;
         if (p.family != Family::Scalar || scalar_span_ok(len, d_inner))
             break;
-        if (fixed_spans || spans >= 64 || p.rot)
+        if (fixed_spans || spans >= 64)
             return MAMBA_ERR_UNSUPPORTED; // span too large for the scalar kernel's addressing
         spans *= 2;
     }
@@ -273,8 +273,9 @@ size_t workspace_bytes_for(int64_t batch, int64_t seqlen, int64_t d_inner, int64
 {
     size_t n = staged_bytes_for(batch, seqlen, d_state, p);
     n += relay_sync_bytes(p) + relay_state_bytes(d_state, p);
-    if (p.n_spans > 1) // decay [c][S], hloc [c][S], h_in [S][c]
-        n += (size_t)3 * (size_t)p.n_spans * (size_t)(batch * d_inner * d_state) * sizeof(float);
+    if (p.n_spans > 1) // decay [c][S], hloc [c][S], h_in [S][c] (+ rotation: 2x2 [pair][S])
+        n += (size_t)(p.rot ? 5 : 3) * (size_t)p.n_spans * (size_t)(batch * d_inner * d_state) *
+             sizeof(float);
     return n;
 }
 
@@ -604,6 +605,7 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     float *ws_decay = ws;
     float *ws_hloc = ws + S * bdn;
     float *ws_hin = ws + 2 * S * bdn;
+    float *ws_rot = plan.rot ? ws + 3 * S * bdn : nullptr; // (pairs * S * 4 = 2 * S * bdn)
 
     ScanLaunch E = L;
     E.h_init = nullptr;
@@ -611,6 +613,7 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     E.ckpt = nullptr; // span summaries hold local states: no checkpoints
     E.ws_decay = ws_decay;
     E.ws_hloc = ws_hloc;
+    E.ws_rot = ws_rot;
     E.first_span = 0;
     E.launch_spans = (int32_t)(S - 1);
     hipError_t e = end(E);
@@ -620,6 +623,7 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     CarryLaunch K{};
     K.ws_decay = ws_decay;
     K.ws_hloc = ws_hloc;
+    K.ws_rot = ws_rot;
     K.h0 = h0;
     K.h_in = ws_hin;
     K.columns = bdn;

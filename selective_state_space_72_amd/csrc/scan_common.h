@@ -19,6 +19,8 @@ struct ScanLaunch {
     void *y;                    // FULL mode output
     float *h_last;              // FULL mode final state (nullable)
     float *ws_decay, *ws_hloc;  // END mode outputs, layout [(b*D + d)*N + n][span]
+    float *ws_rot;              // END mode with the rotation: each state pair's transition
+                                // over the span, 2x2 [(pair)][span][m00, m10, m01, m11]
     int64_t batch, L, d_inner, d_state;
     int64_t span_len;
     int32_t n_spans;
@@ -63,6 +65,7 @@ enum class Family : int { Auto = 0, Block = 1, Rows = 2, Scalar = 3 };
 // h_in[s][c] = state entering span s (s = 0 .. n_spans-1).
 struct CarryLaunch {
     const float *ws_decay, *ws_hloc; // [c][span], spans 0 .. n_spans-2 used
+    const float *ws_rot;             // non-null: the spans' 2x2 pair transitions replace decay
     const float *h0;                 // nullable
     float *h_in;                     // [span][c]
     int64_t columns;

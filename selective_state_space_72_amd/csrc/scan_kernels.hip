@@ -392,8 +392,43 @@ carry_kernel(const float *__restrict__ decay, const float *__restrict__ hloc,
         h_in[(int64_t)(s + 1) * columns + c] = __builtin_fmaf(a, x0, bb);
 }
 
+// Carry with the pair rotation: a span maps a state pair x to M x + b with M its 2x2
+// transition (rotations and unequal decays within a pair do not commute, so the scalar
+// decays do not compose); one thread per pair walks the spans in order.
+__global__ void __launch_bounds__(256)
+carry_rot_kernel(const float *__restrict__ rot, const float *__restrict__ hloc,
+                 const float *__restrict__ h0, float *__restrict__ h_in, int64_t columns,
+                 int32_t n_spans)
+{
+    const int64_t pr = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; // state pair
+    if (pr >= columns / 2)
+        return;
+    const int64_t c = 2 * pr;
+    float x0 = h0 ? h0[c] : 0.0f, x1 = h0 ? h0[c + 1] : 0.0f;
+    h_in[c] = x0;
+    h_in[c + 1] = x1;
+    for (int s = 0; s < n_spans - 1; ++s) {
+        const float *m = rot + (pr * n_spans + s) * 4; // m00, m10, m01, m11
+        const float y0 = __builtin_fmaf(m[0], x0, __builtin_fmaf(m[2], x1, hloc[c * n_spans + s]));
+        const float y1 =
+            __builtin_fmaf(m[1], x0, __builtin_fmaf(m[3], x1, hloc[(c + 1) * n_spans + s]));
+        x0 = y0;
+        x1 = y1;
+        h_in[(int64_t)(s + 1) * columns + c] = x0;
+        h_in[(int64_t)(s + 1) * columns + c + 1] = x1;
+    }
+}
+
 hipError_t launch_carry(const CarryLaunch &p, hipStream_t stream)
 {
+    if (p.ws_rot) {
+        const int64_t pairs = p.columns / 2;
+        if (pairs <= 0)
+            return hipSuccess;
+        hipLaunchKernelGGL(carry_rot_kernel, dim3((uint32_t)((pairs + 255) / 256)), dim3(256), 0,
+                           stream, p.ws_rot, p.ws_hloc, p.h0, p.h_in, p.columns, p.n_spans);
+        return hipGetLastError();
+    }
     const int nmaps = p.n_spans - 1;
     int seg = 1;
     while (seg < nmaps)

@@ -107,6 +107,7 @@ struct Mamba3Args {
     const void *lam, *u_prev, *B_prev, *Bm;
     float *ck;       // checkpoints for the backward pass (CK variants)
     int32_t ck_nseg; // 8-step segments of the whole sequence
+    float *rot_m;    // span pass with the rotation: each pair's 2x2 transition over the span
 };
 
 // DISC: 0 Euler, 1 zero-order hold, 2 exponential-trapezoidal; ROT: rotation of state pairs;
@@ -283,10 +284,24 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
         for (int tl = 0; tl < TC; ++tl)
 #pragma unroll
             for (int i = 0; i < BCW; ++i)
-                bcs[tl][i] = (FULL || i < NQ) ? q[tl * BCW + i] : 0.0f;
+                bcs[tl][i] = (FULL || i < NQ || (ROT && i >= 2 * NQ)) ? q[tl * BCW + i] : 0.0f;
     };
 
     float sum_dt = 0.0f;
+    // span pass with the rotation: the transition of each state pair over the span, a 2x2
+    // matrix (rotations and unequal decays within a pair do not commute), columns
+    // (m00, m10) and (m01, m11) of pair k at rm[4k ..]
+    constexpr bool RM = ROT && !FULL;
+    float rm[RM ? 2 * NQ : 1];
+    if constexpr (RM) {
+#pragma unroll
+        for (int k = 0; k < NQ / 2; ++k) {
+            rm[4 * k] = 1.0f;
+            rm[4 * k + 1] = 0.0f;
+            rm[4 * k + 2] = 0.0f;
+            rm[4 * k + 3] = 1.0f;
+        }
+    }
     // pending epilogue (the previous chunk): this lane's D*u, gate, first step, valid steps
     float e_du[KPL], e_gz[KPL];
     int e_t0 = -1;
@@ -370,8 +385,17 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
             if constexpr (ROT) {
                 // rotate each state pair by Delta * theta before the decay
 #pragma unroll
-                for (int k = 0; k < NQ / 2; ++k)
-                    rotate_pair(dw[tl].x * bcs[tl][2 * NQ + k], h[2 * k], h[2 * k + 1]);
+                for (int k = 0; k < NQ / 2; ++k) {
+                    if constexpr (RM) { // the same turn of the pair's transition columns
+                        float sn, cs;
+                        sincos_fast(dw[tl].x * bcs[tl][2 * NQ + k], sn, cs);
+                        turn_pair(sn, cs, h[2 * k], h[2 * k + 1]);
+                        turn_pair(sn, cs, rm[4 * k], rm[4 * k + 1]);
+                        turn_pair(sn, cs, rm[4 * k + 2], rm[4 * k + 3]);
+                    } else {
+                        rotate_pair(dw[tl].x * bcs[tl][2 * NQ + k], h[2 * k], h[2 * k + 1]);
+                    }
+                }
             }
             // trapezoid: (1 - lam) Delta u_{t-1}, from the previous step (or the carry)
             float p_lb = 0.0f;
@@ -380,6 +404,10 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 const float a = decay_exp2(dw[tl].x, a2[q]);
+                if constexpr (RM) { // row q % 2 of pair q / 2 decays with state q
+                    rm[4 * (q / 2) + (q & 1)] *= a;
+                    rm[4 * (q / 2) + 2 + (q & 1)] *= a;
+                }
                 float bu = dw[tl].y; // Bbar u / B: Euler Delta u (trapezoid: lam Delta u)
                 if constexpr (ZOH)
                     bu = zoh_input(dw[tl].x * an[q], a, dw[tl].y, dw[tl].z * ia[q]);
@@ -492,6 +520,13 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
             ws_decay[(col + q) * n_spans + span] = hw_exp2(a2[q] * sum_dt);
             ws_hloc[(col + q) * n_spans + span] = h[q];
         }
+        if constexpr (RM) {
+#pragma unroll
+            for (int k = 0; k < NQ / 2; ++k)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    m3.rot_m[((col / 2 + k) * n_spans + span) * 4 + j] = rm[4 * k + j];
+        }
     }
 }
 
@@ -523,7 +558,7 @@ hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
     }
     if (blocks <= 0)
         return hipSuccess;
-    Mamba3Args m3{p.lam, p.u_prev, p.B_prev, p.B, p.ckpt, (int32_t)((p.L + 7) / 8)};
+    Mamba3Args m3{p.lam, p.u_prev, p.B_prev, p.B, p.ckpt, (int32_t)((p.L + 7) / 8), p.ws_rot};
     hipLaunchKernelGGL((scan_scalar_kernel<T, N, NW, TC, PD, FULL, GATED, DISC, ROT, CK>),
                        dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, (const T *)p.u,
                        (const T *)p.delta, (const T *)p.z, p.bc_staged, p.A, p.D, p.bias,
@@ -557,8 +592,8 @@ hipError_t launch_stage(const ScanLaunch &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Rotation is compiled for the full-output pass of variants whose waves hold whole state
-// pairs (the span summaries of the split sequence have no rotation form).
+// Rotation is compiled for variants whose waves hold whole state pairs; its span pass also
+// gives each pair's 2x2 transition over the span (ws_rot) for the carry.
 template <typename T, int N, int NW, int TC, int PD, bool FULL, int DISC>
 hipError_t launch_scalar_disc(const ScanLaunch &p, hipStream_t stream)
 {
@@ -572,11 +607,15 @@ hipError_t launch_scalar_disc(const ScanLaunch &p, hipStream_t stream)
             return hipErrorInvalidValue;
     }
     if (p.rot) {
-        if constexpr (FULL && (N / NW) % 2 == 0)
+        // the span pass needs the pairs' transitions (ws_rot) for the carry
+        if constexpr ((N / NW) % 2 == 0) {
+            if (!FULL && !p.ws_rot)
+                return hipErrorInvalidValue;
             return g ? launch_scalar_variant<T, N, NW, TC, PD, FULL, true, DISC, true>(p, stream)
                      : launch_scalar_variant<T, N, NW, TC, PD, FULL, false, DISC, true>(p, stream);
-        else
+        } else {
             return hipErrorInvalidValue;
+        }
     }
     return g ? launch_scalar_variant<T, N, NW, TC, PD, FULL, true, DISC, false>(p, stream)
              : launch_scalar_variant<T, N, NW, TC, PD, FULL, false, DISC, false>(p, stream);

@@ -362,9 +362,8 @@ def scan_ext(lib, *, lam=None, u_prev=None, B_prev=None, theta=None, N=16, L=64,
 
 def test_ext_validation(lib):
     LAM, TH = BASE + 400 * MB, BASE + 500 * MB
-    # rotation needs state pairs within a wave and an unsplit sequence
+    # rotation needs state pairs within a wave and the scalar-B/C kernel
     assert scan_ext(lib, theta=TH, N=8) == UNSUP
-    assert scan_ext(lib, theta=TH, opts=ms.ScanOpts(0, 0, 2, 0, 0, 0)) == UNSUP
     assert scan_ext(lib, theta=TH, opts=ms.ScanOpts(0, 0, 0, ms.MAMBA_KERNEL_ROWS, 0, 0)) == UNSUP
     # the trapezoid replaces the input term: not with the zero-order hold
     assert scan_ext(lib, lam=LAM, opts=ms.ScanOpts(0, 0, 0, 0, 0, ms.MAMBA_DISC_ZOH)) == UNSUP
@@ -386,6 +385,14 @@ def test_ext_workspace(lib):
     bad = ctypes.c_size_t(-1).value
     assert lib.mamba_scan_fwd_workspace_size_ext(
         8, 4096, 5120, 8, ctypes.byref(ms.ScanExt(None, None, None, 1)), None) == bad
+    # a split sequence with the rotation: theta staged (d_state / 2 more floats per staged
+    # row), and the span passes' 2x2 pair transitions (2 more floats per state and span)
+    o = ms.ScanOpts(0, 0, 2, 3, 0, 0)   # scalar-B/C kernel, 2 spans
+    th = ms.ScanExt(None, None, None, 1)
+    split_plain = lib.mamba_scan_fwd_workspace_size_ext(1, 4096, 128, 16, None, ctypes.byref(o))
+    split_rot = lib.mamba_scan_fwd_workspace_size_ext(1, 4096, 128, 16, ctypes.byref(th),
+                                                      ctypes.byref(o))
+    assert split_rot - split_plain == (4096 + 8) * 8 * 4 + 2 * 2 * (128 * 16) * 4
 
 
 def test_decode_ext_validation(lib):

@@ -4,7 +4,7 @@ rotation of state pairs (theta), in the scan and in the decode step.
 
 Shapes span several chunks and 64-channel tiles with ragged tails; the trapezoid is also
 run with the sequence split into spans and with the relay (its look-back crosses those
-boundaries), the rotation with the relay.  Tolerances as for the scan: metric M of
+boundaries), the rotation with the relay and split into spans (2x2 span transitions).  Tolerances as for the scan: metric M of
 gpu_helpers, 1e-5 for fp32 inputs, 2e-2 for bf16 inputs.
 """
 from __future__ import annotations
@@ -110,6 +110,28 @@ def test_rotation_relay_bf16():
     check(inp, m3, "rotation bf16, relay in 2 parts", trap=False, rot=True, relay=2)
 
 
+@pytest.mark.parametrize("n_spans", [2, 3, 5])
+def test_rotation_spans_fp32(n_spans):
+    """The sequence split with the rotation: each span pass also gives every state pair's
+    2x2 transition over the span (the decays of a pair differ here, A = -(n + 1), so the
+    turns and decays do not commute), and the carry composes them."""
+    inp, m3 = make_case("c1", batch=2, seqlen=203, d_inner=96, gate=True, h0=True)
+    check(inp, m3, f"rotation fp32, {n_spans} spans", trap=False, rot=True, n_spans=n_spans)
+
+
+def test_rotation_spans_with_trapezoid_and_zoh_bf16():
+    inp, m3 = make_case("c3", batch=1, seqlen=300, d_inner=130, h0=True)
+    check(inp, m3, "rotation + trapezoid bf16, 4 spans", trap=True, rot=True, n_spans=4)
+    check(inp, m3, "rotation + zero-order hold bf16, 3 spans", trap=False, rot=True,
+          n_spans=3, discretization="zoh")
+
+
+def test_rotation_long_sequence_auto_split():
+    """Few channels over a long sequence: the planner splits it with the rotation too."""
+    inp, m3 = make_case("c4", batch=1, seqlen=8192, d_inner=128, h0=True)
+    check(inp, m3, "rotation bf16, 1 x 8192 x 128, automatic split", trap=False, rot=True)
+
+
 def test_rotation_with_trapezoid_and_zoh():
     inp, m3 = make_case("c1", batch=2, seqlen=90, d_inner=64, gate=True, h0=True)
     check(inp, m3, "rotation + trapezoid fp32", trap=True, rot=True)
@@ -122,8 +144,6 @@ def test_unsupported_combinations():
     with pytest.raises(ms.MambaError, match="UNSUPPORTED"):
         run_gpu(inp, m3, trap=False, rot=True)               # pairs split across waves
     inp, m3 = make_case("c1", batch=1, seqlen=64, d_inner=64, h0=True)
-    with pytest.raises(ms.MambaError, match="UNSUPPORTED"):
-        run_gpu(inp, m3, trap=False, rot=True, n_spans=2)    # no split with rotation
     with pytest.raises(ms.MambaError, match="UNSUPPORTED"):
         run_gpu(inp, m3, trap=True, rot=False, discretization="zoh")
     with pytest.raises(ms.MambaError, match="UNSUPPORTED"):
