@@ -323,7 +323,8 @@ def extra_workloads(dev, flush, steps):
     from selective_state_space_72_amd import synth
     out = {}
     variants = (("c2", {}), ("c4", {}), ("c3_zoh", dict(discretization="zoh")),
-                ("c3_trapezoid", dict(trapezoid=True)), ("c3_rotation", dict(rotation=True)))
+                ("c3_trapezoid", dict(trapezoid=True)), ("c3_rotation", dict(rotation=True)),
+                ("c4_rotation", dict(rotation=True)))
     labels = {"discretization": ", zero-order-hold discretisation",
               "trapezoid": ", exponential-trapezoidal rule (lam, u_prev, B_prev)",
               "rotation": ", data-dependent rotation of state pairs (theta)"}
