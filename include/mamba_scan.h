@@ -406,7 +406,9 @@ MAMBA_API mamba_status_t mamba_scan_bwd_ckpt(const void *u, const void *delta, c
  *       term), where R turns each state pair (2k, 2k+1) by the angle
  *       Delta_t * theta[b,t,k]: (x, w) -> (cos x - sin w, sin x + cos w), before the decay.
  *       d_state must be even; in the scan it needs d_state 16 or 32 (state pairs within
- *       one wave) and an unsplit sequence (n_spans 1), else MAMBA_ERR_UNSUPPORTED.
+ *       one wave), else MAMBA_ERR_UNSUPPORTED.  A split sequence (n_spans > 1) carries
+ *       each pair's 2x2 transition over a span (the turn and the pair's two decays do not
+ *       commute): more workspace (mamba_scan_fwd_workspace_size_ext) and span passes.
  *
  * Both options run in the SCALAR family (AUTO selects it; ROWS or BLOCK return
  * MAMBA_ERR_UNSUPPORTED).  The extension inputs follow the alignment and aliasing rules
