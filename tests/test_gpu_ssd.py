@@ -196,6 +196,21 @@ def test_ssd_split_forced(dtype, d_state, seqlen, n_spans, gate, h0):
     assert ey <= TOL[dtype] and eh <= TOL[dtype] and e0 <= TOL[dtype]
 
 
+def test_ssd_split_one_step_last_span():
+    """257 steps in 5 spans of one chunk: the last span holds a single step; no h0, no gate;
+    and the same call without the final state (h_last not written)."""
+    s = synth.make_ssd_inputs(2, 257, 3, d_state=64, dtype=synth.F32, gate=False, h0=False)
+    y, h = run_gpu(s, relay="off", n_spans=5)
+    (yr, hr), _ = run_oracle(s)
+    ey, eh = metric(from_dev(y), yr), metric(from_dev(h), hr)
+    log(f"ssd split, one-step last span: y {ey:.2e}, h_last {eh:.2e}")
+    assert ey <= TOL[synth.F32] and eh <= TOL[synth.F32]
+    y2, h2 = ms.mamba_ssd_fwd(to_dev(s.x), to_dev(s.dt), to_dev(s.A), to_dev(s.B), to_dev(s.C),
+                              D=to_dev(s.D), dt_bias=to_dev(s.dt_bias), relay="off", n_spans=5)
+    torch.cuda.synchronize()
+    assert h2 is None and torch.equal(y2, y)
+
+
 def test_ssd_split_auto_few_units():
     """One batch row of 4 heads over 2048 steps: 4 units on a device of 512 block slots
     (MI355X) are split automatically (4 spans of 8 chunks); against the oracle."""
