@@ -342,7 +342,8 @@ ssd_chunk_kernel(SsdArgs p)
             for (int i = 0; i < 2; ++i) {
                 const int off = (int)((2 * rp + i) * row_b + cg * 16);
                 fb[k][i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-                fc[k][i] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+                if constexpr (!END) // (the span pass reads no C)
+                    fc[k][i] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
             }
         }
         if (w == 3) {
@@ -374,7 +375,8 @@ ssd_chunk_kernel(SsdArgs p)
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 *reinterpret_cast<u32x4 *>(s_b + LB::idx(2 * rp + i, cg * G)) = fb[k][i];
-                *reinterpret_cast<u32x4 *>(s_c + LC::idx(2 * rp + i, cg * G)) = fc[k][i];
+                if constexpr (!END)
+                    *reinterpret_cast<u32x4 *>(s_c + LC::idx(2 * rp + i, cg * G)) = fc[k][i];
             }
 #pragma unroll
             for (int j = 0; j < G; ++j) {
