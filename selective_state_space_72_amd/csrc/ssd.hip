@@ -248,7 +248,7 @@ ssd_chunk_kernel(SsdArgs p)
     // part 1 waits only for a block of smaller index.
     const int idx = (int)blockIdx.x;
     const int whole = p.units - p.r_units;
-    int bh = idx - p.r_units, part = -1, span = 0;
+    int bh = idx - p.r_units, part = -1, span = 0, slot = 0;
     const int64_t L = p.L;
     int64_t t_begin = 0, t_end = L;
     if (p.n_spans > 1) { // split sequence: block = (span, unit), no relay
@@ -258,18 +258,28 @@ ssd_chunk_kernel(SsdArgs p)
             bh = (bh % 8) * (p.units / 8) + bh / 8;
         t_begin = (int64_t)span * p.span_len;
         t_end = min(t_begin + p.span_len, L);
-    } else if (idx < p.r_units) {
-        bh = whole + idx;
-        part = 0;
-        t_end = p.r_mid;
-    } else if (idx >= p.units) {
-        bh = whole + (idx - p.units);
-        part = 1;
-        t_begin = p.r_mid;
-    } else if (whole % 8 == 0 && p.r_units % 8 == 0) {
-        bh = (bh % 8) * (whole / 8) + bh / 8;
+    } else {
+        // j: index within the block's group (part 0, whole, part 1); a relayed unit's slot
+        int j = idx - p.r_units;
+        if (idx < p.r_units) {
+            j = idx;
+            part = 0;
+            t_end = p.r_mid;
+        } else if (idx >= p.units) {
+            j = idx - p.units;
+            part = 1;
+            t_begin = p.r_mid;
+        }
+        const bool relayed = part >= 0;
+        if (p.units % 8 == 0 && p.r_units % 8 == 0) {
+            // every group starts on XCD 0: XCD x takes units [x, x + 1) * units / 8, its
+            // whole units first, then its relayed ones
+            bh = (j % 8) * (p.units / 8) + (relayed ? whole / 8 : 0) + j / 8;
+        } else {
+            bh = relayed ? whole + j : j;
+        }
+        slot = j;
     }
-    const int slot = bh - whole; // relay slot of a relayed unit
     const int b = bh / p.H, h = bh % p.H;
     const int64_t Dn = (int64_t)p.H * P;
     const int pc = 16 * w + r16; // this lane's column of Y and of H
