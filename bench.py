@@ -534,8 +534,7 @@ def main():
         sys.exit(2)
     import torch
     from selective_state_space_72_amd import build as hip_build
-    if not hip_build.is_built():
-        hip_build.build()
+    hip_build.ensure_built()
     import selective_state_space_72_amd as ms
     from selective_state_space_72_amd import synth
     ms.load_library()

@@ -19,3 +19,10 @@ def pytest_configure(config):
 def orc():
     import oracle
     return oracle.load()
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _hip_library_current():
+    """Rebuild libmambascan.so before any test if its sources changed since it was built."""
+    from selective_state_space_72_amd import build as hip_build
+    hip_build.ensure_built(verbose=False)

@@ -23,8 +23,7 @@ MB = 1 << 20
 
 @pytest.fixture(scope="module")
 def lib():
-    if not hip_build.is_built():
-        hip_build.build()
+    hip_build.ensure_built()
     return ms.load_library()
 
 

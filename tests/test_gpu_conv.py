@@ -21,8 +21,7 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from selective_state_space_72_amd import build as hip_build
-    if not hip_build.is_built():
-        hip_build.build()
+    hip_build.ensure_built()
     ms.load_library()
 
 
