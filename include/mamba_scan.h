@@ -110,7 +110,13 @@ typedef enum {
  *               handing its final state to the next (no recomputation).
  *               0 = auto (two parts, when it evens out the load), 1 = off,
  *               2..8 = that many equal parts (when no units are left over, every
- *               unit is split; for testing).
+ *               unit is split; for testing), -8..-2 = the same, with the first part
+ *               of every relayed unit withholding its hand-off (failure test: the
+ *               next part's bounded wait gives up; see mamba_scan_fwd_relay_faults).
+ *               A wait for a hand-off is bounded (about 2^20 polls of ~8k cycles,
+ *               2^10 in the failure test); one that gives up is counted in the
+ *               workspace and the part continues from a NaN state, so its outputs
+ *               and the unit's final state are NaN, never silently wrong.
  *   discretization : MAMBA_DISC_EULER (0, default) or MAMBA_DISC_ZOH; the zero-
  *               order hold needs the SCALAR family (AUTO selects it).
  * Every supported setting of the other fields gives the same result up to
@@ -448,6 +454,23 @@ MAMBA_API mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, co
                                             const mamba_scan_opts_t *opts,
                                             const mamba_scan_ext_t *ext, void *stream);
 
+/*
+ * Relay hand-offs that timed out in the last mamba_scan_fwd_ex / _ext call that used
+ * `workspace` with the same sizes, opts and ext (mamba_scan_opts_t.relay): *faults = the
+ * number of relay parts whose wait for the previous part's state gave up (their outputs are
+ * NaN).  0 whenever that call planned no relay.  Synchronises `stream` (the call must have
+ * been enqueued on it) and copies one word to the host.  Errors: MAMBA_ERR_NULL_ARG (faults
+ * NULL), the size and option errors of mamba_scan_fwd_ext, MAMBA_ERR_WORKSPACE (workspace
+ * smaller than that call's), MAMBA_ERR_HIP (the copy or the synchronisation failed).
+ */
+MAMBA_API mamba_status_t mamba_scan_fwd_relay_faults(const void *workspace,
+                                                     size_t workspace_bytes, int64_t batch,
+                                                     int64_t seqlen, int64_t d_inner,
+                                                     int64_t d_state,
+                                                     const mamba_scan_opts_t *opts,
+                                                     const mamba_scan_ext_t *ext,
+                                                     uint32_t *faults, void *stream);
+
 /* mamba_state_update_ex with the Mamba-3 options (shapes of the decode step; ext NULL =
  * none).  With lambda the caller passes the previous token's u and B as u_prev, B_prev.
  * ext->ckpt must be NULL (MAMBA_ERR_UNSUPPORTED otherwise). */
@@ -515,7 +538,11 @@ MAMBA_API mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const floa
  * Options (NULL = automatic):
  *   relay:   0 automatic (the overflow is at most half of the slots and the sequence has at
  *            least 8 chunks); 1 off; 2 force two parts on the overflow units, or on every
- *            unit when they fit the slots (testing; sequences of at least 2 chunks).
+ *            unit when they fit the slots (testing; sequences of at least 2 chunks); -2 as 2,
+ *            with the first parts withholding their hand-off (failure test).  A second part's
+ *            wait is bounded; one that gives up is counted in the workspace (read with
+ *            mamba_ssd_relay_faults) and the part continues from a NaN state, so its outputs
+ *            and the unit's final state are NaN, never silently wrong.
  *   n_spans: 0 automatic (as many spans as fill one round, each of at least 8 chunks); 1 no
  *            split; k in [2, 64] force k spans (fewer when the sequence has fewer chunks).
  *   A split takes precedence over the relay; forcing both is MAMBA_ERR_UNSUPPORTED, as are
@@ -523,7 +550,8 @@ MAMBA_API mamba_status_t mamba_ssd_fwd(const void *x, const void *dt, const floa
  * Workspace (caller-owned device memory, 4-byte aligned, not overlapping any argument),
  * size from mamba_ssd_workspace_size for the same arguments on the same device (0: none
  * needed, NULL allowed; (size_t)-1 for arguments mamba_ssd_fwd_ex would reject): relay, one
- * flag and one head_dim x d_state fp32 state per relayed unit; split, (n_spans - 1) states
+ * flag per relayed unit and a fault word (256-byte aligned block) and one head_dim x d_state
+ * fp32 state per relayed unit; split, (n_spans - 1) states
  * and decays per unit.  MAMBA_ERR_WORKSPACE when missing or too small.  Its contents on
  * entry do not matter and are overwritten.  Concurrent calls must not share a workspace.
  */
@@ -544,6 +572,17 @@ MAMBA_API mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const f
                                           int64_t d_state, mamba_dtype_t dtype,
                                           void *workspace, size_t workspace_bytes,
                                           const mamba_ssd_opts_t *opts, void *stream);
+
+/* Relay hand-offs that timed out in the last mamba_ssd_fwd_ex call that used `workspace`
+ * with the same arguments and opts: *faults as for mamba_scan_fwd_relay_faults (0 when that
+ * call planned no relay).  Synchronises `stream`.  Errors as mamba_ssd_fwd_ex's size and
+ * option checks, MAMBA_ERR_NULL_ARG, MAMBA_ERR_WORKSPACE, MAMBA_ERR_HIP. */
+MAMBA_API mamba_status_t mamba_ssd_relay_faults(const void *workspace, size_t workspace_bytes,
+                                                int64_t batch, int64_t seqlen, int64_t n_heads,
+                                                int64_t head_dim, int64_t d_state,
+                                                mamba_dtype_t dtype,
+                                                const mamba_ssd_opts_t *opts, uint32_t *faults,
+                                                void *stream);
 
 /*
  * One decode token of the Mamba-2 SSD on a persistent fp32 state: the recurrence of

@@ -42,6 +42,7 @@ EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_ssd_supported", "mamba_ssd_fwd", "mamba_ssd_workspace_size", "mamba_ssd_fwd_ex",
            "mamba_ssd_state_update",
            "mamba_scan_ckpt_size", "mamba_scan_bwd_ckpt_workspace_size", "mamba_scan_bwd_ckpt",
+           "mamba_scan_fwd_relay_faults", "mamba_ssd_relay_faults",
            "mamba_status_string")
 
 
@@ -158,6 +159,14 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mamba_scan_bwd_ckpt.argtypes = ([_vp] * 21 + [_i64] * 4 + [ctypes.c_int, _vp,
                                                                      ctypes.c_size_t,
                                                                      ctypes.POINTER(ScanOpts), _vp])
+    lib.mamba_scan_fwd_relay_faults.restype = ctypes.c_int
+    lib.mamba_scan_fwd_relay_faults.argtypes = ([_vp, ctypes.c_size_t] + [_i64] * 4 +
+                                                [ctypes.POINTER(ScanOpts), ctypes.POINTER(ScanExt),
+                                                 ctypes.POINTER(ctypes.c_uint32), _vp])
+    lib.mamba_ssd_relay_faults.restype = ctypes.c_int
+    lib.mamba_ssd_relay_faults.argtypes = ([_vp, ctypes.c_size_t] + [_i64] * 5 +
+                                           [ctypes.c_int, ctypes.POINTER(SsdOpts),
+                                            ctypes.POINTER(ctypes.c_uint32), _vp])
     lib.mamba_status_string.restype = ctypes.c_char_p
     lib.mamba_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -322,6 +331,35 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
     if st != 0:
         raise MambaError(st, "mamba_scan_fwd")
     return y, h_last
+
+
+def _ws_arg(workspace):
+    if workspace is None:
+        return None, 0
+    return (workspace.data_ptr() if workspace.numel() > 0 else None,
+            workspace.numel() * workspace.element_size())
+
+
+def mamba_scan_fwd_relay_faults(workspace, batch: int, seqlen: int, d_inner: int, d_state: int,
+                                *, chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
+                                kernel: str = "auto", relay: int = 0,
+                                discretization: str = "euler", trapezoid: bool = False,
+                                rotation: bool = False, device=None) -> int:
+    """Relay hand-offs that timed out in the last mamba_scan_fwd call given this workspace
+    with the same sizes and options (0 when it planned no relay).  Synchronises the current
+    stream."""
+    lib = load_library()
+    o = _opts(chunk_len, waves, n_spans, kernel, relay, discretization)
+    e = ScanExt(1 if trapezoid else None, None, None, 1 if rotation else None)
+    p_ws, ws_bytes = _ws_arg(workspace)
+    dev = workspace.device if workspace is not None else device
+    out = ctypes.c_uint32(0)
+    st = lib.mamba_scan_fwd_relay_faults(p_ws, ws_bytes, batch, seqlen, d_inner, d_state,
+                                         ctypes.byref(o), ctypes.byref(e), ctypes.byref(out),
+                                         _stream(dev) if dev is not None else None)
+    if st != 0:
+        raise MambaError(st, "mamba_scan_fwd_relay_faults")
+    return int(out.value)
 
 
 def mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None,
@@ -557,7 +595,7 @@ def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=No
     return {k: v for k, v in res.items() if k in ("du", "ddelta") or k in want}
 
 
-_SSD_RELAY = {"auto": 0, "off": 1, "force": 2}
+_SSD_RELAY = {"auto": 0, "off": 1, "force": 2, "force_withheld": -2}
 
 
 def _ssd_opts(relay: str, n_spans: int):
@@ -638,6 +676,24 @@ def mamba_ssd_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, h0=None,
     if st != 0:
         raise MambaError(st, "mamba_ssd_fwd_ex")
     return y, h_last
+
+
+def mamba_ssd_relay_faults(workspace, batch: int, seqlen: int, n_heads: int, head_dim: int,
+                           d_state: int, dtype, relay: str = "auto", n_spans: int = 0,
+                           device=None) -> int:
+    """Relay hand-offs that timed out in the last mamba_ssd_fwd call given this workspace with
+    the same arguments (0 when it planned no relay).  Synchronises the current stream."""
+    lib = load_library()
+    o = _ssd_opts(relay, n_spans)
+    p_ws, ws_bytes = _ws_arg(workspace)
+    dev = workspace.device if workspace is not None else device
+    out = ctypes.c_uint32(0)
+    st = lib.mamba_ssd_relay_faults(p_ws, ws_bytes, batch, seqlen, n_heads, head_dim, d_state,
+                                    _dtype_code_of(dtype), ctypes.byref(o), ctypes.byref(out),
+                                    _stream(dev) if dev is not None else None)
+    if st != 0:
+        raise MambaError(st, "mamba_ssd_relay_faults")
+    return int(out.value)
 
 
 def mamba_ssd_state_update(h, x, dt, A, B, C, D=None, z=None, dt_bias=None, *, out=None,

@@ -2,6 +2,7 @@
 // Declarations and the contract live in include/mamba_scan.h.
 #include "mamba_scan.h"
 
+#include "relay.h"
 #include "scan_common.h"
 #include "scan_bwd.h"
 #include "ssd.h"
@@ -92,6 +93,7 @@ struct Plan {
     int relay_parts;      // 1: no relay
     int64_t relay_tiles;  // relayed (batch row, tile) units
     int64_t relay_len;    // steps per relay part (a multiple of chunk)
+    bool relay_withhold;  // failure test: part 0 withholds its hand-off (relay = -k)
     bool zoh;             // zero-order-hold discretisation (scalar family only)
     bool trap, rot;       // exponential-trapezoidal input term, pair rotation (scalar family)
     bool ckpt;            // backward-pass checkpoints written (scalar family, Euler)
@@ -206,11 +208,16 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     // order, round-robin over compute units), gives those compute units half a unit each
     // instead of a whole one (measured at 8 x 4096 x 5120: 747 us against 816 us; a 5/8
     // first part gave 784 us).  More than two parts would chain inside the last round.
-    // Forced part counts (testing) use equal parts.
+    // Forced part counts (testing) use equal parts; a negative count -k forces k parts whose
+    // first part withholds its hand-off, so that the bounded waits give up (failure test).
     p.relay_parts = 1;
-    const int want_relay = opts ? opts->relay : 0;
-    if (want_relay < 0 || want_relay > 8)
+    int want_relay = opts ? opts->relay : 0;
+    if (want_relay < -8 || want_relay > 8 || want_relay == -1)
         return MAMBA_ERR_UNSUPPORTED;
+    if (want_relay < 0) {
+        p.relay_withhold = true;
+        want_relay = -want_relay;
+    }
     if (want_relay >= 2 && (p.family != Family::Scalar || spans != 1))
         return MAMBA_ERR_UNSUPPORTED;
     if (p.family == Family::Scalar && spans == 1 && seqlen > 0 && want_relay != 1) {
@@ -251,12 +258,12 @@ size_t staged_bytes_for(int64_t batch, int64_t seqlen, int64_t d_state, const Pl
     return (bytes + 255) / 256 * 256;
 }
 
-// Relay area: [hand-off flags, 256-byte aligned][hand-off states].
+// Relay area: [hand-off flags, fault word; 256-byte aligned][hand-off states].
 size_t relay_sync_bytes(const Plan &p)
 {
     if (p.relay_parts < 2)
         return 0;
-    const size_t words = (size_t)p.relay_tiles * (size_t)(p.relay_parts - 1);
+    const size_t words = (size_t)p.relay_tiles * (size_t)(p.relay_parts - 1) + 1;
     return (words * sizeof(uint32_t) + 255) / 256 * 256;
 }
 
@@ -583,6 +590,8 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
         L.relay_tiles = (int32_t)plan.relay_tiles;
         L.relay_parts = plan.relay_parts;
         L.relay_len = plan.relay_len;
+        L.relay_withhold = plan.relay_withhold;
+        L.relay_max_polls = plan.relay_withhold ? kRelayTestPolls : kRelayPolls;
     }
     if (plan.family == Family::Scalar) {
         L.bc_staged = reinterpret_cast<float *>(ws_bytes);
@@ -637,6 +646,49 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     L.first_span = 0;
     L.launch_spans = (int32_t)S;
     return hip_status(full(L));
+}
+
+// Reads one fault word of a workspace back to the host (synchronises the stream).
+static mamba_status_t read_fault_word(const uint32_t *word, uint32_t *out, void *stream)
+{
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    uint32_t v = 0;
+    if (hipMemcpyAsync(&v, word, sizeof(v), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return MAMBA_ERR_HIP;
+    *out = v;
+    return MAMBA_OK;
+}
+
+mamba_status_t mamba_scan_fwd_relay_faults(const void *workspace, size_t workspace_bytes,
+                                           int64_t batch, int64_t seqlen, int64_t d_inner,
+                                           int64_t d_state, const mamba_scan_opts_t *opts,
+                                           const mamba_scan_ext_t *ext, uint32_t *faults,
+                                           void *stream)
+{
+    if (!faults)
+        return MAMBA_ERR_NULL_ARG;
+    *faults = 0;
+    int64_t t;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 || !mul_ok(batch, d_inner, &t) ||
+        !mul_ok(t, d_state, &t))
+        return MAMBA_ERR_BAD_SHAPE;
+    if (!d_state_ok(d_state))
+        return MAMBA_ERR_UNSUPPORTED;
+    Plan plan;
+    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, d_state, opts, ext, &plan);
+    if (ps != MAMBA_OK)
+        return ps;
+    if (plan.relay_parts < 2 || seqlen == 0 || batch == 0 || d_inner == 0)
+        return MAMBA_OK; // no relay: nothing can have timed out
+    const size_t need = workspace_bytes_for(batch, seqlen, d_inner, d_state, plan);
+    if (!workspace || workspace_bytes < need)
+        return MAMBA_ERR_WORKSPACE;
+    const size_t staged = staged_bytes_for(batch, seqlen, d_state, plan);
+    const uint32_t *word = reinterpret_cast<const uint32_t *>(
+                               static_cast<const char *>(workspace) + staged) +
+                           plan.relay_tiles * (plan.relay_parts - 1);
+    return read_fault_word(word, faults, stream);
 }
 
 mamba_status_t mamba_scan_fwd(const void *u, const void *delta, const float *A, const void *B,
@@ -1146,6 +1198,7 @@ int32_t mamba_ssd_supported(int64_t head_dim, int64_t d_state)
 // relay_mid, whole chunks before it).
 struct SsdPlan {
     int64_t relay_units = 0, relay_mid = 0;
+    bool relay_withhold = false; // failure test (relay = -2): part 0 keeps its state
     int64_t n_spans = 1, span_len = 0;
 };
 
@@ -1177,8 +1230,12 @@ static mamba_status_t ssd_make_plan(int64_t batch, int64_t seqlen, int64_t n_hea
                                     const mamba_ssd_opts_t *opts, SsdPlan *r)
 {
     *r = SsdPlan{};
-    const int32_t relay = opts ? opts->relay : 0;
+    int32_t relay = opts ? opts->relay : 0;
     const int32_t spans = opts ? opts->n_spans : 0;
+    if (relay == -2) { // forced relay whose first parts withhold their hand-off (testing)
+        r->relay_withhold = true;
+        relay = 2;
+    }
     if (relay < 0 || relay > 2 || spans < 0 || spans > 64 || (relay == 2 && spans >= 2))
         return MAMBA_ERR_UNSUPPORTED;
     const int64_t units = batch * n_heads;
@@ -1219,12 +1276,14 @@ static mamba_status_t ssd_make_plan(int64_t batch, int64_t seqlen, int64_t n_hea
     return MAMBA_OK;
 }
 
-// Workspace: relay [one flag per relayed unit, 256-byte aligned][head_dim x d_state fp32
-// each]; split [(n_spans - 1) x units states of head_dim x d_state fp32][(n_spans - 1) x
-// units decays, fp32].
+// Workspace: relay [one flag per relayed unit and a fault word, 256-byte aligned][head_dim x
+// d_state fp32 each]; split [(n_spans - 1) x units states of head_dim x d_state fp32]
+// [(n_spans - 1) x units decays, fp32].
 static size_t ssd_sync_bytes(const SsdPlan &r)
 {
-    return r.relay_units > 0 ? ((size_t)r.relay_units * sizeof(uint32_t) + 255) / 256 * 256 : 0;
+    return r.relay_units > 0
+               ? (((size_t)r.relay_units + 1) * sizeof(uint32_t) + 255) / 256 * 256
+               : 0;
 }
 
 static size_t ssd_span_state_bytes(const SsdPlan &r, int64_t units, int64_t head_dim,
@@ -1353,8 +1412,36 @@ mamba_status_t mamba_ssd_fwd_ex(const void *x, const void *dt, const float *A, c
         q.relay_mid = plan.relay_mid;
         q.relay_sync = reinterpret_cast<uint32_t *>(ws);
         q.relay_state = reinterpret_cast<float *>(ws + ssd_sync_bytes(plan));
+        q.relay_withhold = plan.relay_withhold;
     }
     return hip_status(launch_ssd(q, st));
+}
+
+mamba_status_t mamba_ssd_relay_faults(const void *workspace, size_t workspace_bytes,
+                                      int64_t batch, int64_t seqlen, int64_t n_heads,
+                                      int64_t head_dim, int64_t d_state, mamba_dtype_t dtype,
+                                      const mamba_ssd_opts_t *opts, uint32_t *faults,
+                                      void *stream)
+{
+    if (!faults)
+        return MAMBA_ERR_NULL_ARG;
+    *faults = 0;
+    const mamba_status_t shape_st =
+        ssd_check_shape(batch, seqlen, n_heads, head_dim, d_state, dtype);
+    if (shape_st != MAMBA_OK)
+        return shape_st;
+    SsdPlan plan;
+    const mamba_status_t plan_st =
+        ssd_make_plan(batch, seqlen, n_heads, d_state, dtype, opts, &plan);
+    if (plan_st != MAMBA_OK)
+        return plan_st;
+    if (plan.n_spans >= 2 || plan.relay_units <= 0 || batch == 0 || n_heads == 0 || seqlen == 0)
+        return MAMBA_OK; // no relay: nothing can have timed out
+    const size_t need = ssd_workspace_bytes(plan, batch * n_heads, head_dim, d_state);
+    if (!workspace || workspace_bytes < need)
+        return MAMBA_ERR_WORKSPACE;
+    return read_fault_word(static_cast<const uint32_t *>(workspace) + plan.relay_units, faults,
+                           stream);
 }
 
 mamba_status_t mamba_ssd_state_update(float *h, const void *x, const void *dt, const float *A,

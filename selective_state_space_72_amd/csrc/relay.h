@@ -1,7 +1,10 @@
 // Hand-off of a state between two blocks of one launch (the "relay" that splits a work
 // unit in time, part 1 continuing from part 0's final state).  Workgroups are dispatched
 // in index order, so a waiting block's predecessor always has a smaller index and already
-// holds a slot; the wait is bounded all the same.
+// holds a slot; the wait is bounded all the same, and a wait that gives up is made visible:
+// it is counted in a fault word next to the flags (the host reads it back, see
+// mamba_scan_fwd_relay_faults) and the receiving block continues from a NaN state, so every
+// output that depends on the missing state is NaN rather than silently wrong.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,18 +12,27 @@
 
 namespace mambascan {
 
+// Polls of a normal relay wait (each about 8k cycles of s_sleep: a few seconds in all).
+constexpr uint32_t kRelayPolls = 1u << 20;
+// Polls when the planner runs the relay's failure test (part 0 withholds its hand-off).
+constexpr uint32_t kRelayTestPolls = 1u << 10;
+
 // Bounded wait for a relay flag (one thread of the block).  Polls with relaxed
 // device-scope loads (no cache invalidation per poll, which would disturb every other
-// wave on the XCD) and long sleeps, then acquires once; gives up after 2^20 polls (a few
-// seconds), so a missing hand-off can never hang the device.
-__device__ __forceinline__ void relay_wait(uint32_t *flag)
+// wave on the XCD) and long sleeps, then acquires once.  True once the flag is raised,
+// false after max_polls polls.
+__device__ __forceinline__ bool relay_wait(uint32_t *flag, uint32_t max_polls)
 {
-    for (uint32_t i = 0; i < (1u << 20); ++i) {
-        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+    bool seen = false;
+    for (uint32_t i = 0; i < max_polls; ++i) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+            seen = true;
             break;
+        }
         __builtin_amdgcn_s_sleep(127);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return seen;
 }
 
 // Publish the state every thread of the block has stored: release its stores at device
@@ -34,13 +46,19 @@ __device__ __forceinline__ void relay_signal(uint32_t *flag)
 }
 
 // The waiting side: thread 0 waits, the block joins it, and every thread acquires before
-// reading the state.
-__device__ __forceinline__ void relay_receive(uint32_t *flag)
+// reading the state.  Returns, to every thread, whether the state arrived; a give-up adds
+// one to *fault (a vector atomic of one lane).
+__device__ __forceinline__ bool relay_receive(uint32_t *flag, uint32_t *fault, uint32_t max_polls)
 {
-    if (threadIdx.x == 0)
-        relay_wait(flag);
-    __syncthreads();
+    int missed = 0;
+    if (threadIdx.x == 0) {
+        missed = relay_wait(flag, max_polls) ? 0 : 1;
+        if (missed)
+            __hip_atomic_fetch_add(fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    missed = __syncthreads_or(missed);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return missed == 0;
 }
 
 } // namespace mambascan

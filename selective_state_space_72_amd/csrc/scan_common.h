@@ -33,11 +33,15 @@ struct ScanLaunch {
     // Relay (scalar family, single span): the last `relay_tiles` (batch row, channel tile)
     // units are split in time into `relay_parts` parts of `relay_len` steps run by different
     // blocks, each part handing its final state to the next through relay_state.
-    // relay_sync[slot] are the hand-off flags, zeroed by the staging pass of the same call.
+    // relay_sync[slot] are the hand-off flags and relay_sync[slots] counts waits that gave
+    // up; the staging pass of the same call zeroes them.  relay_withhold (testing): part 0
+    // of every relayed unit keeps its state, so the waits give up after relay_max_polls.
     uint32_t *relay_sync;
     float *relay_state;         // [slot][n][lane], slot = tile * (parts - 1) + part
     int32_t relay_tiles, relay_parts;
     int64_t relay_len;
+    uint32_t relay_max_polls;
+    bool relay_withhold;
     bool zoh; // zero-order-hold Bbar (scalar family); Euler otherwise
     // Options of the Mamba-3 formulation (scalar family; NULL / false = off):
     // exponential-trapezoidal input term with mixing coefficients lam (B,L,D) and the input
@@ -54,9 +58,12 @@ struct ScanLaunch {
 // Relay arguments as the scan kernel receives them.
 struct RelayArgs {
     uint32_t *sync;
+    uint32_t *fault;             // count of waits that gave up (after the flags)
     float *state;
     int32_t tiles, parts, units; // units = batch * channel tiles
     int32_t len;
+    uint32_t max_polls;
+    int32_t withhold;            // testing: part 0 does not hand its state over
 };
 
 enum class Family : int { Auto = 0, Block = 1, Rows = 2, Scalar = 3 };

@@ -36,8 +36,8 @@ __device__ __forceinline__ void for_c(F &&f)
 
 // bcp[((b * NW + g) * Lp + t) * BCW + {q, NQ + q}] = {B, C}[b, t, g * NQ + q] (0 past L),
 // BCW = 2 NQ; with rotation rates (ROT) also bcp[... + 2 NQ + q / 2] = theta[b, t, (g NQ + q)
-// / 2] for even q, BCW = 2 NQ + NQ / 2.  Also zeroes the relay hand-off flags (n_sync
-// words) for the scan launch that follows on the same stream.
+// / 2] for even q, BCW = 2 NQ + NQ / 2.  Also zeroes the relay hand-off flags and fault word
+// (n_sync words) for the scan launch that follows on the same stream.
 template <typename T, int N, int NW, bool ROT>
 __global__ void __launch_bounds__(256)
 stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, const T *__restrict__ th,
@@ -202,10 +202,17 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     if (relayed && part > 0) {
         // the previous part's final state: wait for its flag, then read it
         const int slot = r_unit * (relay.parts - 1) + part - 1;
-        relay_receive(relay.sync + slot);
+        if (relay_receive(relay.sync + slot, relay.fault, relay.max_polls)) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
-            h[q] = relay.state[((int64_t)slot * N + n0 + q) * 64 + lane];
+            for (int q = 0; q < NQ; ++q)
+                h[q] = relay.state[((int64_t)slot * N + n0 + q) * 64 + lane];
+        } else {
+            // the hand-off never came (counted in relay.fault): a NaN state makes every
+            // output of this part and of the unit's final state NaN instead of wrong
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                h[q] = __builtin_nanf("");
+        }
     }
     const float bias_d = bias ? bias[dc] : 0.0f;
     const float D_d = Dv ? Dv[dc] : 0.0f;
@@ -499,6 +506,8 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     if (relayed && part >= 0 && part < relay.parts - 1) {
         // hand the final state to the next part (every lane: the slot is dense)
         const int slot = r_unit * (relay.parts - 1) + part;
+        if (relay.withhold && part == 0)
+            return; // failure test: the next part's wait gives up
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
             relay.state[((int64_t)slot * N + n0 + q) * 64 + lane] = h[q];
@@ -549,6 +558,9 @@ hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
     relay.parts = 1;
     if (FULL && p.relay_parts > 1) {
         relay.sync = p.relay_sync;
+        relay.fault = p.relay_sync + (int64_t)p.relay_tiles * (p.relay_parts - 1);
+        relay.max_polls = p.relay_max_polls;
+        relay.withhold = p.relay_withhold ? 1 : 0;
         relay.state = p.relay_state;
         relay.tiles = p.relay_tiles;
         relay.parts = p.relay_parts;
@@ -572,7 +584,8 @@ template <typename T, int N, int NW>
 hipError_t launch_stage(const ScanLaunch &p, hipStream_t stream)
 {
     const int64_t total = p.batch * p.staged_rows * N;
-    const int32_t n_sync = p.relay_parts > 1 ? p.relay_tiles * (p.relay_parts - 1) : 0;
+    // hand-off flags and the fault word after them
+    const int32_t n_sync = p.relay_parts > 1 ? p.relay_tiles * (p.relay_parts - 1) + 1 : 0;
     const int64_t blocks = (max(total, (int64_t)n_sync) + 255) / 256;
     if (blocks <= 0)
         return hipSuccess;

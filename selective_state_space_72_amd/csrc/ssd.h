@@ -18,9 +18,12 @@ struct SsdLaunch {
     // second continuing from step relay_mid (a multiple of the chunk) with the first's
     // final state, handed over through relay_state (head_dim x d_state fp32 per unit) and
     // relay_sync (one flag per unit).  relay_units = 0: no relay.
+    // relay_sync[relay_units] counts waits that gave up; relay_withhold (testing): the first
+    // parts keep their states, so the waits give up.
     int64_t relay_units, relay_mid;
     uint32_t *relay_sync;
     float *relay_state;
+    bool relay_withhold;
     // Sequence split (no relay then): n_spans spans of span_len steps (a multiple of the
     // chunk), the spans after the first starting from the state the carry gives them;
     // span_state (n_spans - 1) x units x head_dim x d_state fp32, span_decay (n_spans - 1) x

@@ -190,8 +190,10 @@ struct SsdArgs {
     // from step r_mid; 0 = none
     int32_t units, r_units;
     int64_t r_mid;
-    uint32_t *r_sync;
+    uint32_t *r_sync;  // hand-off flags, then the count of waits that gave up
     float *r_state;
+    uint32_t r_polls;  // poll limit of a wait
+    int32_t r_withhold; // testing: part 0 does not hand its state over
     // sequence split into n_spans spans of span_len steps (a multiple of the chunk); sp holds
     // per span s < n_spans - 1 and unit its final state (END pass, from h0 for span 0 and
     // from zero otherwise), turned by the carry into the state entering span s + 1; sp_dec
@@ -443,12 +445,15 @@ ssd_chunk_kernel(SsdArgs p)
     }
     if (part == 1) {
         // part 0's final state, once its first chunk is on the way
-        relay_receive(p.r_sync + slot);
+        // (a wait that gives up is counted and leaves a NaN state: the outputs of this part
+        // and the final state become NaN instead of wrong)
+        const bool got = relay_receive(p.r_sync + slot, p.r_sync + p.r_units, p.r_polls);
 #pragma unroll
         for (int m = 0; m < NT; ++m)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                hacc[m][v] = p.r_state[((int64_t)slot * P + pc) * N + 16 * m + 4 * g + v];
+                hacc[m][v] = got ? p.r_state[((int64_t)slot * P + pc) * N + 16 * m + 4 * g + v]
+                                 : __builtin_nanf("");
     }
     float decp = 1.0f; // END: the span's total decay, the product of its chunks'
     for (int64_t t0 = t_begin; t0 < t_end; t0 += Q) {
@@ -634,6 +639,8 @@ ssd_chunk_kernel(SsdArgs p)
         return;
     }
     if (part == 0) {
+        if (p.r_withhold)
+            return; // failure test: part 1's wait gives up
         // hand the final state to part 1 (the part covers whole chunks: no tail rows)
 #pragma unroll
         for (int m = 0; m < NT; ++m)
@@ -669,8 +676,8 @@ __global__ void ssd_span_carry_kernel(float *sp, const float *sp_dec, int64_t un
     }
 }
 
-// Zeroes the relay flags before a relayed launch (a kernel, not a memset: the launch
-// sequence stays capturable in a graph).
+// Zeroes the relay flags and the fault word before a relayed launch (a kernel, not a
+// memset: the launch sequence stays capturable in a graph).
 __global__ void ssd_relay_clear_kernel(uint32_t *sync, int32_t n)
 {
     const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
@@ -703,6 +710,8 @@ hipError_t launch_ssd_t(const SsdLaunch &q, hipStream_t stream)
     a.r_mid = q.relay_mid;
     a.r_sync = q.relay_sync;
     a.r_state = q.relay_state;
+    a.r_polls = q.relay_withhold ? kRelayTestPolls : kRelayPolls;
+    a.r_withhold = q.relay_withhold ? 1 : 0;
     a.n_spans = q.n_spans > 1 ? (int32_t)q.n_spans : 1;
     a.span_len = q.span_len;
     a.sp = q.span_state;
@@ -724,7 +733,7 @@ hipError_t launch_ssd_t(const SsdLaunch &q, hipStream_t stream)
     }
     const int64_t blocks = units * a.n_spans + q.relay_units;
     if (q.relay_units > 0) {
-        const int32_t n = (int32_t)q.relay_units;
+        const int32_t n = (int32_t)q.relay_units + 1; // flags and the fault word
         hipLaunchKernelGGL(ssd_relay_clear_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256),
                            0, stream, q.relay_sync, n);
         const hipError_t e = hipGetLastError();

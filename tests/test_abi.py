@@ -130,10 +130,10 @@ def test_scan_workspace_rules(lib):
                 y=BASE + 1500 * MB, ws=BASE + 1500 * MB, ws_bytes=n) == ALIAS
     # many channels: no split; the scalar-B/C kernel stages B and C as fp32 with one
     # chunk of padding rows: batch * (L + 8) * 2 * d_state * 4 bytes.  640 units over 256
-    # compute units leave 128 over: they are relayed in 2 parts (128 flags, padded to 256
-    # bytes, and 128 hand-off states of 64 x 16 floats)
+    # compute units leave 128 over: they are relayed in 2 parts (128 flags and a fault word,
+    # padded to 256 bytes, and 128 hand-off states of 64 x 16 floats)
     staged = 8 * (4096 + 8) * 2 * 16 * 4
-    relay = 512 + 128 * 64 * 16 * 4
+    relay = 768 + 128 * 64 * 16 * 4
     assert lib.mamba_scan_fwd_workspace_size(8, 4096, 5120, 16) == staged + relay
     assert lib.mamba_scan_fwd_workspace_size_ex(8, 4096, 5120, 16,
                                                 ctypes.byref(ms.ScanOpts(0, 0, 0, 0, 1))) == staged
@@ -173,6 +173,9 @@ def test_relay_options(lib):
     assert ws(*small, o=ms.ScanOpts(0, 0, 1, 3, 3)) == staged + 256 + 24 * 64 * 16 * 4
     assert ws(*small, o=ms.ScanOpts(0, 0, 1, 3, 1)) == staged
     assert ws(*small, o=ms.ScanOpts(0, 0, 1, 3, 0)) == staged    # auto: one round, no relay
+    # the failure test (-k: k parts, the first withholding its hand-off) plans the same
+    assert ws(*small, o=ms.ScanOpts(0, 0, 1, 3, -3)) == staged + 256 + 24 * 64 * 16 * 4
+    assert ws(*small, o=ms.ScanOpts(0, 0, 1, 3, -9)) == bad
     # parts are whole chunks and none is empty: 20 steps in chunks of 8 -> 3 parts (8, 8, 4)
     assert ws(3, 20, 200, 16, o=ms.ScanOpts(0, 0, 1, 3, 8)) == \
         3 * (20 + 8) * 2 * 16 * 4 + 256 + 24 * 64 * 16 * 4
