@@ -471,6 +471,30 @@ MAMBA_API mamba_status_t mamba_scan_fwd_relay_faults(const void *workspace,
                                                      const mamba_scan_ext_t *ext,
                                                      uint32_t *faults, void *stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): mamba_scan_fwd with the same arguments
+ * minus the workspace.  The workspace mamba_scan_fwd_workspace_size reports for these sizes
+ * is taken from a device array the library holds on every device it runs on (reserved when
+ * the library's code is loaded, kept until the process ends); the call itself allocates and
+ * frees nothing.  Limit: that size must be at most MAMBA_SCAN_NOALLOC_MAX_WORKSPACE (16 MiB:
+ * the large prefill 8 x 4096 x 5120 needs 4.7 MiB, the long sequence 1 x 131072 x 2048
+ * 12.6 MiB), else MAMBA_ERR_WORKSPACE and nothing is launched.  The array belongs to the
+ * device of `stream` (the current device for NULL); all calls on one device share it, so
+ * calls that overlap on one device race and must be serialised by the caller (for example
+ * by issuing them on one stream).  Results are those of mamba_scan_fwd, bitwise.  Errors as
+ * mamba_scan_fwd; MAMBA_ERR_HIP if the array's address cannot be looked up.
+ */
+#define MAMBA_SCAN_NOALLOC_MAX_WORKSPACE ((size_t)16 << 20)
+MAMBA_API mamba_status_t mamba_scan_fwd_noalloc(const void *u, const void *delta,
+                                                const float *A, const void *B, const void *C,
+                                                const float *D, const void *z,
+                                                const float *delta_bias, const float *h0,
+                                                void *y, float *h_last, int64_t batch,
+                                                int64_t seqlen, int64_t d_inner,
+                                                int64_t d_state, mamba_dtype_t dtype,
+                                                void *stream);
+
 /* mamba_state_update_ex with the Mamba-3 options (shapes of the decode step; ext NULL =
  * none).  With lambda the caller passes the previous token's u and B as u_prev, B_prev.
  * ext->ckpt must be NULL (MAMBA_ERR_UNSUPPORTED otherwise). */

@@ -42,7 +42,7 @@ EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_ssd_supported", "mamba_ssd_fwd", "mamba_ssd_workspace_size", "mamba_ssd_fwd_ex",
            "mamba_ssd_state_update",
            "mamba_scan_ckpt_size", "mamba_scan_bwd_ckpt_workspace_size", "mamba_scan_bwd_ckpt",
-           "mamba_scan_fwd_relay_faults", "mamba_ssd_relay_faults",
+           "mamba_scan_fwd_relay_faults", "mamba_ssd_relay_faults", "mamba_scan_fwd_noalloc",
            "mamba_status_string")
 
 
@@ -167,6 +167,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mamba_ssd_relay_faults.argtypes = ([_vp, ctypes.c_size_t] + [_i64] * 5 +
                                            [ctypes.c_int, ctypes.POINTER(SsdOpts),
                                             ctypes.POINTER(ctypes.c_uint32), _vp])
+    lib.mamba_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.mamba_scan_fwd_noalloc.argtypes = [_vp] * 11 + [_i64] * 4 + [ctypes.c_int, _vp]
     lib.mamba_status_string.restype = ctypes.c_char_p
     lib.mamba_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -360,6 +362,36 @@ def mamba_scan_fwd_relay_faults(workspace, batch: int, seqlen: int, d_inner: int
     if st != 0:
         raise MambaError(st, "mamba_scan_fwd_relay_faults")
     return int(out.value)
+
+
+NOALLOC_MAX_WORKSPACE = 16 << 20  # MAMBA_SCAN_NOALLOC_MAX_WORKSPACE
+
+
+def mamba_scan_fwd_noalloc(u, delta, A, B, C, *, out, D=None, z=None, delta_bias=None,
+                           h0=None, h_last_out=None):
+    """mamba_scan_fwd into caller-provided outputs (out, h_last_out) through the entry point
+    that allocates nothing (its workspace is the library's per-device array).  Returns
+    (out, h_last_out)."""
+    torch = _torch()
+    lib = load_library()
+    if u.dim() != 3 or A.dim() != 2:
+        raise ValueError("u must be (batch, seqlen, d_inner) and A (d_inner, d_state)")
+    batch, seqlen, d_inner = u.shape
+    d_state = A.shape[1]
+    dev, act, f32 = u.device, u.dtype, torch.float32
+    bld = (batch, seqlen, d_inner)
+    st = lib.mamba_scan_fwd_noalloc(
+        _ptr(u, "u", bld, act, dev), _ptr(delta, "delta", bld, act, dev),
+        _ptr(A, "A", (d_inner, d_state), f32, dev),
+        _ptr(B, "B", (batch, seqlen, d_state), act, dev),
+        _ptr(C, "C", (batch, seqlen, d_state), act, dev), _ptr(D, "D", (d_inner,), f32, dev),
+        _ptr(z, "z", bld, act, dev), _ptr(delta_bias, "delta_bias", (d_inner,), f32, dev),
+        _ptr(h0, "h0", (batch, d_inner, d_state), f32, dev), _ptr(out, "out", bld, act, dev),
+        _ptr(h_last_out, "h_last_out", (batch, d_inner, d_state), f32, dev),
+        batch, seqlen, d_inner, d_state, _dtype_code(u), _stream(dev))
+    if st != 0:
+        raise MambaError(st, "mamba_scan_fwd_noalloc")
+    return out, h_last_out
 
 
 def mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None, *, out=None,

@@ -606,3 +606,28 @@ def test_bwd_ckpt_validation(lib):
     assert bwd_ck(lib, ckpt=BASE + 1024 * MB) == ALIAS                       # ckpt over ws
     assert bwd_ck(lib, ws_bytes=16) == WS
     assert bwd_ck(lib, N=64) == UNSUP
+
+
+def noalloc(lib, *, u=BASE, delta=BASE + 64 * MB, A=BASE + 128 * MB, B=BASE + 132 * MB,
+            C=BASE + 136 * MB, y=BASE + 256 * MB, batch=2, L=64, Dn=128, N=16, dtype=BF16):
+    return lib.mamba_scan_fwd_noalloc(u, delta, A, B, C, None, None, None, None, y, None,
+                                      batch, L, Dn, N, dtype, None)
+
+
+def test_noalloc_rejects_before_touching_the_device(lib):
+    """The allocation-free entry point validates like mamba_scan_fwd and refuses sizes whose
+    workspace exceeds its per-device array, before anything runs on the device."""
+    cap = ms.NOALLOC_MAX_WORKSPACE
+    # a long sequence with d_state 32: its span summaries (24 MiB) exceed the array
+    big = lib.mamba_scan_fwd_workspace_size(1, 131072, 2048, 32)
+    assert big > cap
+    assert noalloc(lib, batch=1, L=131072, Dn=2048, N=32) == WS
+    assert lib.mamba_scan_fwd_workspace_size(8, 4096, 5120, 16) <= cap  # the large prefill fits
+    assert noalloc(lib, batch=-1) == lib.mamba_scan_fwd(
+        BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 132 * MB, BASE + 136 * MB, None, None,
+        None, None, BASE + 256 * MB, None, -1, 64, 128, 16, BF16, None, 0, None)
+    assert noalloc(lib, N=12) == UNSUP
+    assert noalloc(lib, u=None) == NULL
+    assert noalloc(lib, dtype=7) == lib.mamba_scan_fwd(
+        BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 132 * MB, BASE + 136 * MB, None, None,
+        None, None, BASE + 256 * MB, None, 2, 64, 128, 16, 7, None, 0, None)
