@@ -30,15 +30,16 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "selective-scan GB/s + Gchan-steps/s (B·L·D) and % of MI355X HBM peak"
-# Plain-ALU roofline of the scan (no MFMA, no packed FP32): MI355X issues 128 fp32 VALU
-# lanes per clock per CU (256 CUs, 2.4 GHz) = 78.6 T lane-instructions/s; v_exp_f32 issues
-# at a quarter of that rate.  One state update (b, t, d, n) needs two multiplies and two
-# FMAs (6 flops, 4 instruction slots) and one v_exp_f32 (4 slots): the mix peaks at
-# 78.6e12 * 6 / 8 = 58.98 TFLOP/s.
-VALU_LANE_INSTR = 256 * 128 * 2.4e9
+# Plain-ALU roofline of the scan (no MFMA, no packed FP32).  One state update (b, t, d, n)
+# needs one v_exp_f32 and four fp32 VALU operations: Delta*A' (an FMA with the exp bias
+# shift), (Delta u)*B, the recurrence FMA and the readout FMA -- 6 flops counting a
+# multiply as 1 and an FMA as 2 (the exp is not counted).  The peak is what the chip's
+# 256 CUs x 4 SIMDs issue of that mix at the rates the probes measure in the same run
+# (mamba_probe_issue): v_exp_f32 at R_exp and the VALU forms at R_fma (all operands in
+# vector registers, the cheaper form), both in wave instructions per second over the chip:
+#   peak = 6 flops x 64 lanes / (1 / R_exp + 4 / R_fma).
 ALU_FLOPS_PER_UPDATE = 6
-ALU_SLOTS_PER_UPDATE = 8
-ALU_PEAK_TFLOPS = VALU_LANE_INSTR * ALU_FLOPS_PER_UPDATE / ALU_SLOTS_PER_UPDATE / 1e12
+ALU_VALU_PER_UPDATE = 4
 
 
 # Sources that determine the dominant kernel's code; HBM traffic measured with counters is
@@ -511,6 +512,70 @@ def ssd_decode_workload(dev, flush, steps):
             "hbm_frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def probe_rates(dev):
+    """The measured ceilings: issue rates of the update's instruction forms (chip-wide wave
+    instructions per second, 8 waves per SIMD) and the bandwidth of a 512 MiB device copy
+    (best over a few grid sizes)."""
+    import ctypes
+    import torch
+    import selective_state_space_72_amd as ms
+    lib = ms.load_library()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    sink = torch.empty(cus * 8 * 256, dtype=torch.float32, device=dev)
+    out = {"compute_units": cus, "waves_per_simd": 8}
+
+    def timed(launch, reps=5):
+        for _ in range(2):
+            launch()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            launch()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+    forms = (("fma_vgpr", 0, 4096), ("fma_sgpr", 1, 4096), ("exp", 2, 2048),
+             ("update", 3, 256))
+    for name, kind, iters in forms:
+        n = ctypes.c_uint64(0)
+
+        def launch(kind=kind, iters=iters, n=n):
+            st = lib.mamba_probe_issue(kind, 8, iters, cus, ctypes.c_void_p(sink.data_ptr()),
+                                       ctypes.byref(n), ctypes.c_void_p(stream))
+            if st != 0:
+                raise ms.MambaError(st, "mamba_probe_issue")
+        sec = timed(launch)
+        rate = n.value / sec
+        out[name] = {"wave_instr_per_s": float(f"{rate:.4e}"),
+                     "simd_cycles_at_2_4_ghz": round(cus * 4 * 2.4e9 / rate, 3)}
+    out["update"]["unit"] = "wave-level state updates"
+    nbytes = 512 << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    best = 0.0
+    for blocks in (1024, 2048, 4096, 16384):
+        def launch(blocks=blocks):
+            st = lib.mamba_probe_copy(ctypes.c_void_p(src.data_ptr()),
+                                      ctypes.c_void_p(dst.data_ptr()), nbytes, blocks,
+                                      ctypes.c_void_p(stream))
+            if st != 0:
+                raise ms.MambaError(st, "mamba_probe_copy")
+        sec = timed(launch, reps=7)
+        best = max(best, 2 * nbytes / sec / 1e9)
+    out["copy_512MiB_GB_s"] = round(best, 1)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    r_exp, r_fma = out["exp"]["wave_instr_per_s"], out["fma_vgpr"]["wave_instr_per_s"]
+    out["alu_peak_tflops"] = round(ALU_FLOPS_PER_UPDATE * 64 /
+                                   (1.0 / r_exp + ALU_VALU_PER_UPDATE / r_fma) / 1e12, 2)
+    out["update_pattern_tflops"] = round(
+        ALU_FLOPS_PER_UPDATE * 64 * out["update"]["wave_instr_per_s"] / 1e12, 2)
+    return out
+
+
 def copy_calibration(dev):
     """Three 512 MiB device copies: the reference kernel that FETCH_SIZE / WRITE_SIZE
     counters of the measured kernels are scaled by."""
@@ -572,7 +637,9 @@ def main():
     case = ScanCase(cfg, dev)
     flush = make_flush(dev)
     log("bench: timing")
-    loop_ms, med_ms, wall_ms = time_steps(case.step, args.steps, args.warmup, flush)
+    # the warmup runs for at least 100 ms: the clock ramps over the first ~40 ms of load
+    loop_ms, med_ms, wall_ms = time_steps(case.step, args.steps, args.warmup, flush,
+                                          warm_ms=100.0)
     ms_per_step = loop_ms
     gbs = case.min_bytes / (ms_per_step * 1e-3) / 1e9
     gcs = cfg.chan_steps / (ms_per_step * 1e-3) / 1e9
@@ -583,15 +650,24 @@ def main():
     # which slightly understates its rate.
     kernel_ms = ms_per_step
     kbytes = case.min_bytes
+    del case
+    torch.cuda.empty_cache()
+    log("bench: probes (issue rates, device copy)")
+    probes = probe_rates(dev)
+    alu_peak = probes["alu_peak_tflops"]
     tflops = elems * ALU_FLOPS_PER_UPDATE / (kernel_ms * 1e-3) / 1e12
-    roof = {"bound": "alu", "achieved": round(tflops, 3), "peak": round(ALU_PEAK_TFLOPS, 2),
-            "unit": "TFLOP/s", "frac": round(tflops / ALU_PEAK_TFLOPS, 4),
+    roof = {"bound": "alu", "achieved": round(tflops, 3), "peak": alu_peak,
+            "unit": "TFLOP/s", "frac": round(tflops / alu_peak, 4),
             "traffic": recorded_traffic(),
             "kernel": "scan_scalar_kernel<bf16, d_state 16, 8 waves, chunk 8> (+ stage_bc_kernel)",
+            "peak_source": "1 v_exp_f32 + 4 fp32 VALU (6 flops) per state update at the probe "
+                           "rates of this run: 6 x 64 / (1/R_exp + 4/R_fma_vgpr)",
+            "update_pattern_peak": probes["update_pattern_tflops"],
             "hbm": {"achieved": round(kbytes / (kernel_ms * 1e-3) / 1e9, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(kbytes / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-            "alu_time_floor_ms": round(elems * ALU_SLOTS_PER_UPDATE / VALU_LANE_INSTR * 1e3, 4),
+                    "frac": round(kbytes / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "copy_probe_GB_s": probes["copy_512MiB_GB_s"]},
+            "alu_time_floor_ms": round(elems * ALU_FLOPS_PER_UPDATE / (alu_peak * 1e12) * 1e3, 4),
             "hbm_time_floor_ms": round(kbytes / HBM_PEAK_GBS / 1e9 * 1e3, 4)}
     line = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -604,12 +680,11 @@ def main():
                        "d_state": cfg.d_state, "io_dtype": "bf16", "parallelism": "none"},
             "gchan_steps_per_s": round(gcs, 2),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "min_bytes_per_step": case.min_bytes,
+            "min_bytes_per_step": kbytes,
             "ms_single_step_mall_flushed": round(med_ms, 4) if med_ms else None,
             "wall_ms_per_step": round(wall_ms, 4),
-            "roofline": roof}
-    del case
-    torch.cuda.empty_cache()
+            "roofline": roof,
+            "probes": probes}
     if args.copy_calibration:
         copy_calibration(dev)
     if not args.no_extra:

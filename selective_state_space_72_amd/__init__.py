@@ -43,6 +43,7 @@ EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_ssd_state_update",
            "mamba_scan_ckpt_size", "mamba_scan_bwd_ckpt_workspace_size", "mamba_scan_bwd_ckpt",
            "mamba_scan_fwd_relay_faults", "mamba_ssd_relay_faults", "mamba_scan_fwd_noalloc",
+           "mamba_probe_copy", "mamba_probe_issue",
            "mamba_status_string")
 
 
@@ -169,6 +170,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                             ctypes.POINTER(ctypes.c_uint32), _vp])
     lib.mamba_scan_fwd_noalloc.restype = ctypes.c_int
     lib.mamba_scan_fwd_noalloc.argtypes = [_vp] * 11 + [_i64] * 4 + [ctypes.c_int, _vp]
+    lib.mamba_probe_copy.restype = ctypes.c_int
+    lib.mamba_probe_copy.argtypes = [_vp, _vp, ctypes.c_size_t, ctypes.c_int32, _vp]
+    lib.mamba_probe_issue.restype = ctypes.c_int
+    lib.mamba_probe_issue.argtypes = ([ctypes.c_int32] * 4 +
+                                      [_vp, ctypes.POINTER(ctypes.c_uint64), _vp])
     lib.mamba_status_string.restype = ctypes.c_char_p
     lib.mamba_status_string.argtypes = [ctypes.c_int]
     _lib = lib

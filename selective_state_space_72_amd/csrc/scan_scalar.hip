@@ -387,6 +387,16 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
         epilogue_store(es);
 
         // ---- recurrence over the chunk ----
+        // The chunk's decay factors first: issued back to back, the exps leave the VALU
+        // free of the switches between exp and FMA forms inside each step (measured 5 %
+        // faster at the large prefill; the values are the same).
+        float ag[TC][NQ];
+#pragma unroll
+        for (int tl = 0; tl < TC; ++tl)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                ag[tl][q] = decay_exp2(dw[tl].x, a2[q]);
+        __builtin_amdgcn_sched_barrier(0);
         auto step = [&](int tl) {
             float yp = 0.0f;
             if constexpr (ROT) {
@@ -410,7 +420,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                 p_lb = dw[tl].z * (tl == 0 ? u_lb : dw[tl > 0 ? tl - 1 : 0].w);
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
-                const float a = decay_exp2(dw[tl].x, a2[q]);
+                const float a = ag[tl][q];
                 if constexpr (RM) { // row q % 2 of pair q / 2 decays with state q
                     rm[4 * (q / 2) + (q & 1)] *= a;
                     rm[4 * (q / 2) + 2 + (q & 1)] *= a;

@@ -28,7 +28,9 @@ def lib():
 
 
 def header_functions():
-    text = open(HEADER).read()
+    import glob
+    text = "".join(open(h).read() for h in sorted(glob.glob(os.path.join(os.path.dirname(HEADER),
+                                                                        "*.h"))))
     return sorted(set(re.findall(r"MAMBA_API\s+[\w\s\*]*?\b(mamba_\w+)\s*\(", text)))
 
 
@@ -631,3 +633,18 @@ def test_noalloc_rejects_before_touching_the_device(lib):
     assert noalloc(lib, dtype=7) == lib.mamba_scan_fwd(
         BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 132 * MB, BASE + 136 * MB, None, None,
         None, None, BASE + 256 * MB, None, 2, 64, 128, 16, 7, None, 0, None)
+
+
+def test_probe_argument_checks(lib):
+    """The probes validate on the host before launching anything."""
+    n = ctypes.c_uint64(0)
+    assert lib.mamba_probe_copy(None, BASE, 64, 4, None) == NULL
+    assert lib.mamba_probe_copy(BASE, BASE + MB, 60, 4, None) == 2          # not 16-byte units
+    assert lib.mamba_probe_copy(BASE, BASE + MB, 64, 0, None) == 2          # no blocks
+    assert lib.mamba_probe_copy(BASE + 8, BASE + MB, 64, 4, None) == ALIGN
+    assert lib.mamba_probe_copy(BASE, BASE + 32, 64, 4, None) == ALIAS
+    assert lib.mamba_probe_copy(BASE, BASE + MB, 0, 4, None) == OK
+    assert lib.mamba_probe_issue(0, 9, 1, 256, BASE, ctypes.byref(n), None) == 2
+    assert lib.mamba_probe_issue(0, 1, 0, 256, BASE, ctypes.byref(n), None) == 2
+    assert lib.mamba_probe_issue(4, 1, 1, 256, BASE, ctypes.byref(n), None) == UNSUP
+    assert lib.mamba_probe_issue(0, 1, 1, 256, None, ctypes.byref(n), None) == NULL
