@@ -477,15 +477,15 @@ MAMBA_API mamba_status_t mamba_scan_fwd_relay_faults(const void *workspace,
  * minus the workspace.  The workspace mamba_scan_fwd_workspace_size reports for these sizes
  * is taken from a device array the library holds on every device it runs on (reserved when
  * the library's code is loaded, kept until the process ends); the call itself allocates and
- * frees nothing.  Limit: that size must be at most MAMBA_SCAN_NOALLOC_MAX_WORKSPACE (16 MiB:
- * the large prefill 8 x 4096 x 5120 needs 4.7 MiB, the long sequence 1 x 131072 x 2048
- * 12.6 MiB), else MAMBA_ERR_WORKSPACE and nothing is launched.  The array belongs to the
+ * frees nothing.  Limit: that size must be at most MAMBA_SCAN_NOALLOC_MAX_WORKSPACE (64 MiB:
+ * the large prefill 8 x 4096 x 5120 needs 4.5 MiB, the long sequence 1 x 131072 x 2048
+ * 40 MiB), else MAMBA_ERR_WORKSPACE and nothing is launched.  The array belongs to the
  * device of `stream` (the current device for NULL); all calls on one device share it, so
  * calls that overlap on one device race and must be serialised by the caller (for example
  * by issuing them on one stream).  Results are those of mamba_scan_fwd, bitwise.  Errors as
  * mamba_scan_fwd; MAMBA_ERR_HIP if the array's address cannot be looked up.
  */
-#define MAMBA_SCAN_NOALLOC_MAX_WORKSPACE ((size_t)16 << 20)
+#define MAMBA_SCAN_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
 MAMBA_API mamba_status_t mamba_scan_fwd_noalloc(const void *u, const void *delta,
                                                 const float *A, const void *B, const void *C,
                                                 const float *D, const void *z,

@@ -370,7 +370,7 @@ def mamba_scan_fwd_relay_faults(workspace, batch: int, seqlen: int, d_inner: int
     return int(out.value)
 
 
-NOALLOC_MAX_WORKSPACE = 16 << 20  # MAMBA_SCAN_NOALLOC_MAX_WORKSPACE
+NOALLOC_MAX_WORKSPACE = 64 << 20  # MAMBA_SCAN_NOALLOC_MAX_WORKSPACE
 
 
 def mamba_scan_fwd_noalloc(u, delta, A, B, C, *, out, D=None, z=None, delta_bias=None,

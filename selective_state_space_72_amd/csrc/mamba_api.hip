@@ -15,16 +15,17 @@ using namespace mambascan;
 
 namespace {
 
-// Kernel family used when the caller does not choose one: the scalar-B/C kernel when
-// the channels alone give every SIMD several waves (no sequence split), else the
-// barrier-free row kernel with a sequence split (fastest measured there); d_state 64,
-// which the scalar kernel does not compile, uses the row kernel too.
+// Kernel family used when the caller does not choose one: the scalar-B/C kernel for
+// d_state up to 32 (with or without a sequence split: measured fastest or equal on the
+// small prefill and the long sequence, 104 us against 108 us and 1.71 ms against 1.82 ms
+// at the best span count of each); d_state 64, which it does not compile, uses the
+// barrier-free row kernel.
 Family auto_family(int64_t batch, int64_t d_inner, int64_t d_state, int cus)
 {
-    const int64_t scalar_waves = batch * ((d_inner + 63) / 64) * 8;
-    if (d_state <= 32 && scalar_waves * 2 >= (int64_t)cus * 4 * 4)
-        return Family::Scalar;
-    return Family::Rows;
+    (void)batch;
+    (void)d_inner;
+    (void)cus;
+    return d_state <= 32 ? Family::Scalar : Family::Rows;
 }
 
 // Scalar-family defaults: (waves, chunk) = (4, 8), (8, 8), (8, 8), (8, 4) for d_state 4..32.
@@ -172,8 +173,14 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
         const int64_t waves_per_span = tiles * p.waves;
         const int64_t want = (int64_t)cus * 4 /*SIMDs*/ * 4 /*waves each*/;
         if (waves_per_span * 2 < want) {
+            // A split sequence runs the END pass over (S - 1) / S of it whatever S is, so
+            // once split, spans are cheap: the scalar kernel takes enough for ~12 waves per
+            // SIMD (span-count sweep: long sequence 2.13 / 1.87 / 1.71 ms at 16 / 32 / 64
+            // spans; small prefill 139 / 104 / 107 us at 4 / 8 / 16, capped there by the
+            // 256-step minimum span), the row kernel enough for 4.
+            const int64_t target = p.family == Family::Scalar ? want * 3 : want;
             int64_t s = 1;
-            while (s * waves_per_span < want && s < 64)
+            while (s * waves_per_span < target && s < 64)
                 s <<= 1;
             const int64_t by_len = seqlen / 256;
             if (s > by_len)
@@ -444,13 +451,19 @@ mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, const float *
                               stream);
 }
 
-mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float *A,
-                                  const void *B, const void *C, const float *D, const void *z,
-                                  const float *delta_bias, const float *h0, void *y,
-                                  float *h_last, int64_t batch, int64_t seqlen, int64_t d_inner,
-                                  int64_t d_state, mamba_dtype_t dtype, void *workspace,
-                                  size_t workspace_bytes, const mamba_scan_opts_t *opts,
-                                  const mamba_scan_ext_t *ext, void *stream)
+} // extern "C"
+
+// The forward scan: argument checks, then the launches.  check_only: run every check that
+// does not involve the workspace and return before touching the device (the allocation-
+// free entry point validates this way before it looks up its device array).
+static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const float *A,
+                                    const void *B, const void *C, const float *D, const void *z,
+                                    const float *delta_bias, const float *h0, void *y,
+                                    float *h_last, int64_t batch, int64_t seqlen,
+                                    int64_t d_inner, int64_t d_state, mamba_dtype_t dtype,
+                                    void *workspace, size_t workspace_bytes,
+                                    const mamba_scan_opts_t *opts, const mamba_scan_ext_t *ext,
+                                    void *stream, bool check_only)
 {
     const void *lam = ext ? ext->lambda : nullptr;
     const void *u_prev = lam ? ext->u_prev : nullptr; // used by the trapezoid only
@@ -496,9 +509,9 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     if (ps != MAMBA_OK)
         return ps;
     const size_t need = workspace_bytes_for(batch, seqlen, d_inner, d_state, plan);
-    if (need > 0 && (!workspace || workspace_bytes < need))
+    if (!check_only && need > 0 && (!workspace || workspace_bytes < need))
         return MAMBA_ERR_WORKSPACE;
-    if (need > 0 && !aligned(workspace, 4))
+    if (!check_only && need > 0 && !aligned(workspace, 4))
         return MAMBA_ERR_MISALIGNED;
 
     // ---- aliasing ----
@@ -512,7 +525,7 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     const Range r_h0 = range_of(h0, bdn * 4);
     const Range r_y = range_of(has_seq ? y : nullptr, bld * es);
     const Range r_hl = range_of(h_last, bdn * 4);
-    const Range r_ws = range_of(need > 0 ? workspace : nullptr, (int64_t)need);
+    const Range r_ws = range_of(need > 0 && !check_only ? workspace : nullptr, (int64_t)need);
     const int64_t ckb = ckpt ? ckpt_bytes(batch, seqlen, d_inner, d_state) : 0;
     if (ckb < 0)
         return MAMBA_ERR_BAD_SHAPE;
@@ -527,6 +540,8 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
         return MAMBA_ERR_ALIASING;
     if (overlaps(r_hl, r_h0) && (const void *)h_last != (const void *)h0)
         return MAMBA_ERR_ALIASING;
+    if (check_only)
+        return MAMBA_OK;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
@@ -646,6 +661,32 @@ mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float 
     L.first_span = 0;
     L.launch_spans = (int32_t)S;
     return hip_status(full(L));
+}
+
+// Checks of mamba_scan_fwd short of the workspace (for mamba_scan_fwd_noalloc).
+mamba_status_t mamba_scan_fwd_check(const void *u, const void *delta, const float *A,
+                                    const void *B, const void *C, const float *D, const void *z,
+                                    const float *delta_bias, const float *h0, void *y,
+                                    float *h_last, int64_t batch, int64_t seqlen,
+                                    int64_t d_inner, int64_t d_state, mamba_dtype_t dtype)
+{
+    return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, h0, y, h_last, batch, seqlen,
+                         d_inner, d_state, dtype, nullptr, 0, nullptr, nullptr, nullptr, true);
+}
+
+extern "C" {
+
+mamba_status_t mamba_scan_fwd_ext(const void *u, const void *delta, const float *A,
+                                  const void *B, const void *C, const float *D, const void *z,
+                                  const float *delta_bias, const float *h0, void *y,
+                                  float *h_last, int64_t batch, int64_t seqlen, int64_t d_inner,
+                                  int64_t d_state, mamba_dtype_t dtype, void *workspace,
+                                  size_t workspace_bytes, const mamba_scan_opts_t *opts,
+                                  const mamba_scan_ext_t *ext, void *stream)
+{
+    return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, h0, y, h_last, batch, seqlen,
+                         d_inner, d_state, dtype, workspace, workspace_bytes, opts, ext, stream,
+                         false);
 }
 
 // Reads one fault word of a workspace back to the host (synchronises the stream).

@@ -12,6 +12,13 @@
 #include <mutex>
 #include <stdint.h>
 
+// Argument checks of mamba_scan_fwd short of the workspace (mamba_api.hip; not exported).
+mamba_status_t mamba_scan_fwd_check(const void *u, const void *delta, const float *A,
+                                    const void *B, const void *C, const float *D, const void *z,
+                                    const float *delta_bias, const float *h0, void *y,
+                                    float *h_last, int64_t batch, int64_t seqlen,
+                                    int64_t d_inner, int64_t d_state, mamba_dtype_t dtype);
+
 namespace {
 
 constexpr size_t kScratchBytes = MAMBA_SCAN_NOALLOC_MAX_WORKSPACE; // per device
@@ -58,10 +65,15 @@ mamba_status_t mamba_scan_fwd_noalloc(const void *u, const void *delta, const fl
                                       int64_t d_inner, int64_t d_state, mamba_dtype_t dtype,
                                       void *stream)
 {
+    // every check first, before anything touches the device
+    const mamba_status_t chk = mamba_scan_fwd_check(u, delta, A, B, C, D, z, delta_bias, h0, y,
+                                                    h_last, batch, seqlen, d_inner, d_state,
+                                                    dtype);
+    if (chk != MAMBA_OK)
+        return chk;
     const size_t need = mamba_scan_fwd_workspace_size(batch, seqlen, d_inner, d_state);
-    if (need == (size_t)-1) // let the full validation name the problem
-        return mamba_scan_fwd(u, delta, A, B, C, D, z, delta_bias, h0, y, h_last, batch, seqlen,
-                              d_inner, d_state, dtype, nullptr, 0, stream);
+    if (need == (size_t)-1)
+        return MAMBA_ERR_BAD_SHAPE;
     if (need > kScratchBytes)
         return MAMBA_ERR_WORKSPACE;
     void *ws = nullptr;

@@ -66,6 +66,10 @@ def scan(lib, *, u=BASE, delta=BASE + 64 * MB, A=BASE + 128 * MB, B=BASE + 132 *
          C=BASE + 136 * MB, D=None, z=None, bias=None, h0=None, y=BASE + 256 * MB,
          h_last=None, batch=2, L=64, Dn=128, N=16, dtype=BF16, ws=None, ws_bytes=0,
          opts=None):
+    # validation cases below use the row kernel unless they choose: it needs no workspace at
+    # these sizes, so the checks under test are the ones that fail
+    if opts is None and ws is None:
+        opts = ms.ScanOpts(0, 0, 0, 2)
     o = ctypes.byref(opts) if opts is not None else None
     return lib.mamba_scan_fwd_ex(u, delta, A, B, C, D, z, bias, h0, y, h_last, batch, L, Dn, N,
                                  dtype, ws, ws_bytes, o, None)
@@ -620,10 +624,13 @@ def test_noalloc_rejects_before_touching_the_device(lib):
     """The allocation-free entry point validates like mamba_scan_fwd and refuses sizes whose
     workspace exceeds its per-device array, before anything runs on the device."""
     cap = ms.NOALLOC_MAX_WORKSPACE
-    # a long sequence with d_state 32: its span summaries (24 MiB) exceed the array
+    # a long sequence with d_state 32: its span summaries (80 MiB) exceed the array
     big = lib.mamba_scan_fwd_workspace_size(1, 131072, 2048, 32)
     assert big > cap
-    assert noalloc(lib, batch=1, L=131072, Dn=2048, N=32) == WS
+    GB = 1 << 30
+    assert noalloc(lib, batch=1, L=131072, Dn=2048, N=32, u=BASE, delta=BASE + GB,
+                   A=BASE + 2 * GB, B=BASE + 3 * GB, C=BASE + 4 * GB, y=BASE + 5 * GB) == WS
+    assert lib.mamba_scan_fwd_workspace_size(1, 131072, 2048, 16) <= cap  # the long sequence fits
     assert lib.mamba_scan_fwd_workspace_size(8, 4096, 5120, 16) <= cap  # the large prefill fits
     assert noalloc(lib, batch=-1) == lib.mamba_scan_fwd(
         BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 132 * MB, BASE + 136 * MB, None, None,
