@@ -75,18 +75,24 @@ def sampled_check(name, cfg, bs, ds, gate):
     check(name, from_dev(y), from_dev(h), yr, hr, inp.dtype)
 
 
-def test_c3_large_prefill_sampled():
+def test_c3_large_prefill_full():
+    """Every output and final-state element of the large prefill (8 x 4096 x 5120, bf16,
+    gated) in the launch configuration the benchmark times, against the threaded oracle."""
+    full_check("c3", synth.make_scan_inputs(synth.CONFIGS["c3"]), gate=True)
+
+
+def test_c4_long_sequence_full():
+    """Every element of the long sequence (1 x 131072 x 2048, h0, no gate): split into spans
+    joined by the carry pass, as the benchmark runs it."""
+    full_check("c4", synth.make_scan_inputs(synth.CONFIGS["c4"]), gate=False)
+
+
+def test_c3_sampled_rows_and_edges():
+    """Channel tile edges and the relayed units' boundary channels of the large prefill."""
     cfg = synth.CONFIGS["c3"]
     rng = np.random.default_rng(1)
     ds = np.unique(np.concatenate([[0, 63, 64, 5119], rng.choice(cfg.d_inner, 44, replace=False)]))
-    sampled_check("c3", cfg, np.array([0, 3, 7]), ds, gate=True)
-
-
-def test_c4_long_sequence_sampled():
-    cfg = synth.CONFIGS["c4"]
-    rng = np.random.default_rng(2)
-    ds = np.unique(np.concatenate([[0, 2047], rng.choice(cfg.d_inner, 22, replace=False)]))
-    sampled_check("c4", cfg, np.array([0]), ds, gate=False)
+    sampled_check("c3 sampled", cfg, np.array([0, 3, 7]), ds, gate=True)
 
 
 def test_c5_decode_1024_chained_steps():
