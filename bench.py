@@ -99,6 +99,9 @@ def parse():
     ap.add_argument("--ssd-only", action="store_true",
                     help="time only the Mamba-2 SSD scan on its large shape (for profiling) and "
                          "print its JSON summary")
+    ap.add_argument("--workload", choices=("c2", "c3", "c4"),
+                    help="time only this prefill workload (small prefill, large prefill, long "
+                         "sequence) and print its JSON summary (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB device copy three times (the reference kernel for "
                          "scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -607,6 +610,19 @@ def main():
     torch.cuda.set_device(dev)
 
     cfg = synth.CONFIGS["c3"]
+    if args.workload:
+        wcfg = synth.CONFIGS[args.workload]
+        log(f"bench: {wcfg.desc} only")
+        case = ScanCase(wcfg, dev)
+        loop_ms, _, _ = time_steps(case.step, args.steps, args.warmup, warm_ms=100.0)
+        if args.copy_calibration:
+            copy_calibration(dev)
+        print(json.dumps({"workload": f"{wcfg.desc}: batch {wcfg.batch}, L {wcfg.seqlen}, "
+                                      f"d_inner {wcfg.d_inner}, d_state {wcfg.d_state}",
+                          "steps": args.steps, "ms_per_step": round(loop_ms, 4),
+                          "min_bytes_per_step": case.min_bytes,
+                          "GB_s": round(case.min_bytes / (loop_ms * 1e-3) / 1e9, 1)}), flush=True)
+        return
     if args.ssd_only:
         log("bench: SSD scan on its large shape")
         res = ssd_workload(dev, make_flush(dev), args.steps)
