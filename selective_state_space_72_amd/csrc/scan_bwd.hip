@@ -24,11 +24,14 @@
 // through LDS, as are B and C (a wave loads its segment's values with one load per lane,
 // a segment ahead, and reads them back as broadcasts).  The per-wave partial sums over
 // state indices (readout, sum mu B, sum A mu Abar h) are summed across waves through LDS
-// in a fixed order.  dB and dC need sums over the block's 64 channels (the lanes): each
-// wave reduces its values of 8 steps with a transposed butterfly (every exchange halves
-// the values a lane holds, so 2*NQ*8 sums across 64 lanes cost about three VALU
-// operations per value) and writes one partial per (tile, t, n); a second kernel sums the
-// tiles, and dA, dD, dbias over the batch rows and spans.
+// in a fixed order.  dB and dC need sums over the block's 64 channels (the lanes), one per
+// (step, state index) and wave; each wave writes one partial per (tile, t, n) and a second
+// kernel sums the tiles, and dA, dD, dbias over the batch rows and spans.  The sums over
+// lanes go either through LDS (LR: every 16 values per lane the wave writes them as rows
+// of a slab, each lane adds 16 entries of one row and two lane exchanges join the row's
+// four quarters -- about one VALU operation per value) or through a transposed butterfly
+// in registers (every exchange halves the values a lane holds, about three operations per
+// value, but no LDS).
 //
 // When the (batch row, tile) units are too few to fill the device, the sequence is split
 // into spans that run as separate blocks: the forward span pass and carry give the state
@@ -98,6 +101,20 @@ __device__ __forceinline__ float halve(float lo, float hi, int lane)
     return keep + partner<BIT>(send);
 }
 
+// v + v of lane ^ 16, then + the same of lane ^ 32: the sum over the four lanes l % 16
+// (every lane gets it, in the same order).  v_permlane16_swap / v_permlane32_swap given
+// two copies of v exchange rows 0 <-> 1 and 2 <-> 3, resp. the wave's halves, between
+// them, so the two results hold v of the lane and of its partner.
+__device__ __forceinline__ float lane_pair_sum(float v)
+{
+    const uint32_t x = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    const float a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const uint32_t y = __float_as_uint(a);
+    const auto r2 = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+    return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+
 template <typename T>
 __device__ __forceinline__ T zero_val()
 {
@@ -106,10 +123,11 @@ __device__ __forceinline__ T zero_val()
 
 // AB: keep the segment's decay factors in registers (else recompute them in the adjoint
 // sweep, one more exp per element, to save S * NQ registers).  WPE: waves per SIMD the
-// register allocation targets.  CKE: the checkpoints hold every segment's entering state
+// register allocation targets.  LR: the dB/dC lane sums through an LDS slab per wave (16
+// rows of 64 lanes; else the register butterfly).  CKE: the checkpoints hold every segment's entering state
 // already (written by the forward scan): no forward pass here, and a later span's entering
 // state is its first checkpoint.
-template <typename T, int N, int NW, int S, bool AB, int WPE, bool GATED, bool CKE = false>
+template <typename T, int N, int NW, int S, bool AB, int WPE, bool LR, bool GATED, bool CKE>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 scan_bwd_kernel(BwdArgs p)
 {
@@ -128,6 +146,11 @@ scan_bwd_kernel(BwdArgs p)
     __shared__ float4 s_in[S][64];       // Delta, Delta*u, ds per (step, channel)
     __shared__ float s_p[3][RH][NW][64]; // readout, sum mu B, sum A mu Abar h per wave
     __shared__ float s_bc[NW][S * BCW];  // this segment's B, C per wave: [step][B(NQ), C(NQ)]
+    // LR: per wave 16 rows (a group of 16 / BCW steps' values) of 64 lanes, padded by 16
+    // bytes so that the row reads below (16 consecutive lanes of one row per lane, rows
+    // lane % 16) fall in distinct banks
+    constexpr int kRow = 68;
+    __shared__ float s_r[LR ? NW : 1][LR ? 16 * kRow : 1];
 
     const int lane = threadIdx.x & 63;
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -386,8 +409,32 @@ scan_bwd_kernel(BwdArgs p)
                 s_p[1][tl][g][lane] = p1;
                 s_p[2][tl][g][lane] = p2;
 
-                // butterfly over the steps of this part: step bit 0, 1, 2 on lane bit 3, 2, 1
-                if (tl & 1) {
+                if constexpr (LR) {
+                    // rows (tl % GS) * BCW + i of the slab; after the group's first step
+                    // (the loop runs backwards) lane l sums row l % 16 over lanes
+                    // 16 (l / 16) .. + 15, and the four quarters are joined across lanes
+                    // (lane permutes: no LDS round trip)
+                    constexpr int GS = 16 / BCW;
+                    float *slab = &s_r[LR ? g : 0][0];
+#pragma unroll
+                    for (int i = 0; i < BCW; ++i)
+                        slab[((tl % GS) * BCW + i) * kRow + lane] = xv[i];
+                    if (tl % GS == 0) {
+                        const float4 *src = reinterpret_cast<const float4 *>(
+                            slab + (lane & 15) * kRow + (lane >> 4) * 16);
+                        const float4 c0 = src[0], c1 = src[1], c2 = src[2], c3 = src[3];
+                        float v = ((c0.x + c0.y) + (c0.z + c0.w)) + ((c1.x + c1.y) + (c1.z + c1.w));
+                        v += ((c2.x + c2.y) + (c2.z + c2.w)) + ((c3.x + c3.y) + (c3.z + c3.w));
+                        v = lane_pair_sum(v);
+                        const int o = lane & 15, j = o % BCW;
+                        const int64_t t = t0 + part * RH + tl + o / BCW;
+                        if (lane < 16 && (!PARTIAL || t < L)) {
+                            const int kind = j / NQ, q = j % NQ;
+                            p.dbc_part[((int64_t)unit * L + t) * (2 * N) + kind * N + n0 + q] = v;
+                        }
+                    }
+                } else if (tl & 1) {
+                    // butterfly over the steps of this part: step bit 0, 1, 2 on lane bit 3, 2, 1
 #pragma unroll
                     for (int i = 0; i < BCW; ++i)
                         pend[i] = xv[i];
@@ -409,6 +456,7 @@ scan_bwd_kernel(BwdArgs p)
                 }
             }
             // value bits (kind, state) on lane bits 0, 4, 5; the remaining lane bits sum
+            if constexpr (!LR) {
             float v;
             if constexpr (BCW == 2) {
                 v = halve<0>(r3[0], r3[1], lane);
@@ -448,6 +496,7 @@ scan_bwd_kernel(BwdArgs p)
                     const int kind = j / NQ, q = j % NQ;
                     p.dbc_part[((int64_t)unit * L + t) * (2 * N) + kind * N + n0 + q] = v;
                 }
+            }
             }
             __syncthreads();
 
@@ -717,12 +766,12 @@ bwd_reduce_params_kernel(const float *__restrict__ dA_part, const float *__restr
 // are all resident: 4.01 ms against 4.50 ms for 8 waves of 2 state indices with stored
 // decay factors (119 VGPRs but 58 KB LDS: two blocks per CU) at 8 x 4096 x 5120.
 #define MAMBA_BWD_VARIANTS(X)        \
-    X(4, 4, 8, true, 4)              \
-    X(8, 8, 8, true, 4)              \
-    X(16, 4, 8, false, 3)            \
-    X(32, 8, 8, true, 2)
+    X(4, 4, 8, true, 4, false)       \
+    X(8, 8, 8, true, 4, false)       \
+    X(16, 4, 8, false, 3, true)      \
+    X(32, 8, 8, true, 2, false)
 
-template <typename T, int N, int NW, int S, bool AB, int WPE>
+template <typename T, int N, int NW, int S, bool AB, int WPE, bool LR>
 hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
 {
     const int64_t tiles = (q.d_inner + 63) / 64;
@@ -794,16 +843,16 @@ hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
     const dim3 grid((uint32_t)(units * q.n_spans));
     if (q.ck_ext) {
         if (gated)
-            hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, true, true>), grid,
+            hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, LR, true, true>), grid,
                                dim3(64 * NW), 0, stream, a);
         else
-            hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, false, true>), grid,
+            hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, LR, false, true>), grid,
                                dim3(64 * NW), 0, stream, a);
     } else if (gated) {
-        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, true>), grid, dim3(64 * NW), 0,
+        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, LR, true, false>), grid, dim3(64 * NW), 0,
                            stream, a);
     } else {
-        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, false>), grid, dim3(64 * NW), 0,
+        hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, LR, false, false>), grid, dim3(64 * NW), 0,
                            stream, a);
     }
     if ((e = hipGetLastError()) != hipSuccess)
@@ -827,7 +876,7 @@ hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
 
 bool bwd_variant(int64_t d_state, int *waves, int *seg_len)
 {
-#define X(N_, W_, S_, AB_, WPE_)      \
+#define X(N_, W_, S_, AB_, WPE_, LR_)      \
     if (d_state == N_) {              \
         *waves = W_;                  \
         *seg_len = S_;                \
@@ -840,11 +889,11 @@ bool bwd_variant(int64_t d_state, int *waves, int *seg_len)
 
 hipError_t launch_scan_bwd(const BwdLaunch &q, hipStream_t stream)
 {
-#define X(N_, W_, S_, AB_, WPE_)                                             \
+#define X(N_, W_, S_, AB_, WPE_, LR_)                                             \
     if (q.d_state == N_) {                                                  \
         if (q.dtype == DType::BF16)                                         \
-            return launch_bwd_t<uint16_t, N_, W_, S_, AB_, WPE_>(q, stream); \
-        return launch_bwd_t<float, N_, W_, S_, AB_, WPE_>(q, stream);        \
+            return launch_bwd_t<uint16_t, N_, W_, S_, AB_, WPE_, LR_>(q, stream); \
+        return launch_bwd_t<float, N_, W_, S_, AB_, WPE_, LR_>(q, stream);        \
     }
     MAMBA_BWD_VARIANTS(X)
 #undef X

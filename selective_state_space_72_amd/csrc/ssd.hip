@@ -300,17 +300,20 @@ ssd_chunk_kernel(SsdArgs p)
 
     // ---- state slab: tile m holds rows n = 16m + 4g + v, column pc ----
     f32x4 hacc[NT];
-    const int64_t hrow = ((int64_t)b * Dn + (int64_t)h * P + pc) * N;
-    // (the span arrays share this layout: unit bh = b * H + h holds P rows of N at hrow)
+    // row pc of this unit's P x N state block: a uniform base plus a 32-bit lane offset
+    // (one register to keep across the chunk loop for the final stores, not a 64-bit index)
+    const int64_t hbase = ((int64_t)b * Dn + (int64_t)h * P) * N;
+    const int hcol = pc * N;
+    // (the span arrays share this layout: unit bh = b * H + h holds P rows of N at hbase)
     const int64_t sp_stride = (int64_t)p.units * P * N;
     if (p.h0 && part != 1 && span == 0) {
 #pragma unroll
         for (int m = 0; m < NT; ++m)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                hacc[m][v] = p.h0[hrow + 16 * m + 4 * g + v];
+                hacc[m][v] = p.h0[hbase + hcol + 16 * m + 4 * g + v];
     } else if (!END && span > 0) { // the state entering this span, from the carry
-        const float *src = p.sp + (int64_t)(span - 1) * sp_stride + hrow;
+        const float *src = p.sp + (int64_t)(span - 1) * sp_stride + hbase + hcol;
 #pragma unroll
         for (int m = 0; m < NT; ++m)
 #pragma unroll
@@ -452,7 +455,7 @@ ssd_chunk_kernel(SsdArgs p)
         for (int m = 0; m < NT; ++m)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                hacc[m][v] = got ? p.r_state[((int64_t)slot * P + pc) * N + 16 * m + 4 * g + v]
+                hacc[m][v] = got ? (p.r_state + (int64_t)slot * P * N)[hcol + 16 * m + 4 * g + v]
                                  : __builtin_nanf("");
     }
     float decp = 1.0f; // END: the span's total decay, the product of its chunks'
@@ -628,7 +631,7 @@ ssd_chunk_kernel(SsdArgs p)
 
     if constexpr (END) {
         // the span's final state and total decay, for the carry
-        float *dst = p.sp + (int64_t)span * sp_stride + hrow;
+        float *dst = p.sp + (int64_t)span * sp_stride + hbase + hcol;
 #pragma unroll
         for (int m = 0; m < NT; ++m)
 #pragma unroll
@@ -646,7 +649,7 @@ ssd_chunk_kernel(SsdArgs p)
         for (int m = 0; m < NT; ++m)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                p.r_state[((int64_t)slot * P + pc) * N + 16 * m + 4 * g + v] = hacc[m][v];
+                (p.r_state + (int64_t)slot * P * N)[hcol + 16 * m + 4 * g + v] = hacc[m][v];
         relay_signal(p.r_sync + slot);
         return;
     }
@@ -655,7 +658,7 @@ ssd_chunk_kernel(SsdArgs p)
         for (int m = 0; m < NT; ++m)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                p.h_last[hrow + 16 * m + 4 * g + v] = hacc[m][v];
+                (p.h_last + hbase)[hcol + 16 * m + 4 * g + v] = hacc[m][v];
     }
 }
 
