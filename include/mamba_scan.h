@@ -74,14 +74,23 @@ typedef enum {
     MAMBA_ERR_NULL_ARG = 1,     /* a required pointer is NULL                       */
     MAMBA_ERR_BAD_SHAPE = 2,    /* negative size, or sizes whose products overflow  */
     MAMBA_ERR_BAD_DTYPE = 3,    /* dtype is not a mamba_dtype_t value               */
-    MAMBA_ERR_UNSUPPORTED = 4,  /* d_state not compiled in, or an unsupported option */
+    MAMBA_ERR_UNSUPPORTED = 4,  /* d_state out of range, or an unsupported option    */
     MAMBA_ERR_MISALIGNED = 5,   /* a pointer is not aligned to its element size     */
     MAMBA_ERR_ALIASING = 6,     /* an output overlaps an input or another output    */
     MAMBA_ERR_WORKSPACE = 7,    /* workspace missing or smaller than required       */
     MAMBA_ERR_HIP = 8           /* a HIP runtime call or kernel launch failed       */
 } mamba_status_t;
 
-/* d_state values compiled into the library. */
+/* Largest d_state of the selective scan.  The kernels are compiled for d_state 4, 8, 16,
+ * 32 and 64; any other d_state from 1 to 64 runs at the next of those sizes: the arrays
+ * indexed by the state index (A, B, C, h0 and the Mamba-3 theta, B_prev) are copied into the
+ * workspace as rows of the larger size, the extra entries of A -1 and all others 0, so the
+ * extra states start at zero, receive zero input, stay exactly zero and add exactly zero
+ * to every readout; results indexed by the state (h_last, dB, dC, dA, dh0) are copied back
+ * to rows of the caller's size.  Those calls need the workspace the size queries report
+ * (larger than at the compiled size) and cost what the compiled size costs, plus the
+ * copies.  The decode step needs no workspace: it runs the state indices of such a size
+ * in the lanes of the next compiled size. */
 #define MAMBA_MAX_D_STATE 64
 
 /* Kernel families (mamba_scan_opts_t.kernel). */
@@ -141,7 +150,8 @@ typedef struct {
 #define MAMBA_DISC_EULER 0
 #define MAMBA_DISC_ZOH 1
 
-/* Returns 1 if d_state is supported by this build, else 0. */
+/* Returns 1 if the selective scan and its decode step take this d_state (1..64), else 0.
+ * (The backward pass takes 1..32; the SSD has its own sizes, mamba_ssd_supported.) */
 MAMBA_API int32_t mamba_d_state_supported(int64_t d_state);
 
 /*
@@ -212,8 +222,9 @@ MAMBA_API mamba_status_t mamba_scan_fwd_ex(const void *u, const void *delta, con
  *   delta_bias (d_inner) float32                     nullable
  *   y          (batch, d_inner) dtype                output, required
  *
- * Alignment: h and A must be 16-byte aligned (each lane moves 4 state values
- * at once); the other pointers as for every entry point.
+ * Alignment: for d_state 4, 8, 16, 32 and 64, h and A must be 16-byte aligned (each
+ * lane moves 4 state values at once); for other sizes 4-byte aligned.  The other
+ * pointers as for every entry point.
  * Aliasing: y and h must not overlap each other or any input.
  */
 MAMBA_API mamba_status_t mamba_state_update(float *h, const void *u, const void *delta, const float *A,
@@ -318,8 +329,9 @@ MAMBA_API mamba_status_t mamba_state_update_ex(float *h, const void *u, const vo
  *
  * Outputs are written, not accumulated.  Sums over channels, batch rows and time are
  * formed in float32 in a fixed order (results are bitwise reproducible); outputs in
- * dtype are rounded to nearest even.  d_state must be 4, 8, 16 or 32
- * (MAMBA_ERR_UNSUPPORTED otherwise).  With seqlen == 0 only dh0 (= dh_last, or 0),
+ * dtype are rounded to nearest even.  d_state must be in 1..32 (4, 8, 16, 32 run as
+ * compiled, the others padded as described at MAMBA_MAX_D_STATE; MAMBA_ERR_UNSUPPORTED
+ * otherwise).  With seqlen == 0 only dh0 (= dh_last, or 0),
  * dA, dD and d_delta_bias (0) are written.  Aliasing: no output may overlap an input
  * or another output, and the workspace overlaps nothing (MAMBA_ERR_ALIASING).
  * Other conventions as for every entry point.
@@ -362,8 +374,9 @@ MAMBA_API mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, con
                                            const mamba_scan_opts_t *opts, void *stream);
 
 /* Bytes of the checkpoint buffer that mamba_scan_fwd_ext writes (ext->ckpt) and
- * mamba_scan_bwd_ckpt reads: (batch * ceil(d_inner / 64)) * ceil(seqlen / 8) * d_state *
- * 64 * 4.  SIZE_MAX for negative sizes, overflow or a d_state other than 4, 8, 16, 32. */
+ * mamba_scan_bwd_ckpt reads: (batch * ceil(d_inner / 64)) * ceil(seqlen / 8) * n * 64 * 4,
+ * n the compiled size d_state runs at (4, 8, 16 or 32: the next one up).  SIZE_MAX for
+ * negative sizes, overflow or a d_state outside 1..32. */
 MAMBA_API size_t mamba_scan_ckpt_size(int64_t batch, int64_t seqlen, int64_t d_inner,
                                       int64_t d_state);
 
@@ -411,8 +424,8 @@ MAMBA_API mamba_status_t mamba_scan_bwd_ckpt(const void *u, const void *delta, c
  *       data-dependent rotation: h_t = exp(Delta_t A) R(Delta_t theta_t) h_{t-1} + (input
  *       term), where R turns each state pair (2k, 2k+1) by the angle
  *       Delta_t * theta[b,t,k]: (x, w) -> (cos x - sin w, sin x + cos w), before the decay.
- *       d_state must be even; in the scan it needs d_state 16 or 32 (state pairs within
- *       one wave), else MAMBA_ERR_UNSUPPORTED.  A split sequence (n_spans > 1) carries
+ *       d_state must be even; in the scan it needs an even d_state from 10 to 32 (run at
+ *       16 or 32, where a wave holds whole state pairs), else MAMBA_ERR_UNSUPPORTED.  A split sequence (n_spans > 1) carries
  *       each pair's 2x2 transition over a span (the turn and the pair's two decays do not
  *       commute): more workspace (mamba_scan_fwd_workspace_size_ext) and span passes.
  *
@@ -427,7 +440,7 @@ MAMBA_API mamba_status_t mamba_scan_bwd_ckpt(const void *u, const void *delta, c
  *       64-channel tile), for mamba_scan_bwd_ckpt.  Its layout is internal to the
  *       library; it is written only, 4-byte aligned, and overlaps no other argument or
  *       the workspace (MAMBA_ERR_ALIASING).  Needs the Euler rule without lambda or
- *       theta and d_state 4, 8, 16 or 32, and runs in the SCALAR family (else
+ *       theta and d_state 1..32, and runs in the SCALAR family (else
  *       MAMBA_ERR_UNSUPPORTED).  It does not change y or h_last. */
 typedef struct {
     const void *lambda;

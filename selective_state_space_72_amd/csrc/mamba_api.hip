@@ -61,8 +61,88 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool mul_ok(int64_t a, int64_t b, int64_t *out) { return !__builtin_mul_overflow(a, b, out); }
 
+// d_state values the scan kernels are compiled for; any other d_state in 1..64 runs at the
+// next compiled size with the state arrays padded (pad.hip), padded_d_state giving that size
+// (0: not supported).
 bool d_state_ok(int64_t n) { return n == 4 || n == 8 || n == 16 || n == 32 || n == 64; }
 bool bwd_d_state_ok(int64_t n) { return n == 4 || n == 8 || n == 16 || n == 32; }
+int64_t padded_d_state(int64_t n)
+{
+    if (n < 1 || n > 64)
+        return 0;
+    int64_t p = 4;
+    while (p < n)
+        p *= 2;
+    return p;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace prefix of a padded forward call: the padded copies of A, B, C, h0, theta,
+// B_prev and the padded final state, each 256-byte aligned (h0 and the final state always
+// reserved: the size query does not know whether they are given).
+struct FwdPad {
+    size_t a, b, c, h0, hl, theta, bprev, total;
+};
+
+bool fwd_pad_layout(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t np, int64_t es,
+                    bool theta, bool bprev, FwdPad *f)
+{
+    int64_t a, bl, bd, t;
+    if (!mul_ok(d_inner, np * 4, &a) || !mul_ok(batch, seqlen, &t) || !mul_ok(t, np * es, &bl) ||
+        !mul_ok(batch, d_inner, &t) || !mul_ok(t, np * 4, &bd))
+        return false;
+    size_t o = 0;
+    f->a = o;
+    o += align256((size_t)a);
+    f->b = o;
+    o += align256((size_t)bl);
+    f->c = o;
+    o += align256((size_t)bl);
+    f->h0 = o;
+    o += align256((size_t)bd);
+    f->hl = o;
+    o += align256((size_t)bd);
+    f->theta = o;
+    if (theta)
+        o += align256((size_t)bl / 2);
+    f->bprev = o;
+    if (bprev)
+        o += align256((size_t)(batch * np * es));
+    f->total = o;
+    return true;
+}
+
+// Workspace prefix of a padded backward call: the padded copies of A, B, C, h0, dh_last
+// and the padded gradients dB, dC, dA, dh0 (B/C-shaped slots sized for 4-byte elements:
+// the size query does not know the dtype).
+struct BwdPad {
+    size_t a, b, c, h0, dhl, db, dc, da, dh0, total;
+};
+
+bool bwd_pad_layout(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t np, BwdPad *f)
+{
+    int64_t a, bl, bd, t;
+    if (!mul_ok(d_inner, np * 4, &a) || !mul_ok(batch, seqlen, &t) || !mul_ok(t, np * 4, &bl) ||
+        !mul_ok(batch, d_inner, &t) || !mul_ok(t, np * 4, &bd))
+        return false;
+    size_t o = 0;
+    auto put = [&](size_t *slot, int64_t bytes) {
+        *slot = o;
+        o += align256((size_t)bytes);
+    };
+    put(&f->a, a);
+    put(&f->b, bl);
+    put(&f->c, bl);
+    put(&f->h0, bd);
+    put(&f->dhl, bd);
+    put(&f->db, bl);
+    put(&f->dc, bl);
+    put(&f->da, a);
+    put(&f->dh0, bd);
+    f->total = o;
+    return true;
+}
 
 // Bytes of the backward-pass checkpoints: (batch * channel tiles) x ceil(L / 8) segments x
 // d_state x 64 lanes, fp32; -1 on overflow.
@@ -410,20 +490,30 @@ const char *mamba_status_string(mamba_status_t s)
     return "MAMBA_ERR_UNKNOWN";
 }
 
-int32_t mamba_d_state_supported(int64_t d_state) { return d_state_ok(d_state) ? 1 : 0; }
+int32_t mamba_d_state_supported(int64_t d_state) { return padded_d_state(d_state) ? 1 : 0; }
 
 size_t mamba_scan_fwd_workspace_size_ext(int64_t batch, int64_t seqlen, int64_t d_inner,
                                          int64_t d_state, const mamba_scan_ext_t *ext,
                                          const mamba_scan_opts_t *opts)
 {
     int64_t tmp;
+    const int64_t np = padded_d_state(d_state);
     if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 ||
-        !mul_ok(batch, d_inner, &tmp) || !mul_ok(tmp, d_state, &tmp) || !d_state_ok(d_state))
+        !mul_ok(batch, d_inner, &tmp) || !mul_ok(tmp, d_state, &tmp) || !np)
         return (size_t)-1;
     Plan p;
-    if (make_plan(batch, seqlen, d_inner, d_state, opts, ext, &p) != MAMBA_OK)
+    if (make_plan(batch, seqlen, d_inner, np, opts, ext, &p) != MAMBA_OK)
         return (size_t)-1;
-    return workspace_bytes_for(batch, seqlen, d_inner, d_state, p);
+    size_t pad = 0;
+    if (np != d_state && seqlen > 0) {
+        FwdPad f;
+        // (the dtype is not known here: room for 4-byte elements)
+        if (!fwd_pad_layout(batch, seqlen, d_inner, np, 4, ext && ext->theta,
+                            ext && ext->lambda && ext->B_prev, &f))
+            return (size_t)-1;
+        pad = f.total;
+    }
+    return pad + workspace_bytes_for(batch, seqlen, d_inner, np, p);
 }
 
 size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_inner,
@@ -475,8 +565,10 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
         return MAMBA_ERR_BAD_SHAPE;
     if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
         return MAMBA_ERR_BAD_DTYPE;
-    if (!d_state_ok(d_state))
+    const int64_t np = padded_d_state(d_state); // the compiled size the scan runs at
+    if (!np || (theta && d_state % 2 != 0))
         return MAMBA_ERR_UNSUPPORTED;
+    const bool padded = np != d_state;
     const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
     int64_t bld, bln, bdn, dn, t;
     if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, d_inner, &bld) || !mul_ok(bld, es, &t) ||
@@ -505,10 +597,14 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
 
     // ---- plan and workspace ----
     Plan plan;
-    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, d_state, opts, ext, &plan);
+    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, np, opts, ext, &plan);
     if (ps != MAMBA_OK)
         return ps;
-    const size_t need = workspace_bytes_for(batch, seqlen, d_inner, d_state, plan);
+    FwdPad pad{};
+    if (padded && seqlen > 0 &&
+        !fwd_pad_layout(batch, seqlen, d_inner, np, 4, theta != nullptr, B_prev != nullptr, &pad))
+        return MAMBA_ERR_BAD_SHAPE;
+    const size_t need = pad.total + workspace_bytes_for(batch, seqlen, d_inner, np, plan);
     if (!check_only && need > 0 && (!workspace || workspace_bytes < need))
         return MAMBA_ERR_WORKSPACE;
     if (!check_only && need > 0 && !aligned(workspace, 4))
@@ -526,7 +622,7 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
     const Range r_y = range_of(has_seq ? y : nullptr, bld * es);
     const Range r_hl = range_of(h_last, bdn * 4);
     const Range r_ws = range_of(need > 0 && !check_only ? workspace : nullptr, (int64_t)need);
-    const int64_t ckb = ckpt ? ckpt_bytes(batch, seqlen, d_inner, d_state) : 0;
+    const int64_t ckb = ckpt ? ckpt_bytes(batch, seqlen, d_inner, np) : 0;
     if (ckb < 0)
         return MAMBA_ERR_BAD_SHAPE;
     const Range r_ck = range_of(has_seq ? ckpt : nullptr, ckb);
@@ -552,6 +648,45 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
         return MAMBA_OK;
     }
 
+    char *ws_bytes = static_cast<char *>(workspace);
+    float *hl_run = h_last; // the final state as the kernels write it
+    if (padded) {
+        // the state arrays as rows of np entries at the front of the workspace
+        char *w = ws_bytes;
+        const int32_t n32 = (int32_t)d_state, np32 = (int32_t)np, es32 = (int32_t)es;
+        if (launch_pad_rows(w + pad.a, A, d_inner, n32, np32, 4, -1.0f, st) != hipSuccess ||
+            launch_pad_rows(w + pad.b, B, batch * seqlen, n32, np32, es32, 0.0f, st) != hipSuccess ||
+            launch_pad_rows(w + pad.c, C, batch * seqlen, n32, np32, es32, 0.0f, st) != hipSuccess)
+            return MAMBA_ERR_HIP;
+        A = reinterpret_cast<const float *>(w + pad.a);
+        B = w + pad.b;
+        C = w + pad.c;
+        if (h0) {
+            if (launch_pad_rows(w + pad.h0, h0, batch * d_inner, n32, np32, 4, 0.0f, st) !=
+                hipSuccess)
+                return MAMBA_ERR_HIP;
+            h0 = reinterpret_cast<const float *>(w + pad.h0);
+        }
+        if (h_last)
+            hl_run = reinterpret_cast<float *>(w + pad.hl);
+        if (theta) {
+            if (launch_pad_rows(w + pad.theta, theta, batch * seqlen, n32 / 2, np32 / 2, es32,
+                                0.0f, st) != hipSuccess)
+                return MAMBA_ERR_HIP;
+            theta = w + pad.theta;
+        }
+        if (B_prev) {
+            if (launch_pad_rows(w + pad.bprev, B_prev, batch, n32, np32, es32, 0.0f, st) !=
+                hipSuccess)
+                return MAMBA_ERR_HIP;
+            B_prev = w + pad.bprev;
+        }
+        ws_bytes += pad.total;
+    }
+    const int64_t N = np;              // the state size of every launch below
+    const int64_t bdk = batch * d_inner * N;
+
+    auto run = [&]() -> mamba_status_t {
     ScanLaunch L{};
     L.u = u;
     L.delta = delta;
@@ -562,11 +697,11 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
     L.D = D;
     L.bias = delta_bias;
     L.y = y;
-    L.h_last = h_last;
+    L.h_last = hl_run;
     L.batch = batch;
     L.L = seqlen;
     L.d_inner = d_inner;
-    L.d_state = d_state;
+    L.d_state = N;
     L.span_len = plan.span_len;
     L.n_spans = plan.n_spans;
     L.waves = plan.waves;
@@ -596,8 +731,7 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
         }
     };
 
-    char *ws_bytes = static_cast<char *>(workspace);
-    const size_t staged = staged_bytes_for(batch, seqlen, d_state, plan);
+    const size_t staged = staged_bytes_for(batch, seqlen, N, plan);
     L.relay_parts = 1;
     if (plan.relay_parts > 1) {
         L.relay_sync = reinterpret_cast<uint32_t *>(ws_bytes + staged);
@@ -627,9 +761,9 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
     const int64_t S = plan.n_spans;
     float *ws = reinterpret_cast<float *>(ws_bytes + staged); // (no relay with spans)
     float *ws_decay = ws;
-    float *ws_hloc = ws + S * bdn;
-    float *ws_hin = ws + 2 * S * bdn;
-    float *ws_rot = plan.rot ? ws + 3 * S * bdn : nullptr; // (pairs * S * 4 = 2 * S * bdn)
+    float *ws_hloc = ws + S * bdk;
+    float *ws_hin = ws + 2 * S * bdk;
+    float *ws_rot = plan.rot ? ws + 3 * S * bdk : nullptr; // (pairs * S * 4 = 2 * S * bdk)
 
     ScanLaunch E = L;
     E.h_init = nullptr;
@@ -650,17 +784,23 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
     K.ws_rot = ws_rot;
     K.h0 = h0;
     K.h_in = ws_hin;
-    K.columns = bdn;
+    K.columns = bdk;
     K.n_spans = (int32_t)S;
     e = launch_carry(K, st);
     if (e != hipSuccess)
         return MAMBA_ERR_HIP;
 
     L.h_init = ws_hin;
-    L.h_init_span_stride = bdn;
+    L.h_init_span_stride = bdk;
     L.first_span = 0;
     L.launch_spans = (int32_t)S;
     return hip_status(full(L));
+    };
+    const mamba_status_t rs = run();
+    if (rs != MAMBA_OK || !padded || !h_last)
+        return rs;
+    return hip_status(launch_unpad_rows(h_last, hl_run, batch * d_inner, (int32_t)d_state,
+                                        (int32_t)N, 4, st));
 }
 
 // Checks of mamba_scan_fwd short of the workspace (for mamba_scan_fwd_noalloc).
@@ -714,18 +854,24 @@ mamba_status_t mamba_scan_fwd_relay_faults(const void *workspace, size_t workspa
     if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 || !mul_ok(batch, d_inner, &t) ||
         !mul_ok(t, d_state, &t))
         return MAMBA_ERR_BAD_SHAPE;
-    if (!d_state_ok(d_state))
+    const int64_t np = padded_d_state(d_state);
+    if (!np)
         return MAMBA_ERR_UNSUPPORTED;
     Plan plan;
-    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, d_state, opts, ext, &plan);
+    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, np, opts, ext, &plan);
     if (ps != MAMBA_OK)
         return ps;
     if (plan.relay_parts < 2 || seqlen == 0 || batch == 0 || d_inner == 0)
         return MAMBA_OK; // no relay: nothing can have timed out
-    const size_t need = workspace_bytes_for(batch, seqlen, d_inner, d_state, plan);
+    FwdPad pad{};
+    if (np != d_state &&
+        !fwd_pad_layout(batch, seqlen, d_inner, np, 4, ext && ext->theta,
+                        ext && ext->lambda && ext->B_prev, &pad))
+        return MAMBA_ERR_BAD_SHAPE;
+    const size_t need = pad.total + workspace_bytes_for(batch, seqlen, d_inner, np, plan);
     if (!workspace || workspace_bytes < need)
         return MAMBA_ERR_WORKSPACE;
-    const size_t staged = staged_bytes_for(batch, seqlen, d_state, plan);
+    const size_t staged = pad.total + staged_bytes_for(batch, seqlen, np, plan);
     const uint32_t *word = reinterpret_cast<const uint32_t *>(
                                static_cast<const char *>(workspace) + staged) +
                            plan.relay_tiles * (plan.relay_parts - 1);
@@ -784,9 +930,11 @@ mamba_status_t mamba_state_update_ext(float *h, const void *u, const void *delta
         return MAMBA_ERR_BAD_SHAPE;
     if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
         return MAMBA_ERR_BAD_DTYPE;
-    if (!d_state_ok(d_state))
+    if (!padded_d_state(d_state))
         return MAMBA_ERR_UNSUPPORTED;
     const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
+    // compiled sizes move the state in 16-byte vectors; the others in 4-byte elements
+    const size_t h_align = d_state_ok(d_state) ? 16 : 4;
     int64_t bd, bn, bdn, dn, t;
     if (!mul_ok(batch, d_inner, &bd) || !mul_ok(bd, es, &t) || !mul_ok(batch, d_state, &bn) ||
         !mul_ok(bd, d_state, &bdn) || !mul_ok(bdn, 4, &t) || !mul_ok(d_inner, d_state, &dn) ||
@@ -801,7 +949,7 @@ mamba_status_t mamba_state_update_ext(float *h, const void *u, const void *delta
     for (const void *p : elem_ptrs)
         if (p && !aligned(p, (size_t)es))
             return MAMBA_ERR_MISALIGNED;
-    if (!aligned(h, 16) || !aligned(A, 16) || (D && !aligned(D, 4)) ||
+    if (!aligned(h, h_align) || !aligned(A, h_align) || (D && !aligned(D, 4)) ||
         (delta_bias && !aligned(delta_bias, 4)))
         return MAMBA_ERR_MISALIGNED;
 
@@ -945,16 +1093,20 @@ static size_t bwd_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
                                  int64_t d_state, const mamba_scan_opts_t *opts, bool ext_ck)
 {
     int64_t t;
-    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 ||
-        !mul_ok(batch, seqlen, &t) || !mul_ok(t, d_inner, &t) || !mul_ok(t, d_state, &t) ||
+    const int64_t np = padded_d_state(d_state);
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 || !np ||
+        !mul_ok(batch, seqlen, &t) || !mul_ok(t, d_inner, &t) || !mul_ok(t, np, &t) ||
         !mul_ok(t, 8, &t))
         return (size_t)-1;
     BwdPlan plan;
-    if (bwd_plan(batch, seqlen, d_inner, d_state, opts, &plan) != MAMBA_OK)
+    if (bwd_plan(batch, seqlen, d_inner, np, opts, &plan) != MAMBA_OK)
         return (size_t)-1;
     size_t off[12];
-    bwd_layout(batch, seqlen, d_inner, d_state, plan, ext_ck, off);
-    return off[11];
+    bwd_layout(batch, seqlen, d_inner, np, plan, ext_ck, off);
+    BwdPad pad{};
+    if (np != d_state && seqlen > 0 && !bwd_pad_layout(batch, seqlen, d_inner, np, &pad))
+        return (size_t)-1;
+    return pad.total + off[11];
 }
 
 size_t mamba_scan_bwd_workspace_size_ex(int64_t batch, int64_t seqlen, int64_t d_inner,
@@ -971,9 +1123,10 @@ size_t mamba_scan_bwd_ckpt_workspace_size(int64_t batch, int64_t seqlen, int64_t
 
 size_t mamba_scan_ckpt_size(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state)
 {
-    if (batch < 0 || seqlen < 0 || d_inner < 0 || !bwd_d_state_ok(d_state))
+    const int64_t np = padded_d_state(d_state);
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || !bwd_d_state_ok(np))
         return (size_t)-1;
-    const int64_t b = ckpt_bytes(batch, seqlen, d_inner, d_state);
+    const int64_t b = ckpt_bytes(batch, seqlen, d_inner, np);
     return b < 0 ? (size_t)-1 : (size_t)b;
 }
 
@@ -1014,8 +1167,12 @@ static mamba_status_t bwd_impl(const void *u, const void *delta, const float *A,
         return MAMBA_ERR_BAD_SHAPE;
     if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
         return MAMBA_ERR_BAD_DTYPE;
+    const int64_t np = padded_d_state(d_state); // the compiled size the kernels run at
+    if (!np)
+        return MAMBA_ERR_UNSUPPORTED;
+    const bool padded = np != d_state;
     BwdPlan plan;
-    const mamba_status_t ps = bwd_plan(batch, seqlen, d_inner, d_state, opts, &plan);
+    const mamba_status_t ps = bwd_plan(batch, seqlen, d_inner, np, opts, &plan);
     if (ps != MAMBA_OK)
         return ps;
     const int S = plan.seg_len;
@@ -1049,7 +1206,7 @@ static mamba_status_t bwd_impl(const void *u, const void *delta, const float *A,
     for (const void *p : f32_ptrs)
         if (p && !aligned(p, 4))
             return MAMBA_ERR_MISALIGNED;
-    const int64_t ckb = ext_ck ? ckpt_bytes(batch, seqlen, d_inner, d_state) : 0;
+    const int64_t ckb = ext_ck ? ckpt_bytes(batch, seqlen, d_inner, np) : 0;
     if (ckb < 0)
         return MAMBA_ERR_BAD_SHAPE;
     if (ext_ck && S != 8)
@@ -1057,8 +1214,11 @@ static mamba_status_t bwd_impl(const void *u, const void *delta, const float *A,
 
     // ---- workspace ----
     size_t off[12];
-    bwd_layout(batch, seqlen, d_inner, d_state, plan, ext_ck, off);
-    const size_t need = off[11];
+    bwd_layout(batch, seqlen, d_inner, np, plan, ext_ck, off);
+    BwdPad pad{};
+    if (padded && has_seq && !bwd_pad_layout(batch, seqlen, d_inner, np, &pad))
+        return MAMBA_ERR_BAD_SHAPE;
+    const size_t need = pad.total + off[11];
     if (need > 0 && (!workspace || workspace_bytes < need))
         return MAMBA_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 4))
@@ -1109,6 +1269,45 @@ static mamba_status_t bwd_impl(const void *u, const void *delta, const float *A,
     }
 
     char *ws = static_cast<char *>(workspace);
+    // a d_state without kernels of its own: the state-indexed inputs padded to np entries
+    // per row at the front of the workspace, the state-indexed gradients written there
+    // and copied back at the end
+    void *dB_out = dB, *dC_out = dC;
+    float *dA_out = dA, *dh0_out = dh0;
+    const int64_t n_real = d_state;
+    if (padded) {
+        const int32_t n32 = (int32_t)d_state, np32 = (int32_t)np, es32 = (int32_t)es;
+        if (launch_pad_rows(ws + pad.a, A, d_inner, n32, np32, 4, -1.0f, st) != hipSuccess ||
+            launch_pad_rows(ws + pad.b, B, batch * seqlen, n32, np32, es32, 0.0f, st) != hipSuccess ||
+            launch_pad_rows(ws + pad.c, C, batch * seqlen, n32, np32, es32, 0.0f, st) != hipSuccess)
+            return MAMBA_ERR_HIP;
+        A = reinterpret_cast<const float *>(ws + pad.a);
+        B = ws + pad.b;
+        C = ws + pad.c;
+        if (h0) {
+            if (launch_pad_rows(ws + pad.h0, h0, batch * d_inner, n32, np32, 4, 0.0f, st) !=
+                hipSuccess)
+                return MAMBA_ERR_HIP;
+            h0 = reinterpret_cast<const float *>(ws + pad.h0);
+        }
+        if (dh_last) {
+            if (launch_pad_rows(ws + pad.dhl, dh_last, batch * d_inner, n32, np32, 4, 0.0f, st) !=
+                hipSuccess)
+                return MAMBA_ERR_HIP;
+            dh_last = reinterpret_cast<const float *>(ws + pad.dhl);
+        }
+        if (dB)
+            dB = ws + pad.db;
+        if (dC)
+            dC = ws + pad.dc;
+        if (dA)
+            dA = reinterpret_cast<float *>(ws + pad.da);
+        if (dh0)
+            dh0 = reinterpret_cast<float *>(ws + pad.dh0);
+        ws += pad.total;
+        d_state = np;
+        bdn = batch * d_inner * np;
+    }
     const DType dt = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
     auto region = [&](int i) { return reinterpret_cast<float *>(ws + off[i]); };
 
@@ -1192,7 +1391,22 @@ static mamba_status_t bwd_impl(const void *u, const void *delta, const float *A,
     P.d_inner = d_inner;
     P.d_state = d_state;
     P.dtype = dt;
-    return hip_status(launch_scan_bwd(P, st));
+    if (launch_scan_bwd(P, st) != hipSuccess)
+        return MAMBA_ERR_HIP;
+    if (!padded)
+        return MAMBA_OK;
+    // the state-indexed gradients back to rows of the caller's d_state
+    const int32_t nr = (int32_t)n_real, np32 = (int32_t)np, es32 = (int32_t)es;
+    hipError_t e = hipSuccess;
+    if (dB_out)
+        e = launch_unpad_rows(dB_out, dB, batch * seqlen, nr, np32, es32, st);
+    if (e == hipSuccess && dC_out)
+        e = launch_unpad_rows(dC_out, dC, batch * seqlen, nr, np32, es32, st);
+    if (e == hipSuccess && dA_out)
+        e = launch_unpad_rows(dA_out, dA, d_inner, nr, np32, 4, st);
+    if (e == hipSuccess && dh0_out)
+        e = launch_unpad_rows(dh0_out, dh0, batch * d_inner, nr, np32, 4, st);
+    return hip_status(e);
 }
 
 mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *A,

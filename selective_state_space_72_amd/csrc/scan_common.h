@@ -126,5 +126,11 @@ hipError_t launch_conv1d_silu(const ConvLaunch &p, hipStream_t stream);
 hipError_t launch_conv1d_silu_update(const ConvLaunch &p, hipStream_t stream);
 // h_last = h0 (or zeros when h0 is NULL), for empty sequences.
 hipError_t launch_copy_state(float *dst, const float *src, int64_t count, hipStream_t stream);
+// Rows of n elements (2 or 4 bytes) to rows of np >= n, the extra entries `fill` (zero for
+// 2-byte elements), and back (pad.hip: d_state values run at the next compiled size).
+hipError_t launch_pad_rows(void *dst, const void *src, int64_t rows, int32_t n, int32_t np,
+                           int32_t elem_bytes, float fill, hipStream_t stream);
+hipError_t launch_unpad_rows(void *dst, const void *src, int64_t rows, int32_t n, int32_t np,
+                             int32_t elem_bytes, hipStream_t stream);
 
 } // namespace mambascan

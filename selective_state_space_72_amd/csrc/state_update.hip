@@ -31,16 +31,22 @@ struct StepExt {
 };
 
 // DISC: 0 Euler, 1 zero-order hold, 2 exponential-trapezoidal; ROT: pair rotation.
-template <typename T, int N, int DISC, bool ROT>
+// GEN: d_state nr below the compiled N (a size without kernels of its own): the lanes of N
+// are kept, state indices >= nr are skipped (their h, A, B, C read as 0, -1, 0, 0 and
+// nothing stored), and the state moves with 4-byte accesses (rows of nr floats need not be
+// 16-byte aligned).
+template <typename T, int N, int DISC, bool ROT, bool GEN>
 __global__ void __launch_bounds__(256)
 state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__restrict__ delta,
                     const T *__restrict__ z, const T *__restrict__ Bm, const T *__restrict__ Cm,
                     const float *__restrict__ A, const float *__restrict__ Dv,
-                    const float *__restrict__ bias, T *__restrict__ y, int32_t Dn, StepExt ext)
+                    const float *__restrict__ bias, T *__restrict__ y, int32_t Dn, StepExt ext,
+                    int32_t n_real)
 {
     constexpr bool ZOH = DISC == 1, TRAP = DISC == 2;
     constexpr int LPC = N / 4; // lanes per channel
     static_assert(N % 4 == 0 && LPC <= 64, "bad d_state");
+    const int nr = GEN ? n_real : N; // row length of h, A, B, C (and B_prev, 2 x theta)
     const int b = blockIdx.y;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; // (d, q) within row b
     const bool valid = i < (int64_t)Dn * LPC;
@@ -49,23 +55,37 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
 
     const int64_t c = (int64_t)b * Dn + d; // channel index
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    f32x4 *hp = reinterpret_cast<f32x4 *>(h + c * N) + q;
-    const f32x4 hv = __builtin_nontemporal_load(hp);
-    const float4 av = reinterpret_cast<const float4 *>(A + (int64_t)d * N)[q];
+    f32x4 *hp = reinterpret_cast<f32x4 *>(h + c * nr) + q;
+    float hin[4], ain[4];
+    bool kv[4]; // state index 4q + k exists
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        kv[k] = !GEN || 4 * q + k < nr;
+    if constexpr (GEN) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            hin[k] = kv[k] ? h[c * nr + 4 * q + k] : 0.0f;
+            ain[k] = kv[k] ? A[(int64_t)d * nr + 4 * q + k] : -1.0f;
+        }
+    } else {
+        const f32x4 hv = __builtin_nontemporal_load(hp);
+        const float4 av = reinterpret_cast<const float4 *>(A + (int64_t)d * N)[q];
+        hin[0] = hv.x, hin[1] = hv.y, hin[2] = hv.z, hin[3] = hv.w;
+        ain[0] = av.x, ain[1] = av.y, ain[2] = av.z, ain[3] = av.w;
+    }
 
     const float uu = load_val(u, c);
     const float dl = softplus_f(load_val(delta, c) + (bias ? bias[d] : 0.0f));
     const float w = dl * uu;
-    const int64_t bn = (int64_t)b * N + 4 * q;
+    const int64_t bn = (int64_t)b * nr + 4 * q;
 
     float hn[4];
-    float hin[4] = {hv.x, hv.y, hv.z, hv.w};
-    const float ain[4] = {av.x, av.y, av.z, av.w};
-    if constexpr (ROT) {
+    if constexpr (ROT) { // (nr even: a pair exists whole or not at all)
 #pragma unroll
         for (int k = 0; k < 4; k += 2)
-            rotate_pair(dl * load_val((const T *)ext.theta, ((int64_t)b * N + 4 * q + k) / 2),
-                        hin[k], hin[k + 1]);
+            if (kv[k])
+                rotate_pair(dl * load_val((const T *)ext.theta, ((int64_t)b * nr + 4 * q + k) / 2),
+                            hin[k], hin[k + 1]);
     }
     float lm = 1.0f, p_lb = 0.0f;
     if constexpr (TRAP) {
@@ -79,14 +99,15 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
         float bu = w; // Bbar u / B: Euler Delta u, or the zero-order hold
         if constexpr (ZOH)
             bu = zoh_input(dl * ain[k], a, w, uu / ain[k]);
+        const float bk = kv[k] ? load_val(Bm, bn + k) : 0.0f;
+        const float ck = kv[k] ? load_val(Cm, bn + k) : 0.0f;
         if constexpr (TRAP) {
-            const float bp = ext.B_prev ? load_val((const T *)ext.B_prev, bn + k) : 0.0f;
-            hn[k] = __builtin_fmaf(a, hin[k],
-                                   __builtin_fmaf(p_lb, bp, lm * w * load_val(Bm, bn + k)));
+            const float bp = ext.B_prev && kv[k] ? load_val((const T *)ext.B_prev, bn + k) : 0.0f;
+            hn[k] = __builtin_fmaf(a, hin[k], __builtin_fmaf(p_lb, bp, lm * w * bk));
         } else {
-            hn[k] = __builtin_fmaf(a, hin[k], bu * load_val(Bm, bn + k));
+            hn[k] = __builtin_fmaf(a, hin[k], bu * bk);
         }
-        yp = __builtin_fmaf(load_val(Cm, bn + k), hn[k], yp);
+        yp = __builtin_fmaf(ck, hn[k], yp);
     }
 #pragma unroll
     for (int m = 1; m < LPC; m <<= 1)
@@ -94,8 +115,15 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
 
     if (!valid)
         return;
-    const f32x4 ho = {hn[0], hn[1], hn[2], hn[3]};
-    __builtin_nontemporal_store(ho, hp);
+    if constexpr (GEN) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (kv[k])
+                h[c * nr + 4 * q + k] = hn[k];
+    } else {
+        const f32x4 ho = {hn[0], hn[1], hn[2], hn[3]};
+        __builtin_nontemporal_store(ho, hp);
+    }
     if (q == 0) {
         float yv = yp + (Dv ? Dv[d] : 0.0f) * uu;
         if (z)
@@ -108,23 +136,35 @@ template <typename T, int N, int DISC, bool ROT>
 static hipError_t launch_step(const StepLaunch &p, hipStream_t stream)
 {
     constexpr int LPC = N / 4;
+    const bool gen = p.d_state != N;
+    const int64_t nr = p.d_state;
     const int64_t lanes = p.d_inner * LPC;
     const uint32_t gx = (uint32_t)((lanes + 255) / 256);
     // gridDim.y is limited; walk the batch in slices of at most 65535 rows
     for (int64_t b0 = 0; b0 < p.batch; b0 += 65535) {
         const int64_t nb = p.batch - b0 < 65535 ? p.batch - b0 : 65535;
-        const int64_t off_bd = b0 * p.d_inner, off_bn = b0 * N;
+        const int64_t off_bd = b0 * p.d_inner, off_bn = b0 * nr;
         StepExt ext{};
         ext.lam = p.lam ? (const T *)p.lam + off_bd : nullptr;
         ext.u_prev = p.u_prev ? (const T *)p.u_prev + off_bd : nullptr;
         ext.B_prev = p.B_prev ? (const T *)p.B_prev + off_bn : nullptr;
-        ext.theta = p.theta ? (const T *)p.theta + b0 * (N / 2) : nullptr;
-        hipLaunchKernelGGL((state_update_kernel<T, N, DISC, ROT>), dim3(gx, (uint32_t)nb),
-                           dim3(256), 0, stream, p.h + off_bd * N, (const T *)p.u + off_bd,
-                           (const T *)p.delta + off_bd,
-                           p.z ? (const T *)p.z + off_bd : nullptr, (const T *)p.B + off_bn,
-                           (const T *)p.C + off_bn, p.A, p.D, p.bias, (T *)p.y + off_bd,
-                           (int32_t)p.d_inner, ext);
+        ext.theta = p.theta ? (const T *)p.theta + b0 * (nr / 2) : nullptr;
+        if (gen)
+            hipLaunchKernelGGL((state_update_kernel<T, N, DISC, ROT, true>),
+                               dim3(gx, (uint32_t)nb), dim3(256), 0, stream,
+                               p.h + off_bd * nr, (const T *)p.u + off_bd,
+                               (const T *)p.delta + off_bd,
+                               p.z ? (const T *)p.z + off_bd : nullptr, (const T *)p.B + off_bn,
+                               (const T *)p.C + off_bn, p.A, p.D, p.bias, (T *)p.y + off_bd,
+                               (int32_t)p.d_inner, ext, (int32_t)nr);
+        else
+            hipLaunchKernelGGL((state_update_kernel<T, N, DISC, ROT, false>),
+                               dim3(gx, (uint32_t)nb), dim3(256), 0, stream,
+                               p.h + off_bd * nr, (const T *)p.u + off_bd,
+                               (const T *)p.delta + off_bd,
+                               p.z ? (const T *)p.z + off_bd : nullptr, (const T *)p.B + off_bn,
+                               (const T *)p.C + off_bn, p.A, p.D, p.bias, (T *)p.y + off_bd,
+                               (int32_t)p.d_inner, ext, (int32_t)nr);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -154,8 +194,12 @@ hipError_t launch_state_update(const StepLaunch &p, hipStream_t stream)
 {
     if (p.batch <= 0 || p.d_inner <= 0)
         return hipSuccess;
+    // a d_state without kernels of its own runs in the next compiled size's lanes
+    int64_t np = 4;
+    while (np < p.d_state)
+        np *= 2;
 #define STEP_CASE(N_)                                                   \
-    if (p.d_state == N_) {                                              \
+    if (np == N_) {                                                     \
         if (p.dtype == DType::BF16)                                     \
             return launch_step_opts<uint16_t, N_>(p, stream);           \
         return launch_step_opts<float, N_>(p, stream);                  \

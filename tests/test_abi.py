@@ -56,9 +56,10 @@ def test_status_strings(lib):
 
 
 def test_d_state_supported(lib):
-    for n in (4, 8, 16, 32, 64):
+    # 4, 8, 16, 32, 64 have kernels of their own; every other size up to 64 runs padded
+    for n in range(1, 65):
         assert lib.mamba_d_state_supported(n) == 1
-    for n in (0, 1, 3, 12, 128, -16):
+    for n in (0, 65, 128, -16):
         assert lib.mamba_d_state_supported(n) == 0
 
 
@@ -89,10 +90,26 @@ def test_scan_rejects_shapes_and_dtypes(lib):
     assert scan(lib, L=-5) == SHAPE
     assert scan(lib, Dn=-1) == SHAPE
     assert scan(lib, N=0) == SHAPE
-    assert scan(lib, N=12) == UNSUP
+    assert scan(lib, N=65) == UNSUP
     assert scan(lib, N=128) == UNSUP
     assert scan(lib, dtype=7) == DTYPE
     assert scan(lib, batch=1 << 40, L=1 << 40) == SHAPE  # element count overflows
+
+
+def test_padded_d_state_takes_workspace(lib):
+    # a d_state without kernels of its own runs at the next compiled size, with padded
+    # copies of the state-indexed arrays at the front of the workspace
+    for n, np_ in ((1, 4), (5, 8), (12, 16), (24, 32), (40, 64)):
+        wn = lib.mamba_scan_fwd_workspace_size(2, 64, 128, n)
+        wp = lib.mamba_scan_fwd_workspace_size(2, 64, 128, np_)
+        assert wn > wp, (n, wn, wp)
+        assert scan(lib, N=n) == WS  # none given
+    for n, np_ in ((3, 4), (12, 16), (20, 32)):
+        assert (lib.mamba_scan_bwd_workspace_size(2, 64, 128, n) >
+                lib.mamba_scan_bwd_workspace_size(2, 64, 128, np_))
+        assert lib.mamba_scan_ckpt_size(2, 64, 128, n) == lib.mamba_scan_ckpt_size(2, 64, 128, np_)
+    # the backward has no kernels above d_state 32
+    assert lib.mamba_scan_bwd_workspace_size(2, 64, 128, 40) == ctypes.c_size_t(-1).value
 
 
 def test_scan_empty_sizes_are_no_ops(lib):
@@ -147,7 +164,7 @@ def test_scan_workspace_rules(lib):
     assert lib.mamba_scan_fwd_workspace_size_ex(8, 4096, 5120, 16,
                                                 ctypes.byref(ms.ScanOpts(0, 0, 1, 1))) == 0
     assert lib.mamba_scan_fwd_workspace_size(-1, 4, 4, 16) == ctypes.c_size_t(-1).value
-    assert lib.mamba_scan_fwd_workspace_size(1, 4, 4, 12) == ctypes.c_size_t(-1).value
+    assert lib.mamba_scan_fwd_workspace_size(1, 4, 4, 65) == ctypes.c_size_t(-1).value
 
 
 def test_scan_rejects_bad_options(lib):
@@ -227,7 +244,7 @@ def test_state_update_validation(lib):
     assert step(lib, h=None) == NULL
     assert step(lib, y=None) == NULL
     assert step(lib, batch=-1) == SHAPE
-    assert step(lib, N=12) == UNSUP
+    assert step(lib, N=65) == UNSUP
     assert step(lib, dtype=5) == DTYPE
     assert step(lib, h=BASE + 4) == ALIGN           # h needs 16-byte alignment
     assert step(lib, A=BASE + 120 * MB + 8) == ALIGN
@@ -244,7 +261,7 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
 
 
 def test_default_plan_is_compiled_for_every_d_state(lib):
-    for n in (4, 8, 16, 32, 64):
+    for n in (1, 3, 4, 5, 8, 12, 16, 24, 32, 40, 64):
         for shape in ((1, 64, 32), (8, 4096, 5120), (1, 131072, 2048)):
             b, L, d = shape
             assert lib.mamba_scan_fwd_workspace_size(b, L, d, n) != ctypes.c_size_t(-1).value, \
@@ -341,7 +358,7 @@ def test_bwd_validation(lib):
     assert bwd(lib, A=None) == NULL
     assert bwd(lib, z=BASE + 200 * MB) == NULL          # a gate needs dz
     assert bwd(lib, N=64) == UNSUP
-    assert bwd(lib, N=12) == UNSUP
+    assert bwd(lib, N=40) == UNSUP  # (no backward kernels above d_state 32)
     assert bwd(lib, dtype=5) == DTYPE
     assert bwd(lib, batch=-1) == SHAPE
     assert bwd(lib, batch=0, u=None, du=None) == OK
@@ -550,8 +567,10 @@ def test_ckpt_size(lib):
     assert lib.mamba_scan_ckpt_size(2, 65, 100, 8) == 2 * 2 * 9 * 8 * 64 * 4   # ragged
     assert lib.mamba_scan_ckpt_size(2, 0, 100, 8) == 0
     bad = ctypes.c_size_t(-1).value
-    for n in (64, 12, 0):
+    for n in (64, 40, 0):
         assert lib.mamba_scan_ckpt_size(2, 64, 64, n) == bad       # no backward pass there
+    # d_state 12 runs at 16: its checkpoints hold 16 states
+    assert lib.mamba_scan_ckpt_size(2, 64, 64, 12) == lib.mamba_scan_ckpt_size(2, 64, 64, 16)
     assert lib.mamba_scan_ckpt_size(-1, 64, 64, 16) == bad
     # the backward's workspace without its own checkpoints (and forward span summaries)
     o = ms.ScanOpts()
@@ -635,7 +654,7 @@ def test_noalloc_rejects_before_touching_the_device(lib):
     assert noalloc(lib, batch=-1) == lib.mamba_scan_fwd(
         BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 132 * MB, BASE + 136 * MB, None, None,
         None, None, BASE + 256 * MB, None, -1, 64, 128, 16, BF16, None, 0, None)
-    assert noalloc(lib, N=12) == UNSUP
+    assert noalloc(lib, N=65) == UNSUP
     assert noalloc(lib, u=None) == NULL
     assert noalloc(lib, dtype=7) == lib.mamba_scan_fwd(
         BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 132 * MB, BASE + 136 * MB, None, None,
