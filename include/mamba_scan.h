@@ -441,13 +441,31 @@ MAMBA_API mamba_status_t mamba_scan_bwd_ckpt(const void *u, const void *delta, c
  *       library; it is written only, 4-byte aligned, and overlaps no other argument or
  *       the workspace (MAMBA_ERR_ALIASING).  Needs the Euler rule without lambda or
  *       theta and d_state 1..32, and runs in the SCALAR family (else
- *       MAMBA_ERR_UNSUPPORTED).  It does not change y or h_last. */
+ *       MAMBA_ERR_UNSUPPORTED).  It does not change y or h_last.
+ *
+ * Row strides of the inputs (elements; 0 = contiguous).  In the Mamba block of
+ * "Understanding Mamba" section 5.2 the scan's z (and x) are the two halves of one
+ * projection, xz.chunk(2, -1), and B, C slices of another: views whose rows (b, t) are
+ * further apart than d_inner (d_state) elements.  With these the scan reads such views in
+ * place instead of the caller copying them:
+ *   u_stride, delta_stride, z_stride : elements from row (b, t) to row (b, t + 1) of u,
+ *       delta, z -- every row, so also from (b, seqlen - 1) to (b + 1, 0): element (b, t, d)
+ *       at ptr[(b * seqlen + t) * stride + d]; >= d_inner.  Decode step: from batch row b to
+ *       b + 1.
+ *   B_stride, C_stride : the same for B and C; >= d_state.
+ * A stride below the row length returns MAMBA_ERR_BAD_SHAPE.  Strides other than the row
+ * length run in the SCALAR family (AUTO selects it; ROWS, BLOCK and d_state above 32 return
+ * MAMBA_ERR_UNSUPPORTED).  The inputs may overlap each other (views of one buffer); y, h_last
+ * and the workspace may not overlap the strided extent of any of them.  lambda, u_prev,
+ * B_prev, theta and every output stay contiguous; the backward entry points take contiguous
+ * inputs only. */
 typedef struct {
     const void *lambda;
     const void *u_prev;
     const void *B_prev;
     const void *theta;
     float *ckpt;
+    int64_t u_stride, delta_stride, z_stride, B_stride, C_stride;
 } mamba_scan_ext_t;
 
 /* Workspace size for mamba_scan_fwd_ext (ext and opts may be NULL). */

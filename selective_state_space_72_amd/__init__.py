@@ -75,10 +75,12 @@ class SsdOpts(ctypes.Structure):
 
 class ScanExt(ctypes.Structure):
     """mamba_scan_ext_t: trapezoid mixing coefficients, look-back input, rotation rates,
-    checkpoint output for the backward pass."""
+    checkpoint output for the backward pass, row strides of u, delta, z, B, C."""
     _fields_ = [("lambda_", ctypes.c_void_p), ("u_prev", ctypes.c_void_p),
                 ("B_prev", ctypes.c_void_p), ("theta", ctypes.c_void_p),
-                ("ckpt", ctypes.c_void_p)]
+                ("ckpt", ctypes.c_void_p), ("u_stride", ctypes.c_int64),
+                ("delta_stride", ctypes.c_int64), ("z_stride", ctypes.c_int64),
+                ("B_stride", ctypes.c_int64), ("C_stride", ctypes.c_int64)]
 
 
 _vp = ctypes.c_void_p
@@ -240,6 +242,36 @@ def _ptr(t, name, shape=None, dtype=None, device=None) -> Optional[int]:
     return t.data_ptr() if t.numel() > 0 else None
 
 
+def _rows_ptr(t, name, shape, dtype, device):
+    """Pointer and row stride (elements between consecutive rows: the leading dimensions
+    taken together) of a tensor whose last dimension is contiguous and whose rows are
+    evenly spaced -- a view such as xz.chunk(2, -1)[1] or a slice of the last dimension.
+    Returns (None, 0) for None; the stride is 0 for a contiguous tensor."""
+    if t is None:
+        return None, 0
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.is_contiguous():
+        return _ptr(t, name, shape, dtype, device), 0
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    lead = [(n, st) for n, st in zip(t.shape[:-1], t.stride()[:-1]) if n > 1]
+    row = lead[-1][1] if lead else t.shape[-1]
+    expect = row
+    for n, st in reversed(lead):
+        if st != expect:
+            raise ValueError(f"{name}: rows must be evenly spaced (strides {t.stride()})")
+        expect = st * n
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return (t.data_ptr() if t.numel() > 0 else None), int(row)
+
+
 def _stream(device) -> int:
     torch = _torch()
     return torch.cuda.current_stream(device).cuda_stream
@@ -258,11 +290,13 @@ def mamba_scan_fwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state
                                   chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
                                   kernel: str = "auto", relay: int = 0,
                                   discretization: str = "euler", trapezoid: bool = False,
-                                  rotation: bool = False) -> int:
+                                  rotation: bool = False, strides=(0, 0, 0, 0, 0)) -> int:
+    """strides: row strides of (u, delta, z, B, C) in elements, 0 = contiguous."""
     lib = load_library()
     o = _opts(chunk_len, waves, n_spans, kernel, relay, discretization)
     # only the presence of the extension inputs matters for the size
-    e = ScanExt(1 if trapezoid else None, None, None, 1 if rotation else None)
+    e = ScanExt(1 if trapezoid else None, None, None, 1 if rotation else None, None,
+                *[int(x) for x in strides])
     n = lib.mamba_scan_fwd_workspace_size_ext(batch, seqlen, d_inner, d_state, ctypes.byref(e),
                                               ctypes.byref(o))
     if n == ctypes.c_size_t(-1).value:
@@ -297,13 +331,14 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
     act = u.dtype
     code = _dtype_code(u)
     f32 = torch.float32
-    p_u = _ptr(u, "u", (batch, seqlen, d_inner), act, dev)
-    p_delta = _ptr(delta, "delta", (batch, seqlen, d_inner), act, dev)
+    # u, delta, z, B, C may be views with evenly spaced rows (passed as row strides)
+    p_u, s_u = _rows_ptr(u, "u", (batch, seqlen, d_inner), act, dev)
+    p_delta, s_d = _rows_ptr(delta, "delta", (batch, seqlen, d_inner), act, dev)
     p_A = _ptr(A, "A", (d_inner, d_state), f32, dev)
-    p_B = _ptr(B, "B", (batch, seqlen, d_state), act, dev)
-    p_C = _ptr(C, "C", (batch, seqlen, d_state), act, dev)
+    p_B, s_B = _rows_ptr(B, "B", (batch, seqlen, d_state), act, dev)
+    p_C, s_C = _rows_ptr(C, "C", (batch, seqlen, d_state), act, dev)
     p_D = _ptr(D, "D", (d_inner,), f32, dev)
-    p_z = _ptr(z, "z", (batch, seqlen, d_inner), act, dev)
+    p_z, s_z = _rows_ptr(z, "z", (batch, seqlen, d_inner), act, dev)
     p_bias = _ptr(delta_bias, "delta_bias", (d_inner,), f32, dev)
     p_h0 = _ptr(h0, "h0", (batch, d_inner, d_state), f32, dev)
     y = out if out is not None else torch.empty((batch, seqlen, d_inner), dtype=act, device=dev)
@@ -316,7 +351,8 @@ def mamba_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
                   _ptr(u_prev, "u_prev", (batch, d_inner), act, dev),
                   _ptr(B_prev, "B_prev", (batch, d_state), act, dev),
                   _ptr(theta, "theta", (batch, seqlen, d_state // 2), act, dev),
-                  _ckpt_ptr(ckpt, batch, seqlen, d_inner, d_state, dev))
+                  _ckpt_ptr(ckpt, batch, seqlen, d_inner, d_state, dev), s_u, s_d, s_z, s_B,
+                  s_C)
     if seqlen == 0:
         # empty tensors have no address; only the presence of an option matters here
         ext.lambda_ = ext.lambda_ or (1 if lam is not None else None)
@@ -352,13 +388,15 @@ def mamba_scan_fwd_relay_faults(workspace, batch: int, seqlen: int, d_inner: int
                                 *, chunk_len: int = 0, waves: int = 0, n_spans: int = 0,
                                 kernel: str = "auto", relay: int = 0,
                                 discretization: str = "euler", trapezoid: bool = False,
-                                rotation: bool = False, device=None) -> int:
+                                rotation: bool = False, strides=(0, 0, 0, 0, 0),
+                                device=None) -> int:
     """Relay hand-offs that timed out in the last mamba_scan_fwd call given this workspace
     with the same sizes and options (0 when it planned no relay).  Synchronises the current
     stream."""
     lib = load_library()
     o = _opts(chunk_len, waves, n_spans, kernel, relay, discretization)
-    e = ScanExt(1 if trapezoid else None, None, None, 1 if rotation else None)
+    e = ScanExt(1 if trapezoid else None, None, None, 1 if rotation else None, None,
+                *[int(x) for x in strides])
     p_ws, ws_bytes = _ws_arg(workspace)
     dev = workspace.device if workspace is not None else device
     out = ctypes.c_uint32(0)
@@ -417,13 +455,14 @@ def mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
     code = _dtype_code(u)
     f32 = torch.float32
     p_h = _ptr(h, "h", (batch, d_inner, d_state), f32, dev)
-    p_u = _ptr(u, "u", (batch, d_inner), act, dev)
-    p_delta = _ptr(delta, "delta", (batch, d_inner), act, dev)
+    # u, delta, z, B, C may be views with evenly spaced batch rows
+    p_u, s_u = _rows_ptr(u, "u", (batch, d_inner), act, dev)
+    p_delta, s_d = _rows_ptr(delta, "delta", (batch, d_inner), act, dev)
     p_A = _ptr(A, "A", (d_inner, d_state), f32, dev)
-    p_B = _ptr(B, "B", (batch, d_state), act, dev)
-    p_C = _ptr(C, "C", (batch, d_state), act, dev)
+    p_B, s_B = _rows_ptr(B, "B", (batch, d_state), act, dev)
+    p_C, s_C = _rows_ptr(C, "C", (batch, d_state), act, dev)
     p_D = _ptr(D, "D", (d_inner,), f32, dev)
-    p_z = _ptr(z, "z", (batch, d_inner), act, dev)
+    p_z, s_z = _rows_ptr(z, "z", (batch, d_inner), act, dev)
     p_bias = _ptr(delta_bias, "delta_bias", (d_inner,), f32, dev)
     y = out if out is not None else torch.empty((batch, d_inner), dtype=act, device=dev)
     p_y = _ptr(y, "out", (batch, d_inner), act, dev)
@@ -432,7 +471,8 @@ def mamba_state_update(h, u, delta, A, B, C, D=None, z=None, delta_bias=None, *,
     ext = ScanExt(_ptr(lam, "lam", (batch, d_inner), act, dev),
                   _ptr(u_prev, "u_prev", (batch, d_inner), act, dev),
                   _ptr(B_prev, "B_prev", (batch, d_state), act, dev),
-                  _ptr(theta, "theta", (batch, d_state // 2), act, dev))
+                  _ptr(theta, "theta", (batch, d_state // 2), act, dev), None, s_u, s_d, s_z,
+                  s_B, s_C)
     st = lib.mamba_state_update_ext(p_h, p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_y,
                                     batch, d_inner, d_state, code,
                                     DISCRETIZATIONS[discretization], ctypes.byref(ext),

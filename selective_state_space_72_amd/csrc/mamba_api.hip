@@ -78,6 +78,43 @@ int64_t padded_d_state(int64_t n)
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Row strides of the activations, in elements (mamba_scan_ext_t; 0 = contiguous).
+struct Rows {
+    int64_t u, d, z, B, C;
+    bool strided;   // some stride is not its row length: the scalar family reads those
+    int64_t widest; // the largest of u, d, z and d_inner (the scalar kernel's span bytes)
+};
+
+// false if a stride is negative or shorter than its row
+bool rows_of(const mamba_scan_ext_t *ext, int64_t d_inner, int64_t d_state, Rows *r)
+{
+    auto one = [](int64_t s, int64_t row, int64_t *out) {
+        *out = s == 0 ? row : s;
+        return s == 0 || s >= row;
+    };
+    const bool ok = one(ext ? ext->u_stride : 0, d_inner, &r->u) &&
+                    one(ext ? ext->delta_stride : 0, d_inner, &r->d) &&
+                    one(ext ? ext->z_stride : 0, d_inner, &r->z) &&
+                    one(ext ? ext->B_stride : 0, d_state, &r->B) &&
+                    one(ext ? ext->C_stride : 0, d_state, &r->C);
+    r->strided = r->u != d_inner || r->d != d_inner || r->z != d_inner || r->B != d_state ||
+                 r->C != d_state;
+    r->widest = std::max(std::max(r->u, r->d), std::max(r->z, d_inner));
+    return ok;
+}
+
+// Bytes from the first element of `rows` rows of `row` elements, `stride` apart, to the
+// end of the last one; -1 on overflow.
+int64_t extent_bytes(int64_t rows, int64_t stride, int64_t row, int64_t es)
+{
+    int64_t t;
+    if (rows <= 0 || row <= 0)
+        return 0;
+    if (!mul_ok(rows - 1, stride, &t) || t > INT64_MAX - row || !mul_ok(t + row, es, &t))
+        return -1;
+    return t;
+}
+
 // Workspace prefix of a padded forward call: the padded copies of A, B, C, h0, theta,
 // B_prev and the padded final state, each 256-byte aligned (h0 and the final state always
 // reserved: the size query does not know whether they are given).
@@ -184,9 +221,12 @@ struct Plan {
 // when a single span cannot give every SIMD a few waves, the sequence is split into spans
 // (at most 64, each at least 256 steps) joined by the carry pass.
 mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
-                         const mamba_scan_opts_t *opts, const mamba_scan_ext_t *ext, Plan *plan)
+                         const mamba_scan_opts_t *opts, const mamba_scan_ext_t *ext, Plan *plan,
+                         const Rows *rows)
 {
     Plan p{};
+    const bool strided = rows && rows->strided;
+    const int64_t widest = rows ? rows->widest : d_inner;
     const int cus = cu_count();
     const int fam = opts ? opts->kernel : MAMBA_KERNEL_AUTO;
     const int disc = opts ? opts->discretization : MAMBA_DISC_EULER;
@@ -201,10 +241,10 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
     if (p.ckpt && (p.zoh || p.trap || p.rot || !bwd_d_state_ok(d_state)))
         return MAMBA_ERR_UNSUPPORTED; // the backward pass is built for Euler only
     Family autof = auto_family(batch, d_inner, d_state, cus);
-    if (autof == Family::Scalar && !scalar_span_ok(seqlen, d_inner))
+    if (autof == Family::Scalar && !scalar_span_ok(seqlen, widest))
         autof = Family::Rows;
-    if (p.zoh || p.trap || p.rot || p.ckpt) {
-        // these options are implemented in the scalar-B/C family only
+    if (p.zoh || p.trap || p.rot || p.ckpt || strided) {
+        // these options (and strided rows) are implemented in the scalar-B/C family only
         if (fam == MAMBA_KERNEL_ROWS || fam == MAMBA_KERNEL_BLOCK)
             return MAMBA_ERR_UNSUPPORTED;
         autof = Family::Scalar;
@@ -213,7 +253,8 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
         // an explicit block shape: the scalar family if it has it, else the block family
         const int w = opts->waves ? opts->waves : scalar_default_waves(d_state);
         const int c = opts->chunk_len ? opts->chunk_len : scalar_default_chunk(d_state);
-        autof = scalar_variant_supported(d_state, w, c) || p.zoh || p.trap || p.rot || p.ckpt
+        autof = scalar_variant_supported(d_state, w, c) || p.zoh || p.trap || p.rot ||
+                        p.ckpt || strided
                     ? Family::Scalar : Family::Block;
     }
     if (fam == MAMBA_KERNEL_ROWS || (fam == MAMBA_KERNEL_AUTO && autof == Family::Rows)) {
@@ -277,7 +318,7 @@ mamba_status_t make_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t
         len = (len + p.chunk - 1) / p.chunk * p.chunk;
         if (len < p.chunk)
             len = p.chunk;
-        if (p.family != Family::Scalar || scalar_span_ok(len, d_inner))
+        if (p.family != Family::Scalar || scalar_span_ok(len, widest))
             break;
         if (fixed_spans || spans >= 64)
             return MAMBA_ERR_UNSUPPORTED; // span too large for the scalar kernel's addressing
@@ -501,8 +542,11 @@ size_t mamba_scan_fwd_workspace_size_ext(int64_t batch, int64_t seqlen, int64_t 
     if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 ||
         !mul_ok(batch, d_inner, &tmp) || !mul_ok(tmp, d_state, &tmp) || !np)
         return (size_t)-1;
+    Rows rows;
+    if (!rows_of(ext, d_inner, d_state, &rows))
+        return (size_t)-1;
     Plan p;
-    if (make_plan(batch, seqlen, d_inner, np, opts, ext, &p) != MAMBA_OK)
+    if (make_plan(batch, seqlen, d_inner, np, opts, ext, &p, &rows) != MAMBA_OK)
         return (size_t)-1;
     size_t pad = 0;
     if (np != d_state && seqlen > 0) {
@@ -577,6 +621,17 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
         !mul_ok(d_inner, d_state, &dn) || !mul_ok(dn, 4, &t) || d_inner > INT32_MAX ||
         batch > INT32_MAX)
         return MAMBA_ERR_BAD_SHAPE;
+    Rows rows;
+    if (!rows_of(ext, d_inner, d_state, &rows))
+        return MAMBA_ERR_BAD_SHAPE;
+    // bytes spanned by each activation (its strided extent)
+    const int64_t x_u = extent_bytes(batch * seqlen, rows.u, d_inner, es),
+                  x_d = extent_bytes(batch * seqlen, rows.d, d_inner, es),
+                  x_z = extent_bytes(batch * seqlen, rows.z, d_inner, es),
+                  x_B = extent_bytes(batch * seqlen, rows.B, d_state, es),
+                  x_C = extent_bytes(batch * seqlen, rows.C, d_state, es);
+    if (x_u < 0 || x_d < 0 || x_z < 0 || x_B < 0 || x_C < 0)
+        return MAMBA_ERR_BAD_SHAPE;
     if (batch == 0 || d_inner == 0)
         return MAMBA_OK;
 
@@ -597,7 +652,7 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
 
     // ---- plan and workspace ----
     Plan plan;
-    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, np, opts, ext, &plan);
+    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, np, opts, ext, &plan, &rows);
     if (ps != MAMBA_OK)
         return ps;
     FwdPad pad{};
@@ -611,9 +666,9 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
         return MAMBA_ERR_MISALIGNED;
 
     // ---- aliasing ----
-    const Range r_in[] = {range_of(u, bld * es),       range_of(delta, bld * es),
-                          range_of(z, bld * es),       range_of(B, bln * es),
-                          range_of(C, bln * es),       range_of(A, dn * 4),
+    const Range r_in[] = {range_of(u, x_u),            range_of(delta, x_d),
+                          range_of(z, x_z),            range_of(B, x_B),
+                          range_of(C, x_C),            range_of(A, dn * 4),
                           range_of(D, d_inner * 4),    range_of(delta_bias, d_inner * 4),
                           range_of(lam, bld * es),     range_of(u_prev, batch * d_inner * es),
                           range_of(B_prev, batch * d_state * es),
@@ -655,9 +710,12 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
         char *w = ws_bytes;
         const int32_t n32 = (int32_t)d_state, np32 = (int32_t)np, es32 = (int32_t)es;
         if (launch_pad_rows(w + pad.a, A, d_inner, n32, np32, 4, -1.0f, st) != hipSuccess ||
-            launch_pad_rows(w + pad.b, B, batch * seqlen, n32, np32, es32, 0.0f, st) != hipSuccess ||
-            launch_pad_rows(w + pad.c, C, batch * seqlen, n32, np32, es32, 0.0f, st) != hipSuccess)
+            launch_pad_rows(w + pad.b, B, batch * seqlen, n32, np32, es32, 0.0f, st,
+                            rows.B) != hipSuccess ||
+            launch_pad_rows(w + pad.c, C, batch * seqlen, n32, np32, es32, 0.0f, st,
+                            rows.C) != hipSuccess)
             return MAMBA_ERR_HIP;
+        rows.B = rows.C = np; // the copies are contiguous
         A = reinterpret_cast<const float *>(w + pad.a);
         B = w + pad.b;
         C = w + pad.c;
@@ -715,6 +773,11 @@ static mamba_status_t scan_fwd_impl(const void *u, const void *delta, const floa
     L.B_prev = B_prev;
     L.theta = theta;
     L.ckpt = plan.ckpt ? ckpt : nullptr;
+    L.su = rows.u;
+    L.sd = rows.d;
+    L.sz = rows.z;
+    L.sB = rows.B;
+    L.sC = rows.C;
 
     auto full = [&](const ScanLaunch &x) {
         switch (plan.family) {
@@ -857,8 +920,11 @@ mamba_status_t mamba_scan_fwd_relay_faults(const void *workspace, size_t workspa
     const int64_t np = padded_d_state(d_state);
     if (!np)
         return MAMBA_ERR_UNSUPPORTED;
+    Rows rows;
+    if (!rows_of(ext, d_inner, d_state, &rows))
+        return MAMBA_ERR_BAD_SHAPE;
     Plan plan;
-    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, np, opts, ext, &plan);
+    const mamba_status_t ps = make_plan(batch, seqlen, d_inner, np, opts, ext, &plan, &rows);
     if (ps != MAMBA_OK)
         return ps;
     if (plan.relay_parts < 2 || seqlen == 0 || batch == 0 || d_inner == 0)
@@ -940,6 +1006,16 @@ mamba_status_t mamba_state_update_ext(float *h, const void *u, const void *delta
         !mul_ok(bd, d_state, &bdn) || !mul_ok(bdn, 4, &t) || !mul_ok(d_inner, d_state, &dn) ||
         !mul_ok(dn, 4, &t) || d_inner > INT32_MAX / 64)
         return MAMBA_ERR_BAD_SHAPE;
+    Rows rows; // strides between batch rows
+    if (!rows_of(ext, d_inner, d_state, &rows))
+        return MAMBA_ERR_BAD_SHAPE;
+    const int64_t x_u = extent_bytes(batch, rows.u, d_inner, es),
+                  x_d = extent_bytes(batch, rows.d, d_inner, es),
+                  x_z = extent_bytes(batch, rows.z, d_inner, es),
+                  x_B = extent_bytes(batch, rows.B, d_state, es),
+                  x_C = extent_bytes(batch, rows.C, d_state, es);
+    if (x_u < 0 || x_d < 0 || x_z < 0 || x_B < 0 || x_C < 0)
+        return MAMBA_ERR_BAD_SHAPE;
     if (batch == 0 || d_inner == 0)
         return MAMBA_OK;
     if (!h || !u || !delta || !A || !B || !C || !y)
@@ -953,9 +1029,9 @@ mamba_status_t mamba_state_update_ext(float *h, const void *u, const void *delta
         (delta_bias && !aligned(delta_bias, 4)))
         return MAMBA_ERR_MISALIGNED;
 
-    const Range r_in[] = {range_of(u, bd * es),       range_of(delta, bd * es),
-                          range_of(z, bd * es),       range_of(B, bn * es),
-                          range_of(C, bn * es),       range_of(A, dn * 4),
+    const Range r_in[] = {range_of(u, x_u),           range_of(delta, x_d),
+                          range_of(z, x_z),           range_of(B, x_B),
+                          range_of(C, x_C),           range_of(A, dn * 4),
                           range_of(D, d_inner * 4),   range_of(delta_bias, d_inner * 4),
                           range_of(lam, bd * es),     range_of(u_prev, bd * es),
                           range_of(B_prev, bn * es),  range_of(theta, bn / 2 * es)};
@@ -989,6 +1065,11 @@ mamba_status_t mamba_state_update_ext(float *h, const void *u, const void *delta
     S.u_prev = u_prev;
     S.B_prev = B_prev;
     S.theta = theta;
+    S.su = rows.u;
+    S.sd = rows.d;
+    S.sz = rows.z;
+    S.sB = rows.B;
+    S.sC = rows.C;
     return hip_status(launch_state_update(S, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -1343,6 +1424,8 @@ static mamba_status_t bwd_impl(const void *u, const void *delta, const float *A,
         E.bc_staged = region(4);
         E.staged_rows = seqlen + plan.fwd_chunk;
         E.relay_parts = 1;
+        E.su = E.sd = E.sz = d_inner;
+        E.sB = E.sC = d_state;
         if (launch_stage_bc(E, st) != hipSuccess || launch_scalar_end(E, st) != hipSuccess)
             return MAMBA_ERR_HIP;
         CarryLaunch K{};

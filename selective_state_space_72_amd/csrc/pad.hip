@@ -13,18 +13,18 @@
 namespace mambascan {
 namespace {
 
-// dst[r * np + c] = src[r * n + c] for c < n, else fill (per element of dst)
+// dst[r * np + c] = src[r * ss + c] for c < n, else fill (per element of dst)
 template <typename E>
 __global__ void __launch_bounds__(256)
 pad_rows_kernel(E *__restrict__ dst, const E *__restrict__ src, int64_t rows, int32_t n,
-                int32_t np, E fill)
+                int32_t np, int64_t ss, E fill)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= rows * np)
         return;
     const int64_t r = i / np;
     const int32_t c = (int32_t)(i - r * np);
-    dst[i] = c < n ? src[r * n + c] : fill;
+    dst[i] = c < n ? src[r * ss + c] : fill;
 }
 
 // dst[r * n + c] = src[r * np + c] (per element of dst)
@@ -46,19 +46,20 @@ uint32_t grid_for(int64_t count) { return (uint32_t)((count + 255) / 256); }
 } // namespace
 
 hipError_t launch_pad_rows(void *dst, const void *src, int64_t rows, int32_t n, int32_t np,
-                           int32_t elem_bytes, float fill, hipStream_t stream)
+                           int32_t elem_bytes, float fill, hipStream_t stream, int64_t src_stride)
 {
     if (rows <= 0)
         return hipSuccess;
     const int64_t count = rows * np;
+    const int64_t ss = src_stride > 0 ? src_stride : n;
     if (elem_bytes == 4)
         hipLaunchKernelGGL(pad_rows_kernel<float>, dim3(grid_for(count)), dim3(256), 0, stream,
                            static_cast<float *>(dst), static_cast<const float *>(src), rows, n,
-                           np, fill);
+                           np, ss, fill);
     else // 16-bit elements: the fill is zero
         hipLaunchKernelGGL(pad_rows_kernel<uint16_t>, dim3(grid_for(count)), dim3(256), 0,
                            stream, static_cast<uint16_t *>(dst),
-                           static_cast<const uint16_t *>(src), rows, n, np, (uint16_t)0);
+                           static_cast<const uint16_t *>(src), rows, n, np, ss, (uint16_t)0);
     return hipGetLastError();
 }
 

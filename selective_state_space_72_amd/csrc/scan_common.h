@@ -53,6 +53,10 @@ struct ScanLaunch {
     // the state entering every 8-step segment s >= 1, at ckpt[((unit * n_seg + s) * N + n)
     // * 64 + lane], unit = channel tile * batch + b, n_seg = ceil(L / 8).
     float *ckpt;
+    // Row strides in elements: (b, t) rows of u, delta, z start su, sd, sz elements apart,
+    // those of B and C sB, sC apart (d_inner, d_state when contiguous; the scalar family
+    // reads other strides, the other families need the contiguous ones).
+    int64_t su, sd, sz, sB, sC;
 };
 
 // Relay arguments as the scan kernel receives them.
@@ -102,6 +106,7 @@ struct StepLaunch {
     bool trap, rot;                          // as in ScanLaunch
     const void *lam, *u_prev, *B_prev;       // (B,D), (B,D), (B,N)
     const void *theta;                       // (B,N/2)
+    int64_t su, sd, sz, sB, sC;              // batch-row strides (elements) of u, delta, z, B, C
 };
 
 // Returns true if the (d_state, waves, chunk) combination is compiled in.
@@ -129,7 +134,8 @@ hipError_t launch_copy_state(float *dst, const float *src, int64_t count, hipStr
 // Rows of n elements (2 or 4 bytes) to rows of np >= n, the extra entries `fill` (zero for
 // 2-byte elements), and back (pad.hip: d_state values run at the next compiled size).
 hipError_t launch_pad_rows(void *dst, const void *src, int64_t rows, int32_t n, int32_t np,
-                           int32_t elem_bytes, float fill, hipStream_t stream);
+                           int32_t elem_bytes, float fill, hipStream_t stream,
+                           int64_t src_stride = 0 /* elements between source rows; 0 = n */);
 hipError_t launch_unpad_rows(void *dst, const void *src, int64_t rows, int32_t n, int32_t np,
                              int32_t elem_bytes, hipStream_t stream);
 

@@ -34,7 +34,8 @@ __device__ __forceinline__ void for_c(F &&f)
     }
 }
 
-// bcp[((b * NW + g) * Lp + t) * BCW + {q, NQ + q}] = {B, C}[b, t, g * NQ + q] (0 past L),
+// bcp[((b * NW + g) * Lp + t) * BCW + {q, NQ + q}] = {B, C}[b, t, g * NQ + q] (0 past L;
+// rows (b, t) of B and C start sB and sC elements apart),
 // BCW = 2 NQ; with rotation rates (ROT) also bcp[... + 2 NQ + q / 2] = theta[b, t, (g NQ + q)
 // / 2] for even q, BCW = 2 NQ + NQ / 2.  Also zeroes the relay hand-off flags and fault word
 // (n_sync words) for the scan launch that follows on the same stream.
@@ -42,7 +43,7 @@ template <typename T, int N, int NW, bool ROT>
 __global__ void __launch_bounds__(256)
 stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, const T *__restrict__ th,
                 float *__restrict__ bcp, int64_t L, int64_t Lp, int64_t total,
-                uint32_t *__restrict__ sync, int32_t n_sync)
+                uint32_t *__restrict__ sync, int32_t n_sync, int64_t sB, int64_t sC)
 {
     constexpr int NQ = N / NW;
     constexpr int BCW = 2 * NQ + (ROT ? NQ / 2 : 0);
@@ -57,8 +58,8 @@ stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, const T *__r
     const int g = n / NQ, q = n % NQ;
     float bv = 0.0f, cv = 0.0f;
     if (t < L) {
-        bv = load_val(Bm, (b * L + t) * N + n);
-        cv = load_val(Cm, (b * L + t) * N + n);
+        bv = load_val(Bm, (b * L + t) * sB + n);
+        cv = load_val(Cm, (b * L + t) * sC + n);
     }
     float *dst = bcp + ((b * NW + g) * Lp + t) * BCW;
     dst[q] = bv;
@@ -108,6 +109,8 @@ struct Mamba3Args {
     float *ck;       // checkpoints for the backward pass (CK variants)
     int32_t ck_nseg; // 8-step segments of the whole sequence
     float *rot_m;    // span pass with the rotation: each pair's 2x2 transition over the span
+    int32_t su, sd, sz, sB; // row strides (elements) of u, delta, z, B; the planner keeps a
+                            // span of rows below 2^31 bytes
 };
 
 // DISC: 0 Euler, 1 zero-order hold, 2 exponential-trapezoidal; ROT: rotation of state pairs;
@@ -224,10 +227,11 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
         b_lb[q] = 0.0f;
     if constexpr (TRAP) {
         if (t_begin > 0) {
-            u_lb = load_val(u, ((int64_t)b * L + t_begin - 1) * Dn + dc);
+            u_lb = load_val(u, ((int64_t)b * L + t_begin - 1) * m3.su + dc);
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
-                b_lb[q] = load_val((const T *)m3.Bm, ((int64_t)b * L + t_begin - 1) * N + n0 + q);
+                b_lb[q] = load_val((const T *)m3.Bm,
+                                   ((int64_t)b * L + t_begin - 1) * m3.sB + n0 + q);
         } else {
             if (m3.u_prev)
                 u_lb = load_val((const T *)m3.u_prev, (int64_t)b * Dn + dc);
@@ -239,17 +243,25 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
         }
     }
 
-    // bytes per time step of one batch row; span bytes stay below 2^31 (planner)
+    // bytes per time step of one batch row (y, lam: d_inner elements; u, delta, z: their row
+    // strides); span bytes stay below 2^31 (planner)
     const uint32_t step_bytes = (uint32_t)Dn * (uint32_t)sizeof(T);
+    const uint32_t step_u = (uint32_t)m3.su * (uint32_t)sizeof(T);
+    const uint32_t step_d = (uint32_t)m3.sd * (uint32_t)sizeof(T);
+    const uint32_t step_z = (uint32_t)m3.sz * (uint32_t)sizeof(T);
     const uint32_t vo_in = (uint32_t)dc * (uint32_t)sizeof(T);
     const uint32_t vo_out = (uint32_t)d * (uint32_t)sizeof(T);
-    const int64_t span0 = ((int64_t)b * L + t_begin) * step_bytes; // byte offset of (b, t_begin)
+    const int64_t row0 = (int64_t)b * L + t_begin; // row (b, t_begin)
+    const int64_t span0 = row0 * step_bytes;       // its byte offset in y (and lam)
     // local time: 0 .. n_loc - 1 within this span (32-bit, as are all loop quantities)
     const int n_loc = (int)(t_end - t_begin);
     const uint32_t span_bytes = (uint32_t)n_loc * step_bytes;
-    const rsrc_t r_u = make_rsrc(reinterpret_cast<const char *>(u) + span0, span_bytes);
-    const rsrc_t r_d = make_rsrc(reinterpret_cast<const char *>(delta) + span0, span_bytes);
-    const rsrc_t r_z = gated ? make_rsrc(reinterpret_cast<const char *>(z) + span0, span_bytes)
+    const rsrc_t r_u = make_rsrc(reinterpret_cast<const char *>(u) + row0 * step_u,
+                                 (uint32_t)n_loc * step_u);
+    const rsrc_t r_d = make_rsrc(reinterpret_cast<const char *>(delta) + row0 * step_d,
+                                 (uint32_t)n_loc * step_d);
+    const rsrc_t r_z = gated ? make_rsrc(reinterpret_cast<const char *>(z) + row0 * step_z,
+                                         (uint32_t)n_loc * step_z)
                              : r_u;
     const rsrc_t r_l = TRAP ? make_rsrc(reinterpret_cast<const char *>(m3.lam) + span0,
                                         span_bytes)
@@ -270,13 +282,12 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
             const int tl = g + k * NW;
             const int t = t0 + tl;
             if (tl < TC && t < n_loc) { // wave-uniform
-                const uint32_t so = (uint32_t)t * step_bytes;
-                ru[j][k] = buf_load(r_u, vo_in, so, (T *)nullptr);
-                rd[j][k] = buf_load(r_d, vo_in, so, (T *)nullptr);
+                ru[j][k] = buf_load(r_u, vo_in, (uint32_t)t * step_u, (T *)nullptr);
+                rd[j][k] = buf_load(r_d, vo_in, (uint32_t)t * step_d, (T *)nullptr);
                 if (gated)
-                    rz[j][k] = buf_load(r_z, vo_in, so, (T *)nullptr);
+                    rz[j][k] = buf_load(r_z, vo_in, (uint32_t)t * step_z, (T *)nullptr);
                 if (TRAP)
-                    rl[j][k] = buf_load(r_l, vo_in, so, (T *)nullptr);
+                    rl[j][k] = buf_load(r_l, vo_in, (uint32_t)t * step_bytes, (T *)nullptr);
             }
         }
     };
@@ -580,7 +591,8 @@ hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
     }
     if (blocks <= 0)
         return hipSuccess;
-    Mamba3Args m3{p.lam, p.u_prev, p.B_prev, p.B, p.ckpt, (int32_t)((p.L + 7) / 8), p.ws_rot};
+    Mamba3Args m3{p.lam,    p.u_prev,  p.B_prev,  p.B,       p.ckpt, (int32_t)((p.L + 7) / 8),
+                  p.ws_rot, (int32_t)p.su, (int32_t)p.sd, (int32_t)p.sz, (int32_t)p.sB};
     hipLaunchKernelGGL((scan_scalar_kernel<T, N, NW, TC, PD, FULL, GATED, DISC, ROT, CK>),
                        dim3((uint32_t)blocks), dim3(64 * NW), 0, stream, (const T *)p.u,
                        (const T *)p.delta, (const T *)p.z, p.bc_staged, p.A, p.D, p.bias,
@@ -604,13 +616,14 @@ hipError_t launch_stage(const ScanLaunch &p, hipStream_t stream)
             hipLaunchKernelGGL((stage_bc_kernel<T, N, NW, true>), dim3((uint32_t)blocks),
                                dim3(256), 0, stream, (const T *)p.B, (const T *)p.C,
                                (const T *)p.theta, p.bc_staged, p.L, p.staged_rows, total,
-                               p.relay_sync, n_sync);
+                               p.relay_sync, n_sync, p.sB, p.sC);
         else
             return hipErrorInvalidValue;
     } else {
         hipLaunchKernelGGL((stage_bc_kernel<T, N, NW, false>), dim3((uint32_t)blocks), dim3(256),
                            0, stream, (const T *)p.B, (const T *)p.C, (const T *)nullptr,
-                           p.bc_staged, p.L, p.staged_rows, total, p.relay_sync, n_sync);
+                           p.bc_staged, p.L, p.staged_rows, total, p.relay_sync, n_sync, p.sB,
+                           p.sC);
     }
     return hipGetLastError();
 }

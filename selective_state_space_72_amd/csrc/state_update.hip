@@ -28,6 +28,7 @@ namespace mambascan {
 
 struct StepExt {
     const void *lam, *u_prev, *B_prev, *theta; // (B,D), (B,D), (B,N), (B,N/2); rows of this launch
+    int64_t su, sd, sz, sB, sC; // elements between batch rows of u, delta, z, B, C
 };
 
 // DISC: 0 Euler, 1 zero-order hold, 2 exponential-trapezoidal; ROT: pair rotation.
@@ -74,10 +75,11 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
         ain[0] = av.x, ain[1] = av.y, ain[2] = av.z, ain[3] = av.w;
     }
 
-    const float uu = load_val(u, c);
-    const float dl = softplus_f(load_val(delta, c) + (bias ? bias[d] : 0.0f));
+    const float uu = load_val(u, b * ext.su + d);
+    const float dl = softplus_f(load_val(delta, b * ext.sd + d) + (bias ? bias[d] : 0.0f));
     const float w = dl * uu;
-    const int64_t bn = (int64_t)b * nr + 4 * q;
+    const int64_t bn = (int64_t)b * nr + 4 * q;                 // B_prev, theta rows
+    const int64_t bB = (int64_t)b * ext.sB + 4 * q, bC = (int64_t)b * ext.sC + 4 * q;
 
     float hn[4];
     if constexpr (ROT) { // (nr even: a pair exists whole or not at all)
@@ -99,8 +101,8 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
         float bu = w; // Bbar u / B: Euler Delta u, or the zero-order hold
         if constexpr (ZOH)
             bu = zoh_input(dl * ain[k], a, w, uu / ain[k]);
-        const float bk = kv[k] ? load_val(Bm, bn + k) : 0.0f;
-        const float ck = kv[k] ? load_val(Cm, bn + k) : 0.0f;
+        const float bk = kv[k] ? load_val(Bm, bB + k) : 0.0f;
+        const float ck = kv[k] ? load_val(Cm, bC + k) : 0.0f;
         if constexpr (TRAP) {
             const float bp = ext.B_prev && kv[k] ? load_val((const T *)ext.B_prev, bn + k) : 0.0f;
             hn[k] = __builtin_fmaf(a, hin[k], __builtin_fmaf(p_lb, bp, lm * w * bk));
@@ -127,7 +129,7 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
     if (q == 0) {
         float yv = yp + (Dv ? Dv[d] : 0.0f) * uu;
         if (z)
-            yv *= silu_f(load_val(z, c));
+            yv *= silu_f(load_val(z, b * ext.sz + d));
         store_val(y, c, yv);
     }
 }
@@ -145,6 +147,11 @@ static hipError_t launch_step(const StepLaunch &p, hipStream_t stream)
         const int64_t nb = p.batch - b0 < 65535 ? p.batch - b0 : 65535;
         const int64_t off_bd = b0 * p.d_inner, off_bn = b0 * nr;
         StepExt ext{};
+        ext.su = p.su;
+        ext.sd = p.sd;
+        ext.sz = p.sz;
+        ext.sB = p.sB;
+        ext.sC = p.sC;
         ext.lam = p.lam ? (const T *)p.lam + off_bd : nullptr;
         ext.u_prev = p.u_prev ? (const T *)p.u_prev + off_bd : nullptr;
         ext.B_prev = p.B_prev ? (const T *)p.B_prev + off_bn : nullptr;
@@ -152,19 +159,19 @@ static hipError_t launch_step(const StepLaunch &p, hipStream_t stream)
         if (gen)
             hipLaunchKernelGGL((state_update_kernel<T, N, DISC, ROT, true>),
                                dim3(gx, (uint32_t)nb), dim3(256), 0, stream,
-                               p.h + off_bd * nr, (const T *)p.u + off_bd,
-                               (const T *)p.delta + off_bd,
-                               p.z ? (const T *)p.z + off_bd : nullptr, (const T *)p.B + off_bn,
-                               (const T *)p.C + off_bn, p.A, p.D, p.bias, (T *)p.y + off_bd,
-                               (int32_t)p.d_inner, ext, (int32_t)nr);
+                               p.h + off_bd * nr, (const T *)p.u + b0 * p.su,
+                               (const T *)p.delta + b0 * p.sd,
+                               p.z ? (const T *)p.z + b0 * p.sz : nullptr,
+                               (const T *)p.B + b0 * p.sB, (const T *)p.C + b0 * p.sC, p.A, p.D,
+                               p.bias, (T *)p.y + off_bd, (int32_t)p.d_inner, ext, (int32_t)nr);
         else
             hipLaunchKernelGGL((state_update_kernel<T, N, DISC, ROT, false>),
                                dim3(gx, (uint32_t)nb), dim3(256), 0, stream,
-                               p.h + off_bd * nr, (const T *)p.u + off_bd,
-                               (const T *)p.delta + off_bd,
-                               p.z ? (const T *)p.z + off_bd : nullptr, (const T *)p.B + off_bn,
-                               (const T *)p.C + off_bn, p.A, p.D, p.bias, (T *)p.y + off_bd,
-                               (int32_t)p.d_inner, ext, (int32_t)nr);
+                               p.h + off_bd * nr, (const T *)p.u + b0 * p.su,
+                               (const T *)p.delta + b0 * p.sd,
+                               p.z ? (const T *)p.z + b0 * p.sz : nullptr,
+                               (const T *)p.B + b0 * p.sB, (const T *)p.C + b0 * p.sC, p.A, p.D,
+                               p.bias, (T *)p.y + off_bd, (int32_t)p.d_inner, ext, (int32_t)nr);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

@@ -400,6 +400,38 @@ def test_ext_validation(lib):
     assert scan_ext(lib, theta=TH, ws=TH + 64) == ALIAS
 
 
+def scan_rows(lib, strides, *, u=BASE, delta=BASE + 64 * MB, z=BASE + 200 * MB, N=16,
+              opts=None, y=BASE + 256 * MB):
+    e = ms.ScanExt(None, None, None, None, None, *strides)
+    o = ctypes.byref(opts) if opts is not None else None
+    return lib.mamba_scan_fwd_ext(u, delta, BASE + 128 * MB, BASE + 132 * MB, BASE + 136 * MB,
+                                  None, z, None, None, y, None, 2, 64, 128, N, BF16,
+                                  BASE + 1024 * MB, 1 << 30, o, ctypes.byref(e), None)
+
+
+def test_row_strides_validation(lib):
+    # (u, delta, z, B, C) strides in elements; 0 = contiguous
+    assert scan_rows(lib, (100, 0, 0, 0, 0)) == SHAPE          # shorter than d_inner = 128
+    assert scan_rows(lib, (0, 0, 0, 8, 0)) == SHAPE            # shorter than d_state
+    assert scan_rows(lib, (0, 0, -256, 0, 0)) == SHAPE
+    rows = ms.ScanOpts(0, 0, 0, ms.MAMBA_KERNEL_ROWS, 0, 0)
+    assert scan_rows(lib, (0, 0, 256, 0, 0), opts=rows) == UNSUP  # scalar family only
+    assert scan_rows(lib, (0, 0, 256, 0, 0), N=64) == UNSUP
+    # u and z as the two halves of one (2, 64, 256) buffer: the views may overlap each
+    # other, but y may not overlap z's strided extent (2 * 64 rows of 256 elements)
+    xz = BASE + 600 * MB
+    assert scan_rows(lib, (256, 0, 256, 0, 0), u=xz, z=xz + 256, y=xz + 2 * 64 * 512 - 2) \
+        == ALIAS
+    assert scan_rows(lib, (256, 0, 256, 0, 0), u=xz, z=xz + 256, y=xz + 2 * 64 * 512) \
+        not in (SHAPE, ALIAS, UNSUP)
+    # the size query sees the strides: they select the scalar family
+    e = ms.ScanExt(None, None, None, None, None, 0, 0, 10240, 0, 0)
+    assert lib.mamba_scan_fwd_workspace_size_ext(8, 4096, 5120, 16, ctypes.byref(e), None) \
+        == lib.mamba_scan_fwd_workspace_size(8, 4096, 5120, 16)
+    assert lib.mamba_scan_fwd_workspace_size_ext(2, 64, 128, 64, ctypes.byref(e), None) \
+        == ctypes.c_size_t(-1).value
+
+
 def test_ext_workspace(lib):
     plain = lib.mamba_scan_fwd_workspace_size_ext(8, 4096, 5120, 16, None, None)
     assert plain == lib.mamba_scan_fwd_workspace_size(8, 4096, 5120, 16)
