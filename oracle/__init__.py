@@ -60,6 +60,9 @@ class Oracle:
         lib.oracle_step_ext.argtypes = [_dp] * 10 + [_i64] * 3 + [ctypes.c_int] + [_dp] * 4
         lib.oracle_scan_bwd.restype = ctypes.c_int
         lib.oracle_scan_bwd.argtypes = [_dp] * 20 + [_i64] * 4 + [ctypes.c_int]
+        lib.oracle_scan_bwd_ext.restype = ctypes.c_int
+        lib.oracle_scan_bwd_ext.argtypes = ([_dp] * 11 + [ctypes.c_int] + [_dp] * 17 +
+                                            [_i64] * 4 + [ctypes.c_int])
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
@@ -147,6 +150,47 @@ class Oracle:
             batch, L, d_inner, d_state, int(nthreads))
         if rc != 0:
             raise ValueError("oracle_scan_bwd rejected its arguments")
+        return out
+
+    def scan_bwd_ext(self, u, delta, A, B, C, dy, D=None, z=None, bias=None, h0=None,
+                     dh_last=None, zoh: bool = False, lam=None, u_prev=None, B_prev=None,
+                     theta=None, nthreads: Optional[int] = None) -> dict:
+        """Gradients of sum(dy * y) + sum(dh_last * h_last) for the scan with the
+        zero-order hold, the trapezoid (lam, u_prev, B_prev) or the rotation (theta): the
+        keys of scan_bwd plus dlam, du_prev, dB_prev (trapezoid) and dtheta (rotation)."""
+        u = _c64(u)
+        batch, L, d_inner = u.shape
+        A = _c64(A)
+        d_state = A.shape[1]
+        delta, B, C, dy = _c64(delta), _c64(B), _c64(C), _c64(dy)
+        D, z, bias, h0, dh_last = _c64(D), _c64(z), _c64(bias), _c64(h0), _c64(dh_last)
+        lam, u_prev, B_prev, theta = _c64(lam), _c64(u_prev), _c64(B_prev), _c64(theta)
+        for a, shp, name in ((delta, u.shape, "delta"), (dy, u.shape, "dy"),
+                             (B, (batch, L, d_state), "B"), (C, (batch, L, d_state), "C"),
+                             (D, (d_inner,), "D"), (bias, (d_inner,), "bias"),
+                             (z, u.shape, "z"), (h0, (batch, d_inner, d_state), "h0"),
+                             (dh_last, (batch, d_inner, d_state), "dh_last"),
+                             (lam, u.shape, "lam"), (u_prev, (batch, d_inner), "u_prev"),
+                             (B_prev, (batch, d_state), "B_prev"),
+                             (theta, (batch, L, d_state // 2), "theta")):
+            _check(a, shp, name)
+        out = dict(du=np.zeros(u.shape), ddelta=np.zeros(u.shape), dA=np.zeros(A.shape),
+                   dB=np.zeros((batch, L, d_state)), dC=np.zeros((batch, L, d_state)),
+                   dD=np.zeros(d_inner), dz=np.zeros(u.shape), dbias=np.zeros(d_inner),
+                   dh0=np.zeros((batch, d_inner, d_state)), dlam=np.zeros(u.shape),
+                   du_prev=np.zeros((batch, d_inner)), dB_prev=np.zeros((batch, d_state)),
+                   dtheta=np.zeros((batch, L, d_state // 2)))
+        if nthreads is None:
+            nthreads = default_threads()
+        rc = self._lib.oracle_scan_bwd_ext(
+            _p(u), _p(delta), _p(A), _p(B), _p(C), _p(D), _p(z), _p(bias), _p(h0), _p(dy),
+            _p(dh_last), int(bool(zoh)), _p(lam), _p(u_prev), _p(B_prev), _p(theta),
+            _p(out["du"]), _p(out["ddelta"]), _p(out["dA"]), _p(out["dB"]), _p(out["dC"]),
+            _p(out["dD"]), _p(out["dz"]), _p(out["dbias"]), _p(out["dh0"]), _p(out["dlam"]),
+            _p(out["du_prev"]), _p(out["dB_prev"]), _p(out["dtheta"]),
+            batch, L, d_inner, d_state, int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_scan_bwd_ext rejected its arguments")
         return out
 
     # -- one decode step ------------------------------------------------------

@@ -475,3 +475,296 @@ int oracle_scan_bwd(const double *u, const double *delta, const double *A, const
     free(dA_part);
     return 0;
 }
+
+/*
+ * Gradients of the scan with the zero-order hold (zoh), the exponential-trapezoidal rule
+ * (lam, u_prev, B_prev) and the rotation (theta) -- the forward definition at the top of
+ * this file with those options -- for the loss with derivatives dy and dh_last.  The chain
+ * rule through each step, written out by hand (the pages give the forward rules only:
+ * "Understanding Mamba" section 12 for the zero-order hold, "State space models and the
+ * Mamba series" sections 2.1 and 2.2 for the other two).  Per step, with h' the previous
+ * state after the rotation and before the decay, a = exp(Delta A), mu = dLoss/dh_t:
+ *     dLoss/dh'      = a mu,     dLoss/dh_{t-1} = R^T (a mu)       (R the step's rotation)
+ *     dDelta        += sum_n mu A a h'  + (input term)'_Delta  + sum_k theta_k dphi_k
+ *     dA[n]         += mu Delta a h'    + (input term)'_A
+ * where dphi_k = dLoss/dphi_k = (a mu)_{2k+1} h'_{2k} - (a mu)_{2k} h'_{2k+1} for the pair
+ * angle phi_k = Delta theta_k (dR/dphi h' = the pair turned by a further quarter turn), and
+ * the input term is Delta B u (Euler), beta B u with beta = expm1(Delta A) / A (zero-order
+ * hold: d beta / dDelta = a, d beta / dA = (Delta a - beta) / A, Delta^2 / 2 at A = 0), or
+ * (1 - lam) Delta B_{t-1} u_{t-1} + lam Delta B u (trapezoid: its first part also sends
+ * gradient to u_{t-1} and B_{t-1} -- to u_prev and B_prev at t = 0 -- and
+ * dlam = sum_n mu Delta (B u - B_{t-1} u_{t-1})).  Outputs as oracle_scan_bwd plus dlam
+ * (batch, L, d_inner), du_prev (batch, d_inner), dB_prev (batch, d_state), dtheta
+ * (batch, L, d_state / 2); each of those may be NULL and is written when its option is on.
+ * Sums over channels (dB, dC, dB_prev, dtheta) and over batch rows are taken in index order.
+ */
+typedef struct {
+    const double *u, *delta, *A, *B, *C, *D, *z, *bias, *h0, *dy, *dh_last;
+    const double *lam, *u_prev, *B_prev, *theta;
+    double *du, *ddelta, *dB, *dC, *dz, *dh0, *dlam, *du_prev, *dB_prev, *dtheta;
+    double *dA_part, *dD_part, *dbias_part;
+    int64_t batch, L, Dn, N;
+    int64_t b_begin, b_end;
+    int zoh;
+} bwd_ext_job;
+
+static void bwd_ext_rows(const bwd_ext_job *j)
+{
+    const int64_t L = j->L, Dn = j->Dn, N = j->N, K = N / 2;
+    const size_t nn = (size_t)(N > 0 ? N : 1);
+    double *hs = (double *)malloc((size_t)(L + 1) * nn * sizeof(double));  /* h_t at t + 1 */
+    double *hpre = (double *)malloc((size_t)(L > 0 ? L : 1) * nn * sizeof(double)); /* h' */
+    double *mu = (double *)malloc(nn * sizeof(double));
+    double *nu = (double *)malloc(nn * sizeof(double));
+    double *lbk = (double *)malloc(nn * sizeof(double)); /* trapezoid look-back weights */
+    for (int64_t b = j->b_begin; b < j->b_end; ++b) {
+        if (j->dB)
+            for (int64_t i = 0; i < L * N; ++i)
+                j->dB[b * L * N + i] = 0.0;
+        if (j->dC)
+            for (int64_t i = 0; i < L * N; ++i)
+                j->dC[b * L * N + i] = 0.0;
+        if (j->dtheta && j->theta)
+            for (int64_t i = 0; i < L * K; ++i)
+                j->dtheta[b * L * K + i] = 0.0;
+        if (j->dB_prev && j->lam)
+            for (int64_t n = 0; n < N; ++n)
+                j->dB_prev[b * N + n] = 0.0;
+        for (int64_t d = 0; d < Dn; ++d) {
+            const double bias = j->bias ? j->bias[d] : 0.0;
+            const double u_pre = j->u_prev ? j->u_prev[b * Dn + d] : 0.0;
+            /* forward, keeping h' and h_t of every step */
+            for (int64_t n = 0; n < N; ++n)
+                hs[n] = j->h0 ? j->h0[(b * Dn + d) * N + n] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t bld = (b * L + t) * Dn + d, bln = (b * L + t) * N;
+                const double dt = oracle_softplus(j->delta[bld] + bias);
+                double *hp = hpre + t * N;
+                for (int64_t n = 0; n < N; ++n)
+                    hp[n] = hs[t * N + n];
+                if (j->theta)
+                    oracle_rotate(hp, j->theta + (b * L + t) * K, dt, N);
+                for (int64_t n = 0; n < N; ++n) {
+                    const double a = j->A[d * N + n];
+                    double in;
+                    if (j->lam) {
+                        const double bp = t > 0 ? j->B[bln - N + n]
+                                                : (j->B_prev ? j->B_prev[b * N + n] : 0.0);
+                        const double up = t > 0 ? j->u[bld - Dn] : u_pre;
+                        in = oracle_trap_input(j->lam[bld], dt, j->B[bln + n], j->u[bld], bp, up);
+                    } else {
+                        in = oracle_bbar(dt, a, j->B[bln + n], j->zoh) * j->u[bld];
+                    }
+                    hs[(t + 1) * N + n] = exp(dt * a) * hp[n] + in;
+                }
+            }
+            /* reverse */
+            for (int64_t n = 0; n < N; ++n) {
+                mu[n] = j->dh_last ? j->dh_last[(b * Dn + d) * N + n] : 0.0;
+                lbk[n] = 0.0;
+            }
+            double dD_acc = 0.0, dbias_acc = 0.0;
+            for (int64_t t = L - 1; t >= 0; --t) {
+                const int64_t bld = (b * L + t) * Dn + d, bln = (b * L + t) * N;
+                const double v = j->delta[bld] + bias;
+                const double dt = oracle_softplus(v);
+                const double ut = j->u[bld];
+                double s = (j->D ? j->D[d] : 0.0) * ut;
+                for (int64_t n = 0; n < N; ++n)
+                    s += j->C[bln + n] * hs[(t + 1) * N + n];
+                double gate = 1.0, dgate = 0.0;
+                if (j->z) {
+                    const double zt = j->z[bld];
+                    const double sig = 1.0 / (1.0 + exp(-zt));
+                    gate = zt * sig;
+                    dgate = sig * (1.0 + zt * (1.0 - sig));
+                }
+                const double ds = j->dy[bld] * gate;
+                if (j->dz)
+                    j->dz[bld] = j->z ? j->dy[bld] * s * dgate : 0.0;
+                double ddt = 0.0, du = ds * (j->D ? j->D[d] : 0.0), dl = 0.0;
+                const double lam = j->lam ? j->lam[bld] : 0.0;
+                const double up = t > 0 ? j->u[bld - Dn] : u_pre;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double Bn = j->B[bln + n];
+                    /* step t + 1's look-back term read u_t and B_t */
+                    if (j->lam) {
+                        du += lbk[n] * Bn;
+                        if (j->dB)
+                            j->dB[bln + n] += lbk[n] * ut;
+                    }
+                    mu[n] += ds * j->C[bln + n];                 /* mu_t */
+                    const double a = j->A[d * N + n];
+                    const double abar = exp(dt * a);
+                    const double hp = hpre[t * N + n];
+                    ddt += mu[n] * a * abar * hp;
+                    double dAn = mu[n] * dt * abar * hp;
+                    if (j->lam) {
+                        const double bp = t > 0 ? j->B[bln - N + n]
+                                                : (j->B_prev ? j->B_prev[b * N + n] : 0.0);
+                        ddt += mu[n] * ((1.0 - lam) * bp * up + lam * Bn * ut);
+                        du += mu[n] * lam * dt * Bn;
+                        if (j->dB)
+                            j->dB[bln + n] += mu[n] * lam * dt * ut;
+                        dl += mu[n] * dt * (Bn * ut - bp * up);
+                        lbk[n] = mu[n] * (1.0 - lam) * dt;       /* for step t - 1 */
+                    } else if (j->zoh) {
+                        const double beta = a != 0.0 ? expm1(dt * a) / a : dt;
+                        ddt += mu[n] * Bn * ut * abar;
+                        du += mu[n] * beta * Bn;
+                        if (j->dB)
+                            j->dB[bln + n] += mu[n] * beta * ut;
+                        dAn += mu[n] * Bn * ut * (a != 0.0 ? (dt * abar - beta) / a
+                                                           : 0.5 * dt * dt);
+                    } else {
+                        ddt += mu[n] * Bn * ut;
+                        du += mu[n] * dt * Bn;
+                        if (j->dB)
+                            j->dB[bln + n] += mu[n] * dt * ut;
+                    }
+                    if (j->dC)
+                        j->dC[bln + n] += ds * hs[(t + 1) * N + n];
+                    if (j->dA_part)
+                        j->dA_part[(b * Dn + d) * N + n] += dAn;
+                    nu[n] = abar * mu[n];                        /* dLoss/dh' */
+                }
+                if (j->theta) {
+                    const double *th = j->theta + (b * L + t) * K;
+                    for (int64_t k = 0; k < K; ++k) {
+                        const double *hp = hpre + t * N + 2 * k;
+                        const double dphi = nu[2 * k + 1] * hp[0] - nu[2 * k] * hp[1];
+                        ddt += th[k] * dphi;
+                        if (j->dtheta)
+                            j->dtheta[(b * L + t) * K + k] += dt * dphi;
+                        const double phi = dt * th[k], c = cos(phi), sn = sin(phi);
+                        mu[2 * k] = c * nu[2 * k] + sn * nu[2 * k + 1];       /* R^T nu */
+                        mu[2 * k + 1] = -sn * nu[2 * k] + c * nu[2 * k + 1];
+                    }
+                } else {
+                    for (int64_t n = 0; n < N; ++n)
+                        mu[n] = nu[n];
+                }
+                dD_acc += ds * ut;
+                const double dv = ddt / (1.0 + exp(-v));
+                j->du[bld] = du;
+                j->ddelta[bld] = dv;
+                if (j->dlam && j->lam)
+                    j->dlam[bld] = dl;
+                dbias_acc += dv;
+            }
+            /* the trapezoid's first look-back read u_prev and B_prev */
+            if (j->lam) {
+                double dup = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double bp = j->B_prev ? j->B_prev[b * N + n] : 0.0;
+                    dup += lbk[n] * bp;
+                    if (j->dB_prev)
+                        j->dB_prev[b * N + n] += lbk[n] * u_pre;
+                }
+                if (j->du_prev)
+                    j->du_prev[b * Dn + d] = dup;
+            }
+            if (j->dh0)
+                for (int64_t n = 0; n < N; ++n)
+                    j->dh0[(b * Dn + d) * N + n] = mu[n];
+            if (j->dD_part)
+                j->dD_part[b * Dn + d] = dD_acc;
+            if (j->dbias_part)
+                j->dbias_part[b * Dn + d] = dbias_acc;
+        }
+    }
+    free(lbk);
+    free(nu);
+    free(mu);
+    free(hpre);
+    free(hs);
+}
+
+static void *bwd_ext_thread(void *arg)
+{
+    bwd_ext_rows((const bwd_ext_job *)arg);
+    return NULL;
+}
+
+int oracle_scan_bwd_ext(const double *u, const double *delta, const double *A, const double *B,
+                        const double *C, const double *D, const double *z, const double *bias,
+                        const double *h0, const double *dy, const double *dh_last, int zoh,
+                        const double *lam, const double *u_prev, const double *B_prev,
+                        const double *theta, double *du, double *ddelta, double *dA,
+                        double *dB, double *dC, double *dD, double *dz, double *dbias,
+                        double *dh0, double *dlam, double *du_prev, double *dB_prev,
+                        double *dtheta, int64_t batch, int64_t L, int64_t d_inner,
+                        int64_t d_state, int nthreads)
+{
+    if (batch < 0 || L < 0 || d_inner < 0 || d_state < 0 || !A)
+        return -1;
+    if ((theta && d_state % 2 != 0) || (lam && zoh))
+        return -1;
+    if (L > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta))
+        return -1;
+    const int64_t Dn = d_inner, N = d_state;
+    double *dA_part = (double *)calloc((size_t)(batch * Dn * N > 0 ? batch * Dn * N : 1), sizeof(double));
+    double *dD_part = (double *)calloc((size_t)(batch * Dn > 0 ? batch * Dn : 1), sizeof(double));
+    double *dbias_part = (double *)calloc((size_t)(batch * Dn > 0 ? batch * Dn : 1), sizeof(double));
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > batch)
+        nthreads = (int)(batch > 0 ? batch : 1);
+    bwd_ext_job *jobs = (bwd_ext_job *)calloc((size_t)nthreads, sizeof(bwd_ext_job));
+    pthread_t *tids = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    for (int i = 0; i < nthreads; ++i) {
+        bwd_ext_job *j = &jobs[i];
+        j->u = u; j->delta = delta; j->A = A; j->B = B; j->C = C; j->D = D; j->z = z;
+        j->bias = bias; j->h0 = h0; j->dy = dy; j->dh_last = dh_last;
+        j->lam = lam; j->u_prev = u_prev; j->B_prev = B_prev; j->theta = theta;
+        j->du = du; j->ddelta = ddelta; j->dB = dB; j->dC = dC; j->dz = dz; j->dh0 = dh0;
+        j->dlam = dlam; j->du_prev = du_prev; j->dB_prev = dB_prev; j->dtheta = dtheta;
+        j->dA_part = dA_part; j->dD_part = dD_part; j->dbias_part = dbias_part;
+        j->batch = batch; j->L = L; j->Dn = Dn; j->N = N;
+        j->b_begin = batch * i / nthreads;
+        j->b_end = batch * (i + 1) / nthreads;
+        j->zoh = zoh;
+    }
+    if (L > 0) {
+        for (int i = 1; i < nthreads; ++i)
+            pthread_create(&tids[i], NULL, bwd_ext_thread, &jobs[i]);
+        bwd_ext_rows(&jobs[0]);
+        for (int i = 1; i < nthreads; ++i)
+            pthread_join(tids[i], NULL);
+    } else {
+        if (dh0)
+            for (int64_t i = 0; i < batch * Dn * N; ++i)
+                dh0[i] = dh_last ? dh_last[i] : 0.0;
+        if (lam && du_prev)
+            for (int64_t i = 0; i < batch * Dn; ++i)
+                du_prev[i] = 0.0;
+        if (lam && dB_prev)
+            for (int64_t i = 0; i < batch * N; ++i)
+                dB_prev[i] = 0.0;
+    }
+    if (dA)
+        for (int64_t i = 0; i < Dn * N; ++i) {
+            double s = 0.0;
+            for (int64_t b = 0; b < batch; ++b)
+                s += dA_part[b * Dn * N + i];
+            dA[i] = s;
+        }
+    if (dD || dbias)
+        for (int64_t d = 0; d < Dn; ++d) {
+            double sD = 0.0, sb = 0.0;
+            for (int64_t b = 0; b < batch; ++b) {
+                sD += dD_part[b * Dn + d];
+                sb += dbias_part[b * Dn + d];
+            }
+            if (dD)
+                dD[d] = sD;
+            if (dbias)
+                dbias[d] = sb;
+        }
+    free(tids);
+    free(jobs);
+    free(dbias_part);
+    free(dD_part);
+    free(dA_part);
+    return 0;
+}

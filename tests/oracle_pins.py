@@ -683,3 +683,90 @@ def pin_rotation_zero_split_decode(orc):
 PINS += [pin_trapezoid_lti_kernel, pin_trapezoid_limits, pin_trapezoid_affine_in_lambda,
          pin_trapezoid_split_and_decode, pin_rotation_complex_form, pin_rotation_pure_and_order,
          pin_rotation_zero_split_decode]
+
+
+# ----------------------------------------------------------------------------
+# gradients of the zero-order hold, the trapezoid and the rotation: central finite
+# differences of the forward oracle with the same option
+# ----------------------------------------------------------------------------
+
+EXT_KEY = {"u": "du", "delta": "ddelta", "A": "dA", "B": "dB", "C": "dC", "D": "dD",
+           "z": "dz", "bias": "dbias", "h0": "dh0", "lam": "dlam", "u_prev": "du_prev",
+           "B_prev": "dB_prev", "theta": "dtheta"}
+
+
+def _ext_loss(orc, case, dy, dh_last):
+    y, h = orc.scan(**case, nthreads=1)
+    return float(np.sum(dy * y) + np.sum(dh_last * h))
+
+
+def _ext_fd_check(orc, case, dy, dh_last, g, names, eps=1e-6, tol=3e-7):
+    for name in names:
+        base = case[name]
+        grad = g[EXT_KEY[name]]
+        scale = max(float(np.max(np.abs(grad))), 1e-12)
+        worst = 0.0
+        for idx in np.ndindex(base.shape):
+            h = eps * max(1.0, abs(base[idx]))
+            old = base[idx]
+            base[idx] = old + h
+            lp = _ext_loss(orc, case, dy, dh_last)
+            base[idx] = old - h
+            lm = _ext_loss(orc, case, dy, dh_last)
+            base[idx] = old
+            worst = max(worst, abs((lp - lm) / (2 * h) - grad[idx]) / scale)
+        assert worst < tol, (name, worst)
+
+
+def _ext_case(rng, *, zoh=False, trap=False, rot=False, prev=True, N=4):
+    case = random_case(rng, batch=2, L=6, Dn=3, N=N)
+    bl = case["u"].shape[:2]
+    if zoh:
+        case["zoh"] = True
+        case["A"][0, 1] = 0.0          # the A = 0 limit of the zero-order hold
+    if trap:
+        case["lam"] = rng.uniform(0.0, 1.0, case["u"].shape)
+        if prev:
+            case["u_prev"] = rng.standard_normal((bl[0], case["u"].shape[2]))
+            case["B_prev"] = rng.standard_normal((bl[0], N))
+    if rot:
+        case["theta"] = rng.uniform(-2.0, 2.0, bl + (N // 2,))
+    return case
+
+
+def pin_option_gradients_finite_differences(orc):
+    """Every gradient entry of the zero-order hold, the trapezoid (with and without the
+    input before t = 0) and the rotation (alone and with each of the other two) against
+    central differences of the forward oracle with that option."""
+    rng = np.random.default_rng(71)
+    for opts in (dict(zoh=True), dict(trap=True), dict(trap=True, prev=False), dict(rot=True),
+                 dict(rot=True, zoh=True), dict(rot=True, trap=True)):
+        case = _ext_case(rng, **opts)
+        dy = rng.standard_normal(case["u"].shape)
+        dh_last = rng.standard_normal(case["h0"].shape)
+        g = orc.scan_bwd_ext(dy=dy, dh_last=dh_last, **case)
+        names = ["u", "delta", "A", "B", "C", "D", "z", "bias", "h0"]
+        names += [k for k in ("lam", "u_prev", "B_prev", "theta") if k in case]
+        _ext_fd_check(orc, case, dy, dh_last, g, names)
+
+
+def pin_option_gradients_reduce_to_euler(orc):
+    """Without options the extended gradients are the Euler ones; lam = 1 (no look-back)
+    and theta = 0 give them too, with zero gradients for the look-back inputs."""
+    rng = np.random.default_rng(72)
+    case = random_case(rng, L=9, N=4)
+    dy = rng.standard_normal(case["u"].shape)
+    dh_last = rng.standard_normal(case["h0"].shape)
+    ref = orc.scan_bwd(dy=dy, dh_last=dh_last, **case)
+    for extra in ({}, dict(lam=np.ones(case["u"].shape),
+                           u_prev=rng.standard_normal((2, 6)),
+                           B_prev=rng.standard_normal((2, 4))),
+                  dict(theta=np.zeros(case["u"].shape[:2] + (2,)))):
+        g = orc.scan_bwd_ext(dy=dy, dh_last=dh_last, **case, **extra)
+        for k in ref:
+            assert rel_err(g[k], ref[k]) < 1e-12, (sorted(extra), k)
+        if "lam" in extra:
+            assert np.all(g["du_prev"] == 0.0) and np.all(g["dB_prev"] == 0.0)
+
+
+PINS += [pin_option_gradients_finite_differences, pin_option_gradients_reduce_to_euler]

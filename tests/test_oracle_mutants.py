@@ -92,6 +92,28 @@ MUTANTS = [
                                     "const double x = h[k], w = h[k + N / 2];")]),
     ("rot_step_missing", [("                oracle_rotate(hb, theta + b * (d_state / 2), dt, d_state);\n",
                            "")]),
+    # gradients of the zero-order hold, the trapezoid and the rotation
+    ("bwdx_zoh_dA_term_dropped", [("dAn += mu[n] * Bn * ut * (a != 0.0 ? (dt * abar - beta) / a",
+                                   "dAn += 0.0 * mu[n] * Bn * ut * (a != 0.0 ? (dt * abar - beta) / a")]),
+    ("bwdx_zoh_ddt_no_abar", [("ddt += mu[n] * Bn * ut * abar;", "ddt += mu[n] * Bn * ut;")]),
+    ("bwdx_zoh_du_euler", [("du += mu[n] * beta * Bn;", "du += mu[n] * dt * Bn;")]),
+    ("bwdx_zoh_limit_wrong", [(": 0.5 * dt * dt);", ": dt * dt);")]),
+    ("bwdx_trap_lookback_not_carried", [("lbk[n] = mu[n] * (1.0 - lam) * dt;", "lbk[n] = 0.0;")]),
+    ("bwdx_trap_lookback_lambda", [("lbk[n] = mu[n] * (1.0 - lam) * dt;",
+                                    "lbk[n] = mu[n] * lam * dt;")]),
+    ("bwdx_trap_dlam_sign", [("dl += mu[n] * dt * (Bn * ut - bp * up);",
+                              "dl += mu[n] * dt * (bp * up - Bn * ut);")]),
+    ("bwdx_trap_du_prev_ignored", [("dup += lbk[n] * bp;", "dup += 0.0 * bp;")]),
+    ("bwdx_rot_not_transposed", [("mu[2 * k] = c * nu[2 * k] + sn * nu[2 * k + 1];",
+                                  "mu[2 * k] = c * nu[2 * k] - sn * nu[2 * k + 1];"),
+                                 ("mu[2 * k + 1] = -sn * nu[2 * k] + c * nu[2 * k + 1];",
+                                  "mu[2 * k + 1] = sn * nu[2 * k] + c * nu[2 * k + 1];")]),
+    ("bwdx_rot_dphi_sign", [("const double dphi = nu[2 * k + 1] * hp[0] - nu[2 * k] * hp[1];",
+                             "const double dphi = nu[2 * k] * hp[1] - nu[2 * k + 1] * hp[0];")]),
+    ("bwdx_rot_dtheta_no_dt", [("j->dtheta[(b * L + t) * K + k] += dt * dphi;",
+                                "j->dtheta[(b * L + t) * K + k] += dphi;")]),
+    ("bwdx_rot_state_unrotated", [("oracle_rotate(hp, j->theta + (b * L + t) * K, dt, N);",
+                                   "(void)hp;")]),
 ]
 
 
