@@ -354,13 +354,16 @@ MAMBA_API mamba_status_t mamba_scan_bwd(const void *u, const void *delta, const 
                                         int64_t d_state, mamba_dtype_t dtype, void *workspace,
                                         size_t workspace_bytes, void *stream);
 
-/* mamba_scan_bwd with explicit options (opts NULL = auto).  Only n_spans may be set:
- * the sequence is split into that many spans (1..64) scanned in parallel and joined by
- * carry passes for the state (forward) and for its gradient (backward in time); the
- * automatic choice splits when the (batch row, 64-channel tile) units cannot fill the
- * device, and depends on the current device's compute-unit count.  Any other nonzero
- * field returns MAMBA_ERR_UNSUPPORTED.  Results agree across span counts up to float32
- * rounding. */
+/* mamba_scan_bwd with explicit options (opts NULL = auto).  n_spans: the sequence is
+ * split into that many spans (1..64) scanned in parallel and joined by carry passes for
+ * the state (forward) and for its gradient (backward in time); the automatic choice splits
+ * when the (batch row, 64-channel tile) units cannot fill the device, and depends on the
+ * current device's compute-unit count.  discretization: MAMBA_DISC_ZOH gives the gradients
+ * of the zero-order-hold scan (mamba_scan_fwd_ex with the same option): through Bbar =
+ * (exp(Delta A) - 1) / A B, dBbar/dDelta = Abar B and dBbar/dA = (Delta Abar - Bbar / B) / A
+ * B (Delta^2 / 2 B at A = 0); not with stored checkpoints (mamba_scan_bwd_ckpt,
+ * MAMBA_ERR_UNSUPPORTED).  Any other nonzero field returns MAMBA_ERR_UNSUPPORTED.  Results
+ * agree across span counts up to float32 rounding. */
 MAMBA_API mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *A,
                                            const void *B, const void *C, const float *D,
                                            const void *z, const float *delta_bias,

@@ -546,11 +546,12 @@ def mamba_conv1d_silu_update(state, x, w, conv_bias=None, *, out=None):
 
 
 def mamba_scan_bwd_workspace_size(batch: int, seqlen: int, d_inner: int, d_state: int,
-                                  n_spans: int = 0, with_ckpt: bool = False) -> int:
+                                  n_spans: int = 0, with_ckpt: bool = False,
+                                  discretization: str = "euler") -> int:
     """Workspace bytes of mamba_scan_bwd (with_ckpt: of the variant that reads the forward
     pass's checkpoints)."""
     lib = load_library()
-    o = ScanOpts(0, 0, int(n_spans), 0, 0, 0)
+    o = ScanOpts(0, 0, int(n_spans), 0, 0, DISCRETIZATIONS[discretization])
     f = lib.mamba_scan_bwd_ckpt_workspace_size if with_ckpt else lib.mamba_scan_bwd_workspace_size_ex
     n = f(batch, seqlen, d_inner, d_state, ctypes.byref(o))
     if n == ctypes.c_size_t(-1).value:
@@ -590,8 +591,9 @@ GRAD_NAMES = ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0")
 
 def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=None,
                    dh_last=None, *, want=GRAD_NAMES, out=None, workspace=None,
-                   n_spans: int = 0, ckpt=None) -> dict:
-    """Gradients of the selective scan (Euler); see include/mamba_scan.h.
+                   n_spans: int = 0, ckpt=None, discretization: str = "euler") -> dict:
+    """Gradients of the selective scan (Euler, or discretization="zoh"); see
+    include/mamba_scan.h.
 
     Returns a dict with the names of ``want`` (a subset of GRAD_NAMES; du and ddelta are
     always computed): du, ddelta, dz, dB, dC in the activations' dtype, dA, dD, dbias,
@@ -643,7 +645,9 @@ def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=No
             t = torch.empty(shape, dtype=dt, device=dev)
         res[name] = t
         ptrs[name] = _ptr(t, name, shape, dt, dev)
-    opts = ScanOpts(0, 0, int(n_spans), 0, 0, 0)
+    if discretization not in DISCRETIZATIONS:
+        raise ValueError(f"discretization must be one of {sorted(DISCRETIZATIONS)}")
+    opts = ScanOpts(0, 0, int(n_spans), 0, 0, DISCRETIZATIONS[discretization])
     p_ck = _ckpt_ptr(ckpt, batch, seqlen, d_inner, d_state, dev)
     size_f = (lib.mamba_scan_bwd_ckpt_workspace_size if ckpt is not None
               else lib.mamba_scan_bwd_workspace_size_ex)

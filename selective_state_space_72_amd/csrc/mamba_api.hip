@@ -425,6 +425,7 @@ struct BwdPlan {
     int n_spans;
     int64_t span_len;
     int fwd_waves, fwd_chunk; // forward span-summary pass (scalar family)
+    bool zoh;                 // zero-order-hold discretisation
 };
 
 mamba_status_t bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
@@ -435,8 +436,10 @@ mamba_status_t bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t 
     if (!bwd_variant(d_state, &waves, &p.seg_len))
         return MAMBA_ERR_UNSUPPORTED;
     if (opts && (opts->chunk_len || opts->waves || opts->kernel || opts->relay ||
-                 opts->discretization != MAMBA_DISC_EULER))
+                 (opts->discretization != MAMBA_DISC_EULER &&
+                  opts->discretization != MAMBA_DISC_ZOH)))
         return MAMBA_ERR_UNSUPPORTED;
+    p.zoh = opts && opts->discretization == MAMBA_DISC_ZOH;
     const bool fixed = opts && opts->n_spans;
     if (fixed && (opts->n_spans < 1 || opts->n_spans > 64))
         return MAMBA_ERR_UNSUPPORTED;
@@ -1290,8 +1293,8 @@ static mamba_status_t bwd_impl(const void *u, const void *delta, const float *A,
     const int64_t ckb = ext_ck ? ckpt_bytes(batch, seqlen, d_inner, np) : 0;
     if (ckb < 0)
         return MAMBA_ERR_BAD_SHAPE;
-    if (ext_ck && S != 8)
-        return MAMBA_ERR_UNSUPPORTED; // the forward stores the state every 8 steps
+    if (ext_ck && (S != 8 || plan.zoh))
+        return MAMBA_ERR_UNSUPPORTED; // the forward stores the state every 8 steps, for Euler
 
     // ---- workspace ----
     size_t off[12];
@@ -1426,6 +1429,7 @@ static mamba_status_t bwd_impl(const void *u, const void *delta, const float *A,
         E.relay_parts = 1;
         E.su = E.sd = E.sz = d_inner;
         E.sB = E.sC = d_state;
+        E.zoh = plan.zoh;
         if (launch_stage_bc(E, st) != hipSuccess || launch_scalar_end(E, st) != hipSuccess)
             return MAMBA_ERR_HIP;
         CarryLaunch K{};
@@ -1474,6 +1478,7 @@ static mamba_status_t bwd_impl(const void *u, const void *delta, const float *A,
     P.d_inner = d_inner;
     P.d_state = d_state;
     P.dtype = dt;
+    P.zoh = plan.zoh;
     if (launch_scan_bwd(P, st) != hipSuccess)
         return MAMBA_ERR_HIP;
     if (!padded)

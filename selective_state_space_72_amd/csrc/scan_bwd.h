@@ -27,6 +27,7 @@ struct BwdLaunch {
     float *mu_dec, *mu_loc, *mu_in;
     int64_t batch, L, d_inner, d_state;
     DType dtype;
+    bool zoh; // zero-order-hold input term (else Euler); not with ck_ext
 };
 
 // (waves, segment length) of the compiled backward variant for d_state; false if none.

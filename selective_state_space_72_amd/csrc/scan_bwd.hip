@@ -124,13 +124,19 @@ __device__ __forceinline__ T zero_val()
 // AB: keep the segment's decay factors in registers (else recompute them in the adjoint
 // sweep, one more exp per element, to save S * NQ registers).  WPE: waves per SIMD the
 // register allocation targets.  LR: the dB/dC lane sums through an LDS slab per wave (16
-// rows of 64 lanes; else the register butterfly).  CKE: the checkpoints hold every segment's entering state
-// already (written by the forward scan): no forward pass here, and a later span's entering
-// state is its first checkpoint.
-template <typename T, int N, int NW, int S, bool AB, int WPE, bool LR, bool GATED, bool CKE>
+// rows of 64 lanes; else the register butterfly).  CKE: the checkpoints hold every segment's
+// entering state already (written by the forward scan): no forward pass here, and a later
+// span's entering state is its first checkpoint.  ZOH: the zero-order-hold input term
+// beta B u, beta = expm1(Delta A) / A (d beta / dDelta = Abar, d beta / dA = Delta^2 psi(Delta
+// A) with psi(x) = (x e^x - e^x + 1) / x^2), which needs one more per-wave partial sum per
+// step (sum Abar mu B, for dDelta).
+template <typename T, int N, int NW, int S, bool AB, int WPE, bool LR, bool GATED, bool CKE,
+          bool ZOH = false>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 scan_bwd_kernel(BwdArgs p)
 {
+    static_assert(!(ZOH && CKE), "the forward stores checkpoints for the Euler rule only");
+    constexpr int NPL = ZOH ? 4 : 3; // per-wave partial sums per (step, channel)
     constexpr int NQ = N / NW;     // state indices per lane
     constexpr int BCW = 2 * NQ;    // B then C per step; also dB/dC values per step
     constexpr int RH = kRH;
@@ -143,8 +149,9 @@ scan_bwd_kernel(BwdArgs p)
     static_assert(BCW == 2 || BCW == 4 || BCW == 8, "butterfly handles 2 to 8 values per step");
     static_assert(S * BCW <= 64 && kTCF * NQ <= 64, "one lane load per B/C value");
 
-    __shared__ float4 s_in[S][64];       // Delta, Delta*u, ds per (step, channel)
-    __shared__ float s_p[3][RH][NW][64]; // readout, sum mu B, sum A mu Abar h per wave
+    __shared__ float4 s_in[S][64];       // Delta, Delta*u, ds (and u: ZOH) per (step, channel)
+    // readout, sum mu B (ZOH: sum mu beta B), sum A mu Abar h (and ZOH: sum Abar mu B)
+    __shared__ float s_p[NPL][RH][NW][64];
     __shared__ float s_bc[NW][S * BCW];  // this segment's B, C per wave: [step][B(NQ), C(NQ)]
     // LR: per wave 16 rows (a group of 16 / BCW steps' values) of 64 lanes, padded by 16
     // bytes so that the row reads below (16 consecutive lanes of one row per lane, rows
@@ -173,7 +180,7 @@ scan_bwd_kernel(BwdArgs p)
     const int seg_lo = (int)(t_begin / S);
     const int seg_hi = (int)((t_end + S - 1) / S);
 
-    float a2[NQ], an[NQ], h[NQ], hstart[NQ];
+    float a2[NQ], an[NQ], ia[NQ], h[NQ], hstart[NQ];
     const int64_t col_c = ((int64_t)b * Dn + dc) * N + n0;       // (b, dc, n0)
     const int64_t span_col = (int64_t)span * p.batch * Dn * N;   // span offset of [span][b][d][n]
 #pragma unroll
@@ -181,6 +188,7 @@ scan_bwd_kernel(BwdArgs p)
         const float av = p.A[(int64_t)dc * N + n0 + q];
         a2[q] = av * kLog2e;
         an[q] = av;
+        ia[q] = ZOH ? 1.0f / av : 0.0f;
         if (span == 0)
             h[q] = p.h0 ? p.h0[col_c + q] : 0.0f;
         else if constexpr (CKE) // unused: the span's first segment reads its checkpoint
@@ -242,7 +250,9 @@ scan_bwd_kernel(BwdArgs p)
             for (int k = 0; k < KF; ++k) {
                 const int tl = g + k * NW;
                 const float dl = softplus_f(widen(fd[k]) + bias_d);
-                s_f[(par * kTCF + tl) * 64 + lane] = make_float2(dl, dl * widen(fu[k]));
+                // (Delta, Delta u); ZOH: (Delta, u)
+                s_f[(par * kTCF + tl) * 64 + lane] =
+                    make_float2(dl, ZOH ? widen(fu[k]) : dl * widen(fu[k]));
             }
             if (lane < kTCF * NQ)
                 s_fb[(par * NW + g) * (kTCF * NQ) + lane] = widen(fb);
@@ -254,8 +264,11 @@ scan_bwd_kernel(BwdArgs p)
             for (int tl = 0; tl < kTCF; ++tl) {
                 const float2 w = s_f[(par * kTCF + tl) * 64 + lane];
 #pragma unroll
-                for (int i = 0; i < NQ; ++i)
-                    h[i] = __builtin_fmaf(decay_exp2(w.x, a2[i]), h[i], w.y * bs[tl * NQ + i]);
+                for (int i = 0; i < NQ; ++i) {
+                    const float a = decay_exp2(w.x, a2[i]);
+                    const float bu = ZOH ? zoh_input(w.x * an[i], a, w.x * w.y, w.y * ia[i]) : w.y;
+                    h[i] = __builtin_fmaf(a, h[i], bu * bs[tl * NQ + i]);
+                }
             }
             if ((t0 + kTCF) % S == 0) {
                 const int64_t seg = (t0 + kTCF) / S;
@@ -335,7 +348,7 @@ scan_bwd_kernel(BwdArgs p)
             e_sig[k] = hw_rcp(1.0f + hw_exp2(-v * kLog2e)); // softplus'(v)
             e_ds[k] = ds;
             e_dyg[k] = dyv * dgate;
-            s_in[tl][lane] = make_float4(dl, dl * uu, ds, 0.0f);
+            s_in[tl][lane] = make_float4(dl, dl * uu, ds, ZOH ? uu : 0.0f);
         }
         if (lane < S * BCW)
             s_bc[g][lane] = widen(bcv);
@@ -361,7 +374,8 @@ scan_bwd_kernel(BwdArgs p)
 #pragma unroll
                     for (int q = 0; q < NQ; ++q) {
                         const float a = decay_exp2(w.x, a2[q]);
-                        hc[q] = __builtin_fmaf(a, hc[q], w.y * s_bc[g][T_ * BCW + q]);
+                        const float bu = ZOH ? zoh_input(w.x * an[q], a, w.y, w.w * ia[q]) : w.y;
+                        hc[q] = __builtin_fmaf(a, hc[q], bu * s_bc[g][T_ * BCW + q]);
                         if constexpr (AB)
                             ab[T_][q] = a;
                         hs[T_][q] = hc[q];
@@ -381,7 +395,7 @@ scan_bwd_kernel(BwdArgs p)
             for (int tl = RH - 1; tl >= 0; --tl) {
                 const int T_ = part * RH + tl;
                 float xv[BCW];
-                float yp = 0.0f, p1 = 0.0f, p2 = 0.0f;
+                float yp = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
 #pragma unroll
                 for (int i = 0; i < BCW; ++i)
                     xv[i] = 0.0f;
@@ -393,21 +407,42 @@ scan_bwd_kernel(BwdArgs p)
                         const float cq = s_bc[g][T_ * BCW + NQ + q];
                         yp = __builtin_fmaf(cq, hs[T_][q], yp);
                         mu[q] = __builtin_fmaf(w.z, cq, mu[q]); // mu_t
-                        p1 = __builtin_fmaf(mu[q], bq, p1);
-                        xv[q] = mu[q] * w.y;                    // dB
                         xv[NQ + q] = w.z * hs[T_][q];           // dC
                         const float hp = T_ == 0 ? hin[q] : hs[T_ > 0 ? T_ - 1 : 0][q];
                         const float abq = AB ? ab[AB ? T_ : 0][q] : decay_exp2(w.x, a2[q]);
                         const float m2 = mu[q] * abq;           // Abar_t mu_t
                         const float qv = m2 * hp;
                         p2 = __builtin_fmaf(an[q], qv, p2);
-                        dA[q] = __builtin_fmaf(w.x, qv, dA[q]);
+                        if constexpr (ZOH) {
+                            // beta = Delta phi(x) and d beta / dA = Delta^2 psi(x), x = Delta A:
+                            // series below |x| = 1/16, else from Abar (as the forward)
+                            const float x = w.x * an[q];
+                            const float beta = zoh_input(x, abq, w.x, ia[q]);
+                            const float psi = __builtin_fmaf(
+                                x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(
+                                    x, 1.0f / 144.0f, 1.0f / 30.0f), 1.0f / 8.0f), 1.0f / 3.0f),
+                                0.5f);
+                            const float dbA = __builtin_fabsf(x) < 0.0625f
+                                                  ? w.x * w.x * psi
+                                                  : (w.x * abq - beta) * ia[q];
+                            const float mb = mu[q] * bq;
+                            p1 = __builtin_fmaf(mb, beta, p1);  // sum mu beta B
+                            p3 = __builtin_fmaf(m2, bq, p3);    // sum Abar mu B
+                            xv[q] = mu[q] * beta * w.w;         // dB
+                            dA[q] = __builtin_fmaf(w.x, qv, __builtin_fmaf(mb * w.w, dbA, dA[q]));
+                        } else {
+                            p1 = __builtin_fmaf(mu[q], bq, p1);
+                            xv[q] = mu[q] * w.y;                // dB
+                            dA[q] = __builtin_fmaf(w.x, qv, dA[q]);
+                        }
                         mu[q] = m2;
                     }
                 }
                 s_p[0][tl][g][lane] = yp;
                 s_p[1][tl][g][lane] = p1;
                 s_p[2][tl][g][lane] = p2;
+                if constexpr (ZOH)
+                    s_p[ZOH ? 3 : 0][tl][g][lane] = p3;
 
                 if constexpr (LR) {
                     // rows (tl % GS) * BCW + i of the slab; after the group's first step
@@ -506,17 +541,22 @@ scan_bwd_kernel(BwdArgs p)
                 const int tl = g + k * NW;
                 const int lt = tl - part * RH;
                 float Y = s_p[0][lt][0][lane], P1 = s_p[1][lt][0][lane], P2 = s_p[2][lt][0][lane];
+                float P3 = ZOH ? s_p[ZOH ? 3 : 0][lt][0][lane] : 0.0f;
 #pragma unroll
                 for (int w = 1; w < NW; ++w) {
                     Y += s_p[0][lt][w][lane];
                     P1 += s_p[1][lt][w][lane];
                     P2 += s_p[2][lt][w][lane];
+                    if constexpr (ZOH)
+                        P3 += s_p[ZOH ? 3 : 0][lt][w][lane];
                 }
                 if (!PARTIAL || tl < nt) {
                     const int64_t t = t0 + tl;
-                    const float ddt = __builtin_fmaf(e_u[k], P1, P2);
+                    // dDelta = sum mu (A Abar h' + B u) (Euler), sum Abar mu (A h' + B u) (ZOH);
+                    // du = ds D + Delta sum mu B (Euler), ds D + sum mu beta B (ZOH)
+                    const float ddt = __builtin_fmaf(e_u[k], ZOH ? P3 : P1, P2);
                     const float dd = ddt * e_sig[k];
-                    const float duv = __builtin_fmaf(e_ds[k], D_d, e_dl[k] * P1);
+                    const float duv = __builtin_fmaf(e_ds[k], D_d, ZOH ? P1 : e_dl[k] * P1);
                     dD_acc = __builtin_fmaf(e_ds[k], e_u[k], dD_acc);
                     db_acc += dd;
                     if (dvalid) {
@@ -841,7 +881,18 @@ hipError_t launch_bwd_t(const BwdLaunch &q, hipStream_t stream)
     a.n_spans = (int32_t)q.n_spans;
     a.span_len = (int32_t)(q.n_spans > 1 ? q.span_len : (q.L + S - 1) / S * S);
     const dim3 grid((uint32_t)(units * q.n_spans));
-    if (q.ck_ext) {
+    if (q.zoh) {
+        // The zero-order hold's extra per-element terms hold more registers: decay factors
+        // recomputed, two waves per SIMD, and the LDS slab for the lane sums (its registers
+        // would spill with the butterfly)
+        constexpr bool LRZ = true;
+        if (gated)
+            hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, false, 2, LRZ, true, false, true>),
+                               grid, dim3(64 * NW), 0, stream, a);
+        else
+            hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, false, 2, LRZ, false, false, true>),
+                               grid, dim3(64 * NW), 0, stream, a);
+    } else if (q.ck_ext) {
         if (gated)
             hipLaunchKernelGGL((scan_bwd_kernel<T, N, NW, S, AB, WPE, LR, true, true>), grid,
                                dim3(64 * NW), 0, stream, a);

@@ -1,0 +1,81 @@
+"""GPU parity of the backward pass with the zero-order hold (mamba_scan_bwd(...,
+discretization="zoh")) against the fp64 oracle's gradients of that rule
+(oracle.scan_bwd_ext(zoh=True), pinned by finite differences).  Metric and bounds of
+gpu_helpers: 1e-5 for fp32 inputs, 2e-2 for bf16.  Shapes span several 8-step segments,
+64-channel tiles with a ragged tail, sequence splits, and a d_state that runs padded.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_72_amd as ms
+from selective_state_space_72_amd import synth
+from gpu_helpers import DEV, TOL, from_dev, log, metric, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0")
+
+
+def case(n, dtype, *, batch=2, seqlen=150, d_inner=72, gate=True, seed=None):
+    cfg = dataclasses.replace(synth.CONFIGS["c3"], d_state=n, dtype=dtype, h0=True, gate=gate,
+                              batch=batch, seqlen=seqlen, d_inner=d_inner,
+                              seed=500 + n if seed is None else seed)
+    inp = synth.make_scan_inputs(cfg)
+    return inp, synth.make_upstream_grads(inp.cfg)
+
+
+def check(label, inp, g, **opts):
+    p = inp.params
+    log(f"case {label}: batch {inp.cfg.batch} L {inp.cfg.seqlen} D {inp.cfg.d_inner} "
+        f"N {inp.cfg.d_state} {inp.dtype} {opts}")
+    out = ms.mamba_scan_bwd(to_dev(inp.u), to_dev(inp.delta), to_dev(p.A), to_dev(inp.B),
+                            to_dev(inp.C), to_dev(g.dy), D=to_dev(p.D), z=to_dev(inp.z),
+                            delta_bias=to_dev(p.bias), h0=to_dev(inp.h0),
+                            dh_last=to_dev(g.dh_last), discretization="zoh", **opts)
+    torch.cuda.synchronize()
+    f = lambda a: synth.to_f64(a, inp.dtype)  # noqa: E731
+    ref = oracle.load().scan_bwd_ext(
+        f(inp.u), f(inp.delta), p.A.astype(np.float64), f(inp.B), f(inp.C), f(g.dy),
+        D=p.D.astype(np.float64), z=f(inp.z) if inp.z is not None else None,
+        bias=p.bias.astype(np.float64), h0=inp.h0.astype(np.float64),
+        dh_last=g.dh_last.astype(np.float64), zoh=True)
+    worst = {k: metric(from_dev(out[k]), ref[k]) for k in GRADS if out.get(k) is not None}
+    log(f"  {label}: " + ", ".join(f"{k} {v:.1e}" for k, v in worst.items()))
+    assert max(worst.values()) <= TOL[inp.dtype], worst
+
+
+@pytest.mark.parametrize("n", [4, 8, 16, 32, 12])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_zoh_backward(n, dtype):
+    inp, g = case(n, dtype)
+    check(f"zoh N={n}", inp, g)
+
+
+@pytest.mark.parametrize("n_spans", [2, 5])
+def test_zoh_backward_split(n_spans):
+    inp, g = case(16, synth.F32, batch=1, seqlen=300, d_inner=130, gate=False)
+    check(f"zoh split {n_spans}", inp, g, n_spans=n_spans)
+
+
+def test_zoh_backward_small_decays():
+    """|Delta A| below and above the 1/16 switch of the series: A spread over decades."""
+    inp, g = case(16, synth.F32, seed=77)
+    rng = np.random.default_rng(3)
+    inp.params.A = -np.exp(rng.uniform(np.log(1e-3), np.log(30.0), inp.params.A.shape)).astype(
+        np.float32)
+    check("zoh A over decades", inp, g)
+
+
+def test_zoh_backward_refuses_stored_checkpoints():
+    inp, g = case(16, synth.F32, batch=1, seqlen=64, d_inner=64)
+    p = inp.params
+    ck = ms.mamba_scan_ckpt_buffer(1, 64, 64, 16, DEV)
+    with pytest.raises(RuntimeError):
+        ms.mamba_scan_bwd(to_dev(inp.u), to_dev(inp.delta), to_dev(p.A), to_dev(inp.B),
+                          to_dev(inp.C), to_dev(g.dy), ckpt=ck, discretization="zoh")
