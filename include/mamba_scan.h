@@ -471,6 +471,47 @@ typedef struct {
     int64_t u_stride, delta_stride, z_stride, B_stride, C_stride;
 } mamba_scan_ext_t;
 
+/* ------------------------------------------------------------------------
+ * Backward of the scan with the Mamba-3 options of mamba_scan_ext_t: the gradients of
+ * mamba_scan_fwd_ext's outputs with lambda (with u_prev, B_prev) and/or theta given, with
+ * the Euler rule or (with theta only) the zero-order hold of opts->discretization -- the
+ * chain rule through the trapezoidal input term and the pair rotation.  Besides the
+ * outputs of mamba_scan_bwd (same shapes, dtypes, rules):
+ *   dlam     (batch, seqlen, d_inner) dtype   dLoss/dlambda        (lambda given; nullable)
+ *   du_prev  (batch, d_inner) dtype           dLoss/du_prev        (lambda given; nullable)
+ *   dB_prev  (batch, d_state) dtype           dLoss/dB_prev        (lambda given; nullable)
+ *   dtheta   (batch, seqlen, d_state/2) dtype dLoss/dtheta         (theta given; nullable)
+ * d_state 4, 8, 16 or 32 (even with theta); opts may set only discretization (n_spans 0 or
+ * 1: no sequence split); ext->ckpt and the row strides must be 0 (else
+ * MAMBA_ERR_UNSUPPORTED).  With neither lambda nor theta the call is mamba_scan_bwd_ex.
+ * This path runs one wave per 64 channels with every state of a channel in one lane: it
+ * is correct for any length, not fast (the large prefill gives it 640 waves). */
+typedef struct {
+    void *dlam;
+    void *du_prev;
+    void *dB_prev;
+    void *dtheta;
+} mamba_scan_ext_grads_t;
+
+MAMBA_API size_t mamba_scan_bwd_ext_workspace_size(int64_t batch, int64_t seqlen,
+                                                   int64_t d_inner, int64_t d_state,
+                                                   const mamba_scan_ext_t *ext,
+                                                   const mamba_scan_opts_t *opts);
+
+MAMBA_API mamba_status_t mamba_scan_bwd_ext(const void *u, const void *delta, const float *A,
+                                            const void *B, const void *C, const float *D,
+                                            const void *z, const float *delta_bias,
+                                            const float *h0, const void *dy,
+                                            const float *dh_last, void *du, void *ddelta,
+                                            float *dA, void *dB, void *dC, float *dD, void *dz,
+                                            float *d_delta_bias, float *dh0,
+                                            const mamba_scan_ext_t *ext,
+                                            const mamba_scan_ext_grads_t *ext_grads,
+                                            int64_t batch, int64_t seqlen, int64_t d_inner,
+                                            int64_t d_state, mamba_dtype_t dtype,
+                                            void *workspace, size_t workspace_bytes,
+                                            const mamba_scan_opts_t *opts, void *stream);
+
 /* Workspace size for mamba_scan_fwd_ext (ext and opts may be NULL). */
 MAMBA_API size_t mamba_scan_fwd_workspace_size_ext(int64_t batch, int64_t seqlen,
                                                    int64_t d_inner, int64_t d_state,

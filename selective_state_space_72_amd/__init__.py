@@ -43,8 +43,8 @@ EXPORTS = ("mamba_d_state_supported", "mamba_scan_fwd_workspace_size",
            "mamba_ssd_state_update",
            "mamba_scan_ckpt_size", "mamba_scan_bwd_ckpt_workspace_size", "mamba_scan_bwd_ckpt",
            "mamba_scan_fwd_relay_faults", "mamba_ssd_relay_faults", "mamba_scan_fwd_noalloc",
-           "mamba_probe_copy", "mamba_probe_issue",
-           "mamba_status_string")
+           "mamba_probe_copy", "mamba_probe_issue", "mamba_scan_bwd_ext_workspace_size",
+           "mamba_scan_bwd_ext", "mamba_status_string")
 
 
 class MambaError(RuntimeError):
@@ -81,6 +81,12 @@ class ScanExt(ctypes.Structure):
                 ("ckpt", ctypes.c_void_p), ("u_stride", ctypes.c_int64),
                 ("delta_stride", ctypes.c_int64), ("z_stride", ctypes.c_int64),
                 ("B_stride", ctypes.c_int64), ("C_stride", ctypes.c_int64)]
+
+
+class ScanExtGrads(ctypes.Structure):
+    """mamba_scan_ext_grads_t: gradients of lambda, u_prev, B_prev, theta."""
+    _fields_ = [("dlam", ctypes.c_void_p), ("du_prev", ctypes.c_void_p),
+                ("dB_prev", ctypes.c_void_p), ("dtheta", ctypes.c_void_p)]
 
 
 _vp = ctypes.c_void_p
@@ -125,6 +131,14 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mamba_scan_bwd.restype = ctypes.c_int
     lib.mamba_scan_bwd.argtypes = [_vp] * 20 + [_i64] * 4 + [ctypes.c_int, _vp, ctypes.c_size_t,
                                                               _vp]
+    lib.mamba_scan_bwd_ext_workspace_size.restype = ctypes.c_size_t
+    lib.mamba_scan_bwd_ext_workspace_size.argtypes = [_i64] * 4 + [ctypes.POINTER(ScanExt),
+                                                                   ctypes.POINTER(ScanOpts)]
+    lib.mamba_scan_bwd_ext.restype = ctypes.c_int
+    lib.mamba_scan_bwd_ext.argtypes = ([_vp] * 20 + [ctypes.POINTER(ScanExt),
+                                                     ctypes.POINTER(ScanExtGrads)] +
+                                       [_i64] * 4 + [ctypes.c_int, _vp, ctypes.c_size_t,
+                                                     ctypes.POINTER(ScanOpts), _vp])
     lib.mamba_scan_bwd_workspace_size_ex.restype = ctypes.c_size_t
     lib.mamba_scan_bwd_workspace_size_ex.argtypes = [_i64] * 4 + [ctypes.POINTER(ScanOpts)]
     lib.mamba_scan_bwd_ex.restype = ctypes.c_int
@@ -591,9 +605,12 @@ GRAD_NAMES = ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0")
 
 def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=None,
                    dh_last=None, *, want=GRAD_NAMES, out=None, workspace=None,
-                   n_spans: int = 0, ckpt=None, discretization: str = "euler") -> dict:
+                   n_spans: int = 0, ckpt=None, discretization: str = "euler", lam=None,
+                   u_prev=None, B_prev=None, theta=None) -> dict:
     """Gradients of the selective scan (Euler, or discretization="zoh"); see
-    include/mamba_scan.h.
+    include/mamba_scan.h.  With lam (u_prev, B_prev) or theta: the gradients of the scan
+    with those Mamba-3 options (mamba_scan_bwd_ext), adding dlam, du_prev, dB_prev or
+    dtheta to the result.
 
     Returns a dict with the names of ``want`` (a subset of GRAD_NAMES; du and ddelta are
     always computed): du, ddelta, dz, dB, dC in the activations' dtype, dA, dD, dbias,
@@ -648,6 +665,12 @@ def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=No
     if discretization not in DISCRETIZATIONS:
         raise ValueError(f"discretization must be one of {sorted(DISCRETIZATIONS)}")
     opts = ScanOpts(0, 0, int(n_spans), 0, 0, DISCRETIZATIONS[discretization])
+    if lam is not None or theta is not None:
+        if ckpt is not None:
+            raise ValueError("stored checkpoints are for the Euler rule without options")
+        return _bwd_m3(lib, res, ptrs, want, opts, dev, act, code, workspace,
+                       (p_u, p_delta, p_A, p_B, p_C, p_D, p_z, p_bias, p_h0, p_dy, p_dhl),
+                       batch, seqlen, d_inner, d_state, lam, u_prev, B_prev, theta)
     p_ck = _ckpt_ptr(ckpt, batch, seqlen, d_inner, d_state, dev)
     size_f = (lib.mamba_scan_bwd_ckpt_workspace_size if ckpt is not None
               else lib.mamba_scan_bwd_workspace_size_ex)
@@ -675,6 +698,47 @@ def mamba_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=No
     if st != 0:
         raise MambaError(st, "mamba_scan_bwd")
     return {k: v for k, v in res.items() if k in ("du", "ddelta") or k in want}
+
+
+def _bwd_m3(lib, res, ptrs, want, opts, dev, act, code, workspace, ins, batch, seqlen, d_inner,
+            d_state, lam, u_prev, B_prev, theta):
+    """mamba_scan_bwd_ext for mamba_scan_bwd with lam or theta."""
+    torch = _torch()
+    bld = (batch, seqlen, d_inner)
+    ext = ScanExt(_ptr(lam, "lam", bld, act, dev),
+                  _ptr(u_prev, "u_prev", (batch, d_inner), act, dev),
+                  _ptr(B_prev, "B_prev", (batch, d_state), act, dev),
+                  _ptr(theta, "theta", (batch, seqlen, d_state // 2), act, dev))
+    if seqlen == 0:  # (only the presence of the options matters)
+        ext.lambda_ = ext.lambda_ or (1 if lam is not None else None)
+        ext.theta = ext.theta or (1 if theta is not None else None)
+    extra = {}
+    if lam is not None:
+        extra["dlam"] = torch.empty(bld, dtype=act, device=dev)
+        extra["du_prev"] = torch.empty((batch, d_inner), dtype=act, device=dev)
+        extra["dB_prev"] = torch.empty((batch, d_state), dtype=act, device=dev)
+    if theta is not None:
+        extra["dtheta"] = torch.empty((batch, seqlen, d_state // 2), dtype=act, device=dev)
+    eg = ScanExtGrads(*[(extra[k].data_ptr() if k in extra and extra[k].numel() else None)
+                        for k in ("dlam", "du_prev", "dB_prev", "dtheta")])
+    need = lib.mamba_scan_bwd_ext_workspace_size(batch, seqlen, d_inner, d_state,
+                                                 ctypes.byref(ext), ctypes.byref(opts))
+    if need == ctypes.c_size_t(-1).value:
+        raise MambaError(4, "mamba_scan_bwd_ext_workspace_size")
+    ws = workspace
+    if need > 0 and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    p_ws = ws.data_ptr() if ws is not None and need > 0 else None
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = lib.mamba_scan_bwd_ext(*ins, ptrs["du"], ptrs["ddelta"], ptrs["dA"], ptrs["dB"],
+                                ptrs["dC"], ptrs["dD"], ptrs["dz"], ptrs["dbias"], ptrs["dh0"],
+                                ctypes.byref(ext), ctypes.byref(eg), batch, seqlen, d_inner,
+                                d_state, code, p_ws, ws_bytes, ctypes.byref(opts), _stream(dev))
+    if st != 0:
+        raise MambaError(st, "mamba_scan_bwd_ext")
+    out = {k: v for k, v in res.items() if k in ("du", "ddelta") or k in want}
+    out.update(extra)
+    return out
 
 
 _SSD_RELAY = {"auto": 0, "off": 1, "force": 2, "force_withheld": -2}

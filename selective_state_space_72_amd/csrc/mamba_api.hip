@@ -1512,6 +1512,211 @@ mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *
                     dtype, workspace, workspace_bytes, opts, stream);
 }
 
+// ---- backward with the Mamba-3 options (scan_bwd_m3.hip) ----
+
+// Options of a backward call with lambda or theta: Euler or (rotation only) the zero-order
+// hold, one span, d_state 4..32 compiled, contiguous inputs, no stored checkpoints.
+static mamba_status_t m3_bwd_check(int64_t d_state, const mamba_scan_ext_t *ext,
+                                   const mamba_scan_opts_t *opts, bool *zoh)
+{
+    *zoh = false;
+    if (!bwd_d_state_ok(d_state) || (ext->theta && d_state % 2 != 0) || ext->ckpt ||
+        ext->u_stride || ext->delta_stride || ext->z_stride || ext->B_stride || ext->C_stride)
+        return MAMBA_ERR_UNSUPPORTED;
+    if (opts) {
+        if (opts->chunk_len || opts->waves || opts->kernel || opts->relay || opts->n_spans > 1 ||
+            opts->n_spans < 0 ||
+            (opts->discretization != MAMBA_DISC_EULER && opts->discretization != MAMBA_DISC_ZOH))
+            return MAMBA_ERR_UNSUPPORTED;
+        *zoh = opts->discretization == MAMBA_DISC_ZOH;
+    }
+    if (*zoh && ext->lambda)
+        return MAMBA_ERR_UNSUPPORTED; // the trapezoid replaces the input term
+    return MAMBA_OK;
+}
+
+size_t mamba_scan_bwd_ext_workspace_size(int64_t batch, int64_t seqlen, int64_t d_inner,
+                                         int64_t d_state, const mamba_scan_ext_t *ext,
+                                         const mamba_scan_opts_t *opts)
+{
+    if (!ext || (!ext->lambda && !ext->theta))
+        return bwd_workspace_size(batch, seqlen, d_inner, d_state, opts, false);
+    int64_t t;
+    bool zoh;
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0 || !mul_ok(batch, seqlen, &t) ||
+        !mul_ok(t, d_inner, &t) || !mul_ok(t, d_state, &t) || !mul_ok(t, 8, &t) ||
+        m3_bwd_check(d_state, ext, opts, &zoh) != MAMBA_OK)
+        return (size_t)-1;
+    size_t off[6];
+    return m3_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, ext->theta != nullptr, off);
+}
+
+mamba_status_t mamba_scan_bwd_ext(const void *u, const void *delta, const float *A,
+                                  const void *B, const void *C, const float *D, const void *z,
+                                  const float *delta_bias, const float *h0, const void *dy,
+                                  const float *dh_last, void *du, void *ddelta, float *dA,
+                                  void *dB, void *dC, float *dD, void *dz, float *d_delta_bias,
+                                  float *dh0, const mamba_scan_ext_t *ext,
+                                  const mamba_scan_ext_grads_t *eg, int64_t batch,
+                                  int64_t seqlen, int64_t d_inner, int64_t d_state,
+                                  mamba_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                                  const mamba_scan_opts_t *opts, void *stream)
+{
+    if (!ext || (!ext->lambda && !ext->theta)) {
+        if (ext && (ext->ckpt || ext->u_stride || ext->delta_stride || ext->z_stride ||
+                    ext->B_stride || ext->C_stride))
+            return MAMBA_ERR_UNSUPPORTED;
+        return bwd_impl(u, delta, A, B, C, D, z, delta_bias, h0, dy, dh_last, nullptr, du,
+                        ddelta, dA, dB, dC, dD, dz, d_delta_bias, dh0, batch, seqlen, d_inner,
+                        d_state, dtype, workspace, workspace_bytes, opts, stream);
+    }
+    const void *lam = ext->lambda, *theta = ext->theta;
+    const void *u_prev = lam ? ext->u_prev : nullptr, *B_prev = lam ? ext->B_prev : nullptr;
+    void *dlam = eg ? eg->dlam : nullptr, *du_prev = eg ? eg->du_prev : nullptr;
+    void *dB_prev = eg ? eg->dB_prev : nullptr, *dtheta = eg ? eg->dtheta : nullptr;
+    if (!lam)
+        dlam = du_prev = dB_prev = nullptr;
+    if (!theta)
+        dtheta = nullptr;
+    // ---- sizes, dtype, options ----
+    if (batch < 0 || seqlen < 0 || d_inner < 0 || d_state <= 0)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (dtype != MAMBA_DTYPE_F32 && dtype != MAMBA_DTYPE_BF16)
+        return MAMBA_ERR_BAD_DTYPE;
+    bool zoh;
+    const mamba_status_t cs = m3_bwd_check(d_state, ext, opts, &zoh);
+    if (cs != MAMBA_OK)
+        return cs;
+    const int64_t es = dtype == MAMBA_DTYPE_F32 ? 4 : 2;
+    int64_t bld, bln, bdn, dn, t;
+    if (!mul_ok(batch, seqlen, &t) || !mul_ok(t, d_inner, &bld) || !mul_ok(bld, es, &t) ||
+        !mul_ok(batch, seqlen, &t) || !mul_ok(t, d_state, &bln) || !mul_ok(bln, es, &t) ||
+        !mul_ok(bld, d_state, &t) || !mul_ok(t, 8, &t) || !mul_ok(batch, d_inner, &t) ||
+        !mul_ok(t, d_state, &bdn) || !mul_ok(bdn, 4, &t) || !mul_ok(d_inner, d_state, &dn) ||
+        !mul_ok(dn, 4, &t) || d_inner > INT32_MAX || batch > INT32_MAX ||
+        batch * ((d_inner + 63) / 64) > INT32_MAX)
+        return MAMBA_ERR_BAD_SHAPE;
+    if (batch == 0 || d_inner == 0)
+        return MAMBA_OK;
+    // ---- pointers ----
+    const bool has_seq = seqlen > 0;
+    if (!A || (has_seq && (!u || !delta || !B || !C || !dy || !du || !ddelta)) ||
+        (has_seq && z && !dz))
+        return MAMBA_ERR_NULL_ARG;
+    if (!z)
+        dz = nullptr;
+    const void *elem_ptrs[] = {u, delta, B, C, z, dy, du, ddelta, dB, dC, dz, lam, u_prev,
+                               B_prev, theta, dlam, du_prev, dB_prev, dtheta};
+    for (const void *pp : elem_ptrs)
+        if (pp && !aligned(pp, (size_t)es))
+            return MAMBA_ERR_MISALIGNED;
+    const void *f32_ptrs[] = {A, D, delta_bias, h0, dh_last, dA, dD, d_delta_bias, dh0};
+    for (const void *pp : f32_ptrs)
+        if (pp && !aligned(pp, 4))
+            return MAMBA_ERR_MISALIGNED;
+    size_t off[6];
+    const size_t need = m3_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, theta != nullptr,
+                                               off);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return MAMBA_ERR_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 4))
+        return MAMBA_ERR_MISALIGNED;
+    // ---- aliasing: every output is disjoint from every input and every other output ----
+    const int64_t bd = batch * d_inner, bn = batch * d_state;
+    const Range r_in[] = {range_of(u, bld * es),           range_of(delta, bld * es),
+                          range_of(z, bld * es),           range_of(dy, bld * es),
+                          range_of(B, bln * es),           range_of(C, bln * es),
+                          range_of(A, dn * 4),             range_of(D, d_inner * 4),
+                          range_of(delta_bias, d_inner * 4), range_of(h0, bdn * 4),
+                          range_of(dh_last, bdn * 4),      range_of(lam, bld * es),
+                          range_of(u_prev, bd * es),       range_of(B_prev, bn * es),
+                          range_of(theta, bln / 2 * es)};
+    const Range r_out[] = {range_of(has_seq ? du : nullptr, bld * es),
+                           range_of(has_seq ? ddelta : nullptr, bld * es),
+                           range_of(has_seq ? dz : nullptr, bld * es),
+                           range_of(has_seq ? dB : nullptr, bln * es),
+                           range_of(has_seq ? dC : nullptr, bln * es),
+                           range_of(dA, dn * 4),
+                           range_of(dD, d_inner * 4),
+                           range_of(d_delta_bias, d_inner * 4),
+                           range_of(dh0, bdn * 4),
+                           range_of(has_seq ? dlam : nullptr, bld * es),
+                           range_of(du_prev, bd * es),
+                           range_of(dB_prev, bn * es),
+                           range_of(has_seq ? dtheta : nullptr, bln / 2 * es),
+                           range_of(need > 0 ? workspace : nullptr, (int64_t)need)};
+    const int n_out = (int)(sizeof(r_out) / sizeof(r_out[0]));
+    for (int i = 0; i < n_out; ++i) {
+        for (const Range &r : r_in)
+            if (overlaps(r_out[i], r))
+                return MAMBA_ERR_ALIASING;
+        for (int j = i + 1; j < n_out; ++j)
+            if (overlaps(r_out[i], r_out[j]))
+                return MAMBA_ERR_ALIASING;
+    }
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (!has_seq) {
+        // nothing ran: dh0 = dh_last, the parameters' and the look-back's gradients zero
+        hipError_t e = hipSuccess;
+        if (dh0)
+            e = launch_copy_state(dh0, dh_last, bdn, st);
+        if (e == hipSuccess && dA)
+            e = launch_copy_state(dA, nullptr, dn, st);
+        if (e == hipSuccess && dD)
+            e = launch_copy_state(dD, nullptr, d_inner, st);
+        if (e == hipSuccess && d_delta_bias)
+            e = launch_copy_state(d_delta_bias, nullptr, d_inner, st);
+        // (zero fills: rows of no source entries padded to one entry of 0)
+        if (e == hipSuccess && du_prev)
+            e = launch_pad_rows(du_prev, nullptr, bd, 0, 1, (int32_t)es, 0.0f, st);
+        if (e == hipSuccess && dB_prev)
+            e = launch_pad_rows(dB_prev, nullptr, bn, 0, 1, (int32_t)es, 0.0f, st);
+        return hip_status(e);
+    }
+    char *ws = static_cast<char *>(workspace);
+    M3BwdLaunch q{};
+    q.u = u;
+    q.delta = delta;
+    q.z = z;
+    q.dy = dy;
+    q.B = B;
+    q.C = C;
+    q.lam = lam;
+    q.u_prev = u_prev;
+    q.B_prev = B_prev;
+    q.theta = theta;
+    q.A = A;
+    q.D = D;
+    q.bias = delta_bias;
+    q.h0 = h0;
+    q.dh_last = dh_last;
+    q.du = du;
+    q.ddelta = ddelta;
+    q.dz = dz;
+    q.dB = dB;
+    q.dC = dC;
+    q.dlam = dlam;
+    q.du_prev = du_prev;
+    q.dB_prev = dB_prev;
+    q.dtheta = dtheta;
+    q.dA = dA;
+    q.dD = dD;
+    q.dbias = d_delta_bias;
+    q.dh0 = dh0;
+    q.ckpt = reinterpret_cast<float *>(ws + off[0]);
+    q.part = reinterpret_cast<float *>(ws + off[1]);
+    q.bprev_part = reinterpret_cast<float *>(ws + off[2]);
+    q.dA_part = reinterpret_cast<float *>(ws + off[3]);
+    q.dDb_part = reinterpret_cast<float *>(ws + off[4]);
+    q.batch = batch;
+    q.L = seqlen;
+    q.d_inner = d_inner;
+    q.d_state = d_state;
+    q.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+    q.zoh = zoh;
+    return hip_status(launch_scan_bwd_m3(q, st));
+}
+
 mamba_status_t mamba_scan_bwd_ckpt(const void *u, const void *delta, const float *A,
                                    const void *B, const void *C, const float *D, const void *z,
                                    const float *delta_bias, const float *h0, const void *dy,

@@ -30,6 +30,24 @@ struct BwdLaunch {
     bool zoh; // zero-order-hold input term (else Euler); not with ck_ext
 };
 
+// Backward of the scan with the Mamba-3 options (trapezoid lam/u_prev/B_prev, rotation
+// theta; the zero-order hold with the rotation): scan_bwd_m3.hip.  Workspace regions from
+// m3_bwd_workspace_bytes (offsets off[0..4], total off[5]): stored states, dB/dC/dtheta
+// tile partials, dB_prev tile partials, dA and dD/dbias per batch row.
+struct M3BwdLaunch {
+    const void *u, *delta, *z, *dy, *B, *C, *lam, *u_prev, *B_prev, *theta;
+    const float *A, *D, *bias, *h0, *dh_last;
+    void *du, *ddelta, *dz, *dB, *dC, *dlam, *du_prev, *dB_prev, *dtheta; // activation dtype
+    float *dA, *dD, *dbias, *dh0;
+    float *ckpt, *part, *bprev_part, *dA_part, *dDb_part; // workspace
+    int64_t batch, L, d_inner, d_state;
+    DType dtype;
+    bool zoh;
+};
+size_t m3_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
+                              bool rot, size_t off[6]);
+hipError_t launch_scan_bwd_m3(const M3BwdLaunch &p, hipStream_t stream);
+
 // (waves, segment length) of the compiled backward variant for d_state; false if none.
 bool bwd_variant(int64_t d_state, int *waves, int *seg_len);
 hipError_t launch_scan_bwd(const BwdLaunch &p, hipStream_t stream);

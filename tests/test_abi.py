@@ -706,3 +706,40 @@ def test_probe_argument_checks(lib):
     assert lib.mamba_probe_issue(0, 1, 0, 256, BASE, ctypes.byref(n), None) == 2
     assert lib.mamba_probe_issue(4, 1, 1, 256, BASE, ctypes.byref(n), None) == UNSUP
     assert lib.mamba_probe_issue(0, 1, 1, 256, None, ctypes.byref(n), None) == NULL
+
+
+# ---- backward with the Mamba-3 options (mamba_scan_bwd_ext) -------------------------------
+
+def bwd_m3(lib, *, lam=None, theta=None, N=16, L=64, opts=None, eg=None, ws=BASE + 1024 * MB,
+           ws_bytes=1 << 30, strides=(0, 0, 0, 0, 0)):
+    e = ms.ScanExt(lam, None, None, theta, None, *strides)
+    g = eg if eg is not None else ms.ScanExtGrads()
+    o = ctypes.byref(opts) if opts is not None else None
+    Z = BASE + 3000 * MB
+    return lib.mamba_scan_bwd_ext(BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 132 * MB,
+                                  BASE + 136 * MB, None, None, None, None, BASE + 140 * MB,
+                                  None, Z, Z + 64 * MB, None, None, None, None, None, None,
+                                  None, ctypes.byref(e), ctypes.byref(g), 2, L, 128, N, BF16,
+                                  ws, ws_bytes, o, None)
+
+
+def test_bwd_ext_validation(lib):
+    LAM, TH = BASE + 400 * MB, BASE + 500 * MB
+    assert bwd_m3(lib, lam=LAM, N=12) == UNSUP               # compiled sizes only
+    assert bwd_m3(lib, theta=TH, N=64) == UNSUP
+    zoh = ms.ScanOpts(0, 0, 0, 0, 0, ms.MAMBA_DISC_ZOH)
+    assert bwd_m3(lib, lam=LAM, opts=zoh) == UNSUP           # the trapezoid replaces the input
+    assert bwd_m3(lib, lam=LAM, opts=ms.ScanOpts(0, 0, 4, 0, 0, 0)) == UNSUP  # no split
+    assert bwd_m3(lib, theta=TH, strides=(0, 0, 256, 0, 0)) == UNSUP
+    assert bwd_m3(lib, lam=LAM, ws_bytes=1024) == WS
+    assert bwd_m3(lib, lam=LAM + 1) == ALIGN
+    # the look-back gradients may not overlap an input
+    assert bwd_m3(lib, lam=LAM, eg=ms.ScanExtGrads(LAM + 64, None, None, None)) == ALIAS
+    assert bwd_m3(lib, theta=TH, eg=ms.ScanExtGrads(None, None, None, BASE + 2)) == ALIAS
+    need = lib.mamba_scan_bwd_ext_workspace_size(2, 64, 128, 16,
+                                                 ctypes.byref(ms.ScanExt(LAM)), None)
+    assert need not in (0, ctypes.c_size_t(-1).value)
+    # without lambda and theta the size is the plain backward's
+    assert lib.mamba_scan_bwd_ext_workspace_size(2, 64, 128, 16, ctypes.byref(ms.ScanExt()),
+                                                 None) \
+        == lib.mamba_scan_bwd_workspace_size(2, 64, 128, 16)

@@ -79,3 +79,63 @@ def test_zoh_backward_refuses_stored_checkpoints():
     with pytest.raises(RuntimeError):
         ms.mamba_scan_bwd(to_dev(inp.u), to_dev(inp.delta), to_dev(p.A), to_dev(inp.B),
                           to_dev(inp.C), to_dev(g.dy), ckpt=ck, discretization="zoh")
+
+
+# ---- the Mamba-3 options: trapezoid (lam, u_prev, B_prev) and rotation (theta) ------------
+
+M3_GRADS = GRADS + ("dlam", "du_prev", "dB_prev", "dtheta")
+
+
+def check_m3(label, inp, g, m3, *, trap, rot, zoh=False, prev=True):
+    p = inp.params
+    log(f"case {label}: batch {inp.cfg.batch} L {inp.cfg.seqlen} D {inp.cfg.d_inner} "
+        f"N {inp.cfg.d_state} {inp.dtype} trap {trap} rot {rot} zoh {zoh}")
+    out = ms.mamba_scan_bwd(to_dev(inp.u), to_dev(inp.delta), to_dev(p.A), to_dev(inp.B),
+                            to_dev(inp.C), to_dev(g.dy), D=to_dev(p.D), z=to_dev(inp.z),
+                            delta_bias=to_dev(p.bias), h0=to_dev(inp.h0),
+                            dh_last=to_dev(g.dh_last),
+                            discretization="zoh" if zoh else "euler",
+                            lam=to_dev(m3.lam) if trap else None,
+                            u_prev=to_dev(m3.u_prev) if (trap and prev) else None,
+                            B_prev=to_dev(m3.B_prev) if (trap and prev) else None,
+                            theta=to_dev(m3.theta) if rot else None)
+    torch.cuda.synchronize()
+    f = lambda a: synth.to_f64(a, inp.dtype)  # noqa: E731
+    ref = oracle.load().scan_bwd_ext(
+        f(inp.u), f(inp.delta), p.A.astype(np.float64), f(inp.B), f(inp.C), f(g.dy),
+        D=p.D.astype(np.float64), z=f(inp.z) if inp.z is not None else None,
+        bias=p.bias.astype(np.float64), h0=inp.h0.astype(np.float64),
+        dh_last=g.dh_last.astype(np.float64), zoh=zoh,
+        lam=f(m3.lam) if trap else None,
+        u_prev=f(m3.u_prev) if (trap and prev) else None,
+        B_prev=f(m3.B_prev) if (trap and prev) else None,
+        theta=f(m3.theta) if rot else None)
+    worst = {}
+    for k in M3_GRADS:
+        if out.get(k) is None:
+            continue
+        if k in ("du_prev", "dB_prev") and not prev:
+            continue
+        assert tuple(out[k].shape) == ref[k].shape, (k, out[k].shape, ref[k].shape)
+        worst[k] = metric(from_dev(out[k]), ref[k])
+    log(f"  {label}: " + ", ".join(f"{k} {v:.1e}" for k, v in worst.items()))
+    assert max(worst.values()) <= TOL[inp.dtype], worst
+
+
+M3_CASES = [(16, True, False, False), (16, False, True, False), (16, True, True, False),
+            (16, False, True, True), (4, True, True, False), (8, False, True, False),
+            (32, True, False, False), (32, False, True, False)]
+
+
+@pytest.mark.parametrize("n,trap,rot,zoh", M3_CASES)
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_m3_backward(n, trap, rot, zoh, dtype):
+    inp, g = case(n, dtype, batch=2, seqlen=77, d_inner=96)
+    m3 = synth.make_mamba3_inputs(inp.cfg)
+    check_m3(f"m3 N={n}", inp, g, m3, trap=trap, rot=rot, zoh=zoh)
+
+
+def test_m3_backward_without_prev_and_gate():
+    inp, g = case(16, synth.F32, batch=1, seqlen=130, d_inner=70, gate=False)
+    m3 = synth.make_mamba3_inputs(inp.cfg)
+    check_m3("m3 no prev, no gate", inp, g, m3, trap=True, rot=True, prev=False)
