@@ -169,7 +169,7 @@ class BwdCase:
     """A backward-pass workload resident on the GPU: the scan's inputs, the upstream
     gradients dy and dh_last, preallocated gradient outputs and workspace."""
 
-    def __init__(self, cfg, dev):
+    def __init__(self, cfg, dev, discretization="euler", trapezoid=False, rotation=False):
         import torch
         import selective_state_space_72_amd as ms
         from selective_state_space_72_amd import synth
@@ -181,11 +181,26 @@ class BwdCase:
                                                       C=inp.C, A=p.A, D=p.D, bias=p.bias,
                                                       h0=inp.h0, dy=g.dy,
                                                       dh_last=g.dh_last).items()}
-        nws = ms.mamba_scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.d_inner, cfg.d_state)
-        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        es = 4 if cfg.dtype == synth.F32 else 2
+        # Mamba-3 options: their inputs, and their gradients among the outputs
+        self.ext = {"discretization": discretization}
+        extra_bytes = 0
+        if trapezoid or rotation:
+            m3 = synth.make_mamba3_inputs(cfg)
+            if trapezoid:
+                self.ext.update(lam=to_dev(m3.lam, dev), u_prev=to_dev(m3.u_prev, dev),
+                                B_prev=to_dev(m3.B_prev, dev))
+                extra_bytes += 2 * es * (m3.lam.size + m3.u_prev.size + m3.B_prev.size)
+            if rotation:
+                self.ext["theta"] = to_dev(m3.theta, dev)
+                extra_bytes += 2 * es * m3.theta.size
+            self.ws = None  # (sized by the binding; torch's caching allocator keeps it)
+        else:
+            nws = ms.mamba_scan_bwd_workspace_size(cfg.batch, cfg.seqlen, cfg.d_inner,
+                                                   cfg.d_state, discretization=discretization)
+            self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
         self.out = None
         self.step()
-        es = 4 if cfg.dtype == synth.F32 else 2
         bld = cfg.batch * cfg.seqlen * cfg.d_inner
         bln = cfg.batch * cfg.seqlen * cfg.d_state
         bdn = cfg.batch * cfg.d_inner * cfg.d_state
@@ -195,14 +210,16 @@ class BwdCase:
         # ddelta, dz out; B, C in and dB, dC out; A, D, bias in and their gradients out;
         # h0 in, dh_last in, dh0 out
         self.min_bytes = (bld * es * (act + 1) + bld * es * act + bln * es * 4 +
-                          (dn + 2 * cfg.d_inner) * 4 * 2 + bdn * 4 * (3 if cfg.h0 else 2))
+                          (dn + 2 * cfg.d_inner) * 4 * 2 + bdn * 4 * (3 if cfg.h0 else 2) +
+                          extra_bytes)
 
     def step(self):
         import selective_state_space_72_amd as ms
         t = self.t
         self.out = ms.mamba_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["dy"],
                                      D=t["D"], z=t["z"], delta_bias=t["bias"], h0=t["h0"],
-                                     dh_last=t["dh_last"], out=self.out, workspace=self.ws)
+                                     dh_last=t["dh_last"], out=self.out, workspace=self.ws,
+                                     **self.ext)
 
 
 class CkptTrainCase(BwdCase):
@@ -356,6 +373,24 @@ def extra_workloads(dev, flush, steps):
             "workload": f"backward of the {cfg.desc}: batch {cfg.batch}, L {cfg.seqlen}, "
                         f"d_inner {cfg.d_inner}, d_state {cfg.d_state}, {cfg.dtype}; du, "
                         "ddelta, dz, dB, dC, dA, dD, dbias, dh0 from dy and dh_last",
+            "ms": round(ms_used, 4), "ms_back_to_back": round(loop_ms, 4),
+            "GB_s": round(case.min_bytes / (ms_used * 1e-3) / 1e9, 1),
+            "gchan_steps_per_s": round(cfg.chan_steps / (ms_used * 1e-3) / 1e9, 2),
+            "hbm_frac": round(case.min_bytes / (ms_used * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del case
+        torch.cuda.empty_cache()
+    # backward of the large prefill with the discretisation variants
+    for name, opts in (("c3_bwd_zoh", dict(discretization="zoh")),
+                       ("c3_bwd_trapezoid", dict(trapezoid=True)),
+                       ("c3_bwd_rotation", dict(rotation=True))):
+        cfg = synth.CONFIGS["c3"]
+        case = BwdCase(cfg, dev, **opts)
+        loop_ms, med, _ = time_steps(case.step, max(10, steps // 4), 3, flush, warm_ms=100.0)
+        ms_used = med if med is not None else loop_ms
+        out[name] = {
+            "workload": f"backward of the {cfg.desc}: batch {cfg.batch}, L {cfg.seqlen}, "
+                        f"d_inner {cfg.d_inner}, d_state {cfg.d_state}, {cfg.dtype}"
+                        + "".join(labels[k] for k in opts) + "; all gradients",
             "ms": round(ms_used, 4), "ms_back_to_back": round(loop_ms, 4),
             "GB_s": round(case.min_bytes / (ms_used * 1e-3) / 1e9, 1),
             "gchan_steps_per_s": round(cfg.chan_steps / (ms_used * 1e-3) / 1e9, 2),

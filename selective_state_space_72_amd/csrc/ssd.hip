@@ -31,7 +31,7 @@
 // holds (4 consecutive n in each of two tiles) are exactly as many as an operand lane
 // takes, so C is read from LDS in the same permuted order and H never passes through LDS.
 // The causal tiles of S (10 of the 16 tiles of 16 x 16) are shared out among the waves
-// and M goes through LDS; the Xtil operand is formed in registers from X^T.
+// and M goes through LDS; the Xtil operand is formed in registers from columns of X.
 //
 // Precision.  The products use v_mfma_f32_16x16x32_bf16 for bf16 inputs and
 // v_mfma_f32_16x16x4f32 for fp32 inputs.  With bf16 inputs, X, B and C are exact bf16
@@ -44,9 +44,13 @@
 // chunk's last row, so rows past the end of the sequence read as zero and stores to them
 // are dropped.  The loads of the next chunk are issued before the current chunk's products
 // and land in registers; the block barriers wait only for LDS traffic, so those loads stay
-// in flight across them.  LDS matrices are unpadded, with the 16-byte granules of each row
-// permuted by an XOR key of the row, which puts the 16 rows of one operand load in distinct
-// banks (measured 7 % faster than 16-byte row padding, which keeps addresses affine).
+// in flight across them.  Every matrix is staged in LDS as rows only: the products that
+// contract over the steps (B^T Xtil, M X) take their X and B operands down the columns
+// with gfx950's transposing LDS reads, so no transposed copy is written.  C and M, read
+// only along rows, are unpadded with the 16-byte granules of each row permuted by an XOR
+// key of the row; X and B rows are padded by 32 bytes, which keeps their addresses affine
+// (unrolled column blocks are immediate offsets) and spreads the rows a transposing read
+// covers over distinct banks.
 // Blocks are numbered so that each XCD takes a contiguous range of (batch row, head) pairs:
 // the heads of one batch row share B and C in that XCD's L2.
 #include <atomic>
@@ -112,16 +116,11 @@ template <> struct Mma<float> {
     static __device__ __forceinline__ float to_float(E v) { return v; }
 };
 
-// Layout of an LDS matrix of RL elements per row (ES bytes each).  Padded: rows padded by
-// 16 bytes (addresses stay affine, so unrolled accesses are immediate offsets).  XOR: rows
-// unpadded, the 16-byte granules of row r permuted by a key of r.  Either puts the 16 rows
-// of one operand load (one column) in distinct banks.
-template <int RL, int ES, bool XOR> struct Lay;
-template <int RL, int ES> struct Lay<RL, ES, false> {
-    static constexpr int size(int rows) { return rows * (RL + 16 / ES); }
-    static __device__ __forceinline__ int idx(int r, int c) { return r * (RL + 16 / ES) + c; }
-};
-template <int RL, int ES> struct Lay<RL, ES, true> {
+// Layouts of the LDS matrices (RL elements of ES bytes per row; 64 banks of 4 bytes).
+// LayX: rows unpadded, the 16-byte granules of row r permuted by an XOR key of r, for the
+// matrices read along their rows (operand loads of 16 lanes on 16 consecutive rows at one
+// granule, which the key puts in distinct banks).
+template <int RL, int ES> struct LayX {
     static constexpr int size(int rows) { return rows * RL; }
     static __device__ __forceinline__ int idx(int r, int c)
     {
@@ -130,6 +129,15 @@ template <int RL, int ES> struct Lay<RL, ES, true> {
         const int key = RB == 128 ? (r >> 1) & 7 : r & 15;
         return r * RL + (((c / G) ^ key) * G) + (c % G);
     }
+};
+// LayT: rows padded by 32 bytes, so consecutive rows start 8 banks apart, for the matrices
+// also read down their columns (col_frag: 32 lanes on 8 consecutive rows, 32 bytes of
+// each).  Addresses stay affine in the column, so the column blocks of an unrolled loop are
+// immediate offsets of one address.
+template <int RL, int ES> struct LayT {
+    static constexpr int kPitch = RL + 32 / ES;
+    static constexpr int size(int rows) { return rows * kPitch; }
+    static __device__ __forceinline__ int idx(int r, int c) { return r * kPitch + c; }
 };
 
 // MFMA operand of KL contiguous elements at index i of an LDS matrix.
@@ -140,6 +148,33 @@ __device__ __forceinline__ typename Mma<T>::Frag frag(const typename Mma<T>::E *
         return *reinterpret_cast<const bf16x8 *>(m + i);
     else
         return m[i];
+}
+
+// MFMA operand running down a column of a row-major LDS matrix, the operand of a
+// contraction over the matrix's rows.  fp32: row r0 of column c0 + r16 (r16 = lane % 16).
+// bf16: operand slots 0..3 from rows r0 .. r0 + 3 and slots 4..7 from rows r1 .. r1 + 3 of
+// column c0 + r16 (r0, r1 may differ between the 16-lane groups), by two transposing reads
+// (ds_read_b64_tr_b16): within each 16-lane group, the lane with index l in the group
+// addresses the 4 elements at row r0 + l / 4, columns c0 + 4 (l % 4) .. + 3, and lane
+// 4a + b of the group receives element b of the lanes a, a + 4, a + 8, a + 12, in that
+// order (measured on gfx950), i.e. rows r0 .. r0 + 3 of column c0 + 4a + b.
+template <typename T, typename LAY>
+__device__ __forceinline__ typename Mma<T>::Frag col_frag(const typename Mma<T>::E *m, int r0,
+                                                          int r1, int c0, int r16)
+{
+    if constexpr (Mma<T>::KL == 8) {
+        typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+        typedef __attribute__((address_space(3))) __bf16 lds_bf16;
+        lds_bf16 *base = (lds_bf16 *)(const_cast<__bf16 *>(m));
+        const int dr = r16 >> 2, c = c0 + 4 * (r16 & 3);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)(base + LAY::idx(r0 + dr, c)));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)(base + LAY::idx(r1 + dr, c)));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+        return m[LAY::idx(r0, c0 + r16)];
+    }
 }
 
 // Split v into hi (its bf16 rounding) and lo (the bf16 rounding of v - hi).
@@ -167,16 +202,6 @@ __device__ __forceinline__ float dpp0(float v)
 __device__ __forceinline__ float lane_63(float v)
 {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-
-// Raw bits of element j of a 16-byte vector of bf16 or fp32 values.
-template <int ES>
-__device__ __forceinline__ uint32_t vec_elem(const u32x4 &v, int j)
-{
-    if constexpr (ES == 2)
-        return (v[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-    else
-        return v[j];
 }
 
 struct SsdArgs {
@@ -220,15 +245,14 @@ ssd_chunk_kernel(SsdArgs p)
     constexpr int NS = M::SPLIT ? 2 : 1;
     static_assert(N % 32 == 0 && Q == 64 && P == 64, "shape");
 
-    // X^T [p][t], B [s][n], B^T [n][s], C [t][n], M [t][s] (hi, then lo when split)
-    typedef Lay<Q, ES, true> LXT;
-    typedef Lay<N, ES, true> LB;
-    typedef Lay<Q, ES, true> LBT;
-    typedef Lay<N, ES, true> LC;
-    typedef Lay<Q, ES, true> LM;
-    __shared__ __attribute__((aligned(16))) E s_xt[LXT::size(P)];
+    // X [t][p], B [s][n], C [t][n], M [t][s] (hi, then lo when split), all row-major; X and
+    // B are also read down their columns (col_frag) as operands of B^T Xtil and M X
+    typedef LayT<P, ES> LX;
+    typedef LayT<N, ES> LB;
+    typedef LayX<N, ES> LC;
+    typedef LayX<Q, ES> LM;
+    __shared__ __attribute__((aligned(16))) E s_x[LX::size(Q)];
     __shared__ __attribute__((aligned(16))) E s_b[LB::size(Q)];
-    __shared__ __attribute__((aligned(16))) E s_bt[LBT::size(N)];
     __shared__ __attribute__((aligned(16))) E s_c[LC::size(Q)];
     __shared__ __attribute__((aligned(16))) E s_m[NS * LM::size(Q)];
     // per step: cumulative decay cs = cs_hi + cs_lo (a compensated sum: M uses differences
@@ -369,20 +393,14 @@ ssd_chunk_kernel(SsdArgs p)
                 fdt = __builtin_amdgcn_raw_buffer_load_b32(rd, lane * p.H * ES, 0, 0);
         }
     };
-    // the registers into LDS: X transposed, B as rows and transposed, C as rows
+    // the registers into LDS, as rows
     auto stage = [&]() {
 #pragma unroll
         for (int k = 0; k < XU; ++k) {
             const int cg = (tid & 7) + 8 * k;
 #pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const int i = LXT::idx(cg * G + j, 2 * rp);
-                const uint32_t a0 = vec_elem<ES>(fx[k][0], j), a1 = vec_elem<ES>(fx[k][1], j);
-                if constexpr (ES == 2)
-                    *reinterpret_cast<uint32_t *>(s_xt + i) = a0 | (a1 << 16);
-                else
-                    *reinterpret_cast<uint2 *>(s_xt + i) = make_uint2(a0, a1);
-            }
+            for (int i = 0; i < 2; ++i)
+                *reinterpret_cast<u32x4 *>(s_x + LX::idx(2 * rp + i, cg * G)) = fx[k][i];
         }
 #pragma unroll
         for (int k = 0; k < BU; ++k) {
@@ -392,15 +410,6 @@ ssd_chunk_kernel(SsdArgs p)
                 *reinterpret_cast<u32x4 *>(s_b + LB::idx(2 * rp + i, cg * G)) = fb[k][i];
                 if constexpr (!END)
                     *reinterpret_cast<u32x4 *>(s_c + LC::idx(2 * rp + i, cg * G)) = fc[k][i];
-            }
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const int i = LBT::idx(cg * G + j, 2 * rp);
-                const uint32_t a0 = vec_elem<ES>(fb[k][0], j), a1 = vec_elem<ES>(fb[k][1], j);
-                if constexpr (ES == 2)
-                    *reinterpret_cast<uint32_t *>(s_bt + i) = a0 | (a1 << 16);
-                else
-                    *reinterpret_cast<uint2 *>(s_bt + i) = make_uint2(a0, a1);
             }
         }
     };
@@ -554,7 +563,7 @@ ssd_chunk_kernel(SsdArgs p)
         }
 
         // ---- H_out = exp(cs_end) H_in + B^T Xtil on this wave's columns ----
-        F xf[Q / KI]; // X^T operands of this lane's column, also used by M X below
+        F xf[Q / KI]; // X operands down this lane's column, also used by M X below
         {
             const float dec = s_dec;
             if constexpr (END)
@@ -564,12 +573,15 @@ ssd_chunk_kernel(SsdArgs p)
                 hacc[m] *= dec;
 #pragma unroll
             for (int js = 0; js < Q / KI; ++js) {
-                const int tk = KI * js + KL * g;
-                xf[js] = frag<T>(s_xt, LXT::idx(pc, tk));
+                // the steps of this lane's operand slots: bf16, slots 0..3 at t0 .. t0 + 3
+                // and 4..7 at t0 + 16 .. t0 + 19 (an order of the contraction index that
+                // M X follows too); fp32, t0
+                const int k0 = KL == 8 ? KI * js + 4 * g : KI * js + g, k1 = k0 + 16;
+                xf[js] = col_frag<T, LX>(s_x, k0, k1, 16 * w, r16);
                 F xh, xl;
                 if constexpr (KL == 8) {
-                    const f32x4 w0 = *reinterpret_cast<const f32x4 *>(s_w + tk);
-                    const f32x4 w1 = *reinterpret_cast<const f32x4 *>(s_w + tk + 4);
+                    const f32x4 w0 = *reinterpret_cast<const f32x4 *>(s_w + k0);
+                    const f32x4 w1 = *reinterpret_cast<const f32x4 *>(s_w + k1);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         __bf16 a, c;
@@ -578,12 +590,12 @@ ssd_chunk_kernel(SsdArgs p)
                         xl[e] = c;
                     }
                 } else {
-                    xh = xf[js] * s_w[tk];
+                    xh = xf[js] * s_w[k0];
                     xl = 0.0f;
                 }
 #pragma unroll
                 for (int m = 0; m < NT; ++m) {
-                    const F a = frag<T>(s_bt, LBT::idx(16 * m + r16, tk));
+                    const F a = col_frag<T, LB>(s_b, k0, k1, 16 * m, r16);
                     hacc[m] = M::mma(a, xh, hacc[m]);
                     if constexpr (M::SPLIT)
                         hacc[m] = M::mma(a, xl, hacc[m]);
@@ -607,10 +619,27 @@ ssd_chunk_kernel(SsdArgs p)
             for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
                 for (int js = 0; js <= (16 * rt + 15) / KI; ++js) {
-                    const int i = LM::idx(16 * rt + r16, KI * js + KL * g);
-                    yacc[rt] = M::mma(frag<T>(s_m, i), xf[js], yacc[rt]);
+                    // M's columns in the order of xf's slots (s = 32 js + 4 g + 0..3, then
+                    // 32 js + 16 + 4 g + 0..3 for bf16)
+                    const int t = 16 * rt + r16;
+                    F mh, ml;
+                    if constexpr (KL == 8) {
+                        auto m8 = [&](const E *mm) {
+                            const bf16x4 a = *reinterpret_cast<const bf16x4 *>(
+                                mm + LM::idx(t, KI * js + 4 * g));
+                            const bf16x4 c = *reinterpret_cast<const bf16x4 *>(
+                                mm + LM::idx(t, KI * js + 16 + 4 * g));
+                            return __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7);
+                        };
+                        mh = m8(s_m);
+                        if constexpr (M::SPLIT)
+                            ml = m8(s_m + LM::size(Q));
+                    } else {
+                        mh = s_m[LM::idx(t, KI * js + g)];
+                    }
+                    yacc[rt] = M::mma(mh, xf[js], yacc[rt]);
                     if constexpr (M::SPLIT)
-                        yacc[rt] = M::mma(frag<T>(s_m + LM::size(Q), i), xf[js], yacc[rt]);
+                        yacc[rt] = M::mma(ml, xf[js], yacc[rt]);
                 }
             }
             const rsrc_t ry = make_rsrc(yb + t0 * row_x, ybytes);
