@@ -140,6 +140,27 @@ template <int RL, int ES> struct LayT {
     static __device__ __forceinline__ int idx(int r, int c) { return r * kPitch + c; }
 };
 
+// Staging map of a chunk's 64-row matrix of RB-byte rows: a thread's unit j is the 16-byte
+// granule gran(lane) of row row(j, w, lane), and each wave instruction covers whole rows, so
+// a quarter-wave's 16-byte writes cover 256 contiguous bytes of one row (RB >= 256) or two
+// 128-byte rows, D apart: rows that start 32 banks apart (D = 4 for the 32-byte-padded
+// LayT, whose rows start 40 banks apart) or rows of different parity (D = 1 for LayX).
+template <int RB, int D> struct StageMap {
+    static constexpr int LPR = RB / 16;           // lanes per row
+    static constexpr int U = 64 * LPR / kThreads; // units per thread
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row bytes");
+    static __device__ __forceinline__ int row(int j, int w, int lane)
+    {
+        if constexpr (LPR >= 16) {
+            return j * (kThreads / LPR) + w * (64 / LPR) + lane / LPR;
+        } else {
+            const int q = lane >> 4, h = (lane >> 3) & 1;
+            return 32 * j + 8 * w + (D == 4 ? q + 4 * h : 2 * q + h);
+        }
+    }
+    static __device__ __forceinline__ int gran(int lane) { return lane % LPR; }
+};
+
 // MFMA operand of KL contiguous elements at index i of an LDS matrix.
 template <typename T>
 __device__ __forceinline__ typename Mma<T>::Frag frag(const typename Mma<T>::E *m, int i)
@@ -352,14 +373,12 @@ ssd_chunk_kernel(SsdArgs p)
     for (int e = tid; e < NS * LM::size(Q); e += kThreads)
         s_m[e] = M::from_float(0.0f);
 
-    // ---- loads of one chunk into registers; a unit is rows (2 rp, 2 rp + 1) x one 16-byte
-    // column group cg: rp = tid / 8, cg = tid % 8 + 8k for the thread's k-th unit (8 lanes
-    // cover 128 contiguous bytes of a row) ----
-    constexpr int XU = P / G / 8; // X units per thread
-    constexpr int BU = N / G / 8; // B and C units per thread
-    static_assert(XU >= 1 && BU >= 1 && (Q / 2) * 8 == kThreads, "units");
-    const int rp = tid >> 3;
-    u32x4 fx[XU][2], fb[BU][2], fc[BU][2];
+    // ---- loads of one chunk into registers, then into LDS as rows (StageMap: each
+    // 16-byte unit of a thread is one granule of one row) ----
+    typedef StageMap<P * ES, 4> MX; // X, B: padded rows (LayT)
+    typedef StageMap<N * ES, 4> MB;
+    typedef StageMap<N * ES, 1> MC; // C: XOR-permuted rows (LayX)
+    u32x4 fx[MX::U], fb[MB::U], fc[MC::U];
     uint32_t fdt = 0;
     auto fetch = [&](int64_t c0) {
         const int nok = (int)min((int64_t)Q, t_end - c0);
@@ -367,23 +386,16 @@ ssd_chunk_kernel(SsdArgs p)
         const rsrc_t rb = make_rsrc(bb + c0 * row_b, (uint32_t)nok * row_b);
         const rsrc_t rc = make_rsrc(cb + c0 * row_b, (uint32_t)nok * row_b);
 #pragma unroll
-        for (int k = 0; k < XU; ++k) {
-            const int cg = (tid & 7) + 8 * k;
+        for (int j = 0; j < MX::U; ++j)
+            fx[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                rx, (int)(MX::row(j, w, lane) * row_x + MX::gran(lane) * 16), 0, 0);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                fx[k][i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rx, (int)((2 * rp + i) * row_x + cg * 16), 0, 0);
-        }
-#pragma unroll
-        for (int k = 0; k < BU; ++k) {
-            const int cg = (tid & 7) + 8 * k;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int off = (int)((2 * rp + i) * row_b + cg * 16);
-                fb[k][i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
-                if constexpr (!END) // (the span pass reads no C)
-                    fc[k][i] = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
-            }
+        for (int j = 0; j < MB::U; ++j) {
+            fb[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                rb, (int)(MB::row(j, w, lane) * row_b + MB::gran(lane) * 16), 0, 0);
+            if constexpr (!END) // (the span pass reads no C)
+                fc[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rc, (int)(MC::row(j, w, lane) * row_b + MC::gran(lane) * 16), 0, 0);
         }
         if (w == 3) {
             const rsrc_t rd = make_rsrc(db + c0 * p.H * ES, (uint32_t)((nok - 1) * p.H + 1) * ES);
@@ -393,24 +405,18 @@ ssd_chunk_kernel(SsdArgs p)
                 fdt = __builtin_amdgcn_raw_buffer_load_b32(rd, lane * p.H * ES, 0, 0);
         }
     };
-    // the registers into LDS, as rows
     auto stage = [&]() {
 #pragma unroll
-        for (int k = 0; k < XU; ++k) {
-            const int cg = (tid & 7) + 8 * k;
+        for (int j = 0; j < MX::U; ++j)
+            *reinterpret_cast<u32x4 *>(s_x + LX::idx(MX::row(j, w, lane), MX::gran(lane) * G)) =
+                fx[j];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                *reinterpret_cast<u32x4 *>(s_x + LX::idx(2 * rp + i, cg * G)) = fx[k][i];
-        }
-#pragma unroll
-        for (int k = 0; k < BU; ++k) {
-            const int cg = (tid & 7) + 8 * k;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                *reinterpret_cast<u32x4 *>(s_b + LB::idx(2 * rp + i, cg * G)) = fb[k][i];
-                if constexpr (!END)
-                    *reinterpret_cast<u32x4 *>(s_c + LC::idx(2 * rp + i, cg * G)) = fc[k][i];
-            }
+        for (int j = 0; j < MB::U; ++j) {
+            *reinterpret_cast<u32x4 *>(s_b + LB::idx(MB::row(j, w, lane), MB::gran(lane) * G)) =
+                fb[j];
+            if constexpr (!END)
+                *reinterpret_cast<u32x4 *>(s_c + LC::idx(MC::row(j, w, lane),
+                                                         MC::gran(lane) * G)) = fc[j];
         }
     };
 
@@ -487,6 +493,8 @@ ssd_chunk_kernel(SsdArgs p)
         lds_barrier(); // this chunk is in LDS; the previous chunk's M is no longer read
 
         // ---- the causal tiles of S = C B^T given to this wave, weighted into M ----
+        // (computed transposed, B C^T, so that a lane holds 4 consecutive s of one row t of
+        // M and writes them with one store per array)
         if constexpr (!END) {
 #pragma unroll
             for (int q = 0; q < 3; ++q) {
@@ -496,24 +504,38 @@ ssd_chunk_kernel(SsdArgs p)
                     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int ks = 0; ks < N / KI; ++ks)
-                        acc = M::mma(frag<T>(s_c, LC::idx(16 * r + r16, KI * ks + KL * g)),
-                                     frag<T>(s_b, LB::idx(16 * c + r16, KI * ks + KL * g)), acc);
-                    const int s = 16 * c + r16;
-                    const float css = s_cs[s], csls = s_csl[s], dls = s_dl[s];
-                    const f32x4 cst = *reinterpret_cast<const f32x4 *>(s_cs + 16 * r + 4 * g);
-                    const f32x4 cstl = *reinterpret_cast<const f32x4 *>(s_csl + 16 * r + 4 * g);
+                        acc = M::mma(frag<T>(s_b, LB::idx(16 * c + r16, KI * ks + KL * g)),
+                                     frag<T>(s_c, LC::idx(16 * r + r16, KI * ks + KL * g)), acc);
+                    const int t = 16 * r + r16, s0 = 16 * c + 4 * g;
+                    const float cst = s_cs[t], cstl = s_csl[t];
+                    const f32x4 css = *reinterpret_cast<const f32x4 *>(s_cs + s0);
+                    const f32x4 csls = *reinterpret_cast<const f32x4 *>(s_csl + s0);
+                    const f32x4 dls = *reinterpret_cast<const f32x4 *>(s_dl + s0);
+                    float mv[4];
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const int t = 16 * r + 4 * g + v;
-                        float m = s <= t ? acc[v] * hw_exp2((cst[v] - css) + (cstl[v] - csls)) * dls
+                        const int s = s0 + v;
+                        float m = s <= t ? acc[v] * hw_exp2((cst - css[v]) + (cstl - csls[v])) *
+                                               dls[v]
                                          : 0.0f;
                         if (s == t)
                             m += Dh;
-                        const int i = LM::idx(t, s);
-                        if constexpr (M::SPLIT)
-                            split_bf16(m, s_m[i], s_m[LM::size(Q) + i]);
-                        else
-                            s_m[i] = m;
+                        mv[v] = m;
+                    }
+                    const int i = LM::idx(t, s0);
+                    if constexpr (M::SPLIT) {
+                        bf16x4 hi, lo;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            __bf16 a, b2;
+                            split_bf16(mv[v], a, b2);
+                            hi[v] = a;
+                            lo[v] = b2;
+                        }
+                        *reinterpret_cast<bf16x4 *>(s_m + i) = hi;
+                        *reinterpret_cast<bf16x4 *>(s_m + LM::size(Q) + i) = lo;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(s_m + i) = f32x4{mv[0], mv[1], mv[2], mv[3]};
                     }
                 }
             }
