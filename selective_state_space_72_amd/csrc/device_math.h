@@ -47,6 +47,20 @@ __device__ __forceinline__ float softplus_f(float v) {
     return __builtin_fmaxf(v, 0.0f) + l;
 }
 
+// v + v of lane ^ 16, then + the same of lane ^ 32: the sum over the four lanes l % 16
+// (every lane gets it, in the same order).  v_permlane16_swap / v_permlane32_swap given
+// two copies of v exchange rows 0 <-> 1 and 2 <-> 3, resp. the wave's halves, between
+// them, so the two results hold v of the lane and of its partner.
+__device__ __forceinline__ float lane_pair_sum(float v)
+{
+    const uint32_t x = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    const float a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const uint32_t y = __float_as_uint(a);
+    const auto r2 = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+    return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+
 // Decay factor of one recurrence step, exp(Delta * A) = 2^(Delta * A'), A' = A log2(e).
 // v_exp_f32 rounds results just below 1 downward more often than to nearest: against a
 // correctly rounded exp2 its mean relative error is about -7e-9 for arguments in

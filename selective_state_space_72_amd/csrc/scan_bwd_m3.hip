@@ -13,15 +13,19 @@
 // and the trapezoid's look-back part sends mu_t (1 - lam_t) Delta_t to u_{t-1}, B_{t-1} (to
 // u_prev, B_prev at t = 0) with dlam_t = sum_n mu Delta (B_t u_t - B_{t-1} u_{t-1}).
 //
-// Work decomposition: one lane per channel holding all d_state states (the look-back and the
-// pair rotation stay inside a lane, no cross-wave sums), one wave per (batch row, 64-channel
-// tile).  The wave runs the forward once storing the state every 8 steps, then walks the
-// 8-step segments backwards; within a segment, sub-segments of S steps (the states of S
-// steps fit the registers) are recomputed from the stored state and their adjoint run.
-// Sums over the tile's channels (dB, dC, dtheta) go through an LDS slab (a row per value,
-// one lane per channel; each lane then adds one row) into per-tile partials, which a
-// second kernel adds in tile order.  This is the correctness-first path of these options:
-// a wave per 64 channels gives the large prefill 640 waves (less than one per SIMD).
+// Work decomposition: a block of four waves per (batch row, 64-channel tile); wave w takes
+// channels 16 w .. 16 w + 15 and lane c + 16 g of a wave holds channel c's states
+// g N/4 .. (g + 1) N/4 - 1 (whole rotation pairs), so the large prefill runs 2560 waves
+// (with the rotation at d_state 4: two waves of 32 channels, two states per lane).  The
+// block runs the forward once storing the state every 8 steps, then walks the 8-step
+// segments backwards; within a segment, sub-segments of S steps (whose states fit the
+// registers) are recomputed from the stored state and their adjoint run.  Per-channel sums
+// over the states (dDelta, du, dlam, the readout for dz) join the four lanes of a channel
+// with two lane exchanges.  Sums over the tile's channels (dB, dC, dtheta per step and state)
+// are added over each lane quad by DPP, written as 16 partials per value to an LDS slab
+// (4 quads x 4 waves), and summed there once per sub-segment into per-tile partials, which
+// a second kernel adds in tile order.  Every sum runs in a fixed order: results are
+// bitwise reproducible.
 #include <type_traits>
 
 #include "device_math.h"
@@ -47,132 +51,209 @@ struct M3Args {
     int32_t Dn, batch, n_seg;
 };
 
+// NV values of a vector of the activation type at element i (NV consecutive elements, i a
+// multiple of NV): one load of 2 NV or 4 NV bytes.
+template <typename T, int NV>
+__device__ __forceinline__ void load_vec(const void *base, int64_t i, float (&out)[NV])
+{
+    if constexpr (std::is_same<T, float>::value) {
+        const float *q = (const float *)base + i;
+        if constexpr (NV % 4 == 0) {
+#pragma unroll
+            for (int k = 0; k < NV; k += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(q + k);
+                out[k] = v.x; out[k + 1] = v.y; out[k + 2] = v.z; out[k + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NV; ++k)
+                out[k] = q[k];
+        }
+    } else {
+        const uint16_t *q = (const uint16_t *)base + i;
+        if constexpr (NV % 4 == 0) {
+#pragma unroll
+            for (int k = 0; k < NV; k += 4) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(q + k);
+                out[k] = __uint_as_float(v.x << 16);
+                out[k + 1] = __uint_as_float(v.x & 0xffff0000u);
+                out[k + 2] = __uint_as_float(v.y << 16);
+                out[k + 3] = __uint_as_float(v.y & 0xffff0000u);
+            }
+        } else if constexpr (NV == 2) {
+            const uint32_t v = *reinterpret_cast<const uint32_t *>(q);
+            out[0] = __uint_as_float(v << 16);
+            out[1] = __uint_as_float(v & 0xffff0000u);
+        } else {
+#pragma unroll
+            for (int k = 0; k < NV; ++k)
+                out[k] = load_val(q, k);
+        }
+    }
+}
+
+// v summed over the lane's quad (lanes 4i .. 4i + 3), every lane of the quad getting the
+// same sum: DPP quad_perm [1,0,3,2], then [2,3,0,1].
+__device__ __forceinline__ float quad_sum(float v)
+{
+    const float a = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1,
+                                                                    0xF, 0xF, false));
+    return a + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF,
+                                                          false));
+}
+
+// Groups of states per channel (lanes per channel): four, or two where four would split the
+// rotation pairs (d_state 4).
+template <int N, bool ROT> constexpr int m3_groups() { return ROT && N < 8 ? 2 : 4; }
+
 template <typename T, int N, bool ZOH, bool TRAP, bool ROT, bool GATED>
-__global__ void __launch_bounds__(64) scan_bwd_m3_kernel(M3Args p)
+__global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
 {
     static_assert(!(ZOH && TRAP), "the trapezoid replaces the input term");
-    constexpr int S = N <= 16 ? 4 : 2; // steps whose states are kept in registers
-    constexpr int SG = kM3Seg / S;      // sub-segments per stored state
+    constexpr int GR = m3_groups<N, ROT>(); // lanes per channel = waves per block
+    constexpr int CW = 64 / GR;           // channels per wave
+    constexpr int NT = 64 * GR;           // threads per block
+    static_assert(N % GR == 0 && (!ROT || (N / GR) % 2 == 0), "states per lane");
+    constexpr int NG = N / GR;            // states per lane: n = g NG + j
+    constexpr int KG = ROT ? NG / 2 : 1;  // rotation pairs per lane: k = g KG + kk
     constexpr int K = N / 2;
+    constexpr int S = NG <= 4 ? 8 : 4;    // steps whose states are kept in registers
+    constexpr int SG = kM3Seg / S;        // sub-segments per stored state
     constexpr int V = 2 * N + (ROT ? K : 0); // values summed over channels per step
-    constexpr int kRow = 68;                 // slab row: 64 lanes + 16 bytes
-    __shared__ __attribute__((aligned(16))) float s_v[V > N ? V : N][kRow];
+    constexpr int kQ = 16;                // partials per value: one per 4 channels
+    __shared__ __attribute__((aligned(16))) float s_v[S * V][kQ];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane % CW, g = lane / CW;
+    const int ch = CW * w + c; // channel within the tile
     const int unit = blockIdx.x; // tile * batch + b
     const int b = unit % p.batch, tile = unit / p.batch;
     const int Dn = p.Dn;
-    const int d = tile * 64 + lane;
+    const int d = tile * 64 + ch;
     const bool dvalid = d < Dn;
     const int dc = dvalid ? d : Dn - 1; // tail lanes compute on a valid channel with dy = 0
+    const int n0 = g * NG, k0 = g * KG;
+    const bool writer = (c & 3) == 0; // the lane that writes its quad's partials
+    // the sum over the GR lanes of a channel (every one of them gets it, in the same order)
+    auto chan_sum = [](float v) {
+        if constexpr (GR == 4) {
+            return lane_pair_sum(v);
+        } else {
+            const uint32_t x = __float_as_uint(v);
+            const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+            return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    };
+    const int qslot = ch >> 2;
     const int64_t L = p.L;
     const int64_t row0 = (int64_t)b * L;
     auto ld = [](const void *base, int64_t i) { return load_val((const T *)base, i); };
 
-    float a2[N], an[N], ia[N];
+    float a2[NG], an[NG], ia[NG];
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        const float av = p.A[(int64_t)dc * N + n];
-        a2[n] = av * kLog2e;
-        an[n] = av;
-        ia[n] = ZOH ? 1.0f / av : 0.0f;
+    for (int j = 0; j < NG; ++j) {
+        const float av = p.A[(int64_t)dc * N + n0 + j];
+        a2[j] = av * kLog2e;
+        an[j] = av;
+        ia[j] = ZOH ? 1.0f / av : 0.0f;
     }
     const float bias_d = p.bias ? p.bias[dc] : 0.0f;
     const float D_d = p.D ? p.D[dc] : 0.0f;
     const float u_pre = TRAP && p.u_prev ? ld(p.u_prev, (int64_t)b * Dn + dc) : 0.0f;
+    float bpre[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+        bpre[j] = 0.0f;
+    if (TRAP && p.B_prev)
+        load_vec<T, NG>(p.B_prev, (int64_t)b * N + n0, bpre);
 
-    // the look-back input (u, B) of step t: the previous step's, or (u_prev, B_prev)
-    auto lookback = [&](int64_t t, float &u_lb, float (&b_lb)[N]) {
+    // the look-back input (u, B of this lane's states) of step t: the previous step's, or
+    // (u_prev, B_prev)
+    auto lookback = [&](int64_t t, float &u_lb, float (&b_lb)[NG]) {
         if constexpr (TRAP) {
             if (t > 0) {
                 u_lb = ld(p.u, (row0 + t - 1) * Dn + dc);
-#pragma unroll
-                for (int n = 0; n < N; ++n)
-                    b_lb[n] = ld(p.B, (row0 + t - 1) * N + n);
+                load_vec<T, NG>(p.B, (row0 + t - 1) * N + n0, b_lb);
             } else {
                 u_lb = u_pre;
 #pragma unroll
-                for (int n = 0; n < N; ++n)
-                    b_lb[n] = p.B_prev ? ld(p.B_prev, (int64_t)b * N + n) : 0.0f;
+                for (int j = 0; j < NG; ++j)
+                    b_lb[j] = bpre[j];
             }
         }
     };
-    // one forward step: rotation, decay, input term; the look-back advances to step t
-    auto advance = [&](float (&h)[N], int64_t t, float &u_lb, float (&b_lb)[N]) {
+    // one forward step: rotation (its sine and cosine returned), decay, input term; the
+    // look-back advances to step t
+    auto advance = [&](float (&h)[NG], int64_t t, float &u_lb, float (&b_lb)[NG],
+                       float (&sn)[KG], float (&cs)[KG]) {
         const int64_t bld = (row0 + t) * Dn + dc;
         const float uu = ld(p.u, bld);
         const float dl = softplus_f(ld(p.delta, bld) + bias_d);
         if constexpr (ROT) {
+            float th[KG];
+            load_vec<T, KG>(p.theta, (row0 + t) * K + k0, th);
 #pragma unroll
-            for (int k = 0; k < K; ++k)
-                rotate_pair(dl * ld(p.theta, (row0 + t) * K + k), h[2 * k], h[2 * k + 1]);
+            for (int kk = 0; kk < KG; ++kk) {
+                sincos_fast(dl * th[kk], sn[kk], cs[kk]);
+                turn_pair(sn[kk], cs[kk], h[2 * kk], h[2 * kk + 1]);
+            }
         }
         const float lm = TRAP ? ld(p.lam, bld) : 0.0f;
+        float bn[NG];
+        load_vec<T, NG>(p.B, (row0 + t) * N + n0, bn);
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const float bn = ld(p.B, (row0 + t) * N + n);
-            const float a = decay_exp2(dl, a2[n]);
+        for (int j = 0; j < NG; ++j) {
+            const float a = decay_exp2(dl, a2[j]);
             float in;
             if constexpr (TRAP)
-                in = __builtin_fmaf((1.0f - lm) * dl * u_lb, b_lb[n], lm * dl * uu * bn);
+                in = __builtin_fmaf((1.0f - lm) * dl * u_lb, b_lb[j], lm * dl * uu * bn[j]);
             else if constexpr (ZOH)
-                in = zoh_input(dl * an[n], a, dl * uu, uu * ia[n]) * bn;
+                in = zoh_input(dl * an[j], a, dl * uu, uu * ia[j]) * bn[j];
             else
-                in = dl * uu * bn;
-            h[n] = __builtin_fmaf(a, h[n], in);
+                in = dl * uu * bn[j];
+            h[j] = __builtin_fmaf(a, h[j], in);
             if constexpr (TRAP)
-                b_lb[n] = bn;
+                b_lb[j] = bn[j];
         }
         if constexpr (TRAP)
             u_lb = uu;
-    };
-    // sums over the 64 lanes of NR values per lane (vals), written by lanes < NR to dst[row]
-    // (fixed order)
-    auto lane_sums = [&](auto NR_, const float (&vals)[decltype(NR_)::value], float *dst) {
-        constexpr int NR = decltype(NR_)::value;
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-            s_v[r][lane] = vals[r];
-        for (int r = lane; r < NR; r += 64) {
-            const float4 *src = reinterpret_cast<const float4 *>(&s_v[r][0]);
-            float s = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float4 c = src[i];
-                s += (c.x + c.y) + (c.z + c.w);
-            }
-            dst[r] = s;
-        }
     };
 
     float *ck = p.ckpt + (int64_t)unit * p.n_seg * N * 64;
 
     // ---- 1. forward: the state entering every 8-step segment ----
     {
-        float h[N], b_lb[N], u_lb = 0.0f;
+        float h[NG], b_lb[NG], u_lb = 0.0f, sn[KG], cs[KG];
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            h[n] = p.h0 ? p.h0[((int64_t)b * Dn + dc) * N + n] : 0.0f;
-            b_lb[n] = 0.0f;
+        for (int j = 0; j < NG; ++j) {
+            h[j] = p.h0 ? p.h0[((int64_t)b * Dn + dc) * N + n0 + j] : 0.0f;
+            b_lb[j] = 0.0f;
         }
         lookback(0, u_lb, b_lb);
-        for (int64_t t = 0; t < L; ++t) {
-            if (t % kM3Seg == 0) {
+        for (int seg = 0; seg < p.n_seg; ++seg) {
+            const int64_t t0 = (int64_t)seg * kM3Seg;
 #pragma unroll
-                for (int n = 0; n < N; ++n)
-                    ck[((t / kM3Seg) * N + n) * 64 + lane] = h[n];
+            for (int j = 0; j < NG; ++j)
+                ck[(seg * N + n0 + j) * 64 + ch] = h[j];
+            if (t0 + kM3Seg <= L) { // (no branch between the steps: their loads go ahead)
+#pragma unroll
+                for (int s = 0; s < kM3Seg; ++s)
+                    advance(h, t0 + s, u_lb, b_lb, sn, cs);
+            } else {
+                for (int64_t t = t0; t < L; ++t)
+                    advance(h, t, u_lb, b_lb, sn, cs);
             }
-            advance(h, t, u_lb, b_lb);
         }
     }
 
     // ---- 2. segments in reverse ----
-    float mu[N], dA[N], lbk[N];
+    float mu[NG], dA[NG], lbk[NG];
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
-        mu[n] = dvalid && p.dh_last ? p.dh_last[((int64_t)b * Dn + dc) * N + n] : 0.0f;
-        dA[n] = 0.0f;
-        lbk[n] = 0.0f; // mu_{t+1} (1 - lam_{t+1}) Delta_{t+1}: the look-back's weights
+    for (int j = 0; j < NG; ++j) {
+        mu[j] = dvalid && p.dh_last ? p.dh_last[((int64_t)b * Dn + dc) * N + n0 + j] : 0.0f;
+        dA[j] = 0.0f;
+        lbk[j] = 0.0f; // mu_{t+1} (1 - lam_{t+1}) Delta_{t+1}: the look-back's weights
     }
     float dD_acc = 0.0f, db_acc = 0.0f;
     for (int seg = p.n_seg - 1; seg >= 0; --seg) {
@@ -181,29 +262,30 @@ __global__ void __launch_bounds__(64) scan_bwd_m3_kernel(M3Args p)
         for (int sg = SG - 1; sg >= 0; --sg) {
             const int64_t ts = t0 + (int64_t)sg * S;
             if (ts >= t1)
-                continue;
+                continue; // (uniform over the block)
             const int ns = (int)min((int64_t)S, t1 - ts);
             // the state entering ts: the stored one, advanced through [t0, ts)
-            float hc[N], b_lb[N], u_lb = 0.0f;
+            float hc[NG], b_lb[NG], u_lb = 0.0f;
+            float rsn[S][KG], rcs[S][KG];
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-                hc[n] = ck[(seg * N + n) * 64 + lane];
-                b_lb[n] = 0.0f;
+            for (int j = 0; j < NG; ++j) {
+                hc[j] = ck[(seg * N + n0 + j) * 64 + ch];
+                b_lb[j] = 0.0f;
             }
             lookback(t0, u_lb, b_lb);
             for (int64_t t = t0; t < ts; ++t)
-                advance(hc, t, u_lb, b_lb);
-            float hin[N], hs[S][N];
+                advance(hc, t, u_lb, b_lb, rsn[0], rcs[0]);
+            float hin[NG], hs[S][NG];
 #pragma unroll
-            for (int n = 0; n < N; ++n)
-                hin[n] = hc[n];
+            for (int j = 0; j < NG; ++j)
+                hin[j] = hc[j];
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 if (s < ns)
-                    advance(hc, ts + s, u_lb, b_lb);
+                    advance(hc, ts + s, u_lb, b_lb, rsn[s], rcs[s]);
 #pragma unroll
-                for (int n = 0; n < N; ++n)
-                    hs[s][n] = hc[n];
+                for (int j = 0; j < NG; ++j)
+                    hs[s][j] = hc[j];
             }
             // adjoint, last step first
 #pragma unroll
@@ -226,85 +308,90 @@ __global__ void __launch_bounds__(64) scan_bwd_m3_kernel(M3Args p)
                 }
                 const float ds = dyv * gate;
                 const float lm = TRAP ? ld(p.lam, bld) : 0.0f;
-                float up = 0.0f, bp[N];
+                float up = 0.0f, bp[NG], bn[NG], cn[NG];
 #pragma unroll
-                for (int n = 0; n < N; ++n)
-                    bp[n] = 0.0f;
+                for (int j = 0; j < NG; ++j)
+                    bp[j] = 0.0f;
                 lookback(t, up, bp);
+                load_vec<T, NG>(p.B, (row0 + t) * N + n0, bn);
+                load_vec<T, NG>(p.C, (row0 + t) * N + n0, cn);
                 // h' : the previous state after the rotation
-                float hp[N];
+                float hp[NG];
 #pragma unroll
-                for (int n = 0; n < N; ++n)
-                    hp[n] = s == 0 ? hin[n] : hs[s > 0 ? s - 1 : 0][n];
+                for (int j = 0; j < NG; ++j)
+                    hp[j] = s == 0 ? hin[j] : hs[s > 0 ? s - 1 : 0][j];
                 if constexpr (ROT) {
 #pragma unroll
-                    for (int k = 0; k < K; ++k)
-                        rotate_pair(dl * ld(p.theta, (row0 + t) * K + k), hp[2 * k],
-                                    hp[2 * k + 1]);
+                    for (int kk = 0; kk < KG; ++kk)
+                        turn_pair(rsn[s][kk], rcs[s][kk], hp[2 * kk], hp[2 * kk + 1]);
                 }
-                float vals[V];
-                float sy = D_d * uu, ddt = 0.0f, du = ds * D_d, dlam = 0.0f;
+                float vb[NG], vc[NG], vt[KG];
+                float sy = 0.0f, ddt = 0.0f, du = 0.0f, dlam = 0.0f;
 #pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    const float cn = ld(p.C, (row0 + t) * N + n);
-                    sy = __builtin_fmaf(cn, hs[s][n], sy);
-                    mu[n] = __builtin_fmaf(ds, cn, mu[n]); // mu_t
-                    vals[N + n] = ds * hs[s][n];           // dC
+                for (int j = 0; j < NG; ++j) {
+                    sy = __builtin_fmaf(cn[j], hs[s][j], sy);
+                    mu[j] = __builtin_fmaf(ds, cn[j], mu[j]); // mu_t
+                    vc[j] = ds * hs[s][j];                    // dC
                 }
 #pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    const float bn = ld(p.B, (row0 + t) * N + n);
-                    const float a = decay_exp2(dl, a2[n]);
-                    const float mah = mu[n] * a * hp[n];
-                    ddt = __builtin_fmaf(an[n], mah, ddt);
-                    dA[n] = __builtin_fmaf(dl, mah, dA[n]);
+                for (int j = 0; j < NG; ++j) {
+                    const float a = decay_exp2(dl, a2[j]);
+                    const float mah = mu[j] * a * hp[j];
+                    ddt = __builtin_fmaf(an[j], mah, ddt);
+                    dA[j] = __builtin_fmaf(dl, mah, dA[j]);
                     if constexpr (TRAP) {
                         // this step's term, and step t + 1's look-back, which read u_t, B_t
-                        ddt += mu[n] * __builtin_fmaf(1.0f - lm, bp[n] * up, lm * bn * uu);
-                        du = __builtin_fmaf(__builtin_fmaf(mu[n], lm * dl, lbk[n]), bn, du);
-                        vals[n] = __builtin_fmaf(mu[n], lm * dl, lbk[n]) * uu; // dB
-                        dlam = __builtin_fmaf(mu[n] * dl, bn * uu - bp[n] * up, dlam);
-                        lbk[n] = mu[n] * (1.0f - lm) * dl;
+                        ddt += mu[j] * __builtin_fmaf(1.0f - lm, bp[j] * up, lm * bn[j] * uu);
+                        const float wgt = __builtin_fmaf(mu[j], lm * dl, lbk[j]);
+                        du = __builtin_fmaf(wgt, bn[j], du);
+                        vb[j] = wgt * uu; // dB
+                        dlam = __builtin_fmaf(mu[j] * dl, bn[j] * uu - bp[j] * up, dlam);
+                        lbk[j] = mu[j] * (1.0f - lm) * dl;
                     } else if constexpr (ZOH) {
-                        const float x = dl * an[n];
-                        const float beta = zoh_input(x, a, dl, ia[n]);
+                        const float x = dl * an[j];
+                        const float beta = zoh_input(x, a, dl, ia[j]);
                         const float psi = __builtin_fmaf(
                             x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(
                                 x, 1.0f / 144.0f, 1.0f / 30.0f), 1.0f / 8.0f), 1.0f / 3.0f),
                             0.5f);
                         const float dbA = __builtin_fabsf(x) < 0.0625f ? dl * dl * psi
-                                                                       : (dl * a - beta) * ia[n];
-                        ddt = __builtin_fmaf(mu[n] * bn * uu, a, ddt);
-                        du = __builtin_fmaf(mu[n] * beta, bn, du);
-                        vals[n] = mu[n] * beta * uu; // dB
-                        dA[n] = __builtin_fmaf(mu[n] * bn * uu, dbA, dA[n]);
+                                                                       : (dl * a - beta) * ia[j];
+                        ddt = __builtin_fmaf(mu[j] * bn[j] * uu, a, ddt);
+                        du = __builtin_fmaf(mu[j] * beta, bn[j], du);
+                        vb[j] = mu[j] * beta * uu; // dB
+                        dA[j] = __builtin_fmaf(mu[j] * bn[j] * uu, dbA, dA[j]);
                     } else {
-                        ddt = __builtin_fmaf(mu[n], bn * uu, ddt);
-                        du = __builtin_fmaf(mu[n] * dl, bn, du);
-                        vals[n] = mu[n] * dl * uu; // dB
+                        ddt = __builtin_fmaf(mu[j], bn[j] * uu, ddt);
+                        du = __builtin_fmaf(mu[j] * dl, bn[j], du);
+                        vb[j] = mu[j] * dl * uu; // dB
                     }
-                    mu[n] *= a; // nu = dLoss/dh'
+                    mu[j] *= a; // nu = dLoss/dh'
                 }
                 if constexpr (ROT) {
+                    float th[KG];
+                    load_vec<T, KG>(p.theta, (row0 + t) * K + k0, th);
 #pragma unroll
-                    for (int k = 0; k < K; ++k) {
-                        const float th = ld(p.theta, (row0 + t) * K + k);
-                        const float dphi = mu[2 * k + 1] * hp[2 * k] - mu[2 * k] * hp[2 * k + 1];
-                        ddt = __builtin_fmaf(th, dphi, ddt);
-                        vals[2 * N + k] = dl * dphi; // dtheta
+                    for (int kk = 0; kk < KG; ++kk) {
+                        const float dphi = mu[2 * kk + 1] * hp[2 * kk] - mu[2 * kk] * hp[2 * kk + 1];
+                        ddt = __builtin_fmaf(th[kk], dphi, ddt);
+                        vt[kk] = dl * dphi; // dtheta
                         // R^T nu: the pair turned back by the step's angle
-                        float sn, cs;
-                        sincos_fast(dl * th, sn, cs);
-                        const float x0 = mu[2 * k], x1 = mu[2 * k + 1];
-                        mu[2 * k] = __builtin_fmaf(cs, x0, sn * x1);
-                        mu[2 * k + 1] = __builtin_fmaf(cs, x1, -sn * x0);
+                        const float x0 = mu[2 * kk], x1 = mu[2 * kk + 1];
+                        mu[2 * kk] = __builtin_fmaf(rcs[s][kk], x0, rsn[s][kk] * x1);
+                        mu[2 * kk + 1] = __builtin_fmaf(rcs[s][kk], x1, -rsn[s][kk] * x0);
                     }
                 }
+                // per-channel sums over the four lanes of the channel
+                ddt = chan_sum(ddt);
+                du = chan_sum(du);
+                sy = chan_sum(sy) + D_d * uu;
+                if constexpr (TRAP)
+                    dlam = chan_sum(dlam);
                 const float dd = ddt * sig;
                 dD_acc = __builtin_fmaf(ds, uu, dD_acc);
                 db_acc += dd;
-                if (dvalid) {
-                    store_val((T *)p.du, bld, du);
+                if (dvalid && g == 0) {
+                    store_val((T *)p.du, bld, __builtin_fmaf(ds, D_d, du));
                     store_val((T *)p.ddelta, bld, dd);
                     if constexpr (GATED)
                         store_val((T *)p.dz, bld, dyv * sy * dgate);
@@ -312,36 +399,78 @@ __global__ void __launch_bounds__(64) scan_bwd_m3_kernel(M3Args p)
                         if (p.dlam)
                             store_val((T *)p.dlam, bld, dlam);
                 }
-                lane_sums(std::integral_constant<int, V>{}, vals,
-                          p.part + ((int64_t)unit * L + t) * V);
+                // sums over the tile's channels: quads by DPP, then the slab
+#pragma unroll
+                for (int j = 0; j < NG; ++j) {
+                    const float sb = quad_sum(vb[j]), sc = quad_sum(vc[j]);
+                    if (writer) {
+                        s_v[s * V + n0 + j][qslot] = sb;
+                        s_v[s * V + N + n0 + j][qslot] = sc;
+                    }
+                }
+                if constexpr (ROT) {
+#pragma unroll
+                    for (int kk = 0; kk < KG; ++kk) {
+                        const float st = quad_sum(vt[kk]);
+                        if (writer)
+                            s_v[s * V + 2 * N + k0 + kk][qslot] = st;
+                    }
+                }
             }
+            __syncthreads();
+            // the sub-segment's per-tile sums, each of the 16 partials in slot order
+            for (int e = tid; e < ns * V; e += NT) {
+                const float4 *src = reinterpret_cast<const float4 *>(&s_v[e][0]);
+                float sum = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kQ / 4; ++i) {
+                    const float4 q = src[i];
+                    sum += (q.x + q.y) + (q.z + q.w);
+                }
+                p.part[((int64_t)unit * L + ts) * V + e] = sum;
+            }
+            __syncthreads();
         }
     }
 
-    // ---- 3. per-wave results ----
+    // ---- 3. per-block results ----
     if constexpr (TRAP) {
         // the first look-back read u_prev and B_prev
-        float bpv[N], dup = 0.0f;
+        float dup = 0.0f;
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const float bp = p.B_prev ? ld(p.B_prev, (int64_t)b * N + n) : 0.0f;
-            dup = __builtin_fmaf(lbk[n], bp, dup);
-            bpv[n] = lbk[n] * u_pre;
+        for (int j = 0; j < NG; ++j) {
+            dup = __builtin_fmaf(lbk[j], bpre[j], dup);
+            const float sbp = quad_sum(lbk[j] * u_pre);
+            if (writer)
+                s_v[n0 + j][qslot] = sbp;
         }
-        if (dvalid && p.du_prev)
+        dup = chan_sum(dup);
+        if (dvalid && g == 0 && p.du_prev)
             store_val((T *)p.du_prev, (int64_t)b * Dn + d, dup);
-        lane_sums(std::integral_constant<int, N>{}, bpv, p.bprev_part + (int64_t)unit * N);
+        __syncthreads();
+        if (tid < N) {
+            const float4 *src = reinterpret_cast<const float4 *>(&s_v[tid][0]);
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kQ / 4; ++i) {
+                const float4 q = src[i];
+                sum += (q.x + q.y) + (q.z + q.w);
+            }
+            p.bprev_part[(int64_t)unit * N + tid] = sum;
+        }
     }
     if (dvalid) {
-        const int64_t col = ((int64_t)b * Dn + d) * N;
+        const int64_t col = ((int64_t)b * Dn + d) * N + n0;
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            p.dA_part[col + n] = dA[n];
+        for (int j = 0; j < NG; ++j) {
+            p.dA_part[col + j] = dA[j];
             if (p.dh0)
-                p.dh0[col + n] = mu[n];
+                p.dh0[col + j] = mu[j];
         }
-        p.dDb_part[((int64_t)b * Dn + d) * 2 + 0] = dD_acc;
-        p.dDb_part[((int64_t)b * Dn + d) * 2 + 1] = db_acc;
+        if (g == 0) {
+            p.dDb_part[((int64_t)b * Dn + d) * 2 + 0] = dD_acc;
+            p.dDb_part[((int64_t)b * Dn + d) * 2 + 1] = db_acc;
+        }
     }
 }
 
@@ -447,10 +576,10 @@ hipError_t launch_m3_t(const M3BwdLaunch &q, hipStream_t stream)
     a.n_seg = (int32_t)((q.L + kM3Seg - 1) / kM3Seg);
     if (q.z)
         hipLaunchKernelGGL((scan_bwd_m3_kernel<T, N, ZOH, TRAP, ROT, true>),
-                           dim3((uint32_t)units), dim3(64), 0, stream, a);
+                           dim3((uint32_t)units), dim3(64 * m3_groups<N, ROT>()), 0, stream, a);
     else
         hipLaunchKernelGGL((scan_bwd_m3_kernel<T, N, ZOH, TRAP, ROT, false>),
-                           dim3((uint32_t)units), dim3(64), 0, stream, a);
+                           dim3((uint32_t)units), dim3(64 * m3_groups<N, ROT>()), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
