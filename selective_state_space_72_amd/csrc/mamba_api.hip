@@ -417,8 +417,9 @@ size_t workspace_bytes_for(int64_t batch, int64_t seqlen, int64_t d_inner, int64
 // Backward launch plan: the compiled variant's segment length, and the sequence split.
 // Units of (batch row, 64-channel tile) run two blocks per compute unit.  The split costs
 // two summary passes over the whole sequence (about a third more work) whatever the span
-// count, so it is used only when the units cannot even give every compute unit one block;
-// then the sequence is cut into enough spans (a power of two, at most 64, each at least 64
+// count, so it is used only when the units cannot even give every compute unit one block,
+// or (zero-order hold) when they overflow one round of two blocks per compute unit; then
+// the sequence is cut into enough spans (a power of two, at most 64, each at least 64
 // steps) for about four full rounds of blocks.
 struct BwdPlan {
     int seg_len;
@@ -450,7 +451,10 @@ mamba_status_t bwd_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t 
     } else if (seqlen >= 128) {
         const int64_t units = batch * ((d_inner + 63) / 64);
         const int64_t cus = cu_count();
-        if (units < cus) {
+        // The zero-order hold's variant holds two blocks per compute unit: past one round of
+        // them, the split also evens out the partial last round (640 units at the large
+        // prefill: 7.8 ms unsplit, 6.7 / 6.4 / 6.5 ms in 2 / 4 / 8 spans).
+        if (units < cus || (p.zoh && units > cus * 2)) {
             const int64_t want = cus * 2 /*blocks each*/ * 4 /*rounds*/;
             while (units * n < want && n < 64 && seqlen / (2 * n) >= 64)
                 n *= 2;

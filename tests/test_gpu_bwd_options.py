@@ -63,6 +63,25 @@ def test_zoh_backward_split(n_spans):
     check(f"zoh split {n_spans}", inp, g, n_spans=n_spans)
 
 
+def test_zoh_backward_auto_split_past_one_round():
+    """More (batch row, tile) units than one round of two blocks per compute unit (576 on
+    256 CUs): the planner splits the zero-order hold's backward into spans by itself; every
+    gradient agrees with the unsplit run within the bf16 bound."""
+    inp, g = case(16, synth.BF16, batch=9, seqlen=256, d_inner=4096, seed=91)
+    p = inp.params
+    args = [to_dev(a) for a in (inp.u, inp.delta, p.A, inp.B, inp.C, g.dy)]
+    kw = dict(D=to_dev(p.D), z=to_dev(inp.z), delta_bias=to_dev(p.bias), h0=to_dev(inp.h0),
+              dh_last=to_dev(g.dh_last), discretization="zoh")
+    log("zoh backward 9 x 256 x 4096: automatic plan against one span")
+    auto = ms.mamba_scan_bwd(*args, **kw)
+    one = ms.mamba_scan_bwd(*args, **kw, n_spans=1)
+    torch.cuda.synchronize()
+    worst = {k: metric(from_dev(auto[k]), from_dev(one[k])) for k in GRADS
+             if auto.get(k) is not None}
+    log("  " + ", ".join(f"{k} {v:.1e}" for k, v in worst.items()))
+    assert max(worst.values()) <= TOL[synth.BF16], worst
+
+
 def test_zoh_backward_small_decays():
     """|Delta A| below and above the 1/16 switch of the series: A spread over decades."""
     inp, g = case(16, synth.F32, seed=77)
