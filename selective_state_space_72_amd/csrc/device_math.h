@@ -130,6 +130,32 @@ __device__ __forceinline__ void rotate_pair(float phi, float &x, float &w) {
     turn_pair(sn, cs, x, w);
 }
 
+// sin and cos of x by the hardware's v_sin_f32 / v_cos_f32 (argument in revolutions, so x is
+// first divided by 2 pi): two transcendental instructions and a multiply instead of the ~21
+// operations of sincos_fast.  Absolute error measured on gfx950 against double over 4M
+// angles per range: 1.4e-7 for |x| <= 1, 3.9e-7 for |x| <= 4, 1.5e-6 for |x| <= 20 (the
+// rounding of x / 2 pi; it grows with |x|).  Used for bf16 activations, whose outputs carry
+// 4e-3 relative rounding; fp32 activations keep sincos_fast.
+__device__ __forceinline__ void sincos_hw(float x, float &sn, float &cs) {
+    const float r = x * 0.159154943091895336f;
+    sn = __builtin_amdgcn_sinf(r);
+    cs = __builtin_amdgcn_cosf(r);
+}
+// The sine and cosine for activations of element type T (uint16_t: bf16).
+template <typename T>
+__device__ __forceinline__ void sincos_act(float x, float &sn, float &cs) {
+    if constexpr (sizeof(T) == 2)
+        sincos_hw(x, sn, cs);
+    else
+        sincos_fast(x, sn, cs);
+}
+template <typename T>
+__device__ __forceinline__ void rotate_pair_act(float phi, float &x, float &w) {
+    float sn, cs;
+    sincos_act<T>(phi, sn, cs);
+    turn_pair(sn, cs, x, w);
+}
+
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z); e^-z = +inf gives -0 as the limit.
 __device__ __forceinline__ float silu_f(float z) {
     return z * hw_rcp(1.0f + hw_exp2(-z * kLog2e));

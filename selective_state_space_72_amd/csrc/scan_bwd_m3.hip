@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
             load_vec<T, KG>(p.theta, (row0 + t) * K + k0, th);
 #pragma unroll
             for (int kk = 0; kk < KG; ++kk) {
-                sincos_fast(dl * th[kk], sn[kk], cs[kk]);
+                sincos_act<T>(dl * th[kk], sn[kk], cs[kk]);
                 turn_pair(sn[kk], cs[kk], h[2 * kk], h[2 * kk + 1]);
             }
         }

@@ -424,12 +424,12 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                 for (int k = 0; k < NQ / 2; ++k) {
                     if constexpr (RM) { // the same turn of the pair's transition columns
                         float sn, cs;
-                        sincos_fast(dw[tl].x * bcs[tl][2 * NQ + k], sn, cs);
+                        sincos_act<T>(dw[tl].x * bcs[tl][2 * NQ + k], sn, cs);
                         turn_pair(sn, cs, h[2 * k], h[2 * k + 1]);
                         turn_pair(sn, cs, rm[4 * k], rm[4 * k + 1]);
                         turn_pair(sn, cs, rm[4 * k + 2], rm[4 * k + 3]);
                     } else {
-                        rotate_pair(dw[tl].x * bcs[tl][2 * NQ + k], h[2 * k], h[2 * k + 1]);
+                        rotate_pair_act<T>(dw[tl].x * bcs[tl][2 * NQ + k], h[2 * k], h[2 * k + 1]);
                     }
                 }
             }

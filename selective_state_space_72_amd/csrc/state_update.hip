@@ -86,7 +86,7 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
 #pragma unroll
         for (int k = 0; k < 4; k += 2)
             if (kv[k])
-                rotate_pair(dl * load_val((const T *)ext.theta, ((int64_t)b * nr + 4 * q + k) / 2),
+                rotate_pair_act<T>(dl * load_val((const T *)ext.theta, ((int64_t)b * nr + 4 * q + k) / 2),
                             hin[k], hin[k + 1]);
     }
     float lm = 1.0f, p_lb = 0.0f;
