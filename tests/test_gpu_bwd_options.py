@@ -158,3 +158,61 @@ def test_m3_backward_without_prev_and_gate():
     inp, g = case(16, synth.F32, batch=1, seqlen=130, d_inner=70, gate=False)
     m3 = synth.make_mamba3_inputs(inp.cfg)
     check_m3("m3 no prev, no gate", inp, g, m3, trap=True, rot=True, prev=False)
+
+
+def m3_oracle_rows(inp, g, m3, ds, rows):
+    """Oracle gradients of the options' backward on batch rows `rows` and channel subset ds
+    (channels are independent; B, C, theta, B_prev are shared, so dB, dC, dtheta, dB_prev
+    are the sums over ds only)."""
+    p = inp.params
+    f = lambda a: synth.to_f64(a, inp.dtype)  # noqa: E731
+    ch = lambda a: np.ascontiguousarray(a[rows][:, :, ds])  # noqa: E731
+    return oracle.load().scan_bwd_ext(
+        f(ch(inp.u)), f(ch(inp.delta)), p.A[ds].astype(np.float64), f(inp.B[rows]),
+        f(inp.C[rows]), f(ch(g.dy)), D=p.D[ds].astype(np.float64), z=f(ch(inp.z)),
+        bias=p.bias[ds].astype(np.float64),
+        h0=None if inp.h0 is None else inp.h0[rows][:, ds].astype(np.float64),
+        dh_last=None if g.dh_last is None else g.dh_last[rows][:, ds].astype(np.float64),
+        lam=f(ch(m3.lam)), u_prev=f(np.ascontiguousarray(m3.u_prev[rows][:, ds])),
+        B_prev=f(m3.B_prev[rows]), theta=f(m3.theta[rows]))
+
+
+def test_m3_backward_c3_full_size_sampled():
+    """The large prefill (8 x 4096 x 5120, bf16) with the trapezoid and the rotation, in the
+    launch configuration the benchmark times: the per-channel gradients on sampled channels
+    of every lane and tile position, and dB, dC, dtheta, dB_prev of batch row 0 from the
+    oracle over all channels (in groups run in parallel, partial sums added in fp64)."""
+    import concurrent.futures
+    cfg = synth.CONFIGS["c3"]
+    inp = synth.make_scan_inputs(cfg)
+    g = synth.make_upstream_grads(cfg)
+    m3 = synth.make_mamba3_inputs(cfg)
+    p = inp.params
+    log("m3 backward, c3 full size: running the GPU backward")
+    out = ms.mamba_scan_bwd(to_dev(inp.u), to_dev(inp.delta), to_dev(p.A), to_dev(inp.B),
+                            to_dev(inp.C), to_dev(g.dy), D=to_dev(p.D), z=to_dev(inp.z),
+                            delta_bias=to_dev(p.bias), h0=to_dev(inp.h0),
+                            dh_last=to_dev(g.dh_last), lam=to_dev(m3.lam),
+                            u_prev=to_dev(m3.u_prev), B_prev=to_dev(m3.B_prev),
+                            theta=to_dev(m3.theta))
+    torch.cuda.synchronize()
+    ds = np.array([0, 1, 15, 16, 63, 64, 2047, 2600, 4095, 5119])
+    di = torch.from_numpy(ds).to(DEV)
+    sub = {"du": out["du"][:, :, di], "ddelta": out["ddelta"][:, :, di],
+           "dz": out["dz"][:, :, di], "dlam": out["dlam"][:, :, di],
+           "du_prev": out["du_prev"][:, di], "dA": out["dA"][di], "dD": out["dD"][di],
+           "dbias": out["dbias"][di], "dh0": out["dh0"][:, di]}
+    sub = {k: from_dev(v.contiguous()) for k, v in sub.items()}
+    row0 = {k: from_dev(out[k][:1].contiguous()) for k in ("dB", "dC", "dtheta", "dB_prev")}
+    del out
+    ref = m3_oracle_rows(inp, g, m3, ds, slice(None))
+    worst = {k: metric(sub[k], ref[k]) for k in sub}
+    log("  sampled channels: " + ", ".join(f"{k} {v:.1e}" for k, v in worst.items()))
+    assert max(worst.values()) <= TOL[synth.BF16], worst
+    groups = np.array_split(np.arange(cfg.d_inner), 16)
+    with concurrent.futures.ThreadPoolExecutor(16) as ex:
+        parts = list(ex.map(lambda dsg: m3_oracle_rows(inp, g, m3, dsg, slice(0, 1)), groups))
+    worst = {k: metric(row0[k], sum(pp[k] for pp in parts)) for k in row0}
+    log("  row 0 over all channels: " + ", ".join(f"{k} {v:.1e}" for k, v in worst.items()))
+    assert max(worst.values()) <= TOL[synth.BF16], worst
+
