@@ -96,6 +96,9 @@ def parse():
     ap.add_argument("--bwd-only", action="store_true",
                     help="time only the backward pass on the large prefill (for profiling) and "
                          "print its JSON summary")
+    ap.add_argument("--bwd-variant", choices=("zoh", "trapezoid", "rotation"),
+                    help="with --bwd-only: time the backward of this discretisation option "
+                         "instead (for profiling)")
     ap.add_argument("--ssd-only", action="store_true",
                     help="time only the Mamba-2 SSD scan on its large shape (for profiling) and "
                          "print its JSON summary")
@@ -664,6 +667,21 @@ def main():
         if args.copy_calibration:
             copy_calibration(dev)
         print(json.dumps(res), flush=True)
+        return
+    if args.bwd_only and args.bwd_variant:
+        opts = {"zoh": dict(discretization="zoh"), "trapezoid": dict(trapezoid=True),
+                "rotation": dict(rotation=True)}[args.bwd_variant]
+        log(f"bench: backward pass on the large prefill, {args.bwd_variant}")
+        bcase = BwdCase(cfg, dev, **opts)
+        loop_ms, _, _ = time_steps(bcase.step, args.steps, args.warmup)
+        if args.copy_calibration:
+            copy_calibration(dev)
+        print(json.dumps({"workload": f"backward of the large-model prefill scan, "
+                                      f"{args.bwd_variant}",
+                          "steps": args.steps, "ms_per_step": round(loop_ms, 4),
+                          "min_bytes_per_step": bcase.min_bytes,
+                          "GB_s": round(bcase.min_bytes / (loop_ms * 1e-3) / 1e9, 1)}),
+              flush=True)
         return
     if args.bwd_only:
         log("bench: backward pass on the large prefill (own states, then from checkpoints)")
