@@ -483,9 +483,11 @@ typedef struct {
  *   dtheta   (batch, seqlen, d_state/2) dtype dLoss/dtheta         (theta given; nullable)
  * d_state 4, 8, 16 or 32 (even with theta); opts may set only discretization (n_spans 0 or
  * 1: no sequence split); ext->ckpt and the row strides must be 0 (else
- * MAMBA_ERR_UNSUPPORTED).  With neither lambda nor theta the call is mamba_scan_bwd_ex.
- * This path runs one wave per 64 channels with every state of a channel in one lane: it
- * is correct for any length, not fast (the large prefill gives it 640 waves). */
+ * MAMBA_ERR_UNSUPPORTED).  B, C, B_prev and theta must be 16-byte aligned (read as vectors
+ * of up to 16 bytes; MAMBA_ERR_MISALIGNED otherwise).  With neither lambda nor theta the
+ * call is mamba_scan_bwd_ex.  This path runs one block per (batch row, 64 channels), the
+ * states of a channel split over 4 lanes (2 for a rotation at d_state 4), and walks the
+ * whole sequence in that block (no sequence split). */
 typedef struct {
     void *dlam;
     void *du_prev;

@@ -1618,6 +1618,10 @@ mamba_status_t mamba_scan_bwd_ext(const void *u, const void *delta, const float 
     for (const void *pp : f32_ptrs)
         if (pp && !aligned(pp, 4))
             return MAMBA_ERR_MISALIGNED;
+    const void *vec_ptrs[] = {B, C, B_prev, theta}; // a lane's states read as one vector
+    for (const void *pp : vec_ptrs)
+        if (pp && !aligned(pp, 16))
+            return MAMBA_ERR_MISALIGNED;
     size_t off[6];
     const size_t need = m3_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, theta != nullptr,
                                                off);

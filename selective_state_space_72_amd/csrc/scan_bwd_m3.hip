@@ -52,7 +52,8 @@ struct M3Args {
 };
 
 // NV values of a vector of the activation type at element i (NV consecutive elements, i a
-// multiple of NV): one load of 2 NV or 4 NV bytes.
+// multiple of NV): one load of 2 NV or 4 NV bytes (the entry point takes the arrays read
+// this way 16-byte aligned only).
 template <typename T, int NV>
 __device__ __forceinline__ void load_vec(const void *base, int64_t i, float (&out)[NV])
 {

@@ -711,16 +711,15 @@ def test_probe_argument_checks(lib):
 # ---- backward with the Mamba-3 options (mamba_scan_bwd_ext) -------------------------------
 
 def bwd_m3(lib, *, lam=None, theta=None, N=16, L=64, opts=None, eg=None, ws=BASE + 1024 * MB,
-           ws_bytes=1 << 30, strides=(0, 0, 0, 0, 0)):
-    e = ms.ScanExt(lam, None, None, theta, None, *strides)
+           ws_bytes=1 << 30, strides=(0, 0, 0, 0, 0), B=BASE + 132 * MB, B_prev=None):
+    e = ms.ScanExt(lam, None, B_prev, theta, None, *strides)
     g = eg if eg is not None else ms.ScanExtGrads()
     o = ctypes.byref(opts) if opts is not None else None
     Z = BASE + 3000 * MB
-    return lib.mamba_scan_bwd_ext(BASE, BASE + 64 * MB, BASE + 128 * MB, BASE + 132 * MB,
-                                  BASE + 136 * MB, None, None, None, None, BASE + 140 * MB,
-                                  None, Z, Z + 64 * MB, None, None, None, None, None, None,
-                                  None, ctypes.byref(e), ctypes.byref(g), 2, L, 128, N, BF16,
-                                  ws, ws_bytes, o, None)
+    return lib.mamba_scan_bwd_ext(BASE, BASE + 64 * MB, BASE + 128 * MB, B, BASE + 136 * MB,
+                                  None, None, None, None, BASE + 140 * MB, None, Z, Z + 64 * MB,
+                                  None, None, None, None, None, None, None, ctypes.byref(e),
+                                  ctypes.byref(g), 2, L, 128, N, BF16, ws, ws_bytes, o, None)
 
 
 def test_bwd_ext_validation(lib):
@@ -733,6 +732,10 @@ def test_bwd_ext_validation(lib):
     assert bwd_m3(lib, theta=TH, strides=(0, 0, 256, 0, 0)) == UNSUP
     assert bwd_m3(lib, lam=LAM, ws_bytes=1024) == WS
     assert bwd_m3(lib, lam=LAM + 1) == ALIGN
+    # B, C, B_prev and theta are read as vectors: 16-byte aligned, not only element-aligned
+    assert bwd_m3(lib, theta=TH + 8) == ALIGN
+    assert bwd_m3(lib, lam=LAM, B=BASE + 132 * MB + 2) == ALIGN
+    assert bwd_m3(lib, lam=LAM, B_prev=BASE + 600 * MB + 4) == ALIGN
     # the look-back gradients may not overlap an input
     assert bwd_m3(lib, lam=LAM, eg=ms.ScanExtGrads(LAM + 64, None, None, None)) == ALIAS
     assert bwd_m3(lib, theta=TH, eg=ms.ScanExtGrads(None, None, None, BASE + 2)) == ALIAS
