@@ -144,6 +144,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
     typedef typename std::conditional<ZOH || TRAP, float4, float2>::type DW;
     __shared__ DW s_dw[2][TC][64];
     __shared__ float s_yp[FULL ? 2 : 1][TC][NW][64]; // partial readouts per (step, wave, channel)
+    __shared__ float s_sdt[FULL ? 1 : NW][64];       // span pass: the waves' sums of Delta
 
     const int lane = threadIdx.x & 63;
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -305,6 +306,8 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                 bcs[tl][i] = (FULL || i < NQ || (ROT && i >= 2 * NQ)) ? q[tl * BCW + i] : 0.0f;
     };
 
+    // span pass: sum of Delta over the span, the waves' shares of the steps (each step is
+    // added once, by the lane that computes its Delta; joined over the waves at the end)
     float sum_dt = 0.0f;
     // span pass with the rotation: the transition of each state pair over the span, a 2x2
     // matrix (rotations and unequal decays within a pair do not commute), columns
@@ -379,6 +382,8 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
             const float dl = softplus_f(widen(rd[j][k]) + bias_d);
             du[k] = FULL ? D_d * uu : 0.0f;
             gz[k] = gated ? silu_f(widen(rz[j][k])) : 1.0f;
+            if (!FULL && tl < nt)
+                sum_dt += dl;
             if (tl < TC) {
                 if constexpr (ZOH) {
                     s_dw[pp][tl][lane] = make_float4(dl, dl * uu, uu, 0.0f);
@@ -458,8 +463,6 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
             }
             if (FULL)
                 s_yp[FULL ? pp : 0][tl][g][lane] = yp;
-            else
-                sum_dt += dw[tl].x;
             if constexpr (CK) {
                 // the state after absolute step tn - 1 enters segment tn / 8 (every lane,
                 // tail lanes included: they hold a valid channel's finite state).  Spans and
@@ -542,6 +545,15 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
             relay.state[((int64_t)slot * N + n0 + q) * 64 + lane] = h[q];
         relay_signal(relay.sync + slot);
         return;
+    }
+    if constexpr (!FULL) {
+        // the span's sum of Delta: the waves' shares in wave order
+        s_sdt[g][lane] = sum_dt;
+        __syncthreads();
+        sum_dt = s_sdt[0][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            sum_dt += s_sdt[w][lane];
     }
     if (!dvalid)
         return;
