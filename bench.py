@@ -382,11 +382,13 @@ def extra_workloads(dev, flush, steps):
             "hbm_frac": round(case.min_bytes / (ms_used * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del case
         torch.cuda.empty_cache()
-    # backward of the large prefill with the discretisation variants
+    # backward of the large prefill with the discretisation variants, and of the long
+    # sequence with the trapezoid (a sequence split)
     for name, opts in (("c3_bwd_zoh", dict(discretization="zoh")),
                        ("c3_bwd_trapezoid", dict(trapezoid=True)),
-                       ("c3_bwd_rotation", dict(rotation=True))):
-        cfg = synth.CONFIGS["c3"]
+                       ("c3_bwd_rotation", dict(rotation=True)),
+                       ("c4_bwd_trapezoid", dict(trapezoid=True))):
+        cfg = synth.CONFIGS[name.split("_")[0]]
         case = BwdCase(cfg, dev, **opts)
         loop_ms, med, _ = time_steps(case.step, max(10, steps // 4), 3, flush, warm_ms=100.0)
         ms_used = med if med is not None else loop_ms

@@ -481,13 +481,19 @@ typedef struct {
  *   du_prev  (batch, d_inner) dtype           dLoss/du_prev        (lambda given; nullable)
  *   dB_prev  (batch, d_state) dtype           dLoss/dB_prev        (lambda given; nullable)
  *   dtheta   (batch, seqlen, d_state/2) dtype dLoss/dtheta         (theta given; nullable)
- * d_state 4, 8, 16 or 32 (even with theta); opts may set only discretization (n_spans 0 or
- * 1: no sequence split); ext->ckpt and the row strides must be 0 (else
- * MAMBA_ERR_UNSUPPORTED).  B, C, B_prev and theta must be 16-byte aligned (read as vectors
- * of up to 16 bytes; MAMBA_ERR_MISALIGNED otherwise).  With neither lambda nor theta the
- * call is mamba_scan_bwd_ex.  This path runs one block per (batch row, 64 channels), the
- * states of a channel split over 4 lanes (2 for a rotation at d_state 4), and walks the
- * whole sequence in that block (no sequence split). */
+ * d_state 4, 8, 16 or 32 (even with theta); opts may set only discretization and n_spans;
+ * ext->ckpt and the row strides must be 0 (else MAMBA_ERR_UNSUPPORTED).  B, C, B_prev and
+ * theta must be 16-byte aligned (read as vectors of up to 16 bytes; MAMBA_ERR_MISALIGNED
+ * otherwise).  With neither lambda nor theta the call is mamba_scan_bwd_ex.  This path runs
+ * one block per (span, batch row, 64 channels), the states of a channel split over 4 lanes
+ * (2 for a rotation at d_state 4).  Sequence split (opts->n_spans: 0 automatic, 1 none, up to
+ * 64): when the (batch row, 64-channel) units leave compute units idle the sequence is cut
+ * into spans of a multiple of 8 steps; the forward's span pass and carry give the state
+ * entering each span, an adjoint span pass and a reverse carry the gradient entering it from
+ * its end, and the trapezoid's look-back shares at span boundaries are added after the spans
+ * (one rounding).  A split with theta needs d_state 16 or 32 (else: unsplit when automatic,
+ * MAMBA_ERR_UNSUPPORTED when requested); its workspace grows by the span regions
+ * (mamba_scan_bwd_ext_workspace_size with the same options). */
 typedef struct {
     void *dlam;
     void *du_prev;

@@ -1519,7 +1519,7 @@ mamba_status_t mamba_scan_bwd_ex(const void *u, const void *delta, const float *
 // ---- backward with the Mamba-3 options (scan_bwd_m3.hip) ----
 
 // Options of a backward call with lambda or theta: Euler or (rotation only) the zero-order
-// hold, one span, d_state 4..32 compiled, contiguous inputs, no stored checkpoints.
+// hold, at most 64 spans, d_state 4..32 compiled, contiguous inputs, no stored checkpoints.
 static mamba_status_t m3_bwd_check(int64_t d_state, const mamba_scan_ext_t *ext,
                                    const mamba_scan_opts_t *opts, bool *zoh)
 {
@@ -1528,7 +1528,7 @@ static mamba_status_t m3_bwd_check(int64_t d_state, const mamba_scan_ext_t *ext,
         ext->u_stride || ext->delta_stride || ext->z_stride || ext->B_stride || ext->C_stride)
         return MAMBA_ERR_UNSUPPORTED;
     if (opts) {
-        if (opts->chunk_len || opts->waves || opts->kernel || opts->relay || opts->n_spans > 1 ||
+        if (opts->chunk_len || opts->waves || opts->kernel || opts->relay || opts->n_spans > 64 ||
             opts->n_spans < 0 ||
             (opts->discretization != MAMBA_DISC_EULER && opts->discretization != MAMBA_DISC_ZOH))
             return MAMBA_ERR_UNSUPPORTED;
@@ -1536,6 +1536,46 @@ static mamba_status_t m3_bwd_check(int64_t d_state, const mamba_scan_ext_t *ext,
     }
     if (*zoh && ext->lambda)
         return MAMBA_ERR_UNSUPPORTED; // the trapezoid replaces the input term
+    return MAMBA_OK;
+}
+
+// Sequence split of the Mamba-3 backward.  One block per (span, batch row, 64-channel tile);
+// the kernel holds about three blocks per compute unit, so when the units alone leave compute
+// units idle the sequence is cut into spans (powers of two, at least 64 steps each) for about
+// two rounds of blocks.  A split needs the forward span pass of the scalar family with the same
+// options (with the rotation: whole state pairs per wave, d_state 16 or 32); without it the
+// call runs unsplit (automatic) or returns MAMBA_ERR_UNSUPPORTED (a requested split).
+static mamba_status_t m3_plan(int64_t batch, int64_t seqlen, int64_t d_inner, int64_t d_state,
+                              bool rot, const mamba_scan_opts_t *opts, M3Plan *plan)
+{
+    M3Plan p{};
+    p.fwd_waves = scalar_default_waves(d_state);
+    p.fwd_chunk = scalar_default_chunk(d_state);
+    const bool fixed = opts && opts->n_spans > 0;
+    int n = fixed ? opts->n_spans : 1;
+    if (!fixed && seqlen >= 128) {
+        const int64_t units = batch * ((d_inner + 63) / 64);
+        const int64_t cus = cu_count();
+        if (units < cus) {
+            const int64_t want = cus * 3 /*blocks each*/ * 2 /*rounds*/;
+            while (units * n < want && n < 64 && seqlen / (2 * n) >= 64)
+                n *= 2;
+        }
+    }
+    constexpr int64_t kSeg = 8; // the kernel's segment between stored states
+    int64_t len = seqlen > 0 ? (seqlen + n - 1) / n : kSeg;
+    len = (len + kSeg - 1) / kSeg * kSeg;
+    n = seqlen > 0 ? (int)((seqlen + len - 1) / len) : 1;
+    if (n > 1 && (!scalar_variant_supported(d_state, p.fwd_waves, p.fwd_chunk) ||
+                  (rot && (d_state / p.fwd_waves) % 2 != 0) || len % p.fwd_chunk != 0 ||
+                  !scalar_span_ok(len, d_inner))) {
+        if (fixed)
+            return MAMBA_ERR_UNSUPPORTED;
+        n = 1;
+    }
+    p.n_spans = n;
+    p.span_len = n > 1 ? len : seqlen;
+    *plan = p;
     return MAMBA_OK;
 }
 
@@ -1551,8 +1591,12 @@ size_t mamba_scan_bwd_ext_workspace_size(int64_t batch, int64_t seqlen, int64_t 
         !mul_ok(t, d_inner, &t) || !mul_ok(t, d_state, &t) || !mul_ok(t, 8, &t) ||
         m3_bwd_check(d_state, ext, opts, &zoh) != MAMBA_OK)
         return (size_t)-1;
-    size_t off[6];
-    return m3_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, ext->theta != nullptr, off);
+    M3Plan plan;
+    if (m3_plan(batch, seqlen, d_inner, d_state, ext->theta != nullptr, opts, &plan) != MAMBA_OK)
+        return (size_t)-1;
+    size_t off[15];
+    return m3_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, ext->theta != nullptr, plan,
+                                  off);
 }
 
 mamba_status_t mamba_scan_bwd_ext(const void *u, const void *delta, const float *A,
@@ -1622,9 +1666,14 @@ mamba_status_t mamba_scan_bwd_ext(const void *u, const void *delta, const float 
     for (const void *pp : vec_ptrs)
         if (pp && !aligned(pp, 16))
             return MAMBA_ERR_MISALIGNED;
-    size_t off[6];
+    M3Plan plan;
+    const mamba_status_t ps = m3_plan(batch, seqlen, d_inner, d_state, theta != nullptr, opts,
+                                      &plan);
+    if (ps != MAMBA_OK)
+        return ps;
+    size_t off[15];
     const size_t need = m3_bwd_workspace_bytes(batch, seqlen, d_inner, d_state, theta != nullptr,
-                                               off);
+                                               plan, off);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return MAMBA_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 4))
@@ -1711,17 +1760,76 @@ mamba_status_t mamba_scan_bwd_ext(const void *u, const void *delta, const float 
     q.dD = dD;
     q.dbias = d_delta_bias;
     q.dh0 = dh0;
-    q.ckpt = reinterpret_cast<float *>(ws + off[0]);
-    q.part = reinterpret_cast<float *>(ws + off[1]);
-    q.bprev_part = reinterpret_cast<float *>(ws + off[2]);
-    q.dA_part = reinterpret_cast<float *>(ws + off[3]);
-    q.dDb_part = reinterpret_cast<float *>(ws + off[4]);
+    auto region = [&](int i) { return reinterpret_cast<float *>(ws + off[i]); };
+    q.ckpt = region(0);
+    q.part = region(1);
+    q.bprev_part = region(2);
+    q.dA_part = region(3);
+    q.dDb_part = region(4);
     q.batch = batch;
     q.L = seqlen;
     q.d_inner = d_inner;
     q.d_state = d_state;
     q.dtype = dtype == MAMBA_DTYPE_BF16 ? DType::BF16 : DType::F32;
     q.zoh = zoh;
+    q.n_spans = plan.n_spans;
+    q.span_len = plan.span_len;
+    if (plan.n_spans > 1) {
+        // the forward span pass over every span (its transitions also serve the adjoint
+        // carry) and the carry: the state entering each span
+        ScanLaunch E{};
+        E.u = u;
+        E.delta = delta;
+        E.B = B;
+        E.C = C;
+        E.A = A;
+        E.bias = delta_bias;
+        E.lam = lam;
+        E.u_prev = u_prev;
+        E.B_prev = B_prev;
+        E.theta = theta;
+        E.trap = lam != nullptr;
+        E.rot = theta != nullptr;
+        E.zoh = zoh;
+        E.ws_decay = region(6);
+        E.ws_hloc = region(7);
+        E.ws_rot = theta ? region(9) : nullptr;
+        E.batch = batch;
+        E.L = seqlen;
+        E.d_inner = d_inner;
+        E.d_state = d_state;
+        E.span_len = plan.span_len;
+        E.n_spans = plan.n_spans;
+        E.first_span = 0;
+        E.launch_spans = plan.n_spans;
+        E.waves = plan.fwd_waves;
+        E.chunk = plan.fwd_chunk;
+        E.dtype = q.dtype;
+        E.bc_staged = region(5);
+        E.staged_rows = seqlen + plan.fwd_chunk;
+        E.relay_parts = 1;
+        E.su = E.sd = E.sz = d_inner;
+        E.sB = E.sC = d_state;
+        if (launch_stage_bc(E, st) != hipSuccess || launch_scalar_end(E, st) != hipSuccess)
+            return MAMBA_ERR_HIP;
+        CarryLaunch K{};
+        K.ws_decay = region(6);
+        K.ws_hloc = region(7);
+        K.ws_rot = theta ? region(9) : nullptr;
+        K.h0 = h0;
+        K.h_in = region(8);
+        K.columns = batch * d_inner * d_state;
+        K.n_spans = plan.n_spans;
+        if (launch_carry(K, st) != hipSuccess)
+            return MAMBA_ERR_HIP;
+        q.ws_decay = region(6);
+        q.ws_rot = theta ? region(9) : nullptr;
+        q.h_in = region(8);
+        q.mu_loc = region(10);
+        q.mu_in = region(11);
+        q.du_edge = region(12);
+        q.du_lb = region(13);
+    }
     return hip_status(launch_scan_bwd_m3(q, st));
 }
 

@@ -45,10 +45,16 @@ struct M3Args {
     float *ckpt;       // [unit][segment][n][lane]
     float *part;       // [unit][t][V]: the tile's sums of dB, dC (and dtheta)
     float *bprev_part; // [unit][N]: the tile's sums of dB_prev
-    float *dA_part;    // [b][d][n]
-    float *dDb_part;   // [b][d][2]: dD, dbias
-    int64_t L;
-    int32_t Dn, batch, n_seg;
+    float *dA_part;    // [span][b][d][n]
+    float *dDb_part;   // [span][b][d][2]: dD, dbias
+    // sequence split (n_spans > 1; else NULL): the state entering each span and the adjoint
+    // entering it from its end, [span][b][d][n]; du of a span's last step before the next
+    // span's look-back share, and that share, [span][b][d]; the adjoint span pass's result
+    const float *h_in, *mu_in;
+    float *du_edge, *du_lb, *mu_loc;
+    int64_t L, span_len;
+    int32_t Dn, batch, n_seg; // n_seg: segments per block (of its span)
+    int32_t n_spans, units;   // units = tiles * batch; block = span * units + unit
 };
 
 // NV values of a vector of the activation type at element i (NV consecutive elements, i a
@@ -107,7 +113,10 @@ __device__ __forceinline__ float quad_sum(float v)
 // rotation pairs (d_state 4).
 template <int N, bool ROT> constexpr int m3_groups() { return ROT && N < 8 ? 2 : 4; }
 
-template <typename T, int N, bool ZOH, bool TRAP, bool ROT, bool GATED>
+// SPLIT: blocks cover the spans of a split sequence (else one block walks the whole sequence:
+// the span quantities below are compile-time constants, which keeps the scalar registers of
+// the unsplit kernel free).
+template <typename T, int N, bool ZOH, bool TRAP, bool ROT, bool GATED, bool SPLIT>
 __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
 {
     static_assert(!(ZOH && TRAP), "the trapezoid replaces the input term");
@@ -128,7 +137,8 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c = lane % CW, g = lane / CW;
     const int ch = CW * w + c; // channel within the tile
-    const int unit = blockIdx.x; // tile * batch + b
+    const int unit = SPLIT ? blockIdx.x % p.units : blockIdx.x; // tile * batch + b
+    const int span = SPLIT ? blockIdx.x / p.units : 0;
     const int b = unit % p.batch, tile = unit / p.batch;
     const int Dn = p.Dn;
     const int d = tile * 64 + ch;
@@ -149,6 +159,10 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
     const int qslot = ch >> 2;
     const int64_t L = p.L;
     const int64_t row0 = (int64_t)b * L;
+    const int64_t tb = SPLIT ? (int64_t)span * p.span_len : 0; // this block's steps [tb, te)
+    const int64_t te = SPLIT ? min(tb + p.span_len, L) : L;
+    const int n_seg = (int)((te - tb + kM3Seg - 1) / kM3Seg);
+    const int64_t bd = (int64_t)p.batch * Dn, bdn = bd * N;
     auto ld = [](const void *base, int64_t i) { return load_val((const T *)base, i); };
 
     float a2[NG], an[NG], ia[NG];
@@ -221,28 +235,29 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
             u_lb = uu;
     };
 
-    float *ck = p.ckpt + (int64_t)unit * p.n_seg * N * 64;
+    float *ck = p.ckpt + (int64_t)blockIdx.x * p.n_seg * N * 64;
 
     // ---- 1. forward: the state entering every 8-step segment ----
     {
         float h[NG], b_lb[NG], u_lb = 0.0f, sn[KG], cs[KG];
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
-            h[j] = p.h0 ? p.h0[((int64_t)b * Dn + dc) * N + n0 + j] : 0.0f;
+            const int64_t hc = ((int64_t)b * Dn + dc) * N + n0 + j;
+            h[j] = SPLIT ? p.h_in[span * bdn + hc] : p.h0 ? p.h0[hc] : 0.0f;
             b_lb[j] = 0.0f;
         }
-        lookback(0, u_lb, b_lb);
-        for (int seg = 0; seg < p.n_seg; ++seg) {
-            const int64_t t0 = (int64_t)seg * kM3Seg;
+        lookback(tb, u_lb, b_lb);
+        for (int seg = 0; seg < n_seg; ++seg) {
+            const int64_t t0 = tb + (int64_t)seg * kM3Seg;
 #pragma unroll
             for (int j = 0; j < NG; ++j)
                 ck[(seg * N + n0 + j) * 64 + ch] = h[j];
-            if (t0 + kM3Seg <= L) { // (no branch between the steps: their loads go ahead)
+            if (t0 + kM3Seg <= te) { // (no branch between the steps: their loads go ahead)
 #pragma unroll
                 for (int s = 0; s < kM3Seg; ++s)
                     advance(h, t0 + s, u_lb, b_lb, sn, cs);
             } else {
-                for (int64_t t = t0; t < L; ++t)
+                for (int64_t t = t0; t < te; ++t)
                     advance(h, t, u_lb, b_lb, sn, cs);
             }
         }
@@ -252,14 +267,20 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
     float mu[NG], dA[NG], lbk[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-        mu[j] = dvalid && p.dh_last ? p.dh_last[((int64_t)b * Dn + dc) * N + n0 + j] : 0.0f;
+        const int64_t hc = ((int64_t)b * Dn + dc) * N + n0 + j;
+        mu[j] = !dvalid     ? 0.0f
+                : SPLIT     ? p.mu_in[span * bdn + hc]
+                : p.dh_last ? p.dh_last[hc]
+                            : 0.0f;
         dA[j] = 0.0f;
         lbk[j] = 0.0f; // mu_{t+1} (1 - lam_{t+1}) Delta_{t+1}: the look-back's weights
     }
     float dD_acc = 0.0f, db_acc = 0.0f;
-    for (int seg = p.n_seg - 1; seg >= 0; --seg) {
-        const int64_t t0 = (int64_t)seg * kM3Seg;
-        const int64_t t1 = min(t0 + (int64_t)kM3Seg, L);
+    // the trapezoid's du of the block's last step waits for the next span's look-back share
+    const int64_t t_edge = SPLIT && TRAP && span < p.n_spans - 1 ? te - 1 : -1;
+    for (int seg = n_seg - 1; seg >= 0; --seg) {
+        const int64_t t0 = tb + (int64_t)seg * kM3Seg;
+        const int64_t t1 = min(t0 + (int64_t)kM3Seg, te);
         for (int sg = SG - 1; sg >= 0; --sg) {
             const int64_t ts = t0 + (int64_t)sg * S;
             if (ts >= t1)
@@ -392,7 +413,11 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
                 dD_acc = __builtin_fmaf(ds, uu, dD_acc);
                 db_acc += dd;
                 if (dvalid && g == 0) {
-                    store_val((T *)p.du, bld, __builtin_fmaf(ds, D_d, du));
+                    const float duv = __builtin_fmaf(ds, D_d, du);
+                    if (t == t_edge)
+                        p.du_edge[span * bd + (int64_t)b * Dn + d] = duv;
+                    else
+                        store_val((T *)p.du, bld, duv);
                     store_val((T *)p.ddelta, bld, dd);
                     if constexpr (GATED)
                         store_val((T *)p.dz, bld, dyv * sy * dgate);
@@ -436,18 +461,25 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
 
     // ---- 3. per-block results ----
     if constexpr (TRAP) {
-        // the first look-back read u_prev and B_prev
+        // the look-back of the block's first step, which read u and B of the step before it
+        // (u_prev and B_prev at t = 0): their shares of du and dB
+        float u_s = 0.0f, b_s[NG];
+        lookback(tb, u_s, b_s);
         float dup = 0.0f;
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
-            dup = __builtin_fmaf(lbk[j], bpre[j], dup);
-            const float sbp = quad_sum(lbk[j] * u_pre);
+            dup = __builtin_fmaf(lbk[j], b_s[j], dup);
+            const float sbp = quad_sum(lbk[j] * u_s);
             if (writer)
                 s_v[n0 + j][qslot] = sbp;
         }
         dup = chan_sum(dup);
-        if (dvalid && g == 0 && p.du_prev)
-            store_val((T *)p.du_prev, (int64_t)b * Dn + d, dup);
+        if (dvalid && g == 0) {
+            if (SPLIT && span > 0)
+                p.du_lb[span * bd + (int64_t)b * Dn + d] = dup;
+            else if (p.du_prev)
+                store_val((T *)p.du_prev, (int64_t)b * Dn + d, dup);
+        }
         __syncthreads();
         if (tid < N) {
             const float4 *src = reinterpret_cast<const float4 *>(&s_v[tid][0]);
@@ -457,33 +489,167 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
                 const float4 q = src[i];
                 sum += (q.x + q.y) + (q.z + q.w);
             }
-            p.bprev_part[(int64_t)unit * N + tid] = sum;
+            p.bprev_part[((int64_t)span * p.units + unit) * N + tid] = sum;
         }
     }
     if (dvalid) {
         const int64_t col = ((int64_t)b * Dn + d) * N + n0;
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
-            p.dA_part[col + j] = dA[j];
-            if (p.dh0)
+            p.dA_part[span * bdn + col + j] = dA[j];
+            if (p.dh0 && span == 0)
                 p.dh0[col + j] = mu[j];
         }
         if (g == 0) {
-            p.dDb_part[((int64_t)b * Dn + d) * 2 + 0] = dD_acc;
-            p.dDb_part[((int64_t)b * Dn + d) * 2 + 1] = db_acc;
+            p.dDb_part[(span * bd + (int64_t)b * Dn + d) * 2 + 0] = dD_acc;
+            p.dDb_part[(span * bd + (int64_t)b * Dn + d) * 2 + 1] = db_acc;
         }
     }
 }
 
-// dB, dC, dtheta: the tiles' partials added in tile order; dB_prev likewise.
+// The adjoint span pass of a split sequence: for each span s >= 1, the adjoint of the state
+// entering it (dLoss/dh at the step before the span) that the span's own outputs produce,
+// walking it backwards from a zero adjoint at its end.  Per step (as the main kernel):
+// mu += ds C, mu *= exp(Delta A), the pairs turned back by the step's angle.  The input
+// term (Euler, zero-order hold, trapezoid) does not enter this recurrence.
+template <typename T, int N, bool ROT, bool GATED>
+__global__ void __launch_bounds__(256) m3_adjoint_span_kernel(M3Args p)
+{
+    constexpr int GR = m3_groups<N, ROT>();
+    constexpr int CW = 64 / GR;
+    constexpr int NG = N / GR;
+    constexpr int KG = ROT ? NG / 2 : 1;
+    constexpr int K = N / 2;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = lane % CW, g = lane / CW;
+    const int unit = blockIdx.x % p.units;
+    const int span = 1 + blockIdx.x / p.units;
+    const int b = unit % p.batch, tile = unit / p.batch;
+    const int Dn = p.Dn;
+    const int d = tile * 64 + CW * w + c;
+    const bool dvalid = d < Dn;
+    const int dc = dvalid ? d : Dn - 1;
+    const int n0 = g * NG, k0 = g * KG;
+    const int64_t L = p.L, row0 = (int64_t)b * L;
+    const int64_t tb = (int64_t)span * p.span_len, te = min(tb + p.span_len, L);
+    float a2[NG], mu[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+        a2[j] = p.A[(int64_t)dc * N + n0 + j] * kLog2e;
+        mu[j] = 0.0f;
+    }
+    const float bias_d = p.bias ? p.bias[dc] : 0.0f;
+    auto step = [&](int64_t t) {
+        const int64_t bld = (row0 + t) * Dn + dc;
+        const float dl = softplus_f(load_val((const T *)p.delta, bld) + bias_d);
+        float ds = dvalid ? load_val((const T *)p.dy, bld) : 0.0f;
+        if constexpr (GATED) {
+            const float zz = load_val((const T *)p.z, bld);
+            ds *= zz * hw_rcp(1.0f + hw_exp2(-zz * kLog2e));
+        }
+        float cn[NG];
+        load_vec<T, NG>(p.C, (row0 + t) * N + n0, cn);
+#pragma unroll
+        for (int j = 0; j < NG; ++j)
+            mu[j] = __builtin_fmaf(ds, cn[j], mu[j]) * decay_exp2(dl, a2[j]);
+        if constexpr (ROT) {
+            float th[KG];
+            load_vec<T, KG>(p.theta, (row0 + t) * K + k0, th);
+#pragma unroll
+            for (int kk = 0; kk < KG; ++kk) {
+                float sn, cs;
+                sincos_act<T>(dl * th[kk], sn, cs);
+                const float x0 = mu[2 * kk], x1 = mu[2 * kk + 1];
+                mu[2 * kk] = __builtin_fmaf(cs, x0, sn * x1);
+                mu[2 * kk + 1] = __builtin_fmaf(cs, x1, -sn * x0);
+            }
+        }
+    };
+    int64_t t = te - 1;
+    for (; t - kM3Seg + 1 >= tb; t -= kM3Seg) { // whole segments: no branch between the steps
+#pragma unroll
+        for (int s = 0; s < kM3Seg; ++s)
+            step(t - s);
+    }
+    for (; t >= tb; --t)
+        step(t);
+    if (dvalid) {
+        const int64_t col = ((int64_t)b * Dn + d) * N + n0;
+#pragma unroll
+        for (int j = 0; j < NG; ++j)
+            p.mu_loc[span * (int64_t)p.batch * Dn * N + col + j] = mu[j];
+    }
+}
+
+// The adjoint entering each span from its end, spans in reverse: mu_in[S - 1] = dh_last,
+// mu_in[s - 1] = M_s^T mu_in[s] + mu_loc[s] with M_s the span's forward transition (its
+// decays, or each state pair's 2x2 matrix, from the forward span pass).  One thread per state
+// (per pair with the rotation).
+__global__ void __launch_bounds__(256)
+m3_mu_carry_kernel(const float *__restrict__ dec, const float *__restrict__ rot,
+                   const float *__restrict__ mu_loc, const float *__restrict__ dh_last,
+                   float *__restrict__ mu_in, int64_t columns, int32_t n_spans)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int S = n_spans;
+    if (rot) {
+        if (i >= columns / 2)
+            return;
+        const int64_t c = 2 * i;
+        float x0 = dh_last ? dh_last[c] : 0.0f, x1 = dh_last ? dh_last[c + 1] : 0.0f;
+        mu_in[(int64_t)(S - 1) * columns + c] = x0;
+        mu_in[(int64_t)(S - 1) * columns + c + 1] = x1;
+        for (int s = S - 1; s >= 1; --s) {
+            const float *m = rot + (i * S + s) * 4; // m00, m10, m01, m11
+            const float y0 =
+                __builtin_fmaf(m[0], x0, __builtin_fmaf(m[1], x1, mu_loc[(int64_t)s * columns + c]));
+            const float y1 = __builtin_fmaf(
+                m[2], x0, __builtin_fmaf(m[3], x1, mu_loc[(int64_t)s * columns + c + 1]));
+            x0 = y0;
+            x1 = y1;
+            mu_in[(int64_t)(s - 1) * columns + c] = x0;
+            mu_in[(int64_t)(s - 1) * columns + c + 1] = x1;
+        }
+    } else {
+        if (i >= columns)
+            return;
+        float x = dh_last ? dh_last[i] : 0.0f;
+        mu_in[(int64_t)(S - 1) * columns + i] = x;
+        for (int s = S - 1; s >= 1; --s) {
+            x = __builtin_fmaf(dec[i * S + s], x, mu_loc[(int64_t)s * columns + i]);
+            mu_in[(int64_t)(s - 1) * columns + i] = x;
+        }
+    }
+}
+
+// du of the step before each span s >= 1: the previous span's own value plus span s's
+// look-back share, rounded once.
+template <typename T>
+__global__ void __launch_bounds__(256)
+m3_du_edge_kernel(const float *__restrict__ du_edge, const float *__restrict__ du_lb, T *du,
+                  int64_t bd, int64_t L, int32_t Dn, int64_t span_len, int32_t n_spans)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)(n_spans - 1) * bd)
+        return;
+    const int64_t s = 1 + i / bd, r = i % bd; // r = b * Dn + d
+    const int64_t b = r / Dn, dd = r % Dn;
+    const int64_t t = s * span_len - 1;
+    store_val(du, (b * L + t) * Dn + dd, du_edge[(s - 1) * bd + r] + du_lb[s * bd + r]);
+}
+
+// dB, dC, dtheta: the tiles' partials added in tile order, then (dB at the step before a
+// span of lb_spans > 1, the trapezoid's) the tiles' look-back shares of that span; dB_prev
+// likewise from span 0's shares.
 template <typename T>
 __global__ void __launch_bounds__(256)
 m3_reduce_kernel(const float *__restrict__ part, const float *__restrict__ bprev_part, T *dB,
                  T *dC, T *dtheta, T *dB_prev, int64_t batch, int64_t L, int32_t N, int32_t V,
-                 int32_t tiles)
+                 int32_t tiles, int64_t span_len, int32_t lb_spans)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t total = batch * L * V;
+    const int64_t units = (int64_t)tiles * batch;
     if (i < total) {
         const int j = (int)(i % V);
         const int64_t bt = i / V;
@@ -492,6 +658,11 @@ m3_reduce_kernel(const float *__restrict__ part, const float *__restrict__ bprev
         for (int tile = 0; tile < tiles; ++tile)
             s += part[(((int64_t)tile * batch + b) * L + t) * V + j];
         if (j < N) {
+            if (lb_spans > 1 && (t + 1) % span_len == 0 && t + 1 < L) {
+                const int64_t sp = (t + 1) / span_len;
+                for (int tile = 0; tile < tiles; ++tile)
+                    s += bprev_part[(sp * units + (int64_t)tile * batch + b) * N + j];
+            }
             if (dB)
                 store_val(dB, bt * N + j, s);
         } else if (j < 2 * N) {
@@ -510,25 +681,25 @@ m3_reduce_kernel(const float *__restrict__ part, const float *__restrict__ bprev
     }
 }
 
-// dA = sum over the batch rows of dA_part; dD, dbias likewise (fixed order).
+// dA = sum over the (span, batch row) pairs of dA_part; dD, dbias likewise (fixed order).
 __global__ void __launch_bounds__(256)
 m3_reduce_params_kernel(const float *__restrict__ dA_part, const float *__restrict__ dDb_part,
-                        float *dA, float *dD, float *dbias, int64_t batch, int64_t Dn, int64_t N)
+                        float *dA, float *dD, float *dbias, int64_t rows, int64_t Dn, int64_t N)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t dn = Dn * N;
     if (i < dn) {
         float s = 0.0f;
-        for (int64_t b = 0; b < batch; ++b)
-            s += dA_part[b * dn + i];
+        for (int64_t r = 0; r < rows; ++r)
+            s += dA_part[r * dn + i];
         if (dA)
             dA[i] = s;
     } else if (i < dn + Dn) {
         const int64_t d = i - dn;
         float sD = 0.0f, sb = 0.0f;
-        for (int64_t b = 0; b < batch; ++b) {
-            sD += dDb_part[(b * Dn + d) * 2 + 0];
-            sb += dDb_part[(b * Dn + d) * 2 + 1];
+        for (int64_t r = 0; r < rows; ++r) {
+            sD += dDb_part[(r * Dn + d) * 2 + 0];
+            sb += dDb_part[(r * Dn + d) * 2 + 1];
         }
         if (dD)
             dD[d] = sD;
@@ -542,6 +713,7 @@ hipError_t launch_m3_t(const M3BwdLaunch &q, hipStream_t stream)
 {
     const int64_t tiles = (q.d_inner + 63) / 64;
     const int64_t units = tiles * q.batch;
+    const int S = q.n_spans;
     if (units <= 0 || q.L <= 0)
         return hipSuccess;
     M3Args a{};
@@ -572,31 +744,77 @@ hipError_t launch_m3_t(const M3BwdLaunch &q, hipStream_t stream)
     a.dA_part = q.dA_part;
     a.dDb_part = q.dDb_part;
     a.L = q.L;
+    a.span_len = S > 1 ? q.span_len : q.L;
     a.Dn = (int32_t)q.d_inner;
     a.batch = (int32_t)q.batch;
-    a.n_seg = (int32_t)((q.L + kM3Seg - 1) / kM3Seg);
-    if (q.z)
-        hipLaunchKernelGGL((scan_bwd_m3_kernel<T, N, ZOH, TRAP, ROT, true>),
-                           dim3((uint32_t)units), dim3(64 * m3_groups<N, ROT>()), 0, stream, a);
-    else
-        hipLaunchKernelGGL((scan_bwd_m3_kernel<T, N, ZOH, TRAP, ROT, false>),
-                           dim3((uint32_t)units), dim3(64 * m3_groups<N, ROT>()), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
+    a.n_seg = (int32_t)((a.span_len + kM3Seg - 1) / kM3Seg);
+    a.n_spans = S;
+    a.units = (int32_t)units;
+    const dim3 block(64 * m3_groups<N, ROT>());
+    hipError_t e;
+    if (S > 1) {
+        a.h_in = q.h_in;
+        a.mu_in = q.mu_in;
+        a.mu_loc = q.mu_loc;
+        a.du_edge = q.du_edge;
+        a.du_lb = q.du_lb;
+        // the adjoint span pass (spans 1 .. S - 1), then the adjoint entering every span
+        const dim3 grid((uint32_t)(units * (S - 1)));
+        if (q.z)
+            hipLaunchKernelGGL((m3_adjoint_span_kernel<T, N, ROT, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((m3_adjoint_span_kernel<T, N, ROT, false>), grid, block, 0, stream, a);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+        const int64_t columns = q.batch * q.d_inner * N;
+        const int64_t threads = ROT ? columns / 2 : columns;
+        hipLaunchKernelGGL(m3_mu_carry_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256),
+                           0, stream, q.ws_decay, ROT ? q.ws_rot : nullptr, q.mu_loc, q.dh_last,
+                           q.mu_in, columns, (int32_t)S);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    const dim3 grid((uint32_t)(units * S));
+    if (S > 1) {
+        if (q.z)
+            hipLaunchKernelGGL((scan_bwd_m3_kernel<T, N, ZOH, TRAP, ROT, true, true>), grid, block,
+                               0, stream, a);
+        else
+            hipLaunchKernelGGL((scan_bwd_m3_kernel<T, N, ZOH, TRAP, ROT, false, true>), grid,
+                               block, 0, stream, a);
+    } else {
+        if (q.z)
+            hipLaunchKernelGGL((scan_bwd_m3_kernel<T, N, ZOH, TRAP, ROT, true, false>), grid,
+                               block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((scan_bwd_m3_kernel<T, N, ZOH, TRAP, ROT, false, false>), grid,
+                               block, 0, stream, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess)
         return e;
     constexpr int V = 2 * N + (ROT ? N / 2 : 0);
     const int64_t nred = q.batch * q.L * V + (TRAP ? q.batch * N : 0);
     hipLaunchKernelGGL((m3_reduce_kernel<T>), dim3((uint32_t)((nred + 255) / 256)), dim3(256), 0,
                        stream, q.part, q.bprev_part, (T *)q.dB, (T *)q.dC, (T *)q.dtheta,
                        TRAP ? (T *)q.dB_prev : (T *)nullptr, q.batch, q.L, (int32_t)N,
-                       (int32_t)V, (int32_t)tiles);
+                       (int32_t)V, (int32_t)tiles, a.span_len, TRAP ? (int32_t)S : 1);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     const int64_t np = q.d_inner * N + q.d_inner;
     hipLaunchKernelGGL(m3_reduce_params_kernel, dim3((uint32_t)((np + 255) / 256)), dim3(256), 0,
-                       stream, q.dA_part, q.dDb_part, q.dA, q.dD, q.dbias, q.batch, q.d_inner,
+                       stream, q.dA_part, q.dDb_part, q.dA, q.dD, q.dbias, q.batch * S, q.d_inner,
                        (int64_t)N);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    if (TRAP && S > 1) {
+        const int64_t bd = q.batch * q.d_inner;
+        const int64_t n = (int64_t)(S - 1) * bd;
+        hipLaunchKernelGGL((m3_du_edge_kernel<T>), dim3((uint32_t)((n + 255) / 256)), dim3(256), 0,
+                           stream, q.du_edge, q.du_lb, (T *)q.du, bd, q.L, (int32_t)q.d_inner,
+                           a.span_len, (int32_t)S);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 template <typename T, int N>
@@ -617,22 +835,34 @@ hipError_t launch_m3_n(const M3BwdLaunch &q, hipStream_t stream)
 } // namespace
 
 size_t m3_bwd_workspace_bytes(int64_t batch, int64_t L, int64_t d_inner, int64_t d_state,
-                              bool rot, size_t off[6])
+                              bool rot, const M3Plan &plan, size_t off[15])
 {
     auto al = [](size_t n) { return (n + 255) / 256 * 256; };
     const size_t units = (size_t)batch * (size_t)((d_inner + 63) / 64);
-    const size_t n_seg = (size_t)((L + kM3Seg - 1) / kM3Seg);
+    const size_t S = (size_t)plan.n_spans;
+    // segments per block: of the whole sequence, or of one span
+    const size_t n_seg = S > 1 ? (size_t)(plan.span_len / kM3Seg)
+                               : (size_t)((L + kM3Seg - 1) / kM3Seg);
     const size_t N = (size_t)d_state, V = 2 * N + (rot ? N / 2 : 0), f = sizeof(float);
-    size_t sz[5];
-    sz[0] = al(units * n_seg * N * 64 * f);           // stored states
-    sz[1] = al(units * (size_t)L * V * f);             // dB, dC, dtheta tile partials
-    sz[2] = al(units * N * f);                         // dB_prev tile partials
-    sz[3] = al((size_t)batch * (size_t)d_inner * N * f); // dA per batch row
-    sz[4] = al((size_t)batch * (size_t)d_inner * 2 * f); // dD, dbias per batch row
+    const size_t bd = (size_t)batch * (size_t)d_inner, bdn = bd * N;
+    size_t sz[14] = {};
+    sz[0] = al(S * units * n_seg * N * 64 * f); // stored states
+    sz[1] = al(units * (size_t)L * V * f);      // dB, dC, dtheta tile partials
+    sz[2] = al(S * units * N * f);              // look-back dB shares (dB_prev at span 0)
+    sz[3] = al(S * bdn * f);                    // dA per (span, batch row)
+    sz[4] = al(S * bd * 2 * f);                 // dD, dbias per (span, batch row)
+    if (S > 1) {
+        const size_t rows = (size_t)L + (size_t)plan.fwd_chunk;
+        sz[5] = al((size_t)batch * rows * (2 * N + (rot ? N / 2 : 0)) * f);
+        sz[6] = sz[7] = sz[8] = al(S * bdn * f);
+        sz[9] = rot ? al(2 * S * bdn * f) : 0;
+        sz[10] = sz[11] = al(S * bdn * f);
+        sz[12] = sz[13] = al(S * bd * f);
+    }
     off[0] = 0;
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < 14; ++i)
         off[i + 1] = off[i] + sz[i];
-    return L > 0 ? off[5] : 0;
+    return L > 0 ? off[14] : 0;
 }
 
 hipError_t launch_scan_bwd_m3(const M3BwdLaunch &q, hipStream_t stream)

@@ -728,7 +728,18 @@ def test_bwd_ext_validation(lib):
     assert bwd_m3(lib, theta=TH, N=64) == UNSUP
     zoh = ms.ScanOpts(0, 0, 0, 0, 0, ms.MAMBA_DISC_ZOH)
     assert bwd_m3(lib, lam=LAM, opts=zoh) == UNSUP           # the trapezoid replaces the input
-    assert bwd_m3(lib, lam=LAM, opts=ms.ScanOpts(0, 0, 4, 0, 0, 0)) == UNSUP  # no split
+    assert bwd_m3(lib, lam=LAM, opts=ms.ScanOpts(0, 0, 65, 0, 0, 0)) == UNSUP  # 64 spans at most
+    # a split needs the forward span pass with the rotation: whole pairs per wave (not d_state 8)
+    assert bwd_m3(lib, theta=TH, N=8, opts=ms.ScanOpts(0, 0, 4, 0, 0, 0)) == UNSUP
+    assert lib.mamba_scan_bwd_ext_workspace_size(2, 64, 128, 8, ctypes.byref(ms.ScanExt(theta=TH)),
+                                                 ctypes.byref(ms.ScanOpts(0, 0, 4, 0, 0, 0))) \
+        == ctypes.c_size_t(-1).value
+    # with a split the workspace grows by the span regions
+    one = lib.mamba_scan_bwd_ext_workspace_size(2, 64, 128, 16, ctypes.byref(ms.ScanExt(LAM)),
+                                                ctypes.byref(ms.ScanOpts(0, 0, 1, 0, 0, 0)))
+    four = lib.mamba_scan_bwd_ext_workspace_size(2, 64, 128, 16, ctypes.byref(ms.ScanExt(LAM)),
+                                                 ctypes.byref(ms.ScanOpts(0, 0, 4, 0, 0, 0)))
+    assert 0 < one < four != ctypes.c_size_t(-1).value
     assert bwd_m3(lib, theta=TH, strides=(0, 0, 256, 0, 0)) == UNSUP
     assert bwd_m3(lib, lam=LAM, ws_bytes=1024) == WS
     assert bwd_m3(lib, lam=LAM + 1) == ALIGN

@@ -6,6 +6,7 @@ gpu_helpers: 1e-5 for fp32 inputs, 2e-2 for bf16.  Shapes span several 8-step se
 """
 from __future__ import annotations
 
+import ctypes
 import dataclasses
 
 import numpy as np
@@ -105,10 +106,10 @@ def test_zoh_backward_refuses_stored_checkpoints():
 M3_GRADS = GRADS + ("dlam", "du_prev", "dB_prev", "dtheta")
 
 
-def check_m3(label, inp, g, m3, *, trap, rot, zoh=False, prev=True):
+def check_m3(label, inp, g, m3, *, trap, rot, zoh=False, prev=True, n_spans=0):
     p = inp.params
     log(f"case {label}: batch {inp.cfg.batch} L {inp.cfg.seqlen} D {inp.cfg.d_inner} "
-        f"N {inp.cfg.d_state} {inp.dtype} trap {trap} rot {rot} zoh {zoh}")
+        f"N {inp.cfg.d_state} {inp.dtype} trap {trap} rot {rot} zoh {zoh} spans {n_spans}")
     out = ms.mamba_scan_bwd(to_dev(inp.u), to_dev(inp.delta), to_dev(p.A), to_dev(inp.B),
                             to_dev(inp.C), to_dev(g.dy), D=to_dev(p.D), z=to_dev(inp.z),
                             delta_bias=to_dev(p.bias), h0=to_dev(inp.h0),
@@ -117,7 +118,7 @@ def check_m3(label, inp, g, m3, *, trap, rot, zoh=False, prev=True):
                             lam=to_dev(m3.lam) if trap else None,
                             u_prev=to_dev(m3.u_prev) if (trap and prev) else None,
                             B_prev=to_dev(m3.B_prev) if (trap and prev) else None,
-                            theta=to_dev(m3.theta) if rot else None)
+                            theta=to_dev(m3.theta) if rot else None, n_spans=n_spans)
     torch.cuda.synchronize()
     f = lambda a: synth.to_f64(a, inp.dtype)  # noqa: E731
     ref = oracle.load().scan_bwd_ext(
@@ -158,6 +159,42 @@ def test_m3_backward_without_prev_and_gate():
     inp, g = case(16, synth.F32, batch=1, seqlen=130, d_inner=70, gate=False)
     m3 = synth.make_mamba3_inputs(inp.cfg)
     check_m3("m3 no prev, no gate", inp, g, m3, trap=True, rot=True, prev=False)
+
+
+# Sequence splits: 203 steps in 2 spans (104 + 99) or 3 (72 + 72 + 59), so the step before
+# each span is inside a segment and the last span ends in a partial segment.  With the
+# rotation a split needs d_state 16 or 32.
+M3_SPLIT_CASES = [(16, True, False, False), (16, False, True, False), (16, True, True, False),
+                  (16, False, True, True), (32, True, True, False), (8, True, False, False)]
+
+
+@pytest.mark.parametrize("n_spans", [2, 3])
+@pytest.mark.parametrize("n,trap,rot,zoh", M3_SPLIT_CASES)
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_m3_backward_split(n, trap, rot, zoh, dtype, n_spans):
+    inp, g = case(n, dtype, batch=2, seqlen=203, d_inner=96)
+    m3 = synth.make_mamba3_inputs(inp.cfg)
+    check_m3(f"m3 split N={n}", inp, g, m3, trap=trap, rot=rot, zoh=zoh, n_spans=n_spans)
+
+
+def test_m3_backward_split_without_prev_and_gate():
+    inp, g = case(16, synth.F32, batch=1, seqlen=300, d_inner=70, gate=False)
+    m3 = synth.make_mamba3_inputs(inp.cfg)
+    check_m3("m3 split, no prev, no gate", inp, g, m3, trap=True, rot=True, prev=False,
+             n_spans=5)
+
+
+def test_m3_backward_auto_split_long_sequence():
+    # one batch row of two channel tiles: the planner splits the sequence by itself
+    inp, g = case(16, synth.BF16, batch=1, seqlen=1024, d_inner=128)
+    m3 = synth.make_mamba3_inputs(inp.cfg)
+    lib = ms.load_library()
+    e = ms.ScanExt(1, None, None, 1)  # (only the options' presence matters for the size)
+    auto = lib.mamba_scan_bwd_ext_workspace_size(1, 1024, 128, 16, ctypes.byref(e), None)
+    one = lib.mamba_scan_bwd_ext_workspace_size(1, 1024, 128, 16, ctypes.byref(e),
+                                                ctypes.byref(ms.ScanOpts(0, 0, 1, 0, 0, 0)))
+    assert auto > one  # the span regions: the call is split
+    check_m3("m3 auto split", inp, g, m3, trap=True, rot=True)
 
 
 def m3_oracle_rows(inp, g, m3, ds, rows):
