@@ -355,6 +355,10 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
                     mu[j] = __builtin_fmaf(ds, cn[j], mu[j]); // mu_t
                     vc[j] = ds * hs[s][j];                    // dC
                 }
+                // trapezoid: the step's input term lam Delta B_t u_t + (1 - lam) Delta B_{t-1}
+                // u_{t-1} enters dDelta and dlam through sum mu B_t and sum mu B_{t-1} only
+                float smb = 0.0f, smp = 0.0f;
+                const float ldl = lm * dl, mdl = (1.0f - lm) * dl;
 #pragma unroll
                 for (int j = 0; j < NG; ++j) {
                     const float a = decay_exp2(dl, a2[j]);
@@ -362,13 +366,13 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
                     ddt = __builtin_fmaf(an[j], mah, ddt);
                     dA[j] = __builtin_fmaf(dl, mah, dA[j]);
                     if constexpr (TRAP) {
-                        // this step's term, and step t + 1's look-back, which read u_t, B_t
-                        ddt += mu[j] * __builtin_fmaf(1.0f - lm, bp[j] * up, lm * bn[j] * uu);
-                        const float wgt = __builtin_fmaf(mu[j], lm * dl, lbk[j]);
+                        smb = __builtin_fmaf(mu[j], bn[j], smb);
+                        smp = __builtin_fmaf(mu[j], bp[j], smp);
+                        // u_t and B_t feed this step's term and step t + 1's look-back
+                        const float wgt = __builtin_fmaf(mu[j], ldl, lbk[j]);
                         du = __builtin_fmaf(wgt, bn[j], du);
                         vb[j] = wgt * uu; // dB
-                        dlam = __builtin_fmaf(mu[j] * dl, bn[j] * uu - bp[j] * up, dlam);
-                        lbk[j] = mu[j] * (1.0f - lm) * dl;
+                        lbk[j] = mu[j] * mdl;
                     } else if constexpr (ZOH) {
                         const float x = dl * an[j];
                         const float beta = zoh_input(x, a, dl, ia[j]);
@@ -388,6 +392,10 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
                         vb[j] = mu[j] * dl * uu; // dB
                     }
                     mu[j] *= a; // nu = dLoss/dh'
+                }
+                if constexpr (TRAP) {
+                    ddt = __builtin_fmaf((1.0f - lm) * up, smp, __builtin_fmaf(lm * uu, smb, ddt));
+                    dlam = dl * __builtin_fmaf(uu, smb, -up * smp);
                 }
                 if constexpr (ROT) {
                     float th[KG];
