@@ -99,6 +99,9 @@ def parse():
     ap.add_argument("--bwd-variant", choices=("zoh", "trapezoid", "rotation"),
                     help="with --bwd-only: time the backward of this discretisation option "
                          "instead (for profiling)")
+    ap.add_argument("--bwd-config", choices=("c2", "c3", "c4"), default="c3",
+                    help="with --bwd-only --bwd-variant: the workload (default: the large "
+                         "prefill)")
     ap.add_argument("--ssd-only", action="store_true",
                     help="time only the Mamba-2 SSD scan on its large shape (for profiling) and "
                          "print its JSON summary")
@@ -673,13 +676,13 @@ def main():
     if args.bwd_only and args.bwd_variant:
         opts = {"zoh": dict(discretization="zoh"), "trapezoid": dict(trapezoid=True),
                 "rotation": dict(rotation=True)}[args.bwd_variant]
-        log(f"bench: backward pass on the large prefill, {args.bwd_variant}")
-        bcase = BwdCase(cfg, dev, **opts)
+        bcfg = synth.CONFIGS[args.bwd_config]
+        log(f"bench: backward pass on the {bcfg.desc}, {args.bwd_variant}")
+        bcase = BwdCase(bcfg, dev, **opts)
         loop_ms, _, _ = time_steps(bcase.step, args.steps, args.warmup)
         if args.copy_calibration:
             copy_calibration(dev)
-        print(json.dumps({"workload": f"backward of the large-model prefill scan, "
-                                      f"{args.bwd_variant}",
+        print(json.dumps({"workload": f"backward of the {bcfg.desc}, {args.bwd_variant}",
                           "steps": args.steps, "ms_per_step": round(loop_ms, 4),
                           "min_bytes_per_step": bcase.min_bytes,
                           "GB_s": round(bcase.min_bytes / (loop_ms * 1e-3) / 1e9, 1)}),
