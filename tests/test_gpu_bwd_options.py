@@ -106,14 +106,14 @@ def test_zoh_backward_refuses_stored_checkpoints():
 M3_GRADS = GRADS + ("dlam", "du_prev", "dB_prev", "dtheta")
 
 
-def check_m3(label, inp, g, m3, *, trap, rot, zoh=False, prev=True, n_spans=0):
+def check_m3(label, inp, g, m3, *, trap, rot, zoh=False, prev=True, n_spans=0, ends=True):
     p = inp.params
     log(f"case {label}: batch {inp.cfg.batch} L {inp.cfg.seqlen} D {inp.cfg.d_inner} "
         f"N {inp.cfg.d_state} {inp.dtype} trap {trap} rot {rot} zoh {zoh} spans {n_spans}")
     out = ms.mamba_scan_bwd(to_dev(inp.u), to_dev(inp.delta), to_dev(p.A), to_dev(inp.B),
                             to_dev(inp.C), to_dev(g.dy), D=to_dev(p.D), z=to_dev(inp.z),
-                            delta_bias=to_dev(p.bias), h0=to_dev(inp.h0),
-                            dh_last=to_dev(g.dh_last),
+                            delta_bias=to_dev(p.bias), h0=to_dev(inp.h0) if ends else None,
+                            dh_last=to_dev(g.dh_last) if ends else None,
                             discretization="zoh" if zoh else "euler",
                             lam=to_dev(m3.lam) if trap else None,
                             u_prev=to_dev(m3.u_prev) if (trap and prev) else None,
@@ -124,8 +124,8 @@ def check_m3(label, inp, g, m3, *, trap, rot, zoh=False, prev=True, n_spans=0):
     ref = oracle.load().scan_bwd_ext(
         f(inp.u), f(inp.delta), p.A.astype(np.float64), f(inp.B), f(inp.C), f(g.dy),
         D=p.D.astype(np.float64), z=f(inp.z) if inp.z is not None else None,
-        bias=p.bias.astype(np.float64), h0=inp.h0.astype(np.float64),
-        dh_last=g.dh_last.astype(np.float64), zoh=zoh,
+        bias=p.bias.astype(np.float64), h0=inp.h0.astype(np.float64) if ends else None,
+        dh_last=g.dh_last.astype(np.float64) if ends else None, zoh=zoh,
         lam=f(m3.lam) if trap else None,
         u_prev=f(m3.u_prev) if (trap and prev) else None,
         B_prev=f(m3.B_prev) if (trap and prev) else None,
@@ -182,6 +182,14 @@ def test_m3_backward_split_without_prev_and_gate():
     m3 = synth.make_mamba3_inputs(inp.cfg)
     check_m3("m3 split, no prev, no gate", inp, g, m3, trap=True, rot=True, prev=False,
              n_spans=5)
+
+
+def test_m3_backward_split_without_h0_and_dh_last():
+    # the spans' entering state from a zero h0, the adjoint from a zero dh_last
+    inp, g = case(16, synth.BF16, batch=2, seqlen=203, d_inner=96)
+    m3 = synth.make_mamba3_inputs(inp.cfg)
+    check_m3("m3 split, no h0, no dh_last", inp, g, m3, trap=True, rot=True, n_spans=3,
+             ends=False)
 
 
 def test_m3_backward_auto_split_long_sequence():
