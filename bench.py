@@ -583,8 +583,8 @@ def probe_rates(dev):
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b) * 1e-3)
         return sorted(ts)[len(ts) // 2]
-    forms = (("fma_vgpr", 0, 4096), ("fma_sgpr", 1, 4096), ("exp", 2, 2048),
-             ("update", 3, 256))
+    forms = (("fma_vgpr", 0, 4096), ("fma_sgpr", 1, 4096), ("fma_dpp", 4, 4096),
+             ("exp", 2, 2048), ("update", 3, 256), ("update_dpp", 5, 256))
     for name, kind, iters in forms:
         n = ctypes.c_uint64(0)
 
@@ -597,7 +597,7 @@ def probe_rates(dev):
         rate = n.value / sec
         out[name] = {"wave_instr_per_s": float(f"{rate:.4e}"),
                      "simd_cycles_at_2_4_ghz": round(cus * 4 * 2.4e9 / rate, 3)}
-    out["update"]["unit"] = "wave-level state updates"
+    out["update"]["unit"] = out["update_dpp"]["unit"] = "wave-level state updates"
     nbytes = 512 << 20
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)

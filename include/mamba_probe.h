@@ -35,11 +35,16 @@ MAMBA_API mamba_status_t mamba_probe_copy(const void *src, void *dst, size_t byt
 #define MAMBA_PROBE_EXP 2      /* v_exp_f32                                             */
 #define MAMBA_PROBE_UPDATE 3   /* the scan's state update: FMA, v_exp_f32, multiply by
                                   a scalar B, FMA (recurrence), FMA by a scalar C        */
+#define MAMBA_PROBE_FMA_DPP 4  /* v_fmac_f32 whose first operand is a DPP row broadcast
+                                  (row_newbcast) of a vector register                     */
+#define MAMBA_PROBE_UPDATE_DPP 5 /* the state update with B and C one value per lane of
+                                  a vector register, taken by DPP row broadcasts folded
+                                  into the multiply and the readout FMA                  */
 
 /* Runs compute_units x waves_per_simd workgroups of 256 threads (one wave per SIMD each),
  * every lane issuing `iters` iterations of 8 independent instructions of the given form
- * (MAMBA_PROBE_UPDATE: 8 steps x 2 states of the update per iteration).  *wave_instr (host)
- * receives the wave-level instructions of the launch (for MAMBA_PROBE_UPDATE: wave-level
+ * (MAMBA_PROBE_UPDATE, _UPDATE_DPP: 8 steps x 2 states of the update per iteration).
+ * *wave_instr (host) receives the wave-level instructions of the launch (for the updates: wave-level
  * state updates), so that instructions / elapsed time is the chip's issue rate of that form.
  * sink: device float buffer of compute_units x waves_per_simd x 256 entries (written, not
  * meaningful).  waves_per_simd in 1..8, iters >= 1, compute_units >= 1 (MAMBA_ERR_BAD_SHAPE),

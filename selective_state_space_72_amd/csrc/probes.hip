@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace {
 
 // Keep the compiler from hoisting, folding or dropping a value without emitting any
@@ -28,6 +30,26 @@ __global__ void __launch_bounds__(256) copy_kernel(const float4 *__restrict__ sr
         dst[i] = src[i];
 }
 
+// Value of v in lane K of the caller's 16-lane row (DPP row_newbcast); as the first
+// operand of a multiply or FMA the broadcast folds into the instruction.
+template <int K>
+__device__ __forceinline__ float row_bcast(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + K, 0xF, 0xF, true));
+}
+
+// acc += (v in lane K of the caller's 16-lane row) * w as one v_fmac_f32_dpp (the compiler
+// does not fold a broadcast into v_fmac).  v must not have been written by a VALU
+// instruction in the two instructions before (DPP read hazard): the callers' v comes from
+// memory or is set up well before the loop.
+template <int K>
+__device__ __forceinline__ void fmac_bcast(float &acc, float v, float w)
+{
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc)
+                 : "v"(v), "v"(w), "i"(K));
+}
+
 // One kernel per instruction form; `iters` iterations of kChains independent instructions.
 template <int KIND>
 __global__ void __launch_bounds__(kThreads) issue_kernel(float s, float s2, int iters,
@@ -45,6 +67,9 @@ __global__ void __launch_bounds__(kThreads) issue_kernel(float s, float s2, int 
                 acc[k] = __builtin_fmaf(v1, v2, acc[k]); // v_fmac_f32, VGPR operands
             } else if constexpr (KIND == MAMBA_PROBE_FMA_SGPR) {
                 acc[k] = __builtin_fmaf(s, v1, acc[k]); // v_fmac_f32 with an SGPR operand
+            } else if constexpr (KIND == MAMBA_PROBE_FMA_DPP) {
+                // v_fmac_f32 with src0 = lane 5 of each 16-lane row (row_newbcast:5)
+                fmac_bcast<5>(acc[k], v1, v2);
             } else if constexpr (KIND == MAMBA_PROBE_EXP) {
                 PROBE_OPAQUE(acc[k]);
                 const float r = __builtin_amdgcn_exp2f(acc[k]); // v_exp_f32
@@ -111,6 +136,65 @@ __global__ void __launch_bounds__(kThreads) update_kernel(UpdBC bc, int iters,
     sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
 }
 
+// The same update with B and C as vector registers holding one (step, state) value per lane
+// of each 16-lane row (lane 2t + q), taken by row broadcasts folded into the multiply and the
+// readout FMA: no scalar operands.
+__global__ void __launch_bounds__(kThreads) update_dpp_kernel(UpdBC bc, int iters,
+                                                               float *__restrict__ sink)
+{
+    float h[kUpdStates], a2[kUpdStates], y = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kUpdStates; ++q) {
+        h[q] = 0.0f;
+        a2[q] = -(q + 1) * 1.4427f - threadIdx.x * 1e-6f;
+    }
+    const int j = threadIdx.x & 15;
+    float vb = bc.b[0][0], vc = bc.c[0][0];
+#pragma unroll
+    for (int t = 0; t < kUpdSteps; ++t)
+#pragma unroll
+        for (int q = 0; q < kUpdStates; ++q) {
+            vb = j == kUpdStates * t + q ? bc.b[t][q] : vb;
+            vc = j == kUpdStates * t + q ? bc.c[t][q] : vc;
+        }
+    float dt[kUpdSteps], du[kUpdSteps];
+#pragma unroll
+    for (int t = 0; t < kUpdSteps; ++t) {
+        dt[t] = 1e-3f * (t + 1) + threadIdx.x * 1e-7f;
+        du[t] = 0.3f * t;
+    }
+    asm volatile("s_nop 4" ::: "memory"); // vb, vc written by VALU just above: DPP hazard
+    auto bcast = [](float v, auto K) { return row_bcast<decltype(K)::value>(v); };
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int t = 0; t < kUpdSteps; ++t) {
+            PROBE_OPAQUE(dt[t]);
+            PROBE_OPAQUE(du[t]);
+        }
+        PROBE_OPAQUE(vb);
+        PROBE_OPAQUE(vc);
+        float a[kUpdSteps][kUpdStates];
+#pragma unroll
+        for (int t = 0; t < kUpdSteps; ++t)
+#pragma unroll
+            for (int q = 0; q < kUpdStates; ++q)
+                a[t][q] = __builtin_amdgcn_exp2f(__builtin_fmaf(dt[t], a2[q], 8e-9f));
+#define UPD_STEP(T, Q)                                                                       \
+    h[Q] = __builtin_fmaf(a[T][Q], h[Q], bcast(vb, std::integral_constant<int, 2 * T + Q>{}) * du[T]); \
+    fmac_bcast<2 * T + Q>(y, vc, h[Q]);
+        UPD_STEP(0, 0) UPD_STEP(0, 1) UPD_STEP(1, 0) UPD_STEP(1, 1)
+        UPD_STEP(2, 0) UPD_STEP(2, 1) UPD_STEP(3, 0) UPD_STEP(3, 1)
+        UPD_STEP(4, 0) UPD_STEP(4, 1) UPD_STEP(5, 0) UPD_STEP(5, 1)
+        UPD_STEP(6, 0) UPD_STEP(6, 1) UPD_STEP(7, 0) UPD_STEP(7, 1)
+#undef UPD_STEP
+    }
+    float r = y;
+#pragma unroll
+    for (int q = 0; q < kUpdStates; ++q)
+        r += h[q];
+    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
 } // namespace
 
 extern "C" {
@@ -158,12 +242,18 @@ mamba_status_t mamba_probe_issue(int32_t kind, int32_t waves_per_simd, int32_t i
                            s, s2, iters, sink);
         *wave_instr = waves * (uint64_t)iters * kChains;
         break;
+    case MAMBA_PROBE_FMA_DPP:
+        hipLaunchKernelGGL(issue_kernel<MAMBA_PROBE_FMA_DPP>, dim3(blocks), dim3(kThreads), 0, st,
+                           s, s2, iters, sink);
+        *wave_instr = waves * (uint64_t)iters * kChains;
+        break;
     case MAMBA_PROBE_EXP:
         hipLaunchKernelGGL(issue_kernel<MAMBA_PROBE_EXP>, dim3(blocks), dim3(kThreads), 0, st, s,
                            s2, iters, sink);
         *wave_instr = waves * (uint64_t)iters * kChains;
         break;
-    case MAMBA_PROBE_UPDATE: {
+    case MAMBA_PROBE_UPDATE:
+    case MAMBA_PROBE_UPDATE_DPP: {
         UpdBC bc;
         for (int t = 0; t < kUpdSteps; ++t) {
             for (int q = 0; q < kUpdStates; ++q) {
@@ -171,7 +261,11 @@ mamba_status_t mamba_probe_issue(int32_t kind, int32_t waves_per_simd, int32_t i
                 bc.c[t][q] = 0.05f * t - q;
             }
         }
-        hipLaunchKernelGGL(update_kernel, dim3(blocks), dim3(kThreads), 0, st, bc, iters, sink);
+        if (kind == MAMBA_PROBE_UPDATE)
+            hipLaunchKernelGGL(update_kernel, dim3(blocks), dim3(kThreads), 0, st, bc, iters, sink);
+        else
+            hipLaunchKernelGGL(update_dpp_kernel, dim3(blocks), dim3(kThreads), 0, st, bc, iters,
+                               sink);
         *wave_instr = waves * (uint64_t)iters * kUpdSteps * kUpdStates; // wave-element updates
         break;
     }

@@ -238,7 +238,7 @@ scan_bwd_kernel(BwdArgs p)
 #pragma unroll
             for (int k = 0; k < KF; ++k) {
                 const int tl = g + k * NW;
-                const float dl = softplus_f(widen(fd[k]) + bias_d);
+                const float dl = softplus_act<T>(widen(fd[k]) + bias_d);
                 // (Delta, Delta u); ZOH: (Delta, u)
                 s_f[(par * kTCF + tl) * 64 + lane] =
                     make_float2(dl, ZOH ? widen(fu[k]) : dl * widen(fu[k]));
@@ -328,7 +328,7 @@ scan_bwd_kernel(BwdArgs p)
             const int tl = g + k * NW;
             const float uu = widen(ru[k]);
             const float v = widen(rd[k]) + bias_d;
-            const float dl = softplus_f(v);
+            const float dl = softplus_act<T>(v);
             const float dyv = dvalid ? widen(rg[k]) : 0.0f; // tail lanes: no gradient
             float gate = 1.0f, dgate = 0.0f;
             if (GATED) {
@@ -694,7 +694,7 @@ scan_bwd_musum_kernel(MuSumArgs p)
                 const float zz = widen(rz[k]);
                 gate = zz * hw_rcp(1.0f + hw_exp2(-zz * kLog2e));
             }
-            s_m[par][tl][lane] = make_float2(softplus_f(v), widen(rg[k]) * gate);
+            s_m[par][tl][lane] = make_float2(softplus_act<T>(v), widen(rg[k]) * gate);
         }
         if (lane < kTCF * NQ)
             s_c[par][g][lane] = cv;

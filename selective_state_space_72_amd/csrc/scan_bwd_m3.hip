@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
                        float (&sn)[KG], float (&cs)[KG]) {
         const int64_t bld = (row0 + t) * Dn + dc;
         const float uu = ld(p.u, bld);
-        const float dl = softplus_f(ld(p.delta, bld) + bias_d);
+        const float dl = softplus_act<T>(ld(p.delta, bld) + bias_d);
         if constexpr (ROT) {
             float th[KG];
             load_vec<T, KG>(p.theta, (row0 + t) * K + k0, th);
@@ -318,7 +318,7 @@ __global__ void __launch_bounds__(256) scan_bwd_m3_kernel(M3Args p)
                 const int64_t bld = (row0 + t) * Dn + dc;
                 const float uu = ld(p.u, bld);
                 const float v = ld(p.delta, bld) + bias_d;
-                const float dl = softplus_f(v);
+                const float dl = softplus_act<T>(v);
                 const float sig = hw_rcp(1.0f + hw_exp2(-v * kLog2e)); // softplus'(v)
                 const float dyv = dvalid ? ld(p.dy, bld) : 0.0f;
                 float gate = 1.0f, dgate = 0.0f;
@@ -549,7 +549,7 @@ __global__ void __launch_bounds__(256) m3_adjoint_span_kernel(M3Args p)
     const float bias_d = p.bias ? p.bias[dc] : 0.0f;
     auto step = [&](int64_t t) {
         const int64_t bld = (row0 + t) * Dn + dc;
-        const float dl = softplus_f(load_val((const T *)p.delta, bld) + bias_d);
+        const float dl = softplus_act<T>(load_val((const T *)p.delta, bld) + bias_d);
         float ds = dvalid ? load_val((const T *)p.dy, bld) : 0.0f;
         if constexpr (GATED) {
             const float zz = load_val((const T *)p.z, bld);

@@ -140,7 +140,7 @@ scan_chunk_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T 
             gz[k] = 1.0f;
             if (tl < nt) {
                 const float uu = widen(ru[j][k]);
-                dl = softplus_f(widen(rd[j][k]) + bias_d);
+                dl = softplus_act<T>(widen(rd[j][k]) + bias_d);
                 w = dl * uu;
                 if (FULL) {
                     du[k] = D_d * uu;

@@ -148,7 +148,7 @@ scan_rows_kernel(const T *__restrict__ u, const T *__restrict__ delta, const T *
         float dl = 0.0f, w = 0.0f, du = 0.0f, gz = 1.0f;
         if (!guarded || r < nt) {
             const float uu = widen(ru[j]);
-            dl = softplus_f(widen(rd[j]) + bias_d);
+            dl = softplus_act<T>(widen(rd[j]) + bias_d);
             w = dl * uu;
             if (FULL) {
                 du = D_d * uu;

@@ -379,7 +379,7 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
         for (int k = 0; k < KPL; ++k) {
             const int tl = g + k * NW;
             const float uu = widen(ru[j][k]);
-            const float dl = softplus_f(widen(rd[j][k]) + bias_d);
+            const float dl = softplus_act<T>(widen(rd[j][k]) + bias_d);
             du[k] = FULL ? D_d * uu : 0.0f;
             gz[k] = gated ? silu_f(widen(rz[j][k])) : 1.0f;
             if (!FULL && tl < nt)

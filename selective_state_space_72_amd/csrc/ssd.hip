@@ -426,7 +426,7 @@ ssd_chunk_kernel(SsdArgs p)
     auto decays = [&](int64_t c0) {
         const int nn = (int)min((int64_t)Q, t_end - c0);
         const float dv = ES == 2 ? __uint_as_float(fdt << 16) : __uint_as_float(fdt);
-        const float dl = lane < nn ? softplus_f(dv + dtb) : 0.0f;
+        const float dl = lane < nn ? softplus_act<T>(dv + dtb) : 0.0f;
         float cs = dl * a2, csl = 0.0f;
         auto add = [&](float vh, float vl) {
             float sh, e;

@@ -45,7 +45,7 @@ ssd_step_kernel(float *__restrict__ h, const T *__restrict__ x, const T *__restr
     const f32x4 hv = __builtin_nontemporal_load(hp);
 
     const float xv = load_val(x, c);
-    const float dl = softplus_f(load_val(dt, (int64_t)b * H + hd) + (bias ? bias[hd] : 0.0f));
+    const float dl = softplus_act<T>(load_val(dt, (int64_t)b * H + hd) + (bias ? bias[hd] : 0.0f));
     const float a = decay_exp2(dl, A[hd] * kLog2e);
     const float w = dl * xv;
     const int64_t bn = (int64_t)b * N + 4 * q;

@@ -76,7 +76,7 @@ state_update_kernel(float *__restrict__ h, const T *__restrict__ u, const T *__r
     }
 
     const float uu = load_val(u, b * ext.su + d);
-    const float dl = softplus_f(load_val(delta, b * ext.sd + d) + (bias ? bias[d] : 0.0f));
+    const float dl = softplus_act<T>(load_val(delta, b * ext.sd + d) + (bias ? bias[d] : 0.0f));
     const float w = dl * uu;
     const int64_t bn = (int64_t)b * nr + 4 * q;                 // B_prev, theta rows
     const int64_t bB = (int64_t)b * ext.sB + 4 * q, bC = (int64_t)b * ext.sC + 4 * q;

@@ -368,6 +368,29 @@ def test_step_size_softplus_accuracy():
     assert rel.max() < 2e-6
 
 
+def test_step_size_softplus_accuracy_bf16():
+    """bf16 activations take the softplus without the log1p compensation term.  L = 1,
+    h0 = 0, u = B = 1: the fp32 final state is h_last[d, n] = Delta exactly, compared with
+    the fp64 softplus of the same bf16 delta: absolute error near 1e-7 (the rounding of
+    1 + e^-|v| and of v_log_f32), far below the bf16 rounding of delta itself."""
+    n, d = 16, 4096
+    delta = torch.linspace(-40.0, 40.0, d).to(torch.bfloat16)
+    dl = delta.view(1, 1, d).to(DEV)
+    u = torch.ones(1, 1, d, device=DEV, dtype=torch.bfloat16)
+    A = -torch.ones(d, n, device=DEV)
+    B = torch.ones(1, 1, n, device=DEV, dtype=torch.bfloat16)
+    C = torch.full((1, 1, n), 1.0 / n, device=DEV, dtype=torch.bfloat16)
+    _, h = ms.mamba_scan_fwd(u, dl, A, B, C, return_last_state=True)
+    torch.cuda.synchronize()
+    ref = np.logaddexp(0.0, delta.float().numpy().astype(np.float64))
+    hd = from_dev(h).reshape(d, n).astype(np.float64)
+    err = np.abs(hd - ref[:, None])
+    assert np.all(hd == hd[:, :1])
+    log(f"  bf16 softplus: max abs err {err.max():.3e}, "
+        f"max rel err above Delta 1e-3 {(err / ref[:, None])[ref >= 1e-3].max():.3e}")
+    assert np.all(err <= 2e-7 + 2e-7 * ref[:, None])
+
+
 def test_long_fp32_decay_error_growth():
     """u = 0, h0 = 1 over 4096 steps (fp32): y_t = sum_n C exp(A_n S_t); the error of the
     running product of v_exp_f32 values grows with t and is reported per quarter."""
