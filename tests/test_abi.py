@@ -704,7 +704,7 @@ def test_probe_argument_checks(lib):
     assert lib.mamba_probe_copy(BASE, BASE + MB, 0, 4, None) == OK
     assert lib.mamba_probe_issue(0, 9, 1, 256, BASE, ctypes.byref(n), None) == 2
     assert lib.mamba_probe_issue(0, 1, 0, 256, BASE, ctypes.byref(n), None) == 2
-    assert lib.mamba_probe_issue(4, 1, 1, 256, BASE, ctypes.byref(n), None) == UNSUP
+    assert lib.mamba_probe_issue(6, 1, 1, 256, BASE, ctypes.byref(n), None) == UNSUP
     assert lib.mamba_probe_issue(0, 1, 1, 256, None, ctypes.byref(n), None) == NULL
 
 
