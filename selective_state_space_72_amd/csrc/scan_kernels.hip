@@ -348,48 +348,60 @@ __device__ __forceinline__ float lane_up(float v)
         return __shfl_up(v, OFF, 64);
 }
 
-// One wave scans 64/SEG state columns; lane = (column, span).  Span s (< n_spans-1)
-// contributes the map x -> decay_s * x + hloc_s; the inclusive composition over spans
-// 0..s applied to h0 is the state entering span s+1.
+// A block carries 64 consecutive state columns; each wave scans 64/SEG of them at a time,
+// lane = (column, span).  Span s (< n_spans-1) contributes the map x -> decay_s * x + hloc_s;
+// the inclusive composition over spans 0..s applied to h0 is the state entering span s+1.
+// The results go through LDS so that the block writes each span's 64 columns as one
+// contiguous run (h_in is [span][column]).
 template <int SEG>
 __global__ void __launch_bounds__(256)
 carry_kernel(const float *__restrict__ decay, const float *__restrict__ hloc,
              const float *__restrict__ h0, float *__restrict__ h_in, int64_t columns,
              int32_t n_spans)
 {
+    constexpr int CPW = 64 / SEG; // columns per wave and round
+    __shared__ float tile[SEG][65];
     const int lane = threadIdx.x & 63;
-    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int w = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
     const int s = lane % SEG;
-    const int64_t col = wave * (64 / SEG) + lane / SEG;
-    const bool valid = col < columns;
-    const int64_t c = valid ? col : columns - 1;
-
     const int nmaps = n_spans - 1; // spans whose summary is needed
-    float a = 1.0f, bb = 0.0f;     // identity map
-    if (s < nmaps) {
-        a = decay[c * n_spans + s];
-        bb = hloc[c * n_spans + s];
-    }
-    auto combine = [&](float ap, float bp, int off) {
-        if (s >= off) { // (prefix up to s-off) then (own segment)
-            bb = __builtin_fmaf(a, bp, bb);
-            a = a * ap;
+    for (int r = 0; r * 4 * CPW < 64; ++r) {
+        const int cl = (r * 4 + w) * CPW + lane / SEG; // local column (wave-uniform bound)
+        if ((r * 4 + w) * CPW >= 64)
+            break;
+        const int64_t col = c0 + cl;
+        const int64_t c = col < columns ? col : columns - 1;
+        float a = 1.0f, bb = 0.0f; // identity map
+        if (s < nmaps) {
+            a = decay[c * n_spans + s];
+            bb = hloc[c * n_spans + s];
         }
-    };
-    if constexpr (SEG > 1) { const float ap = lane_up<SEG, 1>(a), bp = lane_up<SEG, 1>(bb); combine(ap, bp, 1); }
-    if constexpr (SEG > 2) { const float ap = lane_up<SEG, 2>(a), bp = lane_up<SEG, 2>(bb); combine(ap, bp, 2); }
-    if constexpr (SEG > 4) { const float ap = lane_up<SEG, 4>(a), bp = lane_up<SEG, 4>(bb); combine(ap, bp, 4); }
-    if constexpr (SEG > 8) { const float ap = lane_up<SEG, 8>(a), bp = lane_up<SEG, 8>(bb); combine(ap, bp, 8); }
-    if constexpr (SEG > 16) { const float ap = lane_up<SEG, 16>(a), bp = lane_up<SEG, 16>(bb); combine(ap, bp, 16); }
-    if constexpr (SEG > 32) { const float ap = lane_up<SEG, 32>(a), bp = lane_up<SEG, 32>(bb); combine(ap, bp, 32); }
-
-    if (!valid)
-        return;
-    const float x0 = h0 ? h0[c] : 0.0f;
-    if (s == 0)
-        h_in[c] = x0;
-    if (s < nmaps)
-        h_in[(int64_t)(s + 1) * columns + c] = __builtin_fmaf(a, x0, bb);
+        auto combine = [&](float ap, float bp, int off) {
+            if (s >= off) { // (prefix up to s-off) then (own segment)
+                bb = __builtin_fmaf(a, bp, bb);
+                a = a * ap;
+            }
+        };
+        if constexpr (SEG > 1) { const float ap = lane_up<SEG, 1>(a), bp = lane_up<SEG, 1>(bb); combine(ap, bp, 1); }
+        if constexpr (SEG > 2) { const float ap = lane_up<SEG, 2>(a), bp = lane_up<SEG, 2>(bb); combine(ap, bp, 2); }
+        if constexpr (SEG > 4) { const float ap = lane_up<SEG, 4>(a), bp = lane_up<SEG, 4>(bb); combine(ap, bp, 4); }
+        if constexpr (SEG > 8) { const float ap = lane_up<SEG, 8>(a), bp = lane_up<SEG, 8>(bb); combine(ap, bp, 8); }
+        if constexpr (SEG > 16) { const float ap = lane_up<SEG, 16>(a), bp = lane_up<SEG, 16>(bb); combine(ap, bp, 16); }
+        if constexpr (SEG > 32) { const float ap = lane_up<SEG, 32>(a), bp = lane_up<SEG, 32>(bb); combine(ap, bp, 32); }
+        const float x0 = h0 ? h0[c] : 0.0f;
+        tile[s][cl] = __builtin_fmaf(a, x0, bb);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * (nmaps + 1); i += 256) {
+        const int sp = i >> 6, j = i & 63;
+        const int64_t col = c0 + j;
+        if (col >= columns)
+            continue;
+        // span 0 enters with h0; span sp + 1 with the composition over spans 0..sp
+        h_in[(int64_t)sp * columns + col] =
+            sp == 0 ? (h0 ? h0[col] : 0.0f) : tile[sp - 1][j];
+    }
 }
 
 // Carry with the pair rotation: a span maps a state pair x to M x + b with M its 2x2
@@ -435,8 +447,7 @@ hipError_t launch_carry(const CarryLaunch &p, hipStream_t stream)
         seg <<= 1;
     if (seg > 64)
         return hipErrorInvalidValue;
-    const int64_t waves = (p.columns * seg + 63) / 64;
-    const int64_t blocks = (waves + 3) / 4;
+    const int64_t blocks = (p.columns + 63) / 64;
     if (blocks <= 0)
         return hipSuccess;
 #define CARRY_CASE(S_)                                                                    \

@@ -37,8 +37,10 @@ __device__ __forceinline__ void for_c(F &&f)
 // bcp[((b * NW + g) * Lp + t) * BCW + {q, NQ + q}] = {B, C}[b, t, g * NQ + q] (0 past L;
 // rows (b, t) of B and C start sB and sC elements apart),
 // BCW = 2 NQ; with rotation rates (ROT) also bcp[... + 2 NQ + q / 2] = theta[b, t, (g NQ + q)
-// / 2] for even q, BCW = 2 NQ + NQ / 2.  Also zeroes the relay hand-off flags and fault word
-// (n_sync words) for the scan launch that follows on the same stream.
+// / 2] for even q, BCW = 2 NQ + NQ / 2.  One thread per (b, g, t), t fastest, writes the BCW
+// contiguous values of its row, so consecutive threads write consecutive rows.  Also zeroes
+// the relay hand-off flags and fault word (n_sync words) for the scan launch that follows on
+// the same stream.
 template <typename T, int N, int NW, bool ROT>
 __global__ void __launch_bounds__(256)
 stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, const T *__restrict__ th,
@@ -47,27 +49,36 @@ stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, const T *__r
 {
     constexpr int NQ = N / NW;
     constexpr int BCW = 2 * NQ + (ROT ? NQ / 2 : 0);
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; // over batch * Lp * N
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; // over batch * NW * Lp
     if (i < n_sync)
         sync[i] = 0u;
     if (i >= total)
         return;
-    const int n = (int)(i % N);
-    const int64_t t = (i / N) % Lp;
-    const int64_t b = i / ((int64_t)N * Lp);
-    const int g = n / NQ, q = n % NQ;
-    float bv = 0.0f, cv = 0.0f;
+    const int64_t t = i % Lp;
+    const int64_t bg = i / Lp; // b * NW + g
+    const int g = (int)(bg % NW);
+    const int64_t b = bg / NW;
+    const int n0 = g * NQ;
+    float v[BCW];
+#pragma unroll
+    for (int k = 0; k < BCW; ++k)
+        v[k] = 0.0f;
     if (t < L) {
-        bv = load_val(Bm, (b * L + t) * sB + n);
-        cv = load_val(Cm, (b * L + t) * sC + n);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            v[q] = load_val(Bm, (b * L + t) * sB + n0 + q);
+            v[NQ + q] = load_val(Cm, (b * L + t) * sC + n0 + q);
+        }
+        if constexpr (ROT) {
+#pragma unroll
+            for (int k = 0; k < NQ / 2; ++k)
+                v[2 * NQ + k] = load_val(th, (b * L + t) * (N / 2) + n0 / 2 + k);
+        }
     }
-    float *dst = bcp + ((b * NW + g) * Lp + t) * BCW;
-    dst[q] = bv;
-    dst[NQ + q] = cv;
-    if constexpr (ROT) {
-        if (q % 2 == 0)
-            dst[2 * NQ + q / 2] = t < L ? load_val(th, (b * L + t) * (N / 2) + n / 2) : 0.0f;
-    }
+    float *dst = bcp + i * BCW;
+#pragma unroll
+    for (int k = 0; k < BCW; ++k)
+        dst[k] = v[k];
 }
 
 // Activations of one (batch row, span) are read and written through buffer resources
@@ -625,7 +636,7 @@ hipError_t launch_scalar_variant(const ScanLaunch &p, hipStream_t stream)
 template <typename T, int N, int NW>
 hipError_t launch_stage(const ScanLaunch &p, hipStream_t stream)
 {
-    const int64_t total = p.batch * p.staged_rows * N;
+    const int64_t total = p.batch * NW * p.staged_rows; // one thread per (b, wave, t)
     // hand-off flags and the fault word after them
     const int32_t n_sync = p.relay_parts > 1 ? p.relay_tiles * (p.relay_parts - 1) + 1 : 0;
     const int64_t blocks = (max(total, (int64_t)n_sync) + 255) / 256;
