@@ -366,31 +366,40 @@ carry_kernel(const float *__restrict__ decay, const float *__restrict__ hloc,
     const int64_t c0 = (int64_t)blockIdx.x * 64;
     const int s = lane % SEG;
     const int nmaps = n_spans - 1; // spans whose summary is needed
-    for (int r = 0; r * 4 * CPW < 64; ++r) {
-        const int cl = (r * 4 + w) * CPW + lane / SEG; // local column (wave-uniform bound)
-        if ((r * 4 + w) * CPW >= 64)
-            break;
-        const int64_t col = c0 + cl;
+    // rounds per wave; every round's loads are issued before the first scan
+    constexpr int R = 16 / CPW > 0 ? 16 / CPW : 1;
+    float a[R], bb[R], x0[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int cl = (r * 4 + w) * CPW + lane / SEG; // local column
+        const int64_t col = c0 + (cl < 64 ? cl : 63);
         const int64_t c = col < columns ? col : columns - 1;
-        float a = 1.0f, bb = 0.0f; // identity map
+        a[r] = 1.0f; // identity map
+        bb[r] = 0.0f;
         if (s < nmaps) {
-            a = decay[c * n_spans + s];
-            bb = hloc[c * n_spans + s];
+            a[r] = decay[c * n_spans + s];
+            bb[r] = hloc[c * n_spans + s];
         }
+        x0[r] = h0 ? h0[c] : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int cl = (r * 4 + w) * CPW + lane / SEG;
+        float ar = a[r], br = bb[r];
         auto combine = [&](float ap, float bp, int off) {
             if (s >= off) { // (prefix up to s-off) then (own segment)
-                bb = __builtin_fmaf(a, bp, bb);
-                a = a * ap;
+                br = __builtin_fmaf(ar, bp, br);
+                ar = ar * ap;
             }
         };
-        if constexpr (SEG > 1) { const float ap = lane_up<SEG, 1>(a), bp = lane_up<SEG, 1>(bb); combine(ap, bp, 1); }
-        if constexpr (SEG > 2) { const float ap = lane_up<SEG, 2>(a), bp = lane_up<SEG, 2>(bb); combine(ap, bp, 2); }
-        if constexpr (SEG > 4) { const float ap = lane_up<SEG, 4>(a), bp = lane_up<SEG, 4>(bb); combine(ap, bp, 4); }
-        if constexpr (SEG > 8) { const float ap = lane_up<SEG, 8>(a), bp = lane_up<SEG, 8>(bb); combine(ap, bp, 8); }
-        if constexpr (SEG > 16) { const float ap = lane_up<SEG, 16>(a), bp = lane_up<SEG, 16>(bb); combine(ap, bp, 16); }
-        if constexpr (SEG > 32) { const float ap = lane_up<SEG, 32>(a), bp = lane_up<SEG, 32>(bb); combine(ap, bp, 32); }
-        const float x0 = h0 ? h0[c] : 0.0f;
-        tile[s][cl] = __builtin_fmaf(a, x0, bb);
+        if constexpr (SEG > 1) { const float ap = lane_up<SEG, 1>(ar), bp = lane_up<SEG, 1>(br); combine(ap, bp, 1); }
+        if constexpr (SEG > 2) { const float ap = lane_up<SEG, 2>(ar), bp = lane_up<SEG, 2>(br); combine(ap, bp, 2); }
+        if constexpr (SEG > 4) { const float ap = lane_up<SEG, 4>(ar), bp = lane_up<SEG, 4>(br); combine(ap, bp, 4); }
+        if constexpr (SEG > 8) { const float ap = lane_up<SEG, 8>(ar), bp = lane_up<SEG, 8>(br); combine(ap, bp, 8); }
+        if constexpr (SEG > 16) { const float ap = lane_up<SEG, 16>(ar), bp = lane_up<SEG, 16>(br); combine(ap, bp, 16); }
+        if constexpr (SEG > 32) { const float ap = lane_up<SEG, 32>(ar), bp = lane_up<SEG, 32>(br); combine(ap, bp, 32); }
+        if (cl < 64)
+            tile[s][cl] = __builtin_fmaf(ar, x0[r], br);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < 64 * (nmaps + 1); i += 256) {
