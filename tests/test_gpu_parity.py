@@ -141,6 +141,16 @@ VARIANTS = [dict(waves=8, chunk_len=16), dict(waves=8, chunk_len=8), dict(waves=
             dict(kernel="scalar", n_spans=5), dict(kernel="scalar", n_spans=64)]
 
 
+@pytest.mark.parametrize("n_spans", [12, 24, 40])
+def test_carry_span_counts(n_spans):
+    """Span counts whose carry pass runs 16- and 32-lane segments (the other tests cover 1,
+    2, 4, 8 and 64), over 1120 state columns: the last 64-column block of the carry is
+    partial, as is the last channel tile."""
+    inp = synth.make_scan_inputs(synth.CONFIGS["c3"], batch=1, seqlen=2000, d_inner=70, seed=13)
+    inp.h0 = np.random.default_rng(6).standard_normal((1, 70, 16), dtype=np.float32)
+    full_check(f"carry n_spans={n_spans}", inp, kernel="scalar", n_spans=n_spans)
+
+
 @pytest.mark.parametrize("opts", VARIANTS, ids=[str(v) for v in VARIANTS])
 def test_variants_agree_with_oracle(opts):
     inp = synth.make_scan_inputs(synth.CONFIGS["c3"], batch=3, seqlen=1000, d_inner=200, seed=11)
