@@ -107,6 +107,20 @@ __device__ __forceinline__ float zoh_input(float x, float abar, float du, float 
     return __builtin_fabsf(x) < 0.0625f ? small : large;
 }
 
+// zoh_input with the argument in base 2, xb = Delta A log2(e) (the decay factor's exp2
+// argument, shift included): x = xb ln 2, so the series' coefficients carry the powers of
+// ln 2 and the switch is at |xb| = 1 / (16 ln 2).  Saves the multiply that forms x; the
+// shift moves x by 5.5e-9, and phi(x) by less than 3e-9.
+__device__ __forceinline__ float zoh_input_b2(float xb, float abar, float du, float u_over_a) {
+    constexpr float c1 = 0.34657359027997264f;  // ln 2 / 2
+    constexpr float c2 = 0.08007550231970024f;  // (ln 2)^2 / 6
+    constexpr float c3 = 0.013876027166205393f; // (ln 2)^3 / 24
+    const float p = __builtin_fmaf(xb, __builtin_fmaf(xb, __builtin_fmaf(xb, c3, c2), c1), 1.0f);
+    const float small = du * p;
+    const float large = __builtin_fmaf(abar, u_over_a, -u_over_a);
+    return __builtin_fabsf(xb) < 0.09016844005556021f ? small : large;
+}
+
 // sin and cos of x: reduction x = j pi/2 + r with the three-part constant of Cody and
 // Waite (pi/2 = C1 + C2 + C3, C1 with 8 significant bits; each part removed with one FMA),
 // then the single-precision minimax polynomials of S. Moshier's Cephes library for sin and
