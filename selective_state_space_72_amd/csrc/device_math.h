@@ -179,6 +179,20 @@ __device__ __forceinline__ void sincos_act(float x, float &sn, float &cs) {
     else
         sincos_fast(x, sn, cs);
 }
+// The same from an angle staged for element type T: bf16 activations stage the rotation
+// rate already divided by 2 pi, so phi_st is in revolutions and goes to v_sin_f32 /
+// v_cos_f32 without the multiply; fp32 activations stage the rate as given.
+constexpr float kInv2Pi = 0.159154943091895336f;
+template <typename T>
+__device__ __forceinline__ void sincos_staged(float phi_st, float &sn, float &cs) {
+    if constexpr (sizeof(T) == 2) {
+        sn = __builtin_amdgcn_sinf(phi_st);
+        cs = __builtin_amdgcn_cosf(phi_st);
+    } else {
+        sincos_fast(phi_st, sn, cs);
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ void rotate_pair_act(float phi, float &x, float &w) {
     float sn, cs;

@@ -37,7 +37,7 @@ __device__ __forceinline__ void for_c(F &&f)
 // bcp[((b * NW + g) * Lp + t) * BCW + {q, NQ + q}] = {B, C}[b, t, g * NQ + q] (0 past L;
 // rows (b, t) of B and C start sB and sC elements apart),
 // BCW = 2 NQ; with rotation rates (ROT) also bcp[... + 2 NQ + q / 2] = theta[b, t, (g NQ + q)
-// / 2] for even q, BCW = 2 NQ + NQ / 2.  One thread per (b, g, t), t fastest, writes the BCW
+// / 2] for even q (divided by 2 pi for bf16 activations), BCW = 2 NQ + NQ / 2.  One thread per (b, g, t), t fastest, writes the BCW
 // contiguous values of its row, so consecutive threads write consecutive rows.  Also zeroes
 // the relay hand-off flags and fault word (n_sync words) for the scan launch that follows on
 // the same stream.
@@ -72,7 +72,8 @@ stage_bc_kernel(const T *__restrict__ Bm, const T *__restrict__ Cm, const T *__r
         if constexpr (ROT) {
 #pragma unroll
             for (int k = 0; k < NQ / 2; ++k)
-                v[2 * NQ + k] = load_val(th, (b * L + t) * (N / 2) + n0 / 2 + k);
+                v[2 * NQ + k] = load_val(th, (b * L + t) * (N / 2) + n0 / 2 + k) *
+                                (sizeof(T) == 2 ? kInv2Pi : 1.0f); // see sincos_staged
         }
     }
     float *dst = bcp + i * BCW;
@@ -444,12 +445,14 @@ scan_scalar_kernel(const T *__restrict__ u, const T *__restrict__ delta,
                 for (int k = 0; k < NQ / 2; ++k) {
                     if constexpr (RM) { // the same turn of the pair's transition columns
                         float sn, cs;
-                        sincos_act<T>(dw[tl].x * bcs[tl][2 * NQ + k], sn, cs);
+                        sincos_staged<T>(dw[tl].x * bcs[tl][2 * NQ + k], sn, cs);
                         turn_pair(sn, cs, h[2 * k], h[2 * k + 1]);
                         turn_pair(sn, cs, rm[4 * k], rm[4 * k + 1]);
                         turn_pair(sn, cs, rm[4 * k + 2], rm[4 * k + 3]);
                     } else {
-                        rotate_pair_act<T>(dw[tl].x * bcs[tl][2 * NQ + k], h[2 * k], h[2 * k + 1]);
+                        float sn, cs;
+                        sincos_staged<T>(dw[tl].x * bcs[tl][2 * NQ + k], sn, cs);
+                        turn_pair(sn, cs, h[2 * k], h[2 * k + 1]);
                     }
                 }
             }
